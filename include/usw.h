@@ -1,0 +1,188 @@
+/*
+ * usw.h -- bitmap-encoded unstructured-sparse weight x dense activation SpMM
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is Y = W_sp . X with W_sp = W (elementwise) M, the static
+ * unstructured pruning of "Unified Static-Dynamic Pruning for Efficient LLM
+ * Inference" (section 2.2, static-pruning equation), computed from W_sp held
+ * in the TCA-BME bitmap format described in the blog "SpInfer: How bitmaps
+ * make sparse LLMs actually fast" (section "How TCA-BME addresses the
+ * indexing overhead"):
+ *
+ *   - BitmapTile: an 8x8 block of W; one uint64 word, bit p <-> position p of
+ *     the block taken row-major (p = 8*row + col), least significant bit first.
+ *   - TCTile: 16x16 = 2x2 BitmapTiles, stored row-major (top-left, top-right,
+ *     bottom-left, bottom-right).
+ *   - GroupTile: gt_m x gt_k (multiples of 16; 64x64 by default) = TCTiles
+ *     stored row-major; GroupTiles of the matrix stored row-major.
+ *   - bitmaps[NBT]: all BitmapTile words in that storage order (NBT = M*K/64).
+ *   - values[NNZ]: the kept elements, packed with no gaps in the same order
+ *     (GroupTile -> TCTile -> BitmapTile -> position).
+ *   - offsets[NGT+1]: uint32 element index of each GroupTile's first value,
+ *     offsets[0] = 0 and offsets[NGT] = NNZ (NGT = (M/gt_m)*(K/gt_k)).
+ *   Logical storage 4*(NGT+1) + 8*NBT + 2*NNZ bytes (the blog's storage
+ *   equation).  A value is located by masked popcount: its index is the
+ *   GroupTile offset plus the set bits that precede it in storage order (blog
+ *   section "Shared Memory Bitmap Decoding (SMBD)").
+ *
+ * INT4 values (USW_VAL_I4): per output row m a symmetric scale
+ *   scale[m] = fp16_rne(max|w| over row m's kept entries / 7) and
+ *   q = clamp(round_half_even(w / scale[m]), -8, 7), all in fp64 (q = 0 when
+ *   the scale is 0); the dequantised weight is q * scale[m].  Element 2i of the
+ *   packed stream is the low nibble of byte i, element 2i+1 the high nibble,
+ *   two's complement; a trailing high nibble is 0.  Quantisation shrinks the
+ *   payload but not the bitmap metadata ("UnionSparse", motivation section on
+ *   the payload-to-metadata ratio).
+ *
+ * Layouts of the product: X is [N][K] fp16 row-major (one row per token, the
+ * transposed activation tile the pages stage), Y is [N][M] row-major, fp16
+ * (rounded to nearest even from the fp32 accumulator) or fp32.
+ *
+ * Ownership: the caller allocates and owns every buffer.  The library keeps
+ * no pointer after a call returns and never allocates or frees caller memory.
+ * usw_fmt is a non-owning view.
+ *
+ * Errors: every entry point returns a usw_status; argument errors are
+ * reported before anything is written or launched.  Device faults surface at
+ * the next synchronisation of the stream, as for any HIP launch.  Nothing is
+ * printed and no exception crosses this interface.  All entry points are
+ * re-entrant; concurrent calls must not share output or workspace buffers.
+ */
+#ifndef USW_H
+#define USW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define USW_ABI_VERSION 1
+
+typedef int32_t usw_status;
+#define USW_OK 0
+#define USW_ERR_NULL_ARG (-1)     /* a required pointer is NULL */
+#define USW_ERR_BAD_SHAPE (-2)    /* M, K not positive multiples of gt_m, gt_k; gt_* not multiples of 16 */
+#define USW_ERR_BAD_DTYPE (-3)    /* unknown val_type or y_type */
+#define USW_ERR_BAD_N (-4)        /* N < 1 */
+#define USW_ERR_UNSUPPORTED (-5)  /* valid request with no kernel (e.g. GroupTile shape, INT4 with N > 32) */
+#define USW_ERR_MISALIGNED (-6)   /* a device pointer is not 16-byte aligned */
+#define USW_ERR_WORKSPACE (-7)    /* workspace NULL or smaller than usw_spmm_workspace() reports */
+#define USW_ERR_CORRUPT (-8)      /* usw_validate: offsets disagree with the bitmaps */
+#define USW_ERR_HIP (-9)          /* a HIP launch or query failed */
+#define USW_ERR_CAPACITY (-10)    /* an output buffer is smaller than required, or NNZ >= 2^32 */
+
+#define USW_VAL_F16 1             /* fp16 values */
+#define USW_VAL_I4 2              /* INT4 values + fp16 per-row scales */
+#define USW_OUT_F16 1             /* Y in fp16 */
+#define USW_OUT_F32 3             /* Y in fp32 */
+
+/* Non-owning view of one encoded matrix.  For usw_spmm every pointer is a
+ * device pointer; for usw_validate every pointer is a host pointer. */
+typedef struct usw_fmt {
+  int32_t M, K;             /* W is M x K */
+  int32_t gt_m, gt_k;       /* GroupTile shape */
+  int32_t val_type;         /* USW_VAL_F16 or USW_VAL_I4 */
+  int32_t reserved;         /* must be 0 */
+  int64_t nnz;              /* number of kept elements = offsets[NGT] */
+  const uint64_t* bitmaps;  /* [M*K/64] */
+  const uint32_t* offsets;  /* [NGT+1] */
+  const void* values;       /* F16: uint16 bits [NNZ]; I4: uint8 [ceil(NNZ/2)]; see usw_encode_query for padding */
+  const uint16_t* scales;   /* I4: fp16 bits [M]; F16: ignored (may be NULL) */
+} usw_fmt;
+
+/* Version of this interface (USW_ABI_VERSION). */
+int32_t usw_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* usw_status_str(usw_status s);
+
+/*
+ * Sizes of an encoding, computed from the mask alone (host memory).
+ *   W:    fp16 bits [M][K] row-major; read only when mask is NULL.
+ *   mask: uint8 [M][K] row-major, nonzero = kept; NULL means "kept where W is
+ *         nonzero in IEEE terms" (+0 and -0 dropped, NaN kept).
+ * Outputs (each may be NULL if not wanted):
+ *   nnz, and byte sizes of bitmaps (8*NBT), offsets (4*(NGT+1)), values
+ *   (logical: 2*NNZ for F16, ceil(NNZ/2) for I4), values_alloc (the size the
+ *   values buffer must have for usw_spmm: logical rounded up to a multiple of
+ *   16, at least 16; the kernels read whole 16-byte lines), scales (2*M for
+ *   I4, 0 for F16).
+ * Errors: NULL_ARG (W and mask both NULL), BAD_SHAPE, BAD_DTYPE, CAPACITY
+ * (NNZ does not fit the 32-bit offsets).
+ */
+usw_status usw_encode_query(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K,
+                            int32_t gt_m, int32_t gt_k, int32_t val_type, int64_t* nnz,
+                            size_t* bytes_bitmaps, size_t* bytes_offsets, size_t* bytes_values,
+                            size_t* bytes_values_alloc, size_t* bytes_scales);
+
+/*
+ * Encode W (host memory) into caller-allocated host buffers, following the
+ * TCA-BME construction above (blog section "How TCA-BME addresses the indexing
+ * overhead"; INT4 rule in the header comment).  The mask is authoritative: a
+ * kept exact zero sets its bit and stores its bit pattern.
+ *   W:      fp16 bits [M][K] (required).
+ *   mask:   uint8 [M][K] or NULL (see usw_encode_query).
+ *   bitmaps [NBT], offsets [NGT+1]: outputs.
+ *   values: output of values_capacity bytes (>= the logical size); bytes past
+ *           the logical size up to values_capacity are zeroed.
+ *   scales: output fp16 [M] for I4; ignored for F16.
+ * Deterministic: the same input always gives the same bytes.
+ * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, CAPACITY.
+ */
+usw_status usw_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t gt_m,
+                      int32_t gt_k, int32_t val_type, uint64_t* bitmaps, uint32_t* offsets, void* values,
+                      size_t values_capacity, uint16_t* scales);
+
+/*
+ * Check a host copy of an encoding: shape fields, offsets[0] = 0,
+ * non-decreasing offsets, offsets[NGT] = nnz, and each GroupTile's offset span
+ * equal to the popcount of its bitmaps.  Errors: NULL_ARG, BAD_SHAPE,
+ * BAD_DTYPE, CORRUPT.
+ */
+usw_status usw_validate(const usw_fmt* host_fmt);
+
+/*
+ * Workspace bytes usw_spmm needs for this matrix and N (0 when none).
+ * Errors: as usw_spmm's argument checks.
+ */
+usw_status usw_spmm_workspace(const usw_fmt* fmt, int32_t N, size_t* bytes);
+
+/*
+ * Y = W_sp . X on the GPU, for W_sp given by fmt (device pointers).
+ *   X:  device fp16 bits [N][K] row-major, 16-byte aligned.
+ *   Y:  device [N][M] row-major, fp16 (y_type USW_OUT_F16) or fp32
+ *       (USW_OUT_F32), 16-byte aligned; fully overwritten.
+ *   ws: device workspace of ws_bytes >= usw_spmm_workspace(fmt, N); may be
+ *       NULL when that size is 0.  Contents need not be initialised.
+ *   stream: a hipStream_t (NULL = the default stream).  The call only
+ *       enqueues work; it returns before the kernels finish.
+ * Accumulation is fp32 (each product of two fp16 values is exact in fp32);
+ * the result is deterministic: the same inputs give the same bits.
+ * Kernels: fp16 values with N <= 32 take the decode kernel, N > 32 the
+ * prefill (MFMA) kernel; INT4 values take the INT4 kernel (N <= 32).
+ * The values buffer must hold the padded size usw_encode_query reports.
+ * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_N, UNSUPPORTED, MISALIGNED,
+ * WORKSPACE, HIP.
+ */
+usw_status usw_spmm(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y_type, int32_t N, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * As usw_spmm_workspace / usw_spmm, with the split-K factor chosen by the
+ * caller: splits = workgroups that share one 64-row strip of GroupTiles,
+ * each summing a contiguous range of GroupTile columns (0 = automatic).
+ * A factor above 1 adds the partial sums in a second kernel, in split order,
+ * through the fp32 workspace.  The factor is clamped to [1, K/256].  Same
+ * errors as usw_spmm.  Meant for tuning and tests.
+ */
+usw_status usw_spmm_workspace_ex(const usw_fmt* fmt, int32_t N, int32_t splits, size_t* bytes);
+usw_status usw_spmm_ex(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y_type, int32_t N, int32_t splits,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* USW_H */

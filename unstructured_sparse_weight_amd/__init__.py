@@ -1,0 +1,181 @@
+"""Bitmap-encoded unstructured-sparse weight SpMM for AMD MI355X (gfx950).
+
+Thin Python binding over libusw.so (include/usw.h).  Every step of the SpMM
+runs in the library's HIP kernels; this module only marshals arguments,
+using PyTorch for device memory and the current stream.
+
+    enc = encode(W, mask)                 # host C++ encoder -> device tensors
+    y = spmm(enc, x)                      # x [N][K] fp16 on the GPU -> y [N][M]
+
+Format: TCA-BME (blog "SpInfer: How bitmaps make sparse LLMs actually fast",
+section "How TCA-BME addresses the indexing overhead"); see include/usw.h for
+the exact bit and tile orders.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from ._lib import (USW_OUT_F16, USW_OUT_F32, USW_VAL_F16, USW_VAL_I4, EXPORTED, UswError, UswFmt,  # noqa: F401
+                   check, lib)
+
+__all__ = ["HostEncoding", "Encoding", "encode_host", "encode", "to_device", "validate", "spmm",
+           "spmm_workspace_bytes", "UswError", "lib"]
+
+_VAL = {"f16": USW_VAL_F16, "i4": USW_VAL_I4}
+
+
+@dataclass
+class HostEncoding:
+    """Encoded matrix in host memory (numpy), as written by usw_encode."""
+    M: int
+    K: int
+    gt_m: int
+    gt_k: int
+    val_type: int
+    nnz: int
+    bitmaps: np.ndarray          # uint64 [NBT]
+    offsets: np.ndarray          # uint32 [NGT+1]
+    values: np.ndarray           # uint8, padded allocation (values_alloc bytes)
+    values_bytes: int            # logical byte count
+    scales: Optional[np.ndarray]  # uint16 fp16 bits [M] (INT4) or None
+
+    def fmt(self) -> UswFmt:
+        return UswFmt(self.M, self.K, self.gt_m, self.gt_k, self.val_type, 0, self.nnz,
+                      self.bitmaps.ctypes.data, self.offsets.ctypes.data, self.values.ctypes.data,
+                      self.scales.ctypes.data if self.scales is not None else None)
+
+
+@dataclass
+class Encoding:
+    """Encoded matrix on a GPU (torch tensors) plus its usw_fmt view."""
+    M: int
+    K: int
+    gt_m: int
+    gt_k: int
+    val_type: int
+    nnz: int
+    bitmaps: "object"
+    offsets: "object"
+    values: "object"
+    scales: "object"
+
+    def fmt(self) -> UswFmt:
+        return UswFmt(self.M, self.K, self.gt_m, self.gt_k, self.val_type, 0, self.nnz,
+                      self.bitmaps.data_ptr(), self.offsets.data_ptr(), self.values.data_ptr(),
+                      self.scales.data_ptr() if self.scales is not None else None)
+
+    @property
+    def device(self):
+        return self.bitmaps.device
+
+
+def _as_numpy_f16(W) -> np.ndarray:
+    if hasattr(W, "detach"):
+        W = W.detach().cpu().numpy()
+    W = np.ascontiguousarray(W)
+    if W.dtype != np.float16:
+        raise TypeError("W must be float16")
+    return W
+
+
+def encode_host(W, mask=None, gt=(64, 64), dtype: str = "f16") -> HostEncoding:
+    """Run usw_encode on host arrays. ``mask`` None keeps the IEEE nonzeros."""
+    W = _as_numpy_f16(W)
+    if W.ndim != 2:
+        raise ValueError("W must be 2-D")
+    M, K = W.shape
+    if mask is not None:
+        if hasattr(mask, "detach"):
+            mask = mask.detach().cpu().numpy()
+        mask = np.ascontiguousarray(mask.astype(np.uint8, copy=False))
+        if mask.shape != W.shape:
+            raise ValueError("mask shape must match W")
+    vt = _VAL[dtype]
+    L = lib()
+    nnz = ctypes.c_int64()
+    sz = [ctypes.c_size_t() for _ in range(5)]
+    wp = W.ctypes.data
+    mp = mask.ctypes.data if mask is not None else None
+    check(L.usw_encode_query(wp, mp, M, K, gt[0], gt[1], vt, ctypes.byref(nnz), *[ctypes.byref(s) for s in sz]),
+          "usw_encode_query")
+    b_bm, b_off, b_val, b_alloc, b_sc = (s.value for s in sz)
+    bitmaps = np.empty(b_bm // 8, dtype=np.uint64)
+    offsets = np.empty(b_off // 4, dtype=np.uint32)
+    values = np.empty(b_alloc, dtype=np.uint8)
+    scales = np.empty(M, dtype=np.uint16) if vt == USW_VAL_I4 else None
+    check(L.usw_encode(wp, mp, M, K, gt[0], gt[1], vt, bitmaps.ctypes.data, offsets.ctypes.data,
+                       values.ctypes.data, b_alloc, scales.ctypes.data if scales is not None else None),
+          "usw_encode")
+    return HostEncoding(M, K, gt[0], gt[1], vt, nnz.value, bitmaps, offsets, values, b_val, scales)
+
+
+def validate(enc: HostEncoding) -> None:
+    """usw_validate on a host encoding (raises UswError when corrupt)."""
+    f = enc.fmt()
+    check(lib().usw_validate(ctypes.byref(f)), "usw_validate")
+
+
+def to_device(enc: HostEncoding, device="cuda") -> Encoding:
+    import torch
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+    return Encoding(enc.M, enc.K, enc.gt_m, enc.gt_k, enc.val_type, enc.nnz,
+                    t(enc.bitmaps.view(np.int64)), t(enc.offsets.view(np.int32)), t(enc.values),
+                    t(enc.scales.view(np.int16)) if enc.scales is not None else None)
+
+
+def encode(W, mask=None, gt=(64, 64), dtype: str = "f16", device="cuda") -> Encoding:
+    """Encode on the host (usw_encode) and copy the buffers to ``device``."""
+    return to_device(encode_host(W, mask, gt, dtype), device)
+
+
+def spmm_workspace_bytes(enc: Encoding, N: int, splits: int = 0) -> int:
+    f = enc.fmt()
+    b = ctypes.c_size_t()
+    check(lib().usw_spmm_workspace_ex(ctypes.byref(f), int(N), int(splits), ctypes.byref(b)), "usw_spmm_workspace")
+    return b.value
+
+
+_WS = {}
+
+
+def _workspace(device, nbytes: int):
+    import torch
+    key = (str(device),)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+def spmm(enc: Encoding, x, y=None, out_dtype=None, splits: int = 0, stream=None):
+    """Y [N][M] = W_sp . X for x [N][K] fp16 on enc's device (usw_spmm_ex).
+
+    ``y`` (optional) must be a contiguous [N][M] fp16 or fp32 tensor.  The
+    launch goes on ``stream`` (default: torch's current stream).
+    """
+    import torch
+    if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != enc.K:
+        raise ValueError("x must be [N][K] float16")
+    if not x.is_contiguous():
+        x = x.contiguous()
+    N = x.shape[0]
+    if y is None:
+        y = torch.empty((N, enc.M), dtype=out_dtype or torch.float16, device=x.device)
+    if y.shape != (N, enc.M) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [N][M] tensor")
+    yt = {torch.float16: USW_OUT_F16, torch.float32: USW_OUT_F32}.get(y.dtype)
+    if yt is None:
+        raise ValueError("y must be float16 or float32")
+    f = enc.fmt()
+    nbytes = spmm_workspace_bytes(enc, N, splits)
+    ws = _workspace(x.device, nbytes) if nbytes else None
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    check(lib().usw_spmm_ex(ctypes.byref(f), x.data_ptr(), y.data_ptr(), yt, N, int(splits),
+                            ws.data_ptr() if ws is not None else None, nbytes, ctypes.c_void_p(st.cuda_stream)),
+          "usw_spmm")
+    return y

@@ -1,0 +1,313 @@
+// Host half of the usw library: status strings, encoding sizes, the TCA-BME
+// encoder (fp16 and INT4 values) and the format validator.
+//
+// Format: blog "SpInfer: How bitmaps make sparse LLMs actually fast", section
+// "How TCA-BME addresses the indexing overhead" (three-level tiling, Bitmap /
+// Values / GroupTile-offset arrays, storage equation).  The orders inside each
+// level are the row-major readings stated in include/usw.h.
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "usw.h"
+#include "usw_internal.h"
+
+namespace usw {
+
+usw_status make_geometry(int64_t M, int64_t K, int64_t gt_m, int64_t gt_k, Geometry* g) {
+  if (gt_m <= 0 || gt_k <= 0 || gt_m % 16 || gt_k % 16) return USW_ERR_BAD_SHAPE;
+  if (M <= 0 || K <= 0 || M % gt_m || K % gt_k) return USW_ERR_BAD_SHAPE;
+  if (M > (1 << 30) || K > (1 << 30)) return USW_ERR_BAD_SHAPE;
+  g->M = M;
+  g->K = K;
+  g->gt_m = gt_m;
+  g->gt_k = gt_k;
+  g->Gr = M / gt_m;
+  g->Gc = K / gt_k;
+  g->ngt = g->Gr * g->Gc;
+  g->Tr = gt_m / 16;
+  g->Tc = gt_k / 16;
+  g->bt_per_gt = g->Tr * g->Tc * 4;
+  g->nbt = M * K / 64;
+  return USW_OK;
+}
+
+// fp16 bits -> double (exact).
+double f16_to_f64(uint16_t h) {
+  const int sign = h >> 15;
+  const int e = (h >> 10) & 0x1F;
+  const int m = h & 0x3FF;
+  double v;
+  if (e == 0)
+    v = std::ldexp(static_cast<double>(m), -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = std::ldexp(static_cast<double>(1024 + m), e - 25);
+  return sign ? -v : v;
+}
+
+// double -> fp16 bits with a single round-to-nearest-even, from the IEEE
+// binary16 layout (1 sign, 5 exponent bits with bias 15, 10 fraction bits;
+// subnormal unit 2^-24; values at or above 65520 round to infinity).
+uint16_t f64_to_f16_rne(double x) {
+  uint64_t b;
+  std::memcpy(&b, &x, sizeof b);
+  const uint16_t sign = static_cast<uint16_t>((b >> 48) & 0x8000u);
+  const int exp = static_cast<int>((b >> 52) & 0x7FF);
+  const uint64_t frac = b & ((1ull << 52) - 1);
+  if (exp == 0x7FF) return sign | (frac ? 0x7E00 : 0x7C00);
+  if (exp == 0) return sign;  // fp64 subnormals are far below half the fp16 subnormal unit
+  const int e = exp - 1023;   // x = sig * 2^(e - 52), sig in [2^52, 2^53)
+  const uint64_t sig = frac | (1ull << 52);
+  int shift;                  // bits of sig dropped
+  if (e >= -14) {
+    shift = 42;               // keep 11 significant bits
+  } else {
+    shift = 28 - e;           // express in units of 2^-24
+    if (shift > 53) return sign;  // below 2^-25: rounds to zero
+  }
+  uint64_t r = sig >> shift;
+  const uint64_t rem = sig & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (r & 1))) ++r;
+  if (e >= -14) {
+    int ee = e;
+    if (r == 2048) {          // carried into the next binade
+      r = 1024;
+      ++ee;
+    }
+    if (ee > 15) return sign | 0x7C00;
+    return sign | static_cast<uint16_t>(((ee + 15) << 10) | (r & 0x3FF));
+  }
+  // subnormal result (r == 1024 is the smallest normal, encoded the same way)
+  return sign | static_cast<uint16_t>(r);
+}
+
+namespace {
+
+inline bool is_kept(const uint16_t* W, const uint8_t* mask, int64_t idx) {
+  if (mask) return mask[idx] != 0;
+  return (W[idx] & 0x7FFFu) != 0;  // +0 and -0 dropped; NaN and Inf kept
+}
+
+int worker_count(int64_t items) {
+  unsigned hw = std::thread::hardware_concurrency();
+  int n = static_cast<int>(hw ? std::min(hw, 16u) : 4u);
+  if (items < n) n = static_cast<int>(std::max<int64_t>(items, 1));
+  return n;
+}
+
+template <class F>
+void parallel_for(int64_t n, F&& f) {
+  const int nt = worker_count(n);
+  if (nt <= 1) {
+    f(static_cast<int64_t>(0), n);
+    return;
+  }
+  std::vector<std::thread> th;
+  th.reserve(nt);
+  for (int t = 0; t < nt; ++t) {
+    const int64_t lo = n * t / nt, hi = n * (t + 1) / nt;
+    th.emplace_back([&f, lo, hi] { f(lo, hi); });
+  }
+  for (auto& x : th) x.join();
+}
+
+// Visit the elements of GroupTile g in storage order: f(bt_index_in_matrix,
+// position, linear_index_in_W).
+template <class F>
+inline void for_each_in_group(const Geometry& g, int64_t gid, F&& f) {
+  const int64_t gi = gid / g.Gc, gj = gid % g.Gc;
+  for (int64_t t = 0; t < g.Tr * g.Tc; ++t) {
+    const int64_t ti = t / g.Tc, tj = t % g.Tc;
+    for (int b = 0; b < 4; ++b) {
+      const int64_t r0 = gi * g.gt_m + 16 * ti + 8 * (b >> 1);
+      const int64_t c0 = gj * g.gt_k + 16 * tj + 8 * (b & 1);
+      const int64_t bt = gid * g.bt_per_gt + 4 * t + b;
+      for (int p = 0; p < 64; ++p) f(bt, p, (r0 + (p >> 3)) * g.K + c0 + (p & 7));
+    }
+  }
+}
+
+usw_status count_groups(const Geometry& g, const uint16_t* W, const uint8_t* mask, std::vector<int64_t>* off) {
+  off->assign(g.ngt + 1, 0);
+  int64_t* o = off->data();
+  parallel_for(g.Gr, [&](int64_t lo, int64_t hi) {
+    for (int64_t gi = lo; gi < hi; ++gi)
+      for (int64_t gj = 0; gj < g.Gc; ++gj) {
+        int64_t c = 0;
+        for (int64_t r = gi * g.gt_m; r < (gi + 1) * g.gt_m; ++r)
+          for (int64_t k = gj * g.gt_k; k < (gj + 1) * g.gt_k; ++k) c += is_kept(W, mask, r * g.K + k);
+        o[gi * g.Gc + gj + 1] = c;
+      }
+  });
+  for (int64_t i = 0; i < g.ngt; ++i) o[i + 1] += o[i];
+  if (o[g.ngt] >= (int64_t(1) << 32)) return USW_ERR_CAPACITY;
+  return USW_OK;
+}
+
+size_t values_logical_bytes(int32_t val_type, int64_t nnz) {
+  return val_type == USW_VAL_F16 ? static_cast<size_t>(2 * nnz) : static_cast<size_t>((nnz + 1) / 2);
+}
+
+}  // namespace
+
+size_t values_alloc_bytes(int32_t val_type, int64_t nnz) {
+  size_t b = values_logical_bytes(val_type, nnz);
+  b = (b + 15) & ~size_t(15);
+  return b < 16 ? 16 : b;
+}
+
+}  // namespace usw
+
+using namespace usw;
+
+extern "C" {
+
+int32_t usw_abi_version(void) { return USW_ABI_VERSION; }
+
+const char* usw_status_str(usw_status s) {
+  switch (s) {
+    case USW_OK: return "ok";
+    case USW_ERR_NULL_ARG: return "a required pointer is NULL";
+    case USW_ERR_BAD_SHAPE: return "M, K must be positive multiples of gt_m, gt_k; gt_m, gt_k multiples of 16";
+    case USW_ERR_BAD_DTYPE: return "unknown value type or output type";
+    case USW_ERR_BAD_N: return "N must be at least 1";
+    case USW_ERR_UNSUPPORTED: return "no kernel for this request";
+    case USW_ERR_MISALIGNED: return "a device pointer is not 16-byte aligned";
+    case USW_ERR_WORKSPACE: return "workspace missing or too small";
+    case USW_ERR_CORRUPT: return "encoding is corrupt: offsets disagree with bitmaps";
+    case USW_ERR_HIP: return "HIP call failed";
+    case USW_ERR_CAPACITY: return "output buffer too small or NNZ does not fit 32 bits";
+    default: return "unknown status";
+  }
+}
+
+usw_status usw_encode_query(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t gt_m,
+                            int32_t gt_k, int32_t val_type, int64_t* nnz, size_t* bytes_bitmaps,
+                            size_t* bytes_offsets, size_t* bytes_values, size_t* bytes_values_alloc,
+                            size_t* bytes_scales) {
+  if (!W && !mask) return USW_ERR_NULL_ARG;
+  Geometry g;
+  usw_status st = make_geometry(M, K, gt_m, gt_k, &g);
+  if (st) return st;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  std::vector<int64_t> off;
+  st = count_groups(g, W, mask, &off);
+  if (st) return st;
+  const int64_t n = off[g.ngt];
+  if (nnz) *nnz = n;
+  if (bytes_bitmaps) *bytes_bitmaps = static_cast<size_t>(8 * g.nbt);
+  if (bytes_offsets) *bytes_offsets = static_cast<size_t>(4 * (g.ngt + 1));
+  if (bytes_values) *bytes_values = val_type == USW_VAL_F16 ? static_cast<size_t>(2 * n) : static_cast<size_t>((n + 1) / 2);
+  if (bytes_values_alloc) *bytes_values_alloc = values_alloc_bytes(val_type, n);
+  if (bytes_scales) *bytes_scales = val_type == USW_VAL_I4 ? static_cast<size_t>(2 * M) : 0;
+  return USW_OK;
+}
+
+usw_status usw_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t gt_m, int32_t gt_k,
+                      int32_t val_type, uint64_t* bitmaps, uint32_t* offsets, void* values, size_t values_capacity,
+                      uint16_t* scales) {
+  if (!W || !bitmaps || !offsets || !values) return USW_ERR_NULL_ARG;
+  Geometry g;
+  usw_status st = make_geometry(M, K, gt_m, gt_k, &g);
+  if (st) return st;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (val_type == USW_VAL_I4 && !scales) return USW_ERR_NULL_ARG;
+  std::vector<int64_t> off;
+  st = count_groups(g, W, mask, &off);
+  if (st) return st;
+  const int64_t nnz = off[g.ngt];
+  const size_t logical = val_type == USW_VAL_F16 ? static_cast<size_t>(2 * nnz) : static_cast<size_t>((nnz + 1) / 2);
+  if (values_capacity < logical) return USW_ERR_CAPACITY;
+
+  for (int64_t i = 0; i <= g.ngt; ++i) offsets[i] = static_cast<uint32_t>(off[i]);
+
+  // INT4: per-row scale over the kept entries, in fp64.
+  std::vector<double> rscale;
+  if (val_type == USW_VAL_I4) {
+    rscale.assign(M, 0.0);
+    parallel_for(M, [&](int64_t lo, int64_t hi) {
+      for (int64_t m = lo; m < hi; ++m) {
+        double amax = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+          if (is_kept(W, mask, m * K + k)) amax = std::max(amax, std::fabs(f16_to_f64(W[m * K + k])));
+        const uint16_t s = f64_to_f16_rne(amax / 7.0);
+        scales[m] = s;
+        rscale[m] = f16_to_f64(s);
+      }
+    });
+  }
+
+  std::vector<int8_t> q;  // INT4 codes in storage order, packed afterwards
+  if (val_type == USW_VAL_I4) q.assign(static_cast<size_t>(nnz), 0);
+  uint16_t* v16 = static_cast<uint16_t*>(values);
+
+  parallel_for(g.ngt, [&](int64_t lo, int64_t hi) {
+    for (int64_t gid = lo; gid < hi; ++gid) {
+      int64_t idx = off[gid];
+      uint64_t bm = 0;
+      int64_t cur_bt = -1;
+      for_each_in_group(g, gid, [&](int64_t bt, int p, int64_t lin) {
+        if (bt != cur_bt) {
+          if (cur_bt >= 0) bitmaps[cur_bt] = bm;
+          cur_bt = bt;
+          bm = 0;
+        }
+        if (!is_kept(W, mask, lin)) return;
+        bm |= 1ull << p;
+        if (val_type == USW_VAL_F16) {
+          v16[idx] = W[lin];
+        } else {
+          const double s = rscale[lin / g.K];
+          double code = 0.0;
+          if (s > 0.0) code = std::min(7.0, std::max(-8.0, std::nearbyint(f16_to_f64(W[lin]) / s)));
+          q[static_cast<size_t>(idx)] = static_cast<int8_t>(code);
+        }
+        ++idx;
+      });
+      if (cur_bt >= 0) bitmaps[cur_bt] = bm;
+    }
+  });
+
+  uint8_t* vb = static_cast<uint8_t*>(values);
+  if (val_type == USW_VAL_I4) {
+    const int64_t nbytes = (nnz + 1) / 2;
+    parallel_for(nbytes, [&](int64_t lo, int64_t hi) {
+      for (int64_t i = lo; i < hi; ++i) {
+        const uint8_t a = static_cast<uint8_t>(q[2 * i]) & 0xF;
+        const uint8_t b = (2 * i + 1 < nnz) ? (static_cast<uint8_t>(q[2 * i + 1]) & 0xF) : 0;
+        vb[i] = static_cast<uint8_t>(a | (b << 4));
+      }
+    });
+  }
+  if (values_capacity > logical) std::memset(vb + logical, 0, values_capacity - logical);
+  return USW_OK;
+}
+
+usw_status usw_validate(const usw_fmt* f) {
+  if (!f) return USW_ERR_NULL_ARG;
+  Geometry g;
+  usw_status st = make_geometry(f->M, f->K, f->gt_m, f->gt_k, &g);
+  if (st) return st;
+  if (f->val_type != USW_VAL_F16 && f->val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (!f->bitmaps || !f->offsets) return USW_ERR_NULL_ARG;
+  if (f->nnz > 0 && !f->values) return USW_ERR_NULL_ARG;
+  if (f->val_type == USW_VAL_I4 && !f->scales) return USW_ERR_NULL_ARG;
+  if (f->reserved != 0) return USW_ERR_BAD_SHAPE;
+  if (f->nnz < 0 || f->nnz >= (int64_t(1) << 32)) return USW_ERR_CORRUPT;
+  if (f->offsets[0] != 0 || static_cast<int64_t>(f->offsets[g.ngt]) != f->nnz) return USW_ERR_CORRUPT;
+  for (int64_t gid = 0; gid < g.ngt; ++gid) {
+    if (f->offsets[gid + 1] < f->offsets[gid]) return USW_ERR_CORRUPT;
+    int64_t c = 0;
+    for (int64_t b = 0; b < g.bt_per_gt; ++b) c += __builtin_popcountll(f->bitmaps[gid * g.bt_per_gt + b]);
+    if (c != static_cast<int64_t>(f->offsets[gid + 1] - f->offsets[gid])) return USW_ERR_CORRUPT;
+  }
+  return USW_OK;
+}
+
+}  // extern "C"

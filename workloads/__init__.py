@@ -23,6 +23,7 @@ __all__ = [
     "seed_rng",
     "weight_normal",
     "weight_dyadic",
+    "weight_int4_exact",
     "activations_normal",
     "activations_small_int",
     "mask_bernoulli",
@@ -72,6 +73,22 @@ def weight_dyadic(M: int, K: int, rng: np.random.Generator) -> np.ndarray:
     in fp32, so any summation order gives the same bits.
     """
     return (rng.integers(-16, 17, size=(M, K)).astype(np.float64) / 8.0).astype(np.float16)
+
+
+def weight_int4_exact(M: int, K: int, rng: np.random.Generator, mask: np.ndarray) -> np.ndarray:
+    """fp16 weight whose per-row INT4 quantisation is exact.
+
+    Row m holds q * 2^e_m with integer q in [-7, 7] and one kept entry equal
+    to +-7 * 2^e_m, so the row's largest kept magnitude over 7 is the power of
+    two 2^e_m and every kept entry is an exact multiple of it.
+    """
+    e = rng.integers(-9, -3, size=M)
+    q = rng.integers(-7, 8, size=(M, K)).astype(np.float64)
+    for m in range(M):
+        kept = np.flatnonzero(mask[m])
+        if kept.size:
+            q[m, kept[rng.integers(kept.size)]] = 7.0 * (1 if rng.random() < 0.5 else -1)
+    return (q * np.exp2(e)[:, None]).astype(np.float16)
 
 
 def activations_normal(N: int, K: int, rng: np.random.Generator) -> np.ndarray:
