@@ -106,9 +106,9 @@ const char* usw_status_str(usw_status s);
  * Outputs (each may be NULL if not wanted):
  *   nnz, and byte sizes of bitmaps (8*NBT), offsets (4*(NGT+1)), values
  *   (logical: 2*NNZ for F16, ceil(NNZ/2) for I4), values_alloc (the size the
- *   values buffer must have for usw_spmm: logical rounded up to a multiple of
- *   16, at least 16; the kernels read whole 16-byte lines), scales (2*M for
- *   I4, 0 for F16).
+ *   values buffer must have for usw_spmm: the logical size rounded down to a
+ *   multiple of 16, plus 16; the kernels read whole 16-byte chunks), scales
+ *   (2*M for I4, 0 for F16).
  * Errors: NULL_ARG (W and mask both NULL), BAD_SHAPE, BAD_DTYPE, CAPACITY
  * (NNZ does not fit the 32-bit offsets).
  */

@@ -156,10 +156,11 @@ size_t values_logical_bytes(int32_t val_type, int64_t nnz) {
 
 }  // namespace
 
+// The kernels read whole 16-byte chunks starting at the chunk that holds a
+// GroupTile's first value, even for an empty GroupTile at the very end, so
+// the allocation extends to the next 16-byte boundary strictly past the data.
 size_t values_alloc_bytes(int32_t val_type, int64_t nnz) {
-  size_t b = values_logical_bytes(val_type, nnz);
-  b = (b + 15) & ~size_t(15);
-  return b < 16 ? 16 : b;
+  return (values_logical_bytes(val_type, nnz) & ~size_t(15)) + 16;
 }
 
 }  // namespace usw
