@@ -96,7 +96,7 @@ def main():
     L = usw.lib()
     fmts = [e.fmt() for e in encs]
     wsb = usw.spmm_workspace_bytes(encs[0], N, args.splits)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=dev)   # counter region starts at zero
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
 

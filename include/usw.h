@@ -144,7 +144,13 @@ usw_status usw_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t
 usw_status usw_validate(const usw_fmt* host_fmt);
 
 /*
- * Workspace bytes usw_spmm needs for this matrix and N (0 when none).
+ * Workspace bytes usw_spmm needs for this matrix and N (0 when none).  The
+ * workspace starts with one 32-bit counter per 64-row strip of GroupTiles
+ * (the first ceil(4 * M / 64 / 256) * 256 bytes), followed by the fp32
+ * partial sums of the split-K workgroups.  Those counter bytes must be zero
+ * when a call starts: allocate the workspace zero-filled; every call leaves
+ * them zero again.  A workspace last used with a different M (whose partial
+ * sums may cover them) must have them zeroed first.
  * Errors: as usw_spmm's argument checks.
  */
 usw_status usw_spmm_workspace(const usw_fmt* fmt, int32_t N, size_t* bytes);
@@ -173,9 +179,11 @@ usw_status usw_spmm(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y_ty
  * As usw_spmm_workspace / usw_spmm, with the split-K factor chosen by the
  * caller: splits = workgroups that share one 64-row strip of GroupTiles,
  * each summing a contiguous range of GroupTile columns (0 = automatic).
- * A factor above 1 adds the partial sums in a second kernel, in split order,
- * through the fp32 workspace.  The factor is clamped to [1, K/256].  Same
- * errors as usw_spmm.  Meant for tuning and tests.
+ * With a factor above 1 each workgroup writes fp32 partial sums to the
+ * workspace and the last workgroup of a strip to finish adds them in split
+ * order, so results do not depend on scheduling.  The factor is clamped to
+ * [ceil(K / (64 * 4 * 63)), max(1, K / 256)].  Same errors as usw_spmm.
+ * Meant for tuning and tests.
  */
 usw_status usw_spmm_workspace_ex(const usw_fmt* fmt, int32_t N, int32_t splits, size_t* bytes);
 usw_status usw_spmm_ex(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y_type, int32_t N, int32_t splits,

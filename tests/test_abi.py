@@ -166,15 +166,15 @@ def test_argument_errors_return_before_launch():
     assert L.usw_spmm_workspace(B(fmt_of(h, val_type=7)), 8, B(sz)) == -3
     assert L.usw_spmm_workspace(B(fmt_of(h, gt_m=32, M=256)), 8, B(sz)) == -5
     assert L.usw_spmm_workspace(B(fmt_of(h, val_type=2, scales=h.bitmaps.ctypes.data)), 33, B(sz)) == -5
-    # forced split-K needs a workspace of splits * 16 * M fp32 (N <= 16); the
-    # factor is clamped to K/256 (tiny: 1, no workspace)
+    # forced split-K needs 256 B of strip counters plus splits * 16 * M fp32
+    # partial sums (N <= 16); the factor is clamped to K/256 (tiny: 1, none)
     assert L.usw_spmm_workspace_ex(B(f), 8, 1, B(sz)) == 0 and sz.value == 0
     assert L.usw_spmm_workspace_ex(B(f), 8, 2, B(sz)) == 0 and sz.value == 0
     Ww = wl.weight_normal(64, 512, np.random.default_rng(3))
     hw = usw.encode_host(Ww, None)
     fw = hw.fmt()
-    assert L.usw_spmm_workspace_ex(B(fw), 8, 2, B(sz)) == 0 and sz.value == 2 * 16 * 64 * 4
-    assert L.usw_spmm_workspace_ex(B(fw), 20, 9, B(sz)) == 0 and sz.value == 2 * 32 * 64 * 4
+    assert L.usw_spmm_workspace_ex(B(fw), 8, 2, B(sz)) == 0 and sz.value == 256 + 2 * 16 * 64 * 4
+    assert L.usw_spmm_workspace_ex(B(fw), 20, 9, B(sz)) == 0 and sz.value == 256 + 2 * 32 * 64 * 4
     # spmm argument checks (host pointers: any launch would fail)
     x = np.zeros((8, 256), np.uint16)
     y = np.zeros((8, 256), np.uint16)

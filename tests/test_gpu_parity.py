@@ -87,7 +87,7 @@ def test_ragged_n(N):
     assert_parity(Y, Yref, Bnd, f"ragged N={N}")
 
 
-@pytest.mark.parametrize("shape", [(64, 64), (64, 1024), (1024, 64), (192, 320), (128, 4096)])
+@pytest.mark.parametrize("shape", [(64, 64), (64, 1024), (1024, 64), (192, 320), (128, 4096), (64, 32768)])
 @pytest.mark.parametrize("dtype", ["f16", "i4"])
 def test_shapes(shape, dtype):
     M, K = shape
@@ -136,6 +136,69 @@ def test_kept_zeros_and_negative_zero():
     Y = run_gpu(W, mask, X)
     Yref, Bnd = oracle_ref(W, mask, X)
     assert_parity(Y, Yref, Bnd, "kept zeros")
+
+
+@pytest.mark.parametrize("density", [0.8, 0.97])
+@pytest.mark.parametrize("splits", [0, 1, 2])
+def test_dense_groups(density, splits):
+    """GroupTiles denser than a pipeline slot holds are staged in halves."""
+    rng = np.random.default_rng(int(density * 100) + splits)
+    M, K, N = 512, 2048, 16
+    W = wl.weight_normal(M, K, rng)
+    mask = wl.mask_bernoulli(M, K, density, rng)
+    X = wl.activations_normal(N, K, rng)
+    h = usw.encode_host(W, mask)
+    Y = run_gpu(W, mask, X, splits=splits, host=h)
+    Yref, Bnd = oracle_ref(W, mask, X)
+    assert_parity(Y, Yref, Bnd, f"density {density} splits={splits}")
+
+
+def test_split_k_counters_reset_across_calls():
+    """Repeated split-K calls on one workspace (per-strip counters, XCD remap
+    with 8 | workgroups) give identical bits every time."""
+    rng = np.random.default_rng(78)
+    M, K, N = 1024, 3072, 16      # 16 strips x 4 splits = 64 workgroups
+    W = wl.weight_normal(M, K, rng)
+    mask = wl.mask_bernoulli(M, K, 0.5, rng)
+    X = wl.activations_normal(N, K, rng)
+    enc = usw.to_device(usw.encode_host(W, mask), DEV)
+    x = torch.from_numpy(X).to(DEV)
+    outs = [usw.spmm(enc, x, splits=4).float().cpu().numpy() for _ in range(5)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    Yref, Bnd = oracle_ref(W, mask, X)
+    assert_parity(outs[0].astype(np.float64), Yref, Bnd, "split-K repeated")
+
+
+def test_workspace_reuse_across_shapes():
+    """Through the C ABI: one zero-filled workspace serves a small-M then a
+    larger-M matrix once the counter bytes the header names are re-zeroed,
+    and two calls in a row on the same matrix need nothing in between."""
+    import ctypes
+    L = usw.lib()
+    K, N = 3072, 16
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for M in (512, 2048, 2048):
+        rng = np.random.default_rng(M)
+        W = wl.weight_normal(M, K, rng)
+        mask = wl.mask_bernoulli(M, K, 0.5, rng)
+        X = wl.activations_normal(N, K, rng)
+        enc = usw.to_device(usw.encode_host(W, mask), DEV)
+        f = enc.fmt()
+        x = torch.from_numpy(X).to(DEV)
+        y = torch.empty((N, M), dtype=torch.float16, device=DEV)
+        need = usw.spmm_workspace_bytes(enc, N, 4)
+        assert 0 < need <= ws.numel()
+        st = L.usw_spmm_ex(ctypes.byref(f), x.data_ptr(), y.data_ptr(), 1, N, 4, ws.data_ptr(), ws.numel(), stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        counter_bytes = (4 * (M // 64) + 255) // 256 * 256
+        assert not ws[:counter_bytes].any()          # the call left its counters at zero
+        Yref, Bnd = oracle_ref(W, mask, X)
+        assert_parity(y.float().cpu().numpy().astype(np.float64), Yref, Bnd, f"workspace reuse M={M}")
+        ws[:counter_bytes * 4].zero_()               # next shape may have larger counters
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 5])

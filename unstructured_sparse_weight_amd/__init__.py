@@ -142,12 +142,18 @@ def spmm_workspace_bytes(enc: Encoding, N: int, splits: int = 0) -> int:
 _WS = {}
 
 
-def _workspace(device, nbytes: int):
+def _workspace(device, M: int, nbytes: int):
+    """Zero-filled workspace per (device, M).  The first bytes of a workspace
+    hold per-strip counters whose extent depends on M; the library leaves them
+    at zero after each call, but another shape's partial sums could land
+    there, so shapes with different M never share a buffer.  Calls on one
+    device are ordered on the stream they are issued to; do not overlap calls
+    on different streams."""
     import torch
-    key = (str(device),)
+    key = (str(device), int(M))
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS[key] = buf
     return buf
 
@@ -173,7 +179,7 @@ def spmm(enc: Encoding, x, y=None, out_dtype=None, splits: int = 0, stream=None)
         raise ValueError("y must be float16 or float32")
     f = enc.fmt()
     nbytes = spmm_workspace_bytes(enc, N, splits)
-    ws = _workspace(x.device, nbytes) if nbytes else None
+    ws = _workspace(x.device, enc.M, nbytes) if nbytes else None
     st = stream if stream is not None else torch.cuda.current_stream(x.device)
     check(lib().usw_spmm_ex(ctypes.byref(f), x.data_ptr(), y.data_ptr(), yt, N, int(splits),
                             ws.data_ptr() if ws is not None else None, nbytes, ctypes.c_void_p(st.cuda_stream)),

@@ -37,11 +37,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP toolchain is required to build libusw")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libusw.so next to this file; returns its path."""
+def build(verbose: bool = False, tuning: bool = False) -> str:
+    """Compile every source into libusw.so next to this file; returns its path.
+
+    ``tuning`` also compiles the alternative decode launch configurations,
+    selected at run time by the USW_DECODE_CFG environment variable.
+    """
     srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    extra = ["-DUSW_TUNING"] if tuning else []
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,4 +58,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, tuning="--tuning" in sys.argv[1:]))

@@ -49,28 +49,33 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGT = 64;                   // GroupTile side the kernels are built for
 constexpr int kBtPerGt = 64;              // BitmapTiles per 64x64 GroupTile
-constexpr int kWaves = 4;                 // waves per workgroup
-constexpr int kThreads = 64 * kWaves;
 
 // Per-value-type constants.  Every one of a GroupTile's kChunks*64 16-byte
 // chunk slots is loaded and stored unconditionally (slots past the
-// GroupTile's last chunk repeat that chunk), so the loads carry no branches
-// and the compiler can wait for exactly the GroupTile being consumed.
+// Per-value-type constants.  Every one of a slot's kChunks*64 16-byte chunk
+// loads is issued unconditionally (chunks past the GroupTile's last one
+// repeat it), so the loads carry no branches and the compiler waits for
+// exactly the slot being consumed.
 template <bool I4>
 struct ValTraits;
 template <>
 struct ValTraits<false> {
-  static constexpr int kChunks = 6;       // 16-byte chunks per lane kept in flight (6 KB per GroupTile)
-  // A dense GroupTile is 8192 B of values; the buffer adds the <16 B head
-  // before the first value and the <16 B a window reads past the last one.
-  static constexpr int kVbuf = 8192 + 64;
+  static constexpr int kChunks = 6;        // 6 KB of values per slot (density up to ~74%)
+  // LDS value buffer per wave: one slot plus the <16 B a window reads past
+  // the last value.  Denser GroupTiles are staged in two halves of two TCTile
+  // rows each (<= 4 KB + head).
+  static constexpr int kVbuf = 6 * 1024 + 64;
+  static constexpr uint32_t kFastLimit = (16u * 64u * kChunks - 32u) / 2u;   // values per GroupTile
 };
 template <>
 struct ValTraits<true> {
-  static constexpr int kChunks = 3;       // covers every GroupTile (<= 2064 B)
+  static constexpr int kChunks = 3;        // every INT4 GroupTile fits (<= 2 KB + head)
   static constexpr int kVbuf = 3 * 1024 + 64;
+  static constexpr uint32_t kFastLimit = 4096u;
 };
 static_assert(ValTraits<false>::kVbuf >= 1024 * ValTraits<false>::kChunks, "unconditional stores fit");
+static_assert(ValTraits<false>::kVbuf >= 16 * 257 + 16, "a half GroupTile fits");
+static_assert(ValTraits<true>::kVbuf >= 1024 * ValTraits<true>::kChunks, "unconditional stores fit");
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -91,10 +96,23 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   return v;
 }
 
+// Maximum over the 64 lanes (DPP), returned in every lane.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false)));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // v_perm_b32 byte selectors that expand the packed fp16 values of one 4-bit
-// nibble of a BitmapTile row into 4 slots.  Packed value k of the window
-// occupies bytes 2k, 2k+1 (window dword 0 = selector bytes 0-3, dword 1 =
-// bytes 4-7); a clear bit selects 0x0C, which v_perm turns into 0x00.
+// nibble of a BitmapTile row into 4 slots (two output dwords, j = 0, 1).
+// Packed value k of the window occupies bytes 2k, 2k+1 (window dword 0 =
+// selector bytes 0-3, dword 1 = bytes 4-7); a clear bit selects 0x0C, which
+// v_perm turns into 0x00.  16 entries of 8 bytes: the table's 32 dwords sit
+// in distinct LDS banks, so any pattern of lookups is conflict-free.
 __device__ __forceinline__ uint32_t nibble_selector(uint32_t q, int j) {
   uint32_t sel = 0;
   for (int h = 0; h < 2; ++h) {
@@ -109,20 +127,20 @@ __device__ __forceinline__ uint32_t nibble_selector(uint32_t q, int j) {
   return sel;
 }
 
-// v_perm selectors that expand the 8 packed nibbles of one BitmapTile row
-// into 8 byte slots.  Packed nibble k sits in byte k/2 of lo4 (k even) or of
-// hi4 (k odd), lo4 = w & 0x0F0F0F0F and hi4 = (w >> 4) & 0x0F0F0F0F, and
-// v_perm(hi4, lo4, sel) numbers lo4's bytes 0-3 and hi4's bytes 4-7.
-__device__ __forceinline__ uint32_t nibble_byte_selector(uint32_t b, int half) {
+// v_perm selectors that expand the packed nibbles of one 4-bit nibble of a
+// BitmapTile row into 4 byte slots.  Packed nibble k of an 8-nibble window w
+// sits in byte k/2 of lo4 (k even) or of hi4 (k odd), lo4 = w & 0x0F0F0F0F and
+// hi4 = (w >> 4) & 0x0F0F0F0F, and v_perm(hi4, lo4, sel) numbers lo4's bytes
+// 0-3 and hi4's bytes 4-7.
+__device__ __forceinline__ uint32_t nibble_byte_selector(uint32_t q) {
   uint32_t sel = 0;
-  for (int s = 0; s < 4; ++s) {
-    const int p = 4 * half + s;
+  for (int p = 0; p < 4; ++p) {
     uint32_t v = 0x0Cu;
-    if ((b >> p) & 1u) {
-      const uint32_t k = __builtin_popcount(b & ((1u << p) - 1u));
+    if ((q >> p) & 1u) {
+      const uint32_t k = __builtin_popcount(q & ((1u << p) - 1u));
       v = (k & 1u) ? 4u + (k >> 1) : (k >> 1);
     }
-    sel |= v << (8 * s);
+    sel |= v << (8 * p);
   }
   return sel;
 }
@@ -139,33 +157,46 @@ __device__ __forceinline__ u32x2_t lds_window_f16(const uint8_t* buf, uint32_t e
   return w;
 }
 
-// The 8 dense fp16 slots (one BitmapTile row) of a lane's A fragment.
+// 8 packed nibbles starting at nibble e of an LDS buffer, split into the
+// even (lo4) and odd (hi4) nibbles, one per byte.
+__device__ __forceinline__ u32x2_t lds_window_i4(const uint8_t* buf, uint32_t e) {
+  const uint32_t ba = e >> 1;
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(buf + (ba & ~3u));
+  const uint32_t sh = ((ba & 3u) << 3) | ((e & 1u) << 2);
+  const uint32_t win = __builtin_amdgcn_alignbit(p[1], p[0], sh);
+  u32x2_t r;
+  r.x = win & 0x0F0F0F0Fu;
+  r.y = (win >> 4) & 0x0F0F0F0Fu;
+  return r;
+}
+
+// The 8 dense fp16 slots (one BitmapTile row) of a lane's A fragment: the
+// row's kept values start at element rb of the LDS buffer; `byte` is the
+// row's mask.  Slots 0-3 come from a window at rb, slots 4-7 from a window
+// at rb + popcount(low nibble).
 template <bool I4>
 __device__ __forceinline__ half8_t rebuild_row(const uint8_t* vb, const uint32_t* lut, uint32_t rb, uint32_t byte) {
+  const uint32_t pcl = __builtin_popcount(byte & 0xFu);
   if constexpr (!I4) {
-    const u32x4_t sel = reinterpret_cast<const u32x4_t*>(lut)[byte];
-    const uint32_t pcl = __builtin_popcount(byte & 0xFu);
+    const u32x2_t slo = reinterpret_cast<const u32x2_t*>(lut)[byte & 0xFu];
+    const u32x2_t shi = reinterpret_cast<const u32x2_t*>(lut)[byte >> 4];
     const u32x2_t lo = lds_window_f16(vb, rb);
     const u32x2_t hi = lds_window_f16(vb, rb + pcl);
     u32x4_t a;
-    a.x = __builtin_amdgcn_perm(lo.y, lo.x, sel.x);
-    a.y = __builtin_amdgcn_perm(lo.y, lo.x, sel.y);
-    a.z = __builtin_amdgcn_perm(hi.y, hi.x, sel.z);
-    a.w = __builtin_amdgcn_perm(hi.y, hi.x, sel.w);
+    a.x = __builtin_amdgcn_perm(lo.y, lo.x, slo.x);
+    a.y = __builtin_amdgcn_perm(lo.y, lo.x, slo.y);
+    a.z = __builtin_amdgcn_perm(hi.y, hi.x, shi.x);
+    a.w = __builtin_amdgcn_perm(hi.y, hi.x, shi.y);
     return __builtin_bit_cast(half8_t, a);
   } else {
-    const u32x2_t sel = reinterpret_cast<const u32x2_t*>(lut)[byte];
-    // 8 packed nibbles starting at nibble rb.
-    const uint32_t ba = rb >> 1;
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(vb + (ba & ~3u));
-    const uint32_t sh = ((ba & 3u) << 3) | ((rb & 1u) << 2);
-    const uint32_t win = __builtin_amdgcn_alignbit(p[1], p[0], sh);
-    const uint32_t lo4 = win & 0x0F0F0F0Fu;
-    const uint32_t hi4 = (win >> 4) & 0x0F0F0F0Fu;
+    const uint32_t slo = lut[byte & 0xFu];
+    const uint32_t shi = lut[byte >> 4];
+    const u32x2_t lo = lds_window_i4(vb, rb);
+    const u32x2_t hi = lds_window_i4(vb, rb + pcl);
     // Slots as bytes; xor 8 maps the two's-complement nibble q to q + 8 in
     // [0, 15] (an empty slot's 0 becomes 8, i.e. q = 0).
-    const uint32_t e0 = __builtin_amdgcn_perm(hi4, lo4, sel.x) ^ 0x08080808u;
-    const uint32_t e1 = __builtin_amdgcn_perm(hi4, lo4, sel.y) ^ 0x08080808u;
+    const uint32_t e0 = __builtin_amdgcn_perm(lo.y, lo.x, slo) ^ 0x08080808u;
+    const uint32_t e1 = __builtin_amdgcn_perm(hi.y, hi.x, shi) ^ 0x08080808u;
     // fp16 bit pattern 0x6400 | u is 1024 + u exactly; subtracting 1032
     // leaves q exactly.
     u32x4_t a;
@@ -178,6 +209,7 @@ __device__ __forceinline__ half8_t rebuild_row(const uint8_t* vb, const uint32_t
     return h;
   }
 }
+
 
 // Registers holding one GroupTile's loads until they are copied into LDS.
 template <int NB, bool I4>
@@ -197,33 +229,47 @@ struct Args {
   const uint16_t* __restrict__ scales;
   const uint16_t* __restrict__ X;
   void* __restrict__ Y;
-  float* __restrict__ ws;
-  uint64_t values_alloc;   // padded size of the values buffer in bytes (>= 16)
+  float* __restrict__ part;       // split-K partial sums [splits][N][M] (splits > 1)
+  uint32_t* __restrict__ counters;  // per 64-row strip: workgroups done (splits > 1), kept at 0 between calls
+  uint64_t values_alloc;           // padded size of the values buffer in bytes (>= 16)
   int M, K, N, Gc, splits;
+  int remap;                       // 1: keep the splits of a strip on one XCD
 };
 
+// Byte offset of the 16-byte chunk holding value element e (fp16: 2 B per
+// element; INT4: 4 bits per element).
+template <bool I4>
+__device__ __forceinline__ uint64_t chunk_start(uint32_t e) {
+  return I4 ? ((static_cast<uint64_t>(e) >> 1) & ~15ull) : ((2ull * e) & ~15ull);
+}
+
+// Elements of the first chunk that precede element e.
+template <bool I4>
+__device__ __forceinline__ uint32_t chunk_delta(uint32_t e, uint64_t a0) {
+  return I4 ? static_cast<uint32_t>(e - 2 * a0) : static_cast<uint32_t>((2ull * e - a0) >> 1);
+}
+
+// 16-byte chunks spanned by elements [e0, e1) counted from a0.
+template <bool I4>
+__device__ __forceinline__ uint32_t chunk_count(uint32_t e1, uint64_t a0) {
+  const uint64_t end = I4 ? ((static_cast<uint64_t>(e1) + 1) >> 1) : 2ull * e1;   // first byte past the values
+  return static_cast<uint32_t>((end - a0 + 15ull) >> 4);
+}
+
+// Issue the loads of GroupTile c of strip gi, whose values occupy elements
+// [o0, o1) of the stream.
 template <int NB, bool I4>
-__device__ __forceinline__ void slot_load(Slot<NB, I4>& s, const Args& a, int gi, int c, int lane) {
+__device__ __forceinline__ void slot_load(Slot<NB, I4>& s, const Args& a, int gi, int c, int lane, uint32_t o0,
+                                          uint32_t o1) {
   const int64_t g = static_cast<int64_t>(gi) * a.Gc + c;
-  const uint32_t o0 = a.offsets[g];
-  const uint32_t o1 = a.offsets[g + 1];
-  if constexpr (!I4) {
-    s.a0 = (2ull * o0) & ~15ull;
-    s.nch = static_cast<uint32_t>((2ull * o1 - s.a0 + 15ull) >> 4);
-    s.delta = static_cast<uint32_t>((2ull * o0 - s.a0) >> 1);
-  } else {
-    s.a0 = (static_cast<uint64_t>(o0) >> 1) & ~15ull;
-    const uint64_t bend = (static_cast<uint64_t>(o1) + 1) >> 1;   // first byte past the last nibble
-    s.nch = static_cast<uint32_t>((bend - s.a0 + 15ull) >> 4);
-    s.delta = static_cast<uint32_t>(o0 - 2 * s.a0);
-  }
-  // Chunk slots past the last chunk reload it (chunk 0 of an empty
-  // GroupTile lies inside the padded allocation).  The clamps keep every
-  // load inside the buffer and every store inside the LDS slot even for
-  // offsets that disagree with the bitmaps.
+  // The clamps keep every load inside the padded allocation and every store
+  // inside the LDS buffer even for offsets that disagree with the bitmaps.
   const uint64_t top = a.values_alloc - 16;
-  s.a0 = min(s.a0, top);
-  s.nch = min(s.nch, static_cast<uint32_t>((ValTraits<I4>::kVbuf - 16) / 16));
+  s.a0 = min(chunk_start<I4>(o0), top);
+  s.delta = chunk_delta<I4>(o0, s.a0);
+  s.nch = min(chunk_count<I4>(o1, s.a0), static_cast<uint32_t>((ValTraits<I4>::kVbuf - 16) / 16));
+  // Chunk slots past the last chunk reload it (chunk 0 of an empty
+  // GroupTile lies inside the padded allocation).
   const uint32_t last = min(s.nch > 0 ? s.nch - 1 : 0u, static_cast<uint32_t>((top - s.a0) >> 4));
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + s.a0);
 #pragma unroll
@@ -249,26 +295,15 @@ __device__ __forceinline__ void slot_commit(const Slot<NB, I4>& s, uint8_t* vb, 
   reinterpret_cast<u32x4_t*>(bb)[lane & 31] = s.bm;
 }
 
-// Copies the chunks a slot does not hold (GroupTiles denser than the slot
-// covers; only the unpipelined path meets them).
-template <int NB, bool I4>
-__device__ __forceinline__ void slot_commit_rest(const Slot<NB, I4>& s, const Args& a, uint8_t* vb, int lane) {
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + s.a0);
-  const uint32_t last = static_cast<uint32_t>((a.values_alloc - 16 - s.a0) >> 4);
-  for (uint32_t ch = lane + 64 * ValTraits<I4>::kChunks; ch < s.nch; ch += 64)
-    reinterpret_cast<u32x4_t*>(vb)[ch] = src[min(ch, last)];
-}
-
-// Rebuild and multiply one GroupTile already in LDS.
-template <int NB, bool I4>
-__device__ __forceinline__ void tile_compute(const Slot<NB, I4>& s, const uint8_t* vb, const uint64_t* bb,
-                                             const uint32_t* lut, f32x4_t (&acc)[4][NB], int lane, int bt_lane,
-                                             int r8, uint64_t rowmask) {
-  const uint64_t bme = bb[lane];
-  const uint32_t pc = __popcll(bme);
-  const uint32_t ebase = wave_inclusive_scan(pc) - pc + s.delta;
+// Rebuild and multiply TCTile rows RS0 .. RS0+RSN-1 of a GroupTile whose
+// bitmaps are in bb and whose values are in vb; ebase (lane i) is where
+// BitmapTile i's values start in vb.
+template <int NB, bool I4, int RS0, int RSN>
+__device__ __forceinline__ void tile_rows(const u32x4_t (&x)[2][NB], const uint8_t* vb, const uint64_t* bb,
+                                          const uint32_t* lut, f32x4_t (&acc)[4][NB], uint32_t ebase, int bt_lane,
+                                          int r8, uint64_t rowmask) {
 #pragma unroll
-  for (int rs = 0; rs < 4; ++rs) {
+  for (int rs = RS0; rs < RS0 + RSN; ++rs) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int bt = 16 * rs + 8 * ks + bt_lane;
@@ -279,49 +314,70 @@ __device__ __forceinline__ void tile_compute(const Slot<NB, I4>& s, const uint8_
       const half8_t ah = rebuild_row<I4>(vb, lut, rb, byte);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        acc[rs][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(half8_t, s.x[ks][nb]),
+        acc[rs][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(half8_t, x[ks][nb]),
                                                              acc[rs][nb], 0, 0, 0);
     }
   }
 }
 
-template <int NB, bool I4, bool OUT_F16>
-__global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
+// Exclusive prefix of the BitmapTile popcounts of the GroupTile in bb
+// (lane i <-> BitmapTile i).
+__device__ __forceinline__ uint32_t bitmap_prefix(const uint64_t* bb, int lane) {
+  const uint32_t pc = __popcll(bb[lane]);
+  return wave_inclusive_scan(pc) - pc;
+}
+
+// Launch shape of the decode kernel: waves per workgroup, GroupTiles loaded
+// ahead of the one being computed (1 or 2), and the minimum waves per SIMD
+// the register allocation must allow.
+template <int WAVES_, int DEPTH_, int OCC_>
+struct Cfg {
+  static constexpr int kWavesPerGroup = WAVES_;
+  static constexpr int kDepth = DEPTH_;
+  static constexpr int kOcc = OCC_;
+  static constexpr int kThreadsPerGroup = 64 * WAVES_;
+};
+
+template <int NB, bool I4, bool OUT_F16, class C>
+__global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Args a) {
   using VT = ValTraits<I4>;
-  __shared__ __attribute__((aligned(16))) uint32_t lut[I4 ? 2 * 256 : 4 * 256];
+  constexpr int kW = C::kWavesPerGroup;
+  constexpr int kThreads = C::kThreadsPerGroup;
+  __shared__ __attribute__((aligned(16))) uint32_t lut[I4 ? 16 : 32];
   // Staging (per wave: values, then bitmaps); reused for the final reduction.
-  constexpr int kStage = kWaves * (VT::kVbuf + 8 * kBtPerGt);
-  constexpr int kRed = kWaves * 4 * NB * 64 * 4 * 4;
+  constexpr int kStage = kW * (VT::kVbuf + 8 * kBtPerGt);
+  constexpr int kRed = kW * 4 * NB * 64 * 4 * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStage > kRed ? kStage : kRed];
+  __shared__ uint32_t last_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // The wave index is uniform across the wave; saying so keeps the wave's
-  // GroupTile range, the offsets loads and the loop control scalar.
+  // GroupTile range, its offsets and the loop control scalar.
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int gi = blockIdx.x / a.splits;
-  const int sidx = blockIdx.x - gi * a.splits;
+  // Workgroups are dealt to the 8 XCDs round robin; with remap the splits of
+  // one strip land on the same XCD (one L2 for their partial sums).
+  const int nblk = static_cast<int>(gridDim.x);
+  const int b = static_cast<int>(blockIdx.x);
+  const int L = a.remap ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int gi = L / a.splits;
+  const int sidx = L - gi * a.splits;
 
-  for (int b = tid; b < 256; b += kThreads) {
+  if (tid < 16) {
     if constexpr (!I4) {
-      u32x4_t e;
-      e.x = nibble_selector(b & 15, 0);
-      e.y = nibble_selector(b & 15, 1);
-      e.z = nibble_selector(b >> 4, 0);
-      e.w = nibble_selector(b >> 4, 1);
-      reinterpret_cast<u32x4_t*>(lut)[b] = e;
-    } else {
       u32x2_t e;
-      e.x = nibble_byte_selector(b, 0);
-      e.y = nibble_byte_selector(b, 1);
-      reinterpret_cast<u32x2_t*>(lut)[b] = e;
+      e.x = nibble_selector(tid, 0);
+      e.y = nibble_selector(tid, 1);
+      reinterpret_cast<u32x2_t*>(lut)[tid] = e;
+    } else {
+      lut[tid] = nibble_byte_selector(tid);
     }
   }
   __syncthreads();
 
   // Columns of GroupTiles this wave streams.
-  const int parts = a.splits * kWaves;
-  const int q = sidx * kWaves + w;
+  const int parts = a.splits * kW;
+  const int q = sidx * kW + w;
   const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * q / parts);
   const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (q + 1) / parts);
 
@@ -339,44 +395,75 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   uint8_t* vb = smem + w * VT::kVbuf;
-  uint64_t* bb = reinterpret_cast<uint64_t*>(smem + kWaves * VT::kVbuf) + w * kBtPerGt;
+  uint64_t* bb = reinterpret_cast<uint64_t*>(smem + kW * VT::kVbuf) + w * kBtPerGt;
 
-  // A wave may own no GroupTile column (K < 256): it only joins the
+  // The wave's GroupTile offsets, one per lane: lane i holds
+  // offsets[g_begin + i] for i <= count (the host keeps count <= 63), so a
+  // slot's value range comes from two v_readlane.
+  const int cnt = c_end - c_begin;
+  const int64_t g_begin = static_cast<int64_t>(gi) * a.Gc + c_begin;
+  const uint32_t ov = a.offsets[g_begin + min(lane, max(cnt, 0))];
+  auto off_at = [&](int c) -> uint32_t { return __builtin_amdgcn_readlane(ov, min(c - c_begin, 63)); };
+
+  // A wave may own no GroupTile column (K < 64 * waves): it only joins the
   // reduction.  A GroupTile whose values span more chunks than a slot holds
-  // (fp16 density above ~75%) sends the whole wave down the unpipelined path.
-  uint32_t widest = 0;
-  for (int c = c_begin; c < c_end; ++c) {
-    const int64_t g = static_cast<int64_t>(gi) * a.Gc + c;
-    widest = max(widest, a.offsets[g + 1] - a.offsets[g]);
-  }
-  const uint32_t fast_limit = I4 ? 4096u : (16u * 64u * VT::kChunks - 32u) / 2u;
+  // (fp16 density above ~74%) sends the whole wave down the unpipelined path.
+  const uint32_t ov_next = __shfl_down(ov, 1);
+  const uint32_t widest = wave_max(lane < cnt ? ov_next - ov : 0u);
 
-  if (c_begin >= c_end) {
+  if (cnt <= 0) {
     // nothing to stream
-  } else if (widest > fast_limit) {
-    for (int c = c_begin; c < c_end; ++c) {
-      Slot<NB, I4> s0;
-      slot_load(s0, a, gi, c, lane);
-      slot_commit(s0, vb, bb, lane);
-      slot_commit_rest(s0, a, vb, lane);
-      wave_sync();
-      tile_compute(s0, vb, bb, lut, acc, lane, bt_lane, r8, rowmask);
-      wave_sync();
+  } else if (widest > VT::kFastLimit) {
+    if constexpr (!I4) {
+      // Unpipelined: per GroupTile, bitmaps first, then the values of TCTile
+      // rows 0-1 and of rows 2-3, each half rebuilt from the wave's buffer.
+      const uint64_t top = a.values_alloc - 16;
+      for (int c = c_begin; c < c_end; ++c) {
+        const uint32_t o0 = off_at(c), o1 = off_at(c + 1);
+        Slot<NB, I4> s0;
+        slot_load(s0, a, gi, c, lane, o0, o1);
+        reinterpret_cast<u32x4_t*>(bb)[lane & 31] = s0.bm;
+        wave_sync();
+        const uint32_t excl = bitmap_prefix(bb, lane);
+        const uint32_t mid = __builtin_amdgcn_readlane(excl, 32);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t hs = o0 + (h ? mid : 0u);
+          const uint32_t he = h ? o1 : o0 + mid;
+          const uint64_t a0 = min(chunk_start<I4>(hs), top);
+          const uint32_t delta = chunk_delta<I4>(hs, a0);
+          const uint32_t nch = min(chunk_count<I4>(he, a0), static_cast<uint32_t>((VT::kVbuf - 16) / 16));
+          const uint32_t last = static_cast<uint32_t>((top - a0) >> 4);
+          const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
+          for (uint32_t ch = lane; ch < nch; ch += 64) reinterpret_cast<u32x4_t*>(vb)[ch] = src[min(ch, last)];
+          wave_sync();
+          const uint32_t ebase = excl - (h ? mid : 0u) + delta;
+          if (h == 0)
+            tile_rows<NB, I4, 0, 2>(s0.x, vb, bb, lut, acc, ebase, bt_lane, r8, rowmask);
+          else
+            tile_rows<NB, I4, 2, 2>(s0.x, vb, bb, lut, acc, ebase, bt_lane, r8, rowmask);
+          wave_sync();
+        }
+      }
     }
-  } else {
+  } else if constexpr (C::kDepth == 2) {
     // Three register slots: GroupTile c is in LDS while c+1 and c+2 load.
-    // Loads past the wave's last GroupTile repeat it (every wave owns at
+    // Loads past the wave's last GroupTile repeat it (every wave here owns at
     // least one), so each step issues the same loads and waits for exactly
-    // one slot.
+    // one slot.  A step issues the loads of c+2 before waiting for c.
     const int c_last = c_end - 1;
+    auto load = [&](Slot<NB, I4>& sl, int c) {
+      const int cc = min(c, c_last);
+      slot_load(sl, a, gi, cc, lane, off_at(cc), off_at(cc + 1));
+    };
     Slot<NB, I4> s0, s1, s2;
-    slot_load(s0, a, gi, c_begin, lane);
-    slot_load(s1, a, gi, min(c_begin + 1, c_last), lane);
+    load(s0, c_begin);
+    load(s1, c_begin + 1);
     auto step = [&](Slot<NB, I4>& cur, int c, Slot<NB, I4>& nxt) {
+      load(nxt, c + 2);
       slot_commit(cur, vb, bb, lane);
       wave_sync();
-      slot_load(nxt, a, gi, min(c + 2, c_last), lane);
-      tile_compute(cur, vb, bb, lut, acc, lane, bt_lane, r8, rowmask);
+      tile_rows<NB, I4, 0, 4>(cur.x, vb, bb, lut, acc, bitmap_prefix(bb, lane) + cur.delta, bt_lane, r8, rowmask);
       wave_sync();
     };
     int c = c_begin;
@@ -387,11 +474,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
     }
     if (c < c_end) step(s0, c, s2);
     if (c + 1 < c_end) step(s1, c + 1, s0);
+  } else {
+    // Two register slots: GroupTile c is in LDS while c+1 loads.
+    const int c_last = c_end - 1;
+    auto load = [&](Slot<NB, I4>& sl, int c) {
+      const int cc = min(c, c_last);
+      slot_load(sl, a, gi, cc, lane, off_at(cc), off_at(cc + 1));
+    };
+    Slot<NB, I4> s0, s1;
+    load(s0, c_begin);
+    auto step = [&](Slot<NB, I4>& cur, int c, Slot<NB, I4>& nxt) {
+      load(nxt, c + 1);
+      slot_commit(cur, vb, bb, lane);
+      wave_sync();
+      tile_rows<NB, I4, 0, 4>(cur.x, vb, bb, lut, acc, bitmap_prefix(bb, lane) + cur.delta, bt_lane, r8, rowmask);
+      wave_sync();
+    };
+    int c = c_begin;
+    for (; c + 2 <= c_end; c += 2) {
+      step(s0, c, s1);
+      step(s1, c + 1, s0);
+    }
+    if (c < c_end) step(s0, c, s1);
   }
 
-  // Workgroup reduction over waves (fixed order), then store.
+  // Workgroup reduction over waves (fixed order).
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);   // [kWaves][4][NB][64 lanes][4]
+  float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll
   for (int rs = 0; rs < 4; ++rs)
 #pragma unroll
@@ -400,6 +509,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   __syncthreads();
 
   const int m0 = gi * kGT;
+  auto store_y = [&](int n, int ml, float sum) {
+    if constexpr (I4) sum *= static_cast<float>(__builtin_bit_cast(_Float16, a.scales[m0 + ml]));
+    const size_t yi = static_cast<size_t>(n) * a.M + m0 + ml;
+    if constexpr (OUT_F16)
+      reinterpret_cast<_Float16*>(a.Y)[yi] = static_cast<_Float16>(sum);
+    else
+      reinterpret_cast<float*>(a.Y)[yi] = sum;
+  };
   for (int e = tid; e < 64 * 16 * NB; e += kThreads) {
     const int n = e >> 6;
     const int ml = e & 63;
@@ -410,47 +527,96 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
     const int nb = n >> 4;
     float sum = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) sum += red[(((ww * 4 + rs) * NB + nb) * 64 + ln) * 4 + i];
-    const size_t yi = static_cast<size_t>(n) * a.M + m0 + ml;
-    if (a.splits > 1) {
-      a.ws[static_cast<size_t>(sidx) * a.N * a.M + yi] = sum;   // INT4: unscaled; the reduction scales
-    } else {
-      if constexpr (I4) sum *= static_cast<float>(__builtin_bit_cast(_Float16, a.scales[m0 + ml]));
-      if constexpr (OUT_F16)
-        reinterpret_cast<_Float16*>(a.Y)[yi] = static_cast<_Float16>(sum);
-      else
-        reinterpret_cast<float*>(a.Y)[yi] = sum;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Split-K reduction: Y[n][m] = scale[m] * sum_{s} ws[s][n][m], fixed order.
-// ---------------------------------------------------------------------------
-template <bool OUT_F16>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, void* __restrict__ Y,
-                                                            const uint16_t* __restrict__ scales, int M, int N,
-                                                            int splits) {
-  const size_t total = static_cast<size_t>(M) * N;
-  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < total;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    float s = 0.f;
-    for (int p = 0; p < splits; ++p) s += ws[static_cast<size_t>(p) * total + i];
-    if (scales) s *= static_cast<float>(__builtin_bit_cast(_Float16, scales[i % M]));
-    if (OUT_F16)
-      reinterpret_cast<_Float16*>(Y)[i] = static_cast<_Float16>(s);
+    for (int ww = 0; ww < kW; ++ww) sum += red[(((ww * 4 + rs) * NB + nb) * 64 + ln) * 4 + i];
+    if (a.splits > 1)
+      // Device-coherent store: it reaches the level every XCD reads from, so
+      // no L2 write-back of the whole cache is needed before the counter.
+      __hip_atomic_store(&a.part[(static_cast<size_t>(sidx) * a.N + n) * a.M + m0 + ml], sum, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     else
-      reinterpret_cast<float*>(Y)[i] = s;
+      store_y(n, ml, sum);
   }
+  if (a.splits <= 1) return;
+
+  // Split K: the last workgroup of the strip to finish adds the partial sums
+  // of all its splits, in split order, and writes Y; the counter goes back
+  // to 0 for the next call.  Every thread's partial stores have completed
+  // (s_waitcnt) before the barrier that precedes the counter increment, and
+  // the last workgroup reads the partials with device-coherent loads issued
+  // after it has seen the final count.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (tid == 0)
+    last_flag = __hip_atomic_fetch_add(&a.counters[gi], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                static_cast<uint32_t>(a.splits - 1);
+  __syncthreads();
+  if (!last_flag) return;
+  for (int e = tid; e < 64 * a.N; e += kThreads) {
+    const int n = e >> 6;
+    const int ml = e & 63;
+    float sum = 0.f;
+    for (int p = 0; p < a.splits; ++p)
+      sum += __hip_atomic_load(&a.part[(static_cast<size_t>(p) * a.N + n) * a.M + m0 + ml], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    store_y(n, ml, sum);
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
 // Host dispatch
 // ---------------------------------------------------------------------------
 
+// Decode launch configurations (waves per workgroup, pipeline depth,
+// minimum waves per SIMD).  The default is the measured best on MI355X; a
+// tuning build (-DUSW_TUNING) also compiles the others and picks one from
+// the USW_DECODE_CFG environment variable.
+using DefaultCfg = Cfg<4, 1, 4>;
+#ifdef USW_TUNING
+using TuneCfg1 = Cfg<4, 1, 3>;
+using TuneCfg2 = Cfg<4, 2, 3>;
+using TuneCfg3 = Cfg<8, 1, 4>;
+using TuneCfg4 = Cfg<8, 1, 3>;
+using TuneCfg5 = Cfg<4, 2, 2>;
+#endif
+
+int choose_cfg() {
+#ifdef USW_TUNING
+  const char* e = std::getenv("USW_DECODE_CFG");
+  if (e) return std::atoi(e);
+#endif
+  return 0;
+}
+
+struct CfgInfo {
+  int waves;   // waves per workgroup
+  int occ;     // waves per SIMD the configuration allows
+};
+
+CfgInfo cfg_info(int cfg) {
+  switch (cfg) {
+#ifdef USW_TUNING
+    case 1: return {TuneCfg1::kWavesPerGroup, TuneCfg1::kOcc};
+    case 2: return {TuneCfg2::kWavesPerGroup, TuneCfg2::kOcc};
+    case 3: return {TuneCfg3::kWavesPerGroup, TuneCfg3::kOcc};
+    case 4: return {TuneCfg4::kWavesPerGroup, TuneCfg4::kOcc};
+    case 5: return {TuneCfg5::kWavesPerGroup, TuneCfg5::kOcc};
+#endif
+    default: return {DefaultCfg::kWavesPerGroup, DefaultCfg::kOcc};
+  }
+}
+
+// Compute units of MI355X; the automatic split aims at one full round of
+// resident workgroups on all of them.
+constexpr int64_t kComputeUnits = 256;
+
 struct Plan {
   int splits;     // workgroups per 64-row strip
   int nchunk;     // columns of N per kernel pass (16 or 32)
+  int cfg;        // launch configuration
+  int waves;      // waves per workgroup
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -458,16 +624,22 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 Plan make_plan(const usw::Geometry& g, int N, int splits_req) {
   Plan p;
   p.nchunk = N <= 16 ? 16 : 32;
-  int s = splits_req;
+  p.cfg = choose_cfg();
+  const CfgInfo ci = cfg_info(p.cfg);
+  p.waves = ci.waves;
+  int64_t s = splits_req;
   if (s <= 0) {
-    // Enough workgroups to cover the 256 compute units, but each wave keeps
-    // at least 4 GroupTiles to stream.
-    s = static_cast<int>((256 + g.Gr - 1) / g.Gr);
-    const int cap = static_cast<int>(std::max<int64_t>(1, g.Gc / (kWaves * 4)));
-    s = std::min(s, cap);
+    // About one round of resident workgroups (occ waves per SIMD, 4 SIMDs
+    // per compute unit), each wave keeping at least 3 GroupTiles to stream.
+    const int64_t target = kComputeUnits * 4 * ci.occ / ci.waves;
+    s = std::max<int64_t>(1, (target + g.Gr / 2) / g.Gr);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, g.Gc / (p.waves * 3)));
   }
-  const int smax = static_cast<int>(std::max<int64_t>(1, g.Gc / kWaves));
-  p.splits = std::max(1, std::min(s, smax));
+  const int64_t smax = std::max<int64_t>(1, g.Gc / p.waves);
+  // Each wave caches its GroupTile offsets in one register: at most 63
+  // GroupTiles per wave.
+  const int64_t smin = (g.Gc + 63 * p.waves - 1) / (63 * p.waves);
+  p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
   return p;
 }
 
@@ -486,17 +658,35 @@ usw_status check_common(const usw_fmt* f, int32_t y_type, int32_t N, usw::Geomet
   return USW_OK;
 }
 
+// Workspace: per-strip counters (4 B each, padded to 256 B) then the fp32
+// partial sums of every split.
+size_t counters_bytes(const usw::Geometry& g) { return (static_cast<size_t>(4 * g.Gr) + 255) & ~size_t(255); }
+
 size_t workspace_bytes(const usw::Geometry& g, const Plan& p) {
   if (p.splits <= 1) return 0;
-  return static_cast<size_t>(p.splits) * p.nchunk * g.M * sizeof(float);
+  return counters_bytes(g) + static_cast<size_t>(p.splits) * p.nchunk * g.M * sizeof(float);
+}
+
+template <int NB, bool I4, class C>
+void launch_cfg(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
+  if (f16out)
+    decode_kernel<NB, I4, true, C><<<grid, C::kThreadsPerGroup, 0, s>>>(a);
+  else
+    decode_kernel<NB, I4, false, C><<<grid, C::kThreadsPerGroup, 0, s>>>(a);
 }
 
 template <int NB, bool I4>
-void launch_decode(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
-  if (f16out)
-    decode_kernel<NB, I4, true><<<grid, kThreads, 0, s>>>(a);
-  else
-    decode_kernel<NB, I4, false><<<grid, kThreads, 0, s>>>(a);
+void launch_decode(const Args& a, bool f16out, dim3 grid, hipStream_t s, int cfg) {
+  switch (cfg) {
+#ifdef USW_TUNING
+    case 1: launch_cfg<NB, I4, TuneCfg1>(a, f16out, grid, s); return;
+    case 2: launch_cfg<NB, I4, TuneCfg2>(a, f16out, grid, s); return;
+    case 3: launch_cfg<NB, I4, TuneCfg3>(a, f16out, grid, s); return;
+    case 4: launch_cfg<NB, I4, TuneCfg4>(a, f16out, grid, s); return;
+    case 5: launch_cfg<NB, I4, TuneCfg5>(a, f16out, grid, s); return;
+#endif
+    default: launch_cfg<NB, I4, DefaultCfg>(a, f16out, grid, s); return;
+  }
 }
 
 usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_type, int32_t N, void* ws,
@@ -516,7 +706,8 @@ usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_typ
     if (!aligned16(ws)) return USW_ERR_MISALIGNED;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>(g.Gr * p.splits));
+  const int64_t nblk = g.Gr * p.splits;
+  const dim3 grid(static_cast<unsigned>(nblk));
   const int M = static_cast<int>(g.M), K = static_cast<int>(g.K), Gc = static_cast<int>(g.Gc);
   const size_t ybytes = y_type == USW_OUT_F16 ? 2 : 4;
   const bool f16out = y_type == USW_OUT_F16;
@@ -531,31 +722,24 @@ usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_typ
     a.scales = i4 ? f->scales : nullptr;
     a.X = X + static_cast<size_t>(n0) * K;
     a.Y = static_cast<uint8_t*>(Y) + static_cast<size_t>(n0) * M * ybytes;
-    a.ws = static_cast<float*>(ws);
+    a.counters = need ? static_cast<uint32_t*>(ws) : nullptr;
+    a.part = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counters_bytes(g)) : nullptr;
     a.values_alloc = usw::values_alloc_bytes(f->val_type, f->nnz);
     a.M = M;
     a.K = K;
     a.N = nc;
     a.Gc = Gc;
     a.splits = p.splits;
+    a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
     const bool two = nc > 16;
     if (i4) {
-      if (two) launch_decode<2, true>(a, f16out, grid, s);
-      else launch_decode<1, true>(a, f16out, grid, s);
+      if (two) launch_decode<2, true>(a, f16out, grid, s, p.cfg);
+      else launch_decode<1, true>(a, f16out, grid, s, p.cfg);
     } else {
-      if (two) launch_decode<2, false>(a, f16out, grid, s);
-      else launch_decode<1, false>(a, f16out, grid, s);
+      if (two) launch_decode<2, false>(a, f16out, grid, s, p.cfg);
+      else launch_decode<1, false>(a, f16out, grid, s, p.cfg);
     }
     if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
-    if (p.splits > 1) {
-      const size_t total = static_cast<size_t>(M) * nc;
-      const unsigned rg = static_cast<unsigned>(std::min<size_t>((total + 255) / 256, 4096));
-      if (f16out)
-        splitk_reduce_kernel<true><<<rg, 256, 0, s>>>(a.ws, a.Y, a.scales, M, nc, p.splits);
-      else
-        splitk_reduce_kernel<false><<<rg, 256, 0, s>>>(a.ws, a.Y, a.scales, M, nc, p.splits);
-      if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
-    }
   }
   return USW_OK;
 }
