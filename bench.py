@@ -76,8 +76,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     M, K, N, s = args.M, args.K, args.N, args.sparsity
-    layer_id = 2 if (M, K) == (20480, 5120) else 0
-    cfg_id = 5 if args.dtype == "i4" else 2
+    prefill = args.dtype == "f16" and N > 32
+    layer_id = {(20480, 5120): 2, (11008, 4096): 0, (4096, 11008): 1}.get((M, K), 0)
+    cfg_id = 5 if args.dtype == "i4" else (4 if prefill else 2)
 
     log(f"[bench] generating W {M}x{K} (magnitude pruning s={s}) and X [{N}][{K}]")
     W, mask, X = wl.config_case(cfg_id, M, K, N, s, layer_id=layer_id)
@@ -165,6 +166,25 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(W, mask, X, M, K, N, args.dtype, args.cpu_reps)
 
+    kname = "prefill_kernel" if prefill else ("decode_f16_kernel" if args.dtype == "f16" else "decode_i4_kernel")
+    if prefill:
+        # Compute-bound: the matrix cores run the dense 64x64 tiles rebuilt
+        # from the bitmaps, 2*M*K*N flops per launch.
+        tf = flops / (kern_avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tf, 1), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None, "kernel": kname,
+                    "kernel_avg_us": round(kern_avg_ms * 1e3, 3), "alg_flops_per_launch": int(flops),
+                    "alg_bytes_per_launch": int(alg)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": kname,
+                    "kernel_avg_us": round(kern_avg_ms * 1e3, 3), "alg_bytes_per_launch": int(alg)}
+    if (M, K) == (20480, 5120):
+        workload = f"opt13b_ffn_up_{M}x{K}_s{s}_N{N}"
+    elif prefill and (M, K) in ((11008, 4096), (4096, 11008)):
+        workload = f"llama7b_prefill_{M}x{K}_s{s}_N{N}"
+    else:
+        workload = f"spmm_{M}x{K}_s{s}_N{N}"
     out = {
         "metric": METRIC if (M, K, N, s, args.dtype) == (20480, 5120, 16, 0.5, "f16") else
         f"effective TFLOP/s + HBM GB/s, bitmap SpMM M={M} K={K} s={int(s * 100)}% N={N} {args.dtype}",
@@ -179,15 +199,12 @@ def main():
         "vs_baseline": None,
         "dtype": "f16" if args.dtype == "f16" else "i4",
         "data": "synthetic (seeded N(0,0.02) weights, magnitude pruning, N(0,1) activations)",
-        "config": {"workload": f"opt13b_ffn_up_{M}x{K}_s{s}_N{N}" if (M, K) == (20480, 5120) else f"spmm_{M}x{K}_s{s}_N{N}",
+        "config": {"workload": workload,
                    "M": M, "K": K, "N": N, "sparsity": s, "values": args.dtype, "groupTile": "64x64",
                    "rotation_copies": R, "splits": args.splits or "auto"},
         "gbps": round(gbps_step, 1),
         "hbm_frac": round(gbps_step / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "decode_f16_kernel" if args.dtype == "f16" else "decode_i4_kernel",
-                     "kernel_avg_us": round(kern_avg_ms * 1e3, 3), "alg_bytes_per_launch": int(alg)},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "dense_fp16": dense,
         "nnz": int(h.nnz),

@@ -145,12 +145,13 @@ usw_status usw_validate(const usw_fmt* host_fmt);
 
 /*
  * Workspace bytes usw_spmm needs for this matrix and N (0 when none).  The
- * workspace starts with one 32-bit counter per 64-row strip of GroupTiles
- * (the first ceil(4 * M / 64 / 256) * 256 bytes), followed by the fp32
- * partial sums of the split-K workgroups.  Those counter bytes must be zero
- * when a call starts: allocate the workspace zero-filled; every call leaves
- * them zero again.  A workspace last used with a different M (whose partial
- * sums may cover them) must have them zeroed first.
+ * workspace starts with 32-bit counters (usw_spmm_counter_bytes of them,
+ * one per output tile) followed by the fp32 partial sums of the split-K
+ * workgroups.  The counter bytes must be zero when a call starts: allocate
+ * the workspace zero-filled; every call leaves its counter bytes zero again.
+ * A workspace last used by a call with a different counter size (another M,
+ * or N on the other side of 32, or another prefill token tiling) may hold
+ * partial sums there: zero the new call's counter bytes before it.
  * Errors: as usw_spmm's argument checks.
  */
 usw_status usw_spmm_workspace(const usw_fmt* fmt, int32_t N, size_t* bytes);
@@ -177,15 +178,24 @@ usw_status usw_spmm(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y_ty
 
 /*
  * As usw_spmm_workspace / usw_spmm, with the split-K factor chosen by the
- * caller: splits = workgroups that share one 64-row strip of GroupTiles,
- * each summing a contiguous range of GroupTile columns (0 = automatic).
- * With a factor above 1 each workgroup writes fp32 partial sums to the
- * workspace and the last workgroup of a strip to finish adds them in split
- * order, so results do not depend on scheduling.  The factor is clamped to
- * [ceil(K / (64 * 4 * 63)), max(1, K / 256)].  Same errors as usw_spmm.
- * Meant for tuning and tests.
+ * caller: splits = workgroups that share one output tile (a 64-row strip of
+ * GroupTiles, with all N columns for the decode kernel, or 256 / 512 of them
+ * for the prefill kernel), each summing a contiguous range of GroupTile
+ * columns (0 = automatic).  With a factor above 1 each workgroup writes fp32
+ * partial sums to the workspace and the last workgroup of a tile to finish
+ * adds them in split order, so results do not depend on scheduling.  The
+ * factor is clamped to [ceil(K / (64 * 4 * 63)), max(1, K / 256)] for the
+ * decode kernels and to [ceil(K / 65536), K / 64] for the prefill kernel.
+ * Same errors as usw_spmm.  Meant for tuning and tests.
  */
 usw_status usw_spmm_workspace_ex(const usw_fmt* fmt, int32_t N, int32_t splits, size_t* bytes);
+
+/*
+ * Bytes at the start of the workspace of usw_spmm_ex(fmt, N, splits) that
+ * hold its per-tile counters and must be zero when the call starts (0 when
+ * the call needs no workspace).  Same errors as usw_spmm_workspace_ex.
+ */
+usw_status usw_spmm_counter_bytes(const usw_fmt* fmt, int32_t N, int32_t splits, size_t* bytes);
 usw_status usw_spmm_ex(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y_type, int32_t N, int32_t splits,
                        void* ws, size_t ws_bytes, void* stream);
 

@@ -23,7 +23,7 @@ from ._lib import (USW_OUT_F16, USW_OUT_F32, USW_VAL_F16, USW_VAL_I4, EXPORTED, 
                    check, lib)
 
 __all__ = ["HostEncoding", "Encoding", "encode_host", "encode", "to_device", "validate", "spmm",
-           "spmm_workspace_bytes", "UswError", "lib"]
+           "spmm_workspace_bytes", "spmm_counter_bytes", "UswError", "lib"]
 
 _VAL = {"f16": USW_VAL_F16, "i4": USW_VAL_I4}
 
@@ -142,20 +142,30 @@ def spmm_workspace_bytes(enc: Encoding, N: int, splits: int = 0) -> int:
 _WS = {}
 
 
-def _workspace(device, M: int, nbytes: int):
-    """Zero-filled workspace per (device, M).  The first bytes of a workspace
-    hold per-strip counters whose extent depends on M; the library leaves them
-    at zero after each call, but another shape's partial sums could land
-    there, so shapes with different M never share a buffer.  Calls on one
-    device are ordered on the stream they are issued to; do not overlap calls
-    on different streams."""
+def spmm_counter_bytes(enc: Encoding, N: int, splits: int = 0) -> int:
+    f = enc.fmt()
+    b = ctypes.c_size_t()
+    check(lib().usw_spmm_counter_bytes(ctypes.byref(f), int(N), int(splits), ctypes.byref(b)), "usw_spmm_counter_bytes")
+    return b.value
+
+
+def _workspace(device, nbytes: int, counter_bytes: int):
+    """One zero-filled workspace per device.  Its first ``counter_bytes``
+    bytes must be zero when a call starts; each call leaves them zero, but a
+    call with another counter size may have written partial sums there, so
+    they are cleared (a small fill kernel on the current stream) whenever the
+    counter size changes.  Calls on one device are ordered on the stream they
+    are issued to; do not overlap calls on different streams."""
     import torch
-    key = (str(device), int(M))
-    buf = _WS.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _WS[key] = buf
-    return buf
+    key = str(device)
+    ent = _WS.get(key)
+    if ent is None or ent[0].numel() < nbytes:
+        ent = [torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device), counter_bytes]
+        _WS[key] = ent
+    elif ent[1] != counter_bytes:
+        ent[0][:counter_bytes].zero_()
+        ent[1] = counter_bytes
+    return ent[0]
 
 
 def spmm(enc: Encoding, x, y=None, out_dtype=None, splits: int = 0, stream=None):
@@ -179,7 +189,7 @@ def spmm(enc: Encoding, x, y=None, out_dtype=None, splits: int = 0, stream=None)
         raise ValueError("y must be float16 or float32")
     f = enc.fmt()
     nbytes = spmm_workspace_bytes(enc, N, splits)
-    ws = _workspace(x.device, enc.M, nbytes) if nbytes else None
+    ws = _workspace(x.device, nbytes, spmm_counter_bytes(enc, N, splits)) if nbytes else None
     st = stream if stream is not None else torch.cuda.current_stream(x.device)
     check(lib().usw_spmm_ex(ctypes.byref(f), x.data_ptr(), y.data_ptr(), yt, N, int(splits),
                             ws.data_ptr() if ws is not None else None, nbytes, ctypes.c_void_p(st.cuda_stream)),

@@ -1,0 +1,179 @@
+// Device helpers shared by the bitmap SpMM kernels (gfx950, wave64): lane
+// scans, the byte selectors and LDS windows that expand one BitmapTile row
+// of packed values into the 8 dense slots of an MFMA A fragment, and the
+// 16-byte chunk arithmetic of the value stream.
+//
+// Format: TCA-BME (blog "SpInfer: How bitmaps make sparse LLMs actually
+// fast", section "How TCA-BME addresses the indexing overhead"); a value is
+// found by masked popcount (same blog, "Shared Memory Bitmap Decoding").
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace usw_dev {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGT = 64;                   // GroupTile side the kernels are built for
+constexpr int kBtPerGt = 64;              // BitmapTiles per 64x64 GroupTile
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP (no LDS round trips):
+// Hillis-Steele inside each 16-lane row, then the row totals are carried by
+// the row_bcast:15 and row_bcast:31 broadcasts.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
+// Maximum over the 64 lanes (DPP), returned in every lane.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false)));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// v_perm_b32 byte selectors that expand the packed fp16 values of one 4-bit
+// nibble of a BitmapTile row into 4 slots (two output dwords, j = 0, 1).
+// Packed value k of the window occupies bytes 2k, 2k+1 (window dword 0 =
+// selector bytes 0-3, dword 1 = bytes 4-7); a clear bit selects 0x0C, which
+// v_perm turns into 0x00.  16 entries of 8 bytes: the table's 32 dwords sit
+// in distinct LDS banks, so any pattern of lookups is conflict-free.
+__device__ __forceinline__ uint32_t nibble_selector(uint32_t q, int j) {
+  uint32_t sel = 0;
+  for (int h = 0; h < 2; ++h) {
+    const int p = 2 * j + h;
+    uint32_t s16 = 0x0C0Cu;
+    if ((q >> p) & 1u) {
+      const uint32_t k = __builtin_popcount(q & ((1u << p) - 1u));
+      s16 = (2u * k) | ((2u * k + 1u) << 8);
+    }
+    sel |= s16 << (16 * h);
+  }
+  return sel;
+}
+
+// v_perm selectors that expand the packed nibbles of one 4-bit nibble of a
+// BitmapTile row into 4 byte slots.  Packed nibble k of an 8-nibble window w
+// sits in byte k/2 of lo4 (k even) or of hi4 (k odd), lo4 = w & 0x0F0F0F0F and
+// hi4 = (w >> 4) & 0x0F0F0F0F, and v_perm(hi4, lo4, sel) numbers lo4's bytes
+// 0-3 and hi4's bytes 4-7.
+__device__ __forceinline__ uint32_t nibble_byte_selector(uint32_t q) {
+  uint32_t sel = 0;
+  for (int p = 0; p < 4; ++p) {
+    uint32_t v = 0x0Cu;
+    if ((q >> p) & 1u) {
+      const uint32_t k = __builtin_popcount(q & ((1u << p) - 1u));
+      v = (k & 1u) ? 4u + (k >> 1) : (k >> 1);
+    }
+    sel |= v << (8 * p);
+  }
+  return sel;
+}
+
+// Two dwords holding packed fp16 values e, e+1, e+2, e+3 of an LDS buffer
+// (element e starts at byte 2e; the buffer is dword aligned).
+__device__ __forceinline__ u32x2_t lds_window_f16(const uint8_t* buf, uint32_t e) {
+  const uint32_t ba = 2u * e;
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(buf + (ba & ~3u));
+  const uint32_t d0 = p[0], d1 = p[1], d2 = p[2];
+  u32x2_t w;
+  w.x = __builtin_amdgcn_alignbyte(d1, d0, ba & 3u);
+  w.y = __builtin_amdgcn_alignbyte(d2, d1, ba & 3u);
+  return w;
+}
+
+// 8 packed nibbles starting at nibble e of an LDS buffer, split into the
+// even (lo4) and odd (hi4) nibbles, one per byte.
+__device__ __forceinline__ u32x2_t lds_window_i4(const uint8_t* buf, uint32_t e) {
+  const uint32_t ba = e >> 1;
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(buf + (ba & ~3u));
+  const uint32_t sh = ((ba & 3u) << 3) | ((e & 1u) << 2);
+  const uint32_t win = __builtin_amdgcn_alignbit(p[1], p[0], sh);
+  u32x2_t r;
+  r.x = win & 0x0F0F0F0Fu;
+  r.y = (win >> 4) & 0x0F0F0F0Fu;
+  return r;
+}
+
+// The 8 dense fp16 slots (one BitmapTile row) of a lane's A fragment: the
+// row's kept values start at element rb of the LDS buffer; `byte` is the
+// row's mask.  Slots 0-3 come from a window at rb, slots 4-7 from a window
+// at rb + popcount(low nibble).
+template <bool I4>
+__device__ __forceinline__ half8_t rebuild_row(const uint8_t* vb, const uint32_t* lut, uint32_t rb, uint32_t byte) {
+  const uint32_t pcl = __builtin_popcount(byte & 0xFu);
+  if constexpr (!I4) {
+    const u32x2_t slo = reinterpret_cast<const u32x2_t*>(lut)[byte & 0xFu];
+    const u32x2_t shi = reinterpret_cast<const u32x2_t*>(lut)[byte >> 4];
+    const u32x2_t lo = lds_window_f16(vb, rb);
+    const u32x2_t hi = lds_window_f16(vb, rb + pcl);
+    u32x4_t a;
+    a.x = __builtin_amdgcn_perm(lo.y, lo.x, slo.x);
+    a.y = __builtin_amdgcn_perm(lo.y, lo.x, slo.y);
+    a.z = __builtin_amdgcn_perm(hi.y, hi.x, shi.x);
+    a.w = __builtin_amdgcn_perm(hi.y, hi.x, shi.y);
+    return __builtin_bit_cast(half8_t, a);
+  } else {
+    const uint32_t slo = lut[byte & 0xFu];
+    const uint32_t shi = lut[byte >> 4];
+    const u32x2_t lo = lds_window_i4(vb, rb);
+    const u32x2_t hi = lds_window_i4(vb, rb + pcl);
+    // Slots as bytes; xor 8 maps the two's-complement nibble q to q + 8 in
+    // [0, 15] (an empty slot's 0 becomes 8, i.e. q = 0).
+    const uint32_t e0 = __builtin_amdgcn_perm(lo.y, lo.x, slo) ^ 0x08080808u;
+    const uint32_t e1 = __builtin_amdgcn_perm(hi.y, hi.x, shi) ^ 0x08080808u;
+    // fp16 bit pattern 0x6400 | u is 1024 + u exactly; subtracting 1032
+    // leaves q exactly.
+    u32x4_t a;
+    a.x = __builtin_amdgcn_perm(0x64646464u, e0, 0x04010400u);
+    a.y = __builtin_amdgcn_perm(0x64646464u, e0, 0x04030402u);
+    a.z = __builtin_amdgcn_perm(0x64646464u, e1, 0x04010400u);
+    a.w = __builtin_amdgcn_perm(0x64646464u, e1, 0x04030402u);
+    half8_t h = __builtin_bit_cast(half8_t, a);
+    h += static_cast<_Float16>(-1032.0f);
+    return h;
+  }
+}
+
+
+// Byte offset of the 16-byte chunk holding value element e (fp16: 2 B per
+// element; INT4: 4 bits per element).
+template <bool I4>
+__device__ __forceinline__ uint64_t chunk_start(uint32_t e) {
+  return I4 ? ((static_cast<uint64_t>(e) >> 1) & ~15ull) : ((2ull * e) & ~15ull);
+}
+
+// Elements of the first chunk that precede element e.
+template <bool I4>
+__device__ __forceinline__ uint32_t chunk_delta(uint32_t e, uint64_t a0) {
+  return I4 ? static_cast<uint32_t>(e - 2 * a0) : static_cast<uint32_t>((2ull * e - a0) >> 1);
+}
+
+// 16-byte chunks spanned by elements [e0, e1) counted from a0.
+template <bool I4>
+__device__ __forceinline__ uint32_t chunk_count(uint32_t e1, uint64_t a0) {
+  const uint64_t end = I4 ? ((static_cast<uint64_t>(e1) + 1) >> 1) : 2ull * e1;   // first byte past the values
+  return static_cast<uint32_t>((end - a0 + 15ull) >> 4);
+}
+
+}  // namespace usw_dev

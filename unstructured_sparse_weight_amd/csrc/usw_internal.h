@@ -21,4 +21,17 @@ size_t values_alloc_bytes(int32_t val_type, int64_t nnz);
 double f16_to_f64(uint16_t h);
 uint16_t f64_to_f16_rne(double x);
 
+// Prefill (MFMA) kernel for fp16 values and N > 32: launch shape and split-K
+// factor, workspace size, launch.
+struct PrefillPlan {
+  int waves;    // waves per workgroup (64 tokens each)
+  int ntiles;   // token tiles of 64 * waves
+  int splits;   // workgroups per (strip, token tile)
+};
+PrefillPlan prefill_plan(const Geometry& g, int N, int splits_req);
+size_t prefill_counter_bytes(const Geometry& g, const PrefillPlan& p);
+size_t prefill_workspace_bytes(const Geometry& g, int N, const PrefillPlan& p);
+usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X, void* Y, bool f16out, int N, void* ws,
+                          const PrefillPlan& p, void* stream);
+
 }  // namespace usw

@@ -1,0 +1,374 @@
+// Prefill kernel of libusw (fp16 values, N > 32): Y[n][m] = sum_k W_sp[m][k] X[n][k]
+// with W_sp in the TCA-BME bitmap format (blog "SpInfer: How bitmaps make
+// sparse LLMs actually fast", section "How TCA-BME addresses the indexing
+// overhead"), fed to the fp16 matrix cores.
+//
+// At large N the product is a dense contraction: every rebuilt 64x64
+// GroupTile meets many tokens, so the cost that matters is the matrix-core
+// work plus the rebuild, which is paid once per GroupTile per workgroup.
+// Design (gfx950, wave64):
+//   * A workgroup owns one 64-row strip of GroupTiles and 64 tokens per wave
+//     (256 or 512 tokens), and walks a range of GroupTile columns.
+//   * Per GroupTile the workgroup stages the bitmaps and the value range
+//     [offsets[g], offsets[g+1]) in LDS with 16-byte loads issued one
+//     GroupTile ahead; each wave rebuilds 8 / waves of the 8 A fragments
+//     (16 rows x 32 columns each; lane l holds row l%16, columns
+//     8*(l/16)..+7, i.e. one row of one BitmapTile) by masked popcount and
+//     writes them to a double-buffered LDS tile that every wave reads.
+//   * Each wave multiplies the 64x64 tile with its 64 tokens: 32
+//     v_mfma_f32_16x16x32_f16 per GroupTile, fp32 accumulators in VGPRs.  Its
+//     slice of X (X is [N][K]: 64 tokens x 128 B) is loaded a GroupTile
+//     ahead in whole cache lines and staged in the wave's own LDS region,
+//     from which the X^T fragments are read (no other wave uses them).
+//   * Split K (more workgroups than strips x token tiles): fp32 partial sums
+//     go to the workspace and the last workgroup of a tile adds them in
+//     split order, so the result does not depend on scheduling.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "usw.h"
+#include "usw_internal.h"
+#include "usw_device.h"
+
+namespace {
+
+using namespace usw_dev;
+
+constexpr int kMaxCols = 1024;      // GroupTile columns per workgroup (offsets table in LDS)
+constexpr int kStageChunks = 520;   // >= 513 16-byte chunks: a dense GroupTile plus a partial first chunk
+
+struct PArgs {
+  const uint64_t* __restrict__ bitmaps;
+  const uint32_t* __restrict__ offsets;
+  const uint8_t* __restrict__ values;
+  const uint16_t* __restrict__ X;
+  void* __restrict__ Y;
+  float* __restrict__ part;         // split-K partial sums [splits][N][M]
+  uint32_t* __restrict__ counters;  // per (strip, token tile): workgroups done; kept at 0 between calls
+  uint64_t values_alloc;            // padded size of the values buffer in bytes
+  int M, K, N, Gc, splits, ntiles;
+  int remap;                        // 1: keep consecutive tiles (and a tile's splits) on one XCD
+};
+
+template <int WAVES>
+struct PTraits {
+  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int kCpt = (kStageChunks + kThreads - 1) / kThreads;  // value chunks per thread
+  static constexpr int kFrags = 8 / WAVES;                                // A fragments each wave rebuilds
+  static constexpr int kStageBytes = kThreads * kCpt * 16 + 16;
+  static constexpr int kBN = 64 * WAVES;                                  // tokens per workgroup
+};
+
+template <int CPT>
+struct VSlot {
+  u32x4_t v[CPT];
+  u32x4_t bm;
+};
+
+template <int WAVES, bool OUT_F16>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a) {
+  using T = PTraits<WAVES>;
+  constexpr int kThreads = T::kThreads;
+  constexpr int kCpt = T::kCpt;
+
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2][T::kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint64_t bbuf[2][kBtPerGt];
+  __shared__ __attribute__((aligned(16))) u32x4_t abuf[2][8 * 64];   // two rebuilt 64x64 tiles, fragment order
+  __shared__ __attribute__((aligned(16))) u32x4_t xs[WAVES][64 * 8];   // per wave: its 64 tokens x 64 k of X
+  __shared__ __attribute__((aligned(16))) uint32_t lut[32];
+  __shared__ uint32_t offtab[kMaxCols + 1];
+  __shared__ uint32_t last_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int nblk = static_cast<int>(gridDim.x);
+  const int b = static_cast<int>(blockIdx.x);
+  const int L = a.remap ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int tile = L / a.splits;
+  const int sidx = L - tile * a.splits;
+  const int gi = tile / a.ntiles;
+  const int nt = tile - gi * a.ntiles;
+  const int m0 = gi * kGT;
+  const int nw = nt * T::kBN + 64 * w;   // first token of this wave
+
+  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * sidx / a.splits);
+  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (sidx + 1) / a.splits);
+  const int cnt = c_end - c_begin;        // >= 1: the host keeps splits <= Gc
+  const int c_last = c_end - 1;
+  const int64_t g_row = static_cast<int64_t>(gi) * a.Gc;
+
+  if (tid < 16) {
+    u32x2_t e;
+    e.x = nibble_selector(tid, 0);
+    e.y = nibble_selector(tid, 1);
+    reinterpret_cast<u32x2_t*>(lut)[tid] = e;
+  }
+  for (int i = tid; i <= cnt; i += kThreads) offtab[i] = a.offsets[g_row + c_begin + i];
+  __syncthreads();
+
+  const uint64_t top = a.values_alloc - 16;
+  auto load_v = [&](VSlot<kCpt>& s, int c) {
+    const uint32_t o0 = offtab[c - c_begin], o1 = offtab[c - c_begin + 1];
+    const uint64_t a0 = min(chunk_start<false>(o0), top);
+    const uint32_t nch = min(chunk_count<false>(o1, a0), static_cast<uint32_t>(kThreads * kCpt));
+    const uint32_t last = min(nch > 0 ? nch - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
+#pragma unroll
+    for (int i = 0; i < kCpt; ++i) s.v[i] = src[min(static_cast<uint32_t>(tid + kThreads * i), last)];
+    s.bm = reinterpret_cast<const u32x4_t*>(a.bitmaps + (g_row + c) * kBtPerGt)[tid & 31];
+  };
+  auto commit_v = [&](const VSlot<kCpt>& s, int buf) {
+#pragma unroll
+    for (int i = 0; i < kCpt; ++i) reinterpret_cast<u32x4_t*>(stage[buf])[tid + kThreads * i] = s.v[i];
+    // Wave 0 stores the bitmaps (its two half-waves hold the same 512 B).
+    if (w == 0) reinterpret_cast<u32x4_t*>(bbuf[buf])[lane & 31] = s.bm;
+  };
+
+  // X for this wave's 64 tokens and GroupTile column c: 64 rows of 128 B,
+  // loaded 8 lanes per row (whole cache lines) and kept in the wave's LDS
+  // region, 16-byte chunk q of row r at slot 8r + (q ^ ((r >> 1) & 7)) so
+  // that both these row writes and the fragment reads below (16 rows, one
+  // chunk) touch 16 distinct bank groups.  Tokens past N repeat token N-1;
+  // their products land in columns never stored.
+  const int row = lane & 15, kb = lane >> 4;
+  auto xslot = [](int r, int q) { return 8 * r + (q ^ ((r >> 1) & 7)); };
+  auto load_x = [&](u32x4_t (&x)[8], int c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = min(nw + (lane >> 3) + 8 * j, a.N - 1);
+      x[j] = *reinterpret_cast<const u32x4_t*>(a.X + static_cast<size_t>(n) * a.K + c * kGT + (lane & 7) * 8);
+    }
+  };
+  auto store_x = [&](const u32x4_t (&x)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xs[w][xslot((lane >> 3) + 8 * j, lane & 7)] = x[j];
+  };
+
+  // Lane constants of the 16x32 A fragment.
+  const int r8 = row & 7;
+  const int bt_lane = 4 * (kb >> 1) + 2 * (row >> 3) + (kb & 1);
+  const uint64_t rowmask = (1ull << (8 * r8)) - 1ull;
+
+  // Rebuild this wave's fragments of GroupTile column c, staged in
+  // stage[c&1], into abuf[c&1].
+  auto rebuild = [&](int c) {
+    const int buf = c & 1;
+    const uint8_t* vb = stage[buf];
+    const uint64_t* bb = bbuf[buf];
+    const uint32_t o0 = offtab[c - c_begin];
+    const uint64_t a0 = min(chunk_start<false>(o0), top);
+    const uint32_t delta = chunk_delta<false>(o0, a0);
+    const uint32_t pc = __popcll(bb[lane]);
+    const uint32_t ebase = wave_inclusive_scan(pc) - pc + delta;
+#pragma unroll
+    for (int j = 0; j < T::kFrags; ++j) {
+      const int f = w * T::kFrags + j;
+      const int rs = f >> 1, ks = f & 1;
+      const int bt = 16 * rs + 8 * ks + bt_lane;
+      const uint64_t bm = bb[bt];
+      const uint32_t base = __builtin_amdgcn_ds_bpermute(bt << 2, ebase);
+      const uint32_t rb = base + __popcll(bm & rowmask);
+      const uint32_t byte = static_cast<uint32_t>(bm >> (8 * r8)) & 0xFFu;
+      abuf[buf][f * 64 + lane] = __builtin_bit_cast(u32x4_t, rebuild_row<false>(vb, lut, rb, byte));
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // X^T fragment (ks, nb): lane l holds token 16nb + l%16, k = 32ks + 8(l/16) .. +7.
+  auto mma = [&](int buf) {
+    u32x4_t af[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) af[f] = abuf[buf][f * 64 + lane];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const u32x4_t bf = xs[w][xslot(16 * nb + row, 4 * ks + kb)];
+#pragma unroll
+        for (int rs = 0; rs < 4; ++rs)
+          acc[rs][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, af[rs * 2 + ks]),
+                                                               __builtin_bit_cast(half8_t, bf), acc[rs][nb], 0, 0, 0);
+      }
+  };
+
+  // Pipeline, one barrier per GroupTile column c, loads two columns ahead.
+  // A step issues the loads of X(c+2) and of the values of c+3 into one
+  // register slot, rebuilds tile c+1 (staged in stage[(c+1)&1]) into
+  // abuf[(c+1)&1] while multiplying tile c (abuf[c&1], X(c) in the wave's
+  // LDS region), then moves the other slot, loaded a step earlier, into LDS:
+  // X(c+1) replaces X(c), and the values of c+2 go to stage[c&1], rebuilt in
+  // the step before.  Loads past the last column repeat it.
+  VSlot<kCpt> vs0, vs1;
+  u32x4_t xr0[8], xr1[8];
+  load_x(xr0, c_begin);
+  load_v(vs0, c_begin);
+  commit_v(vs0, c_begin & 1);
+  store_x(xr0);
+  load_v(vs0, min(c_begin + 1, c_last));
+  commit_v(vs0, (c_begin + 1) & 1);
+  load_x(xr1, min(c_begin + 1, c_last));
+  load_v(vs1, min(c_begin + 2, c_last));
+  __syncthreads();
+  rebuild(c_begin);
+  __syncthreads();
+
+  auto step = [&](int c, u32x4_t (&xl)[8], VSlot<kCpt>& vl, const u32x4_t (&xu)[8], const VSlot<kCpt>& vu) {
+    load_x(xl, min(c + 2, c_last));
+    load_v(vl, min(c + 3, c_last));
+    // Keep the loads ahead of the compute they are meant to overlap.
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < c_end) rebuild(c + 1);
+    mma(c & 1);
+    // The wave's own LDS operations run in order: the fragment reads above
+    // see X(c), the stores below replace it with X(c+1).
+    store_x(xu);
+    commit_v(vu, c & 1);
+    __syncthreads();
+  };
+  int c = c_begin;
+  for (; c + 2 <= c_end; c += 2) {
+    step(c, xr0, vs0, xr1, vs1);
+    step(c + 1, xr1, vs1, xr0, vs0);
+  }
+  if (c < c_end) step(c, xr0, vs0, xr1, vs1);
+
+  // Epilogue: lane l of block (rs, nb) holds rows 16rs + 4(l/16) + i and
+  // token 16nb + l%16.
+  auto store_y4 = [&](int n, int m, f32x4_t v) {
+    const size_t yi = static_cast<size_t>(n) * a.M + m;
+    if constexpr (OUT_F16) {
+      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+      half4_t h;
+      h.x = static_cast<_Float16>(v.x);
+      h.y = static_cast<_Float16>(v.y);
+      h.z = static_cast<_Float16>(v.z);
+      h.w = static_cast<_Float16>(v.w);
+      *reinterpret_cast<half4_t*>(reinterpret_cast<_Float16*>(a.Y) + yi) = h;
+    } else {
+      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.Y) + yi) = v;
+    }
+  };
+#pragma unroll
+  for (int rs = 0; rs < 4; ++rs)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = nw + nb * 16 + row;
+      const int m = m0 + rs * 16 + 4 * kb;
+      if (n >= a.N) continue;
+      if (a.splits > 1) {
+        float* p = a.part + (static_cast<size_t>(sidx) * a.N + n) * a.M + m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) __hip_atomic_store(p + i, acc[rs][nb][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        store_y4(n, m, acc[rs][nb]);
+      }
+    }
+  if (a.splits <= 1) return;
+
+  // Split K: the last workgroup of the tile adds the partial sums of all its
+  // splits in split order (device-coherent stores, completed before the
+  // barrier that precedes the counter increment) and resets the counter.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (tid == 0)
+    last_flag = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                static_cast<uint32_t>(a.splits - 1);
+  __syncthreads();
+  if (!last_flag) return;
+  const int n_base = nt * T::kBN;
+  for (int e = tid; e < T::kBN * 16; e += kThreads) {
+    const int n = n_base + (e >> 4);
+    const int m = m0 + 4 * (e & 15);
+    if (n >= a.N) continue;
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < a.splits; ++p) {
+      const float* q = a.part + (static_cast<size_t>(p) * a.N + n) * a.M + m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] += __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    store_y4(n, m, s);
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int64_t kComputeUnits = 256;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+namespace usw {
+
+PrefillPlan prefill_plan(const Geometry& g, int N, int splits_req) {
+  PrefillPlan p;
+  p.waves = N > 256 ? 8 : 4;
+  const int bn = 64 * p.waves;
+  p.ntiles = (N + bn - 1) / bn;
+  const int64_t tiles = g.Gr * p.ntiles;
+  int64_t s = splits_req;
+  if (s <= 0) {
+    // One workgroup per compute unit is resident.  Split K only when the
+    // tiles leave more than half of the compute units idle; each split keeps
+    // at least 16 GroupTile columns.
+    s = 1;
+    if (tiles * 2 <= kComputeUnits) s = std::min<int64_t>((kComputeUnits + tiles - 1) / tiles, std::max<int64_t>(1, g.Gc / 16));
+  }
+  const int64_t smin = (g.Gc + kMaxCols - 1) / kMaxCols;
+  p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min<int64_t>(s, g.Gc))));
+  return p;
+}
+
+size_t prefill_counter_bytes(const Geometry& g, const PrefillPlan& p) {
+  return p.splits > 1 ? align256(static_cast<size_t>(4) * g.Gr * p.ntiles) : 0;
+}
+
+size_t prefill_workspace_bytes(const Geometry& g, int N, const PrefillPlan& p) {
+  if (p.splits <= 1) return 0;
+  return prefill_counter_bytes(g, p) + static_cast<size_t>(p.splits) * N * g.M * sizeof(float);
+}
+
+usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X, void* Y, bool f16out, int N, void* ws,
+                          const PrefillPlan& p, void* stream) {
+  PArgs a;
+  a.bitmaps = f->bitmaps;
+  a.offsets = f->offsets;
+  a.values = static_cast<const uint8_t*>(f->values);
+  a.X = X;
+  a.Y = Y;
+  const size_t cbytes = prefill_counter_bytes(g, p);
+  a.counters = p.splits > 1 ? static_cast<uint32_t*>(ws) : nullptr;
+  a.part = p.splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + cbytes) : nullptr;
+  a.values_alloc = values_alloc_bytes(f->val_type, f->nnz);
+  a.M = static_cast<int>(g.M);
+  a.K = static_cast<int>(g.K);
+  a.N = N;
+  a.Gc = static_cast<int>(g.Gc);
+  a.splits = p.splits;
+  a.ntiles = p.ntiles;
+  const int64_t nblk = g.Gr * p.ntiles * p.splits;
+  a.remap = nblk % 8 == 0 ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(nblk));
+  if (p.waves == 8) {
+    if (f16out) prefill_kernel<8, true><<<grid, 512, 0, s>>>(a);
+    else prefill_kernel<8, false><<<grid, 512, 0, s>>>(a);
+  } else {
+    if (f16out) prefill_kernel<4, true><<<grid, 256, 0, s>>>(a);
+    else prefill_kernel<4, false><<<grid, 256, 0, s>>>(a);
+  }
+  return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
+}
+
+}  // namespace usw
