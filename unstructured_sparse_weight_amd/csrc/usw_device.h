@@ -91,24 +91,25 @@ __device__ __forceinline__ uint32_t nibble_byte_selector(uint32_t q) {
 }
 
 // Two dwords holding packed fp16 values e, e+1, e+2, e+3 of an LDS buffer
-// (element e starts at byte 2e; the buffer is dword aligned).
+// (element e starts at byte 2e; the buffer is dword aligned).  v_alignbyte
+// uses only the low two bits of its shift operand.
 __device__ __forceinline__ u32x2_t lds_window_f16(const uint8_t* buf, uint32_t e) {
   const uint32_t ba = 2u * e;
   const uint32_t* p = reinterpret_cast<const uint32_t*>(buf + (ba & ~3u));
   const uint32_t d0 = p[0], d1 = p[1], d2 = p[2];
   u32x2_t w;
-  w.x = __builtin_amdgcn_alignbyte(d1, d0, ba & 3u);
-  w.y = __builtin_amdgcn_alignbyte(d2, d1, ba & 3u);
+  w.x = __builtin_amdgcn_alignbyte(d1, d0, ba);
+  w.y = __builtin_amdgcn_alignbyte(d2, d1, ba);
   return w;
 }
 
 // 8 packed nibbles starting at nibble e of an LDS buffer, split into the
-// even (lo4) and odd (hi4) nibbles, one per byte.
+// even (lo4) and odd (hi4) nibbles, one per byte.  v_alignbit uses only the
+// low five bits of its shift operand, here 4 * (e mod 8).
 __device__ __forceinline__ u32x2_t lds_window_i4(const uint8_t* buf, uint32_t e) {
   const uint32_t ba = e >> 1;
   const uint32_t* p = reinterpret_cast<const uint32_t*>(buf + (ba & ~3u));
-  const uint32_t sh = ((ba & 3u) << 3) | ((e & 1u) << 2);
-  const uint32_t win = __builtin_amdgcn_alignbit(p[1], p[0], sh);
+  const uint32_t win = __builtin_amdgcn_alignbit(p[1], p[0], e << 2);
   u32x2_t r;
   r.x = win & 0x0F0F0F0Fu;
   r.y = (win >> 4) & 0x0F0F0F0Fu;

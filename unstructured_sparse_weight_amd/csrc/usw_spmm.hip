@@ -134,27 +134,74 @@ __device__ __forceinline__ void slot_commit(const Slot<NB, I4>& s, uint8_t* vb, 
   reinterpret_cast<u32x4_t*>(bb)[lane & 31] = s.bm;
 }
 
-// Rebuild and multiply TCTile rows RS0 .. RS0+RSN-1 of a GroupTile whose
-// bitmaps are in bb and whose values are in vb; ebase (lane i) is where
-// BitmapTile i's values start in vb.
-template <int NB, bool I4, int RS0, int RSN>
-__device__ __forceinline__ void tile_rows(const u32x4_t (&x)[2][NB], const uint8_t* vb, const uint64_t* bb,
-                                          const uint32_t* lut, f32x4_t (&acc)[4][NB], uint32_t ebase, int bt_lane,
-                                          int r8, uint64_t rowmask) {
+// Which rows a lane rebuilds.  The A fragments of a GroupTile come in two
+// halves H (BitmapTile rows 4H .. 4H+3 of the GroupTile, i.e. TCTile rows 2H
+// and 2H+1, whose values are contiguous in the stream).  In fragment
+// (H, jj, ks), lane l with i = l % 16 and g = l / 16 holds row 4jj + i/4 of
+// the BitmapTile in BitmapTile row R = 4H + i%4 and BitmapTile column
+// C = 4ks + g, i.e. columns 8C .. 8C+7: the k layout of the fragment is the
+// usual one, and D row i of the fragment is row 8R + 4jj + i/4 of the strip.
+// A lane thus rebuilds rows r and r + 4 (r = i/4) of 4 BitmapTiles per
+// GroupTile, reading each bitmap once.
+struct LaneMap {
+  int bt[2][2];      // [H][ks]: the lane's BitmapTile, in storage order
+  uint32_t sh;       // 8r: bit offset of row r in a bitmap word
+  uint32_t pmask;    // bits of rows 0 .. r-1
+};
+
+__device__ __forceinline__ LaneMap lane_map(int lane) {
+  LaneMap m;
+  const int i = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int rs = RS0; rs < RS0 + RSN; ++rs) {
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int bt = 16 * rs + 8 * ks + bt_lane;
-      const uint64_t bm = bb[bt];
-      const uint32_t base = __builtin_amdgcn_ds_bpermute(bt << 2, ebase);
-      const uint32_t rb = base + __popcll(bm & rowmask);
-      const uint32_t byte = static_cast<uint32_t>(bm >> (8 * r8)) & 0xFFu;
-      const half8_t ah = rebuild_row<I4>(vb, lut, rb, byte);
+      const int R = 4 * h + (i & 3), C = 4 * ks + g;
+      // TCTiles row-major (4 per row), BitmapTiles row-major inside a TCTile.
+      m.bt[h][ks] = 16 * (R >> 1) + 4 * (C >> 1) + 2 * (R & 1) + (C & 1);
+    }
+  m.sh = 8u * static_cast<uint32_t>(i >> 2);
+  m.pmask = (1u << m.sh) - 1u;
+  return m;
+}
+
+// Row of the strip that accumulator acc[j] (j = 2H + jj) holds at D row i,
+// and its inverse (used by the workgroup reduction); checked at compile time.
+constexpr int strip_row(int j, int i) { return 32 * (j >> 1) + 8 * (i & 3) + 4 * (j & 1) + (i >> 2); }
+constexpr int acc_of_row(int ml) { return 2 * (ml >> 5) + ((ml >> 2) & 1); }
+constexpr int drow_of_row(int ml) { return 4 * (ml & 3) + ((ml >> 3) & 3); }
+constexpr bool strip_map_is_inverse() {
+  for (int ml = 0; ml < 64; ++ml)
+    if (strip_row(acc_of_row(ml), drow_of_row(ml)) != ml) return false;
+  return true;
+}
+static_assert(strip_map_is_inverse(), "row map of the A fragments");
+
+// Rebuild and multiply half H of a GroupTile whose bitmaps are in bb and
+// whose values are in the LDS buffer at vbase; ebase (lane t) is where
+// BitmapTile t's values start, counted from vbase.
+template <int NB, bool I4, int H>
+__device__ __forceinline__ void tile_half(const u32x4_t (&x)[2][NB], const uint8_t* vbase, const uint64_t* bb,
+                                          const uint32_t* lut, f32x4_t (&acc)[4][NB], uint32_t ebase,
+                                          const LaneMap& lm) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[rs][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(half8_t, x[ks][nb]),
-                                                             acc[rs][nb], 0, 0, 0);
+  for (int ks = 0; ks < 2; ++ks) {
+    const int bt = lm.bt[H][ks];
+    const uint64_t bm = bb[bt];
+    const uint32_t lo = static_cast<uint32_t>(bm), hi = static_cast<uint32_t>(bm >> 32);
+    const uint32_t base = __builtin_amdgcn_ds_bpermute(bt << 2, ebase);
+    // Row r starts after the set bits of rows 0 .. r-1; row r + 4 after
+    // those of rows 0 .. r+3 (the 32 bits from bit 8r on cover rows r .. r+3).
+    const uint32_t rb0 = base + __builtin_popcount(lo & lm.pmask);
+    const uint32_t rb1 = rb0 + __builtin_popcount(__builtin_amdgcn_alignbit(hi, lo, lm.sh));
+    const half8_t a0 = rebuild_row<I4>(vbase, lut, rb0, (lo >> lm.sh) & 0xFFu);
+    const half8_t a1 = rebuild_row<I4>(vbase, lut, rb1, (hi >> lm.sh) & 0xFFu);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      acc[2 * H][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, __builtin_bit_cast(half8_t, x[ks][nb]),
+                                                              acc[2 * H][nb], 0, 0, 0);
+      acc[2 * H + 1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, __builtin_bit_cast(half8_t, x[ks][nb]),
+                                                                  acc[2 * H + 1][nb], 0, 0, 0);
     }
   }
 }
@@ -220,12 +267,7 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * q / parts);
   const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (q + 1) / parts);
 
-  // Lane constants of the 16x32 A fragment.
-  const int row = lane & 15;               // row inside the 16-row slice
-  const int kb = lane >> 4;                // which 8-column group of the 32
-  const int r8 = row & 7;                  // row inside the BitmapTile
-  const int bt_lane = 4 * (kb >> 1) + 2 * (row >> 3) + (kb & 1);  // BitmapTile among the 8 of a fragment
-  const uint64_t rowmask = (1ull << (8 * r8)) - 1ull;
+  const LaneMap lm = lane_map(lane);
 
   f32x4_t acc[4][NB];
 #pragma unroll
@@ -234,6 +276,9 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   uint8_t* vb = smem + w * VT::kVbuf;
+  // The rebuild addresses the wave's value buffer from smem: its offset, in
+  // value elements, is folded into the BitmapTile bases.
+  const uint32_t vb_elems = I4 ? static_cast<uint32_t>(w * VT::kVbuf * 2) : static_cast<uint32_t>(w * VT::kVbuf / 2);
   uint64_t* bb = reinterpret_cast<uint64_t*>(smem + kW * VT::kVbuf) + w * kBtPerGt;
 
   // The wave's GroupTile offsets, one per lane: lane i holds
@@ -276,11 +321,11 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
           const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
           for (uint32_t ch = lane; ch < nch; ch += 64) reinterpret_cast<u32x4_t*>(vb)[ch] = src[min(ch, last)];
           wave_sync();
-          const uint32_t ebase = excl - (h ? mid : 0u) + delta;
+          const uint32_t ebase = excl - (h ? mid : 0u) + delta + vb_elems;
           if (h == 0)
-            tile_rows<NB, I4, 0, 2>(s0.x, vb, bb, lut, acc, ebase, bt_lane, r8, rowmask);
+            tile_half<NB, I4, 0>(s0.x, smem, bb, lut, acc, ebase, lm);
           else
-            tile_rows<NB, I4, 2, 2>(s0.x, vb, bb, lut, acc, ebase, bt_lane, r8, rowmask);
+            tile_half<NB, I4, 1>(s0.x, smem, bb, lut, acc, ebase, lm);
           wave_sync();
         }
       }
@@ -302,7 +347,11 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
       load(nxt, c + 2);
       slot_commit(cur, vb, bb, lane);
       wave_sync();
-      tile_rows<NB, I4, 0, 4>(cur.x, vb, bb, lut, acc, bitmap_prefix(bb, lane) + cur.delta, bt_lane, r8, rowmask);
+      {
+        const uint32_t ebase = bitmap_prefix(bb, lane) + cur.delta + vb_elems;
+        tile_half<NB, I4, 0>(cur.x, smem, bb, lut, acc, ebase, lm);
+        tile_half<NB, I4, 1>(cur.x, smem, bb, lut, acc, ebase, lm);
+      }
       wave_sync();
     };
     int c = c_begin;
@@ -326,7 +375,11 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
       load(nxt, c + 1);
       slot_commit(cur, vb, bb, lane);
       wave_sync();
-      tile_rows<NB, I4, 0, 4>(cur.x, vb, bb, lut, acc, bitmap_prefix(bb, lane) + cur.delta, bt_lane, r8, rowmask);
+      {
+        const uint32_t ebase = bitmap_prefix(bb, lane) + cur.delta + vb_elems;
+        tile_half<NB, I4, 0>(cur.x, smem, bb, lut, acc, ebase, lm);
+        tile_half<NB, I4, 1>(cur.x, smem, bb, lut, acc, ebase, lm);
+      }
       wave_sync();
     };
     int c = c_begin;
@@ -360,9 +413,12 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
     const int n = e >> 6;
     const int ml = e & 63;
     if (n >= a.N) continue;
-    const int rs = ml >> 4, r16 = ml & 15;
-    const int ln = ((r16 >> 2) << 4) | (n & 15);
-    const int i = r16 & 3;
+    // Strip row ml sits in accumulator acc_of_row(ml) at D row
+    // drow_of_row(ml) = 4 * (lane / 16) + i.
+    const int rs = acc_of_row(ml);
+    const int dr = drow_of_row(ml);
+    const int ln = ((dr >> 2) << 4) | (n & 15);
+    const int i = dr & 3;
     const int nb = n >> 4;
     float sum = 0.f;
 #pragma unroll
@@ -413,6 +469,9 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
 // tuning build (-DUSW_TUNING) also compiles the others and picks one from
 // the USW_DECODE_CFG environment variable.
 using DefaultCfg = Cfg<4, 1, 4>;
+// 17..32 columns of N: twice the accumulators and X fragments, which do not
+// fit 128 registers; three waves per SIMD leave room for them.
+using DefaultCfg2 = Cfg<4, 1, 3>;
 #ifdef USW_TUNING
 using TuneCfg1 = Cfg<4, 1, 3>;
 using TuneCfg2 = Cfg<4, 2, 3>;
@@ -434,7 +493,7 @@ struct CfgInfo {
   int occ;     // waves per SIMD the configuration allows
 };
 
-CfgInfo cfg_info(int cfg) {
+CfgInfo cfg_info(int cfg, bool two) {
   switch (cfg) {
 #ifdef USW_TUNING
     case 1: return {TuneCfg1::kWavesPerGroup, TuneCfg1::kOcc};
@@ -443,7 +502,9 @@ CfgInfo cfg_info(int cfg) {
     case 4: return {TuneCfg4::kWavesPerGroup, TuneCfg4::kOcc};
     case 5: return {TuneCfg5::kWavesPerGroup, TuneCfg5::kOcc};
 #endif
-    default: return {DefaultCfg::kWavesPerGroup, DefaultCfg::kOcc};
+    default:
+      return two ? CfgInfo{DefaultCfg2::kWavesPerGroup, DefaultCfg2::kOcc}
+                 : CfgInfo{DefaultCfg::kWavesPerGroup, DefaultCfg::kOcc};
   }
 }
 
@@ -464,7 +525,7 @@ Plan make_plan(const usw::Geometry& g, int N, int splits_req) {
   Plan p;
   p.nchunk = N <= 16 ? 16 : 32;
   p.cfg = choose_cfg();
-  const CfgInfo ci = cfg_info(p.cfg);
+  const CfgInfo ci = cfg_info(p.cfg, N > 16);
   p.waves = ci.waves;
   int64_t s = splits_req;
   if (s <= 0) {
@@ -524,7 +585,12 @@ void launch_decode(const Args& a, bool f16out, dim3 grid, hipStream_t s, int cfg
     case 4: launch_cfg<NB, I4, TuneCfg4>(a, f16out, grid, s); return;
     case 5: launch_cfg<NB, I4, TuneCfg5>(a, f16out, grid, s); return;
 #endif
-    default: launch_cfg<NB, I4, DefaultCfg>(a, f16out, grid, s); return;
+    default:
+      if constexpr (NB == 2)
+        launch_cfg<NB, I4, DefaultCfg2>(a, f16out, grid, s);
+      else
+        launch_cfg<NB, I4, DefaultCfg>(a, f16out, grid, s);
+      return;
   }
 }
 
