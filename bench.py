@@ -24,8 +24,11 @@ import os
 import sys
 import time
 
+import hashlib
+
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "effective TFLOP/s + HBM GB/s, bitmap SpMM M=20480 K=5120 s=50% N=16"
@@ -52,8 +55,69 @@ def parse():
     p.add_argument("--N", type=int, default=16)
     p.add_argument("--sparsity", type=float, default=0.5)
     p.add_argument("--dtype", default="f16", choices=["f16", "i4"])
-    p.add_argument("--cpu-reps", type=int, default=3)
+    p.add_argument("--cpu-reps", type=int, default=5)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain device copy of known size (for scaling the FETCH_SIZE and WRITE_SIZE counters)")
     return p.parse_args()
+
+
+# Sources that make up each kernel: a measured traffic figure is only used
+# while they are unchanged.
+KERNEL_SOURCES = {
+    "decode": ["unstructured_sparse_weight_amd/csrc/usw_spmm.hip", "unstructured_sparse_weight_amd/csrc/usw_device.h"],
+    "prefill": ["unstructured_sparse_weight_amd/csrc/usw_prefill.hip", "unstructured_sparse_weight_amd/csrc/usw_device.h"],
+}
+
+
+def kernel_hash(kind):
+    """Hash of the kernel's code: its sources without // comments and blank
+    lines, so that comment edits do not invalidate a measurement."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, kind):
+    """HBM bytes per launch from profiles/traffic_<name>.md (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's readings), or None when there is no
+    such summary or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_sources_sha256_16") != kernel_hash(kind):
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(args):
+    """A plain copy of 1 GiB (read 1 GiB, write 1 GiB), rotating over two
+    buffer pairs so that it streams from HBM."""
+    import torch
+    n = 1 << 30
+    dev = torch.device("cuda:0")
+    bufs = [(torch.ones(n, dtype=torch.uint8, device=dev), torch.empty(n, dtype=torch.uint8, device=dev))
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        src, dst = bufs[i % 2]
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "launches": args.steps}), flush=True)
 
 
 def log(*a):
@@ -74,6 +138,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args)
+        return
     dev = torch.device("cuda:0")
     M, K, N, s = args.M, args.K, args.N, args.sparsity
     prefill = args.dtype == "f16" and N > 32
@@ -185,6 +252,9 @@ def main():
         workload = f"llama7b_prefill_{M}x{K}_s{s}_N{N}"
     else:
         workload = f"spmm_{M}x{K}_s{s}_N{N}"
+    if args.splits == 0:
+        roofline["traffic"] = measured_traffic(f"{kname}_{workload}", "prefill" if prefill else "decode")
+    roofline["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     out = {
         "metric": METRIC if (M, K, N, s, args.dtype) == (20480, 5120, 16, 0.5, "f16") else
         f"effective TFLOP/s + HBM GB/s, bitmap SpMM M={M} K={K} s={int(s * 100)}% N={N} {args.dtype}",

@@ -11,25 +11,29 @@
 //     of GroupTile columns; each of its waves streams its own contiguous run
 //     of GroupTiles (bitmaps and values of consecutive GroupTiles of a strip
 //     are contiguous in memory), so the main loop has no workgroup barrier.
-//   * Loads run two GroupTiles ahead of the compute: the 16-byte global loads
-//     of GroupTiles c+1 and c+2 (bitmaps, the value range [offsets[g],
-//     offsets[g+1]) from a 16-byte aligned start, and the X^T fragments) sit
-//     in registers while GroupTile c, already copied into the wave's private
-//     LDS buffer, is rebuilt and multiplied.
-//   * Rebuild: v_mfma_f32_16x16x32_f16 gives lane l the row l%16 and the 8
-//     consecutive columns 8*(l/16)..+7 of a 16x32 block, which is exactly one
-//     row of one BitmapTile; its kept values are contiguous in the stream.
-//     The lane finds where they start (GroupTile offset + popcounts of the
-//     earlier BitmapTiles, from a DPP wave prefix scan, + popcount of the
-//     earlier rows of its own BitmapTile) and expands them into 8 slots with
-//     two aligned LDS windows and v_perm_b32 byte selectors looked up by the
-//     row's 8-bit mask (zero for clear bits).
-//   * The rebuilt 16x32 fragment meets the X^T fragment (X is [N][K], so each
+//   * Loads run one GroupTile ahead of the compute: the 16-byte global loads
+//     of GroupTile c+1 (bitmaps, the value range [offsets[g], offsets[g+1])
+//     from a 16-byte aligned start, and the X^T fragments) sit in registers
+//     while GroupTile c, already copied into the wave's private LDS buffer,
+//     is rebuilt and multiplied.  Every load is issued unconditionally
+//     (clamped indices), so the compiler waits for exactly the slot in use.
+//   * Rebuild: v_mfma_f32_16x16x32_f16 gives lane l 8 consecutive columns
+//     8*(l/16)..+7 of one row of a 16x32 block, which is exactly one row of
+//     one BitmapTile; its kept values are contiguous in the stream.  Rows are
+//     assigned so that a lane rebuilds rows r and r+4 of four BitmapTiles
+//     per GroupTile.  The lane finds where a row's values start (GroupTile
+//     offset + popcounts of the earlier BitmapTiles, from a DPP wave prefix
+//     scan, + popcount of the earlier rows of its own BitmapTile) and expands
+//     them into 8 slots with two aligned LDS windows and v_perm_b32 byte
+//     selectors looked up by the row's 4-bit halves (zero for clear bits).
+//   * The rebuilt fragment meets the X^T fragment (X is [N][K], so each
 //     lane's 8 k values are one 16-byte load) on the matrix cores with fp32
 //     accumulation, which leaves the vector ALUs to the rebuild.
 //   * Partial sums of the waves of a workgroup are added in LDS in a fixed
-//     order; across workgroups (split K) they go through an fp32 workspace and
-//     a second kernel adds them in a fixed order: results are deterministic.
+//     order.  Split K (several workgroups per strip): each writes its sums to
+//     an fp32 workspace with device-coherent stores and the last workgroup of
+//     the strip, found with a per-strip counter, adds them in split order, so
+//     results do not depend on scheduling.
 
 #include <hip/hip_runtime.h>
 
