@@ -9,9 +9,11 @@
 // Design (gfx950, wave64):
 //   * A workgroup owns one 64-row strip of GroupTiles and 64 tokens per wave
 //     (256 or 512 tokens), and walks a range of GroupTile columns.
-//   * Per GroupTile the workgroup stages the bitmaps and the value range
-//     [offsets[g], offsets[g+1]) in LDS with 16-byte loads issued one
-//     GroupTile ahead; each wave rebuilds 8 / waves of the 8 A fragments
+//   * Per GroupTile the workgroup stages the value range [offsets[g],
+//     offsets[g+1]) in LDS with 16-byte loads issued ahead; the bitmap
+//     words stay in registers, where each wave derives the BitmapTile bases
+//     of its fragments a step before the rebuild.  Each wave rebuilds 8 /
+//     waves of the 8 A fragments
 //     (16 rows x 32 columns each; lane l holds row l%16, columns
 //     8*(l/16)..+7, i.e. one row of one BitmapTile) by masked popcount and
 //     writes them to a double-buffered LDS tile that every wave reads.
@@ -65,7 +67,17 @@ struct PTraits {
 template <int CPT>
 struct VSlot {
   u32x4_t v[CPT];
-  u32x4_t bm;
+  u32x2_t bm;       // lane t: bitmap word t of the GroupTile
+};
+
+// What a lane needs from a GroupTile's bitmaps to rebuild its fragments:
+// the value base and the bitmap word of each of its BitmapTiles.  Computed
+// from the slot's registers when the GroupTile is copied into LDS, a step
+// before its rebuild, so the rebuild itself waits on one LDS round trip.
+template <int FRAGS>
+struct RbIn {
+  uint32_t base[FRAGS];
+  uint32_t lo[FRAGS], hi[FRAGS];
 };
 
 template <int WAVES, bool OUT_F16>
@@ -75,7 +87,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a)
   constexpr int kCpt = T::kCpt;
 
   __shared__ __attribute__((aligned(16))) uint8_t stage[2][T::kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint64_t bbuf[2][kBtPerGt];
   __shared__ __attribute__((aligned(16))) u32x4_t abuf[2][8 * 64];   // two rebuilt 64x64 tiles, fragment order
   __shared__ __attribute__((aligned(16))) u32x4_t xs[WAVES][64 * 8];   // per wave: its 64 tokens x 64 k of X
   __shared__ __attribute__((aligned(16))) uint32_t lut[32];
@@ -120,13 +131,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a)
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
 #pragma unroll
     for (int i = 0; i < kCpt; ++i) s.v[i] = src[min(static_cast<uint32_t>(tid + kThreads * i), last)];
-    s.bm = reinterpret_cast<const u32x4_t*>(a.bitmaps + (g_row + c) * kBtPerGt)[tid & 31];
+    s.bm = reinterpret_cast<const u32x2_t*>(a.bitmaps + (g_row + c) * kBtPerGt)[lane];
   };
   auto commit_v = [&](const VSlot<kCpt>& s, int buf) {
 #pragma unroll
     for (int i = 0; i < kCpt; ++i) reinterpret_cast<u32x4_t*>(stage[buf])[tid + kThreads * i] = s.v[i];
-    // Wave 0 stores the bitmaps (its two half-waves hold the same 512 B).
-    if (w == 0) reinterpret_cast<u32x4_t*>(bbuf[buf])[lane & 31] = s.bm;
   };
 
   // X for this wave's 64 tokens and GroupTile column c: 64 rows of 128 B,
@@ -154,25 +163,37 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a)
   const int bt_lane = 4 * (kb >> 1) + 2 * (row >> 3) + (kb & 1);
   const uint64_t rowmask = (1ull << (8 * r8)) - 1ull;
 
-  // Rebuild this wave's fragments of GroupTile column c, staged in
-  // stage[c&1], into abuf[c&1].
-  auto rebuild = [&](int c) {
-    const int buf = c & 1;
-    const uint8_t* vb = stage[buf];
-    const uint64_t* bb = bbuf[buf];
+  // Rebuild inputs of GroupTile column c from its slot: DPP prefix scan of
+  // the BitmapTile popcounts (lane t <-> BitmapTile t, plus the value
+  // elements before the GroupTile's first one in its first chunk), then each
+  // fragment's BitmapTile base and bitmap word via ds_bpermute.
+  auto prep = [&](const VSlot<kCpt>& s, int c) {
+    RbIn<T::kFrags> in;
     const uint32_t o0 = offtab[c - c_begin];
     const uint64_t a0 = min(chunk_start<false>(o0), top);
-    const uint32_t delta = chunk_delta<false>(o0, a0);
-    const uint32_t pc = __popcll(bb[lane]);
-    const uint32_t ebase = wave_inclusive_scan(pc) - pc + delta;
+    const uint32_t pc = __builtin_popcount(s.bm.x) + __builtin_popcount(s.bm.y);
+    const uint32_t ebase = wave_inclusive_scan(pc) - pc + chunk_delta<false>(o0, a0);
 #pragma unroll
     for (int j = 0; j < T::kFrags; ++j) {
       const int f = w * T::kFrags + j;
-      const int rs = f >> 1, ks = f & 1;
-      const int bt = 16 * rs + 8 * ks + bt_lane;
-      const uint64_t bm = bb[bt];
-      const uint32_t base = __builtin_amdgcn_ds_bpermute(bt << 2, ebase);
-      const uint32_t rb = base + __popcll(bm & rowmask);
+      const int bt = 16 * (f >> 1) + 8 * (f & 1) + bt_lane;
+      in.base[j] = __builtin_amdgcn_ds_bpermute(bt << 2, ebase);
+      in.lo[j] = __builtin_amdgcn_ds_bpermute(bt << 2, s.bm.x);
+      in.hi[j] = __builtin_amdgcn_ds_bpermute(bt << 2, s.bm.y);
+    }
+    return in;
+  };
+
+  // Rebuild this wave's fragments of GroupTile column c, staged in
+  // stage[c&1], into abuf[c&1].
+  auto rebuild = [&](int c, const RbIn<T::kFrags>& in) {
+    const int buf = c & 1;
+    const uint8_t* vb = stage[buf];
+#pragma unroll
+    for (int j = 0; j < T::kFrags; ++j) {
+      const int f = w * T::kFrags + j;
+      const uint64_t bm = (static_cast<uint64_t>(in.hi[j]) << 32) | in.lo[j];
+      const uint32_t rb = in.base[j] + __popcll(bm & rowmask);
       const uint32_t byte = static_cast<uint32_t>(bm >> (8 * r8)) & 0xFFu;
       abuf[buf][f * 64 + lane] = __builtin_bit_cast(u32x4_t, rebuild_row<false>(vb, lut, rb, byte));
     }
@@ -213,26 +234,30 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a)
   load_x(xr0, c_begin);
   load_v(vs0, c_begin);
   commit_v(vs0, c_begin & 1);
-  store_x(xr0);
+  const RbIn<T::kFrags> rin0 = prep(vs0, c_begin);
   load_v(vs0, min(c_begin + 1, c_last));
   commit_v(vs0, (c_begin + 1) & 1);
+  RbIn<T::kFrags> rin = prep(vs0, min(c_begin + 1, c_last));
+  store_x(xr0);
   load_x(xr1, min(c_begin + 1, c_last));
   load_v(vs1, min(c_begin + 2, c_last));
   __syncthreads();
-  rebuild(c_begin);
+  rebuild(c_begin, rin0);
   __syncthreads();
 
+  // rin holds the rebuild inputs of column c+1 when step c starts.
   auto step = [&](int c, u32x4_t (&xl)[8], VSlot<kCpt>& vl, const u32x4_t (&xu)[8], const VSlot<kCpt>& vu) {
     load_x(xl, min(c + 2, c_last));
     load_v(vl, min(c + 3, c_last));
     // Keep the loads ahead of the compute they are meant to overlap.
     __builtin_amdgcn_sched_barrier(0);
-    if (c + 1 < c_end) rebuild(c + 1);
+    if (c + 1 < c_end) rebuild(c + 1, rin);
     mma(c & 1);
     // The wave's own LDS operations run in order: the fragment reads above
     // see X(c), the stores below replace it with X(c+1).
     store_x(xu);
     commit_v(vu, c & 1);
+    rin = prep(vu, min(c + 2, c_last));
     __syncthreads();
   };
   int c = c_begin;

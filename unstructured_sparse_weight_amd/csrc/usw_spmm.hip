@@ -78,7 +78,7 @@ static_assert(ValTraits<true>::kVbuf >= 1024 * ValTraits<true>::kChunks, "uncond
 template <int NB, bool I4>
 struct Slot {
   u32x4_t v[ValTraits<I4>::kChunks];
-  u32x4_t bm;
+  u32x2_t bm;       // lane t: bitmap word t of the GroupTile
   u32x4_t x[2][NB];
   uint32_t nch;     // 16-byte chunks of values spanned (wave-uniform)
   uint32_t delta;   // value elements before the GroupTile's first one in its first chunk
@@ -117,7 +117,7 @@ __device__ __forceinline__ void slot_load(Slot<NB, I4>& s, const Args& a, int gi
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + s.a0);
 #pragma unroll
   for (int i = 0; i < ValTraits<I4>::kChunks; ++i) s.v[i] = src[min(static_cast<uint32_t>(lane + 64 * i), last)];
-  s.bm = reinterpret_cast<const u32x4_t*>(a.bitmaps + g * kBtPerGt)[lane & 31];
+  s.bm = reinterpret_cast<const u32x2_t*>(a.bitmaps + g * kBtPerGt)[lane];
   // X^T fragments.  Columns n >= N of B only feed columns n >= N of the
   // product, which are never stored, so those lanes just repeat row N-1.
   const int row = lane & 15, kb = lane >> 4;
@@ -130,12 +130,11 @@ __device__ __forceinline__ void slot_load(Slot<NB, I4>& s, const Args& a, int gi
     }
 }
 
-template <int NB, bool I4>
+template <int NB, bool I4, bool BITMAPS = false>
 __device__ __forceinline__ void slot_commit(const Slot<NB, I4>& s, uint8_t* vb, uint64_t* bb, int lane) {
 #pragma unroll
   for (int i = 0; i < ValTraits<I4>::kChunks; ++i) reinterpret_cast<u32x4_t*>(vb)[lane + 64 * i] = s.v[i];
-  // Both half-waves hold the same 512 B of bitmaps and store them alike.
-  reinterpret_cast<u32x4_t*>(bb)[lane & 31] = s.bm;
+  if constexpr (BITMAPS) reinterpret_cast<u32x2_t*>(bb)[lane] = s.bm;
 }
 
 // Which rows a lane rebuilds.  The A fragments of a GroupTile come in two
@@ -210,10 +209,63 @@ __device__ __forceinline__ void tile_half(const u32x4_t (&x)[2][NB], const uint8
   }
 }
 
+// What a lane needs from a GroupTile's bitmaps: the bitmap words and value
+// bases of its four BitmapTiles, taken with ds_bpermute from the slot's
+// registers (lane t holds bitmap word t; ebase lane t is where BitmapTile t's
+// values start).  Nothing here waits for the slot's copy into LDS.
+struct RowsIn {
+  uint32_t lo[2][2], hi[2][2], base[2][2];
+};
+
+__device__ __forceinline__ RowsIn rows_in(u32x2_t bm, uint32_t ebase, const LaneMap& lm) {
+  RowsIn r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int addr = lm.bt[h][ks] << 2;
+      r.lo[h][ks] = __builtin_amdgcn_ds_bpermute(addr, bm.x);
+      r.hi[h][ks] = __builtin_amdgcn_ds_bpermute(addr, bm.y);
+      r.base[h][ks] = __builtin_amdgcn_ds_bpermute(addr, ebase);
+    }
+  return r;
+}
+
+// Rebuild and multiply a whole GroupTile (both halves) whose values are in
+// the LDS buffer at vbase.
+template <int NB, bool I4>
+__device__ __forceinline__ void tile_full(const u32x4_t (&x)[2][NB], const uint8_t* vbase, const RowsIn& in,
+                                          const uint32_t* lut, f32x4_t (&acc)[4][NB], const LaneMap& lm) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t lo = in.lo[h][ks], hi = in.hi[h][ks];
+      const uint32_t rb0 = in.base[h][ks] + __builtin_popcount(lo & lm.pmask);
+      const uint32_t rb1 = rb0 + __builtin_popcount(__builtin_amdgcn_alignbit(hi, lo, lm.sh));
+      const half8_t a0 = rebuild_row<I4>(vbase, lut, rb0, (lo >> lm.sh) & 0xFFu);
+      const half8_t a1 = rebuild_row<I4>(vbase, lut, rb1, (hi >> lm.sh) & 0xFFu);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        acc[2 * h][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, __builtin_bit_cast(half8_t, x[ks][nb]),
+                                                                acc[2 * h][nb], 0, 0, 0);
+        acc[2 * h + 1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, __builtin_bit_cast(half8_t, x[ks][nb]),
+                                                                    acc[2 * h + 1][nb], 0, 0, 0);
+      }
+    }
+}
+
 // Exclusive prefix of the BitmapTile popcounts of the GroupTile in bb
 // (lane i <-> BitmapTile i).
 __device__ __forceinline__ uint32_t bitmap_prefix(const uint64_t* bb, int lane) {
   const uint32_t pc = __popcll(bb[lane]);
+  return wave_inclusive_scan(pc) - pc;
+}
+
+// The same from the slot's registers (lane t holds bitmap word t), which
+// keeps an LDS round trip out of the chain that leads to the rebuild.
+__device__ __forceinline__ uint32_t bitmap_prefix_reg(u32x2_t bm) {
+  const uint32_t pc = __builtin_popcount(bm.x) + __builtin_popcount(bm.y);
   return wave_inclusive_scan(pc) - pc;
 }
 
@@ -310,7 +362,7 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
         const uint32_t o0 = off_at(c), o1 = off_at(c + 1);
         Slot<NB, I4> s0;
         slot_load(s0, a, gi, c, lane, o0, o1);
-        reinterpret_cast<u32x4_t*>(bb)[lane & 31] = s0.bm;
+        reinterpret_cast<u32x2_t*>(bb)[lane] = s0.bm;
         wave_sync();
         const uint32_t excl = bitmap_prefix(bb, lane);
         const uint32_t mid = __builtin_amdgcn_readlane(excl, 32);
@@ -334,6 +386,59 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
         }
       }
     }
+  } else if constexpr (C::kDepth == 0) {
+    // One register slot: GroupTile c is copied into LDS, then the loads of
+    // c+1 are issued into the same registers while c is rebuilt and
+    // multiplied.  Fewer registers, more waves per SIMD.
+    const int c_last = c_end - 1;
+    Slot<NB, I4> s0;
+    slot_load(s0, a, gi, c_begin, lane, off_at(c_begin), off_at(c_begin + 1));
+    for (int c = c_begin; c < c_end; ++c) {
+      const RowsIn rin = rows_in(s0.bm, bitmap_prefix_reg(s0.bm) + s0.delta + vb_elems, lm);
+      slot_commit(s0, vb, bb, lane);
+      u32x4_t xc[2][NB];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) xc[ks][nb] = s0.x[ks][nb];
+      const int cn = min(c + 1, c_last);
+      slot_load(s0, a, gi, cn, lane, off_at(cn), off_at(cn + 1));
+      wave_sync();
+      {
+        tile_full<NB, I4>(xc, smem, rin, lut, acc, lm);
+      }
+      wave_sync();
+    }
+  } else if constexpr (C::kDepth == 3) {
+    // Four register slots: GroupTile c is in LDS while c+1, c+2 and c+3
+    // load, so a wave keeps three GroupTiles of loads in flight.
+    const int c_last = c_end - 1;
+    auto load = [&](Slot<NB, I4>& sl, int c) {
+      const int cc = min(c, c_last);
+      slot_load(sl, a, gi, cc, lane, off_at(cc), off_at(cc + 1));
+    };
+    Slot<NB, I4> s0, s1, s2, s3;
+    load(s0, c_begin);
+    load(s1, c_begin + 1);
+    load(s2, c_begin + 2);
+    auto step = [&](Slot<NB, I4>& cur, int c, Slot<NB, I4>& nxt) {
+      load(nxt, c + 3);
+      const RowsIn rin = rows_in(cur.bm, bitmap_prefix_reg(cur.bm) + cur.delta + vb_elems, lm);
+      slot_commit(cur, vb, bb, lane);
+      wave_sync();
+      tile_full<NB, I4>(cur.x, smem, rin, lut, acc, lm);
+      wave_sync();
+    };
+    int c = c_begin;
+    for (; c + 4 <= c_end; c += 4) {
+      step(s0, c, s3);
+      step(s1, c + 1, s0);
+      step(s2, c + 2, s1);
+      step(s3, c + 3, s2);
+    }
+    if (c < c_end) step(s0, c, s3);
+    if (c + 1 < c_end) step(s1, c + 1, s0);
+    if (c + 2 < c_end) step(s2, c + 2, s1);
   } else if constexpr (C::kDepth == 2) {
     // Three register slots: GroupTile c is in LDS while c+1 and c+2 load.
     // Loads past the wave's last GroupTile repeat it (every wave here owns at
@@ -349,13 +454,10 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
     load(s1, c_begin + 1);
     auto step = [&](Slot<NB, I4>& cur, int c, Slot<NB, I4>& nxt) {
       load(nxt, c + 2);
+      const RowsIn rin = rows_in(cur.bm, bitmap_prefix_reg(cur.bm) + cur.delta + vb_elems, lm);
       slot_commit(cur, vb, bb, lane);
       wave_sync();
-      {
-        const uint32_t ebase = bitmap_prefix(bb, lane) + cur.delta + vb_elems;
-        tile_half<NB, I4, 0>(cur.x, smem, bb, lut, acc, ebase, lm);
-        tile_half<NB, I4, 1>(cur.x, smem, bb, lut, acc, ebase, lm);
-      }
+      tile_full<NB, I4>(cur.x, smem, rin, lut, acc, lm);
       wave_sync();
     };
     int c = c_begin;
@@ -377,13 +479,10 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
     load(s0, c_begin);
     auto step = [&](Slot<NB, I4>& cur, int c, Slot<NB, I4>& nxt) {
       load(nxt, c + 1);
+      const RowsIn rin = rows_in(cur.bm, bitmap_prefix_reg(cur.bm) + cur.delta + vb_elems, lm);
       slot_commit(cur, vb, bb, lane);
       wave_sync();
-      {
-        const uint32_t ebase = bitmap_prefix(bb, lane) + cur.delta + vb_elems;
-        tile_half<NB, I4, 0>(cur.x, smem, bb, lut, acc, ebase, lm);
-        tile_half<NB, I4, 1>(cur.x, smem, bb, lut, acc, ebase, lm);
-      }
+      tile_full<NB, I4>(cur.x, smem, rin, lut, acc, lm);
       wave_sync();
     };
     int c = c_begin;
@@ -482,6 +581,13 @@ using TuneCfg2 = Cfg<4, 2, 3>;
 using TuneCfg3 = Cfg<8, 1, 4>;
 using TuneCfg4 = Cfg<8, 1, 3>;
 using TuneCfg5 = Cfg<4, 2, 2>;
+using TuneCfg6 = Cfg<4, 3, 2>;
+using TuneCfg7 = Cfg<4, 3, 3>;
+using TuneCfg8 = Cfg<8, 3, 2>;
+using TuneCfg9 = Cfg<2, 3, 2>;
+using TuneCfg10 = Cfg<4, 0, 5>;
+using TuneCfg11 = Cfg<4, 0, 6>;
+using TuneCfg12 = Cfg<4, 0, 4>;
 #endif
 
 int choose_cfg() {
@@ -505,6 +611,13 @@ CfgInfo cfg_info(int cfg, bool two) {
     case 3: return {TuneCfg3::kWavesPerGroup, TuneCfg3::kOcc};
     case 4: return {TuneCfg4::kWavesPerGroup, TuneCfg4::kOcc};
     case 5: return {TuneCfg5::kWavesPerGroup, TuneCfg5::kOcc};
+    case 6: return {TuneCfg6::kWavesPerGroup, TuneCfg6::kOcc};
+    case 7: return {TuneCfg7::kWavesPerGroup, TuneCfg7::kOcc};
+    case 8: return {TuneCfg8::kWavesPerGroup, TuneCfg8::kOcc};
+    case 9: return {TuneCfg9::kWavesPerGroup, TuneCfg9::kOcc};
+    case 10: return {TuneCfg10::kWavesPerGroup, TuneCfg10::kOcc};
+    case 11: return {TuneCfg11::kWavesPerGroup, TuneCfg11::kOcc};
+    case 12: return {TuneCfg12::kWavesPerGroup, TuneCfg12::kOcc};
 #endif
     default:
       return two ? CfgInfo{DefaultCfg2::kWavesPerGroup, DefaultCfg2::kOcc}
@@ -588,6 +701,13 @@ void launch_decode(const Args& a, bool f16out, dim3 grid, hipStream_t s, int cfg
     case 3: launch_cfg<NB, I4, TuneCfg3>(a, f16out, grid, s); return;
     case 4: launch_cfg<NB, I4, TuneCfg4>(a, f16out, grid, s); return;
     case 5: launch_cfg<NB, I4, TuneCfg5>(a, f16out, grid, s); return;
+    case 6: launch_cfg<NB, I4, TuneCfg6>(a, f16out, grid, s); return;
+    case 7: launch_cfg<NB, I4, TuneCfg7>(a, f16out, grid, s); return;
+    case 8: launch_cfg<NB, I4, TuneCfg8>(a, f16out, grid, s); return;
+    case 9: launch_cfg<NB, I4, TuneCfg9>(a, f16out, grid, s); return;
+    case 10: launch_cfg<NB, I4, TuneCfg10>(a, f16out, grid, s); return;
+    case 11: launch_cfg<NB, I4, TuneCfg11>(a, f16out, grid, s); return;
+    case 12: launch_cfg<NB, I4, TuneCfg12>(a, f16out, grid, s); return;
 #endif
     default:
       if constexpr (NB == 2)
