@@ -328,6 +328,276 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a)
   if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS byte address
+// lds + 16 l (lds wave-uniform, in M0), counted by vmcnt like any vector
+// load.  Issued through asm so that the compiler, which cannot tell which LDS
+// bytes such a load writes, does not wait for every one in flight before
+// each LDS read and barrier; the caller waits with producer_barrier.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) T*)p));
+}
+
+// Wait until at most N of this wave's vector memory operations are in flight
+// and its LDS operations are done, then a workgroup barrier.
+#define USW_PRODUCER_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" : : : "memory")
+
+// Producer/consumer variant for N > 256: 512 tokens per workgroup.  Waves
+// 0-3 (consumers) only multiply: each owns 128 tokens (64 rows x 128 tokens
+// of fp32 accumulators) and per half GroupTile column (32 k) reads 4 A and
+// 8 X^T fragments from LDS for 32 MFMAs.  Waves 4-7 (producers) bring the
+// operands into LDS with global_load_lds_dwordx4 (no register round trip):
+// the X tile in 32-column halves, three buffers deep, one half a phase ahead
+// of its use, and each GroupTile's values a column ahead; they also rebuild
+// the A tile (two fragments each per column).  A barrier ends every half
+// column, after each producer's own loads of the previous phase are known
+// to have landed (s_waitcnt vmcnt); both roles pass the same barriers.
+template <bool OUT_F16>
+__global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PArgs a) {
+  constexpr int kBN = 512;
+  constexpr int kPThreads = 256;
+  constexpr int kCpt = (kStageChunks + kPThreads - 1) / kPThreads;   // value chunks per producer thread
+  constexpr int kStageBytes = kPThreads * kCpt * 16 + 16;
+
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStageBytes];
+  __shared__ __attribute__((aligned(16))) u32x4_t abuf[2][8 * 64];
+  // X tile halves: xs[b][4n + (q ^ ((n >> 2) & 3))] holds the 16-byte chunk q
+  // (k = 32h + 8q .. +7) of token n of the tile; a fragment read (16 tokens,
+  // one chunk) covers 16 distinct bank groups.
+  __shared__ __attribute__((aligned(16))) u32x4_t xs[3][kBN * 4];
+  __shared__ __attribute__((aligned(16))) uint32_t lut[32];
+  __shared__ __attribute__((aligned(16))) u32x2_t bmw[4][64];   // each producer wave's bitmap words
+  __shared__ uint32_t offtab[kMaxCols + 1];
+  __shared__ uint32_t last_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int nblk = static_cast<int>(gridDim.x);
+  const int b = static_cast<int>(blockIdx.x);
+  const int L = a.remap ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int tile = L / a.splits;
+  const int sidx = L - tile * a.splits;
+  const int gi = tile / a.ntiles;
+  const int nt = tile - gi * a.ntiles;
+  const int m0 = gi * kGT;
+  const int n_base = nt * kBN;
+
+  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * sidx / a.splits);
+  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (sidx + 1) / a.splits);
+  const int cnt = c_end - c_begin;        // >= 1: the host keeps splits <= Gc
+  const int c_last = c_end - 1;
+  const int64_t g_row = static_cast<int64_t>(gi) * a.Gc;
+
+  if (tid < 16) {
+    u32x2_t e;
+    e.x = nibble_selector(tid, 0);
+    e.y = nibble_selector(tid, 1);
+    reinterpret_cast<u32x2_t*>(lut)[tid] = e;
+  }
+  for (int i = tid; i <= cnt; i += 512) offtab[i] = a.offsets[g_row + c_begin + i];
+  __syncthreads();
+
+  auto xslot = [](int n, int q) { return 4 * n + (q ^ ((n >> 2) & 3)); };
+  const int row = lane & 15, kb = lane >> 4;
+
+  auto store_y4 = [&](int n, int m, f32x4_t v) {
+    const size_t yi = static_cast<size_t>(n) * a.M + m;
+    if constexpr (OUT_F16) {
+      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+      half4_t h;
+      h.x = static_cast<_Float16>(v.x);
+      h.y = static_cast<_Float16>(v.y);
+      h.z = static_cast<_Float16>(v.z);
+      h.w = static_cast<_Float16>(v.w);
+      *reinterpret_cast<half4_t*>(reinterpret_cast<_Float16*>(a.Y) + yi) = h;
+    } else {
+      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.Y) + yi) = v;
+    }
+  };
+
+  if (w < 4) {
+    // ---------------- consumer ----------------
+    const int nl = 128 * w;               // first token of this wave inside the tile
+    f32x4_t acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();   // producers: first column's values and X halves landed
+    __syncthreads();   // producers: first column's A tile rebuilt
+    for (int c = c_begin; c < c_end; ++c) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t* xb = xs[(2 * (c - c_begin) + h) % 3];
+        u32x4_t af[4];
+#pragma unroll
+        for (int rs = 0; rs < 4; ++rs) af[rs] = abuf[c & 1][(rs * 2 + h) * 64 + lane];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const u32x4_t bf = xb[xslot(nl + 16 * nb + row, kb)];
+#pragma unroll
+          for (int rs = 0; rs < 4; ++rs)
+            acc[rs][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, af[rs]),
+                                                                 __builtin_bit_cast(half8_t, bf), acc[rs][nb], 0, 0,
+                                                                 0);
+        }
+        __syncthreads();
+      }
+    }
+    // lane l of block (rs, nb): rows 16rs + 4(l/16) + i, token 16nb + l%16.
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int n = n_base + nl + nb * 16 + row;
+        const int m = m0 + rs * 16 + 4 * kb;
+        if (n >= a.N) continue;
+        if (a.splits > 1) {
+          float* pp = a.part + (static_cast<size_t>(sidx) * a.N + n) * a.M + m;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            __hip_atomic_store(pp + i, acc[rs][nb][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          store_y4(n, m, acc[rs][nb]);
+        }
+      }
+  } else {
+    // ---------------- producer ----------------
+    const int pw = w - 4;                 // producer wave: tokens 128pw .. +127, fragments 2pw, 2pw+1
+    const uint64_t top = a.values_alloc - 16;
+    // Values of column c into stage[buf]: chunk slot 64pw + lane + 256i of
+    // the buffer takes chunk min(slot, last) of the GroupTile's range.
+    auto dma_v = [&](int c, int buf) {
+      const uint32_t o0 = offtab[c - c_begin], o1 = offtab[c - c_begin + 1];
+      const uint64_t a0 = min(chunk_start<false>(o0), top);
+      const uint32_t nch = min(chunk_count<false>(o1, a0), static_cast<uint32_t>(kPThreads * kCpt));
+      const uint32_t last = min(nch > 0 ? nch - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
+      const uint32_t dst = lds_addr(stage[buf]) + 16 * 64 * pw;
+#pragma unroll
+      for (int i = 0; i < kCpt; ++i) {
+        const uint32_t slot = static_cast<uint32_t>(64 * pw + lane + kPThreads * i);
+        lds_dma16(src + min(slot, last), dst + 16 * kPThreads * i);
+      }
+    };
+    // The 64 bitmap words of column c into this wave's own copy (lanes 0-31,
+    // two words each).
+    const uint32_t bm_lds = lds_addr(bmw[pw]);
+    auto dma_bm = [&](int c) {
+      if (lane < 32) lds_dma16(a.bitmaps + (g_row + c) * kBtPerGt + 2 * lane, bm_lds);
+    };
+    // X half j (counted from the first column: column c_begin + j/2, k half
+    // j%2) for this wave's 128 tokens into xs[j % 3]: instruction i fills the
+    // 1 KB of slots of tokens 128pw + 16i .. +15, lane l the slot
+    // 4(128pw + 16i) + l, i.e. token n = 128pw + 16i + l/4, chunk
+    // q = (l & 3) ^ ((n >> 2) & 3).
+    auto dma_x = [&](int j) {
+      const int cc = min(c_begin + (j >> 1), c_last);
+      const uint32_t dst = lds_addr(xs[j % 3]) + 16 * 4 * 128 * pw;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int nloc = 128 * pw + 16 * i + (lane >> 2);
+        const int q = (lane & 3) ^ ((nloc >> 2) & 3);
+        const int n = min(n_base + nloc, a.N - 1);
+        lds_dma16(a.X + static_cast<size_t>(n) * a.K + cc * kGT + (j & 1) * 32 + q * 8, dst + 1024 * i);
+      }
+    };
+    const int r8 = row & 7;
+    const int bt_lane = 4 * (kb >> 1) + 2 * (row >> 3) + (kb & 1);
+    const uint64_t rowmask = (1ull << (8 * r8)) - 1ull;
+    auto prep = [&](u32x2_t bmv, int c) {
+      RbIn<2> in;
+      const uint32_t o0 = offtab[c - c_begin];
+      const uint64_t a0 = min(chunk_start<false>(o0), top);
+      const uint32_t pc = __builtin_popcount(bmv.x) + __builtin_popcount(bmv.y);
+      const uint32_t ebase = wave_inclusive_scan(pc) - pc + chunk_delta<false>(o0, a0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int f = 2 * pw + j;
+        const int bt = 16 * (f >> 1) + 8 * (f & 1) + bt_lane;
+        in.base[j] = __builtin_amdgcn_ds_bpermute(bt << 2, ebase);
+        in.lo[j] = __builtin_amdgcn_ds_bpermute(bt << 2, bmv.x);
+        in.hi[j] = __builtin_amdgcn_ds_bpermute(bt << 2, bmv.y);
+      }
+      return in;
+    };
+    auto rebuild = [&](int c, int j, const RbIn<2>& in) {
+      const int f = 2 * pw + j;
+      const uint64_t bm = (static_cast<uint64_t>(in.hi[j]) << 32) | in.lo[j];
+      const uint32_t rb = in.base[j] + __popcll(bm & rowmask);
+      const uint32_t byte = static_cast<uint32_t>(bm >> (8 * r8)) & 0xFFu;
+      abuf[c & 1][f * 64 + lane] = __builtin_bit_cast(u32x4_t, rebuild_row<false>(stage[c & 1], lut, rb, byte));
+    };
+    auto load_bm = [&](int c) { return reinterpret_cast<const u32x2_t*>(a.bitmaps + (g_row + c) * kBtPerGt)[lane]; };
+
+    const RbIn<2> rin0 = prep(load_bm(c_begin), c_begin);
+    RbIn<2> rin = prep(load_bm(min(c_begin + 1, c_last)), min(c_begin + 1, c_last));
+    dma_x(0);
+    dma_x(1);
+    dma_v(c_begin, c_begin & 1);
+    dma_v(min(c_begin + 1, c_last), (c_begin + 1) & 1);
+    USW_PRODUCER_BARRIER(0);
+    rebuild(c_begin, 0, rin0);
+    rebuild(c_begin, 1, rin0);
+    USW_PRODUCER_BARRIER(0);
+
+    // Phase t = 2 (c - c_begin) + h: consumers read X half t from xs[t % 3].
+    // First phase of column c: bitmap words and values of column c+2 (into
+    // stage[c & 1], rebuilt in the column before), X half t+2 into
+    // xs[(t+2) % 3] (read in phase t-1), fragment 2pw of column c+1.  The
+    // barrier waits for all but this phase's 11 values and X loads: the
+    // bitmap words and X half t+1.  Second phase: fragment 2pw+1 of column
+    // c+1, the rebuild inputs of c+2, X half t+3; the barrier waits for all
+    // but its 8 X loads, so the values of c+2 are in place for the next
+    // column.
+    for (int c = c_begin; c < c_end; ++c) {
+      const int t = 2 * (c - c_begin);
+      const int c2 = min(c + 2, c_last);
+      dma_bm(c2);
+      dma_v(c2, c & 1);
+      dma_x(t + 2);
+      if (c + 1 < c_end) rebuild(c + 1, 0, rin);
+      USW_PRODUCER_BARRIER(11);
+      if (c + 1 < c_end) rebuild(c + 1, 1, rin);
+      rin = prep(reinterpret_cast<const u32x2_t*>(bmw[pw])[lane], c2);
+      dma_x(t + 3);
+      USW_PRODUCER_BARRIER(8);
+    }
+    __builtin_amdgcn_s_waitcnt(0);     // no LDS write of this wave outlives it
+  }
+  if (a.splits <= 1) return;
+
+  // Split K: as in prefill_kernel (consumers wrote the partial sums).
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (tid == 0)
+    last_flag = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                static_cast<uint32_t>(a.splits - 1);
+  __syncthreads();
+  if (!last_flag) return;
+  for (int e = tid; e < kBN * 16; e += 512) {
+    const int n = n_base + (e >> 4);
+    const int m = m0 + 4 * (e & 15);
+    if (n >= a.N) continue;
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+    for (int pp = 0; pp < a.splits; ++pp) {
+      const float* q = a.part + (static_cast<size_t>(pp) * a.N + n) * a.M + m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[i] += __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    store_y4(n, m, sum);
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 constexpr int64_t kComputeUnits = 256;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -387,8 +657,8 @@ usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(nblk));
   if (p.waves == 8) {
-    if (f16out) prefill_kernel<8, true><<<grid, 512, 0, s>>>(a);
-    else prefill_kernel<8, false><<<grid, 512, 0, s>>>(a);
+    if (f16out) prefill_ws_kernel<true><<<grid, 512, 0, s>>>(a);
+    else prefill_ws_kernel<false><<<grid, 512, 0, s>>>(a);
   } else {
     if (f16out) prefill_kernel<4, true><<<grid, 256, 0, s>>>(a);
     else prefill_kernel<4, false><<<grid, 256, 0, s>>>(a);
