@@ -146,8 +146,8 @@ usw_status usw_validate(const usw_fmt* host_fmt);
 /*
  * Workspace bytes usw_spmm needs for this matrix and N (0 when none).  The
  * workspace starts with 32-bit counters (usw_spmm_counter_bytes of them,
- * one per output tile) followed by the fp32 partial sums of the split-K
- * workgroups.  The counter bytes must be zero when a call starts: allocate
+ * one per output tile) followed by the fp32 partial sums of the workgroups
+ * that share an output tile.  The counter bytes must be zero when a call starts: allocate
  * the workspace zero-filled; every call leaves its counter bytes zero again.
  * A workspace last used by a call with a different counter size (another M,
  * or N on the other side of 32, or another prefill token tiling) may hold
@@ -181,11 +181,17 @@ usw_status usw_spmm(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y_ty
  * caller: splits = workgroups that share one output tile (a 64-row strip of
  * GroupTiles, with all N columns for the decode kernel, or 256 / 512 of them
  * for the prefill kernel), each summing a contiguous range of GroupTile
- * columns (0 = automatic).  With a factor above 1 each workgroup writes fp32
- * partial sums to the workspace and the last workgroup of a tile to finish
- * adds them in split order, so results do not depend on scheduling.  The
- * factor is clamped to [ceil(K / (64 * 4 * 63)), max(1, K / 256)] for the
- * decode kernels and to [ceil(K / 65536), K / 64] for the prefill kernel.
+ * columns.  With a factor above 1 each workgroup writes fp32 partial sums to
+ * the workspace and the last workgroup of a tile to finish adds them in
+ * split order, so results do not depend on scheduling.  The factor is
+ * clamped to [ceil(K / (64 * 4 * 63)), max(1, K / 256)] for the decode
+ * kernels and to [ceil(K / 65536), K / 64] for the prefill kernel.
+ * splits = 0 is the automatic choice of usw_spmm: for the prefill kernel
+ * with N > 256 and K <= 65536 that is a stream-K split, in which each
+ * workgroup (one per compute unit, or fewer for small problems) runs the
+ * same number of GroupTile columns -- whole tiles and an even share of the
+ * columns of the tiles left over -- and the tiles shared by several
+ * workgroups are summed in a fixed order as above.
  * Same errors as usw_spmm.  Meant for tuning and tests.
  */
 usw_status usw_spmm_workspace_ex(const usw_fmt* fmt, int32_t N, int32_t splits, size_t* bytes);

@@ -204,3 +204,39 @@ def test_prefill_full_size_integer_exact_bitwise(name):
     Y = gpu(usw.encode_host(W, mask), X, torch.float32)
     Wd = np.where(mask, W, np.float16(0))
     assert np.array_equal(Y, ob.spmm_fp64(Wd, X))
+
+
+# Work-split cases of the 512-token kernel (automatic split): the tile count a
+# multiple of the workgroup count (whole tiles only), fewer tiles than
+# workgroups (every tile split), whole rounds plus a split remainder, and a
+# remainder too small to give every workgroup a column (one round goes back
+# into the split part).
+@pytest.mark.parametrize("M,K,N", [(4096, 512, 512), (1024, 1024, 600), (1280, 1024, 1100), (16448, 64, 512),
+                                   (2048, 448, 1024)])
+def test_prefill_stream_k_integer_exact_bitwise(M, K, N):
+    rng = np.random.default_rng(M + 3 * K + N)
+    W = wl.weight_dyadic(M, K, rng)
+    mask = wl.mask_bernoulli(M, K, 0.5, rng)
+    X = wl.activations_small_int(N, K, rng)
+    say(f"[prefill stream-K] {M}x{K} N={N}")
+    h = usw.encode_host(W, mask)
+    Wd = np.where(mask, W, np.float16(0))
+    Yref = ob.spmm_fp64(Wd, X)
+    assert np.array_equal(gpu(h, X, torch.float32), Yref)
+    assert np.array_equal(gpu(h, X, torch.float16), Yref.astype(np.float16).astype(np.float64))
+
+
+def test_prefill_stream_k_deterministic():
+    """Split tiles are summed in a fixed order: repeated calls give the same
+    bits for general inputs."""
+    rng = np.random.default_rng(123)
+    M, K, N = 1280, 2048, 700
+    W = wl.weight_normal(M, K, rng)
+    mask = wl.mask_bernoulli(M, K, 0.5, rng)
+    X = wl.activations_normal(N, K, rng)
+    h = usw.encode_host(W, mask)
+    Ya = gpu(h, X, torch.float32)
+    Yb = gpu(h, X, torch.float32)
+    assert np.array_equal(Ya, Yb)
+    Yref, Bnd = ref(W, mask, X)
+    check(Ya, Yref, Bnd, "prefill stream-K")

@@ -27,6 +27,7 @@ struct PrefillPlan {
   int waves;    // waves per workgroup (64 tokens each)
   int ntiles;   // token tiles of 64 * waves
   int splits;   // workgroups per (strip, token tile)
+  int wgs;      // > 0: stream-K over this many workgroups (512-token tiles only)
 };
 PrefillPlan prefill_plan(const Geometry& g, int N, int splits_req);
 size_t prefill_counter_bytes(const Geometry& g, const PrefillPlan& p);

@@ -48,10 +48,12 @@ struct PArgs {
   const uint8_t* __restrict__ values;
   const uint16_t* __restrict__ X;
   void* __restrict__ Y;
-  float* __restrict__ part;         // split-K partial sums [splits][N][M]
+  float* __restrict__ part;         // partial sums: [splits][N][M], or slots of 512 x 64 (prefill_ws_kernel)
   uint32_t* __restrict__ counters;  // per (strip, token tile): workgroups done; kept at 0 between calls
   uint64_t values_alloc;            // padded size of the values buffer in bytes
   int M, K, N, Gc, splits, ntiles;
+  int tiles;                        // strips x token tiles
+  int wgs;                          // prefill_ws_kernel: > 0 stream-K over this many workgroups
   int remap;                        // 1: keep consecutive tiles (and a tile's splits) on one XCD
 };
 
@@ -328,13 +330,23 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a)
   if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Buffer resource word 3 for raw 32-bit-addressed buffers on this target,
+// and the cache-policy operand that sets sc1: the access goes to the level
+// that is coherent across the device, as agent-scope atomics do.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCacheSc1 = 16;
+
 // global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS byte address
-// lds + 16 l (lds wave-uniform, in M0), counted by vmcnt like any vector
-// load.  Issued through asm so that the compiler, which cannot tell which LDS
-// bytes such a load writes, does not wait for every one in flight before
-// each LDS read and barrier; the caller waits with producer_barrier.
+// lds + 16 l (lds the same in every lane; it goes to M0), counted by vmcnt
+// like any vector load.  Issued through asm so that the compiler, which
+// cannot tell which LDS bytes such a load writes, does not wait for every
+// one in flight before each LDS read and barrier; the caller waits with an
+// explicit vmcnt before the barrier that publishes the data.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
 }
 
 template <typename T>
@@ -346,22 +358,58 @@ __device__ __forceinline__ uint32_t lds_addr(T* p) {
 // and its LDS operations are done, then a workgroup barrier.
 #define USW_PRODUCER_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" : : : "memory")
 
-// Producer/consumer variant for N > 256: 512 tokens per workgroup.  Waves
-// 0-3 (consumers) only multiply: each owns 128 tokens (64 rows x 128 tokens
-// of fp32 accumulators) and per half GroupTile column (32 k) reads 4 A and
-// 8 X^T fragments from LDS for 32 MFMAs.  Waves 4-7 (producers) bring the
-// operands into LDS with global_load_lds_dwordx4 (no register round trip):
-// the X tile in 32-column halves, three buffers deep, one half a phase ahead
-// of its use, and each GroupTile's values a column ahead; they also rebuild
-// the A tile (two fragments each per column).  A barrier ends every half
-// column, after each producer's own loads of the previous phase are known
-// to have landed (s_waitcnt vmcnt); both roles pass the same barriers.
+// The same for a wave-uniform count n in [8, 12].
+__device__ __forceinline__ void producer_barrier(int n) {
+  switch (__builtin_amdgcn_readfirstlane(n)) {
+    case 8: USW_PRODUCER_BARRIER(8); break;
+    case 9: USW_PRODUCER_BARRIER(9); break;
+    case 10: USW_PRODUCER_BARRIER(10); break;
+    case 11: USW_PRODUCER_BARRIER(11); break;
+    default: USW_PRODUCER_BARRIER(12); break;
+  }
+}
+
+// Warp-specialised variant for N > 256: a tile is 64 rows (one GroupTile
+// strip) by 512 tokens, and twelve waves in three roles pass the same
+// barriers, one per half GroupTile column (32 k).
+//  - Waves 0-3 (consumers) only multiply: each owns 128 tokens (64 rows x
+//    128 tokens of fp32 accumulators) and per half column reads 4 A and 8
+//    X^T fragments from LDS for 32 MFMAs.
+//  - Waves 4-7 (loaders) bring the operands into LDS with
+//    global_load_lds_dwordx4 (no register round trip): the X tile in
+//    32-column halves, three buffers deep, one half a phase ahead of its
+//    use, and the values and bitmap words of a GroupTile two columns ahead.
+//    Before each barrier a loader waits until the loads the next phase
+//    reads have landed (s_waitcnt vmcnt).
+//  - Waves 8-11 (builders) rebuild the A tile of the next column, two
+//    fragments each, from the staged values.
+// A loader spends most of its time waiting for the address unit to accept
+// its loads, a builder for LDS round trips; in separate waves the two
+// overlap.
+//
+// Work split.  The (tile, GroupTile column) units are numbered tile-major.
+// With a.wgs > 0 (stream-K) every compute unit gets the same number of
+// columns whatever the tile count: workgroup p of P = a.wgs takes R whole
+// tiles p, p + P, ... and an even share [B + U p / P, B + U (p + 1) / P) of
+// the units of the tiles left over (B = R P Gc; R = 0 when there are fewer
+// tiles than workgroups).  Otherwise (split-K) workgroup L takes split
+// L % splits of tile L / splits.  A workgroup first runs the pieces of its
+// range (one per tile it touches) from the last to the first -- the
+// workgroups that share a tile then start its columns at both ends at once,
+// so that at any moment they all stream nearly the same few X columns, and
+// the partial sums are added while whole tiles still run -- then its whole
+// tiles.  A piece that covers its whole tile stores Y; otherwise it stores
+// fp32 partial sums in a slot of its own, and the workgroup that completes
+// the tile's count adds the tile's slots in a fixed order (that of the
+// ranges), so results do not depend on timing.
 template <bool OUT_F16>
-__global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PArgs a) {
+__global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
   constexpr int kBN = 512;
-  constexpr int kPThreads = 256;
-  constexpr int kCpt = (kStageChunks + kPThreads - 1) / kPThreads;   // value chunks per producer thread
+  constexpr int kThreads = 768;
+  constexpr int kPThreads = 256;                                      // loader threads
+  constexpr int kCpt = (kStageChunks + kPThreads - 1) / kPThreads;   // value chunks per loader thread
   constexpr int kStageBytes = kPThreads * kCpt * 16 + 16;
+  constexpr int kSlot = kBN * kGT;                                    // floats per partial-sum slot
 
   __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStageBytes];
   __shared__ __attribute__((aligned(16))) u32x4_t abuf[2][8 * 64];
@@ -370,29 +418,37 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PArgs a) {
   // one chunk) covers 16 distinct bank groups.
   __shared__ __attribute__((aligned(16))) u32x4_t xs[3][kBN * 4];
   __shared__ __attribute__((aligned(16))) uint32_t lut[32];
-  __shared__ __attribute__((aligned(16))) u32x2_t bmw[4][64];   // each producer wave's bitmap words
+  __shared__ __attribute__((aligned(16))) u32x2_t bmw[2][64];   // bitmap words of columns c, c+1 (by c & 1)
   __shared__ uint32_t offtab[kMaxCols + 1];
   __shared__ uint32_t last_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = lane & 15, kb = lane >> 4;
 
   const int nblk = static_cast<int>(gridDim.x);
   const int b = static_cast<int>(blockIdx.x);
   const int L = a.remap ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
-  const int tile = L / a.splits;
-  const int sidx = L - tile * a.splits;
-  const int gi = tile / a.ntiles;
-  const int nt = tile - gi * a.ntiles;
-  const int m0 = gi * kGT;
-  const int n_base = nt * kBN;
-
-  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * sidx / a.splits);
-  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (sidx + 1) / a.splits);
-  const int cnt = c_end - c_begin;        // >= 1: the host keeps splits <= Gc
-  const int c_last = c_end - 1;
-  const int64_t g_row = static_cast<int64_t>(gi) * a.Gc;
+  const int64_t Gc = a.Gc;
+  // Stream-K: R whole rounds of tiles L, L + P, ..., and the units of the
+  // remaining tiles, [B, B + U) with B = R P Gc, split evenly.  R is
+  // tiles / P, one less when the remainder would give some workgroup no
+  // unit (the host keeps tiles * Gc >= P): an empty range between two owners
+  // of a tile would leave its count short.
+  int R = a.wgs > 0 ? a.tiles / nblk : 0;
+  if (R > 0 && a.tiles % nblk != 0 && static_cast<int64_t>(a.tiles - R * nblk) * Gc < nblk) --R;
+  const int64_t B = static_cast<int64_t>(R) * nblk * Gc;
+  const int64_t U = static_cast<int64_t>(a.tiles) * Gc - B;
+  int64_t r0, r1;
+  if (a.wgs > 0) {
+    r0 = B + U * L / nblk;
+    r1 = B + U * (L + 1) / nblk;
+  } else {
+    const int tile = L / a.splits, sidx = L - tile * a.splits;
+    r0 = tile * Gc + Gc * sidx / a.splits;
+    r1 = tile * Gc + Gc * (sidx + 1) / a.splits;
+  }
 
   if (tid < 16) {
     u32x2_t e;
@@ -400,11 +456,8 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PArgs a) {
     e.y = nibble_selector(tid, 1);
     reinterpret_cast<u32x2_t*>(lut)[tid] = e;
   }
-  for (int i = tid; i <= cnt; i += 512) offtab[i] = a.offsets[g_row + c_begin + i];
-  __syncthreads();
 
   auto xslot = [](int n, int q) { return 4 * n + (q ^ ((n >> 2) & 3)); };
-  const int row = lane & 15, kb = lane >> 4;
 
   auto store_y4 = [&](int n, int m, f32x4_t v) {
     const size_t yi = static_cast<size_t>(n) * a.M + m;
@@ -421,184 +474,322 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PArgs a) {
     }
   };
 
+  // One piece: columns [c_begin, c_end) of one tile.
+  struct Piece {
+    int tile, c_begin, c_end, c_last, cnt, m0, n_base, slot;
+    int64_t t0, g_row;
+    bool full;
+  };
+
+  // Split tile: after every wave's partial-sum stores have completed, count
+  // the piece; the tile's last piece (the one whose count completes it) then
+  // has the consumers add the tile's slots in range order.  Returns the first
+  // owner and the number of pieces in *q0, *np.
+  auto count_split = [&](const Piece& pc, int* q0, int* np) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (a.wgs > 0) {
+      // Owners of the tile: workgroups p with B + U p / P <= t0 + Gc - 1
+      // and B + U (p + 1) / P > t0.
+      const int64_t x0 = pc.t0 - B;
+      *q0 = static_cast<int>(((x0 + 1) * nblk + U - 1) / U) - 1;
+      *np = static_cast<int>(((x0 + Gc) * nblk + U - 1) / U) - *q0;
+    } else {
+      *q0 = pc.tile * a.splits;
+      *np = a.splits;
+    }
+    if (tid == 0)
+      last_flag = __hip_atomic_fetch_add(&a.counters[pc.tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  static_cast<uint32_t>(*np - 1);
+    __syncthreads();
+    return last_flag != 0;
+  };
+  // Partial-sum slot of owner q of a split tile.
+  auto slot_of = [&](const Piece& pc, int q) {
+    return a.wgs > 0 ? 2 * q + (B + U * q / nblk >= pc.t0 ? 0 : 1) : q;
+  };
+  // The tile's sum, owner by owner in range order, by all threads: thread
+  // tid takes slot elements e = tid + kThreads j, element e being 4 floats
+  // of token 128 wv + 16 nb + ln % 16, rows 16 rs + 4 (ln / 16) .. +3 for
+  // e = ((wv * 4 + rs) * 8 + nb) * 64 + ln.  Loads reach the device-coherent
+  // level (sc1), where the owners' stores went.
+  auto reduce_tile = [&](const Piece& pc, int q0, int np) {
+    constexpr int kE = kSlot / 4;                       // float4 elements per slot
+    constexpr int kJ = (kE + kThreads - 1) / kThreads;
+    // The thread index through an empty asm: what is derived from it is
+    // recomputed here instead of being hoisted out of the piece loop, where
+    // it would stay live in every role's registers.
+    int me = tid;
+    asm volatile("" : "+v"(me));
+    f32x4_t sum[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) sum[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < np; ++k) {
+      const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(slot_of(pc, q0 + k)) * kSlot, 0,
+                                                          kSlot * 4, kBufferRsrcWord3);
+      f32x4_t v[kJ];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+        v[j] = __builtin_bit_cast(f32x4_t,
+                                  __builtin_amdgcn_raw_buffer_load_b128(rsrc, (me + kThreads * j) * 16, 0, kCacheSc1));
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) sum[j] += v[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int e = me + kThreads * j;
+      if (e >= kE) break;
+      const int ln = e & 63, nb = (e >> 6) & 7, rs = (e >> 9) & 3, wv = e >> 11;
+      const int n = pc.n_base + 128 * wv + 16 * nb + (ln & 15);
+      if (n < a.N) store_y4(n, pc.m0 + 16 * rs + 4 * (ln >> 4), sum[j]);
+    }
+  };
+
+  auto run_piece = [&](auto&& body, int tile, int c_begin, int c_end) {
+    Piece pc;
+    pc.tile = tile;
+    pc.t0 = tile * Gc;
+    pc.c_begin = c_begin;
+    pc.c_end = c_end;
+    pc.full = c_begin == 0 && c_end == a.Gc;
+    // Partial-sum slot: stream-K, 2p for the piece that opens workgroup p's
+    // range, 2p + 1 for the one that closes it; split-K, L.
+    pc.slot = a.wgs > 0 ? 2 * L + (pc.t0 + c_begin == r0 ? 0 : 1) : L;
+    const int gi = tile / a.ntiles;
+    pc.m0 = gi * kGT;
+    pc.n_base = (tile - gi * a.ntiles) * kBN;
+    pc.cnt = c_end - c_begin;           // >= 1
+    pc.c_last = c_end - 1;
+    pc.g_row = static_cast<int64_t>(gi) * a.Gc;
+
+    const uint32_t* otab = a.offsets + pc.g_row + c_begin;
+    for (int i = tid; i <= pc.cnt; i += kThreads) offtab[i] = otab[i];
+    __syncthreads();
+    body(pc);
+    if (!pc.full) {
+      int q0, np;
+      if (count_split(pc, &q0, &np)) {
+        reduce_tile(pc, q0, np);
+        if (tid == 0) __hip_atomic_store(&a.counters[pc.tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();   // LDS buffers and offtab are reused by the next piece
+  };
+  // Runs body(piece) for every piece of this workgroup: first the pieces of
+  // its range [r0, r1) from the last to the first, then (stream-K) its whole
+  // tiles.  Each role calls it with its own body, so that the values a role
+  // keeps across pieces are only live in that role's code.  All roles pass
+  // the same barriers: the offset table fill, the body's, and those of the
+  // split-tile count.
+  auto for_pieces = [&](auto&& body) {
+    for (int64_t u1 = r1; u1 > r0;) {
+      const int tile = static_cast<int>((u1 - 1) / Gc);
+      const int64_t t0 = tile * Gc;
+      const int c_begin = static_cast<int>(max(r0, t0) - t0);
+      run_piece(body, tile, c_begin, static_cast<int>(u1 - t0));
+      u1 = t0 + c_begin;
+    }
+    for (int r = 0; r < R; ++r) run_piece(body, L + r * nblk, 0, a.Gc);
+  };
+
   if (w < 4) {
     // ---------------- consumer ----------------
     const int nl = 128 * w;               // first token of this wave inside the tile
-    f32x4_t acc[4][8];
+    for_pieces([&](const Piece& pc) {
+      f32x4_t acc[4][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();   // producers: first column's values and X halves landed
-    __syncthreads();   // producers: first column's A tile rebuilt
-    for (int c = c_begin; c < c_end; ++c) {
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();   // loaders: X halves 0, 1 and two columns' values landed
+      __syncthreads();   // builders: first column's A tile rebuilt
+      for (int c = pc.c_begin; c < pc.c_end; ++c) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4_t* xb = xs[(2 * (c - c_begin) + h) % 3];
-        u32x4_t af[4];
+        for (int h = 0; h < 2; ++h) {
+          const u32x4_t* xb = xs[(2 * (c - pc.c_begin) + h) % 3];
+          u32x4_t af[4];
 #pragma unroll
-        for (int rs = 0; rs < 4; ++rs) af[rs] = abuf[c & 1][(rs * 2 + h) * 64 + lane];
+          for (int rs = 0; rs < 4; ++rs) af[rs] = abuf[c & 1][(rs * 2 + h) * 64 + lane];
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          const u32x4_t bf = xb[xslot(nl + 16 * nb + row, kb)];
+          for (int nb = 0; nb < 8; ++nb) {
+            const u32x4_t bf = xb[xslot(nl + 16 * nb + row, kb)];
 #pragma unroll
-          for (int rs = 0; rs < 4; ++rs)
-            acc[rs][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, af[rs]),
-                                                                 __builtin_bit_cast(half8_t, bf), acc[rs][nb], 0, 0,
-                                                                 0);
+            for (int rs = 0; rs < 4; ++rs)
+              acc[rs][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, af[rs]),
+                                                                   __builtin_bit_cast(half8_t, bf), acc[rs][nb], 0,
+                                                                   0, 0);
+          }
+          __syncthreads();
+        }
+      }
+      // lane l of block (rs, nb): rows 16rs + 4(l/16) + i, token 16nb + l%16.
+      if (pc.full) {
+#pragma unroll
+        for (int rs = 0; rs < 4; ++rs)
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const int n = pc.n_base + nl + nb * 16 + row;
+            if (n < a.N) store_y4(n, pc.m0 + rs * 16 + 4 * kb, acc[rs][nb]);
+          }
+      } else {
+        // Stores that reach the device-coherent level (sc1), as agent-scope
+        // atomic stores do, 16 bytes at a time; the slot keeps the
+        // accumulators in register order, [wave][rs][nb][lane][i].
+        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(pc.slot) * kSlot + w * (kSlot / 4),
+                                                            0, kSlot, kBufferRsrcWord3);
+#pragma unroll
+        for (int rs = 0; rs < 4; ++rs)
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[rs][nb]), rsrc,
+                                                   ((rs * 8 + nb) * 64 + lane) * 16, 0, kCacheSc1);
+      }
+    });
+  } else if (w < 8) {
+    // ---------------- loader ----------------
+    for_pieces([&](const Piece& pc) {
+      const int dw = w - 4;               // X of tokens 128dw .. +127; value chunk slots 64dw + 256i + lane
+      const uint64_t top = a.values_alloc - 16;
+      // Values of column c into stage[buf]: slot 64dw + lane + 256i of the
+      // buffer takes chunk slot of the GroupTile's range; an instruction
+      // whose 64 slots all lie past the range is not issued.  Returns how
+      // many were.
+      auto dma_v = [&](int c, int buf) {
+        const uint32_t o0 = offtab[c - pc.c_begin], o1 = offtab[c - pc.c_begin + 1];
+        const uint64_t a0 = min(chunk_start<false>(o0), top);
+        const uint32_t nch = __builtin_amdgcn_readfirstlane(
+            min(chunk_count<false>(o1, a0), static_cast<uint32_t>((top - a0) >> 4) + 1u));
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
+        const uint32_t dst = lds_addr(stage[buf]) + 16 * 64 * dw;
+        int issued = 0;
+#pragma unroll
+        for (int i = 0; i < kCpt; ++i) {
+          const uint32_t slot0 = static_cast<uint32_t>(64 * dw + kPThreads * i);
+          if (slot0 < nch) {
+            lds_dma16(src + min(slot0 + lane, nch - 1), dst + 16 * kPThreads * i);
+            ++issued;
+          }
+        }
+        return issued;
+      };
+      // The 64 bitmap words of column c into bmw[c & 1] (loader 0, lanes
+      // 0-31, two words each).  Returns how many loads this wave issued.
+      auto dma_bm = [&](int c) {
+        if (dw != 0) return 0;
+        if (lane < 32) lds_dma16(a.bitmaps + (pc.g_row + c) * kBtPerGt + 2 * lane, lds_addr(bmw[c & 1]));
+        return 1;
+      };
+      // X half j (counted from the first column: column pc.c_begin + j/2, k
+      // half j%2) for this wave's 128 tokens into xs[j % 3]: instruction i
+      // fills the 1 KB of slots of tokens 128dw + 16i .. +15, lane l the
+      // slot 4(128dw + 16i) + l, i.e. token n = 128dw + 16i + l/4, chunk
+      // q = (l & 3) ^ ((n >> 2) & 3).
+      auto dma_x = [&](int j) {
+        const int cc = min(pc.c_begin + (j >> 1), pc.c_last);
+        const uint32_t dst = lds_addr(xs[j % 3]) + 16 * 4 * 128 * dw;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int nloc = 128 * dw + 16 * i + (lane >> 2);
+          const int q = (lane & 3) ^ ((nloc >> 2) & 3);
+          const int n = min(pc.n_base + nloc, a.N - 1);
+          lds_dma16(a.X + static_cast<size_t>(n) * a.K + cc * kGT + (j & 1) * 32 + q * 8, dst + 1024 * i);
+        }
+      };
+
+      const int c1 = min(pc.c_begin + 1, pc.c_last);
+      dma_x(0);
+      dma_x(1);
+      dma_bm(pc.c_begin);
+      dma_v(pc.c_begin, pc.c_begin & 1);
+      if (c1 != pc.c_begin) {
+        dma_bm(c1);
+        dma_v(c1, c1 & 1);
+      }
+      USW_PRODUCER_BARRIER(0);
+      USW_PRODUCER_BARRIER(0);   // builders: first column's A tile rebuilt
+
+      // Phase t = 2 (c - pc.c_begin) + h: consumers read X half t from
+      // xs[t % 3].  First phase of column c: the bitmap words and values of
+      // column c+2 (into bmw[c & 1] and stage[c & 1], both read for column
+      // c in the column before), then X half t+2 into xs[(t+2) % 3] (read
+      // in phase t-1).  All of them may still be in flight at the barrier;
+      // X half t+1 has landed.  Second phase: X half t+3; everything older
+      // than it lands before the barrier, so column c+2's values and bitmap
+      // words are in place for the builders of the next column.
+      for (int c = pc.c_begin; c < pc.c_end; ++c) {
+        const int t = 2 * (c - pc.c_begin);
+        int n = 8;
+        if (c + 2 < pc.c_end) {
+          n += dma_bm(c + 2);
+          n += dma_v(c + 2, c & 1);
+        }
+        dma_x(t + 2);
+        producer_barrier(n);
+        dma_x(t + 3);
+        USW_PRODUCER_BARRIER(8);
+      }
+      __builtin_amdgcn_s_waitcnt(0);   // no LDS write of this wave outlives the piece
+    });
+  } else {
+    // ---------------- builder ----------------
+    for_pieces([&](const Piece& pc) {
+      const int bw = w - 8;               // A fragments 2bw, 2bw+1: rows 16bw .. +15, k halves 0 and 1
+      const uint64_t top = a.values_alloc - 16;
+      const int r8 = row & 7;
+      const int bt_lane = 4 * (kb >> 1) + 2 * (row >> 3) + (kb & 1);
+      const uint64_t rowmask = (1ull << (8 * r8)) - 1ull;
+      // Rebuild inputs of column c for this wave's two fragments: for the
+      // BitmapTile row a lane rebuilds, the bitmap and the element index of
+      // the tile's first value inside the staged chunk range.
+      auto prep = [&](int c) {
+        const u32x2_t bmv = reinterpret_cast<const u32x2_t*>(bmw[c & 1])[lane];
+        RbIn<2> in;
+        const uint32_t o0 = offtab[c - pc.c_begin];
+        const uint64_t a0 = min(chunk_start<false>(o0), top);
+        const uint32_t pc = __builtin_popcount(bmv.x) + __builtin_popcount(bmv.y);
+        const uint32_t ebase = wave_inclusive_scan(pc) - pc + chunk_delta<false>(o0, a0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int f = 2 * bw + j;
+          const int bt = 16 * (f >> 1) + 8 * (f & 1) + bt_lane;
+          in.base[j] = __builtin_amdgcn_ds_bpermute(bt << 2, ebase);
+          in.lo[j] = __builtin_amdgcn_ds_bpermute(bt << 2, bmv.x);
+          in.hi[j] = __builtin_amdgcn_ds_bpermute(bt << 2, bmv.y);
+        }
+        return in;
+      };
+      auto rebuild = [&](int c, int j, const RbIn<2>& in) {
+        const int f = 2 * bw + j;
+        const uint64_t bm = (static_cast<uint64_t>(in.hi[j]) << 32) | in.lo[j];
+        const uint32_t rb = in.base[j] + __popcll(bm & rowmask);
+        const uint32_t byte = static_cast<uint32_t>(bm >> (8 * r8)) & 0xFFu;
+        abuf[c & 1][f * 64 + lane] = __builtin_bit_cast(u32x4_t, rebuild_row<false>(stage[c & 1], lut, rb, byte));
+      };
+
+      __syncthreads();   // loaders: first two columns' values and bitmap words landed
+      RbIn<2> rin = prep(pc.c_begin);
+      rebuild(pc.c_begin, 0, rin);
+      rebuild(pc.c_begin, 1, rin);
+      __syncthreads();
+      // Column c: rebuild column c+1 (staged in the column before), one
+      // fragment per phase.
+      for (int c = pc.c_begin; c < pc.c_end; ++c) {
+        if (c + 1 < pc.c_end) {
+          rin = prep(c + 1);
+          rebuild(c + 1, 0, rin);
         }
         __syncthreads();
+        if (c + 1 < pc.c_end) rebuild(c + 1, 1, rin);
+        __syncthreads();
       }
-    }
-    // lane l of block (rs, nb): rows 16rs + 4(l/16) + i, token 16nb + l%16.
-#pragma unroll
-    for (int rs = 0; rs < 4; ++rs)
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int n = n_base + nl + nb * 16 + row;
-        const int m = m0 + rs * 16 + 4 * kb;
-        if (n >= a.N) continue;
-        if (a.splits > 1) {
-          float* pp = a.part + (static_cast<size_t>(sidx) * a.N + n) * a.M + m;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            __hip_atomic_store(pp + i, acc[rs][nb][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-          store_y4(n, m, acc[rs][nb]);
-        }
-      }
-  } else {
-    // ---------------- producer ----------------
-    const int pw = w - 4;                 // producer wave: tokens 128pw .. +127, fragments 2pw, 2pw+1
-    const uint64_t top = a.values_alloc - 16;
-    // Values of column c into stage[buf]: chunk slot 64pw + lane + 256i of
-    // the buffer takes chunk min(slot, last) of the GroupTile's range.
-    auto dma_v = [&](int c, int buf) {
-      const uint32_t o0 = offtab[c - c_begin], o1 = offtab[c - c_begin + 1];
-      const uint64_t a0 = min(chunk_start<false>(o0), top);
-      const uint32_t nch = min(chunk_count<false>(o1, a0), static_cast<uint32_t>(kPThreads * kCpt));
-      const uint32_t last = min(nch > 0 ? nch - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
-      const uint32_t dst = lds_addr(stage[buf]) + 16 * 64 * pw;
-#pragma unroll
-      for (int i = 0; i < kCpt; ++i) {
-        const uint32_t slot = static_cast<uint32_t>(64 * pw + lane + kPThreads * i);
-        lds_dma16(src + min(slot, last), dst + 16 * kPThreads * i);
-      }
-    };
-    // The 64 bitmap words of column c into this wave's own copy (lanes 0-31,
-    // two words each).
-    const uint32_t bm_lds = lds_addr(bmw[pw]);
-    auto dma_bm = [&](int c) {
-      if (lane < 32) lds_dma16(a.bitmaps + (g_row + c) * kBtPerGt + 2 * lane, bm_lds);
-    };
-    // X half j (counted from the first column: column c_begin + j/2, k half
-    // j%2) for this wave's 128 tokens into xs[j % 3]: instruction i fills the
-    // 1 KB of slots of tokens 128pw + 16i .. +15, lane l the slot
-    // 4(128pw + 16i) + l, i.e. token n = 128pw + 16i + l/4, chunk
-    // q = (l & 3) ^ ((n >> 2) & 3).
-    auto dma_x = [&](int j) {
-      const int cc = min(c_begin + (j >> 1), c_last);
-      const uint32_t dst = lds_addr(xs[j % 3]) + 16 * 4 * 128 * pw;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int nloc = 128 * pw + 16 * i + (lane >> 2);
-        const int q = (lane & 3) ^ ((nloc >> 2) & 3);
-        const int n = min(n_base + nloc, a.N - 1);
-        lds_dma16(a.X + static_cast<size_t>(n) * a.K + cc * kGT + (j & 1) * 32 + q * 8, dst + 1024 * i);
-      }
-    };
-    const int r8 = row & 7;
-    const int bt_lane = 4 * (kb >> 1) + 2 * (row >> 3) + (kb & 1);
-    const uint64_t rowmask = (1ull << (8 * r8)) - 1ull;
-    auto prep = [&](u32x2_t bmv, int c) {
-      RbIn<2> in;
-      const uint32_t o0 = offtab[c - c_begin];
-      const uint64_t a0 = min(chunk_start<false>(o0), top);
-      const uint32_t pc = __builtin_popcount(bmv.x) + __builtin_popcount(bmv.y);
-      const uint32_t ebase = wave_inclusive_scan(pc) - pc + chunk_delta<false>(o0, a0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int f = 2 * pw + j;
-        const int bt = 16 * (f >> 1) + 8 * (f & 1) + bt_lane;
-        in.base[j] = __builtin_amdgcn_ds_bpermute(bt << 2, ebase);
-        in.lo[j] = __builtin_amdgcn_ds_bpermute(bt << 2, bmv.x);
-        in.hi[j] = __builtin_amdgcn_ds_bpermute(bt << 2, bmv.y);
-      }
-      return in;
-    };
-    auto rebuild = [&](int c, int j, const RbIn<2>& in) {
-      const int f = 2 * pw + j;
-      const uint64_t bm = (static_cast<uint64_t>(in.hi[j]) << 32) | in.lo[j];
-      const uint32_t rb = in.base[j] + __popcll(bm & rowmask);
-      const uint32_t byte = static_cast<uint32_t>(bm >> (8 * r8)) & 0xFFu;
-      abuf[c & 1][f * 64 + lane] = __builtin_bit_cast(u32x4_t, rebuild_row<false>(stage[c & 1], lut, rb, byte));
-    };
-    auto load_bm = [&](int c) { return reinterpret_cast<const u32x2_t*>(a.bitmaps + (g_row + c) * kBtPerGt)[lane]; };
-
-    const RbIn<2> rin0 = prep(load_bm(c_begin), c_begin);
-    RbIn<2> rin = prep(load_bm(min(c_begin + 1, c_last)), min(c_begin + 1, c_last));
-    dma_x(0);
-    dma_x(1);
-    dma_v(c_begin, c_begin & 1);
-    dma_v(min(c_begin + 1, c_last), (c_begin + 1) & 1);
-    USW_PRODUCER_BARRIER(0);
-    rebuild(c_begin, 0, rin0);
-    rebuild(c_begin, 1, rin0);
-    USW_PRODUCER_BARRIER(0);
-
-    // Phase t = 2 (c - c_begin) + h: consumers read X half t from xs[t % 3].
-    // First phase of column c: bitmap words and values of column c+2 (into
-    // stage[c & 1], rebuilt in the column before), X half t+2 into
-    // xs[(t+2) % 3] (read in phase t-1), fragment 2pw of column c+1.  The
-    // barrier waits for all but this phase's 11 values and X loads: the
-    // bitmap words and X half t+1.  Second phase: fragment 2pw+1 of column
-    // c+1, the rebuild inputs of c+2, X half t+3; the barrier waits for all
-    // but its 8 X loads, so the values of c+2 are in place for the next
-    // column.
-    for (int c = c_begin; c < c_end; ++c) {
-      const int t = 2 * (c - c_begin);
-      const int c2 = min(c + 2, c_last);
-      dma_bm(c2);
-      dma_v(c2, c & 1);
-      dma_x(t + 2);
-      if (c + 1 < c_end) rebuild(c + 1, 0, rin);
-      USW_PRODUCER_BARRIER(11);
-      if (c + 1 < c_end) rebuild(c + 1, 1, rin);
-      rin = prep(reinterpret_cast<const u32x2_t*>(bmw[pw])[lane], c2);
-      dma_x(t + 3);
-      USW_PRODUCER_BARRIER(8);
-    }
-    __builtin_amdgcn_s_waitcnt(0);     // no LDS write of this wave outlives it
+    });
   }
-  if (a.splits <= 1) return;
-
-  // Split K: as in prefill_kernel (consumers wrote the partial sums).
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (tid == 0)
-    last_flag = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                static_cast<uint32_t>(a.splits - 1);
-  __syncthreads();
-  if (!last_flag) return;
-  for (int e = tid; e < kBN * 16; e += 512) {
-    const int n = n_base + (e >> 4);
-    const int m = m0 + 4 * (e & 15);
-    if (n >= a.N) continue;
-    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-    for (int pp = 0; pp < a.splits; ++pp) {
-      const float* q = a.part + (static_cast<size_t>(pp) * a.N + n) * a.M + m;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sum[i] += __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    store_y4(n, m, sum);
-  }
-  if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kMinStreamCols = 8;   // fewest GroupTile columns a stream-K workgroup takes
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -611,7 +802,17 @@ PrefillPlan prefill_plan(const Geometry& g, int N, int splits_req) {
   p.waves = N > 256 ? 8 : 4;
   const int bn = 64 * p.waves;
   p.ntiles = (N + bn - 1) / bn;
+  p.wgs = 0;
   const int64_t tiles = g.Gr * p.ntiles;
+  const int64_t smin = (g.Gc + kMaxCols - 1) / kMaxCols;
+  if (p.waves == 8 && splits_req <= 0 && smin == 1) {
+    // Stream-K: every compute unit takes the same number of GroupTile
+    // columns (at least kMinStreamCols, unless the whole problem is smaller).
+    const int64_t units = tiles * g.Gc;
+    p.wgs = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kComputeUnits, units / kMinStreamCols)));
+    p.splits = 1;
+    return p;
+  }
   int64_t s = splits_req;
   if (s <= 0) {
     // One workgroup per compute unit is resident.  Split K only when the
@@ -620,20 +821,26 @@ PrefillPlan prefill_plan(const Geometry& g, int N, int splits_req) {
     s = 1;
     if (tiles * 2 <= kComputeUnits) s = std::min<int64_t>((kComputeUnits + tiles - 1) / tiles, std::max<int64_t>(1, g.Gc / 16));
   }
-  const int64_t smin = (g.Gc + kMaxCols - 1) / kMaxCols;
   p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min<int64_t>(s, g.Gc))));
   return p;
 }
 
+static bool uses_slots(const PrefillPlan& p) { return p.waves == 8 && (p.wgs > 0 || p.splits > 1); }
+
 size_t prefill_counter_bytes(const Geometry& g, const PrefillPlan& p) {
-  return p.splits > 1 ? align256(static_cast<size_t>(4) * g.Gr * p.ntiles) : 0;
+  return (p.splits > 1 || p.wgs > 0) ? align256(static_cast<size_t>(4) * g.Gr * p.ntiles) : 0;
 }
-
 size_t prefill_workspace_bytes(const Geometry& g, int N, const PrefillPlan& p) {
-  if (p.splits <= 1) return 0;
-  return prefill_counter_bytes(g, p) + static_cast<size_t>(p.splits) * N * g.M * sizeof(float);
+  const size_t cb = prefill_counter_bytes(g, p);
+  if (cb == 0) return 0;
+  if (uses_slots(p)) {
+    // Partial-sum slots of 512 tokens x 64 rows: two per stream-K workgroup
+    // (the pieces that open and close its range), one per split-K workgroup.
+    const size_t slots = p.wgs > 0 ? static_cast<size_t>(2) * p.wgs : static_cast<size_t>(g.Gr) * p.ntiles * p.splits;
+    return cb + slots * 512 * kGT * sizeof(float);
+  }
+  return cb + static_cast<size_t>(p.splits) * N * g.M * sizeof(float);
 }
-
 usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X, void* Y, bool f16out, int N, void* ws,
                           const PrefillPlan& p, void* stream) {
   PArgs a;
@@ -643,8 +850,8 @@ usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X
   a.X = X;
   a.Y = Y;
   const size_t cbytes = prefill_counter_bytes(g, p);
-  a.counters = p.splits > 1 ? static_cast<uint32_t*>(ws) : nullptr;
-  a.part = p.splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + cbytes) : nullptr;
+  a.counters = cbytes > 0 ? static_cast<uint32_t*>(ws) : nullptr;
+  a.part = cbytes > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + cbytes) : nullptr;
   a.values_alloc = values_alloc_bytes(f->val_type, f->nnz);
   a.M = static_cast<int>(g.M);
   a.K = static_cast<int>(g.K);
@@ -652,13 +859,15 @@ usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X
   a.Gc = static_cast<int>(g.Gc);
   a.splits = p.splits;
   a.ntiles = p.ntiles;
-  const int64_t nblk = g.Gr * p.ntiles * p.splits;
+  a.tiles = static_cast<int>(g.Gr * p.ntiles);
+  a.wgs = p.wgs;
+  const int64_t nblk = p.wgs > 0 ? p.wgs : g.Gr * p.ntiles * p.splits;
   a.remap = nblk % 8 == 0 ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(nblk));
   if (p.waves == 8) {
-    if (f16out) prefill_ws_kernel<true><<<grid, 512, 0, s>>>(a);
-    else prefill_ws_kernel<false><<<grid, 512, 0, s>>>(a);
+    if (f16out) prefill_ws_kernel<true><<<grid, 768, 0, s>>>(a);
+    else prefill_ws_kernel<false><<<grid, 768, 0, s>>>(a);
   } else {
     if (f16out) prefill_kernel<4, true><<<grid, 256, 0, s>>>(a);
     else prefill_kernel<4, false><<<grid, 256, 0, s>>>(a);
