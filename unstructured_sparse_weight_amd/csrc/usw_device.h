@@ -22,6 +22,13 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kGT = 64;                   // GroupTile side the kernels are built for
 constexpr int kBtPerGt = 64;              // BitmapTiles per 64x64 GroupTile
 
+// Buffer resource word 3 for raw byte-addressed buffers on this target, and
+// the cache-policy operand that sets sc1: the access goes to the level that
+// is coherent across the device (all XCDs), as agent-scope atomics do.
+// Partial sums shared between workgroups travel this way, 16 bytes at a time.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCacheSc1 = 16;
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -330,12 +330,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a)
   if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Buffer resource word 3 for raw 32-bit-addressed buffers on this target,
-// and the cache-policy operand that sets sc1: the access goes to the level
-// that is coherent across the device, as agent-scope atomics do.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-constexpr int kCacheSc1 = 16;
-
 // global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS byte address
 // lds + 16 l (lds the same in every lane; it goes to M0), counted by vmcnt
 // like any vector load.  Issued through asm so that the compiler, which

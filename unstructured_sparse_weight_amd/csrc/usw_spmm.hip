@@ -504,35 +504,52 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   __syncthreads();
 
   const int m0 = gi * kGT;
-  auto store_y = [&](int n, int ml, float sum) {
-    if constexpr (I4) sum *= static_cast<float>(__builtin_bit_cast(_Float16, a.scales[m0 + ml]));
-    const size_t yi = static_cast<size_t>(n) * a.M + m0 + ml;
-    if constexpr (OUT_F16)
-      reinterpret_cast<_Float16*>(a.Y)[yi] = static_cast<_Float16>(sum);
-    else
-      reinterpret_cast<float*>(a.Y)[yi] = sum;
-  };
-  for (int e = tid; e < 64 * 16 * NB; e += kThreads) {
-    const int n = e >> 6;
-    const int ml = e & 63;
-    if (n >= a.N) continue;
-    // Strip row ml sits in accumulator acc_of_row(ml) at D row
-    // drow_of_row(ml) = 4 * (lane / 16) + i.
-    const int rs = acc_of_row(ml);
-    const int dr = drow_of_row(ml);
-    const int ln = ((dr >> 2) << 4) | (n & 15);
-    const int i = dr & 3;
-    const int nb = n >> 4;
-    float sum = 0.f;
+  // Y[n][m0 + ml .. +3] from four consecutive row sums.
+  auto store_y4 = [&](int n, int ml, f32x4_t v) {
+    if constexpr (I4) {
 #pragma unroll
-    for (int ww = 0; ww < kW; ++ww) sum += red[(((ww * 4 + rs) * NB + nb) * 64 + ln) * 4 + i];
+      for (int j = 0; j < 4; ++j) v[j] *= static_cast<float>(__builtin_bit_cast(_Float16, a.scales[m0 + ml + j]));
+    }
+    const size_t yi = static_cast<size_t>(n) * a.M + m0 + ml;
+    if constexpr (OUT_F16) {
+      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+      half4_t h;
+      h.x = static_cast<_Float16>(v.x);
+      h.y = static_cast<_Float16>(v.y);
+      h.z = static_cast<_Float16>(v.z);
+      h.w = static_cast<_Float16>(v.w);
+      *reinterpret_cast<half4_t*>(reinterpret_cast<_Float16*>(a.Y) + yi) = h;
+    } else {
+      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.Y) + yi) = v;
+    }
+  };
+  // Partial sums of split s: [N][M] fp32 at part + s N M, read and written
+  // with device-coherent (sc1) 16-byte accesses.
+  auto part_rsrc = [&](int s) {
+    return __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(s) * a.N * a.M, 0, a.N * a.M * 4,
+                                             kBufferRsrcWord3);
+  };
+  // Thread element e: token n = e / 16, strip rows ml = 4 (e % 16) .. +3.
+  for (int e = tid; e < 16 * 16 * NB; e += kThreads) {
+    const int n = e >> 4;
+    const int ml = 4 * (e & 15);
+    if (n >= a.N) continue;
+    // Strip row ml + j sits in accumulator acc_of_row(ml) (the same for the
+    // four rows) at D row drow_of_row(ml + j) = 4 j + (ml / 8) % 4, i.e.
+    // lane 16 j + n % 16, register (ml / 8) % 4.
+    const int rs = acc_of_row(ml);
+    const int i = drow_of_row(ml) & 3;
+    const int nb = n >> 4;
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < kW; ++ww)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum[j] += red[(((ww * 4 + rs) * NB + nb) * 64 + 16 * j + (n & 15)) * 4 + i];
     if (a.splits > 1)
-      // Device-coherent store: it reaches the level every XCD reads from, so
-      // no L2 write-back of the whole cache is needed before the counter.
-      __hip_atomic_store(&a.part[(static_cast<size_t>(sidx) * a.N + n) * a.M + m0 + ml], sum, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sum), part_rsrc(sidx),
+                                             (n * a.M + m0 + ml) * 4, 0, kCacheSc1);
     else
-      store_y(n, ml, sum);
+      store_y4(n, ml, sum);
   }
   if (a.splits <= 1) return;
 
@@ -551,14 +568,23 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
                 static_cast<uint32_t>(a.splits - 1);
   __syncthreads();
   if (!last_flag) return;
-  for (int e = tid; e < 64 * a.N; e += kThreads) {
-    const int n = e >> 6;
-    const int ml = e & 63;
-    float sum = 0.f;
-    for (int p = 0; p < a.splits; ++p)
-      sum += __hip_atomic_load(&a.part[(static_cast<size_t>(p) * a.N + n) * a.M + m0 + ml], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    store_y(n, ml, sum);
+  for (int e = tid; e < 16 * a.N; e += kThreads) {
+    const int n = e >> 4;
+    const int ml = 4 * (e & 15);
+    const int off = (n * a.M + m0 + ml) * 4;
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+    // Up to four splits' loads in flight at once; added in split order.
+    for (int p0 = 0; p0 < a.splits; p0 += 4) {
+      f32x4_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (p0 + j < a.splits)
+          v[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(part_rsrc(p0 + j), off, 0, kCacheSc1));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (p0 + j < a.splits) sum += v[j];
+    }
+    store_y4(n, ml, sum);
   }
   if (tid == 0) __hip_atomic_store(&a.counters[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
