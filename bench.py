@@ -56,6 +56,10 @@ def parse():
     p.add_argument("--sparsity", type=float, default=0.5)
     p.add_argument("--dtype", default="f16", choices=["f16", "i4"])
     p.add_argument("--cpu-reps", type=int, default=5)
+    p.add_argument("--rotation", type=int, default=0,
+                   help="number of encoded copies the steps rotate over (default: enough for > 512 MB, so reads come"
+                        " from HBM; 1 keeps a layer resident in the 256 MB Infinity Cache, which is not the"
+                        " measured configuration)")
     p.add_argument("--eager", action="store_true",
                    help="launch each timed step from Python with its own pair of HIP events instead of replaying"
                         " the steps from a HIP graph")
@@ -159,7 +163,7 @@ def main():
     vbytes = 2.0 if args.dtype == "f16" else 0.5
     alg = algorithmic_bytes(M, K, N, h.nnz, ngt, vbytes, 2, args.dtype == "i4")
     enc_bytes = h.bitmaps.nbytes + h.offsets.nbytes + h.values.nbytes
-    R = max(5, math.ceil(600e6 / enc_bytes))
+    R = args.rotation if args.rotation > 0 else max(5, math.ceil(600e6 / enc_bytes))
     encs = [usw.to_device(h, dev) for _ in range(R)]
     xs = [torch.from_numpy(X).to(dev) for _ in range(R)]
     ys = [torch.empty((N, M), dtype=torch.float16, device=dev) for _ in range(R)]
@@ -226,12 +230,30 @@ def main():
         kern_med_ms = kern_avg_ms
     ms_step = (t1 - t0) * 1e3 / args.steps
 
+    # Streaming-read ceiling: the library's plain read kernel over 1 GiB
+    # (more than the 256 MB Infinity Cache), same stream, HIP events.
+    probe = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1 << 12, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        L.usw_probe_read(probe.data_ptr(), probe.numel(), sink.data_ptr(), sp)
+    pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a_, b_ in pe:
+        a_.record(stream)
+        st = L.usw_probe_read(probe.data_ptr(), probe.numel(), sink.data_ptr(), sp)
+        b_.record(stream)
+        if st != 0:
+            raise RuntimeError(f"usw_probe_read failed: {st}")
+    torch.cuda.synchronize()
+    stream_gbps = probe.numel() / (float(np.median([a_.elapsed_time(b_) for a_, b_ in pe])) * 1e-3) / 1e9
+    del probe, sink
+
     flops = 2.0 * M * K * N
     value = flops / (ms_step * 1e-3) / 1e12
     gbps_step = alg / (ms_step * 1e-3) / 1e9
     achieved = alg / (kern_avg_ms * 1e-3) / 1e9
     log(f"[bench] step {ms_step * 1e3:.2f} us, kernel avg {kern_avg_ms * 1e3:.2f} us (median {kern_med_ms * 1e3:.2f}),"
-        f" {achieved:.0f} GB/s algorithmic, {flops / (kern_avg_ms * 1e-3) / 1e12:.1f} eff TFLOP/s")
+        f" {achieved:.0f} GB/s algorithmic, {flops / (kern_avg_ms * 1e-3) / 1e12:.1f} eff TFLOP/s;"
+        f" streaming-read ceiling {stream_gbps:.0f} GB/s")
 
     # Dense fp16 baseline of the same shape and rotation (hipBLASLt through
     # torch.matmul); its output also serves as a sanity check of the timed
@@ -279,7 +301,9 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": kname,
-                    "kernel_avg_us": round(kern_avg_ms * 1e3, 3), "alg_bytes_per_launch": int(alg)}
+                    "kernel_avg_us": round(kern_avg_ms * 1e3, 3), "alg_bytes_per_launch": int(alg),
+                    "streaming_read_ceiling": round(stream_gbps, 1),
+                    "frac_of_streaming_ceiling": round(achieved / stream_gbps, 4)}
     if (M, K) == (20480, 5120):
         workload = f"opt13b_ffn_up_{M}x{K}_s{s}_N{N}"
     elif prefill and (M, K) in ((11008, 4096), (4096, 11008)):
@@ -330,13 +354,35 @@ def cpu_baseline(W, mask, X, M, K, N, dtype, reps):
         times.append(time.perf_counter() - t)
         del Y
     best = min(times)
+    # One more run with the BLAS pool held to a single thread.
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t = time.perf_counter()
+            Y = ob.spmm(enc, X)
+            single = time.perf_counter() - t
+            del Y
+    except ImportError:
+        pass
     cores = len(os.sched_getaffinity(0))
     threads = os.environ.get("OMP_NUM_THREADS")
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(2.0 * M * K * N / best / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "blas_threads": int(threads) if threads and threads.isdigit() else cores, "kind": "oracle",
             "sample": f"whole layer {M}x{K}, N={N}: decode + fp64 matmul, best of {reps} ({sum(times):.1f} s total);"
                       f" oracle encode {t_enc:.1f} s excluded",
-            "seconds_per_step": round(best, 3)}
+            "seconds_per_step": round(best, 3),
+            "single_thread_seconds_per_step": round(single, 3) if single is not None else None,
+            "cpu_model": model}
 
 
 if __name__ == "__main__":

@@ -205,6 +205,19 @@ usw_status usw_spmm_counter_bytes(const usw_fmt* fmt, int32_t N, int32_t splits,
 usw_status usw_spmm_ex(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y_type, int32_t N, int32_t splits,
                        void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Measurement utility, not part of the SpMM path: reads the first
+ * bytes / 16 * 16 bytes of the device buffer buf once (16-byte loads,
+ * non-temporal) on the stream, so that a caller can time the GPU's
+ * streaming-read rate, the practical ceiling of the memory-bound SpMM.
+ *   buf:  device pointer, 16-byte aligned.
+ *   sink: device buffer of at least ceil(bytes / 262144) uint32 words; the
+ *         kernel may write some of them (their values carry no meaning).
+ * Errors: NULL_ARG, MISALIGNED, BAD_SHAPE (more than 2^31 - 1 blocks of
+ * 256 KB), HIP.
+ */
+usw_status usw_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

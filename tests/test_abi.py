@@ -194,6 +194,12 @@ def test_argument_errors_return_before_launch():
     assert L.usw_spmm_ex(B(fw), xw.ctypes.data, ya, 1, 8, 2, None, 0, None) == -7
     small = np.zeros(16, np.uint8)
     assert L.usw_spmm_ex(B(fw), xw.ctypes.data, ya, 1, 8, 2, small.ctypes.data, 16, None) == -7
+    # streaming-read probe: argument errors, and nothing to read, return
+    # before any launch
+    assert L.usw_probe_read(None, 1024, ya, None) == -1
+    assert L.usw_probe_read(xa, 1024, None, None) == -1
+    assert L.usw_probe_read(xa + 4, 1024, ya, None) == -6
+    assert L.usw_probe_read(xa, 15, ya, None) == 0
     # encode argument checks
     nnz = ctypes.c_int64()
     assert L.usw_encode_query(None, None, 256, 256, 64, 64, 1, B(nnz), None, None, None, None, None) == -1

@@ -6,6 +6,7 @@ error <= 1e-3 and |error| <= 2e-3 * sum|w||x| per output); integer-exact
 inputs (dyadic W, small-integer X, power-of-two INT4 scales) must match the
 oracle bit for bit, whatever the summation order.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -297,3 +298,15 @@ def test_full_size_integer_exact_bitwise():
     Y = run_gpu(W, mask, X, out=torch.float32)
     Wd = np.where(mask, W, np.float16(0))
     assert np.array_equal(Y, ob.spmm_fp64(Wd, X))
+
+
+def test_probe_read_runs():
+    """The streaming-read probe bench.py reports the memory-bound kernels
+    against: it reads a device buffer and returns OK; a ragged byte count
+    reads the whole 16-byte units only."""
+    L = usw.lib()
+    buf = torch.randint(0, 255, (3 * 262144 + 100,), dtype=torch.uint8, device=DEV)
+    sink = torch.zeros(8, dtype=torch.int32, device=DEV)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.usw_probe_read(buf.data_ptr(), buf.numel(), sink.data_ptr(), stream) == 0
+    torch.cuda.synchronize()

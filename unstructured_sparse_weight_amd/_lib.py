@@ -26,6 +26,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "usw_abi_version", "usw_status_str", "usw_encode_query", "usw_encode", "usw_validate",
     "usw_spmm_workspace", "usw_spmm", "usw_spmm_workspace_ex", "usw_spmm_ex", "usw_spmm_counter_bytes",
+    "usw_probe_read",
 )
 
 
@@ -74,6 +75,8 @@ def _declare(lib):
     lib.usw_spmm_ex.argtypes = [P(UswFmt), c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]
     lib.usw_spmm_counter_bytes.restype = c_i32
     lib.usw_spmm_counter_bytes.argtypes = [P(UswFmt), c_i32, c_i32, P(c_sz)]
+    lib.usw_probe_read.restype = c_i32
+    lib.usw_probe_read.argtypes = [ctypes.c_void_p, c_sz, ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
