@@ -352,14 +352,15 @@ __device__ __forceinline__ uint32_t lds_addr(T* p) {
 // and its LDS operations are done, then a workgroup barrier.
 #define USW_PRODUCER_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" : : : "memory")
 
-// The same for a wave-uniform count n in [8, 12].
+// The same for a wave-uniform count n in [8, 12]; any other count waits as
+// for 8 (never for fewer loads than asked).
 __device__ __forceinline__ void producer_barrier(int n) {
   switch (__builtin_amdgcn_readfirstlane(n)) {
-    case 8: USW_PRODUCER_BARRIER(8); break;
     case 9: USW_PRODUCER_BARRIER(9); break;
     case 10: USW_PRODUCER_BARRIER(10); break;
     case 11: USW_PRODUCER_BARRIER(11); break;
-    default: USW_PRODUCER_BARRIER(12); break;
+    case 12: USW_PRODUCER_BARRIER(12); break;
+    default: USW_PRODUCER_BARRIER(8); break;
   }
 }
 
@@ -405,14 +406,14 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
   constexpr int kStageBytes = kPThreads * kCpt * 16 + 16;
   constexpr int kSlot = kBN * kGT;                                    // floats per partial-sum slot
 
-  __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[3][kStageBytes];   // values of columns c .. c+2 (by c % 3)
   __shared__ __attribute__((aligned(16))) u32x4_t abuf[2][8 * 64];
   // X tile halves: xs[b][4n + (q ^ ((n >> 2) & 3))] holds the 16-byte chunk q
   // (k = 32h + 8q .. +7) of token n of the tile; a fragment read (16 tokens,
   // one chunk) covers 16 distinct bank groups.
   __shared__ __attribute__((aligned(16))) u32x4_t xs[3][kBN * 4];
   __shared__ __attribute__((aligned(16))) uint32_t lut[32];
-  __shared__ __attribute__((aligned(16))) u32x2_t bmw[2][64];   // bitmap words of columns c, c+1 (by c & 1)
+  __shared__ __attribute__((aligned(16))) u32x2_t bmw[3][64];   // their bitmap words
   __shared__ uint32_t offtab[kMaxCols + 1];
   __shared__ uint32_t last_flag;
 
@@ -597,7 +598,7 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      __syncthreads();   // loaders: X halves 0, 1 and two columns' values landed
+      __syncthreads();   // loaders: X halves 0, 1 and three columns' values landed
       __syncthreads();   // builders: first column's A tile rebuilt
       for (int c = pc.c_begin; c < pc.c_end; ++c) {
 #pragma unroll
@@ -606,14 +607,24 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
           u32x4_t af[4];
 #pragma unroll
           for (int rs = 0; rs < 4; ++rs) af[rs] = abuf[c & 1][(rs * 2 + h) * 64 + lane];
+          u32x4_t bf[8];
 #pragma unroll
-          for (int nb = 0; nb < 8; ++nb) {
-            const u32x4_t bf = xb[xslot(nl + 16 * nb + row, kb)];
+          for (int nb = 0; nb < 8; ++nb) bf[nb] = xb[xslot(nl + 16 * nb + row, kb)];
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
             for (int rs = 0; rs < 4; ++rs)
               acc[rs][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, af[rs]),
-                                                                   __builtin_bit_cast(half8_t, bf), acc[rs][nb], 0,
+                                                                   __builtin_bit_cast(half8_t, bf[nb]), acc[rs][nb], 0,
                                                                    0, 0);
+          // Schedule: the 4 A reads and the first 2 X^T reads, then for each
+          // X^T fragment its 4 MFMAs followed by the read 2 fragments ahead,
+          // so that two LDS reads are always in flight behind the MFMAs.
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            if (nb + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
           __syncthreads();
         }
@@ -646,17 +657,17 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
     for_pieces([&](const Piece& pc) {
       const int dw = w - 4;               // X of tokens 128dw .. +127; value chunk slots 64dw + 256i + lane
       const uint64_t top = a.values_alloc - 16;
-      // Values of column c into stage[buf]: slot 64dw + lane + 256i of the
-      // buffer takes chunk slot of the GroupTile's range; an instruction
+      // Values of column c into stage[c % 3]: slot 64dw + lane + 256i of
+      // the buffer takes chunk slot of the GroupTile's range; an instruction
       // whose 64 slots all lie past the range is not issued.  Returns how
       // many were.
-      auto dma_v = [&](int c, int buf) {
+      auto dma_v = [&](int c) {
         const uint32_t o0 = offtab[c - pc.c_begin], o1 = offtab[c - pc.c_begin + 1];
         const uint64_t a0 = min(chunk_start<false>(o0), top);
         const uint32_t nch = __builtin_amdgcn_readfirstlane(
             min(chunk_count<false>(o1, a0), static_cast<uint32_t>((top - a0) >> 4) + 1u));
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
-        const uint32_t dst = lds_addr(stage[buf]) + 16 * 64 * dw;
+        const uint32_t dst = lds_addr(stage[c % 3]) + 16 * 64 * dw;
         int issued = 0;
 #pragma unroll
         for (int i = 0; i < kCpt; ++i) {
@@ -668,11 +679,11 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
         }
         return issued;
       };
-      // The 64 bitmap words of column c into bmw[c & 1] (loader 0, lanes
+      // The 64 bitmap words of column c into bmw[c % 3] (loader 0, lanes
       // 0-31, two words each).  Returns how many loads this wave issued.
       auto dma_bm = [&](int c) {
         if (dw != 0) return 0;
-        if (lane < 32) lds_dma16(a.bitmaps + (pc.g_row + c) * kBtPerGt + 2 * lane, lds_addr(bmw[c & 1]));
+        if (lane < 32) lds_dma16(a.bitmaps + (pc.g_row + c) * kBtPerGt + 2 * lane, lds_addr(bmw[c % 3]));
         return 1;
       };
       // X half j (counted from the first column: column pc.c_begin + j/2, k
@@ -692,37 +703,33 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
         }
       };
 
-      const int c1 = min(pc.c_begin + 1, pc.c_last);
       dma_x(0);
       dma_x(1);
-      dma_bm(pc.c_begin);
-      dma_v(pc.c_begin, pc.c_begin & 1);
-      if (c1 != pc.c_begin) {
-        dma_bm(c1);
-        dma_v(c1, c1 & 1);
+      for (int c = pc.c_begin; c < min(pc.c_begin + 3, pc.c_end); ++c) {
+        dma_bm(c);
+        dma_v(c);
       }
       USW_PRODUCER_BARRIER(0);
       USW_PRODUCER_BARRIER(0);   // builders: first column's A tile rebuilt
 
       // Phase t = 2 (c - pc.c_begin) + h: consumers read X half t from
-      // xs[t % 3].  First phase of column c: the bitmap words and values of
-      // column c+2 (into bmw[c & 1] and stage[c & 1], both read for column
-      // c in the column before), then X half t+2 into xs[(t+2) % 3] (read
-      // in phase t-1).  All of them may still be in flight at the barrier;
-      // X half t+1 has landed.  Second phase: X half t+3; everything older
-      // than it lands before the barrier, so column c+2's values and bitmap
-      // words are in place for the builders of the next column.
+      // xs[t % 3].  First phase of column c: X half t+2 into xs[(t+2) % 3]
+      // (read in phase t-1); at the barrier everything older has landed: X
+      // half t+1 and column c+2's values and bitmap words.  Second phase: X
+      // half t+3, then the bitmap words and values of column c+3 into
+      // bmw[c % 3] and stage[c % 3] (read for column c in the column
+      // before); at the barrier X half t+2 has landed.
       for (int c = pc.c_begin; c < pc.c_end; ++c) {
         const int t = 2 * (c - pc.c_begin);
-        int n = 8;
-        if (c + 2 < pc.c_end) {
-          n += dma_bm(c + 2);
-          n += dma_v(c + 2, c & 1);
-        }
         dma_x(t + 2);
-        producer_barrier(n);
-        dma_x(t + 3);
         USW_PRODUCER_BARRIER(8);
+        dma_x(t + 3);
+        int n = 8;
+        if (c + 3 < pc.c_end) {
+          n += dma_bm(c + 3);
+          n += dma_v(c + 3);
+        }
+        producer_barrier(n);
       }
       __builtin_amdgcn_s_waitcnt(0);   // no LDS write of this wave outlives the piece
     });
@@ -738,7 +745,7 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
       // BitmapTile row a lane rebuilds, the bitmap and the element index of
       // the tile's first value inside the staged chunk range.
       auto prep = [&](int c) {
-        const u32x2_t bmv = reinterpret_cast<const u32x2_t*>(bmw[c & 1])[lane];
+        const u32x2_t bmv = reinterpret_cast<const u32x2_t*>(bmw[c % 3])[lane];
         RbIn<2> in;
         const uint32_t o0 = offtab[c - pc.c_begin];
         const uint64_t a0 = min(chunk_start<false>(o0), top);
@@ -759,15 +766,15 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
         const uint64_t bm = (static_cast<uint64_t>(in.hi[j]) << 32) | in.lo[j];
         const uint32_t rb = in.base[j] + __popcll(bm & rowmask);
         const uint32_t byte = static_cast<uint32_t>(bm >> (8 * r8)) & 0xFFu;
-        abuf[c & 1][f * 64 + lane] = __builtin_bit_cast(u32x4_t, rebuild_row<false>(stage[c & 1], lut, rb, byte));
+        abuf[c & 1][f * 64 + lane] = __builtin_bit_cast(u32x4_t, rebuild_row<false>(stage[c % 3], lut, rb, byte));
       };
 
-      __syncthreads();   // loaders: first two columns' values and bitmap words landed
+      __syncthreads();   // loaders: first three columns' values and bitmap words landed
       RbIn<2> rin = prep(pc.c_begin);
       rebuild(pc.c_begin, 0, rin);
       rebuild(pc.c_begin, 1, rin);
       __syncthreads();
-      // Column c: rebuild column c+1 (staged in the column before), one
+      // Column c: rebuild column c+1 (staged two columns before), one
       // fragment per phase.
       for (int c = pc.c_begin; c < pc.c_end; ++c) {
         if (c + 1 < pc.c_end) {
