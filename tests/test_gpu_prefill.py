@@ -240,3 +240,18 @@ def test_prefill_stream_k_deterministic():
     assert np.array_equal(Ya, Yb)
     Yref, Bnd = ref(W, mask, X)
     check(Ya, Yref, Bnd, "prefill stream-K")
+
+
+def test_prefill_ws_long_k_split():
+    """N > 256 with K > 65536 (1040 GroupTile columns): more columns than the
+    512-token kernel stages per workgroup, so the automatic split falls back
+    from stream-K to split K (two splits); integer-exact, so bit for bit."""
+    M, K, N = 64, 66560, 300
+    rng = np.random.default_rng(515)
+    W = wl.weight_dyadic(M, K, rng)
+    mask = wl.mask_bernoulli(M, K, 0.5, rng)
+    X = wl.activations_small_int(N, K, rng)
+    say(f"[prefill long K] {M}x{K} N={N}")
+    h = usw.encode_host(W, mask)
+    Wd = np.where(mask, W, np.float16(0))
+    assert np.array_equal(gpu(h, X, torch.float32), ob.spmm_fp64(Wd, X))
