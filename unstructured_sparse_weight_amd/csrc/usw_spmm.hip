@@ -19,13 +19,16 @@
 //     (clamped indices), so the compiler waits for exactly the slot in use.
 //   * Rebuild: v_mfma_f32_16x16x32_f16 gives lane l 8 consecutive columns
 //     8*(l/16)..+7 of one row of a 16x32 block, which is exactly one row of
-//     one BitmapTile; its kept values are contiguous in the stream.  Rows are
-//     assigned so that a lane rebuilds rows r and r+4 of four BitmapTiles
-//     per GroupTile.  The lane finds where a row's values start (GroupTile
-//     offset + popcounts of the earlier BitmapTiles, from a DPP wave prefix
-//     scan, + popcount of the earlier rows of its own BitmapTile) and expands
-//     them into 8 slots with two aligned LDS windows and v_perm_b32 byte
-//     selectors looked up by the row's 4-bit halves (zero for clear bits).
+//     one BitmapTile; its kept values are contiguous in the stream.  A
+//     fragment is one TCTile row (16 strip rows) by four BitmapTile columns,
+//     so the 32 lanes the LDS serves together read rows of a single TCTile,
+//     whose values are contiguous (few bank conflicts).  Where each
+//     BitmapTile's values start (GroupTile offset + a DPP wave prefix scan of
+//     the BitmapTile popcounts) goes with its bitmap words into a small LDS
+//     table one GroupTile ahead; a lane reads its row's word and base, adds
+//     the popcount of the earlier rows, and expands the row into 8 slots with
+//     two aligned LDS windows and v_perm_b32 byte selectors looked up by the
+//     row's 4-bit halves (zero for clear bits).
 //   * The rebuilt fragment meets the X^T fragment (X is [N][K], so each
 //     lane's 8 k values are one 16-byte load) on the matrix cores with fp32
 //     accumulation, which leaves the vector ALUs to the rebuild.
@@ -107,6 +110,9 @@ __device__ __forceinline__ void slot_load(Slot<NB, I4>& s, const Args& a, int gi
   const int64_t g = static_cast<int64_t>(gi) * a.Gc + c;
   // The clamps keep every load inside the padded allocation and every store
   // inside the LDS buffer even for offsets that disagree with the bitmaps.
+  // Bitmaps first: the bitmap table of a slot is written while its values
+  // and X^T fragments may still be in flight.
+  s.bm = reinterpret_cast<const u32x2_t*>(a.bitmaps + g * kBtPerGt)[lane];
   const uint64_t top = a.values_alloc - 16;
   s.a0 = min(chunk_start<I4>(o0), top);
   s.delta = chunk_delta<I4>(o0, s.a0);
@@ -117,7 +123,6 @@ __device__ __forceinline__ void slot_load(Slot<NB, I4>& s, const Args& a, int gi
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + s.a0);
 #pragma unroll
   for (int i = 0; i < ValTraits<I4>::kChunks; ++i) s.v[i] = src[min(static_cast<uint32_t>(lane + 64 * i), last)];
-  s.bm = reinterpret_cast<const u32x2_t*>(a.bitmaps + g * kBtPerGt)[lane];
   // X^T fragments.  Columns n >= N of B only feed columns n >= N of the
   // product, which are never stored, so those lanes just repeat row N-1.
   const int row = lane & 15, kb = lane >> 4;
@@ -130,143 +135,87 @@ __device__ __forceinline__ void slot_load(Slot<NB, I4>& s, const Args& a, int gi
     }
 }
 
-template <int NB, bool I4, bool BITMAPS = false>
-__device__ __forceinline__ void slot_commit(const Slot<NB, I4>& s, uint8_t* vb, uint64_t* bb, int lane) {
+template <int NB, bool I4>
+__device__ __forceinline__ void slot_commit(const Slot<NB, I4>& s, uint8_t* vb, int lane) {
 #pragma unroll
   for (int i = 0; i < ValTraits<I4>::kChunks; ++i) reinterpret_cast<u32x4_t*>(vb)[lane + 64 * i] = s.v[i];
-  if constexpr (BITMAPS) reinterpret_cast<u32x2_t*>(bb)[lane] = s.bm;
 }
 
-// Which rows a lane rebuilds.  The A fragments of a GroupTile come in two
-// halves H (BitmapTile rows 4H .. 4H+3 of the GroupTile, i.e. TCTile rows 2H
-// and 2H+1, whose values are contiguous in the stream).  In fragment
-// (H, jj, ks), lane l with i = l % 16 and g = l / 16 holds row 4jj + i/4 of
-// the BitmapTile in BitmapTile row R = 4H + i%4 and BitmapTile column
-// C = 4ks + g, i.e. columns 8C .. 8C+7: the k layout of the fragment is the
-// usual one, and D row i of the fragment is row 8R + 4jj + i/4 of the strip.
-// A lane thus rebuilds rows r and r + 4 (r = i/4) of 4 BitmapTiles per
-// GroupTile, reading each bitmap once.
+// Which rows a lane rebuilds.  Fragment (f, ks) of a GroupTile (f = 0..3,
+// ks = 0, 1) is the 16 x 32 block of strip rows 16f .. 16f+15 and GroupTile
+// columns 32ks .. 32ks+31.  Lane l with i = l % 16 and g = l / 16 holds row i,
+// columns 8g .. 8g+7 of the block, which is row r = i % 8 of the BitmapTile
+// in BitmapTile row R = 2f + i / 8 and BitmapTile column C = 4ks + g.  The
+// 32 lanes that the LDS serves together (g = 0, 1 or g = 2, 3) thus read the
+// rows of one TCTile, whose values are contiguous, so their windows spread
+// over few bytes and few bank conflicts; and D row i of fragment f is strip
+// row 16f + i.
 struct LaneMap {
-  int bt[2][2];      // [H][ks]: the lane's BitmapTile, in storage order
-  uint32_t sh;       // 8r: bit offset of row r in a bitmap word
-  uint32_t pmask;    // bits of rows 0 .. r-1
+  uint32_t tab;     // byte offset of the lane's entry for f = ks = 0 in the bitmap table
+  uint32_t sh;      // 8 (r % 4): bit offset of row r in its bitmap word
+  uint32_t pmask;   // bits of the rows before r in that word
 };
 
 __device__ __forceinline__ LaneMap lane_map(int lane) {
+  const int i = lane & 15, g = lane >> 4, r = i & 7;
+  // BitmapTile (R, C) is number 16 (R / 2) + 4 (C / 2) + 2 (R % 2) + C % 2 in
+  // storage order (TCTiles row-major, BitmapTiles row-major inside them);
+  // fragment (f, ks) adds 16 f + 8 ks to the BitmapTile number below.
+  const int bt = 4 * (g >> 1) + 2 * (i >> 3) + (g & 1);
   LaneMap m;
-  const int i = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int R = 4 * h + (i & 3), C = 4 * ks + g;
-      // TCTiles row-major (4 per row), BitmapTiles row-major inside a TCTile.
-      m.bt[h][ks] = 16 * (R >> 1) + 4 * (C >> 1) + 2 * (R & 1) + (C & 1);
-    }
-  m.sh = 8u * static_cast<uint32_t>(i >> 2);
+  m.tab = 16u * static_cast<uint32_t>(bt) + 8u * static_cast<uint32_t>(r >> 2);
+  m.sh = 8u * static_cast<uint32_t>(r & 3);
   m.pmask = (1u << m.sh) - 1u;
   return m;
 }
 
-// Row of the strip that accumulator acc[j] (j = 2H + jj) holds at D row i,
-// and its inverse (used by the workgroup reduction); checked at compile time.
-constexpr int strip_row(int j, int i) { return 32 * (j >> 1) + 8 * (i & 3) + 4 * (j & 1) + (i >> 2); }
-constexpr int acc_of_row(int ml) { return 2 * (ml >> 5) + ((ml >> 2) & 1); }
-constexpr int drow_of_row(int ml) { return 4 * (ml & 3) + ((ml >> 3) & 3); }
-constexpr bool strip_map_is_inverse() {
-  for (int ml = 0; ml < 64; ++ml)
-    if (strip_row(acc_of_row(ml), drow_of_row(ml)) != ml) return false;
-  return true;
-}
-static_assert(strip_map_is_inverse(), "row map of the A fragments");
+constexpr int kTabBytes = 16 * kBtPerGt;
 
-// Rebuild and multiply half H of a GroupTile whose bitmaps are in bb and
-// whose values are in the LDS buffer at vbase; ebase (lane t) is where
-// BitmapTile t's values start, counted from vbase.
-template <int NB, bool I4, int H>
-__device__ __forceinline__ void tile_half(const u32x4_t (&x)[2][NB], const uint8_t* vbase, const uint64_t* bb,
-                                          const uint32_t* lut, f32x4_t (&acc)[4][NB], uint32_t ebase,
-                                          const LaneMap& lm) {
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int bt = lm.bt[H][ks];
-    const uint64_t bm = bb[bt];
-    const uint32_t lo = static_cast<uint32_t>(bm), hi = static_cast<uint32_t>(bm >> 32);
-    const uint32_t base = __builtin_amdgcn_ds_bpermute(bt << 2, ebase);
-    // Row r starts after the set bits of rows 0 .. r-1; row r + 4 after
-    // those of rows 0 .. r+3 (the 32 bits from bit 8r on cover rows r .. r+3).
-    const uint32_t rb0 = base + __builtin_popcount(lo & lm.pmask);
-    const uint32_t rb1 = rb0 + __builtin_popcount(__builtin_amdgcn_alignbit(hi, lo, lm.sh));
-    const half8_t a0 = rebuild_row<I4>(vbase, lut, rb0, (lo >> lm.sh) & 0xFFu);
-    const half8_t a1 = rebuild_row<I4>(vbase, lut, rb1, (hi >> lm.sh) & 0xFFu);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      acc[2 * H][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, __builtin_bit_cast(half8_t, x[ks][nb]),
-                                                              acc[2 * H][nb], 0, 0, 0);
-      acc[2 * H + 1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, __builtin_bit_cast(half8_t, x[ks][nb]),
-                                                                  acc[2 * H + 1][nb], 0, 0, 0);
-    }
-  }
+// Bitmap table of a GroupTile in LDS, 16 bytes per BitmapTile, written by
+// lane t for BitmapTile t: bitmap rows 0-3, where row 0's values start,
+// bitmap rows 4-7, where row 4's values start (value positions counted in
+// elements from the start of the staging area).  base is where the
+// BitmapTile's values start.
+__device__ __forceinline__ void tab_write(uint8_t* tab, u32x2_t bm, uint32_t base, int lane) {
+  u32x4_t e;
+  e.x = bm.x;
+  e.y = base;
+  e.z = bm.y;
+  e.w = base + __builtin_popcount(bm.x);
+  reinterpret_cast<u32x4_t*>(tab)[lane] = e;
 }
 
-// What a lane needs from a GroupTile's bitmaps: the bitmap words and value
-// bases of its four BitmapTiles, taken with ds_bpermute from the slot's
-// registers (lane t holds bitmap word t; ebase lane t is where BitmapTile t's
-// values start).  Nothing here waits for the slot's copy into LDS.
-struct RowsIn {
-  uint32_t lo[2][2], hi[2][2], base[2][2];
-};
-
-__device__ __forceinline__ RowsIn rows_in(u32x2_t bm, uint32_t ebase, const LaneMap& lm) {
-  RowsIn r;
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int addr = lm.bt[h][ks] << 2;
-      r.lo[h][ks] = __builtin_amdgcn_ds_bpermute(addr, bm.x);
-      r.hi[h][ks] = __builtin_amdgcn_ds_bpermute(addr, bm.y);
-      r.base[h][ks] = __builtin_amdgcn_ds_bpermute(addr, ebase);
-    }
-  return r;
-}
-
-// Rebuild and multiply a whole GroupTile (both halves) whose values are in
-// the LDS buffer at vbase.
-template <int NB, bool I4>
-__device__ __forceinline__ void tile_full(const u32x4_t (&x)[2][NB], const uint8_t* vbase, const RowsIn& in,
-                                          const uint32_t* lut, f32x4_t (&acc)[4][NB], const LaneMap& lm) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t lo = in.lo[h][ks], hi = in.hi[h][ks];
-      const uint32_t rb0 = in.base[h][ks] + __builtin_popcount(lo & lm.pmask);
-      const uint32_t rb1 = rb0 + __builtin_popcount(__builtin_amdgcn_alignbit(hi, lo, lm.sh));
-      const half8_t a0 = rebuild_row<I4>(vbase, lut, rb0, (lo >> lm.sh) & 0xFFu);
-      const half8_t a1 = rebuild_row<I4>(vbase, lut, rb1, (hi >> lm.sh) & 0xFFu);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        acc[2 * h][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, __builtin_bit_cast(half8_t, x[ks][nb]),
-                                                                acc[2 * h][nb], 0, 0, 0);
-        acc[2 * h + 1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, __builtin_bit_cast(half8_t, x[ks][nb]),
-                                                                    acc[2 * h + 1][nb], 0, 0, 0);
-      }
-    }
-}
-
-// Exclusive prefix of the BitmapTile popcounts of the GroupTile in bb
-// (lane i <-> BitmapTile i).
-__device__ __forceinline__ uint32_t bitmap_prefix(const uint64_t* bb, int lane) {
-  const uint32_t pc = __popcll(bb[lane]);
-  return wave_inclusive_scan(pc) - pc;
-}
-
-// The same from the slot's registers (lane t holds bitmap word t), which
-// keeps an LDS round trip out of the chain that leads to the rebuild.
+// Exclusive prefix of the BitmapTile popcounts of a GroupTile from the
+// slot's registers (lane t holds bitmap word t).
 __device__ __forceinline__ uint32_t bitmap_prefix_reg(u32x2_t bm) {
   const uint32_t pc = __builtin_popcount(bm.x) + __builtin_popcount(bm.y);
   return wave_inclusive_scan(pc) - pc;
+}
+
+// Rebuild and multiply fragments f = F0 .. F1-1 (both ks) of a GroupTile
+// whose bitmap table is at tab and whose values are in the LDS staging area
+// starting at vals.
+template <int NB, bool I4, int F0 = 0, int F1 = 4>
+__device__ __forceinline__ void tile_mma(const u32x4_t (&x)[2][NB], const uint8_t* vals, const uint8_t* tab,
+                                         const uint32_t* lut, f32x4_t (&acc)[4][NB], const LaneMap& lm) {
+  u32x2_t e[F1 - F0][2];
+#pragma unroll
+  for (int f = F0; f < F1; ++f)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      e[f - F0][ks] = *reinterpret_cast<const u32x2_t*>(tab + lm.tab + 256 * f + 128 * ks);
+#pragma unroll
+  for (int f = F0; f < F1; ++f)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t word = e[f - F0][ks].x;
+      const uint32_t rb = e[f - F0][ks].y + __builtin_popcount(word & lm.pmask);
+      const half8_t a = rebuild_row<I4>(vals, lut, rb, __builtin_amdgcn_ubfe(word, lm.sh, 8));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[f][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, x[ks][nb]), acc[f][nb], 0,
+                                                            0, 0);
+    }
 }
 
 // Launch shape of the decode kernel: waves per workgroup, GroupTiles loaded
@@ -285,9 +234,11 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   using VT = ValTraits<I4>;
   constexpr int kW = C::kWavesPerGroup;
   constexpr int kThreads = C::kThreadsPerGroup;
+  constexpr int kD = C::kDepth;
   __shared__ __attribute__((aligned(16))) uint32_t lut[I4 ? 16 : 32];
-  // Staging (per wave: values, then bitmaps); reused for the final reduction.
-  constexpr int kStage = kW * (VT::kVbuf + 8 * kBtPerGt);
+  // Staging (per wave: values, then the bitmap table); reused for the final
+  // reduction.
+  constexpr int kStage = kW * (VT::kVbuf + kTabBytes);
   constexpr int kRed = kW * 4 * NB * 64 * 4 * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStage > kRed ? kStage : kRed];
   __shared__ uint32_t last_flag;
@@ -332,10 +283,10 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   uint8_t* vb = smem + w * VT::kVbuf;
+  uint8_t* tab = smem + kW * VT::kVbuf + w * kTabBytes;
   // The rebuild addresses the wave's value buffer from smem: its offset, in
   // value elements, is folded into the BitmapTile bases.
   const uint32_t vb_elems = I4 ? static_cast<uint32_t>(w * VT::kVbuf * 2) : static_cast<uint32_t>(w * VT::kVbuf / 2);
-  uint64_t* bb = reinterpret_cast<uint64_t*>(smem + kW * VT::kVbuf) + w * kBtPerGt;
 
   // The wave's GroupTile offsets, one per lane: lane i holds
   // offsets[g_begin + i] for i <= count (the host keeps count <= 63), so a
@@ -351,20 +302,24 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   const uint32_t ov_next = __shfl_down(ov, 1);
   const uint32_t widest = wave_max(lane < cnt ? ov_next - ov : 0u);
 
+  // The bitmap table of the GroupTile in slot s.
+  auto write_tab = [&](const Slot<NB, I4>& s) {
+    tab_write(tab, s.bm, bitmap_prefix_reg(s.bm) + s.delta + vb_elems, lane);
+  };
+
   if (cnt <= 0) {
     // nothing to stream
   } else if (widest > VT::kFastLimit) {
     if constexpr (!I4) {
-      // Unpipelined: per GroupTile, bitmaps first, then the values of TCTile
-      // rows 0-1 and of rows 2-3, each half rebuilt from the wave's buffer.
+      // Unpipelined: per GroupTile, the values of TCTile rows 0-1 (fragments
+      // f = 0, 1), then those of TCTile rows 2-3 (f = 2, 3), each staged in
+      // the wave's buffer with its own bitmap table bases.
       const uint64_t top = a.values_alloc - 16;
       for (int c = c_begin; c < c_end; ++c) {
         const uint32_t o0 = off_at(c), o1 = off_at(c + 1);
         Slot<NB, I4> s0;
         slot_load(s0, a, gi, c, lane, o0, o1);
-        reinterpret_cast<u32x2_t*>(bb)[lane] = s0.bm;
-        wave_sync();
-        const uint32_t excl = bitmap_prefix(bb, lane);
+        const uint32_t excl = bitmap_prefix_reg(s0.bm);
         const uint32_t mid = __builtin_amdgcn_readlane(excl, 32);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -376,26 +331,27 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
           const uint32_t last = static_cast<uint32_t>((top - a0) >> 4);
           const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
           for (uint32_t ch = lane; ch < nch; ch += 64) reinterpret_cast<u32x4_t*>(vb)[ch] = src[min(ch, last)];
+          // Entries of the other half get bases that are never read.
+          tab_write(tab, s0.bm, excl - (h ? mid : 0u) + delta + vb_elems, lane);
           wave_sync();
-          const uint32_t ebase = excl - (h ? mid : 0u) + delta + vb_elems;
           if (h == 0)
-            tile_half<NB, I4, 0>(s0.x, smem, bb, lut, acc, ebase, lm);
+            tile_mma<NB, I4, 0, 2>(s0.x, smem, tab, lut, acc, lm);
           else
-            tile_half<NB, I4, 1>(s0.x, smem, bb, lut, acc, ebase, lm);
+            tile_mma<NB, I4, 2, 4>(s0.x, smem, tab, lut, acc, lm);
           wave_sync();
         }
       }
     }
-  } else if constexpr (C::kDepth == 0) {
+  } else if constexpr (kD == 0) {
     // One register slot: GroupTile c is copied into LDS, then the loads of
     // c+1 are issued into the same registers while c is rebuilt and
     // multiplied.  Fewer registers, more waves per SIMD.
     const int c_last = c_end - 1;
     Slot<NB, I4> s0;
     slot_load(s0, a, gi, c_begin, lane, off_at(c_begin), off_at(c_begin + 1));
+    write_tab(s0);
     for (int c = c_begin; c < c_end; ++c) {
-      const RowsIn rin = rows_in(s0.bm, bitmap_prefix_reg(s0.bm) + s0.delta + vb_elems, lm);
-      slot_commit(s0, vb, bb, lane);
+      slot_commit(s0, vb, lane);
       u32x4_t xc[2][NB];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -404,103 +360,53 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
       const int cn = min(c + 1, c_last);
       slot_load(s0, a, gi, cn, lane, off_at(cn), off_at(cn + 1));
       wave_sync();
-      {
-        tile_full<NB, I4>(xc, smem, rin, lut, acc, lm);
-      }
+      tile_mma<NB, I4>(xc, smem, tab, lut, acc, lm);
       wave_sync();
+      write_tab(s0);
     }
-  } else if constexpr (C::kDepth == 3) {
-    // Four register slots: GroupTile c is in LDS while c+1, c+2 and c+3
-    // load, so a wave keeps three GroupTiles of loads in flight.
-    const int c_last = c_end - 1;
-    auto load = [&](Slot<NB, I4>& sl, int c) {
-      const int cc = min(c, c_last);
-      slot_load(sl, a, gi, cc, lane, off_at(cc), off_at(cc + 1));
-    };
-    Slot<NB, I4> s0, s1, s2, s3;
-    load(s0, c_begin);
-    load(s1, c_begin + 1);
-    load(s2, c_begin + 2);
-    auto step = [&](Slot<NB, I4>& cur, int c, Slot<NB, I4>& nxt) {
-      load(nxt, c + 3);
-      const RowsIn rin = rows_in(cur.bm, bitmap_prefix_reg(cur.bm) + cur.delta + vb_elems, lm);
-      slot_commit(cur, vb, bb, lane);
-      wave_sync();
-      tile_full<NB, I4>(cur.x, smem, rin, lut, acc, lm);
-      wave_sync();
-    };
-    int c = c_begin;
-    for (; c + 4 <= c_end; c += 4) {
-      step(s0, c, s3);
-      step(s1, c + 1, s0);
-      step(s2, c + 2, s1);
-      step(s3, c + 3, s2);
-    }
-    if (c < c_end) step(s0, c, s3);
-    if (c + 1 < c_end) step(s1, c + 1, s0);
-    if (c + 2 < c_end) step(s2, c + 2, s1);
-  } else if constexpr (C::kDepth == 2) {
-    // Three register slots: GroupTile c is in LDS while c+1 and c+2 load.
+  } else {
+    // kD + 1 register slots: GroupTile c is in LDS while c+1 .. c+kD load.
     // Loads past the wave's last GroupTile repeat it (every wave here owns at
     // least one), so each step issues the same loads and waits for exactly
-    // one slot.  A step issues the loads of c+2 before waiting for c.
+    // one slot.  A step issues the loads of c+kD before it waits for c, and
+    // ends by writing the bitmap table of c+1 (the bitmaps are the first
+    // load of a slot, long arrived by then).
+    constexpr int kS = kD + 1;
     const int c_last = c_end - 1;
     auto load = [&](Slot<NB, I4>& sl, int c) {
       const int cc = min(c, c_last);
       slot_load(sl, a, gi, cc, lane, off_at(cc), off_at(cc + 1));
     };
-    Slot<NB, I4> s0, s1, s2;
-    load(s0, c_begin);
-    load(s1, c_begin + 1);
-    auto step = [&](Slot<NB, I4>& cur, int c, Slot<NB, I4>& nxt) {
-      load(nxt, c + 2);
-      const RowsIn rin = rows_in(cur.bm, bitmap_prefix_reg(cur.bm) + cur.delta + vb_elems, lm);
-      slot_commit(cur, vb, bb, lane);
+    Slot<NB, I4> s[kS];
+#pragma unroll
+    for (int j = 0; j < kD; ++j) load(s[j], c_begin + j);
+    write_tab(s[0]);
+    auto step = [&](Slot<NB, I4>& cur, int c, Slot<NB, I4>& nxt, const Slot<NB, I4>& after) {
+      load(nxt, c + kD);
+      slot_commit(cur, vb, lane);
       wave_sync();
-      tile_full<NB, I4>(cur.x, smem, rin, lut, acc, lm);
+      tile_mma<NB, I4>(cur.x, smem, tab, lut, acc, lm);
       wave_sync();
+      write_tab(after);
     };
     int c = c_begin;
-    for (; c + 3 <= c_end; c += 3) {
-      step(s0, c, s2);
-      step(s1, c + 1, s0);
-      step(s2, c + 2, s1);
+    for (; c + kS <= c_end; c += kS) {
+#pragma unroll
+      for (int j = 0; j < kS; ++j) step(s[j], c + j, s[(j + kD) % kS], s[(j + 1) % kS]);
     }
-    if (c < c_end) step(s0, c, s2);
-    if (c + 1 < c_end) step(s1, c + 1, s0);
-  } else {
-    // Two register slots: GroupTile c is in LDS while c+1 loads.
-    const int c_last = c_end - 1;
-    auto load = [&](Slot<NB, I4>& sl, int c) {
-      const int cc = min(c, c_last);
-      slot_load(sl, a, gi, cc, lane, off_at(cc), off_at(cc + 1));
-    };
-    Slot<NB, I4> s0, s1;
-    load(s0, c_begin);
-    auto step = [&](Slot<NB, I4>& cur, int c, Slot<NB, I4>& nxt) {
-      load(nxt, c + 1);
-      const RowsIn rin = rows_in(cur.bm, bitmap_prefix_reg(cur.bm) + cur.delta + vb_elems, lm);
-      slot_commit(cur, vb, bb, lane);
-      wave_sync();
-      tile_full<NB, I4>(cur.x, smem, rin, lut, acc, lm);
-      wave_sync();
-    };
-    int c = c_begin;
-    for (; c + 2 <= c_end; c += 2) {
-      step(s0, c, s1);
-      step(s1, c + 1, s0);
-    }
-    if (c < c_end) step(s0, c, s1);
+#pragma unroll
+    for (int j = 0; j < kD; ++j)
+      if (c + j < c_end) step(s[j], c + j, s[(j + kD) % kS], s[(j + 1) % kS]);
   }
 
   // Workgroup reduction over waves (fixed order).
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll
-  for (int rs = 0; rs < 4; ++rs)
+  for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + rs) * NB + nb) * 64 + lane) * 4) = acc[rs][nb];
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb];
   __syncthreads();
 
   const int m0 = gi * kGT;
@@ -534,17 +440,14 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
     const int n = e >> 4;
     const int ml = 4 * (e & 15);
     if (n >= a.N) continue;
-    // Strip row ml + j sits in accumulator acc_of_row(ml) (the same for the
-    // four rows) at D row drow_of_row(ml + j) = 4 j + (ml / 8) % 4, i.e.
-    // lane 16 j + n % 16, register (ml / 8) % 4.
-    const int rs = acc_of_row(ml);
-    const int i = drow_of_row(ml) & 3;
+    // Strip rows ml .. ml+3 are D rows 4g .. 4g+3 (g = (ml / 4) % 4) of
+    // fragment ml / 16: registers 0-3 of lane 16 g + n % 16.
+    const int f = ml >> 4;
+    const int ln = 16 * ((ml >> 2) & 3) + (n & 15);
     const int nb = n >> 4;
     f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ww = 0; ww < kW; ++ww)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sum[j] += red[(((ww * 4 + rs) * NB + nb) * 64 + 16 * j + (n & 15)) * 4 + i];
+    for (int ww = 0; ww < kW; ++ww) sum += *reinterpret_cast<const f32x4_t*>(red + (((ww * 4 + f) * NB + nb) * 64 + ln) * 4);
     if (a.splits > 1)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sum), part_rsrc(sidx),
                                              (n * a.M + m0 + ml) * 4, 0, kCacheSc1);
