@@ -154,6 +154,25 @@ def test_dense_groups(density, splits):
     assert_parity(Y, Yref, Bnd, f"density {density} splits={splits}")
 
 
+@pytest.mark.parametrize("N", [1, 16, 24])
+def test_dense_groups_in_a_sparse_matrix(N):
+    """A matrix at most 55% dense on average gets the five-chunk value slot;
+    its few GroupTiles too dense for that slot (70% here) send their waves
+    down the two-half path, one at 60% still fits.  Integer-exact inputs, so
+    bit for bit."""
+    rng = np.random.default_rng(300 + N)
+    M, K = 256, 1024            # 4 x 16 GroupTiles
+    W = wl.weight_dyadic(M, K, rng)
+    mask = wl.mask_bernoulli(M, K, 0.45, rng)
+    mask[64:128, 192:384] = rng.random((64, 192)) < 0.7     # GroupTiles (1, 3..5)
+    mask[192:256, 640:704] = rng.random((64, 64)) < 0.6     # GroupTile (3, 10)
+    assert mask.mean() <= 0.55
+    X = wl.activations_small_int(N, K, rng)
+    Y = run_gpu(W, mask, X, out=torch.float32)
+    Wd = np.where(mask, W, np.float16(0))
+    assert np.array_equal(Y, ob.spmm_fp64(Wd, X))
+
+
 def test_split_k_counters_reset_across_calls():
     """Repeated split-K calls on one workspace (per-strip counters, XCD remap
     with 8 | workgroups) give identical bits every time."""

@@ -52,40 +52,33 @@ namespace {
 
 using namespace usw_dev;
 
-// Per-value-type constants.  Every one of a slot's kChunks*64 16-byte chunk
-// loads is issued unconditionally (chunks past the GroupTile's last one
-// repeat it), so the loads carry no branches and the compiler waits for
-// exactly the slot being consumed.
-template <bool I4>
-struct ValTraits;
-template <>
-struct ValTraits<false> {
-  static constexpr int kChunks = 6;        // 6 KB of values per slot (density up to ~74%)
+// Value slot constants: CH 1 KB chunks per GroupTile, i.e. 64 lanes x 16 B
+// per chunk.  fp16 takes 5 chunks (GroupTiles up to ~62% dense) when the
+// matrix is at most 55% dense on average, else 6 (~74%); INT4 takes 3, which
+// every GroupTile fits (<= 2 KB + head).  Denser GroupTiles are staged in two
+// halves of two TCTile rows each (<= 4 KB + head).  Every chunk load is
+// issued unconditionally, so the loads carry no branches and the compiler
+// waits for exactly the slot being consumed.
+template <bool I4, int CH>
+struct ValTraits {
+  static constexpr int kChunks = CH;
   // LDS value buffer per wave: one slot plus the <16 B a window reads past
-  // the last value.  Denser GroupTiles are staged in two halves of two TCTile
-  // rows each (<= 4 KB + head).
-  static constexpr int kVbuf = 6 * 1024 + 64;
-  static constexpr uint32_t kFastLimit = (16u * 64u * kChunks - 32u) / 2u;   // values per GroupTile
+  // the last value.
+  static constexpr int kVbuf = CH * 1024 + 64;
+  static constexpr uint32_t kFastLimit = I4 ? 4096u : (16u * 64u * CH - 32u) / 2u;   // values per GroupTile
+  static_assert(I4 || kVbuf >= 16 * 257 + 16, "a half GroupTile fits");
+  static_assert(!I4 || kFastLimit / 2 + 16 <= 1024 * CH, "every INT4 GroupTile fits");
 };
-template <>
-struct ValTraits<true> {
-  static constexpr int kChunks = 3;        // every INT4 GroupTile fits (<= 2 KB + head)
-  static constexpr int kVbuf = 3 * 1024 + 64;
-  static constexpr uint32_t kFastLimit = 4096u;
-};
-static_assert(ValTraits<false>::kVbuf >= 1024 * ValTraits<false>::kChunks, "unconditional stores fit");
-static_assert(ValTraits<false>::kVbuf >= 16 * 257 + 16, "a half GroupTile fits");
-static_assert(ValTraits<true>::kVbuf >= 1024 * ValTraits<true>::kChunks, "unconditional stores fit");
 
 // Registers holding one GroupTile's loads until they are copied into LDS.
-template <int NB, bool I4>
+template <int NB, bool I4, int CH>
 struct Slot {
-  u32x4_t v[ValTraits<I4>::kChunks];
+  u32x4_t v[CH];
   u32x2_t bm;       // lane t: bitmap word t of the GroupTile
   u32x4_t x[2][NB];
-  uint32_t nch;     // 16-byte chunks of values spanned (wave-uniform)
-  uint32_t delta;   // value elements before the GroupTile's first one in its first chunk
-  uint64_t a0;      // byte offset of the first chunk
+  uint32_t nch;     // 16-byte pieces of values spanned (wave-uniform)
+  uint32_t delta;   // value elements before the GroupTile's first one in its first piece
+  uint64_t a0;      // byte offset of the first piece
 };
 
 struct Args {
@@ -104,25 +97,32 @@ struct Args {
 
 // Issue the loads of GroupTile c of strip gi, whose values occupy elements
 // [o0, o1) of the stream.
-template <int NB, bool I4>
-__device__ __forceinline__ void slot_load(Slot<NB, I4>& s, const Args& a, int gi, int c, int lane, uint32_t o0,
+template <int NB, bool I4, int CH>
+__device__ __forceinline__ void slot_load(Slot<NB, I4, CH>& s, const Args& a, int gi, int c, int lane, uint32_t o0,
                                           uint32_t o1) {
+  using VT = ValTraits<I4, CH>;
   const int64_t g = static_cast<int64_t>(gi) * a.Gc + c;
-  // The clamps keep every load inside the padded allocation and every store
-  // inside the LDS buffer even for offsets that disagree with the bitmaps.
   // Bitmaps first: the bitmap table of a slot is written while its values
   // and X^T fragments may still be in flight.
   s.bm = reinterpret_cast<const u32x2_t*>(a.bitmaps + g * kBtPerGt)[lane];
+  // The clamps keep every load inside the padded allocation and every store
+  // inside the LDS buffer even for offsets that disagree with the bitmaps.
   const uint64_t top = a.values_alloc - 16;
   s.a0 = min(chunk_start<I4>(o0), top);
   s.delta = chunk_delta<I4>(o0, s.a0);
-  s.nch = min(chunk_count<I4>(o1, s.a0), static_cast<uint32_t>((ValTraits<I4>::kVbuf - 16) / 16));
-  // Chunk slots past the last chunk reload it (chunk 0 of an empty
-  // GroupTile lies inside the padded allocation).
+  s.nch = min(chunk_count<I4>(o1, s.a0), static_cast<uint32_t>((VT::kVbuf - 16) / 16));
+  // The values go through buffer resources, one per chunk, that end after
+  // the GroupTile's last piece (piece 0 of an empty GroupTile lies inside the
+  // padded allocation): pieces past it read as zero, with no clamp per piece
+  // and one vector offset (the lane's) for all chunks.
   const uint32_t last = min(s.nch > 0 ? s.nch - 1 : 0u, static_cast<uint32_t>((top - s.a0) >> 4));
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + s.a0);
+  const int span = static_cast<int>(16 * (last + 1));
 #pragma unroll
-  for (int i = 0; i < ValTraits<I4>::kChunks; ++i) s.v[i] = src[min(static_cast<uint32_t>(lane + 64 * i), last)];
+  for (int i = 0; i < CH; ++i) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values + s.a0 + 1024 * i), 0,
+                                                        max(span - 1024 * i, 0), kBufferRsrcWord3);
+    s.v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * lane, 0, 0));
+  }
   // X^T fragments.  Columns n >= N of B only feed columns n >= N of the
   // product, which are never stored, so those lanes just repeat row N-1.
   const int row = lane & 15, kb = lane >> 4;
@@ -135,10 +135,10 @@ __device__ __forceinline__ void slot_load(Slot<NB, I4>& s, const Args& a, int gi
     }
 }
 
-template <int NB, bool I4>
-__device__ __forceinline__ void slot_commit(const Slot<NB, I4>& s, uint8_t* vb, int lane) {
+template <int NB, bool I4, int CH>
+__device__ __forceinline__ void slot_commit(const Slot<NB, I4, CH>& s, uint8_t* vb, int lane) {
 #pragma unroll
-  for (int i = 0; i < ValTraits<I4>::kChunks; ++i) reinterpret_cast<u32x4_t*>(vb)[lane + 64 * i] = s.v[i];
+  for (int i = 0; i < CH; ++i) reinterpret_cast<u32x4_t*>(vb)[lane + 64 * i] = s.v[i];
 }
 
 // Which rows a lane rebuilds.  Fragment (f, ks) of a GroupTile (f = 0..3,
@@ -229,9 +229,9 @@ struct Cfg {
   static constexpr int kThreadsPerGroup = 64 * WAVES_;
 };
 
-template <int NB, bool I4, bool OUT_F16, class C>
+template <int NB, bool I4, int CH, bool OUT_F16, class C>
 __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Args a) {
-  using VT = ValTraits<I4>;
+  using VT = ValTraits<I4, CH>;
   constexpr int kW = C::kWavesPerGroup;
   constexpr int kThreads = C::kThreadsPerGroup;
   constexpr int kD = C::kDepth;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   const uint32_t widest = wave_max(lane < cnt ? ov_next - ov : 0u);
 
   // The bitmap table of the GroupTile in slot s.
-  auto write_tab = [&](const Slot<NB, I4>& s) {
+  auto write_tab = [&](const Slot<NB, I4, CH>& s) {
     tab_write(tab, s.bm, bitmap_prefix_reg(s.bm) + s.delta + vb_elems, lane);
   };
 
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
       const uint64_t top = a.values_alloc - 16;
       for (int c = c_begin; c < c_end; ++c) {
         const uint32_t o0 = off_at(c), o1 = off_at(c + 1);
-        Slot<NB, I4> s0;
+        Slot<NB, I4, CH> s0;
         slot_load(s0, a, gi, c, lane, o0, o1);
         const uint32_t excl = bitmap_prefix_reg(s0.bm);
         const uint32_t mid = __builtin_amdgcn_readlane(excl, 32);
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
     // c+1 are issued into the same registers while c is rebuilt and
     // multiplied.  Fewer registers, more waves per SIMD.
     const int c_last = c_end - 1;
-    Slot<NB, I4> s0;
+    Slot<NB, I4, CH> s0;
     slot_load(s0, a, gi, c_begin, lane, off_at(c_begin), off_at(c_begin + 1));
     write_tab(s0);
     for (int c = c_begin; c < c_end; ++c) {
@@ -373,15 +373,15 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
     // load of a slot, long arrived by then).
     constexpr int kS = kD + 1;
     const int c_last = c_end - 1;
-    auto load = [&](Slot<NB, I4>& sl, int c) {
+    auto load = [&](Slot<NB, I4, CH>& sl, int c) {
       const int cc = min(c, c_last);
       slot_load(sl, a, gi, cc, lane, off_at(cc), off_at(cc + 1));
     };
-    Slot<NB, I4> s[kS];
+    Slot<NB, I4, CH> s[kS];
 #pragma unroll
     for (int j = 0; j < kD; ++j) load(s[j], c_begin + j);
     write_tab(s[0]);
-    auto step = [&](Slot<NB, I4>& cur, int c, Slot<NB, I4>& nxt, const Slot<NB, I4>& after) {
+    auto step = [&](Slot<NB, I4, CH>& cur, int c, Slot<NB, I4, CH>& nxt, const Slot<NB, I4, CH>& after) {
       load(nxt, c + kD);
       slot_commit(cur, vb, lane);
       wave_sync();
@@ -501,6 +501,9 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
 // tuning build (-DUSW_TUNING) also compiles the others and picks one from
 // the USW_DECODE_CFG environment variable.
 using DefaultCfg = Cfg<4, 1, 4>;
+// fp16 with five-chunk value slots: 96 VGPRs, so a fifth wave per SIMD fits
+// (measured 2% faster than four on the 20480x5120 layer at N = 16).
+using DefaultCfgLean = Cfg<4, 1, 5>;
 // 17..32 columns of N: twice the accumulators and X fragments, which do not
 // fit 128 registers; three waves per SIMD leave room for them.
 using DefaultCfg2 = Cfg<4, 1, 3>;
@@ -539,7 +542,7 @@ struct CfgInfo {
   int occ;     // waves per SIMD the configuration allows
 };
 
-CfgInfo cfg_info(int cfg, bool two, bool i4) {
+CfgInfo cfg_info(int cfg, bool two, bool i4, bool lean) {
   switch (cfg) {
 #ifdef USW_TUNING
     case 1: return {TuneCfg1::kWavesPerGroup, TuneCfg1::kOcc};
@@ -560,8 +563,9 @@ CfgInfo cfg_info(int cfg, bool two, bool i4) {
 #endif
     default:
       if (two) return CfgInfo{DefaultCfg2::kWavesPerGroup, DefaultCfg2::kOcc};
-      return i4 ? CfgInfo{DefaultCfgI4::kWavesPerGroup, DefaultCfgI4::kOcc}
-                : CfgInfo{DefaultCfg::kWavesPerGroup, DefaultCfg::kOcc};
+      if (i4) return CfgInfo{DefaultCfgI4::kWavesPerGroup, DefaultCfgI4::kOcc};
+      return lean ? CfgInfo{DefaultCfgLean::kWavesPerGroup, DefaultCfgLean::kOcc}
+                  : CfgInfo{DefaultCfg::kWavesPerGroup, DefaultCfg::kOcc};
   }
 }
 
@@ -578,11 +582,19 @@ struct Plan {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-Plan make_plan(const usw::Geometry& g, int N, int splits_req, bool i4) {
+// Five 1 KB value chunks per slot when an fp16 matrix is at most 55% dense on
+// average (a GroupTile then needs more than five only far in the tail; such
+// a wave takes the two-half path), six otherwise.
+bool lean_values(const usw_fmt* f, const usw::Geometry& g) {
+  return f->val_type == USW_VAL_F16 &&
+         static_cast<double>(f->nnz) <= 0.55 * static_cast<double>(g.M) * static_cast<double>(g.K);
+}
+
+Plan make_plan(const usw::Geometry& g, int N, int splits_req, bool i4, bool lean) {
   Plan p;
   p.nchunk = N <= 16 ? 16 : 32;
   p.cfg = choose_cfg();
-  const CfgInfo ci = cfg_info(p.cfg, N > 16, i4);
+  const CfgInfo ci = cfg_info(p.cfg, N > 16, i4, lean);
   p.waves = ci.waves;
   int64_t s = splits_req;
   if (s <= 0) {
@@ -624,41 +636,43 @@ size_t workspace_bytes(const usw::Geometry& g, const Plan& p) {
   return counters_bytes(g) + static_cast<size_t>(p.splits) * p.nchunk * g.M * sizeof(float);
 }
 
-template <int NB, bool I4, class C>
+template <int NB, bool I4, int CH, class C>
 void launch_cfg(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
   if (f16out)
-    decode_kernel<NB, I4, true, C><<<grid, C::kThreadsPerGroup, 0, s>>>(a);
+    decode_kernel<NB, I4, CH, true, C><<<grid, C::kThreadsPerGroup, 0, s>>>(a);
   else
-    decode_kernel<NB, I4, false, C><<<grid, C::kThreadsPerGroup, 0, s>>>(a);
+    decode_kernel<NB, I4, CH, false, C><<<grid, C::kThreadsPerGroup, 0, s>>>(a);
 }
 
-template <int NB, bool I4>
+template <int NB, bool I4, int CH>
 void launch_decode(const Args& a, bool f16out, dim3 grid, hipStream_t s, int cfg) {
   switch (cfg) {
 #ifdef USW_TUNING
-    case 1: launch_cfg<NB, I4, TuneCfg1>(a, f16out, grid, s); return;
-    case 2: launch_cfg<NB, I4, TuneCfg2>(a, f16out, grid, s); return;
-    case 3: launch_cfg<NB, I4, TuneCfg3>(a, f16out, grid, s); return;
-    case 4: launch_cfg<NB, I4, TuneCfg4>(a, f16out, grid, s); return;
-    case 5: launch_cfg<NB, I4, TuneCfg5>(a, f16out, grid, s); return;
-    case 6: launch_cfg<NB, I4, TuneCfg6>(a, f16out, grid, s); return;
-    case 7: launch_cfg<NB, I4, TuneCfg7>(a, f16out, grid, s); return;
-    case 8: launch_cfg<NB, I4, TuneCfg8>(a, f16out, grid, s); return;
-    case 9: launch_cfg<NB, I4, TuneCfg9>(a, f16out, grid, s); return;
-    case 10: launch_cfg<NB, I4, TuneCfg10>(a, f16out, grid, s); return;
-    case 11: launch_cfg<NB, I4, TuneCfg11>(a, f16out, grid, s); return;
-    case 12: launch_cfg<NB, I4, TuneCfg12>(a, f16out, grid, s); return;
-    case 13: launch_cfg<NB, I4, TuneCfg13>(a, f16out, grid, s); return;
-    case 14: launch_cfg<NB, I4, TuneCfg14>(a, f16out, grid, s); return;
-    case 15: launch_cfg<NB, I4, TuneCfg15>(a, f16out, grid, s); return;
+    case 1: launch_cfg<NB, I4, CH, TuneCfg1>(a, f16out, grid, s); return;
+    case 2: launch_cfg<NB, I4, CH, TuneCfg2>(a, f16out, grid, s); return;
+    case 3: launch_cfg<NB, I4, CH, TuneCfg3>(a, f16out, grid, s); return;
+    case 4: launch_cfg<NB, I4, CH, TuneCfg4>(a, f16out, grid, s); return;
+    case 5: launch_cfg<NB, I4, CH, TuneCfg5>(a, f16out, grid, s); return;
+    case 6: launch_cfg<NB, I4, CH, TuneCfg6>(a, f16out, grid, s); return;
+    case 7: launch_cfg<NB, I4, CH, TuneCfg7>(a, f16out, grid, s); return;
+    case 8: launch_cfg<NB, I4, CH, TuneCfg8>(a, f16out, grid, s); return;
+    case 9: launch_cfg<NB, I4, CH, TuneCfg9>(a, f16out, grid, s); return;
+    case 10: launch_cfg<NB, I4, CH, TuneCfg10>(a, f16out, grid, s); return;
+    case 11: launch_cfg<NB, I4, CH, TuneCfg11>(a, f16out, grid, s); return;
+    case 12: launch_cfg<NB, I4, CH, TuneCfg12>(a, f16out, grid, s); return;
+    case 13: launch_cfg<NB, I4, CH, TuneCfg13>(a, f16out, grid, s); return;
+    case 14: launch_cfg<NB, I4, CH, TuneCfg14>(a, f16out, grid, s); return;
+    case 15: launch_cfg<NB, I4, CH, TuneCfg15>(a, f16out, grid, s); return;
 #endif
     default:
       if constexpr (NB == 2)
-        launch_cfg<NB, I4, DefaultCfg2>(a, f16out, grid, s);
+        launch_cfg<NB, I4, CH, DefaultCfg2>(a, f16out, grid, s);
       else if constexpr (I4)
-        launch_cfg<NB, I4, DefaultCfgI4>(a, f16out, grid, s);
+        launch_cfg<NB, I4, CH, DefaultCfgI4>(a, f16out, grid, s);
+      else if constexpr (CH == 5)
+        launch_cfg<NB, I4, CH, DefaultCfgLean>(a, f16out, grid, s);
       else
-        launch_cfg<NB, I4, DefaultCfg>(a, f16out, grid, s);
+        launch_cfg<NB, I4, CH, DefaultCfg>(a, f16out, grid, s);
       return;
   }
 }
@@ -682,7 +696,7 @@ usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_typ
     }
     return usw::prefill_launch(f, g, X, Y, y_type == USW_OUT_F16, N, ws, pp, stream);
   }
-  const Plan p = make_plan(g, N, splits_req, f->val_type == USW_VAL_I4);
+  const Plan p = make_plan(g, N, splits_req, f->val_type == USW_VAL_I4, lean_values(f, g));
   const size_t need = workspace_bytes(g, p);
   if (need > 0) {
     if (!ws || ws_bytes < need) return USW_ERR_WORKSPACE;
@@ -695,6 +709,7 @@ usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_typ
   const size_t ybytes = y_type == USW_OUT_F16 ? 2 : 4;
   const bool f16out = y_type == USW_OUT_F16;
   const bool i4 = f->val_type == USW_VAL_I4;
+  const bool lean = lean_values(f, g);
 
   for (int n0 = 0; n0 < N; n0 += p.nchunk) {
     const int nc = std::min(p.nchunk, N - n0);
@@ -716,11 +731,14 @@ usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_typ
     a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
     const bool two = nc > 16;
     if (i4) {
-      if (two) launch_decode<2, true>(a, f16out, grid, s, p.cfg);
-      else launch_decode<1, true>(a, f16out, grid, s, p.cfg);
+      if (two) launch_decode<2, true, 3>(a, f16out, grid, s, p.cfg);
+      else launch_decode<1, true, 3>(a, f16out, grid, s, p.cfg);
+    } else if (lean) {
+      if (two) launch_decode<2, false, 5>(a, f16out, grid, s, p.cfg);
+      else launch_decode<1, false, 5>(a, f16out, grid, s, p.cfg);
     } else {
-      if (two) launch_decode<2, false>(a, f16out, grid, s, p.cfg);
-      else launch_decode<1, false>(a, f16out, grid, s, p.cfg);
+      if (two) launch_decode<2, false, 6>(a, f16out, grid, s, p.cfg);
+      else launch_decode<1, false, 6>(a, f16out, grid, s, p.cfg);
     }
     if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
   }
@@ -749,7 +767,7 @@ usw_status usw_spmm_workspace_ex(const usw_fmt* f, int32_t N, int32_t splits, si
   if (f->val_type == USW_VAL_F16 && N > 32)
     *bytes = usw::prefill_workspace_bytes(g, N, usw::prefill_plan(g, N, sr));
   else
-    *bytes = workspace_bytes(g, make_plan(g, N, sr, f->val_type == USW_VAL_I4));
+    *bytes = workspace_bytes(g, make_plan(g, N, sr, f->val_type == USW_VAL_I4, lean_values(f, g)));
   return USW_OK;
 }
 
@@ -762,7 +780,7 @@ usw_status usw_spmm_counter_bytes(const usw_fmt* f, int32_t N, int32_t splits, s
   if (f->val_type == USW_VAL_F16 && N > 32) {
     *bytes = usw::prefill_counter_bytes(g, usw::prefill_plan(g, N, sr));
   } else {
-    const Plan p = make_plan(g, N, sr, f->val_type == USW_VAL_I4);
+    const Plan p = make_plan(g, N, sr, f->val_type == USW_VAL_I4, lean_values(f, g));
     *bytes = p.splits > 1 ? counters_bytes(g) : 0;
   }
   return USW_OK;
