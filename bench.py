@@ -289,7 +289,12 @@ def main():
     if prefill:
         kname = "prefill_ws_kernel" if N > 256 else "prefill_kernel"
     else:
-        kname = "decode_f16_kernel" if args.dtype == "f16" else "decode_i4_kernel"
+        # fp16 values at most 55% dense with N <= 16 take the workgroup-
+        # cooperative kernel, the rest the per-wave one.
+        if args.dtype == "f16" and N <= 16 and s >= 0.45:
+            kname = "decode_ring_kernel"
+        else:
+            kname = "decode_f16_kernel" if args.dtype == "f16" else "decode_i4_kernel"
     if prefill:
         # Compute-bound: the matrix cores run the dense 64x64 tiles rebuilt
         # from the bitmaps, 2*M*K*N flops per launch.

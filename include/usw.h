@@ -185,7 +185,9 @@ usw_status usw_spmm(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y_ty
  * the workspace and the last workgroup of a tile to finish adds them in
  * split order, so results do not depend on scheduling.  The factor is
  * clamped to [ceil(K / (64 * 4 * 63)), max(1, K / 256)] for the decode
- * kernels and to [ceil(K / 65536), K / 64] for the prefill kernel.
+ * kernels (lower bound ceil(K / (64 * 63)) for fp16 values at most 55%
+ * dense with N <= 16, whose workgroups stream their whole range together)
+ * and to [ceil(K / 65536), K / 64] for the prefill kernel.
  * splits = 0 is the automatic choice of usw_spmm: for the prefill kernel
  * with N > 256 and K <= 65536 that is a stream-K split, in which each
  * workgroup (one per compute unit, or fewer for small problems) runs the

@@ -35,6 +35,79 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS byte address
+// lds + 16 l (lds the same in every lane; it goes to M0), counted by vmcnt
+// like any vector load.  Issued through asm so that the compiler, which
+// cannot tell which LDS bytes such a load writes, does not wait for every
+// one in flight before each LDS read and barrier; the caller waits with an
+// explicit vmcnt before the barrier that publishes the data.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) T*)p));
+}
+
+// Wait until at most N of this wave's vector memory operations are in flight
+// and its LDS operations are done, then a workgroup barrier.
+#define USW_PRODUCER_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" : : : "memory")
+
+// The same load through the compiler's builtin, which counts it in vmcnt
+// like any load (the LDS address is wave-uniform).  A wave that uses it must
+// keep its own LDS accesses out of the compiler's sight (below), or the
+// compiler waits for every such load before each of them.
+template <typename T>
+__device__ __forceinline__ void lds_dma16_tracked(const void* src, T* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// LDS accesses of a wave that keeps LDS-DMA loads in flight, written as asm:
+// before an LDS access the compiler would itself place an s_waitcnt vmcnt(0),
+// i.e. wait for every load in flight (it cannot tell which LDS bytes they
+// write).  The read waits for its own result.
+__device__ __forceinline__ u32x2_t lds_load_b64(uint32_t addr) {
+  u32x2_t v;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_store_b128(uint32_t addr, u32x4_t v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// Wait until at most n of this wave's vector memory operations are in
+// flight (n wave-uniform; above 15 it waits as for 15, i.e. never for fewer
+// operations than asked).
+#define USW_WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" : : : "memory")
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (__builtin_amdgcn_readfirstlane(n)) {
+    case 0: USW_WAIT_VM(0); break;
+    case 1: USW_WAIT_VM(1); break;
+    case 2: USW_WAIT_VM(2); break;
+    case 3: USW_WAIT_VM(3); break;
+    case 4: USW_WAIT_VM(4); break;
+    case 5: USW_WAIT_VM(5); break;
+    case 6: USW_WAIT_VM(6); break;
+    case 7: USW_WAIT_VM(7); break;
+    case 8: USW_WAIT_VM(8); break;
+    case 9: USW_WAIT_VM(9); break;
+    case 10: USW_WAIT_VM(10); break;
+    case 11: USW_WAIT_VM(11); break;
+    case 12: USW_WAIT_VM(12); break;
+    case 13: USW_WAIT_VM(13); break;
+    case 14: USW_WAIT_VM(14); break;
+    default: USW_WAIT_VM(15); break;
+  }
+}
+
+// Wait for this wave's LDS operations, then a workgroup barrier (vector
+// memory loads stay in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
 // Inclusive prefix sum over the 64 lanes with DPP (no LDS round trips):
 // Hillis-Steele inside each 16-lane row, then the row totals are carried by
 // the row_bcast:15 and row_bcast:31 broadcasts.

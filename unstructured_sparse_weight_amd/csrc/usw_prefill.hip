@@ -330,28 +330,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a)
   if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS byte address
-// lds + 16 l (lds the same in every lane; it goes to M0), counted by vmcnt
-// like any vector load.  Issued through asm so that the compiler, which
-// cannot tell which LDS bytes such a load writes, does not wait for every
-// one in flight before each LDS read and barrier; the caller waits with an
-// explicit vmcnt before the barrier that publishes the data.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-}
-
-template <typename T>
-__device__ __forceinline__ uint32_t lds_addr(T* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) T*)p));
-}
-
-// Wait until at most N of this wave's vector memory operations are in flight
-// and its LDS operations are done, then a workgroup barrier.
-#define USW_PRODUCER_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" : : : "memory")
-
 // The same for a wave-uniform count n in [8, 12]; any other count waits as
 // for 8 (never for fewer loads than asked).
 __device__ __forceinline__ void producer_barrier(int n) {

@@ -6,7 +6,13 @@
 // fast", section "How TCA-BME addresses the indexing overhead").  Values are
 // located by masked popcount (same blog, "Shared Memory Bitmap Decoding").
 //
-// Design (gfx950, wave64):
+// Two kernels: decode_ring_kernel (fp16 values, N <= 16, matrices at most
+// 55% dense), in which a workgroup's waves share each GroupTile through an
+// LDS ring filled by a loader wave (described where it is defined), and
+// decode_kernel (everything else in decode), described here.  They share
+// the rebuild and the split-K epilogue.
+//
+// Design of decode_kernel (gfx950, wave64):
 //   * One workgroup owns one 64-row strip of GroupTiles (64x64) and a range
 //     of GroupTile columns; each of its waves streams its own contiguous run
 //     of GroupTiles (bitmaps and values of consecutive GroupTiles of a strip
@@ -218,6 +224,89 @@ __device__ __forceinline__ void tile_mma(const u32x4_t (&x)[2][NB], const uint8_
     }
 }
 
+// Writes a strip's sums to Y or, with split K, to split sidx's partial sums.
+// sum_of(n, ml) gives token n's sums for strip rows ml .. ml+3.  Split K:
+// the last workgroup of the strip to finish adds the partial sums of all its
+// splits, in split order, and writes Y; the counter goes back to 0 for the
+// next call.
+template <int NB, bool I4, bool OUT_F16, class SumFn>
+__device__ __forceinline__ void finish_strip(const Args& a, int gi, int sidx, int nthreads, uint32_t& last_flag,
+                                             SumFn sum_of) {
+  const int tid = threadIdx.x;
+  const int m0 = gi * kGT;
+  // Y[n][m0 + ml .. +3] from four consecutive row sums.
+  auto store_y4 = [&](int n, int ml, f32x4_t v) {
+    if constexpr (I4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] *= static_cast<float>(__builtin_bit_cast(_Float16, a.scales[m0 + ml + j]));
+    }
+    const size_t yi = static_cast<size_t>(n) * a.M + m0 + ml;
+    if constexpr (OUT_F16) {
+      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+      half4_t h;
+      h.x = static_cast<_Float16>(v.x);
+      h.y = static_cast<_Float16>(v.y);
+      h.z = static_cast<_Float16>(v.z);
+      h.w = static_cast<_Float16>(v.w);
+      *reinterpret_cast<half4_t*>(reinterpret_cast<_Float16*>(a.Y) + yi) = h;
+    } else {
+      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.Y) + yi) = v;
+    }
+  };
+  // Partial sums of split s: [N][M] fp32 at part + s N M, read and written
+  // with device-coherent (sc1) 16-byte accesses.
+  auto part_rsrc = [&](int s) {
+    return __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(s) * a.N * a.M, 0, a.N * a.M * 4,
+                                             kBufferRsrcWord3);
+  };
+  // Thread element e: token n = e / 16, strip rows ml = 4 (e % 16) .. +3.
+  for (int e = tid; e < 16 * 16 * NB; e += nthreads) {
+    const int n = e >> 4;
+    const int ml = 4 * (e & 15);
+    if (n >= a.N) continue;
+    const f32x4_t sum = sum_of(n, ml);
+    if (a.splits > 1)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sum), part_rsrc(sidx),
+                                             (n * a.M + m0 + ml) * 4, 0, kCacheSc1);
+    else
+      store_y4(n, ml, sum);
+  }
+  if (a.splits <= 1) return;
+
+  // Every thread's partial stores have completed
+  // (s_waitcnt) before the barrier that precedes the counter increment, and
+  // the last workgroup reads the partials with device-coherent loads issued
+  // after it has seen the final count.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (tid == 0)
+    last_flag = __hip_atomic_fetch_add(&a.counters[gi], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                static_cast<uint32_t>(a.splits - 1);
+  __syncthreads();
+  if (!last_flag) return;
+  for (int e = tid; e < 16 * a.N; e += nthreads) {
+    const int n = e >> 4;
+    const int ml = 4 * (e & 15);
+    const int off = (n * a.M + m0 + ml) * 4;
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+    // Up to four splits' loads in flight at once; added in split order.
+    for (int p0 = 0; p0 < a.splits; p0 += 4) {
+      f32x4_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (p0 + j < a.splits)
+          v[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(part_rsrc(p0 + j), off, 0, kCacheSc1));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (p0 + j < a.splits) sum += v[j];
+    }
+    store_y4(n, ml, sum);
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Launch shape of the decode kernel: waves per workgroup, GroupTiles loaded
 // ahead of the one being computed (1 or 2), and the minimum waves per SIMD
 // the register allocation must allow.
@@ -409,37 +498,7 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
       *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb];
   __syncthreads();
 
-  const int m0 = gi * kGT;
-  // Y[n][m0 + ml .. +3] from four consecutive row sums.
-  auto store_y4 = [&](int n, int ml, f32x4_t v) {
-    if constexpr (I4) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] *= static_cast<float>(__builtin_bit_cast(_Float16, a.scales[m0 + ml + j]));
-    }
-    const size_t yi = static_cast<size_t>(n) * a.M + m0 + ml;
-    if constexpr (OUT_F16) {
-      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-      half4_t h;
-      h.x = static_cast<_Float16>(v.x);
-      h.y = static_cast<_Float16>(v.y);
-      h.z = static_cast<_Float16>(v.z);
-      h.w = static_cast<_Float16>(v.w);
-      *reinterpret_cast<half4_t*>(reinterpret_cast<_Float16*>(a.Y) + yi) = h;
-    } else {
-      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.Y) + yi) = v;
-    }
-  };
-  // Partial sums of split s: [N][M] fp32 at part + s N M, read and written
-  // with device-coherent (sc1) 16-byte accesses.
-  auto part_rsrc = [&](int s) {
-    return __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(s) * a.N * a.M, 0, a.N * a.M * 4,
-                                             kBufferRsrcWord3);
-  };
-  // Thread element e: token n = e / 16, strip rows ml = 4 (e % 16) .. +3.
-  for (int e = tid; e < 16 * 16 * NB; e += kThreads) {
-    const int n = e >> 4;
-    const int ml = 4 * (e & 15);
-    if (n >= a.N) continue;
+  finish_strip<NB, I4, OUT_F16>(a, gi, sidx, kThreads, last_flag, [&](int n, int ml) {
     // Strip rows ml .. ml+3 are D rows 4g .. 4g+3 (g = (ml / 4) % 4) of
     // fragment ml / 16: registers 0-3 of lane 16 g + n % 16.
     const int f = ml >> 4;
@@ -447,49 +506,290 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
     const int nb = n >> 4;
     f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ww = 0; ww < kW; ++ww) sum += *reinterpret_cast<const f32x4_t*>(red + (((ww * 4 + f) * NB + nb) * 64 + ln) * 4);
-    if (a.splits > 1)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sum), part_rsrc(sidx),
-                                             (n * a.M + m0 + ml) * 4, 0, kCacheSc1);
-    else
-      store_y4(n, ml, sum);
-  }
-  if (a.splits <= 1) return;
+    for (int ww = 0; ww < kW; ++ww)
+      sum += *reinterpret_cast<const f32x4_t*>(red + (((ww * 4 + f) * NB + nb) * 64 + ln) * 4);
+    return sum;
+  });
+}
 
-  // Split K: the last workgroup of the strip to finish adds the partial sums
-  // of all its splits, in split order, and writes Y; the counter goes back
-  // to 0 for the next call.  Every thread's partial stores have completed
-  // (s_waitcnt) before the barrier that precedes the counter increment, and
-  // the last workgroup reads the partials with device-coherent loads issued
-  // after it has seen the final count.
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (tid == 0)
-    last_flag = __hip_atomic_fetch_add(&a.counters[gi], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                static_cast<uint32_t>(a.splits - 1);
-  __syncthreads();
-  if (!last_flag) return;
-  for (int e = tid; e < 16 * a.N; e += kThreads) {
-    const int n = e >> 4;
-    const int ml = 4 * (e & 15);
-    const int off = (n * a.M + m0 + ml) * 4;
-    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-    // Up to four splits' loads in flight at once; added in split order.
-    for (int p0 = 0; p0 < a.splits; p0 += 4) {
-      f32x4_t v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (p0 + j < a.splits)
-          v[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(part_rsrc(p0 + j), off, 0, kCacheSc1));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (p0 + j < a.splits) sum += v[j];
-    }
-    store_y4(n, ml, sum);
+// ---------------------------------------------------------------------------
+// Workgroup-cooperative decode: fp16 values, N <= 16, matrices at most 55%
+// dense on average
+// ---------------------------------------------------------------------------
+//
+// One workgroup is four compute waves and two loader waves over one strip's
+// range of GroupTile columns; all six pass one barrier per GroupTile.
+//  * Wave 4 moves each GroupTile's values and X^T column, and the bitmap
+//    words of the GroupTile after, straight into a ring of R LDS slots with
+//    global_load_lds_dwordx4,
+//    R - 1 GroupTiles ahead, so no register holds them in flight.  It waits
+//    for its own loads with explicit vmcnt counts before each barrier.
+//  * Wave 5 writes the bitmap table of the next GroupTile into its slot.
+//  * Compute wave q (0-3) rebuilds fragments f = 2 (q / 2) and 2 (q / 2) + 1
+//    for ks = q % 2: two rows per lane per GroupTile, and multiplies them
+//    with its X^T fragment, which wave 4 also stages in the slot.  The MFMA B
+//    layout puts a different token in each of four consecutive lanes, so as
+//    a global load every compute wave's fragment would cost four times the
+//    address-unit cycles of a contiguous one; the compute waves issue no
+//    global loads at all.
+// A workgroup whose range holds a GroupTile too wide for a slot runs the
+// range unpipelined, half a GroupTile (two TCTile rows) at a time in slot 0.
+
+constexpr int kRingVals = 5 * 1024 + 64;                 // value bytes per slot
+constexpr int kRingX = 2048;                             // X^T of one GroupTile column, 16 tokens
+constexpr int kRingSlot = kRingVals + 512 + kTabBytes + kRingX;   // + bitmap words, table, X^T
+constexpr uint32_t kRingPieces = 5 * 64;                 // 16-byte value pieces a slot takes
+constexpr uint32_t kRingFast = (16u * kRingPieces - 32u) / 2u;   // values per GroupTile that fit a slot
+constexpr int kRingThreads = 384;
+static_assert(kRingSlot % 16 == 0, "slots keep 16-byte alignment");
+static_assert(16 * kRingPieces + 16 <= kRingVals, "windows past the last piece stay in the slot");
+
+template <int R, bool OUT_F16>
+__global__ __launch_bounds__(kRingThreads, 5) void decode_ring_kernel(Args a) {
+  constexpr int NB = 1;
+  constexpr int kRed = 2 * 4 * 64 * 16;          // [ks][f][64 lanes][4] fp32
+  constexpr int kRing = R * kRingSlot;
+  __shared__ __attribute__((aligned(16))) uint32_t lut[32];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing > kRed ? kRing : kRed];
+  __shared__ uint32_t last_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nblk = static_cast<int>(gridDim.x);
+  const int b = static_cast<int>(blockIdx.x);
+  const int L = a.remap ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int gi = L / a.splits;
+  const int sidx = L - gi * a.splits;
+
+  if (tid < 16) {
+    u32x2_t e;
+    e.x = nibble_selector(tid, 0);
+    e.y = nibble_selector(tid, 1);
+    reinterpret_cast<u32x2_t*>(lut)[tid] = e;
   }
-  if (tid == 0) __hip_atomic_store(&a.counters[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+
+  // The workgroup's GroupTile columns (the host keeps 1 <= count <= 63) and
+  // their offsets, lane i holding offsets[g_begin + i].
+  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * sidx / a.splits);
+  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (sidx + 1) / a.splits);
+  const int cnt = c_end - c_begin;
+  const int64_t g_begin = static_cast<int64_t>(gi) * a.Gc + c_begin;
+  const uint32_t ov = a.offsets[g_begin + min(lane, cnt)];
+  auto off_at = [&](int c) -> uint32_t { return __builtin_amdgcn_readlane(ov, min(c - c_begin, 63)); };
+  // The shuffle runs in all lanes (a lane reading an inactive one gets 0).
+  const uint32_t ov_next = __shfl_down(ov, 1);
+  const uint32_t widest = wave_max(lane < cnt ? ov_next - ov : 0u);
+
+  const int role = w < 4 ? 0 : w - 3;   // 0 compute, 1 loads, 2 bitmap tables
+  const uint64_t top = a.values_alloc - 16;
+  auto slot_vals = [&](int s) { return smem + s * kRingSlot; };
+  auto slot_bm = [&](int s) { return smem + s * kRingSlot + kRingVals; };
+  auto slot_tab = [&](int s) { return smem + s * kRingSlot + kRingVals + 512; };
+  auto slot_x = [&](int s) { return smem + s * kRingSlot + kRingVals + 512 + kTabBytes; };
+
+  // Loader: the bitmap words of GroupTile c (lanes 0-31, 16 bytes each) into
+  // slot s; one load.
+  auto issue_bm = [&](int c, int s) {
+    const int64_t g = static_cast<int64_t>(gi) * a.Gc + c;
+    if (lane < 32) lds_dma16_tracked(a.bitmaps + g * kBtPerGt + 2 * lane, slot_bm(s));
+  };
+  // Loader: value elements [e0, e1) into slot s, from the 16-byte piece
+  // holding e0 on; returns the number of loads (1 KB each).  Pieces past the
+  // range repeat its last one, and the range is cut to what a slot takes.
+  auto issue_vals = [&](uint32_t e0, uint32_t e1, int s) -> int {
+    const uint64_t a0 = min(chunk_start<false>(e0), top);
+    const uint32_t pieces = min(chunk_count<false>(e1, a0), kRingPieces);
+    const uint32_t last = min(pieces > 0 ? pieces - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
+    const int nl = static_cast<int>((pieces + 63) / 64);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
+    for (int i = 0; i < nl; ++i) lds_dma16_tracked(src + min(64u * i + lane, last), slot_vals(s) + 1024 * i);
+    return nl;
+  };
+  // Loader: X^T of GroupTile column c (16 tokens x 64 k) into slot s, two
+  // loads of 1 KB, one per k half.  Four consecutive lanes read one token's
+  // 64 contiguous bytes of the half (one address-unit cycle, where the MFMA
+  // B layout would take four); their pieces are rotated by token / 4 so that
+  // the compute waves' 16-lane reads of B fragments fall in 16 different
+  // bank groups.  Lane 4j + t holds piece (t - j/4) mod 4 of token j.
+  auto issue_x = [&](int c, int s) {
+    const int j = lane >> 2, t = lane & 3;
+    const int piece = (t - (j >> 2)) & 3;
+    const uint16_t* src = a.X + static_cast<size_t>(min(j, a.N - 1)) * a.K + c * kGT + piece * 8;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16_tracked(src + 32 * i, slot_x(s) + 1024 * i);
+  };
+  // The bitmap table of the value range starting at element e0 whose bitmaps
+  // are in slot s; `skip` values of the GroupTile precede the range.  Its LDS
+  // accesses are asm, so that in the wave that issues the LDS-DMA loads they
+  // do not wait for those in flight.
+  auto build_tab = [&](uint32_t e0, uint32_t skip, int s) {
+    const u32x2_t bm = lds_load_b64(lds_addr(slot_bm(s)) + 8 * lane);
+    const uint64_t a0 = min(chunk_start<false>(e0), top);
+    const uint32_t base = bitmap_prefix_reg(bm) - skip + chunk_delta<false>(e0, a0) + (s * kRingSlot) / 2;
+    u32x4_t e;
+    e.x = bm.x;
+    e.y = base;
+    e.z = bm.y;
+    e.w = base + __builtin_popcount(bm.x);
+    lds_store_b128(lds_addr(slot_tab(s)) + 16 * lane, e);
+  };
+
+  // Compute waves.
+  const int ks = w & 1;
+  const int f0 = 2 * (w >> 1);
+  const LaneMap lm = lane_map(lane);
+  const uint32_t toff = lm.tab + 256u * f0 + 128u * ks;
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  // The lane's B fragment (token n = lane % 16, k group g = lane / 16 of half
+  // ks) in a slot's X^T area: position 4n + (g + n/4) mod 4 of the half.
+  const uint32_t xoff = 1024u * ks + 16u * (4 * (lane & 15) + (((lane >> 4) + ((lane & 15) >> 2)) & 3));
+  auto compute = [&](int s) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(slot_x(s) + xoff);
+    const uint8_t* tab = slot_tab(s);
+    u32x2_t e[2];
+    e[0] = *reinterpret_cast<const u32x2_t*>(tab + toff);
+    e[1] = *reinterpret_cast<const u32x2_t*>(tab + toff + 256);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t rb = e[j].y + __builtin_popcount(e[j].x & lm.pmask);
+      const half8_t av = rebuild_row<false>(smem, lut, rb, __builtin_amdgcn_ubfe(e[j].x, lm.sh, 8));
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, x), acc[j], 0, 0, 0);
+    }
+  };
+
+  // The offsets load completes here, before the loader's first LDS-DMA: the
+  // compiler does not count those, so a later wait for it would wait for
+  // them too.
+  asm volatile("" : : "v"(ov));
+  // The roles are separate uniform paths (a branch taken by the whole wave),
+  // so that no wait for the compute waves' X^T loads can land in the
+  // loader's code.  All pass the same number of barriers: two before the
+  // first GroupTile, then one per GroupTile (four per GroupTile unpipelined).
+  const bool fast = widest <= kRingFast;
+  const int rl = __builtin_amdgcn_readfirstlane(role);
+  if (rl == 1) {
+    if (fast) {
+      // Step c issues the values of c+R-1 and the bitmaps of c+R, then waits
+      // until those issued R-2 steps before (values of c+1, bitmaps of c+2)
+      // have landed.  pend[j]: loads issued by step c-R+2+j.
+      auto step_loads = [&](int c) -> int {
+        const int sv = (c + R - 1 - c_begin) % R;
+        int n = 0;
+        if (c + R - 1 < c_end) {
+          issue_x(c + R - 1, sv);
+          n += 2 + issue_vals(off_at(c + R - 1), off_at(c + R), sv);
+        }
+        if (c + R < c_end) {
+          issue_bm(c + R, sv == R - 1 ? 0 : sv + 1);
+          ++n;
+        }
+        return n;
+      };
+      // Before the first GroupTile: the bitmaps of c_begin, then steps
+      // c_begin-R+1 .. c_begin-1.
+      issue_bm(c_begin, 0);
+      int pend[R - 1];
+#pragma unroll
+      for (int j = 0; j < R - 1; ++j) pend[j] = step_loads(c_begin - R + 1 + j);
+      int later = 0;
+#pragma unroll
+      for (int j = 0; j < R - 1; ++j) later += pend[j];
+      wait_vm(later);                              // bitmaps of c_begin
+      lds_barrier();
+      later -= pend[0];
+      wait_vm(later);                              // values of c_begin, bitmaps of c_begin+1
+      lds_barrier();
+      for (int c = c_begin; c < c_end; ++c) {
+#pragma unroll
+        for (int j = 0; j < R - 2; ++j) pend[j] = pend[j + 1];
+        pend[R - 2] = step_loads(c);
+        later = 0;
+#pragma unroll
+        for (int j = 1; j < R - 1; ++j) later += pend[j];
+        wait_vm(later);                            // values of c+1, bitmaps of c+2
+        lds_barrier();
+      }
+    } else {
+      // Unpipelined: per GroupTile, its bitmaps, then the values of TCTile
+      // rows 0-1 and of rows 2-3 in turn (each at most 4 KB + head), all in
+      // slot 0; two barriers per half.
+      lds_barrier();
+      lds_barrier();
+      for (int c = c_begin; c < c_end; ++c) {
+        const uint32_t o0 = off_at(c), o1 = off_at(c + 1);
+        issue_bm(c, 0);
+        wait_vm(0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x2_t bm = lds_load_b64(lds_addr(slot_bm(0)) + 8 * lane);
+          const uint32_t mid = __builtin_amdgcn_readlane(bitmap_prefix_reg(bm), 32);
+          const uint32_t hs = o0 + (h ? mid : 0u);
+          if (h == 0) issue_x(c, 0);
+          issue_vals(hs, h ? o1 : o0 + mid, 0);
+          wait_vm(0);
+          build_tab(hs, h ? mid : 0u, 0);
+          lds_barrier();
+          lds_barrier();
+        }
+      }
+    }
+  } else if (rl == 2) {
+    // The bitmap table of c+1 (its bitmaps landed before the barrier that
+    // opened step c) goes into its slot during step c.
+    lds_barrier();
+    if (fast) build_tab(off_at(c_begin), 0, 0);
+    lds_barrier();
+    if (fast) {
+      for (int c = c_begin; c < c_end; ++c) {
+        if (c + 1 < c_end) build_tab(off_at(c + 1), 0, (c + 1 - c_begin) % R);
+        lds_barrier();
+      }
+    } else {
+      for (int c = c_begin; c < c_end; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          lds_barrier();
+          lds_barrier();
+        }
+    }
+  } else {
+    lds_barrier();
+    lds_barrier();
+    if (fast) {
+      int s = 0;
+      for (int c = c_begin; c < c_end; ++c) {
+        compute(s);
+        s = s + 1 == R ? 0 : s + 1;
+        lds_barrier();
+      }
+    } else {
+      for (int c = c_begin; c < c_end; ++c) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          lds_barrier();
+          if (f0 == 2 * h) compute(0);
+          lds_barrier();
+        }
+      }
+    }
+  }
+
+  // Sum the two k halves of every fragment (fixed order) and finish.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+  if (role == 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) *reinterpret_cast<f32x4_t*>(red + ((ks * 4 + f0 + j) * 64 + lane) * 4) = acc[j];
+  }
+  __syncthreads();
+  finish_strip<NB, false, OUT_F16>(a, gi, sidx, kRingThreads, last_flag, [&](int n, int ml) {
+    const int f = ml >> 4;
+    const int ln = 16 * ((ml >> 2) & 3) + (n & 15);
+    return *reinterpret_cast<const f32x4_t*>(red + (f * 64 + ln) * 4) +
+           *reinterpret_cast<const f32x4_t*>(red + ((4 + f) * 64 + ln) * 4);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -578,7 +878,38 @@ struct Plan {
   int nchunk;     // columns of N per kernel pass (16 or 32)
   int cfg;        // launch configuration
   int waves;      // waves per workgroup
+  int ring;       // > 0: the workgroup-cooperative kernel with this many LDS slots
 };
+
+// Ring depth of the workgroup-cooperative decode (0: not used).  The default
+// is the measured best on MI355X; a tuning build reads USW_DECODE_RING.
+int choose_ring() {
+#ifdef USW_TUNING
+  const char* e = std::getenv("USW_DECODE_RING");
+  if (e) return std::atoi(e);
+#endif
+  return 3;
+}
+
+template <int R>
+void ring_launch(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
+  if (f16out)
+    decode_ring_kernel<R, true><<<grid, kRingThreads, 0, s>>>(a);
+  else
+    decode_ring_kernel<R, false><<<grid, kRingThreads, 0, s>>>(a);
+}
+
+// Workgroups of the ring kernel resident per compute unit (registers, LDS).
+int ring_resident(int R) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (R) {
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ring_kernel<2, true>, kRingThreads, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ring_kernel<4, true>, kRingThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ring_kernel<3, true>, kRingThreads, 0); break;
+  }
+  return (e == hipSuccess && n > 0) ? n : 4;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -594,6 +925,20 @@ Plan make_plan(const usw::Geometry& g, int N, int splits_req, bool i4, bool lean
   Plan p;
   p.nchunk = N <= 16 ? 16 : 32;
   p.cfg = choose_cfg();
+  p.ring = (!i4 && lean && N <= 16) ? choose_ring() : 0;
+  if (p.ring == 1 || p.ring > 4) p.ring = 3;
+  if (p.ring > 0) {
+    // One round of resident workgroups, each keeping at most 63 GroupTiles;
+    // the factor is clamped to K/256 like the other decode kernel's.
+    p.waves = 5;
+    static int resident[5] = {0, 0, 0, 0, 0};
+    if (resident[p.ring] == 0) resident[p.ring] = ring_resident(p.ring);
+    int64_t s = splits_req > 0 ? splits_req : (kComputeUnits * resident[p.ring]) / g.Gr;
+    const int64_t smax = std::max<int64_t>(1, g.Gc / 4);
+    const int64_t smin = (g.Gc + 62) / 63;
+    p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
+    return p;
+  }
   const CfgInfo ci = cfg_info(p.cfg, N > 16, i4, lean);
   p.waves = ci.waves;
   int64_t s = splits_req;
@@ -730,7 +1075,11 @@ usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_typ
     a.splits = p.splits;
     a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
     const bool two = nc > 16;
-    if (i4) {
+    if (p.ring > 0) {
+      if (p.ring == 2) ring_launch<2>(a, f16out, grid, s);
+      else if (p.ring == 4) ring_launch<4>(a, f16out, grid, s);
+      else ring_launch<3>(a, f16out, grid, s);
+    } else if (i4) {
       if (two) launch_decode<2, true, 3>(a, f16out, grid, s, p.cfg);
       else launch_decode<1, true, 3>(a, f16out, grid, s, p.cfg);
     } else if (lean) {
