@@ -150,9 +150,13 @@ def main():
         return
     dev = torch.device("cuda:0")
     M, K, N, s = args.M, args.K, args.N, args.sparsity
-    prefill = args.dtype == "f16" and N > 32
+    # Kernel family as usw_spmm picks it: fp16 with more than 96 tokens runs
+    # the prefill kernels, everything else the decode kernels (in passes of
+    # up to 32 tokens).  The synthetic inputs follow the prefill workload's
+    # recipe from 33 tokens on.
+    prefill = args.dtype == "f16" and N > 96
     layer_id = {(20480, 5120): 2, (11008, 4096): 0, (4096, 11008): 1}.get((M, K), 0)
-    cfg_id = 5 if args.dtype == "i4" else (4 if prefill else 2)
+    cfg_id = 5 if args.dtype == "i4" else (4 if N > 32 else 2)
 
     log(f"[bench] generating W {M}x{K} (magnitude pruning s={s}) and X [{N}][{K}]")
     W, mask, X = wl.config_case(cfg_id, M, K, N, s, layer_id=layer_id)

@@ -66,7 +66,7 @@ typedef int32_t usw_status;
 #define USW_ERR_BAD_SHAPE (-2)    /* M, K not positive multiples of gt_m, gt_k; gt_* not multiples of 16 */
 #define USW_ERR_BAD_DTYPE (-3)    /* unknown val_type or y_type */
 #define USW_ERR_BAD_N (-4)        /* N < 1 */
-#define USW_ERR_UNSUPPORTED (-5)  /* valid request with no kernel (e.g. GroupTile shape, INT4 with N > 32) */
+#define USW_ERR_UNSUPPORTED (-5)  /* valid request with no kernel (a GroupTile shape other than 64x64) */
 #define USW_ERR_MISALIGNED (-6)   /* a device pointer is not 16-byte aligned */
 #define USW_ERR_WORKSPACE (-7)    /* workspace NULL or smaller than usw_spmm_workspace() reports */
 #define USW_ERR_CORRUPT (-8)      /* usw_validate: offsets disagree with the bitmaps */
@@ -167,8 +167,10 @@ usw_status usw_spmm_workspace(const usw_fmt* fmt, int32_t N, size_t* bytes);
  *       enqueues work; it returns before the kernels finish.
  * Accumulation is fp32 (each product of two fp16 values is exact in fp32);
  * the result is deterministic: the same inputs give the same bits.
- * Kernels: fp16 values with N <= 32 take the decode kernel, N > 32 the
- * prefill (MFMA) kernel; INT4 values take the INT4 kernel (N <= 32).
+ * Kernels: fp16 values with N <= 96 take the decode kernels, in passes of
+ * up to 32 tokens (one pass for N <= 32), N > 96 the prefill (MFMA)
+ * kernels; INT4 values take the INT4 decode kernel, in passes of up to 32
+ * tokens, for any N.
  * The values buffer must hold the padded size usw_encode_query reports.
  * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_N, UNSUPPORTED, MISALIGNED,
  * WORKSPACE, HIP.

@@ -298,6 +298,21 @@ def test_prefill_layers(lid, name):
         assert_parity(Y[rows], ob.spmm_fp64(Wd, Xs), ob.abs_bound(Wd, Xs), f"prefill {name} N={N} (48 sampled rows)")
 
 
+@pytest.mark.parametrize("N", [33, 48, 100])
+def test_int4_many_tokens(N):
+    """INT4 values with more than 32 tokens run in 32-token decode passes;
+    power-of-two scales and small-integer X make the result exact, so bit
+    for bit against the oracle."""
+    rng = np.random.default_rng(400 + N)
+    M, K = 320, 448
+    mask = wl.mask_bernoulli(M, K, 0.5, rng)
+    W = wl.weight_int4_exact(M, K, rng, mask)
+    X = wl.activations_small_int(N, K, rng)
+    Y = run_gpu(W, mask, X, "i4", out=torch.float32)
+    Yref, _ = oracle_ref(W, mask, X, "i4")
+    assert np.array_equal(Y, Yref)
+
+
 def test_int4_layer():
     M, K = 20480, 5120
     W, mask, X = wl.config_case(5, M, K, 2, 0.5)

@@ -913,6 +913,21 @@ int ring_resident(int R) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// fp16 values with more than this many tokens take the prefill kernels;
+// fewer take the decode kernels in passes of up to 32 tokens, which re-read
+// the weight per pass but beat the 256-token prefill tiles up to 96 tokens
+// on MI355X (11008x4096 and 4096x11008: 1.3-2.0x at 48-96, even at 128).
+// A tuning build reads USW_DECODE_MAX_N.
+int decode_max_n() {
+#ifdef USW_TUNING
+  const char* e = std::getenv("USW_DECODE_MAX_N");
+  if (e) return std::atoi(e);
+#endif
+  return 96;
+}
+
+bool use_prefill(const usw_fmt* f, int32_t N) { return f->val_type == USW_VAL_F16 && N > decode_max_n(); }
+
 // Five 1 KB value chunks per slot when an fp16 matrix is at most 55% dense on
 // average (a GroupTile then needs more than five only far in the tail; such
 // a wave takes the two-half path), six otherwise.
@@ -966,7 +981,6 @@ usw_status check_common(const usw_fmt* f, int32_t y_type, int32_t N, usw::Geomet
   if (N < 1) return USW_ERR_BAD_N;
   if (f->reserved != 0) return USW_ERR_BAD_SHAPE;
   if (f->gt_m != kGT || f->gt_k != kGT) return USW_ERR_UNSUPPORTED;
-  if (f->val_type == USW_VAL_I4 && N > 32) return USW_ERR_UNSUPPORTED;
   if (f->nnz < 0 || f->nnz >= (int64_t(1) << 32)) return USW_ERR_BAD_SHAPE;
   if (static_cast<int64_t>(N) * g->M > (int64_t(1) << 40)) return USW_ERR_BAD_SHAPE;
   return USW_OK;
@@ -1032,7 +1046,7 @@ usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_typ
   if (!aligned16(X) || !aligned16(Y) || !aligned16(f->bitmaps) || !aligned16(f->values) ||
       (reinterpret_cast<uintptr_t>(f->offsets) & 3u))
     return USW_ERR_MISALIGNED;
-  if (f->val_type == USW_VAL_F16 && N > 32) {
+  if (use_prefill(f, N)) {
     const usw::PrefillPlan pp = usw::prefill_plan(g, N, splits_req);
     const size_t need = usw::prefill_workspace_bytes(g, N, pp);
     if (need > 0) {
@@ -1113,7 +1127,7 @@ usw_status usw_spmm_workspace_ex(const usw_fmt* f, int32_t N, int32_t splits, si
   usw_status st = check_common(f, USW_OUT_F16, N, &g);
   if (st) return st;
   const int sr = splits < 0 ? 0 : splits;
-  if (f->val_type == USW_VAL_F16 && N > 32)
+  if (use_prefill(f, N))
     *bytes = usw::prefill_workspace_bytes(g, N, usw::prefill_plan(g, N, sr));
   else
     *bytes = workspace_bytes(g, make_plan(g, N, sr, f->val_type == USW_VAL_I4, lean_values(f, g)));
@@ -1126,7 +1140,7 @@ usw_status usw_spmm_counter_bytes(const usw_fmt* f, int32_t N, int32_t splits, s
   usw_status st = check_common(f, USW_OUT_F16, N, &g);
   if (st) return st;
   const int sr = splits < 0 ? 0 : splits;
-  if (f->val_type == USW_VAL_F16 && N > 32) {
+  if (use_prefill(f, N)) {
     *bytes = usw::prefill_counter_bytes(g, usw::prefill_plan(g, N, sr));
   } else {
     const Plan p = make_plan(g, N, sr, f->val_type == USW_VAL_I4, lean_values(f, g));
