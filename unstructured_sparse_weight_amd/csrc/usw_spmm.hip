@@ -521,9 +521,9 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
 // range of GroupTile columns; all six pass one barrier per GroupTile.
 //  * Wave 4 moves each GroupTile's values and X^T column, and the bitmap
 //    words of the GroupTile after, straight into a ring of R LDS slots with
-//    global_load_lds_dwordx4,
-//    R - 1 GroupTiles ahead, so no register holds them in flight.  It waits
-//    for its own loads with explicit vmcnt counts before each barrier.
+//    global_load_lds_dwordx4, R - 1 GroupTiles ahead, so no register holds
+//    them in flight.  It waits for its own loads with explicit vmcnt counts
+//    before each barrier.
 //  * Wave 5 writes the bitmap table of the next GroupTile into its slot.
 //  * Compute wave q (0-3) rebuilds fragments f = 2 (q / 2) and 2 (q / 2) + 1
 //    for ks = q % 2: two rows per lane per GroupTile, and multiplies them
@@ -663,17 +663,19 @@ __global__ __launch_bounds__(kRingThreads, 5) void decode_ring_kernel(Args a) {
   // compiler does not count those, so a later wait for it would wait for
   // them too.
   asm volatile("" : : "v"(ov));
-  // The roles are separate uniform paths (a branch taken by the whole wave),
-  // so that no wait for the compute waves' X^T loads can land in the
-  // loader's code.  All pass the same number of barriers: two before the
-  // first GroupTile, then one per GroupTile (four per GroupTile unpipelined).
+  // The roles are separate uniform paths (a branch taken by the whole wave).
+  // Lowered as a divergent branch, one role's code would follow another's,
+  // and the compute waves' LDS reads would wait for the loader's LDS-DMA
+  // loads.  All pass the same number of barriers: two before the first
+  // GroupTile, then one per GroupTile (four per GroupTile unpipelined).
   const bool fast = widest <= kRingFast;
   const int rl = __builtin_amdgcn_readfirstlane(role);
   if (rl == 1) {
     if (fast) {
-      // Step c issues the values of c+R-1 and the bitmaps of c+R, then waits
-      // until those issued R-2 steps before (values of c+1, bitmaps of c+2)
-      // have landed.  pend[j]: loads issued by step c-R+2+j.
+      // Step c issues the values and X^T of c+R-1 and the bitmaps of c+R,
+      // then waits until those issued R-2 steps before (values and X^T of
+      // c+1, bitmaps of c+2) have landed.  pend[j]: loads issued by step
+      // c-R+2+j.
       auto step_loads = [&](int c) -> int {
         const int sv = (c + R - 1 - c_begin) % R;
         int n = 0;
@@ -699,7 +701,7 @@ __global__ __launch_bounds__(kRingThreads, 5) void decode_ring_kernel(Args a) {
       wait_vm(later);                              // bitmaps of c_begin
       lds_barrier();
       later -= pend[0];
-      wait_vm(later);                              // values of c_begin, bitmaps of c_begin+1
+      wait_vm(later);                              // values and X^T of c_begin, bitmaps of c_begin+1
       lds_barrier();
       for (int c = c_begin; c < c_end; ++c) {
 #pragma unroll
@@ -708,7 +710,7 @@ __global__ __launch_bounds__(kRingThreads, 5) void decode_ring_kernel(Args a) {
         later = 0;
 #pragma unroll
         for (int j = 1; j < R - 1; ++j) later += pend[j];
-        wait_vm(later);                            // values of c+1, bitmaps of c+2
+        wait_vm(later);                            // values and X^T of c+1, bitmaps of c+2
         lds_barrier();
       }
     } else {
