@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--N", type=int, default=16)
     p.add_argument("--sparsity", type=float, default=0.5)
     p.add_argument("--dtype", default="f16", choices=["f16", "i4"])
+    p.add_argument("--format", default="tca", choices=["tca", "union"],
+                   help="tca: TCA-BME bitmaps (usw_spmm); union: IE-BME union-mask INT4 with 64x64 tiles and 2x2"
+                        " areas (usw_union_spmm; implies --dtype i4)")
     p.add_argument("--cpu-reps", type=int, default=5)
     p.add_argument("--rotation", type=int, default=0,
                    help="number of encoded copies the steps rotate over (default: enough for > 512 MB, so reads come"
@@ -71,7 +74,10 @@ def parse():
 # Sources that make up each kernel: a measured traffic figure is only used
 # while they are unchanged.
 KERNEL_SOURCES = {
-    "decode": ["unstructured_sparse_weight_amd/csrc/usw_spmm.hip", "unstructured_sparse_weight_amd/csrc/usw_device.h"],
+    "decode": ["unstructured_sparse_weight_amd/csrc/usw_spmm.hip", "unstructured_sparse_weight_amd/csrc/usw_decode_common.h",
+               "unstructured_sparse_weight_amd/csrc/usw_device.h"],
+    "union": ["unstructured_sparse_weight_amd/csrc/usw_union.hip", "unstructured_sparse_weight_amd/csrc/usw_decode_common.h",
+              "unstructured_sparse_weight_amd/csrc/usw_device.h"],
     "prefill": ["unstructured_sparse_weight_amd/csrc/usw_prefill.hip", "unstructured_sparse_weight_amd/csrc/usw_device.h"],
 }
 
@@ -149,6 +155,9 @@ def main():
         calibrate_copy(args)
         return
     dev = torch.device("cuda:0")
+    union = args.format == "union"
+    if union:
+        args.dtype = "i4"
     M, K, N, s = args.M, args.K, args.N, args.sparsity
     # Kernel family as usw_spmm picks it: fp16 with more than 96 tokens runs
     # the prefill kernels, everything else the decode kernels (in passes of
@@ -161,30 +170,46 @@ def main():
     log(f"[bench] generating W {M}x{K} (magnitude pruning s={s}) and X [{N}][{K}]")
     W, mask, X = wl.config_case(cfg_id, M, K, N, s, layer_id=layer_id)
     t = time.time()
-    h = usw.encode_host(W, mask, (64, 64), args.dtype)
-    log(f"[bench] host encode {time.time() - t:.2f} s, nnz={h.nnz}")
-    ngt = (M // 64) * (K // 64)
-    vbytes = 2.0 if args.dtype == "f16" else 0.5
-    alg = algorithmic_bytes(M, K, N, h.nnz, ngt, vbytes, 2, args.dtype == "i4")
+    if union:
+        h = usw.union_encode_host(W, mask, (64, 64), (2, 2), "i4")
+        kept = int(mask.sum())
+        log(f"[bench] host union encode {time.time() - t:.2f} s, payload={h.payload} for nnz={kept}"
+            f" ({h.payload / max(kept, 1):.3f} stored per kept weight)")
+        # Union words, offsets, INT4 payload, scales, X and Y, each moved once.
+        alg = (h.bitmaps.nbytes + h.offsets.nbytes + h.values_bytes + 2 * M + 2 * N * K + 2 * N * M)
+    else:
+        h = usw.encode_host(W, mask, (64, 64), args.dtype)
+        log(f"[bench] host encode {time.time() - t:.2f} s, nnz={h.nnz}")
+        ngt = (M // 64) * (K // 64)
+        vbytes = 2.0 if args.dtype == "f16" else 0.5
+        alg = algorithmic_bytes(M, K, N, h.nnz, ngt, vbytes, 2, args.dtype == "i4")
     enc_bytes = h.bitmaps.nbytes + h.offsets.nbytes + h.values.nbytes
     R = args.rotation if args.rotation > 0 else max(5, math.ceil(600e6 / enc_bytes))
-    encs = [usw.to_device(h, dev) for _ in range(R)]
+    to_dev = usw.union_to_device if union else usw.to_device
+    encs = [to_dev(h, dev) for _ in range(R)]
     xs = [torch.from_numpy(X).to(dev) for _ in range(R)]
     ys = [torch.empty((N, M), dtype=torch.float16, device=dev) for _ in range(R)]
 
     L = usw.lib()
     fmts = [e.fmt() for e in encs]
-    wsb = usw.spmm_workspace_bytes(encs[0], N, args.splits)
+    if union:
+        wsb = usw.union_workspace_bytes(encs[0], N, args.splits)[0]
+    else:
+        wsb = usw.spmm_workspace_bytes(encs[0], N, args.splits)
     ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=dev)   # counter region starts at zero
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
 
     def step(i, on=sp):
         j = i % R
-        st = L.usw_spmm_ex(ctypes.byref(fmts[j]), xs[j].data_ptr(), ys[j].data_ptr(), 1, N, args.splits,
-                           ws.data_ptr(), wsb, on)
+        if union:
+            st = L.usw_union_spmm(ctypes.byref(fmts[j]), xs[j].data_ptr(), ys[j].data_ptr(), 1, N, args.splits,
+                                  ws.data_ptr(), wsb, on)
+        else:
+            st = L.usw_spmm_ex(ctypes.byref(fmts[j]), xs[j].data_ptr(), ys[j].data_ptr(), 1, N, args.splits,
+                               ws.data_ptr(), wsb, on)
         if st != 0:
-            raise RuntimeError(f"usw_spmm failed: {st}")
+            raise RuntimeError(f"spmm failed: {st}")
 
     for i in range(args.warmup):
         step(i)
@@ -288,9 +313,11 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(W, mask, X, M, K, N, args.dtype, args.cpu_reps)
+        cpu = cpu_baseline(W, mask, X, M, K, N, args.dtype, args.cpu_reps, union)
 
-    if prefill:
+    if union:
+        kname = "union_decode_kernel"
+    elif prefill:
         kname = "prefill_ws_kernel" if N > 256 else "prefill_kernel"
     else:
         # fp16 values at most 55% dense with N <= 16 take the workgroup-
@@ -320,7 +347,8 @@ def main():
     else:
         workload = f"spmm_{M}x{K}_s{s}_N{N}"
     if args.splits == 0:
-        roofline["traffic"] = measured_traffic(f"{kname}_{workload}", "prefill" if prefill else "decode")
+        roofline["traffic"] = measured_traffic(f"{kname}_{workload}",
+                                               "union" if union else ("prefill" if prefill else "decode"))
     roofline["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     out = {
         "metric": METRIC if (M, K, N, s, args.dtype) == (20480, 5120, 16, 0.5, "f16") else
@@ -336,7 +364,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16" if args.dtype == "f16" else "i4",
         "data": "synthetic (seeded N(0,0.02) weights, magnitude pruning, N(0,1) activations)",
-        "config": {"workload": workload,
+        "config": {"workload": workload, "format": "ie_bme_union_2x2" if union else "tca_bme",
                    "M": M, "K": K, "N": N, "sparsity": s, "values": args.dtype, "groupTile": "64x64",
                    "rotation_copies": R, "splits": args.splits or "auto",
                    "launch": "eager" if args.eager else "hip_graph"},
@@ -345,21 +373,29 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "dense_fp16": dense,
-        "nnz": int(h.nnz),
+        "nnz": int(mask.sum()) if union else int(h.nnz),
     }
+    if union:
+        out["union_payload"] = int(h.payload)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(W, mask, X, M, K, N, dtype, reps):
+def cpu_baseline(W, mask, X, M, K, N, dtype, reps, union=False):
     """The oracle as it stands (decode + fp64 product) on the host cores."""
     import oracle.tca_bme as ob
+    import oracle.ie_bme as ou
     t = time.perf_counter()
-    enc = ob.encode(W, mask) if dtype == "f16" else ob.encode_i4(W, mask)
+    if union:
+        enc = ou.encode_union(W, mask, 64, 64, 2, 2, ob.VAL_I4)
+        product = ou.spmm_union
+    else:
+        enc = ob.encode(W, mask) if dtype == "f16" else ob.encode_i4(W, mask)
+        product = ob.spmm
     t_enc = time.perf_counter() - t
     times = []
     for _ in range(reps):
         t = time.perf_counter()
-        Y = ob.spmm(enc, X)
+        Y = product(enc, X)
         times.append(time.perf_counter() - t)
         del Y
     best = min(times)
@@ -369,7 +405,7 @@ def cpu_baseline(W, mask, X, M, K, N, dtype, reps):
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
             t = time.perf_counter()
-            Y = ob.spmm(enc, X)
+            Y = product(enc, X)
             single = time.perf_counter() - t
             del Y
     except ImportError:

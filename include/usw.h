@@ -210,6 +210,99 @@ usw_status usw_spmm_ex(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ---------------------------------------------------------------------------
+ * IE-BME union-mask low-bit format ("UnionSparse: An Index-Efficient Sparsity
+ * Framework for Low-Bit Sparse LLM Inference on Edge", section on IE-BME; the
+ * gather follows its LSPD section).
+ *
+ *   - Local tile (LT): lt_m x lt_k weights; LTs of the matrix stored
+ *     row-major.  An LT is cut into an r_a x c_a grid of areas of
+ *     (lt_m/r_a) x (lt_k/c_a), Q = r_a * c_a; area q = a_r * c_a + a_c.
+ *   - Union mask: bit (i, j) of an LT is set when any of the Q weights
+ *     W[a_r lt_m/r_a + i][a_c lt_k/c_a + j] of the LT is kept.  It is scanned
+ *     row-major and packed into uint64 words, least significant bit first;
+ *     (lt_m/r_a) (lt_k/c_a) must be a multiple of 64, so each LT owns
+ *     NW = lt_m lt_k / (64 Q) whole words.  bitmaps[NLT * NW].
+ *   - offsets[NLT+1]: uint32 payload-element index of each LT's payload,
+ *     offsets[t+1] = offsets[t] + Q * P_t with P_t the LT's set union bits.
+ *   - values: per LT, Q streams of P_t elements one after the other; the
+ *     element of area q at the active position of compact rank r (active
+ *     positions before it, row-major) is values[offsets[t] + q P_t + r].  A
+ *     pruned weight of an active group is stored as 0.  INT4 elements are
+ *     packed and quantised as above (per-row scales over the kept weights).
+ * The mask is authoritative, as for usw_encode.  Activations stay fp16.
+ * ---------------------------------------------------------------------------
+ */
+
+/* Non-owning view of one IE-BME encoding (device pointers for usw_union_spmm,
+ * host pointers for usw_union_validate). */
+typedef struct usw_union_fmt {
+  int32_t M, K;             /* W is M x K */
+  int32_t lt_m, lt_k;       /* LT shape */
+  int32_t r_a, c_a;         /* area grid of an LT */
+  int32_t val_type;         /* USW_VAL_I4 (USW_VAL_F16 for host-side use only) */
+  int32_t reserved;         /* must be 0 */
+  int64_t payload;          /* stored payload elements = offsets[NLT] */
+  const uint64_t* bitmaps;  /* [NLT * NW] */
+  const uint32_t* offsets;  /* [NLT+1] */
+  const void* values;       /* I4: uint8 [ceil(payload/2)], padded as usw_union_encode_query says */
+  const uint16_t* scales;   /* I4: fp16 bits [M] */
+} usw_union_fmt;
+
+/*
+ * Sizes of an IE-BME encoding from the mask alone (host memory); arguments as
+ * usw_encode_query plus the LT shape and area grid.  payload = sum of Q P_t.
+ * values_alloc is the logical size rounded down to 16 bytes, plus 16.
+ * Errors: NULL_ARG, BAD_SHAPE (M, K not multiples of lt_m, lt_k; lt_m, lt_k
+ * not multiples of r_a, c_a; an area position count not a multiple of 64),
+ * BAD_DTYPE, CAPACITY (payload >= 2^32).
+ */
+usw_status usw_union_encode_query(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
+                                  int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type, int64_t* payload,
+                                  size_t* bytes_bitmaps, size_t* bytes_offsets, size_t* bytes_values,
+                                  size_t* bytes_values_alloc, size_t* bytes_scales);
+
+/*
+ * Encode W (host memory) into caller-allocated host buffers following the
+ * IE-BME construction above.  Buffers as usw_encode; values_capacity bytes
+ * of values are written (zero past the logical size).  Deterministic.
+ * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, CAPACITY.
+ */
+usw_status usw_union_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
+                            int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type, uint64_t* bitmaps,
+                            uint32_t* offsets, void* values, size_t values_capacity, uint16_t* scales);
+
+/*
+ * Check a host copy of an IE-BME encoding: shape fields, offsets[0] = 0,
+ * offsets[NLT] = payload, and each LT's span equal to Q times the popcount
+ * of its union words.  Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, CORRUPT.
+ */
+usw_status usw_union_validate(const usw_union_fmt* host_fmt);
+
+/*
+ * Workspace bytes and counter bytes of usw_union_spmm for this matrix, N and
+ * split factor (splits = 0: automatic; otherwise clamped to
+ * [ceil(K / (64 * 4 * 63)), max(1, K / 256)]).  The workspace starts with
+ * the counter bytes, which must be zero when a call starts (each call leaves
+ * them zero), then fp32 partial sums.  Errors: as usw_union_spmm's checks.
+ */
+usw_status usw_union_spmm_workspace(const usw_union_fmt* fmt, int32_t N, int32_t splits, size_t* bytes);
+usw_status usw_union_spmm_counter_bytes(const usw_union_fmt* fmt, int32_t N, int32_t splits, size_t* bytes);
+
+/*
+ * Y = W_sp . X on the GPU from an IE-BME encoding (device pointers), with the
+ * same X, Y, workspace and stream conventions as usw_spmm.  The kernel takes
+ * INT4 values, 64 x 64 LTs and a 2 x 2 area grid, in passes of up to 32
+ * tokens; each lane reads one union-mask row's rank once and gathers the
+ * rows of all four areas with it (the LSPD gather).  fp32 accumulation,
+ * deterministic.  Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_N,
+ * UNSUPPORTED (other LT shapes or area grids, or fp16 values), MISALIGNED,
+ * WORKSPACE, HIP.
+ */
+usw_status usw_union_spmm(const usw_union_fmt* fmt, const uint16_t* X, void* Y, int32_t y_type, int32_t N,
+                          int32_t splits, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Measurement utility, not part of the SpMM path: reads the first
  * bytes / 16 * 16 bytes of the device buffer buf once (16-byte loads,
  * non-temporal) on the stream, so that a caller can time the GPU's

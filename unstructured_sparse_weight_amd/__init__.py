@@ -20,10 +20,12 @@ from typing import Optional
 import numpy as np
 
 from ._lib import (USW_OUT_F16, USW_OUT_F32, USW_VAL_F16, USW_VAL_I4, EXPORTED, UswError, UswFmt,  # noqa: F401
-                   check, lib)
+                   UswUnionFmt, check, lib)
 
 __all__ = ["HostEncoding", "Encoding", "encode_host", "encode", "to_device", "validate", "spmm",
-           "spmm_workspace_bytes", "spmm_counter_bytes", "UswError", "lib"]
+           "spmm_workspace_bytes", "spmm_counter_bytes", "UnionHostEncoding", "UnionEncoding",
+           "union_encode_host", "union_encode", "union_to_device", "union_validate", "union_spmm",
+           "union_workspace_bytes", "UswError", "lib"]
 
 _VAL = {"f16": USW_VAL_F16, "i4": USW_VAL_I4}
 
@@ -73,6 +75,51 @@ class Encoding:
         return self.bitmaps.device
 
 
+@dataclass
+class UnionHostEncoding:
+    """IE-BME encoding in host memory (numpy), as written by usw_union_encode."""
+    M: int
+    K: int
+    lt_m: int
+    lt_k: int
+    r_a: int
+    c_a: int
+    val_type: int
+    payload: int
+    bitmaps: np.ndarray           # uint64 [NLT * NW]
+    offsets: np.ndarray           # uint32 [NLT+1]
+    values: np.ndarray            # uint8, padded allocation
+    values_bytes: int             # logical byte count
+    scales: Optional[np.ndarray]  # uint16 fp16 bits [M] (INT4) or None
+
+    def fmt(self) -> UswUnionFmt:
+        return UswUnionFmt(self.M, self.K, self.lt_m, self.lt_k, self.r_a, self.c_a, self.val_type, 0, self.payload,
+                           self.bitmaps.ctypes.data, self.offsets.ctypes.data, self.values.ctypes.data,
+                           self.scales.ctypes.data if self.scales is not None else None)
+
+
+@dataclass
+class UnionEncoding:
+    """IE-BME encoding on a GPU (torch tensors) plus its usw_union_fmt view."""
+    M: int
+    K: int
+    lt_m: int
+    lt_k: int
+    r_a: int
+    c_a: int
+    val_type: int
+    payload: int
+    bitmaps: "object"
+    offsets: "object"
+    values: "object"
+    scales: "object"
+
+    def fmt(self) -> UswUnionFmt:
+        return UswUnionFmt(self.M, self.K, self.lt_m, self.lt_k, self.r_a, self.c_a, self.val_type, 0, self.payload,
+                           self.bitmaps.data_ptr(), self.offsets.data_ptr(), self.values.data_ptr(),
+                           self.scales.data_ptr() if self.scales is not None else None)
+
+
 def _as_numpy_f16(W) -> np.ndarray:
     if hasattr(W, "detach"):
         W = W.detach().cpu().numpy()
@@ -111,6 +158,100 @@ def encode_host(W, mask=None, gt=(64, 64), dtype: str = "f16") -> HostEncoding:
                        values.ctypes.data, b_alloc, scales.ctypes.data if scales is not None else None),
           "usw_encode")
     return HostEncoding(M, K, gt[0], gt[1], vt, nnz.value, bitmaps, offsets, values, b_val, scales)
+
+
+def _as_mask(mask, shape):
+    if mask is None:
+        return None
+    if hasattr(mask, "detach"):
+        mask = mask.detach().cpu().numpy()
+    mask = np.ascontiguousarray(mask.astype(np.uint8, copy=False))
+    if mask.shape != shape:
+        raise ValueError("mask shape must match W")
+    return mask
+
+
+def union_encode_host(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4") -> UnionHostEncoding:
+    """Run usw_union_encode on host arrays (IE-BME union-mask format)."""
+    W = _as_numpy_f16(W)
+    if W.ndim != 2:
+        raise ValueError("W must be 2-D")
+    M, K = W.shape
+    mask = _as_mask(mask, W.shape)
+    vt = _VAL[dtype]
+    L = lib()
+    payload = ctypes.c_int64()
+    sz = [ctypes.c_size_t() for _ in range(5)]
+    wp = W.ctypes.data
+    mp = mask.ctypes.data if mask is not None else None
+    check(L.usw_union_encode_query(wp, mp, M, K, lt[0], lt[1], areas[0], areas[1], vt, ctypes.byref(payload),
+                                   *[ctypes.byref(s) for s in sz]), "usw_union_encode_query")
+    b_bm, b_off, b_val, b_alloc, _ = (s.value for s in sz)
+    bitmaps = np.empty(b_bm // 8, dtype=np.uint64)
+    offsets = np.empty(b_off // 4, dtype=np.uint32)
+    values = np.empty(b_alloc, dtype=np.uint8)
+    scales = np.empty(M, dtype=np.uint16) if vt == USW_VAL_I4 else None
+    check(L.usw_union_encode(wp, mp, M, K, lt[0], lt[1], areas[0], areas[1], vt, bitmaps.ctypes.data,
+                             offsets.ctypes.data, values.ctypes.data, b_alloc,
+                             scales.ctypes.data if scales is not None else None), "usw_union_encode")
+    return UnionHostEncoding(M, K, lt[0], lt[1], areas[0], areas[1], vt, payload.value, bitmaps, offsets, values,
+                             b_val, scales)
+
+
+def union_validate(enc: UnionHostEncoding) -> None:
+    """usw_union_validate on a host encoding (raises UswError when corrupt)."""
+    f = enc.fmt()
+    check(lib().usw_union_validate(ctypes.byref(f)), "usw_union_validate")
+
+
+def union_to_device(enc: UnionHostEncoding, device="cuda") -> UnionEncoding:
+    import torch
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+    return UnionEncoding(enc.M, enc.K, enc.lt_m, enc.lt_k, enc.r_a, enc.c_a, enc.val_type, enc.payload,
+                         t(enc.bitmaps.view(np.int64)), t(enc.offsets.view(np.int32)), t(enc.values),
+                         t(enc.scales.view(np.int16)) if enc.scales is not None else None)
+
+
+def union_encode(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4", device="cuda") -> UnionEncoding:
+    """Encode on the host (usw_union_encode) and copy the buffers to ``device``."""
+    return union_to_device(union_encode_host(W, mask, lt, areas, dtype), device)
+
+
+def union_workspace_bytes(enc: UnionEncoding, N: int, splits: int = 0):
+    """(workspace bytes, counter bytes) of usw_union_spmm."""
+    f = enc.fmt()
+    b = ctypes.c_size_t()
+    c = ctypes.c_size_t()
+    check(lib().usw_union_spmm_workspace(ctypes.byref(f), int(N), int(splits), ctypes.byref(b)),
+          "usw_union_spmm_workspace")
+    check(lib().usw_union_spmm_counter_bytes(ctypes.byref(f), int(N), int(splits), ctypes.byref(c)),
+          "usw_union_spmm_counter_bytes")
+    return b.value, c.value
+
+
+def union_spmm(enc: UnionEncoding, x, y=None, out_dtype=None, splits: int = 0, stream=None):
+    """Y [N][M] = W_sp . X from an IE-BME encoding (usw_union_spmm)."""
+    import torch
+    if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != enc.K:
+        raise ValueError("x must be [N][K] float16")
+    if not x.is_contiguous():
+        x = x.contiguous()
+    N = x.shape[0]
+    if y is None:
+        y = torch.empty((N, enc.M), dtype=out_dtype or torch.float16, device=x.device)
+    if y.shape != (N, enc.M) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [N][M] tensor")
+    yt = {torch.float16: USW_OUT_F16, torch.float32: USW_OUT_F32}.get(y.dtype)
+    if yt is None:
+        raise ValueError("y must be float16 or float32")
+    f = enc.fmt()
+    nbytes, cbytes = union_workspace_bytes(enc, N, splits)
+    ws = _workspace(x.device, nbytes, cbytes) if nbytes else None
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    check(lib().usw_union_spmm(ctypes.byref(f), x.data_ptr(), y.data_ptr(), yt, N, int(splits),
+                               ws.data_ptr() if ws is not None else None, nbytes, ctypes.c_void_p(st.cuda_stream)),
+          "usw_union_spmm")
+    return y
 
 
 def validate(enc: HostEncoding) -> None:

@@ -27,6 +27,8 @@ EXPORTED = (
     "usw_abi_version", "usw_status_str", "usw_encode_query", "usw_encode", "usw_validate",
     "usw_spmm_workspace", "usw_spmm", "usw_spmm_workspace_ex", "usw_spmm_ex", "usw_spmm_counter_bytes",
     "usw_probe_read",
+    "usw_union_encode_query", "usw_union_encode", "usw_union_validate", "usw_union_spmm_workspace",
+    "usw_union_spmm_counter_bytes", "usw_union_spmm",
 )
 
 
@@ -43,6 +45,19 @@ class UswFmt(ctypes.Structure):
         ("gt_m", ctypes.c_int32), ("gt_k", ctypes.c_int32),
         ("val_type", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("nnz", ctypes.c_int64),
+        ("bitmaps", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+        ("values", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+    ]
+
+
+class UswUnionFmt(ctypes.Structure):
+    """Mirror of ``usw_union_fmt``."""
+    _fields_ = [
+        ("M", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("lt_m", ctypes.c_int32), ("lt_k", ctypes.c_int32),
+        ("r_a", ctypes.c_int32), ("c_a", ctypes.c_int32),
+        ("val_type", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("payload", ctypes.c_int64),
         ("bitmaps", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
         ("values", ctypes.c_void_p), ("scales", ctypes.c_void_p),
     ]
@@ -77,6 +92,20 @@ def _declare(lib):
     lib.usw_spmm_counter_bytes.argtypes = [P(UswFmt), c_i32, c_i32, P(c_sz)]
     lib.usw_probe_read.restype = c_i32
     lib.usw_probe_read.argtypes = [ctypes.c_void_p, c_sz, ctypes.c_void_p, ctypes.c_void_p]
+    lib.usw_union_encode_query.restype = c_i32
+    lib.usw_union_encode_query.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, P(c_i64),
+                                           P(c_sz), P(c_sz), P(c_sz), P(c_sz), P(c_sz)]
+    lib.usw_union_encode.restype = c_i32
+    lib.usw_union_encode.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                     c_sz, c_vp]
+    lib.usw_union_validate.restype = c_i32
+    lib.usw_union_validate.argtypes = [P(UswUnionFmt)]
+    lib.usw_union_spmm_workspace.restype = c_i32
+    lib.usw_union_spmm_workspace.argtypes = [P(UswUnionFmt), c_i32, c_i32, P(c_sz)]
+    lib.usw_union_spmm_counter_bytes.restype = c_i32
+    lib.usw_union_spmm_counter_bytes.argtypes = [P(UswUnionFmt), c_i32, c_i32, P(c_sz)]
+    lib.usw_union_spmm.restype = c_i32
+    lib.usw_union_spmm.argtypes = [P(UswUnionFmt), c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]
     return lib
 
 

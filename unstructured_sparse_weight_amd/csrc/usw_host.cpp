@@ -36,6 +36,29 @@ usw_status make_geometry(int64_t M, int64_t K, int64_t gt_m, int64_t gt_k, Geome
 }
 
 // fp16 bits -> double (exact).
+usw_status make_union_geometry(int64_t M, int64_t K, int64_t lt_m, int64_t lt_k, int64_t r_a, int64_t c_a,
+                               UnionGeometry* g) {
+  if (M <= 0 || K <= 0 || lt_m <= 0 || lt_k <= 0 || r_a <= 0 || c_a <= 0) return USW_ERR_BAD_SHAPE;
+  if (M % lt_m || K % lt_k || lt_m % r_a || lt_k % c_a) return USW_ERR_BAD_SHAPE;
+  if (M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 31) - 1) return USW_ERR_BAD_SHAPE;
+  const int64_t am = lt_m / r_a, ak = lt_k / c_a;
+  if ((am * ak) % 64) return USW_ERR_BAD_SHAPE;
+  g->M = M;
+  g->K = K;
+  g->lt_m = lt_m;
+  g->lt_k = lt_k;
+  g->r_a = r_a;
+  g->c_a = c_a;
+  g->Q = r_a * c_a;
+  g->am = am;
+  g->ak = ak;
+  g->lr = M / lt_m;
+  g->lc = K / lt_k;
+  g->nlt = g->lr * g->lc;
+  g->nw = am * ak / 64;
+  return USW_OK;
+}
+
 double f16_to_f64(uint16_t h) {
   const int sign = h >> 15;
   const int e = (h >> 10) & 0x1F;
@@ -154,6 +177,71 @@ size_t values_logical_bytes(int32_t val_type, int64_t nnz) {
   return val_type == USW_VAL_F16 ? static_cast<size_t>(2 * nnz) : static_cast<size_t>((nnz + 1) / 2);
 }
 
+// INT4 row scales over the kept entries (fp64 max, fp16 RNE of max / 7):
+// writes the fp16 bits and returns their values.
+std::vector<double> row_scales(const uint16_t* W, const uint8_t* mask, int64_t M, int64_t K, uint16_t* scales) {
+  std::vector<double> rscale(static_cast<size_t>(M), 0.0);
+  parallel_for(M, [&](int64_t lo, int64_t hi) {
+    for (int64_t m = lo; m < hi; ++m) {
+      double amax = 0.0;
+      for (int64_t k = 0; k < K; ++k)
+        if (is_kept(W, mask, m * K + k)) amax = std::max(amax, std::fabs(f16_to_f64(W[m * K + k])));
+      const uint16_t s = f64_to_f16_rne(amax / 7.0);
+      scales[m] = s;
+      rscale[m] = f16_to_f64(s);
+    }
+  });
+  return rscale;
+}
+
+// q = clamp(round_half_even(w / scale), -8, 7) in fp64 (0 for a zero scale).
+inline int8_t i4_code(uint16_t w, double s) {
+  if (!(s > 0.0)) return 0;
+  return static_cast<int8_t>(std::min(7.0, std::max(-8.0, std::nearbyint(f16_to_f64(w) / s))));
+}
+
+// Packs INT4 codes two per byte, element 2i in the low nibble of byte i.
+void pack_i4(const std::vector<int8_t>& q, int64_t n, uint8_t* vb) {
+  parallel_for((n + 1) / 2, [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i) {
+      const uint8_t a = static_cast<uint8_t>(q[2 * i]) & 0xF;
+      const uint8_t b = (2 * i + 1 < n) ? (static_cast<uint8_t>(q[2 * i + 1]) & 0xF) : 0;
+      vb[i] = static_cast<uint8_t>(a | (b << 4));
+    }
+  });
+}
+
+// Linear index in W of position p = i * ak + j of area q of LT t.
+inline int64_t union_elem(const UnionGeometry& g, int64_t t, int64_t q, int64_t p) {
+  const int64_t ti = t / g.lc, tj = t % g.lc;
+  const int64_t ar = q / g.c_a, ac = q % g.c_a;
+  const int64_t i = p / g.ak, j = p % g.ak;
+  return (ti * g.lt_m + ar * g.am + i) * g.K + tj * g.lt_k + ac * g.ak + j;
+}
+
+// Union bit of position p of LT t: any of the Q area weights kept.
+inline bool union_on(const UnionGeometry& g, const uint16_t* W, const uint8_t* mask, int64_t t, int64_t p) {
+  for (int64_t q = 0; q < g.Q; ++q)
+    if (is_kept(W, mask, union_elem(g, t, q, p))) return true;
+  return false;
+}
+
+// offsets[t] = payload elements before LT t (Q times the active positions).
+usw_status count_union(const UnionGeometry& g, const uint16_t* W, const uint8_t* mask, std::vector<int64_t>* off) {
+  off->assign(g.nlt + 1, 0);
+  int64_t* o = off->data();
+  parallel_for(g.nlt, [&](int64_t lo, int64_t hi) {
+    for (int64_t t = lo; t < hi; ++t) {
+      int64_t c = 0;
+      for (int64_t p = 0; p < g.am * g.ak; ++p) c += union_on(g, W, mask, t, p);
+      o[t + 1] = g.Q * c;
+    }
+  });
+  for (int64_t i = 0; i < g.nlt; ++i) o[i + 1] += o[i];
+  if (o[g.nlt] >= (int64_t(1) << 32)) return USW_ERR_CAPACITY;
+  return USW_OK;
+}
+
 }  // namespace
 
 // The kernels read whole 16-byte chunks starting at the chunk that holds a
@@ -230,19 +318,7 @@ usw_status usw_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t
 
   // INT4: per-row scale over the kept entries, in fp64.
   std::vector<double> rscale;
-  if (val_type == USW_VAL_I4) {
-    rscale.assign(M, 0.0);
-    parallel_for(M, [&](int64_t lo, int64_t hi) {
-      for (int64_t m = lo; m < hi; ++m) {
-        double amax = 0.0;
-        for (int64_t k = 0; k < K; ++k)
-          if (is_kept(W, mask, m * K + k)) amax = std::max(amax, std::fabs(f16_to_f64(W[m * K + k])));
-        const uint16_t s = f64_to_f16_rne(amax / 7.0);
-        scales[m] = s;
-        rscale[m] = f16_to_f64(s);
-      }
-    });
-  }
+  if (val_type == USW_VAL_I4) rscale = row_scales(W, mask, M, K, scales);
 
   std::vector<int8_t> q;  // INT4 codes in storage order, packed afterwards
   if (val_type == USW_VAL_I4) q.assign(static_cast<size_t>(nnz), 0);
@@ -264,10 +340,7 @@ usw_status usw_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t
         if (val_type == USW_VAL_F16) {
           v16[idx] = W[lin];
         } else {
-          const double s = rscale[lin / g.K];
-          double code = 0.0;
-          if (s > 0.0) code = std::min(7.0, std::max(-8.0, std::nearbyint(f16_to_f64(W[lin]) / s)));
-          q[static_cast<size_t>(idx)] = static_cast<int8_t>(code);
+          q[static_cast<size_t>(idx)] = i4_code(W[lin], rscale[lin / g.K]);
         }
         ++idx;
       });
@@ -276,16 +349,7 @@ usw_status usw_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t
   });
 
   uint8_t* vb = static_cast<uint8_t*>(values);
-  if (val_type == USW_VAL_I4) {
-    const int64_t nbytes = (nnz + 1) / 2;
-    parallel_for(nbytes, [&](int64_t lo, int64_t hi) {
-      for (int64_t i = lo; i < hi; ++i) {
-        const uint8_t a = static_cast<uint8_t>(q[2 * i]) & 0xF;
-        const uint8_t b = (2 * i + 1 < nnz) ? (static_cast<uint8_t>(q[2 * i + 1]) & 0xF) : 0;
-        vb[i] = static_cast<uint8_t>(a | (b << 4));
-      }
-    });
-  }
+  if (val_type == USW_VAL_I4) pack_i4(q, nnz, vb);
   if (values_capacity > logical) std::memset(vb + logical, 0, values_capacity - logical);
   return USW_OK;
 }
@@ -307,6 +371,105 @@ usw_status usw_validate(const usw_fmt* f) {
     int64_t c = 0;
     for (int64_t b = 0; b < g.bt_per_gt; ++b) c += __builtin_popcountll(f->bitmaps[gid * g.bt_per_gt + b]);
     if (c != static_cast<int64_t>(f->offsets[gid + 1] - f->offsets[gid])) return USW_ERR_CORRUPT;
+  }
+  return USW_OK;
+}
+
+usw_status usw_union_encode_query(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
+                                  int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type, int64_t* payload,
+                                  size_t* bytes_bitmaps, size_t* bytes_offsets, size_t* bytes_values,
+                                  size_t* bytes_values_alloc, size_t* bytes_scales) {
+  if (!W && !mask) return USW_ERR_NULL_ARG;
+  UnionGeometry g;
+  usw_status st = make_union_geometry(M, K, lt_m, lt_k, r_a, c_a, &g);
+  if (st) return st;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  std::vector<int64_t> off;
+  st = count_union(g, W, mask, &off);
+  if (st) return st;
+  const int64_t n = off[g.nlt];
+  if (payload) *payload = n;
+  if (bytes_bitmaps) *bytes_bitmaps = static_cast<size_t>(8 * g.nlt * g.nw);
+  if (bytes_offsets) *bytes_offsets = static_cast<size_t>(4 * (g.nlt + 1));
+  if (bytes_values) *bytes_values = values_logical_bytes(val_type, n);
+  if (bytes_values_alloc) *bytes_values_alloc = values_alloc_bytes(val_type, n);
+  if (bytes_scales) *bytes_scales = val_type == USW_VAL_I4 ? static_cast<size_t>(2 * M) : 0;
+  return USW_OK;
+}
+
+usw_status usw_union_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
+                            int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type, uint64_t* bitmaps,
+                            uint32_t* offsets, void* values, size_t values_capacity, uint16_t* scales) {
+  if (!W || !bitmaps || !offsets || !values) return USW_ERR_NULL_ARG;
+  UnionGeometry g;
+  usw_status st = make_union_geometry(M, K, lt_m, lt_k, r_a, c_a, &g);
+  if (st) return st;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (val_type == USW_VAL_I4 && !scales) return USW_ERR_NULL_ARG;
+  std::vector<int64_t> off;
+  st = count_union(g, W, mask, &off);
+  if (st) return st;
+  const int64_t total = off[g.nlt];
+  const size_t logical = values_logical_bytes(val_type, total);
+  if (values_capacity < logical) return USW_ERR_CAPACITY;
+  for (int64_t i = 0; i <= g.nlt; ++i) offsets[i] = static_cast<uint32_t>(off[i]);
+
+  std::vector<double> rscale;
+  if (val_type == USW_VAL_I4) rscale = row_scales(W, mask, M, K, scales);
+  std::vector<int8_t> q;
+  if (val_type == USW_VAL_I4) q.assign(static_cast<size_t>(total), 0);
+  uint16_t* v16 = static_cast<uint16_t*>(values);
+
+  // Per LT: the union words, then the Q area streams, each holding the area's
+  // weight (0 where pruned) at every active position in row-major order.
+  parallel_for(g.nlt, [&](int64_t lo, int64_t hi) {
+    std::vector<int64_t> active;
+    for (int64_t t = lo; t < hi; ++t) {
+      active.clear();
+      uint64_t* words = bitmaps + t * g.nw;
+      for (int64_t w = 0; w < g.nw; ++w) words[w] = 0;
+      for (int64_t p = 0; p < g.am * g.ak; ++p)
+        if (union_on(g, W, mask, t, p)) {
+          words[p >> 6] |= 1ull << (p & 63);
+          active.push_back(p);
+        }
+      const int64_t P = static_cast<int64_t>(active.size());
+      for (int64_t qa = 0; qa < g.Q; ++qa)
+        for (int64_t r = 0; r < P; ++r) {
+          const int64_t lin = union_elem(g, t, qa, active[static_cast<size_t>(r)]);
+          const int64_t idx = off[t] + qa * P + r;
+          const bool kept = is_kept(W, mask, lin);
+          if (val_type == USW_VAL_F16)
+            v16[idx] = kept ? W[lin] : uint16_t(0);
+          else
+            q[static_cast<size_t>(idx)] = kept ? i4_code(W[lin], rscale[lin / g.K]) : int8_t(0);
+        }
+    }
+  });
+
+  uint8_t* vb = static_cast<uint8_t*>(values);
+  if (val_type == USW_VAL_I4) pack_i4(q, total, vb);
+  if (values_capacity > logical) std::memset(vb + logical, 0, values_capacity - logical);
+  return USW_OK;
+}
+
+usw_status usw_union_validate(const usw_union_fmt* f) {
+  if (!f) return USW_ERR_NULL_ARG;
+  UnionGeometry g;
+  usw_status st = make_union_geometry(f->M, f->K, f->lt_m, f->lt_k, f->r_a, f->c_a, &g);
+  if (st) return st;
+  if (f->val_type != USW_VAL_F16 && f->val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (!f->bitmaps || !f->offsets) return USW_ERR_NULL_ARG;
+  if (f->payload > 0 && !f->values) return USW_ERR_NULL_ARG;
+  if (f->val_type == USW_VAL_I4 && !f->scales) return USW_ERR_NULL_ARG;
+  if (f->reserved != 0) return USW_ERR_BAD_SHAPE;
+  if (f->payload < 0 || f->payload >= (int64_t(1) << 32)) return USW_ERR_CORRUPT;
+  if (f->offsets[0] != 0 || static_cast<int64_t>(f->offsets[g.nlt]) != f->payload) return USW_ERR_CORRUPT;
+  for (int64_t t = 0; t < g.nlt; ++t) {
+    if (f->offsets[t + 1] < f->offsets[t]) return USW_ERR_CORRUPT;
+    int64_t c = 0;
+    for (int64_t w = 0; w < g.nw; ++w) c += __builtin_popcountll(f->bitmaps[t * g.nw + w]);
+    if (g.Q * c != static_cast<int64_t>(f->offsets[t + 1] - f->offsets[t])) return USW_ERR_CORRUPT;
   }
   return USW_OK;
 }

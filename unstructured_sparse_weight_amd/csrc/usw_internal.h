@@ -17,6 +17,19 @@ struct Geometry {
 };
 
 usw_status make_geometry(int64_t M, int64_t K, int64_t gt_m, int64_t gt_k, Geometry* g);
+
+// IE-BME: local tiles of lt_m x lt_k cut into r_a x c_a areas of am x ak.
+struct UnionGeometry {
+  int64_t M, K, lt_m, lt_k, r_a, c_a;
+  int64_t Q;          // areas per LT
+  int64_t am, ak;     // area shape = union-mask shape of an LT
+  int64_t lr, lc;     // LT rows and columns of the matrix
+  int64_t nlt;        // LTs
+  int64_t nw;         // union words per LT
+};
+
+usw_status make_union_geometry(int64_t M, int64_t K, int64_t lt_m, int64_t lt_k, int64_t r_a, int64_t c_a,
+                               UnionGeometry* g);
 size_t values_alloc_bytes(int32_t val_type, int64_t nnz);
 double f16_to_f64(uint16_t h);
 uint16_t f64_to_f16_rne(double x);

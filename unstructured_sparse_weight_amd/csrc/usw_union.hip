@@ -1,0 +1,393 @@
+// Device half of the IE-BME union-mask path: the INT4 decode kernel for
+// gfx950 and the usw_union_spmm dispatcher.
+//
+// What is computed: Y[n][m] = sum_k W_sp[m][k] X[n][k], W_sp held in the
+// IE-BME union-mask format ("UnionSparse: An Index-Efficient Sparsity
+// Framework for Low-Bit Sparse LLM Inference on Edge", section on IE-BME):
+// a 64 x 64 local tile (LT) is cut into a 2 x 2 grid of 32 x 32 areas, one
+// union bit covers the four area-aligned weights of a position, and the four
+// areas' values sit in four aligned streams indexed by one compact rank.
+//
+// Design (wave64, MFMA v_mfma_f32_16x16x32_f16):
+//   * One workgroup owns one 64-row strip of LTs and a range of LT columns;
+//     each of its four waves streams its own run of LTs, one LT ahead in
+//     registers (union words, the LT's payload chunks, X^T fragments), the
+//     current LT in the wave's LDS buffer.  No workgroup barrier in the loop.
+//   * Fragment (f, ks) of an LT (strip rows 16f..16f+15, LT columns
+//     32ks..32ks+31) lies in area (f / 2, ks), logical rows 16 (f % 2) ..
+//     +15.  Lane l (i = l % 16, g = l / 16) holds its row i, columns
+//     8g..8g+7, i.e. byte g of logical row r = 16 (f % 2) + i of the union
+//     mask.  The four fragments f % 2 = h, f / 2 and ks free, share that byte
+//     and its rank: the lane reads the row's word and the rank of its first
+//     bit once (a 32-entry LDS table per LT, written by lanes 0-31 with a
+//     DPP prefix scan), adds one masked popcount and looks up the v_perm
+//     selectors of the byte once, then gathers the row of each area from
+//     stream q at rank + q P_t: one bitmap traversal and one rank for Q
+//     payload rows, the point of the section's LSPD gather.
+//   * The INT4 window and fp16 conversion are those of the TCA-BME INT4
+//     kernel: an 8-nibble v_alignbit window, v_perm placement by the
+//     selectors (zero for clear bits), and the 0x6400 bias for exact fp16.
+//   * The per-row scale is applied in the split-K epilogue shared with the
+//     TCA-BME decode kernels.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "usw.h"
+#include "usw_internal.h"
+#include "usw_device.h"
+#include "usw_decode_common.h"
+
+namespace {
+
+using namespace usw_dev;
+
+constexpr int kLtWords = 16;                    // union words per 64x64 LT (32 x 32 bits)
+constexpr int kUChunks = 3;                     // 1 KB value chunks per LT: payload <= 2 KB plus head
+constexpr int kUVbuf = kUChunks * 1024 + 64;    // wave's LDS value buffer (+ what a window reads past it)
+constexpr int kURowTab = 32 * 8;                // per logical row: its bits and the rank of its first bit
+constexpr int kUWaves = 4;
+constexpr int kUThreads = 64 * kUWaves;
+static_assert(16 * 64 * kUChunks >= 4 * 1024 / 2 + 16, "every LT's payload fits a slot");
+
+// Registers holding one LT's loads until they are copied into LDS.
+template <int NB>
+struct USlot {
+  u32x4_t v[kUChunks];
+  uint32_t rowbits;    // lane t: union row t % 32
+  u32x4_t x[2][NB];
+  uint32_t delta;      // payload elements before the LT's first one in its first piece
+  uint32_t P;          // active union positions of the LT (wave-uniform)
+};
+
+// Issue the loads of LT column c of strip gi, whose payload occupies
+// elements [o0, o1) of the stream.
+template <int NB>
+__device__ __forceinline__ void uslot_load(USlot<NB>& s, const Args& a, int gi, int c, int lane, uint32_t o0,
+                                           uint32_t o1) {
+  const int64_t t = static_cast<int64_t>(gi) * a.Gc + c;
+  // Union words first: the LT's row table is written while its payload and
+  // X^T fragments may still be in flight.  Row r of the 32 x 32 mask is
+  // dword r of the LT's words (little-endian 64-bit words, rows of 32 bits).
+  s.rowbits = reinterpret_cast<const uint32_t*>(a.bitmaps + t * kLtWords)[lane & 31];
+  // An LT holds at most 1024 active positions; the clamp keeps every window
+  // inside the wave's LDS buffer even for offsets that disagree with the
+  // union words.
+  s.P = min((o1 - o0) >> 2, 1024u);
+  const uint64_t top = a.values_alloc - 16;
+  const uint64_t a0 = min(chunk_start<true>(o0), top);
+  s.delta = chunk_delta<true>(o0, a0);
+  const uint32_t nch = min(chunk_count<true>(o1, a0), static_cast<uint32_t>((kUVbuf - 16) / 16));
+  // Buffer resources that end after the LT's last piece: pieces past it read
+  // as zero, one vector offset (the lane's) for all chunks.
+  const uint32_t last = min(nch > 0 ? nch - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
+  const int span = static_cast<int>(16 * (last + 1));
+#pragma unroll
+  for (int i = 0; i < kUChunks; ++i) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values + a0 + 1024 * i), 0,
+                                                        max(span - 1024 * i, 0), kBufferRsrcWord3);
+    s.v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * lane, 0, 0));
+  }
+  // X^T fragments; tokens past N repeat N-1 (they only feed outputs that are
+  // never stored).
+  const int row = lane & 15, kb = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = min(nb * 16 + row, a.N - 1);
+      s.x[ks][nb] = *reinterpret_cast<const u32x4_t*>(a.X + static_cast<size_t>(n) * a.K + c * kGT + ks * 32 + kb * 8);
+    }
+}
+
+// The row table of an LT: entry r = {row r's bits, element position of the
+// row's first active value in the LDS buffer (area 0's stream)}.
+__device__ __forceinline__ void urow_tab_write(uint8_t* tab, uint32_t rowbits, uint32_t base, int lane) {
+  const uint32_t pc = lane < 32 ? __builtin_popcount(rowbits) : 0u;
+  const uint32_t excl = wave_inclusive_scan(pc) - pc;
+  if (lane < 32) {
+    u32x2_t e;
+    e.x = rowbits;
+    e.y = base + excl;
+    reinterpret_cast<u32x2_t*>(tab)[lane] = e;
+  }
+}
+
+// Rebuild the 8 fragments of an LT whose row table is at tab and whose
+// payload is in LDS, and multiply them with the X^T fragments.
+template <int NB>
+__device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const uint8_t* smem, const uint8_t* tab,
+                                               const uint32_t* lut, uint32_t P, f32x4_t (&acc)[4][NB], int lane) {
+  const int i = lane & 15;
+  const uint32_t sh = 8u * static_cast<uint32_t>(lane >> 4);
+  const uint32_t pmask = (1u << sh) - 1u;
+  u32x2_t e[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) e[h] = reinterpret_cast<const u32x2_t*>(tab)[16 * h + i];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t byte = __builtin_amdgcn_ubfe(e[h].x, sh, 8);
+    const uint32_t rb = e[h].y + __builtin_popcount(e[h].x & pmask);
+    const uint32_t pcl = __builtin_popcount(byte & 0xFu);
+    const uint32_t slo = lut[byte & 0xFu];
+    const uint32_t shi = lut[byte >> 4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t rq = rb + static_cast<uint32_t>(q) * P;
+      const u32x2_t lo = lds_window_i4(smem, rq);
+      const u32x2_t hi = lds_window_i4(smem, rq + pcl);
+      // Slots as bytes; xor 8 maps the nibble q to q + 8 (an empty slot's 0
+      // becomes 8, i.e. 0), then 0x6400 | u is fp16 1024 + u exactly.
+      const uint32_t e0 = __builtin_amdgcn_perm(lo.y, lo.x, slo) ^ 0x08080808u;
+      const uint32_t e1 = __builtin_amdgcn_perm(hi.y, hi.x, shi) ^ 0x08080808u;
+      u32x4_t w;
+      w.x = __builtin_amdgcn_perm(0x64646464u, e0, 0x04010400u);
+      w.y = __builtin_amdgcn_perm(0x64646464u, e0, 0x04030402u);
+      w.z = __builtin_amdgcn_perm(0x64646464u, e1, 0x04010400u);
+      w.w = __builtin_amdgcn_perm(0x64646464u, e1, 0x04030402u);
+      half8_t av = __builtin_bit_cast(half8_t, w);
+      av += static_cast<_Float16>(-1032.0f);
+      const int f = 2 * (q >> 1) + h;   // area row q / 2, logical row half h
+      const int ks = q & 1;             // area column
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[f][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, x[ks][nb]), acc[f][nb],
+                                                            0, 0, 0);
+    }
+  }
+}
+
+template <int NB, bool OUT_F16, int OCC>
+__global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) uint32_t lut[16];
+  constexpr int kStage = kUWaves * (kUVbuf + kURowTab);
+  constexpr int kRed = kUWaves * 4 * NB * 64 * 4 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStage > kRed ? kStage : kRed];
+  __shared__ uint32_t last_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nblk = static_cast<int>(gridDim.x);
+  const int b = static_cast<int>(blockIdx.x);
+  const int L = a.remap ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int gi = L / a.splits;
+  const int sidx = L - gi * a.splits;
+
+  if (tid < 16) lut[tid] = nibble_byte_selector(tid);
+  __syncthreads();
+
+  const int parts = a.splits * kUWaves;
+  const int qw = sidx * kUWaves + w;
+  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * qw / parts);
+  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (qw + 1) / parts);
+
+  f32x4_t acc[4][NB];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[f][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint8_t* vb = smem + w * kUVbuf;
+  uint8_t* tab = smem + kUWaves * kUVbuf + w * kURowTab;
+  // Windows address smem directly: the wave buffer's offset in payload
+  // elements (nibbles) is folded into the row bases.
+  const uint32_t vb_elems = static_cast<uint32_t>(w * kUVbuf * 2);
+
+  // The wave's LT offsets, lane i holding offsets[t_begin + i] (the host
+  // keeps the count <= 63).
+  const int cnt = c_end - c_begin;
+  const int64_t t_begin = static_cast<int64_t>(gi) * a.Gc + c_begin;
+  const uint32_t ov = a.offsets[t_begin + min(lane, max(cnt, 0))];
+  auto off_at = [&](int c) -> uint32_t { return __builtin_amdgcn_readlane(ov, min(c - c_begin, 63)); };
+
+  if (cnt > 0) {
+    // Two register slots: LT c is in LDS while c+1 loads.  Loads past the
+    // wave's last LT repeat it, so every step issues the same loads.
+    const int c_last = c_end - 1;
+    auto load = [&](USlot<NB>& sl, int c) {
+      const int cc = min(c, c_last);
+      uslot_load(sl, a, gi, cc, lane, off_at(cc), off_at(cc + 1));
+    };
+    auto commit = [&](const USlot<NB>& sl) {
+#pragma unroll
+      for (int i = 0; i < kUChunks; ++i) reinterpret_cast<u32x4_t*>(vb)[lane + 64 * i] = sl.v[i];
+    };
+    auto write_tab = [&](const USlot<NB>& sl) { urow_tab_write(tab, sl.rowbits, sl.delta + vb_elems, lane); };
+    USlot<NB> s[2];
+    load(s[0], c_begin);
+    write_tab(s[0]);
+    auto step = [&](USlot<NB>& cur, int c, USlot<NB>& nxt) {
+      load(nxt, c + 1);
+      commit(cur);
+      wave_sync();
+      union_tile_mma<NB>(cur.x, smem, tab, lut, cur.P, acc, lane);
+      wave_sync();
+      write_tab(nxt);
+    };
+    int c = c_begin;
+    for (; c + 2 <= c_end; c += 2) {
+      step(s[0], c, s[1]);
+      step(s[1], c + 1, s[0]);
+    }
+    if (c < c_end) step(s[0], c, s[1]);
+  }
+
+  // Workgroup reduction over waves (fixed order).
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb];
+  __syncthreads();
+
+  finish_strip<NB, true, OUT_F16>(a, gi, sidx, kUThreads, last_flag, [&](int n, int ml) {
+    // Strip rows ml .. ml+3 are D rows 4g .. 4g+3 (g = (ml / 4) % 4) of
+    // fragment ml / 16: registers 0-3 of lane 16 g + n % 16.
+    const int f = ml >> 4;
+    const int ln = 16 * ((ml >> 2) & 3) + (n & 15);
+    const int nb = n >> 4;
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < kUWaves; ++ww)
+      sum += *reinterpret_cast<const f32x4_t*>(red + (((ww * 4 + f) * NB + nb) * 64 + ln) * 4);
+    return sum;
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Host dispatch
+// ---------------------------------------------------------------------------
+
+// Waves per SIMD the register allocation allows: 5 up to 16 tokens, 3 for
+// 17..32 (twice the accumulators and X fragments).
+constexpr int kOcc1 = 5;
+constexpr int kOcc2 = 3;
+
+struct UPlan {
+  int splits;
+  int nchunk;   // tokens per pass (16 or 32)
+};
+
+UPlan union_plan(const usw::UnionGeometry& g, int N, int splits_req) {
+  UPlan p;
+  p.nchunk = N <= 16 ? 16 : 32;
+  const int occ = N <= 16 ? kOcc1 : kOcc2;
+  int64_t s = splits_req;
+  if (s <= 0) {
+    // About one round of resident workgroups, each wave keeping at least 3
+    // LTs to stream.
+    const int64_t target = 256 * 4 * occ / kUWaves;
+    s = std::max<int64_t>(1, (target + g.lr / 2) / g.lr);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, g.lc / (kUWaves * 3)));
+  }
+  const int64_t smax = std::max<int64_t>(1, g.lc / kUWaves);
+  const int64_t smin = (g.lc + 63 * kUWaves - 1) / (63 * kUWaves);
+  p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
+  return p;
+}
+
+size_t union_counter_bytes(const usw::UnionGeometry& g) { return (static_cast<size_t>(4 * g.lr) + 255) & ~size_t(255); }
+
+size_t union_workspace_bytes(const usw::UnionGeometry& g, const UPlan& p) {
+  if (p.splits <= 1) return 0;
+  return union_counter_bytes(g) + static_cast<size_t>(p.splits) * p.nchunk * g.M * sizeof(float);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+usw_status union_check(const usw_union_fmt* f, int32_t y_type, int32_t N, usw::UnionGeometry* g) {
+  if (!f) return USW_ERR_NULL_ARG;
+  usw_status st = usw::make_union_geometry(f->M, f->K, f->lt_m, f->lt_k, f->r_a, f->c_a, g);
+  if (st) return st;
+  if (f->val_type != USW_VAL_F16 && f->val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (y_type != USW_OUT_F16 && y_type != USW_OUT_F32) return USW_ERR_BAD_DTYPE;
+  if (f->reserved != 0) return USW_ERR_BAD_SHAPE;
+  if (N < 1) return USW_ERR_BAD_N;
+  if (f->val_type != USW_VAL_I4 || f->lt_m != 64 || f->lt_k != 64 || f->r_a != 2 || f->c_a != 2)
+    return USW_ERR_UNSUPPORTED;
+  if (f->payload < 0 || f->payload >= (int64_t(1) << 32)) return USW_ERR_BAD_SHAPE;
+  if (static_cast<int64_t>(N) * g->M > (int64_t(1) << 40)) return USW_ERR_BAD_SHAPE;
+  return USW_OK;
+}
+
+template <int NB>
+void union_launch(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
+  constexpr int occ = NB == 1 ? kOcc1 : kOcc2;
+  if (f16out)
+    union_decode_kernel<NB, true, occ><<<grid, kUThreads, 0, s>>>(a);
+  else
+    union_decode_kernel<NB, false, occ><<<grid, kUThreads, 0, s>>>(a);
+}
+
+}  // namespace
+
+extern "C" {
+
+usw_status usw_union_spmm_workspace(const usw_union_fmt* f, int32_t N, int32_t splits, size_t* bytes) {
+  if (!bytes) return USW_ERR_NULL_ARG;
+  usw::UnionGeometry g;
+  usw_status st = union_check(f, USW_OUT_F16, N, &g);
+  if (st) return st;
+  *bytes = union_workspace_bytes(g, union_plan(g, N, splits < 0 ? 0 : splits));
+  return USW_OK;
+}
+
+usw_status usw_union_spmm_counter_bytes(const usw_union_fmt* f, int32_t N, int32_t splits, size_t* bytes) {
+  if (!bytes) return USW_ERR_NULL_ARG;
+  usw::UnionGeometry g;
+  usw_status st = union_check(f, USW_OUT_F16, N, &g);
+  if (st) return st;
+  *bytes = union_plan(g, N, splits < 0 ? 0 : splits).splits > 1 ? union_counter_bytes(g) : 0;
+  return USW_OK;
+}
+
+usw_status usw_union_spmm(const usw_union_fmt* f, const uint16_t* X, void* Y, int32_t y_type, int32_t N,
+                          int32_t splits, void* ws, size_t ws_bytes, void* stream) {
+  usw::UnionGeometry g;
+  usw_status st = union_check(f, y_type, N, &g);
+  if (st) return st;
+  // The kernel reads whole 16-byte chunks of values even for an empty payload.
+  if (!X || !Y || !f->bitmaps || !f->offsets || !f->scales || !f->values) return USW_ERR_NULL_ARG;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(f->bitmaps) || !aligned16(f->values)) return USW_ERR_MISALIGNED;
+  const UPlan p = union_plan(g, N, splits < 0 ? 0 : splits);
+  const size_t need = union_workspace_bytes(g, p);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return USW_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nblk = g.lr * p.splits;
+  const dim3 grid(static_cast<unsigned>(nblk));
+  const size_t ybytes = y_type == USW_OUT_F16 ? 2 : 4;
+  const bool f16out = y_type == USW_OUT_F16;
+  for (int n0 = 0; n0 < N; n0 += p.nchunk) {
+    const int nc = std::min(p.nchunk, N - n0);
+    Args a;
+    a.bitmaps = f->bitmaps;
+    a.offsets = f->offsets;
+    a.values = static_cast<const uint8_t*>(f->values);
+    a.scales = f->scales;
+    a.X = X + static_cast<size_t>(n0) * g.K;
+    a.Y = static_cast<uint8_t*>(Y) + static_cast<size_t>(n0) * g.M * ybytes;
+    a.counters = need ? static_cast<uint32_t*>(ws) : nullptr;
+    a.part = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + union_counter_bytes(g)) : nullptr;
+    a.values_alloc = usw::values_alloc_bytes(USW_VAL_I4, f->payload);
+    a.M = static_cast<int>(g.M);
+    a.K = static_cast<int>(g.K);
+    a.N = nc;
+    a.Gc = static_cast<int>(g.lc);
+    a.splits = p.splits;
+    a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
+    if (nc > 16)
+      union_launch<2>(a, f16out, grid, s);
+    else
+      union_launch<1>(a, f16out, grid, s);
+    if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
+  }
+  return USW_OK;
+}
+
+}  // extern "C"
