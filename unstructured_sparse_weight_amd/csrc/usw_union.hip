@@ -21,12 +21,14 @@
 //     and its rank: the lane reads the row's word and the rank of its first
 //     bit once (a 32-entry LDS table per LT, written by lanes 0-31 with a
 //     DPP prefix scan), adds one masked popcount and looks up the v_perm
-//     selectors of the byte once, then gathers the row of each area from
-//     stream q at rank + q P_t: one bitmap traversal and one rank for Q
+//     selectors of the whole byte once, then gathers the row of each area
+//     from stream q at rank + q P_t: one bitmap traversal and one rank for Q
 //     payload rows, the point of the section's LSPD gather.
-//   * The INT4 window and fp16 conversion are those of the TCA-BME INT4
-//     kernel: an 8-nibble v_alignbit window, v_perm placement by the
-//     selectors (zero for clear bits), and the 0x6400 bias for exact fp16.
+//   * A row's at most 8 values are the 8 nibbles from its rank on, so one
+//     v_alignbit window per area row holds them all; the 256-entry selector
+//     table (8 bytes per mask byte) places nibble k of the window into the
+//     slot of the k-th set bit (zero for clear bits), and the 0x6400 bias
+//     turns each slot into exact fp16.
 //   * The per-row scale is applied in the split-K epilogue shared with the
 //     TCA-BME decode kernels.
 
@@ -51,6 +53,7 @@ constexpr int kURowTab = 32 * 8;                // per logical row: its bits and
 constexpr int kUWaves = 4;
 constexpr int kUThreads = 64 * kUWaves;
 static_assert(16 * 64 * kUChunks >= 4 * 1024 / 2 + 16, "every LT's payload fits a slot");
+static_assert(kUThreads == 256, "one thread per entry of the selector table");
 
 // Registers holding one LT's loads until they are copied into LDS.
 template <int NB>
@@ -81,9 +84,11 @@ __device__ __forceinline__ void uslot_load(USlot<NB>& s, const Args& a, int gi, 
   s.delta = chunk_delta<true>(o0, a0);
   const uint32_t nch = min(chunk_count<true>(o1, a0), static_cast<uint32_t>((kUVbuf - 16) / 16));
   // Buffer resources that end after the LT's last piece: pieces past it read
-  // as zero, one vector offset (the lane's) for all chunks.
+  // as zero, one vector offset (the lane's) for all chunks.  The size is
+  // wave-uniform; saying so keeps the compiler from wrapping each load in a
+  // loop over distinct descriptors.
   const uint32_t last = min(nch > 0 ? nch - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
-  const int span = static_cast<int>(16 * (last + 1));
+  const int span = __builtin_amdgcn_readfirstlane(static_cast<int>(16 * (last + 1)));
 #pragma unroll
   for (int i = 0; i < kUChunks; ++i) {
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values + a0 + 1024 * i), 0,
@@ -119,7 +124,7 @@ __device__ __forceinline__ void urow_tab_write(uint8_t* tab, uint32_t rowbits, u
 // payload is in LDS, and multiply them with the X^T fragments.
 template <int NB>
 __device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const uint8_t* smem, const uint8_t* tab,
-                                               const uint32_t* lut, uint32_t P, f32x4_t (&acc)[4][NB], int lane) {
+                                               const u32x2_t* lut, uint32_t P, f32x4_t (&acc)[4][NB], int lane) {
   const int i = lane & 15;
   const uint32_t sh = 8u * static_cast<uint32_t>(lane >> 4);
   const uint32_t pmask = (1u << sh) - 1u;
@@ -130,18 +135,14 @@ __device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const 
   for (int h = 0; h < 2; ++h) {
     const uint32_t byte = __builtin_amdgcn_ubfe(e[h].x, sh, 8);
     const uint32_t rb = e[h].y + __builtin_popcount(e[h].x & pmask);
-    const uint32_t pcl = __builtin_popcount(byte & 0xFu);
-    const uint32_t slo = lut[byte & 0xFu];
-    const uint32_t shi = lut[byte >> 4];
+    const u32x2_t sel = lut[byte];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t rq = rb + static_cast<uint32_t>(q) * P;
-      const u32x2_t lo = lds_window_i4(smem, rq);
-      const u32x2_t hi = lds_window_i4(smem, rq + pcl);
+      const u32x2_t w8 = lds_window_i4(smem, rb + static_cast<uint32_t>(q) * P);
       // Slots as bytes; xor 8 maps the nibble q to q + 8 (an empty slot's 0
       // becomes 8, i.e. 0), then 0x6400 | u is fp16 1024 + u exactly.
-      const uint32_t e0 = __builtin_amdgcn_perm(lo.y, lo.x, slo) ^ 0x08080808u;
-      const uint32_t e1 = __builtin_amdgcn_perm(hi.y, hi.x, shi) ^ 0x08080808u;
+      const uint32_t e0 = __builtin_amdgcn_perm(w8.y, w8.x, sel.x) ^ 0x08080808u;
+      const uint32_t e1 = __builtin_amdgcn_perm(w8.y, w8.x, sel.y) ^ 0x08080808u;
       u32x4_t w;
       w.x = __builtin_amdgcn_perm(0x64646464u, e0, 0x04010400u);
       w.y = __builtin_amdgcn_perm(0x64646464u, e0, 0x04030402u);
@@ -159,9 +160,30 @@ __device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const 
   }
 }
 
+// v_perm selectors that expand the 8 packed nibbles of a window into the 8
+// slots of a row with mask byte b: slot p takes nibble k = (set bits of b
+// below p) when bit p is set, else zero.  Nibble k sits in byte k/2 of lo4
+// (k even) or of hi4 (k odd), lo4 = w & 0x0F0F0F0F, hi4 = (w >> 4) &
+// 0x0F0F0F0F; v_perm(hi4, lo4, sel) numbers lo4's bytes 0-3 and hi4's 4-7.
+__device__ __forceinline__ u32x2_t row_byte_selectors(uint32_t b) {
+  u32x2_t sel = {0u, 0u};
+  for (int p = 0; p < 8; ++p) {
+    uint32_t v = 0x0Cu;
+    if ((b >> p) & 1u) {
+      const uint32_t k = __builtin_popcount(b & ((1u << p) - 1u));
+      v = (k & 1u) ? 4u + (k >> 1) : (k >> 1);
+    }
+    if (p < 4)
+      sel.x |= v << (8 * p);
+    else
+      sel.y |= v << (8 * (p - 4));
+  }
+  return sel;
+}
+
 template <int NB, bool OUT_F16, int OCC>
 __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) uint32_t lut[16];
+  __shared__ __attribute__((aligned(16))) u32x2_t lut[256];
   constexpr int kStage = kUWaves * (kUVbuf + kURowTab);
   constexpr int kRed = kUWaves * 4 * NB * 64 * 4 * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStage > kRed ? kStage : kRed];
@@ -176,7 +198,7 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
   const int gi = L / a.splits;
   const int sidx = L - gi * a.splits;
 
-  if (tid < 16) lut[tid] = nibble_byte_selector(tid);
+  lut[tid] = row_byte_selectors(static_cast<uint32_t>(tid));
   __syncthreads();
 
   const int parts = a.splits * kUWaves;
