@@ -152,20 +152,25 @@ __device__ __forceinline__ uint32_t nibble_selector(uint32_t q, int j) {
   return sel;
 }
 
-// v_perm selectors that expand the packed nibbles of one 4-bit nibble of a
-// BitmapTile row into 4 byte slots.  Packed nibble k of an 8-nibble window w
-// sits in byte k/2 of lo4 (k even) or of hi4 (k odd), lo4 = w & 0x0F0F0F0F and
+// v_perm selectors that expand the packed nibbles of an 8-nibble window into
+// the 8 slots of a BitmapTile row with mask byte b: slot p takes nibble
+// k = (set bits of b below p) when bit p is set, else zero.  Nibble k sits in
+// byte k/2 of lo4 (k even) or of hi4 (k odd), lo4 = w & 0x0F0F0F0F and
 // hi4 = (w >> 4) & 0x0F0F0F0F, and v_perm(hi4, lo4, sel) numbers lo4's bytes
-// 0-3 and hi4's bytes 4-7.
-__device__ __forceinline__ uint32_t nibble_byte_selector(uint32_t q) {
-  uint32_t sel = 0;
-  for (int p = 0; p < 4; ++p) {
+// 0-3 and hi4's bytes 4-7.  .x serves slots 0-3, .y slots 4-7; a table of
+// all 256 mask bytes lives in LDS.
+__device__ __forceinline__ u32x2_t row_byte_selectors(uint32_t b) {
+  u32x2_t sel = {0u, 0u};
+  for (int p = 0; p < 8; ++p) {
     uint32_t v = 0x0Cu;
-    if ((q >> p) & 1u) {
-      const uint32_t k = __builtin_popcount(q & ((1u << p) - 1u));
+    if ((b >> p) & 1u) {
+      const uint32_t k = __builtin_popcount(b & ((1u << p) - 1u));
       v = (k & 1u) ? 4u + (k >> 1) : (k >> 1);
     }
-    sel |= v << (8 * p);
+    if (p < 4)
+      sel.x |= v << (8 * p);
+    else
+      sel.y |= v << (8 * (p - 4));
   }
   return sel;
 }
@@ -196,14 +201,38 @@ __device__ __forceinline__ u32x2_t lds_window_i4(const uint8_t* buf, uint32_t e)
   return r;
 }
 
+// The 8 fp16 slots of an INT4 row from its 8-nibble window (split into
+// lo4 / hi4 by lds_window_i4) and its selectors.
+__device__ __forceinline__ half8_t expand_row_i4(u32x2_t w8, u32x2_t sel) {
+  // Slots as bytes; xor 8 maps the two's-complement nibble q to q + 8 in
+  // [0, 15] (an empty slot's 0 becomes 8, i.e. q = 0).
+  const uint32_t e0 = __builtin_amdgcn_perm(w8.y, w8.x, sel.x) ^ 0x08080808u;
+  const uint32_t e1 = __builtin_amdgcn_perm(w8.y, w8.x, sel.y) ^ 0x08080808u;
+  // fp16 bit pattern 0x6400 | u is 1024 + u exactly; subtracting 1032
+  // leaves q exactly.
+  u32x4_t a;
+  a.x = __builtin_amdgcn_perm(0x64646464u, e0, 0x04010400u);
+  a.y = __builtin_amdgcn_perm(0x64646464u, e0, 0x04030402u);
+  a.z = __builtin_amdgcn_perm(0x64646464u, e1, 0x04010400u);
+  a.w = __builtin_amdgcn_perm(0x64646464u, e1, 0x04030402u);
+  half8_t h = __builtin_bit_cast(half8_t, a);
+  h += static_cast<_Float16>(-1032.0f);
+  return h;
+}
+
 // The 8 dense fp16 slots (one BitmapTile row) of a lane's A fragment: the
 // row's kept values start at element rb of the LDS buffer; `byte` is the
-// row's mask.  Slots 0-3 come from a window at rb, slots 4-7 from a window
-// at rb + popcount(low nibble).
+// row's mask.
+//  * fp16: slots 0-3 come from a window at rb, slots 4-7 from a window at
+//    rb + popcount(low nibble), with selectors from a 16-entry table (two
+//    dwords per nibble) indexed by each half of the mask.
+//  * INT4: a row's at most 8 values are the 8 nibbles from rb on, so one
+//    window holds them all; selectors from the 256-entry table of
+//    row_byte_selectors indexed by the whole mask.
 template <bool I4>
 __device__ __forceinline__ half8_t rebuild_row(const uint8_t* vb, const uint32_t* lut, uint32_t rb, uint32_t byte) {
-  const uint32_t pcl = __builtin_popcount(byte & 0xFu);
   if constexpr (!I4) {
+    const uint32_t pcl = __builtin_popcount(byte & 0xFu);
     const u32x2_t slo = reinterpret_cast<const u32x2_t*>(lut)[byte & 0xFu];
     const u32x2_t shi = reinterpret_cast<const u32x2_t*>(lut)[byte >> 4];
     const u32x2_t lo = lds_window_f16(vb, rb);
@@ -215,27 +244,9 @@ __device__ __forceinline__ half8_t rebuild_row(const uint8_t* vb, const uint32_t
     a.w = __builtin_amdgcn_perm(hi.y, hi.x, shi.y);
     return __builtin_bit_cast(half8_t, a);
   } else {
-    const uint32_t slo = lut[byte & 0xFu];
-    const uint32_t shi = lut[byte >> 4];
-    const u32x2_t lo = lds_window_i4(vb, rb);
-    const u32x2_t hi = lds_window_i4(vb, rb + pcl);
-    // Slots as bytes; xor 8 maps the two's-complement nibble q to q + 8 in
-    // [0, 15] (an empty slot's 0 becomes 8, i.e. q = 0).
-    const uint32_t e0 = __builtin_amdgcn_perm(lo.y, lo.x, slo) ^ 0x08080808u;
-    const uint32_t e1 = __builtin_amdgcn_perm(hi.y, hi.x, shi) ^ 0x08080808u;
-    // fp16 bit pattern 0x6400 | u is 1024 + u exactly; subtracting 1032
-    // leaves q exactly.
-    u32x4_t a;
-    a.x = __builtin_amdgcn_perm(0x64646464u, e0, 0x04010400u);
-    a.y = __builtin_amdgcn_perm(0x64646464u, e0, 0x04030402u);
-    a.z = __builtin_amdgcn_perm(0x64646464u, e1, 0x04010400u);
-    a.w = __builtin_amdgcn_perm(0x64646464u, e1, 0x04030402u);
-    half8_t h = __builtin_bit_cast(half8_t, a);
-    h += static_cast<_Float16>(-1032.0f);
-    return h;
+    return expand_row_i4(lds_window_i4(vb, rb), reinterpret_cast<const u32x2_t*>(lut)[byte]);
   }
 }
-
 
 // Byte offset of the 16-byte chunk holding value element e (fp16: 2 B per
 // element; INT4: 4 bits per element).

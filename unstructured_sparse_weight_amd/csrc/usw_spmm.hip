@@ -229,7 +229,9 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   constexpr int kW = C::kWavesPerGroup;
   constexpr int kThreads = C::kThreadsPerGroup;
   constexpr int kD = C::kDepth;
-  __shared__ __attribute__((aligned(16))) uint32_t lut[I4 ? 16 : 32];
+  // Row selectors: fp16 16 nibble entries of two dwords, INT4 256 byte
+  // entries of two dwords.
+  __shared__ __attribute__((aligned(16))) uint32_t lut[I4 ? 512 : 32];
   // Staging (per wave: values, then the bitmap table); reused for the final
   // reduction.
   constexpr int kStage = kW * (VT::kVbuf + kTabBytes);
@@ -256,9 +258,10 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
       e.x = nibble_selector(tid, 0);
       e.y = nibble_selector(tid, 1);
       reinterpret_cast<u32x2_t*>(lut)[tid] = e;
-    } else {
-      lut[tid] = nibble_byte_selector(tid);
     }
+  }
+  if constexpr (I4) {
+    for (int i = tid; i < 256; i += kThreads) reinterpret_cast<u32x2_t*>(lut)[i] = row_byte_selectors(i);
   }
   __syncthreads();
 

@@ -138,18 +138,7 @@ __device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const 
     const u32x2_t sel = lut[byte];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const u32x2_t w8 = lds_window_i4(smem, rb + static_cast<uint32_t>(q) * P);
-      // Slots as bytes; xor 8 maps the nibble q to q + 8 (an empty slot's 0
-      // becomes 8, i.e. 0), then 0x6400 | u is fp16 1024 + u exactly.
-      const uint32_t e0 = __builtin_amdgcn_perm(w8.y, w8.x, sel.x) ^ 0x08080808u;
-      const uint32_t e1 = __builtin_amdgcn_perm(w8.y, w8.x, sel.y) ^ 0x08080808u;
-      u32x4_t w;
-      w.x = __builtin_amdgcn_perm(0x64646464u, e0, 0x04010400u);
-      w.y = __builtin_amdgcn_perm(0x64646464u, e0, 0x04030402u);
-      w.z = __builtin_amdgcn_perm(0x64646464u, e1, 0x04010400u);
-      w.w = __builtin_amdgcn_perm(0x64646464u, e1, 0x04030402u);
-      half8_t av = __builtin_bit_cast(half8_t, w);
-      av += static_cast<_Float16>(-1032.0f);
+      const half8_t av = expand_row_i4(lds_window_i4(smem, rb + static_cast<uint32_t>(q) * P), sel);
       const int f = 2 * (q >> 1) + h;   // area row q / 2, logical row half h
       const int ks = q & 1;             // area column
 #pragma unroll
@@ -158,27 +147,6 @@ __device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const 
                                                             0, 0, 0);
     }
   }
-}
-
-// v_perm selectors that expand the 8 packed nibbles of a window into the 8
-// slots of a row with mask byte b: slot p takes nibble k = (set bits of b
-// below p) when bit p is set, else zero.  Nibble k sits in byte k/2 of lo4
-// (k even) or of hi4 (k odd), lo4 = w & 0x0F0F0F0F, hi4 = (w >> 4) &
-// 0x0F0F0F0F; v_perm(hi4, lo4, sel) numbers lo4's bytes 0-3 and hi4's 4-7.
-__device__ __forceinline__ u32x2_t row_byte_selectors(uint32_t b) {
-  u32x2_t sel = {0u, 0u};
-  for (int p = 0; p < 8; ++p) {
-    uint32_t v = 0x0Cu;
-    if ((b >> p) & 1u) {
-      const uint32_t k = __builtin_popcount(b & ((1u << p) - 1u));
-      v = (k & 1u) ? 4u + (k >> 1) : (k >> 1);
-    }
-    if (p < 4)
-      sel.x |= v << (8 * p);
-    else
-      sel.y |= v << (8 * (p - 4));
-  }
-  return sel;
 }
 
 template <int NB, bool OUT_F16, int OCC>
