@@ -55,9 +55,12 @@ def parse():
     p.add_argument("--N", type=int, default=16)
     p.add_argument("--sparsity", type=float, default=0.5)
     p.add_argument("--dtype", default="f16", choices=["f16", "i4"])
-    p.add_argument("--format", default="tca", choices=["tca", "union"],
+    p.add_argument("--format", default="tca", choices=["tca", "union", "cbc"],
                    help="tca: TCA-BME bitmaps (usw_spmm); union: IE-BME union-mask INT4 with 64x64 tiles and 2x2"
-                        " areas (usw_union_spmm; implies --dtype i4)")
+                        " areas (usw_union_spmm; implies --dtype i4); cbc: Tiled-CBC spMspV with dynamic pruning"
+                        " (usw_cbc_spmspv; implies --N 1 and fp16)")
+    p.add_argument("--dp", type=float, default=0.5,
+                   help="cbc: fraction of activations below the pruning threshold (tau is that quantile of |x|)")
     p.add_argument("--cpu-reps", type=int, default=5)
     p.add_argument("--rotation", type=int, default=0,
                    help="number of encoded copies the steps rotate over (default: enough for > 512 MB, so reads come"
@@ -78,6 +81,7 @@ KERNEL_SOURCES = {
                "unstructured_sparse_weight_amd/csrc/usw_device.h"],
     "union": ["unstructured_sparse_weight_amd/csrc/usw_union.hip", "unstructured_sparse_weight_amd/csrc/usw_decode_common.h",
               "unstructured_sparse_weight_amd/csrc/usw_device.h"],
+    "cbc": ["unstructured_sparse_weight_amd/csrc/usw_cbc.hip", "unstructured_sparse_weight_amd/csrc/usw_device.h"],
     "prefill": ["unstructured_sparse_weight_amd/csrc/usw_prefill.hip", "unstructured_sparse_weight_amd/csrc/usw_device.h"],
 }
 
@@ -156,8 +160,11 @@ def main():
         return
     dev = torch.device("cuda:0")
     union = args.format == "union"
+    cbc = args.format == "cbc"
     if union:
         args.dtype = "i4"
+    if cbc:
+        args.dtype, args.N = "f16", 1
     M, K, N, s = args.M, args.K, args.N, args.sparsity
     # Kernel family as usw_spmm picks it: fp16 with more than 96 tokens runs
     # the prefill kernels, everything else the decode kernels (in passes of
@@ -170,7 +177,21 @@ def main():
     log(f"[bench] generating W {M}x{K} (magnitude pruning s={s}) and X [{N}][{K}]")
     W, mask, X = wl.config_case(cfg_id, M, K, N, s, layer_id=layer_id)
     t = time.time()
-    if union:
+    tau = 0.0
+    if cbc:
+        h = usw.cbc_encode_host(W, mask)
+        xa = np.abs(X[0].astype(np.float32))
+        tau = float(np.quantile(xa, args.dp)) if args.dp > 0 else 0.0
+        active = xa >= np.float32(tau)
+        log(f"[bench] host Tiled-CBC encode {time.time() - t:.2f} s, nnz={h.nnz} padded={h.nnz_padded};"
+            f" tau={tau:.4f} keeps {int(active.sum())} of {K} columns")
+        # Per GTile: tile offset and 16 ColInfo words; per active column:
+        # its 4 bitmap words and its padded run; x and y once.
+        runs = ((h.colinfo & 0xFFFF).astype(np.int64) + 7) // 8 * 8
+        act_cols = np.tile(active.reshape(-1, 16), (M // 256, 1)).reshape(-1)
+        alg = (h.tile_offsets.nbytes + h.colinfo.nbytes + 2 * K + 2 * M
+               + int((32 + 2 * runs[act_cols]).sum()))
+    elif union:
         h = usw.union_encode_host(W, mask, (64, 64), (2, 2), "i4")
         kept = int(mask.sum())
         log(f"[bench] host union encode {time.time() - t:.2f} s, payload={h.payload} for nnz={kept}"
@@ -183,16 +204,18 @@ def main():
         ngt = (M // 64) * (K // 64)
         vbytes = 2.0 if args.dtype == "f16" else 0.5
         alg = algorithmic_bytes(M, K, N, h.nnz, ngt, vbytes, 2, args.dtype == "i4")
-    enc_bytes = h.bitmaps.nbytes + h.offsets.nbytes + h.values.nbytes
+    enc_bytes = h.bitmaps.nbytes + (h.tile_offsets.nbytes + h.colinfo.nbytes if cbc else h.offsets.nbytes) + h.values.nbytes
     R = args.rotation if args.rotation > 0 else max(5, math.ceil(600e6 / enc_bytes))
-    to_dev = usw.union_to_device if union else usw.to_device
+    to_dev = usw.cbc_to_device if cbc else (usw.union_to_device if union else usw.to_device)
     encs = [to_dev(h, dev) for _ in range(R)]
     xs = [torch.from_numpy(X).to(dev) for _ in range(R)]
     ys = [torch.empty((N, M), dtype=torch.float16, device=dev) for _ in range(R)]
 
     L = usw.lib()
     fmts = [e.fmt() for e in encs]
-    if union:
+    if cbc:
+        wsb = usw.cbc_workspace_bytes(encs[0], args.splits)[0]
+    elif union:
         wsb = usw.union_workspace_bytes(encs[0], N, args.splits)[0]
     else:
         wsb = usw.spmm_workspace_bytes(encs[0], N, args.splits)
@@ -202,7 +225,10 @@ def main():
 
     def step(i, on=sp):
         j = i % R
-        if union:
+        if cbc:
+            st = L.usw_cbc_spmspv(ctypes.byref(fmts[j]), xs[j].data_ptr(), ys[j].data_ptr(), 1, tau, args.splits,
+                                  ws.data_ptr(), wsb, on)
+        elif union:
             st = L.usw_union_spmm(ctypes.byref(fmts[j]), xs[j].data_ptr(), ys[j].data_ptr(), 1, N, args.splits,
                                   ws.data_ptr(), wsb, on)
         else:
@@ -313,9 +339,11 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(W, mask, X, M, K, N, args.dtype, args.cpu_reps, union)
+        cpu = cpu_baseline(W, mask, X, M, K, N, args.dtype, args.cpu_reps, union, cbc, tau)
 
-    if union:
+    if cbc:
+        kname = "cbc_spmspv_kernel"
+    elif union:
         kname = "union_decode_kernel"
     elif prefill:
         kname = "prefill_ws_kernel" if N > 256 else "prefill_kernel"
@@ -347,8 +375,9 @@ def main():
     else:
         workload = f"spmm_{M}x{K}_s{s}_N{N}"
     if args.splits == 0:
-        roofline["traffic"] = measured_traffic(f"{kname}_{workload}",
-                                               "union" if union else ("prefill" if prefill else "decode"))
+        roofline["traffic"] = measured_traffic(f"{kname}_{workload}" + (f"_dp{args.dp}" if cbc else ""),
+                                               "cbc" if cbc else ("union" if union else
+                                                                  ("prefill" if prefill else "decode")))
     roofline["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     out = {
         "metric": METRIC if (M, K, N, s, args.dtype) == (20480, 5120, 16, 0.5, "f16") else
@@ -364,7 +393,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f16" if args.dtype == "f16" else "i4",
         "data": "synthetic (seeded N(0,0.02) weights, magnitude pruning, N(0,1) activations)",
-        "config": {"workload": workload, "format": "ie_bme_union_2x2" if union else "tca_bme",
+        "config": {"workload": workload,
+                   "format": "tiled_cbc_spmspv" if cbc else ("ie_bme_union_2x2" if union else "tca_bme"),
                    "M": M, "K": K, "N": N, "sparsity": s, "values": args.dtype, "groupTile": "64x64",
                    "rotation_copies": R, "splits": args.splits or "auto",
                    "launch": "eager" if args.eager else "hip_graph"},
@@ -377,15 +407,22 @@ def main():
     }
     if union:
         out["union_payload"] = int(h.payload)
+    if cbc:
+        out["config"]["dynamic_sparsity"] = args.dp
+        out["config"]["tau"] = tau
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(W, mask, X, M, K, N, dtype, reps, union=False):
+def cpu_baseline(W, mask, X, M, K, N, dtype, reps, union=False, cbc=False, tau=0.0):
     """The oracle as it stands (decode + fp64 product) on the host cores."""
     import oracle.tca_bme as ob
     import oracle.ie_bme as ou
+    import oracle.tiled_cbc as oc
     t = time.perf_counter()
-    if union:
+    if cbc:
+        enc = oc.encode_cbc(W, mask)
+        product = lambda e, Xm: oc.spmspv(e, Xm[0], tau)  # noqa: E731
+    elif union:
         enc = ou.encode_union(W, mask, 64, 64, 2, 2, ob.VAL_I4)
         product = ou.spmm_union
     else:

@@ -303,6 +303,94 @@ usw_status usw_union_spmm(const usw_union_fmt* fmt, const uint16_t* X, void* Y, 
                           int32_t splits, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ---------------------------------------------------------------------------
+ * Tiled-CBC and the dynamically pruned spMspV ("Unified Static-Dynamic
+ * Pruning for Efficient LLM Inference", section 4.1 Tiled-CBC and section
+ * 4.2 decode phase).
+ *
+ *   - GTile: 256 x 16 weights; GTiles of the matrix stored row-major.  A
+ *     GTile is 16 column tiles of 256 x 1.
+ *   - bitmaps[NGT * 16 * 4]: per column tile, 4 uint64 words; bit i of word
+ *     j <-> row 64 j + i of the column, least significant bit first.
+ *   - values: fp16 bits of the kept weights column by column (rows top to
+ *     bottom), each column's run padded with +0.0 to a multiple of 8 values
+ *     (16 bytes).
+ *   - tile_offsets[NGT+1]: uint32 index of each GTile's first value
+ *     (tile_offsets[NGT] = nnz_padded); colinfo[NGT * 16]: per column, its
+ *     run's offset inside the GTile (upper 16 bits) and its kept count
+ *     (lower 16 bits).
+ *   Storage 4 (NGT+1) + 4 NGT 16 + 8 NBM + 2 nnz_padded bytes (the section's
+ *   equation, NNZ counting the padded runs).
+ * Dynamic pruning: column k takes part when |x_k| >= tau, compared in fp32;
+ * the product is y = sum over those k of W_sp[:, k] x_k, fp32 accumulation.
+ * ---------------------------------------------------------------------------
+ */
+
+/* Non-owning view of one Tiled-CBC encoding (device pointers for
+ * usw_cbc_spmspv, host pointers for usw_cbc_validate). */
+typedef struct usw_cbc_fmt {
+  int32_t M, K;                 /* W is M x K, multiples of 256 and 16 */
+  int32_t tile_m, tile_k;       /* 256, 16 */
+  int32_t val_type;             /* USW_VAL_F16 */
+  int32_t reserved;             /* must be 0 */
+  int64_t nnz_padded;           /* stored values = tile_offsets[NGT] */
+  const uint64_t* bitmaps;      /* [NGT * 64] */
+  const uint32_t* tile_offsets; /* [NGT+1] */
+  const uint32_t* colinfo;      /* [NGT * 16] */
+  const uint16_t* values;       /* [nnz_padded] fp16 bits, 16-byte aligned */
+} usw_cbc_fmt;
+
+/*
+ * Sizes of a Tiled-CBC encoding from the mask alone (host memory); W and
+ * mask as usw_encode_query.  Outputs (each may be NULL): kept count, padded
+ * count, byte sizes of bitmaps, tile_offsets, colinfo and values.
+ * Errors: NULL_ARG, BAD_SHAPE (M not a multiple of 256 or K of 16),
+ * CAPACITY (padded count >= 2^32).
+ */
+usw_status usw_cbc_encode_query(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int64_t* nnz,
+                                int64_t* nnz_padded, size_t* bytes_bitmaps, size_t* bytes_tile_offsets,
+                                size_t* bytes_colinfo, size_t* bytes_values);
+
+/*
+ * Encode W (host memory) into caller-allocated host buffers following the
+ * Tiled-CBC construction above; values_capacity must be at least the values
+ * size usw_cbc_encode_query reports.  Deterministic.
+ * Errors: NULL_ARG, BAD_SHAPE, CAPACITY.
+ */
+usw_status usw_cbc_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, uint64_t* bitmaps,
+                          uint32_t* tile_offsets, uint32_t* colinfo, uint16_t* values, size_t values_capacity);
+
+/*
+ * Check a host copy of a Tiled-CBC encoding: shape fields, tile offsets
+ * framing the values, and every ColInfo entry agreeing with its column's
+ * bitmap words and with the padded runs before it.
+ * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, CORRUPT.
+ */
+usw_status usw_cbc_validate(const usw_cbc_fmt* host_fmt);
+
+/*
+ * Workspace bytes and leading counter bytes of usw_cbc_spmspv for this
+ * matrix and split factor (splits = 0: automatic; otherwise clamped to
+ * [1, K / 16]).  The counter bytes must be zero when a call starts; each
+ * call leaves them zero.  Errors: as usw_cbc_spmspv's checks.
+ */
+usw_status usw_cbc_spmspv_workspace(const usw_cbc_fmt* fmt, int32_t splits, size_t* bytes, size_t* counter_bytes);
+
+/*
+ * y = W_sp x with dynamic pruning on the GPU (N = 1, the section's
+ * spMspV): columns with |x_k| < tau are skipped, their bitmaps and values
+ * are not read.  x: device fp16 bits [K], y: device [M] fp16 (y_type
+ * USW_OUT_F16, rounded to nearest even from fp32) or fp32, both 16-byte
+ * aligned; tau >= 0 (tau = 0 keeps every column).  fp32 accumulation;
+ * deterministic (split partial sums added in split order).
+ * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED (tile shape other than
+ * 256 x 16, values other than fp16, tau negative or NaN), MISALIGNED,
+ * WORKSPACE, HIP.
+ */
+usw_status usw_cbc_spmspv(const usw_cbc_fmt* fmt, const uint16_t* x, void* y, int32_t y_type, float tau,
+                          int32_t splits, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Measurement utility, not part of the SpMM path: reads the first
  * bytes / 16 * 16 bytes of the device buffer buf once (16-byte loads,
  * non-temporal) on the stream, so that a caller can time the GPU's

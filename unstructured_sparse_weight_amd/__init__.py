@@ -19,13 +19,14 @@ from typing import Optional
 
 import numpy as np
 
-from ._lib import (USW_OUT_F16, USW_OUT_F32, USW_VAL_F16, USW_VAL_I4, EXPORTED, UswError, UswFmt,  # noqa: F401
-                   UswUnionFmt, check, lib)
+from ._lib import (USW_OUT_F16, USW_OUT_F32, USW_VAL_F16, USW_VAL_I4, EXPORTED, UswCbcFmt, UswError,  # noqa: F401
+                   UswFmt, UswUnionFmt, check, lib)
 
 __all__ = ["HostEncoding", "Encoding", "encode_host", "encode", "to_device", "validate", "spmm",
            "spmm_workspace_bytes", "spmm_counter_bytes", "UnionHostEncoding", "UnionEncoding",
            "union_encode_host", "union_encode", "union_to_device", "union_validate", "union_spmm",
-           "union_workspace_bytes", "UswError", "lib"]
+           "union_workspace_bytes", "CbcHostEncoding", "CbcEncoding", "cbc_encode_host", "cbc_encode",
+           "cbc_to_device", "cbc_validate", "cbc_spmspv", "cbc_workspace_bytes", "UswError", "lib"]
 
 _VAL = {"f16": USW_VAL_F16, "i4": USW_VAL_I4}
 
@@ -118,6 +119,40 @@ class UnionEncoding:
         return UswUnionFmt(self.M, self.K, self.lt_m, self.lt_k, self.r_a, self.c_a, self.val_type, 0, self.payload,
                            self.bitmaps.data_ptr(), self.offsets.data_ptr(), self.values.data_ptr(),
                            self.scales.data_ptr() if self.scales is not None else None)
+
+
+@dataclass
+class CbcHostEncoding:
+    """Tiled-CBC encoding in host memory (numpy), as written by usw_cbc_encode."""
+    M: int
+    K: int
+    nnz: int
+    nnz_padded: int
+    bitmaps: np.ndarray        # uint64 [NGT * 64]
+    tile_offsets: np.ndarray   # uint32 [NGT+1]
+    colinfo: np.ndarray        # uint32 [NGT * 16]
+    values: np.ndarray         # uint16 fp16 bits [nnz_padded]
+
+    def fmt(self) -> UswCbcFmt:
+        return UswCbcFmt(self.M, self.K, 256, 16, USW_VAL_F16, 0, self.nnz_padded, self.bitmaps.ctypes.data,
+                         self.tile_offsets.ctypes.data, self.colinfo.ctypes.data, self.values.ctypes.data)
+
+
+@dataclass
+class CbcEncoding:
+    """Tiled-CBC encoding on a GPU (torch tensors) plus its usw_cbc_fmt view."""
+    M: int
+    K: int
+    nnz: int
+    nnz_padded: int
+    bitmaps: "object"
+    tile_offsets: "object"
+    colinfo: "object"
+    values: "object"
+
+    def fmt(self) -> UswCbcFmt:
+        return UswCbcFmt(self.M, self.K, 256, 16, USW_VAL_F16, 0, self.nnz_padded, self.bitmaps.data_ptr(),
+                         self.tile_offsets.data_ptr(), self.colinfo.data_ptr(), self.values.data_ptr())
 
 
 def _as_numpy_f16(W) -> np.ndarray:
@@ -251,6 +286,80 @@ def union_spmm(enc: UnionEncoding, x, y=None, out_dtype=None, splits: int = 0, s
     check(lib().usw_union_spmm(ctypes.byref(f), x.data_ptr(), y.data_ptr(), yt, N, int(splits),
                                ws.data_ptr() if ws is not None else None, nbytes, ctypes.c_void_p(st.cuda_stream)),
           "usw_union_spmm")
+    return y
+
+
+def cbc_encode_host(W, mask=None) -> CbcHostEncoding:
+    """Run usw_cbc_encode on host arrays (Tiled-CBC, 256x16 GTiles, fp16 values)."""
+    W = _as_numpy_f16(W)
+    if W.ndim != 2:
+        raise ValueError("W must be 2-D")
+    M, K = W.shape
+    mask = _as_mask(mask, W.shape)
+    L = lib()
+    nnz, npad = ctypes.c_int64(), ctypes.c_int64()
+    sz = [ctypes.c_size_t() for _ in range(4)]
+    wp = W.ctypes.data
+    mp = mask.ctypes.data if mask is not None else None
+    check(L.usw_cbc_encode_query(wp, mp, M, K, ctypes.byref(nnz), ctypes.byref(npad), *[ctypes.byref(s) for s in sz]),
+          "usw_cbc_encode_query")
+    b_bm, b_off, b_ci, b_val = (s.value for s in sz)
+    bitmaps = np.empty(b_bm // 8, dtype=np.uint64)
+    offs = np.empty(b_off // 4, dtype=np.uint32)
+    colinfo = np.empty(b_ci // 4, dtype=np.uint32)
+    values = np.empty(max(b_val // 2, 8), dtype=np.uint16)
+    check(L.usw_cbc_encode(wp, mp, M, K, bitmaps.ctypes.data, offs.ctypes.data, colinfo.ctypes.data,
+                           values.ctypes.data, values.nbytes), "usw_cbc_encode")
+    return CbcHostEncoding(M, K, nnz.value, npad.value, bitmaps, offs, colinfo, values)
+
+
+def cbc_validate(enc: CbcHostEncoding) -> None:
+    """usw_cbc_validate on a host encoding (raises UswError when corrupt)."""
+    f = enc.fmt()
+    check(lib().usw_cbc_validate(ctypes.byref(f)), "usw_cbc_validate")
+
+
+def cbc_to_device(enc: CbcHostEncoding, device="cuda") -> CbcEncoding:
+    import torch
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+    return CbcEncoding(enc.M, enc.K, enc.nnz, enc.nnz_padded, t(enc.bitmaps.view(np.int64)),
+                       t(enc.tile_offsets.view(np.int32)), t(enc.colinfo.view(np.int32)), t(enc.values.view(np.int16)))
+
+
+def cbc_encode(W, mask=None, device="cuda") -> CbcEncoding:
+    """Encode on the host (usw_cbc_encode) and copy the buffers to ``device``."""
+    return cbc_to_device(cbc_encode_host(W, mask), device)
+
+
+def cbc_workspace_bytes(enc: CbcEncoding, splits: int = 0):
+    """(workspace bytes, counter bytes) of usw_cbc_spmspv."""
+    f = enc.fmt()
+    b, c = ctypes.c_size_t(), ctypes.c_size_t()
+    check(lib().usw_cbc_spmspv_workspace(ctypes.byref(f), int(splits), ctypes.byref(b), ctypes.byref(c)),
+          "usw_cbc_spmspv_workspace")
+    return b.value, c.value
+
+
+def cbc_spmspv(enc: CbcEncoding, x, tau: float = 0.0, y=None, out_dtype=None, splits: int = 0, stream=None):
+    """y [M] = W_sp x over the columns with |x_k| >= tau (usw_cbc_spmspv)."""
+    import torch
+    if x.dtype != torch.float16 or x.numel() != enc.K:
+        raise ValueError("x must hold K float16 values")
+    x = x.reshape(-1).contiguous()
+    if y is None:
+        y = torch.empty(enc.M, dtype=out_dtype or torch.float16, device=x.device)
+    if y.numel() != enc.M or not y.is_contiguous():
+        raise ValueError("y must be a contiguous tensor of M values")
+    yt = {torch.float16: USW_OUT_F16, torch.float32: USW_OUT_F32}.get(y.dtype)
+    if yt is None:
+        raise ValueError("y must be float16 or float32")
+    f = enc.fmt()
+    nbytes, cbytes = cbc_workspace_bytes(enc, splits)
+    ws = _workspace(x.device, nbytes, cbytes) if nbytes else None
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    check(lib().usw_cbc_spmspv(ctypes.byref(f), x.data_ptr(), y.data_ptr(), yt, float(tau), int(splits),
+                               ws.data_ptr() if ws is not None else None, nbytes, ctypes.c_void_p(st.cuda_stream)),
+          "usw_cbc_spmspv")
     return y
 
 

@@ -29,6 +29,7 @@ EXPORTED = (
     "usw_probe_read",
     "usw_union_encode_query", "usw_union_encode", "usw_union_validate", "usw_union_spmm_workspace",
     "usw_union_spmm_counter_bytes", "usw_union_spmm",
+    "usw_cbc_encode_query", "usw_cbc_encode", "usw_cbc_validate", "usw_cbc_spmspv_workspace", "usw_cbc_spmspv",
 )
 
 
@@ -60,6 +61,18 @@ class UswUnionFmt(ctypes.Structure):
         ("payload", ctypes.c_int64),
         ("bitmaps", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
         ("values", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+    ]
+
+
+class UswCbcFmt(ctypes.Structure):
+    """Mirror of ``usw_cbc_fmt``."""
+    _fields_ = [
+        ("M", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("tile_m", ctypes.c_int32), ("tile_k", ctypes.c_int32),
+        ("val_type", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("nnz_padded", ctypes.c_int64),
+        ("bitmaps", ctypes.c_void_p), ("tile_offsets", ctypes.c_void_p),
+        ("colinfo", ctypes.c_void_p), ("values", ctypes.c_void_p),
     ]
 
 
@@ -106,6 +119,17 @@ def _declare(lib):
     lib.usw_union_spmm_counter_bytes.argtypes = [P(UswUnionFmt), c_i32, c_i32, P(c_sz)]
     lib.usw_union_spmm.restype = c_i32
     lib.usw_union_spmm.argtypes = [P(UswUnionFmt), c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]
+    lib.usw_cbc_encode_query.restype = c_i32
+    lib.usw_cbc_encode_query.argtypes = [c_vp, c_vp, c_i32, c_i32, P(c_i64), P(c_i64), P(c_sz), P(c_sz), P(c_sz),
+                                         P(c_sz)]
+    lib.usw_cbc_encode.restype = c_i32
+    lib.usw_cbc_encode.argtypes = [c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz]
+    lib.usw_cbc_validate.restype = c_i32
+    lib.usw_cbc_validate.argtypes = [P(UswCbcFmt)]
+    lib.usw_cbc_spmspv_workspace.restype = c_i32
+    lib.usw_cbc_spmspv_workspace.argtypes = [P(UswCbcFmt), c_i32, P(c_sz), P(c_sz)]
+    lib.usw_cbc_spmspv.restype = c_i32
+    lib.usw_cbc_spmspv.argtypes = [P(UswCbcFmt), c_vp, c_vp, c_i32, ctypes.c_float, c_i32, c_vp, c_sz, c_vp]
     return lib
 
 

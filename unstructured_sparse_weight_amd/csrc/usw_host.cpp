@@ -59,6 +59,17 @@ usw_status make_union_geometry(int64_t M, int64_t K, int64_t lt_m, int64_t lt_k,
   return USW_OK;
 }
 
+usw_status make_cbc_geometry(int64_t M, int64_t K, CbcGeometry* g) {
+  if (M <= 0 || K <= 0 || M % kCbcTM || K % kCbcTK) return USW_ERR_BAD_SHAPE;
+  if (M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 31) - 1) return USW_ERR_BAD_SHAPE;
+  g->M = M;
+  g->K = K;
+  g->gr = M / kCbcTM;
+  g->gc = K / kCbcTK;
+  g->ngt = g->gr * g->gc;
+  return USW_OK;
+}
+
 double f16_to_f64(uint16_t h) {
   const int sign = h >> 15;
   const int e = (h >> 10) & 0x1F;
@@ -226,6 +237,30 @@ inline bool union_on(const UnionGeometry& g, const uint16_t* W, const uint8_t* m
   return false;
 }
 
+// Kept count of every column tile (GTile t, column c at t * 16 + c), their
+// total and the total of the runs padded to 8.
+void count_cbc(const CbcGeometry& g, const uint16_t* W, const uint8_t* mask, std::vector<int64_t>* cnt,
+               int64_t* total, int64_t* padded) {
+  cnt->assign(static_cast<size_t>(g.ngt * kCbcTK), 0);
+  int64_t* c = cnt->data();
+  parallel_for(g.ngt, [&](int64_t lo, int64_t hi) {
+    for (int64_t t = lo; t < hi; ++t) {
+      const int64_t ti = t / g.gc, tj = t % g.gc;
+      for (int k = 0; k < kCbcTK; ++k) {
+        int64_t n = 0;
+        for (int r = 0; r < kCbcTM; ++r) n += is_kept(W, mask, (ti * kCbcTM + r) * g.K + tj * kCbcTK + k);
+        c[t * kCbcTK + k] = n;
+      }
+    }
+  });
+  *total = 0;
+  *padded = 0;
+  for (int64_t i = 0; i < g.ngt * kCbcTK; ++i) {
+    *total += c[i];
+    *padded += (c[i] + 7) / 8 * 8;
+  }
+}
+
 // offsets[t] = payload elements before LT t (Q times the active positions).
 usw_status count_union(const UnionGeometry& g, const uint16_t* W, const uint8_t* mask, std::vector<int64_t>* off) {
   off->assign(g.nlt + 1, 0);
@@ -371,6 +406,98 @@ usw_status usw_validate(const usw_fmt* f) {
     int64_t c = 0;
     for (int64_t b = 0; b < g.bt_per_gt; ++b) c += __builtin_popcountll(f->bitmaps[gid * g.bt_per_gt + b]);
     if (c != static_cast<int64_t>(f->offsets[gid + 1] - f->offsets[gid])) return USW_ERR_CORRUPT;
+  }
+  return USW_OK;
+}
+
+usw_status usw_cbc_encode_query(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int64_t* nnz,
+                                int64_t* nnz_padded, size_t* bytes_bitmaps, size_t* bytes_tile_offsets,
+                                size_t* bytes_colinfo, size_t* bytes_values) {
+  if (!W && !mask) return USW_ERR_NULL_ARG;
+  CbcGeometry g;
+  usw_status st = make_cbc_geometry(M, K, &g);
+  if (st) return st;
+  std::vector<int64_t> cnt;
+  int64_t total = 0, padded = 0;
+  count_cbc(g, W, mask, &cnt, &total, &padded);
+  if (padded >= (int64_t(1) << 32)) return USW_ERR_CAPACITY;
+  if (nnz) *nnz = total;
+  if (nnz_padded) *nnz_padded = padded;
+  if (bytes_bitmaps) *bytes_bitmaps = static_cast<size_t>(8 * g.ngt * kCbcTK * kCbcWpc);
+  if (bytes_tile_offsets) *bytes_tile_offsets = static_cast<size_t>(4 * (g.ngt + 1));
+  if (bytes_colinfo) *bytes_colinfo = static_cast<size_t>(4 * g.ngt * kCbcTK);
+  if (bytes_values) *bytes_values = static_cast<size_t>(2 * padded);
+  return USW_OK;
+}
+
+usw_status usw_cbc_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, uint64_t* bitmaps,
+                          uint32_t* tile_offsets, uint32_t* colinfo, uint16_t* values, size_t values_capacity) {
+  if (!W || !bitmaps || !tile_offsets || !colinfo || (!values && values_capacity)) return USW_ERR_NULL_ARG;
+  CbcGeometry g;
+  usw_status st = make_cbc_geometry(M, K, &g);
+  if (st) return st;
+  std::vector<int64_t> cnt;
+  int64_t total = 0, padded = 0;
+  count_cbc(g, W, mask, &cnt, &total, &padded);
+  if (padded >= (int64_t(1) << 32)) return USW_ERR_CAPACITY;
+  if (values_capacity < static_cast<size_t>(2 * padded)) return USW_ERR_CAPACITY;
+  // Tile offsets: prefix of the padded runs of each GTile's columns.
+  int64_t acc = 0;
+  for (int64_t t = 0; t < g.ngt; ++t) {
+    tile_offsets[t] = static_cast<uint32_t>(acc);
+    for (int c = 0; c < kCbcTK; ++c) acc += (cnt[static_cast<size_t>(t * kCbcTK + c)] + 7) / 8 * 8;
+  }
+  tile_offsets[g.ngt] = static_cast<uint32_t>(acc);
+  parallel_for(g.ngt, [&](int64_t lo, int64_t hi) {
+    for (int64_t t = lo; t < hi; ++t) {
+      const int64_t ti = t / g.gc, tj = t % g.gc;
+      int64_t idx = tile_offsets[t], run = 0;
+      for (int c = 0; c < kCbcTK; ++c) {
+        const int64_t col = tj * kCbcTK + c;
+        uint64_t* words = bitmaps + (t * kCbcTK + c) * kCbcWpc;
+        for (int j = 0; j < kCbcWpc; ++j) words[j] = 0;
+        int64_t n = 0;
+        for (int r = 0; r < kCbcTM; ++r) {
+          const int64_t lin = (ti * kCbcTM + r) * g.K + col;
+          if (!is_kept(W, mask, lin)) continue;
+          words[r >> 6] |= 1ull << (r & 63);
+          values[idx + n] = W[lin];
+          ++n;
+        }
+        const int64_t np = (n + 7) / 8 * 8;
+        for (int64_t i = n; i < np; ++i) values[idx + i] = 0;
+        colinfo[t * kCbcTK + c] = static_cast<uint32_t>((run << 16) | n);
+        idx += np;
+        run += np;
+      }
+    }
+  });
+  for (size_t i = static_cast<size_t>(padded); i < values_capacity / 2; ++i) values[i] = 0;
+  return USW_OK;
+}
+
+usw_status usw_cbc_validate(const usw_cbc_fmt* f) {
+  if (!f) return USW_ERR_NULL_ARG;
+  CbcGeometry g;
+  usw_status st = make_cbc_geometry(f->M, f->K, &g);
+  if (st) return st;
+  if (f->tile_m != kCbcTM || f->tile_k != kCbcTK || f->reserved != 0) return USW_ERR_BAD_SHAPE;
+  if (f->val_type != USW_VAL_F16) return USW_ERR_BAD_DTYPE;
+  if (!f->bitmaps || !f->tile_offsets || !f->colinfo || (f->nnz_padded > 0 && !f->values)) return USW_ERR_NULL_ARG;
+  if (f->nnz_padded < 0 || f->nnz_padded >= (int64_t(1) << 32)) return USW_ERR_CORRUPT;
+  if (f->tile_offsets[0] != 0 || static_cast<int64_t>(f->tile_offsets[g.ngt]) != f->nnz_padded) return USW_ERR_CORRUPT;
+  for (int64_t t = 0; t < g.ngt; ++t) {
+    int64_t run = 0;
+    for (int c = 0; c < kCbcTK; ++c) {
+      int64_t n = 0;
+      for (int j = 0; j < kCbcWpc; ++j) n += __builtin_popcountll(f->bitmaps[(t * kCbcTK + c) * kCbcWpc + j]);
+      const uint32_t ci = f->colinfo[t * kCbcTK + c];
+      if (static_cast<int64_t>(ci >> 16) != run || static_cast<int64_t>(ci & 0xFFFFu) != n) return USW_ERR_CORRUPT;
+      run += (n + 7) / 8 * 8;
+    }
+    if (f->tile_offsets[t + 1] < f->tile_offsets[t] ||
+        static_cast<int64_t>(f->tile_offsets[t + 1] - f->tile_offsets[t]) != run)
+      return USW_ERR_CORRUPT;
   }
   return USW_OK;
 }

@@ -28,6 +28,19 @@ struct UnionGeometry {
   int64_t nw;         // union words per LT
 };
 
+// Tiled-CBC: GTiles of 256 x 16, columns of 256 x 1 with 4 bitmap words.
+constexpr int kCbcTM = 256;
+constexpr int kCbcTK = 16;
+constexpr int kCbcWpc = kCbcTM / 64;
+
+struct CbcGeometry {
+  int64_t M, K;
+  int64_t gr, gc;   // GTile rows and columns
+  int64_t ngt;
+};
+
+usw_status make_cbc_geometry(int64_t M, int64_t K, CbcGeometry* g);
+
 usw_status make_union_geometry(int64_t M, int64_t K, int64_t lt_m, int64_t lt_k, int64_t r_a, int64_t c_a,
                                UnionGeometry* g);
 size_t values_alloc_bytes(int32_t val_type, int64_t nnz);
