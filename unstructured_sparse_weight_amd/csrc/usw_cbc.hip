@@ -9,20 +9,25 @@
 //
 // Design (wave64):
 //   * One workgroup of four waves owns one 256-row strip of GTiles and a
-//     range of GTile columns; thread t owns strip row t, so no reduction
-//     across waves is needed.
-//   * Per GTile: lane j (mod 16) reads column j's ColInfo and x_j and the
-//     wave ballots |x_j| >= tau into a 16-bit mask of active columns (the
-//     same in every wave).  Wave w copies the padded runs of its active
-//     columns 4w..4w+3 into LDS (16-byte loads, at most 32 per column);
-//     inactive columns cost neither bitmap nor value bytes.
-//   * The active columns' bitmap words arrive as one 8-byte load per lane
-//     (lane 4c + q: word q of column c) with the popcounts of the words
-//     before them in the column.  For each active column (a scalar loop over
-//     the mask) the wave takes word w and its base with v_readlane, and each
-//     lane whose bit is set takes its value at base + v_mbcnt of the word
-//     (the masked popcount of the bits below it) from LDS and multiplies it
-//     with x_k.
+//     range of GTile columns; each wave streams its own run of GTiles over
+//     all 256 rows (lane l holds rows l, 64 + l, 128 + l, 192 + l), with its
+//     own LDS staging area, so the main loop has no workgroup barrier.  The
+//     four waves' row sums are added in LDS at the end, in a fixed order.
+//   * Per GTile: lane j (mod 16) reads column j's ColInfo and x_j, and the
+//     wave ballots |x_j| >= tau into a 16-bit mask of active columns.  The
+//     padded runs of the active columns are loaded (16 bytes per load; lane
+//     4c + q takes pieces q, q + 4, ... of column c) into registers one
+//     GTile ahead and copied into LDS just before the next GTile's loads
+//     reuse those registers; inactive columns cost neither bitmap nor value
+//     bytes.  ColInfo, x and TileOffset run two GTiles ahead, since the
+//     value loads depend on them.
+//   * The active columns' bitmap words load with the values (lane 4c + q:
+//     word q of column c).  For each active column (a scalar loop over the
+//     mask) v_readlane brings its four words into SGPRs and SALU popcounts
+//     give each word's base.  Per word, every lane takes base + v_mbcnt of the word
+//     (the masked popcount of the bits below it) as its rank, reads that
+//     value from LDS, and accumulates it times x_k, with x_k replaced by 0
+//     where its bit is clear.
 //   * Split K: each workgroup writes its row sums to an fp32 workspace with
 //     device-coherent stores; the last workgroup of the strip (a per-strip
 //     counter) adds them in split order and writes y.
@@ -44,8 +49,12 @@ using namespace usw_dev;
 constexpr int kTM = usw::kCbcTM;    // GTile rows
 constexpr int kTK = usw::kCbcTK;    // GTile columns
 constexpr int kWpc = usw::kCbcWpc;  // bitmap words per column
-constexpr int kCThreads = kTM;      // one strip row per thread
-static_assert(kCThreads == 256 && kTK == 16 && kWpc == 4, "four waves of 64 rows, four columns each to stage");
+constexpr int kCWaves = 4;
+constexpr int kCThreads = 64 * kCWaves;
+constexpr int kColBytes = 2 * kTM;          // LDS bytes of one column's run (at most 256 values)
+constexpr int kWaveBuf = kTK * kColBytes;   // a wave's staging area: 8 KB
+constexpr int kLoads = kTM / 8 / 4;         // 16-byte loads per lane per GTile: 32 pieces, 4 lanes per column
+static_assert(kTK == 16 && kWpc == 4 && kTM == 256, "lane 4c + q serves column c; words 0-3 cover 256 rows");
 
 struct CArgs {
   const uint64_t* __restrict__ bitmaps;
@@ -62,9 +71,98 @@ struct CArgs {
   int remap;                         // 1: keep the splits of a strip on one XCD
 };
 
+// Metadata of one GTile: lane j (mod 16) holds column j's ColInfo and x_j;
+// tbase is the GTile's TileOffset.
+struct CMeta {
+  uint32_t ci;
+  float xf;
+  uint32_t tbase;
+};
+
+// One GTile's loads, held in registers until they are copied into LDS.
+struct CData {
+  u32x4_t v[kLoads];   // lane 4c + q: pieces q + 4i of column c
+  u32x2_t bw;          // lane 4c + q: bitmap word q of column c (0 when inactive)
+  float xf;            // lane j: x_j
+  uint32_t amask;      // active columns (wave-uniform)
+  uint32_t pieces;     // lane 4c + q: 16-byte pieces of column c's run (0 when inactive)
+};
+
+__device__ __forceinline__ CMeta cbc_meta(const CArgs& a, int gi, int c, int lane) {
+  const int64_t t = static_cast<int64_t>(gi) * a.Gc + c;
+  CMeta m;
+  m.ci = a.colinfo[t * kTK + (lane & 15)];
+  m.xf = static_cast<float>(__builtin_bit_cast(_Float16, a.x[c * kTK + (lane & 15)]));
+  m.tbase = a.toff[t];
+  return m;
+}
+
+__device__ __forceinline__ void cbc_load(CData& d, const CArgs& a, int gi, int c, const CMeta& m, int lane) {
+  const int64_t t = static_cast<int64_t>(gi) * a.Gc + c;
+  d.xf = m.xf;
+  d.amask = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(fabsf(m.xf) >= a.tau)) & 0xFFFFu;
+  const uint32_t tbase = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(m.tbase));
+  const int bc = lane >> 2, bq = lane & 3;
+  const uint32_t cib = __shfl(m.ci, bc);
+  d.pieces = ((d.amask >> bc) & 1u) ? ((cib & 0xFFFFu) + 7u) >> 3 : 0u;
+  d.bw = u32x2_t{0u, 0u};
+  if ((d.amask >> bc) & 1u) d.bw = reinterpret_cast<const u32x2_t*>(a.bitmaps)[(t * kTK + bc) * kWpc + bq];
+  // The bound on the stored values keeps a corrupt ColInfo inside the buffer.
+  const uint64_t src0 = static_cast<uint64_t>(tbase) + (cib >> 16);
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const uint32_t q = static_cast<uint32_t>(bq + 4 * i);
+    d.v[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (q < d.pieces && src0 + 8u * q + 8u <= a.nvals)
+      d.v[i] = *reinterpret_cast<const u32x4_t*>(a.values + src0 + 8u * q);
+  }
+}
+
+__device__ __forceinline__ void cbc_commit(const CData& d, uint8_t* buf, int lane) {
+  const int bc = lane >> 2, bq = lane & 3;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i)
+    if (static_cast<uint32_t>(bq + 4 * i) < d.pieces)
+      *reinterpret_cast<u32x4_t*>(buf + bc * kColBytes + 16 * (bq + 4 * i)) = d.v[i];
+}
+
+// x_k where the lane's bit of word is set, else 0 (the word is wave-uniform,
+// so it serves directly as the lane mask of v_cndmask).
+__device__ __forceinline__ float select_by_word(float xk, uint64_t word) {
+  float r;
+  asm volatile("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(r) : "v"(xk), "s"(word));
+  return r;
+}
+
+// Accumulate a staged GTile over its active columns.  bw is the GTile's
+// bitmap words (lane 4c + q: word q of column c); each word is read into
+// SGPRs with v_readlane, its base is the SALU popcount of the column's
+// earlier words.
+__device__ __forceinline__ void cbc_compute(float xf, uint32_t amask, u32x2_t bw, const _Float16* vals,
+                                            float (&acc)[4]) {
+  for (uint32_t m = amask; m != 0; m &= m - 1) {
+    const int cc = __builtin_ctz(m);
+    const float xc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xf), cc));
+    // The word's base (set bits of the column's earlier words) goes into
+    // the scalar part of the address; a rank counts bits among the
+    // column's 256 rows, so it stays below 256.
+    const _Float16* col = vals + cc * kTM;
+#pragma unroll
+    for (int q = 0; q < kWpc; ++q) {
+      const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(bw.x, 4 * cc + q));
+      const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(bw.y, 4 * cc + q));
+      const uint64_t word = (static_cast<uint64_t>(hi) << 32) | lo;
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+      const float v = static_cast<float>(col[below]);
+      acc[q] = fmaf(v, select_by_word(xc, word), acc[q]);
+      col += __builtin_popcountll(word);
+    }
+  }
+}
+
 template <bool OUT_F16>
-__global__ __launch_bounds__(kCThreads, 2) void cbc_spmspv_kernel(CArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 vals[kTK * kTM];   // column c's run at [256 c, 256 c + 256)
+__global__ __launch_bounds__(kCThreads, 4) void cbc_spmspv_kernel(CArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kCWaves * kWaveBuf];   // staging; then the wave reduction
   __shared__ uint32_t last_flag;
 
   const int tid = threadIdx.x;
@@ -75,65 +173,53 @@ __global__ __launch_bounds__(kCThreads, 2) void cbc_spmspv_kernel(CArgs a) {
   const int L = a.remap ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
   const int gi = L / a.splits;
   const int sidx = L - gi * a.splits;
-  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * sidx / a.splits);
-  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (sidx + 1) / a.splits);
+  const int parts = a.splits * kCWaves;
+  const int qw = sidx * kCWaves + w;
+  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * qw / parts);
+  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (qw + 1) / parts);
 
-  const int j = lane & 15;      // the column whose metadata this lane reads
-  const int cs = 4 * w + (lane >> 4);   // the column whose run this lane helps to stage
-  float acc = 0.f;
-  for (int c = c_begin; c < c_end; ++c) {
-    const int64_t t = static_cast<int64_t>(gi) * a.Gc + c;
-    const uint32_t ci = a.colinfo[t * kTK + j];
-    const float xf = static_cast<float>(__builtin_bit_cast(_Float16, a.x[c * kTK + j]));
-    const uint32_t amask = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(fabsf(xf) >= a.tau)) & 0xFFFFu;
-    const uint32_t tbase = __builtin_amdgcn_readfirstlane(a.toff[t]);
-
-    // Stage the runs of the active columns 4w .. 4w+3 (lanes 16 q .. 16 q + 15
-    // copy column 4w + q, pieces p and p + 16 of 16 bytes).  The bound on the
-    // stored values keeps a corrupt ColInfo inside the buffer.
-    const uint32_t cci = __shfl(ci, cs);
-    if ((amask >> cs) & 1u) {
-      const uint32_t pieces = ((cci & 0xFFFFu) + 7u) >> 3;
-      const uint64_t src0 = static_cast<uint64_t>(tbase) + (cci >> 16);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  uint8_t* buf = smem + w * kWaveBuf;
+  const _Float16* vals = reinterpret_cast<const _Float16*>(buf);
+  // A lane whose bit is clear still reads a value (then weighted by 0);
+  // zeroing the staging area first means such a read only ever sees a
+  // finite weight of this call or 0.
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t p = static_cast<uint32_t>(lane & 15) + 16u * h;
-        if (p < pieces && src0 + 8u * p + 8u <= a.nvals)
-          *reinterpret_cast<u32x4_t*>(vals + cs * kTM + 8 * p) =
-              *reinterpret_cast<const u32x4_t*>(a.values + src0 + 8u * p);
-      }
+  for (int i = 0; i < kWaveBuf / 1024; ++i) reinterpret_cast<u32x4_t*>(buf)[lane + 64 * i] = u32x4_t{0u, 0u, 0u, 0u};
+  wave_sync();
+  if (c_begin < c_end) {
+    // One register slot: a step copies GTile c's values into LDS, then
+    // issues c+1's value loads into the same registers (and c+2's metadata)
+    // and multiplies c while they are in flight.  Loads past the wave's last
+    // GTile repeat it, so every step issues the same loads.
+    const int c_last = c_end - 1;
+    CMeta m1 = cbc_meta(a, gi, min(c_begin + 1, c_last), lane);
+    CData d;
+    cbc_load(d, a, gi, c_begin, cbc_meta(a, gi, c_begin, lane), lane);
+    for (int c = c_begin; c < c_end; ++c) {
+      const CMeta m2 = cbc_meta(a, gi, min(c + 2, c_last), lane);
+      cbc_commit(d, buf, lane);
+      const float xf = d.xf;
+      const uint32_t amask = d.amask;
+      const u32x2_t bw = d.bw;
+      cbc_load(d, a, gi, min(c + 1, c_last), m1, lane);
+      wave_sync();
+      cbc_compute(xf, amask, bw, vals, acc);
+      wave_sync();
+      m1 = m2;
     }
-    // The active columns' bitmap words, one per lane: lane 4 c + q holds word
-    // q of column c, and the set bits of words 0..q-1 (a prefix inside each
-    // group of four lanes).
-    const int bc = lane >> 2, bq = lane & 3;
-    u32x2_t bw = {0u, 0u};
-    if ((amask >> bc) & 1u) bw = reinterpret_cast<const u32x2_t*>(a.bitmaps)[(t * kTK + bc) * kWpc + bq];
-    const uint32_t pc = __builtin_popcount(bw.x) + __builtin_popcount(bw.y);
-    const int q0 = lane & ~3;
-    const uint32_t p0 = __shfl(pc, q0), p1 = __shfl(pc, q0 + 1), p2 = __shfl(pc, q0 + 2);
-    const uint32_t before = (bq > 0 ? p0 : 0u) + (bq > 1 ? p1 : 0u) + (bq > 2 ? p2 : 0u);
-    __syncthreads();
-
-    // Each active column: word w holds this wave's 64 rows; the rank of a
-    // kept row is the set bits of words 0..w-1 plus those below it in word w.
-    for (uint32_t m = amask; m != 0; m &= m - 1) {
-      const int cc = __builtin_ctz(m);
-      const int src = 4 * cc + w;
-      const uint32_t lo = __builtin_amdgcn_readlane(bw.x, src);
-      const uint32_t hi = __builtin_amdgcn_readlane(bw.y, src);
-      const uint32_t base = __builtin_amdgcn_readlane(before, src);
-      const float xc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xf), cc));
-      const uint64_t word = (static_cast<uint64_t>(hi) << 32) | lo;
-      if ((word >> lane) & 1ull) {
-        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, base));
-        acc = fmaf(static_cast<float>(vals[cc * kTM + (rank & (kTM - 1))]), xc, acc);
-      }
-    }
-    __syncthreads();
   }
 
-  // Row gi * 256 + tid.
+  // The waves' sums of strip row 64 q + lane, added in wave order.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);   // [waves][256]
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[w * kTM + 64 * q + lane] = acc[q];
+  __syncthreads();
+  float rsum = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < kCWaves; ++ww) rsum += red[ww * kTM + tid];
+
   const int m = gi * kTM + tid;
   auto store_y = [&](float v) {
     if constexpr (OUT_F16)
@@ -142,13 +228,13 @@ __global__ __launch_bounds__(kCThreads, 2) void cbc_spmspv_kernel(CArgs a) {
       reinterpret_cast<float*>(a.y)[m] = v;
   };
   if (a.splits <= 1) {
-    store_y(acc);
+    store_y(rsum);
     return;
   }
   auto part_rsrc = [&](int s) {
     return __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(s) * a.M, 0, a.M * 4, kBufferRsrcWord3);
   };
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc), part_rsrc(sidx), m * 4, 0, kCacheSc1);
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, rsum), part_rsrc(sidx), m * 4, 0, kCacheSc1);
   // Every thread's partial store has completed (s_waitcnt) before the
   // barrier that precedes the counter increment; the last workgroup reads
   // the partials with device-coherent loads after it has seen the count.
@@ -170,7 +256,7 @@ __global__ __launch_bounds__(kCThreads, 2) void cbc_spmspv_kernel(CArgs a) {
 
 int cbc_splits(const usw::CbcGeometry& g, int splits_req) {
   int64_t s = splits_req;
-  if (s <= 0) s = (2048 + g.gr / 2) / g.gr;   // about eight resident workgroups per compute unit
+  if (s <= 0) s = std::max<int64_t>(1, 1024 / g.gr);   // one round of four resident workgroups per compute unit
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, g.gc)));
 }
 
