@@ -383,9 +383,9 @@ usw_status usw_cbc_spmspv_workspace(const usw_cbc_fmt* fmt, int32_t splits, size
  * USW_OUT_F16, rounded to nearest even from fp32) or fp32, both 16-byte
  * aligned; tau >= 0 (tau = 0 keeps every column).  fp32 accumulation;
  * deterministic (split partial sums added in split order).
- * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED (tile shape other than
- * 256 x 16, values other than fp16, tau negative or NaN), MISALIGNED,
- * WORKSPACE, HIP.
+ * Errors: NULL_ARG, BAD_SHAPE (also M > 2^28 or 2 nnz_padded >= 2^31 - 16
+ * bytes), BAD_DTYPE, UNSUPPORTED (tile shape other than 256 x 16, values
+ * other than fp16, tau negative or NaN), MISALIGNED, WORKSPACE, HIP.
  */
 usw_status usw_cbc_spmspv(const usw_cbc_fmt* fmt, const uint16_t* x, void* y, int32_t y_type, float tau,
                           int32_t splits, void* ws, size_t ws_bytes, void* stream);

@@ -55,6 +55,8 @@ constexpr int kColBytes = 2 * kTM;          // LDS bytes of one column's run (at
 constexpr int kWaveBuf = kTK * kColBytes;   // a wave's staging area: 8 KB
 constexpr int kLoads = kTM / 8 / 4;         // 16-byte loads per lane per GTile: 32 pieces, 4 lanes per column
 static_assert(kTK == 16 && kWpc == 4 && kTM == 256, "lane 4c + q serves column c; words 0-3 cover 256 rows");
+// A buffer offset past any values array the host accepts (< 2^31 - 16 bytes).
+constexpr uint32_t kPastValues = 0x7FFFFFF0u;
 
 struct CArgs {
   const uint64_t* __restrict__ bitmaps;
@@ -107,23 +109,27 @@ __device__ __forceinline__ void cbc_load(CData& d, const CArgs& a, int gi, int c
   d.pieces = ((d.amask >> bc) & 1u) ? ((cib & 0xFFFFu) + 7u) >> 3 : 0u;
   d.bw = u32x2_t{0u, 0u};
   if ((d.amask >> bc) & 1u) d.bw = reinterpret_cast<const u32x2_t*>(a.bitmaps)[(t * kTK + bc) * kWpc + bq];
-  // The bound on the stored values keeps a corrupt ColInfo inside the buffer.
-  const uint64_t src0 = static_cast<uint64_t>(tbase) + (cib >> 16);
+  // Buffer loads over the whole values array: a lane past its column's run
+  // (or on an inactive column) gets an offset beyond the array, which the
+  // hardware answers with zeros without a fetch, so no branch is needed;
+  // the same bound keeps a corrupt ColInfo inside the array.
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.values), 0,
+                                                      static_cast<int>(2 * a.nvals), kBufferRsrcWord3);
+  const uint32_t src0 = 2u * (tbase + (cib >> 16));
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const uint32_t q = static_cast<uint32_t>(bq + 4 * i);
-    d.v[i] = u32x4_t{0u, 0u, 0u, 0u};
-    if (q < d.pieces && src0 + 8u * q + 8u <= a.nvals)
-      d.v[i] = *reinterpret_cast<const u32x4_t*>(a.values + src0 + 8u * q);
+    const uint32_t off = q < d.pieces ? src0 + 16u * q : kPastValues;
+    d.v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(off), 0, 0));
   }
 }
 
+// Every lane stores its pieces, zeros past the run included (such slots are
+// only read by lanes whose bit is clear, which weight them by 0).
 __device__ __forceinline__ void cbc_commit(const CData& d, uint8_t* buf, int lane) {
   const int bc = lane >> 2, bq = lane & 3;
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i)
-    if (static_cast<uint32_t>(bq + 4 * i) < d.pieces)
-      *reinterpret_cast<u32x4_t*>(buf + bc * kColBytes + 16 * (bq + 4 * i)) = d.v[i];
+  for (int i = 0; i < kLoads; ++i) *reinterpret_cast<u32x4_t*>(buf + bc * kColBytes + 16 * (bq + 4 * i)) = d.v[i];
 }
 
 // x_k where the lane's bit of word is set, else 0 (the word is wave-uniform,
@@ -279,6 +285,8 @@ usw_status cbc_check(const usw_cbc_fmt* f, int32_t y_type, usw::CbcGeometry* g) 
   if (f->val_type != USW_VAL_F16 || f->tile_m != kTM || f->tile_k != kTK) return USW_ERR_UNSUPPORTED;
   if (f->nnz_padded < 0 || f->nnz_padded >= (int64_t(1) << 32)) return USW_ERR_BAD_SHAPE;
   if (g->M > (int64_t(1) << 28)) return USW_ERR_BAD_SHAPE;   // split partial sums are addressed in 32 bits
+  // Values are read through one buffer descriptor with 32-bit byte offsets.
+  if (2 * f->nnz_padded > static_cast<int64_t>(kPastValues)) return USW_ERR_BAD_SHAPE;
   return USW_OK;
 }
 
