@@ -342,7 +342,9 @@ def quantize_rows_i4(W: np.ndarray, mask: np.ndarray):
     s64 = scales.astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint(Wd / s64[:, None])
-    q = np.where(s64[:, None] > 0, q, 0.0)
+    # Zero scale (nothing but zeros kept), NaN scale (a kept NaN makes the
+    # row maximum NaN) and a NaN quotient (inf / inf) all give code 0.
+    q = np.where((s64[:, None] > 0) & ~np.isnan(q), q, 0.0)
     q = np.clip(q, -8, 7)
     q = np.where(mask, q, 0.0).astype(np.int8)
     return scales, q

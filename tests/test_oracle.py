@@ -384,6 +384,27 @@ def test_int4_quantisation_rule():
     assert q.min() >= -8 and q.max() <= 7
 
 
+def test_int4_non_finite_weights_reading():
+    """The pages state the INT4 rule for finite weights only; the reading
+    taken: a kept NaN makes the row's maximum (so its scale) NaN and every
+    code of the row 0; a kept infinity makes the scale infinite, so finite
+    weights of the row quantise to 0 and the infinity itself (inf / inf) to 0."""
+    W = np.zeros((16, 16), dtype=np.float16)
+    W[0, :3] = [0.5, np.nan, -0.25]
+    W[1, :3] = [0.5, np.inf, -np.inf]
+    W[2, :2] = [0.7, -0.7]
+    mask = np.zeros((16, 16), bool)
+    mask[:3, :3] = True
+    scales, q = ob.quantize_rows_i4(W, mask)
+    assert np.isnan(scales[0]) and not q[0].any()
+    assert scales[1] == np.inf and not q[1].any()
+    assert q[2, 0] == 7 and q[2, 1] == -7            # finite rows unaffected
+    W[0, 1] = np.float16(0.0)                         # a NaN outside the mask is ignored
+    mask[0, 1] = False
+    scales, q = ob.quantize_rows_i4(W, mask)
+    assert scales[0] == ob.fp16_rne(0.5 / 7) and q[0, 0] == 7
+
+
 def test_int4_nibble_packing():
     q = np.array([1, -1, 7, -8, 3], dtype=np.int8)
     assert list(ob.pack_nibbles(q)) == [0xF1, 0x87, 0x03]

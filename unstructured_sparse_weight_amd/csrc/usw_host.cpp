@@ -14,6 +14,7 @@
 
 #include "usw.h"
 #include "usw_internal.h"
+#include "usw_quant.h"
 
 namespace usw {
 
@@ -35,7 +36,6 @@ usw_status make_geometry(int64_t M, int64_t K, int64_t gt_m, int64_t gt_k, Geome
   return USW_OK;
 }
 
-// fp16 bits -> double (exact).
 usw_status make_union_geometry(int64_t M, int64_t K, int64_t lt_m, int64_t lt_k, int64_t r_a, int64_t c_a,
                                UnionGeometry* g) {
   if (M <= 0 || K <= 0 || lt_m <= 0 || lt_k <= 0 || r_a <= 0 || c_a <= 0) return USW_ERR_BAD_SHAPE;
@@ -68,57 +68,6 @@ usw_status make_cbc_geometry(int64_t M, int64_t K, CbcGeometry* g) {
   g->gc = K / kCbcTK;
   g->ngt = g->gr * g->gc;
   return USW_OK;
-}
-
-double f16_to_f64(uint16_t h) {
-  const int sign = h >> 15;
-  const int e = (h >> 10) & 0x1F;
-  const int m = h & 0x3FF;
-  double v;
-  if (e == 0)
-    v = std::ldexp(static_cast<double>(m), -24);
-  else if (e == 31)
-    v = m ? NAN : INFINITY;
-  else
-    v = std::ldexp(static_cast<double>(1024 + m), e - 25);
-  return sign ? -v : v;
-}
-
-// double -> fp16 bits with a single round-to-nearest-even, from the IEEE
-// binary16 layout (1 sign, 5 exponent bits with bias 15, 10 fraction bits;
-// subnormal unit 2^-24; values at or above 65520 round to infinity).
-uint16_t f64_to_f16_rne(double x) {
-  uint64_t b;
-  std::memcpy(&b, &x, sizeof b);
-  const uint16_t sign = static_cast<uint16_t>((b >> 48) & 0x8000u);
-  const int exp = static_cast<int>((b >> 52) & 0x7FF);
-  const uint64_t frac = b & ((1ull << 52) - 1);
-  if (exp == 0x7FF) return sign | (frac ? 0x7E00 : 0x7C00);
-  if (exp == 0) return sign;  // fp64 subnormals are far below half the fp16 subnormal unit
-  const int e = exp - 1023;   // x = sig * 2^(e - 52), sig in [2^52, 2^53)
-  const uint64_t sig = frac | (1ull << 52);
-  int shift;                  // bits of sig dropped
-  if (e >= -14) {
-    shift = 42;               // keep 11 significant bits
-  } else {
-    shift = 28 - e;           // express in units of 2^-24
-    if (shift > 53) return sign;  // below 2^-25: rounds to zero
-  }
-  uint64_t r = sig >> shift;
-  const uint64_t rem = sig & ((1ull << shift) - 1);
-  const uint64_t half = 1ull << (shift - 1);
-  if (rem > half || (rem == half && (r & 1))) ++r;
-  if (e >= -14) {
-    int ee = e;
-    if (r == 2048) {          // carried into the next binade
-      r = 1024;
-      ++ee;
-    }
-    if (ee > 15) return sign | 0x7C00;
-    return sign | static_cast<uint16_t>(((ee + 15) << 10) | (r & 0x3FF));
-  }
-  // subnormal result (r == 1024 is the smallest normal, encoded the same way)
-  return sign | static_cast<uint16_t>(r);
 }
 
 namespace {
@@ -188,27 +137,24 @@ size_t values_logical_bytes(int32_t val_type, int64_t nnz) {
   return val_type == USW_VAL_F16 ? static_cast<size_t>(2 * nnz) : static_cast<size_t>((nnz + 1) / 2);
 }
 
-// INT4 row scales over the kept entries (fp64 max, fp16 RNE of max / 7):
-// writes the fp16 bits and returns their values.
+// INT4 row scales over the kept entries (largest kept magnitude as
+// sign-cleared fp16 bits, then i4_scale_bits): writes the fp16 bits and
+// returns their values.
 std::vector<double> row_scales(const uint16_t* W, const uint8_t* mask, int64_t M, int64_t K, uint16_t* scales) {
   std::vector<double> rscale(static_cast<size_t>(M), 0.0);
   parallel_for(M, [&](int64_t lo, int64_t hi) {
     for (int64_t m = lo; m < hi; ++m) {
-      double amax = 0.0;
-      for (int64_t k = 0; k < K; ++k)
-        if (is_kept(W, mask, m * K + k)) amax = std::max(amax, std::fabs(f16_to_f64(W[m * K + k])));
-      const uint16_t s = f64_to_f16_rne(amax / 7.0);
+      uint16_t amax = 0;
+      for (int64_t k = 0; k < K; ++k) {
+        const uint16_t a = W[m * K + k] & 0x7FFFu;
+        if (a > amax && is_kept(W, mask, m * K + k)) amax = a;
+      }
+      const uint16_t s = i4_scale_bits(amax);
       scales[m] = s;
       rscale[m] = f16_to_f64(s);
     }
   });
   return rscale;
-}
-
-// q = clamp(round_half_even(w / scale), -8, 7) in fp64 (0 for a zero scale).
-inline int8_t i4_code(uint16_t w, double s) {
-  if (!(s > 0.0)) return 0;
-  return static_cast<int8_t>(std::min(7.0, std::max(-8.0, std::nearbyint(f16_to_f64(w) / s))));
 }
 
 // Packs INT4 codes two per byte, element 2i in the low nibble of byte i.

@@ -44,8 +44,6 @@ usw_status make_cbc_geometry(int64_t M, int64_t K, CbcGeometry* g);
 usw_status make_union_geometry(int64_t M, int64_t K, int64_t lt_m, int64_t lt_k, int64_t r_a, int64_t c_a,
                                UnionGeometry* g);
 size_t values_alloc_bytes(int32_t val_type, int64_t nnz);
-double f16_to_f64(uint16_t h);
-uint16_t f64_to_f16_rne(double x);
 
 // Prefill (MFMA) kernel for fp16 values and N > 32: launch shape and split-K
 // factor, workspace size, launch.
