@@ -144,6 +144,49 @@ usw_status usw_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t
 usw_status usw_validate(const usw_fmt* host_fmt);
 
 /*
+ * On-device TCA-BME encoder, for a W already in GPU memory (the same
+ * construction and the same bytes as usw_encode; blog section "How TCA-BME
+ * addresses the indexing overhead").  Two calls, because the caller sizes
+ * the values buffer from NNZ in between:
+ *
+ * usw_encode_device_index: bitmaps, GroupTile offsets and, for I4, the
+ * per-row scales.
+ *   W:       device fp16 bits [M][K] row-major, 16-byte aligned (required).
+ *   mask:    device uint8 [M][K] row-major, 8-byte aligned, or NULL (kept
+ *            where W is nonzero in IEEE terms, as usw_encode_query).
+ *   bitmaps: device output [NBT]; offsets: device output [NGT+1], 4-byte
+ *            aligned, ending in offsets[NGT] = NNZ; scales: device output
+ *            fp16 [M] for I4 (ignored for F16).
+ *   stream:  a hipStream_t (NULL = the default stream); the call only
+ *            enqueues work.  Read offsets[NGT] after the stream reaches it.
+ * Errors: NULL_ARG, BAD_SHAPE (as usw_encode, and M*K >= 2^32), BAD_DTYPE,
+ * UNSUPPORTED (a GroupTile of more than 64 BitmapTiles, i.e. gt_m*gt_k >
+ * 4096), MISALIGNED, HIP.
+ */
+usw_status usw_encode_device_index(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t gt_m,
+                                   int32_t gt_k, int32_t val_type, uint64_t* bitmaps, uint32_t* offsets,
+                                   uint16_t* scales, void* stream);
+
+/*
+ * usw_encode_device_values: the values of the encoding, from W and the
+ * bitmaps, offsets and scales that usw_encode_device_index wrote (mask not
+ * needed: the bitmaps carry it).
+ *   nnz:    offsets[NGT] as read back by the caller.
+ *   values: device output of values_capacity bytes, 2-byte aligned; at least
+ *           the logical size (2*NNZ for F16, ceil(NNZ/2) for I4), with the
+ *           size usw_encode_query calls values_alloc for use by usw_spmm.
+ *           Bytes past the logical size are zeroed.
+ * Writes stay below the logical size even when nnz disagrees with offsets.
+ * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED, CAPACITY (nnz
+ * negative or above M*K, or values_capacity below the logical size),
+ * MISALIGNED, HIP.
+ */
+usw_status usw_encode_device_values(const uint16_t* W, int32_t M, int32_t K, int32_t gt_m, int32_t gt_k,
+                                    int32_t val_type, const uint64_t* bitmaps, const uint32_t* offsets,
+                                    const uint16_t* scales, int64_t nnz, void* values, size_t values_capacity,
+                                    void* stream);
+
+/*
  * Workspace bytes usw_spmm needs for this matrix and N (0 when none).  The
  * workspace starts with 32-bit counters (usw_spmm_counter_bytes of them,
  * one per output tile) followed by the fp32 partial sums of the workgroups

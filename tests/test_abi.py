@@ -75,6 +75,22 @@ def test_encoder_null_mask_matches_oracle():
     assert_same_encoding(h, o)
 
 
+def test_int4_encoder_non_finite_weights_match_oracle():
+    """Kept NaN and infinities in INT4 mode: scales and codes as the oracle's
+    reading (NaN row scale with zero codes; infinite scale, codes 0)."""
+    rng = np.random.default_rng(4)
+    W = wl.weight_normal(64, 128, rng)
+    W[rng.random(W.shape) < 0.4] = np.float16(0.0)
+    W[0, 1] = np.float16(np.nan)
+    W[1, 5] = np.float16(np.inf)
+    W[2, 7] = np.float16(-np.inf)
+    W[3, 9] = np.float16(np.nan)
+    h = usw.encode_host(W, None, (64, 64), "i4")
+    o = ob.encode_i4(W, None)
+    assert_same_encoding(h, o)
+    assert h.scales[0] == 0x7E00 and h.scales[1] == 0x7C00
+
+
 @pytest.mark.parametrize("config_id", [1, 2, 3, 4, 5])
 def test_encoder_matches_oracle_configs(config_id):
     """Bit-exact buffers on every workload (full-size shapes for the first
@@ -211,6 +227,44 @@ def test_argument_errors_return_before_launch():
                         h.offsets.copy().ctypes.data, vals.ctypes.data, 4, None) == -10
     assert L.usw_encode(W.ctypes.data, None, 256, 256, 64, 64, 2, h.bitmaps.copy().ctypes.data,
                         h.offsets.copy().ctypes.data, vals.ctypes.data, 4, None) == -1
+
+
+def test_device_encoder_argument_errors_return_before_launch():
+    """usw_encode_device_index / _values report every argument error before
+    any launch (host pointers here: a launch would fail)."""
+    L = usw.lib()
+    W = np.zeros((256, 256), np.uint16)
+    m = np.zeros((256, 256), np.uint8)
+    bm = np.zeros(1024, np.uint64)
+    off = np.zeros(64, np.uint32)
+    sc = np.zeros(256, np.uint16)
+    vals = np.zeros(4096, np.uint8)
+    w, mp, b, o, s, v = (a.ctypes.data for a in (W, m, bm, off, sc, vals))
+    idx = L.usw_encode_device_index
+    assert idx(None, mp, 256, 256, 64, 64, 1, b, o, None, None) == -1
+    assert idx(w, mp, 256, 256, 64, 64, 1, None, o, None, None) == -1
+    assert idx(w, mp, 256, 256, 64, 64, 1, b, None, None, None) == -1
+    assert idx(w, mp, 256, 256, 64, 64, 2, b, o, None, None) == -1        # I4 needs scales
+    assert idx(w, mp, 256, 250, 64, 64, 1, b, o, None, None) == -2
+    assert idx(w, mp, 256, 256, 64, 48, 1, b, o, None, None) == -2
+    assert idx(w, mp, 65536, 65536, 64, 64, 1, b, o, None, None) == -2    # M*K >= 2^32
+    assert idx(w, mp, 256, 256, 64, 64, 5, b, o, None, None) == -3
+    assert idx(w, mp, 256, 256, 128, 64, 1, b, o, None, None) == -5       # 128 BitmapTiles per GroupTile
+    assert idx(w + 2, mp, 256, 256, 64, 64, 1, b, o, None, None) == -6
+    assert idx(w, mp + 4, 256, 256, 64, 64, 1, b, o, None, None) == -6
+    assert idx(w, mp, 256, 256, 64, 64, 1, b + 4, o, None, None) == -6
+    assert idx(w, mp, 256, 256, 64, 64, 2, b, o, s + 1, None) == -6
+    val = L.usw_encode_device_values
+    assert val(None, 256, 256, 64, 64, 1, b, o, None, 10, v, 4096, None) == -1
+    assert val(w, 256, 256, 64, 64, 1, b, o, None, 10, None, 4096, None) == -1
+    assert val(w, 256, 256, 64, 64, 2, b, o, None, 10, v, 4096, None) == -1
+    assert val(w, 256, 256, 64, 64, 9, b, o, None, 10, v, 4096, None) == -3
+    assert val(w, 256, 256, 128, 64, 1, b, o, None, 10, v, 4096, None) == -5
+    assert val(w, 256, 256, 64, 64, 1, b, o, None, -1, v, 4096, None) == -10
+    assert val(w, 256, 256, 64, 64, 1, b, o, None, 256 * 256 + 1, v, 1 << 20, None) == -10
+    assert val(w, 256, 256, 64, 64, 1, b, o, None, 2049, v, 4096, None) == -10   # 2*2049 > 4096
+    assert val(w, 256, 256, 64, 64, 2, b, o, s, 8193, v, 4096, None) == -10      # ceil(8193/2) > 4096
+    assert val(w, 256, 256, 64, 64, 1, b, o, None, 10, v + 1, 4096, None) == -6
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -382,6 +382,58 @@ def encode(W, mask=None, gt=(64, 64), dtype: str = "f16", device="cuda") -> Enco
     return to_device(encode_host(W, mask, gt, dtype), device)
 
 
+def _values_alloc_bytes(val_type: int, nnz: int) -> int:
+    """Values allocation usw_spmm expects: the logical size rounded down to a
+    multiple of 16, plus 16 (as usw_encode_query reports it)."""
+    logical = 2 * nnz if val_type == USW_VAL_F16 else (nnz + 1) // 2
+    return (logical & ~15) + 16
+
+
+def encode_device(W, mask=None, gt=(64, 64), dtype: str = "f16") -> Encoding:
+    """Encode a weight that is already on the GPU (usw_encode_device_index,
+    then usw_encode_device_values) on torch's current stream.
+
+    ``W`` is a contiguous [M][K] float16 CUDA tensor; ``mask`` None keeps the
+    IEEE nonzeros, else a [M][K] bool or uint8 tensor on the same device.
+    The result has the same bytes as ``encode(W, mask, gt, dtype)``.  Reading
+    NNZ between the two calls synchronises the stream.
+    """
+    import torch
+    if not (torch.is_tensor(W) and W.is_cuda and W.dtype == torch.float16 and W.dim() == 2):
+        raise TypeError("W must be a 2-D float16 CUDA tensor")
+    W = W.contiguous()
+    M, K = W.shape
+    if mask is not None:
+        if not torch.is_tensor(mask) or mask.shape != W.shape or mask.device != W.device:
+            raise ValueError("mask must be a tensor of W's shape on W's device")
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        elif mask.dtype != torch.uint8:
+            mask = (mask != 0).view(torch.uint8)
+        mask = mask.contiguous()
+    vt = _VAL[dtype]
+    dev = W.device
+    if gt[0] <= 0 or gt[1] <= 0 or M % gt[0] or K % gt[1]:
+        raise ValueError("M and K must be multiples of the GroupTile shape")
+    ngt = (M // gt[0]) * (K // gt[1])
+    bitmaps = torch.empty(M * K // 64, dtype=torch.int64, device=dev)
+    offsets = torch.empty(ngt + 1, dtype=torch.int32, device=dev)
+    scales = torch.empty(M, dtype=torch.int16, device=dev) if vt == USW_VAL_I4 else None
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    L = lib()
+    check(L.usw_encode_device_index(W.data_ptr(), mask.data_ptr() if mask is not None else None, M, K, gt[0], gt[1],
+                                    vt, bitmaps.data_ptr(), offsets.data_ptr(),
+                                    scales.data_ptr() if scales is not None else None, st),
+          "usw_encode_device_index")
+    nnz = int(offsets[ngt].item()) & 0xFFFFFFFF
+    values = torch.empty(_values_alloc_bytes(vt, nnz), dtype=torch.uint8, device=dev)
+    check(L.usw_encode_device_values(W.data_ptr(), M, K, gt[0], gt[1], vt, bitmaps.data_ptr(), offsets.data_ptr(),
+                                     scales.data_ptr() if scales is not None else None, nnz, values.data_ptr(),
+                                     values.numel(), st),
+          "usw_encode_device_values")
+    return Encoding(M, K, gt[0], gt[1], vt, nnz, bitmaps, offsets, values, scales)
+
+
 def spmm_workspace_bytes(enc: Encoding, N: int, splits: int = 0) -> int:
     f = enc.fmt()
     b = ctypes.c_size_t()

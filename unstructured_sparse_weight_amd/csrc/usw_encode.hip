@@ -1,0 +1,368 @@
+// Device half of the TCA-BME encoder: builds the bitmap encoding of a weight
+// matrix that already sits in GPU memory, the same bytes the host encoder
+// (usw_encode) writes.
+//
+// Format: blog "SpInfer: How bitmaps make sparse LLMs actually fast", section
+// "How TCA-BME addresses the indexing overhead" (8x8 BitmapTiles in one
+// 64-bit word, 2x2 of them per 16x16 TCTile, TCTiles row-major in a
+// GroupTile; Values in that tile order; one offset per GroupTile).  INT4
+// values follow the round-to-nearest rule of usw_quant.h.
+//
+// Passes, in order on one stream:
+//   1. index:  one wave per GroupTile, one BitmapTile per lane.  The lane
+//      reads its 8 rows of 8 weights (one 16-byte load per row, or 8 mask
+//      bytes), writes the 64-bit bitmap, and the wave's popcount goes to
+//      offsets[g] as a count.
+//   2. scan:   one workgroup turns the counts in offsets[0..NGT) into the
+//      exclusive prefix offsets[0..NGT] in place.
+//   3. scales (INT4): one wave per row: the largest kept magnitude as
+//      sign-cleared fp16 bits, then i4_scale_bits.
+//   4. values: one wave per GroupTile: lane j ranks the kept weights of its
+//      BitmapTile from the bitmap (the wave's exclusive popcount prefix plus
+//      the position inside the tile) and stages the fp16 bits, or the INT4
+//      codes, in LDS in storage order; the wave then writes the GroupTile's
+//      run with consecutive lanes on consecutive elements.  INT4 byte b
+//      (codes 2b and 2b + 1) is written by the GroupTile that holds code 2b;
+//      when its run ends on an even code, the wave quantises the first kept
+//      weight of the next non-empty GroupTile for the high nibble.
+//   5. the values buffer past the logical size is zeroed.
+// Every pass is bound by HBM: W is read once by pass 1 (the mask instead
+// when one is given), once more by pass 3 for INT4, and pass 4 reads the
+// 16-byte rows that hold kept weights.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "usw.h"
+#include "usw_device.h"
+#include "usw_internal.h"
+#include "usw_quant.h"
+
+namespace {
+
+constexpr int kEThreads = 256;   // four waves, one GroupTile (or row) each
+constexpr int kEWaves = kEThreads / 64;
+constexpr int kMaxBt = 64;       // BitmapTiles per GroupTile handled by one wave
+
+struct EncGeom {
+  int K;           // row length
+  int gt_m, gt_k;  // GroupTile shape
+  int Gc;          // GroupTile columns
+  int Tc;          // TCTiles per GroupTile row
+  int bpg;         // BitmapTiles per GroupTile (<= 64)
+  int ngt;         // GroupTiles
+};
+
+// Linear index in W of the top-left element of BitmapTile j of GroupTile
+// gid: TCTile t = j / 4 (row-major in the GroupTile), BitmapTile j % 4
+// row-major in the TCTile.
+__device__ inline uint64_t bt_origin(const EncGeom& g, int gid, int j) {
+  const int gi = gid / g.Gc, gj = gid - gi * g.Gc;
+  const int t = j >> 2, b = j & 3;
+  const int ti = t / g.Tc, tj = t - ti * g.Tc;
+  const uint64_t r0 = static_cast<uint64_t>(gi) * g.gt_m + 16 * ti + 8 * (b >> 1);
+  const uint64_t c0 = static_cast<uint64_t>(gj) * g.gt_k + 16 * tj + 8 * (b & 1);
+  return r0 * static_cast<uint64_t>(g.K) + c0;
+}
+
+// Bit c set where fp16 weight c of the 8 is nonzero in IEEE terms (+0 and
+// -0 dropped, NaN and infinities kept).
+__device__ inline uint32_t nonzero8(const uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r |= static_cast<uint32_t>((w[i] & 0x7FFFu) != 0) << (2 * i);
+    r |= static_cast<uint32_t>((w[i] & 0x7FFF0000u) != 0) << (2 * i + 1);
+  }
+  return r;
+}
+
+// Bit c set where mask byte c of the 8 is nonzero.
+__device__ inline uint32_t kept8(const uint2 m) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    r |= static_cast<uint32_t>(((m.x >> (8 * c)) & 0xFFu) != 0) << c;
+    r |= static_cast<uint32_t>(((m.y >> (8 * c)) & 0xFFu) != 0) << (c + 4);
+  }
+  return r;
+}
+
+__device__ inline uint16_t half_of(const uint4 v, int c) {
+  const uint32_t w = c < 2 ? v.x : c < 4 ? v.y : c < 6 ? v.z : v.w;
+  return static_cast<uint16_t>(w >> (16 * (c & 1)));
+}
+
+template <bool MASK>
+__global__ __launch_bounds__(kEThreads) void enc_index_kernel(const uint16_t* __restrict__ W,
+                                                              const uint8_t* __restrict__ mask,
+                                                              uint64_t* __restrict__ bitmaps,
+                                                              uint32_t* __restrict__ counts, EncGeom g) {
+  const int lane = threadIdx.x & 63;
+  const int gid = blockIdx.x * kEWaves + (threadIdx.x >> 6);
+  if (gid >= g.ngt) return;
+  uint64_t bm = 0;
+  if (lane < g.bpg) {
+    const uint64_t at = bt_origin(g, gid, lane);
+    uint32_t rows[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint64_t e = at + static_cast<uint64_t>(p) * g.K;
+      rows[p] = MASK ? kept8(*reinterpret_cast<const uint2*>(mask + e))
+                     : nonzero8(*reinterpret_cast<const uint4*>(W + e));
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) bm |= static_cast<uint64_t>(rows[p]) << (8 * p);
+    bitmaps[static_cast<uint64_t>(gid) * g.bpg + lane] = bm;
+  }
+  uint32_t cnt = __popcll(bm);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  if (lane == 0) counts[gid] = cnt;
+}
+
+// In-place exclusive prefix sum of offsets[0..n), total to offsets[n]; one
+// workgroup of 1024 threads, four consecutive entries per thread per round.
+__global__ __launch_bounds__(1024) void enc_scan_kernel(uint32_t* __restrict__ offsets, int n) {
+  __shared__ uint32_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t carry = 0;
+  for (int base = 0; base < n; base += 4096) {
+    const int i0 = base + 4 * tid;
+    uint32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = i0 + k < n ? offsets[i0 + k] : 0u;
+    const uint32_t s = v[0] + v[1] + v[2] + v[3];
+    uint32_t inc = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(inc, o);
+      if (lane >= o) inc += t;
+    }
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t x = wsum[q];
+      before += q < w ? x : 0u;
+      total += x;
+    }
+    uint32_t run = carry + before + inc - s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (i0 + k < n) offsets[i0 + k] = run;
+      run += v[k];
+    }
+    carry += total;
+    __syncthreads();   // wsum is rewritten by the next round
+  }
+  if (tid == 0) offsets[n] = carry;
+}
+
+template <bool MASK>
+__global__ __launch_bounds__(kEThreads) void enc_scales_kernel(const uint16_t* __restrict__ W,
+                                                               const uint8_t* __restrict__ mask,
+                                                               uint16_t* __restrict__ scales, int M, int K) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * kEWaves + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const uint64_t row = static_cast<uint64_t>(m) * K;
+  uint32_t amax = 0;
+  for (int c = 8 * lane; c < K; c += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(W + row + c);
+    const uint32_t keep = MASK ? kept8(*reinterpret_cast<const uint2*>(mask + row + c)) : nonzero8(v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = half_of(v, i) & 0x7FFFu;
+      if ((keep >> i) & 1u) amax = a > amax ? a : amax;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t t = __shfl_xor(amax, o);
+    amax = t > amax ? t : amax;
+  }
+  if (lane == 0) scales[m] = usw::i4_scale_bits(static_cast<uint16_t>(amax));
+}
+
+// INT4 code of the first kept weight of GroupTile gid (0 when it has none).
+// Wave-uniform: every lane returns the same value.
+__device__ inline uint32_t first_code(const EncGeom& g, const uint16_t* W, const uint64_t* bitmaps,
+                                      const uint16_t* scales, int gid, int lane) {
+  const uint64_t bm = lane < g.bpg ? bitmaps[static_cast<uint64_t>(gid) * g.bpg + lane] : 0ull;
+  const uint64_t any = __ballot(bm != 0);
+  if (!any) return 0;
+  const int f = __builtin_ctzll(any);
+  const uint32_t lo = __shfl(static_cast<uint32_t>(bm), f), hi = __shfl(static_cast<uint32_t>(bm >> 32), f);
+  const uint64_t word = (static_cast<uint64_t>(hi) << 32) | lo;
+  const int p = __builtin_ctzll(word);
+  const uint64_t e = bt_origin(g, gid, f) + static_cast<uint64_t>(p >> 3) * g.K + (p & 7);
+  const uint32_t row = static_cast<uint32_t>(e / static_cast<uint64_t>(g.K));
+  return static_cast<uint32_t>(usw::i4_code(W[e], usw::f16_to_f64(scales[row]))) & 0xFu;
+}
+
+template <bool I4>
+__global__ __launch_bounds__(kEThreads) void enc_values_kernel(const uint16_t* __restrict__ W,
+                                                               const uint64_t* __restrict__ bitmaps,
+                                                               const uint32_t* __restrict__ offsets,
+                                                               const uint16_t* __restrict__ scales,
+                                                               void* __restrict__ values, EncGeom g, uint64_t nnz,
+                                                               uint64_t logical) {
+  __shared__ uint16_t stage[kEWaves][kMaxBt * 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int gid = blockIdx.x * kEWaves + wv;
+  if (gid >= g.ngt) return;
+  uint16_t* st = stage[wv];
+  const uint64_t o0 = offsets[gid];
+  const uint64_t bm = lane < g.bpg ? bitmaps[static_cast<uint64_t>(gid) * g.bpg + lane] : 0ull;
+  const uint32_t cnt = __popcll(bm);
+  uint32_t inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  const uint32_t total = __shfl(inc, 63);
+  if (bm) {
+    const uint64_t at = bt_origin(g, gid, lane);
+    uint32_t pos = inc - cnt;
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t byte = static_cast<uint32_t>(bm >> (8 * p)) & 0xFFu;
+      if (!byte) continue;
+      const uint64_t e = at + static_cast<uint64_t>(p) * g.K;
+      const uint4 v = *reinterpret_cast<const uint4*>(W + e);
+      double s = 0.0;
+      if (I4) s = usw::f16_to_f64(scales[e / static_cast<uint64_t>(g.K)]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if (!((byte >> c) & 1u)) continue;
+        const uint16_t h = half_of(v, c);
+        st[pos++] = I4 ? static_cast<uint16_t>(static_cast<uint32_t>(usw::i4_code(h, s)) & 0xFu) : h;
+      }
+    }
+  }
+  usw_dev::wave_sync();
+  if (!I4) {
+    uint16_t* out = static_cast<uint16_t*>(values);
+    for (uint32_t i = lane; i < total; i += 64)
+      if (o0 + i < nnz) out[o0 + i] = st[i];
+    return;
+  }
+  // INT4: bytes ceil(o0 / 2) .. ceil(e / 2) - 1 belong to this GroupTile.
+  const uint64_t e = o0 + total;
+  uint32_t next = 0;
+  if (total && (e & 1) && e < nnz && gid + 1 < g.ngt) {
+    // The GroupTile holding code e: the first one after gid whose run ends past e.
+    int lo = gid + 1, hi = g.ngt - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (offsets[mid + 1] > e)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    next = first_code(g, W, bitmaps, scales, lo, lane);
+  }
+  uint8_t* out = static_cast<uint8_t*>(values);
+  for (uint64_t b = (o0 + 1) / 2 + lane; b < (e + 1) / 2; b += 64) {
+    const uint32_t lo4 = st[2 * b - o0];
+    const uint32_t hi4 = 2 * b + 1 < e ? st[2 * b + 1 - o0] : next;
+    if (b < logical) out[b] = static_cast<uint8_t>(lo4 | (hi4 << 4));
+  }
+}
+
+__global__ __launch_bounds__(kEThreads) void enc_zero_kernel(uint8_t* __restrict__ p, uint64_t n) {
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kEThreads + threadIdx.x; i < n;
+       i += static_cast<uint64_t>(gridDim.x) * kEThreads)
+    p[i] = 0;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+usw_status enc_geometry(int32_t M, int32_t K, int32_t gt_m, int32_t gt_k, int32_t val_type, usw::Geometry* g,
+                        EncGeom* eg) {
+  usw_status st = usw::make_geometry(M, K, gt_m, gt_k, g);
+  if (st) return st;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (g->M * g->K >= (int64_t(1) << 32)) return USW_ERR_BAD_SHAPE;   // NNZ then fits the 32-bit offsets
+  if (g->bt_per_gt > kMaxBt) return USW_ERR_UNSUPPORTED;
+  eg->K = static_cast<int>(g->K);
+  eg->gt_m = static_cast<int>(g->gt_m);
+  eg->gt_k = static_cast<int>(g->gt_k);
+  eg->Gc = static_cast<int>(g->Gc);
+  eg->Tc = static_cast<int>(g->Tc);
+  eg->bpg = static_cast<int>(g->bt_per_gt);
+  eg->ngt = static_cast<int>(g->ngt);
+  return USW_OK;
+}
+
+unsigned blocks_for(int64_t items) { return static_cast<unsigned>((items + kEWaves - 1) / kEWaves); }
+
+}  // namespace
+
+extern "C" {
+
+usw_status usw_encode_device_index(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t gt_m,
+                                   int32_t gt_k, int32_t val_type, uint64_t* bitmaps, uint32_t* offsets,
+                                   uint16_t* scales, void* stream) {
+  if (!W || !bitmaps || !offsets) return USW_ERR_NULL_ARG;
+  usw::Geometry g;
+  EncGeom eg;
+  usw_status st = enc_geometry(M, K, gt_m, gt_k, val_type, &g, &eg);
+  if (st) return st;
+  if (val_type == USW_VAL_I4 && !scales) return USW_ERR_NULL_ARG;
+  if (!aligned(W, 16) || (mask && !aligned(mask, 8)) || !aligned(bitmaps, 8) || !aligned(offsets, 4) ||
+      (val_type == USW_VAL_I4 && !aligned(scales, 2)))
+    return USW_ERR_MISALIGNED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (mask)
+    enc_index_kernel<true><<<blocks_for(g.ngt), kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, eg);
+  else
+    enc_index_kernel<false><<<blocks_for(g.ngt), kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, eg);
+  enc_scan_kernel<<<1, 1024, 0, hs>>>(offsets, eg.ngt);
+  if (val_type == USW_VAL_I4) {
+    if (mask)
+      enc_scales_kernel<true><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K);
+    else
+      enc_scales_kernel<false><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K);
+  }
+  return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
+}
+
+usw_status usw_encode_device_values(const uint16_t* W, int32_t M, int32_t K, int32_t gt_m, int32_t gt_k,
+                                    int32_t val_type, const uint64_t* bitmaps, const uint32_t* offsets,
+                                    const uint16_t* scales, int64_t nnz, void* values, size_t values_capacity,
+                                    void* stream) {
+  if (!W || !bitmaps || !offsets || !values) return USW_ERR_NULL_ARG;
+  usw::Geometry g;
+  EncGeom eg;
+  usw_status st = enc_geometry(M, K, gt_m, gt_k, val_type, &g, &eg);
+  if (st) return st;
+  if (val_type == USW_VAL_I4 && !scales) return USW_ERR_NULL_ARG;
+  if (nnz < 0 || nnz > g.M * g.K) return USW_ERR_CAPACITY;
+  const bool i4 = val_type == USW_VAL_I4;
+  const uint64_t logical = i4 ? static_cast<uint64_t>(nnz + 1) / 2 : 2 * static_cast<uint64_t>(nnz);
+  if (values_capacity < logical) return USW_ERR_CAPACITY;
+  if (!aligned(W, 16) || !aligned(bitmaps, 8) || !aligned(offsets, 4) || !aligned(values, 2) ||
+      (i4 && !aligned(scales, 2)))
+    return USW_ERR_MISALIGNED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (i4)
+    enc_values_kernel<true><<<blocks_for(g.ngt), kEThreads, 0, hs>>>(W, bitmaps, offsets, scales, values, eg,
+                                                                      static_cast<uint64_t>(nnz), logical);
+  else
+    enc_values_kernel<false><<<blocks_for(g.ngt), kEThreads, 0, hs>>>(W, bitmaps, offsets, scales, values, eg,
+                                                                       static_cast<uint64_t>(nnz), logical);
+  const uint64_t tail = values_capacity - logical;
+  if (tail) {
+    const uint64_t blocks = (tail + kEThreads - 1) / kEThreads;
+    enc_zero_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), kEThreads, 0, hs>>>(
+        static_cast<uint8_t*>(values) + logical, tail);
+  }
+  return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
+}
+
+}  // extern "C"
