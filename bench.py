@@ -55,10 +55,11 @@ def parse():
     p.add_argument("--N", type=int, default=16)
     p.add_argument("--sparsity", type=float, default=0.5)
     p.add_argument("--dtype", default="f16", choices=["f16", "i4"])
-    p.add_argument("--format", default="tca", choices=["tca", "union", "cbc"],
+    p.add_argument("--format", default="tca", choices=["tca", "union", "cbc", "encode"],
                    help="tca: TCA-BME bitmaps (usw_spmm); union: IE-BME union-mask INT4 with 64x64 tiles and 2x2"
                         " areas (usw_union_spmm; implies --dtype i4); cbc: Tiled-CBC spMspV with dynamic pruning"
-                        " (usw_cbc_spmspv; implies --N 1 and fp16)")
+                        " (usw_cbc_spmspv; implies --N 1 and fp16); encode: the on-device TCA-BME encoder"
+                        " (usw_encode_device_index + usw_encode_device_values) of the weight, not the SpMM")
     p.add_argument("--dp", type=float, default=0.5,
                    help="cbc: fraction of activations below the pruning threshold (tau is that quantile of |x|)")
     p.add_argument("--cpu-reps", type=int, default=5)
@@ -157,6 +158,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args)
+        return
+    if args.format == "encode":
+        encode_bench(args)
         return
     dev = torch.device("cuda:0")
     union = args.format == "union"
@@ -410,6 +414,120 @@ def main():
     if cbc:
         out["config"]["dynamic_sparsity"] = args.dp
         out["config"]["tau"] = tau
+    print(json.dumps(out), flush=True)
+
+
+def encode_bench(args):
+    """Throughput of the on-device encoder on one layer (default FFN-up
+    20480 x 5120, 50% magnitude pruning, with a mask).  A step is one
+    usw_encode_device_index call (bitmaps, counts, scan, INT4 scales) and one
+    usw_encode_device_values call, given the NNZ that an untimed first run
+    read back (the work per step is the same).  Algorithmic bytes: W and the
+    mask read once, bitmaps, offsets, values and scales written once.  W and
+    mask rotate over copies of more than 512 MB in total so that reads come
+    from HBM."""
+    import torch
+    import unstructured_sparse_weight_amd as usw
+    import workloads as wl
+    import oracle.tca_bme as ob
+
+    dev = torch.device("cuda:0")
+    M, K, s = args.M, args.K, args.sparsity
+    vt = usw.USW_VAL_F16 if args.dtype == "f16" else usw.USW_VAL_I4
+    W, mask, _ = wl.config_case(5 if args.dtype == "i4" else 2, M, K, 1, s, layer_id=2)
+    in_bytes = W.nbytes + mask.nbytes
+    R = args.rotation if args.rotation > 0 else max(2, math.ceil(600e6 / in_bytes))
+    Ws = [torch.from_numpy(W).to(dev) for _ in range(R)]
+    ms = [torch.from_numpy(mask.view(np.uint8)).to(dev) for _ in range(R)]
+    first = usw.encode_device(Ws[0], ms[0], (64, 64), args.dtype)
+    torch.cuda.synchronize()
+    nnz = first.nnz
+    ngt = (M // 64) * (K // 64)
+    outs = [usw.encode_device(Ws[0], ms[0], (64, 64), args.dtype) for _ in range(R)]
+    L = usw.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i, ev=None):
+        j = i % R
+        o = outs[j]
+        sc = o.scales.data_ptr() if o.scales is not None else None
+        if ev:
+            ev[0].record(stream)
+        st = L.usw_encode_device_index(Ws[j].data_ptr(), ms[j].data_ptr(), M, K, 64, 64, vt, o.bitmaps.data_ptr(),
+                                       o.offsets.data_ptr(), sc, sp)
+        if ev:
+            ev[1].record(stream)
+        st = st or L.usw_encode_device_values(Ws[j].data_ptr(), M, K, 64, 64, vt, o.bitmaps.data_ptr(),
+                                              o.offsets.data_ptr(), sc, nnz, o.values.data_ptr(), o.values.numel(),
+                                              sp)
+        if ev:
+            ev[2].record(stream)
+        if st != 0:
+            raise RuntimeError(f"device encode failed: {st}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    idx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    val_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    for o in outs:      # every rotated copy holds the same encoding as the first
+        if not (torch.equal(o.bitmaps, first.bitmaps) and torch.equal(o.offsets, first.offsets)
+                and torch.equal(o.values, first.values)):
+            raise RuntimeError("device encode is not deterministic")
+    vbytes = 2 * nnz if args.dtype == "f16" else (nnz + 1) // 2
+    out_bytes = 8 * (M * K // 64) + 4 * (ngt + 1) + vbytes + (2 * M if args.dtype == "i4" else 0)
+    alg = in_bytes + out_bytes
+    enc_ms = idx_ms + val_ms
+    achieved = alg / (enc_ms * 1e-3) / 1e9
+    log(f"[bench] device encode: index pass {idx_ms * 1e3:.1f} us, values pass {val_ms * 1e3:.1f} us,"
+        f" {achieved:.0f} GB/s algorithmic; step {ms_step * 1e3:.1f} us")
+
+    # Host encoder (the library's multithreaded C++) and the oracle encoder,
+    # each on the whole layer once, for context.
+    t = time.perf_counter()
+    usw.encode_host(W, mask, (64, 64), args.dtype)
+    host_s = time.perf_counter() - t
+    cpu = None
+    if not args.no_cpu:
+        t = time.perf_counter()
+        (ob.encode if args.dtype == "f16" else ob.encode_i4)(W, mask)
+        oracle_s = time.perf_counter() - t
+        cpu = {"value": round(alg / oracle_s / 1e9, 3), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "sample": f"whole layer {M}x{K}: oracle encoder once ({oracle_s:.1f} s)",
+               "seconds_per_step": round(oracle_s, 3)}
+    workload = f"encode_{M}x{K}_s{s}_{args.dtype}"
+    out = {
+        "metric": f"device encode GB/s (algorithmic), TCA-BME M={M} K={K} s={int(s * 100)}% {args.dtype}",
+        "value": round(achieved, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic (seeded N(0,0.02) weights, magnitude pruning)",
+        "config": {"workload": workload, "format": "tca_bme", "M": M, "K": K, "sparsity": s, "values": args.dtype,
+                   "groupTile": "64x64", "rotation_copies": R, "launch": "eager"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "encode (index + scan + scales, then values)",
+                     "index_call_avg_us": round(idx_ms * 1e3, 2), "values_call_avg_us": round(val_ms * 1e3, 2),
+                     "alg_bytes_per_launch": int(alg)},
+        "cpu_baseline": cpu,
+        "host_encoder_seconds": round(host_s, 3),
+        "nnz": int(nnz),
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -28,7 +28,9 @@
  * INT4 values (USW_VAL_I4): per output row m a symmetric scale
  *   scale[m] = fp16_rne(max|w| over row m's kept entries / 7) and
  *   q = clamp(round_half_even(w / scale[m]), -8, 7), all in fp64 (q = 0 when
- *   the scale is 0); the dequantised weight is q * scale[m].  Element 2i of the
+ *   the scale is 0); the dequantised weight is q * scale[m].  Non-finite kept
+ *   weights: a NaN makes the row's scale NaN (0x7E00) and its codes 0; an
+ *   infinity makes the scale infinite, and inf / inf gives code 0.  Element 2i of the
  *   packed stream is the low nibble of byte i, element 2i+1 the high nibble,
  *   two's complement; a trailing high nibble is 0.  Quantisation shrinks the
  *   payload but not the bitmap metadata ("UnionSparse", motivation section on
@@ -172,7 +174,7 @@ usw_status usw_encode_device_index(const uint16_t* W, const uint8_t* mask, int32
  * bitmaps, offsets and scales that usw_encode_device_index wrote (mask not
  * needed: the bitmaps carry it).
  *   nnz:    offsets[NGT] as read back by the caller.
- *   values: device output of values_capacity bytes, 2-byte aligned; at least
+ *   values: device output of values_capacity bytes, 16-byte aligned; at least
  *           the logical size (2*NNZ for F16, ceil(NNZ/2) for I4), with the
  *           size usw_encode_query calls values_alloc for use by usw_spmm.
  *           Bytes past the logical size are zeroed.

@@ -265,6 +265,7 @@ def test_device_encoder_argument_errors_return_before_launch():
     assert val(w, 256, 256, 64, 64, 1, b, o, None, 2049, v, 4096, None) == -10   # 2*2049 > 4096
     assert val(w, 256, 256, 64, 64, 2, b, o, s, 8193, v, 4096, None) == -10      # ceil(8193/2) > 4096
     assert val(w, 256, 256, 64, 64, 1, b, o, None, 10, v + 1, 4096, None) == -6
+    assert val(w, 256, 256, 64, 64, 1, b, o, None, 10, v + 8, 4096, None) == -6
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

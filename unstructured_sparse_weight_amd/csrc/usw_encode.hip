@@ -54,16 +54,19 @@ struct EncGeom {
   int ngt;         // GroupTiles
 };
 
-// Linear index in W of the top-left element of BitmapTile j of GroupTile
-// gid: TCTile t = j / 4 (row-major in the GroupTile), BitmapTile j % 4
-// row-major in the TCTile.
-__device__ inline uint64_t bt_origin(const EncGeom& g, int gid, int j) {
+// Top-left element (row r0, column c0) of BitmapTile j of GroupTile gid:
+// TCTile t = j / 4 (row-major in the GroupTile), BitmapTile j % 4 row-major
+// in the TCTile.
+__device__ inline void bt_origin(const EncGeom& g, int gid, int j, uint32_t& r0, uint32_t& c0) {
   const int gi = gid / g.Gc, gj = gid - gi * g.Gc;
   const int t = j >> 2, b = j & 3;
   const int ti = t / g.Tc, tj = t - ti * g.Tc;
-  const uint64_t r0 = static_cast<uint64_t>(gi) * g.gt_m + 16 * ti + 8 * (b >> 1);
-  const uint64_t c0 = static_cast<uint64_t>(gj) * g.gt_k + 16 * tj + 8 * (b & 1);
-  return r0 * static_cast<uint64_t>(g.K) + c0;
+  r0 = static_cast<uint32_t>(gi * g.gt_m + 16 * ti + 8 * (b >> 1));
+  c0 = static_cast<uint32_t>(gj * g.gt_k + 16 * tj + 8 * (b & 1));
+}
+
+__device__ inline uint64_t elem(const EncGeom& g, uint32_t r, uint32_t c) {
+  return static_cast<uint64_t>(r) * static_cast<uint64_t>(g.K) + c;
 }
 
 // Bit c set where fp16 weight c of the 8 is nonzero in IEEE terms (+0 and
@@ -105,7 +108,9 @@ __global__ __launch_bounds__(kEThreads) void enc_index_kernel(const uint16_t* __
   if (gid >= g.ngt) return;
   uint64_t bm = 0;
   if (lane < g.bpg) {
-    const uint64_t at = bt_origin(g, gid, lane);
+    uint32_t r0, c0;
+    bt_origin(g, gid, lane, r0, c0);
+    const uint64_t at = elem(g, r0, c0);
     uint32_t rows[8];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -199,9 +204,10 @@ __device__ inline uint32_t first_code(const EncGeom& g, const uint16_t* W, const
   const uint32_t lo = __shfl(static_cast<uint32_t>(bm), f), hi = __shfl(static_cast<uint32_t>(bm >> 32), f);
   const uint64_t word = (static_cast<uint64_t>(hi) << 32) | lo;
   const int p = __builtin_ctzll(word);
-  const uint64_t e = bt_origin(g, gid, f) + static_cast<uint64_t>(p >> 3) * g.K + (p & 7);
-  const uint32_t row = static_cast<uint32_t>(e / static_cast<uint64_t>(g.K));
-  return static_cast<uint32_t>(usw::i4_code(W[e], usw::f16_to_f64(scales[row]))) & 0xFu;
+  uint32_t r0, c0;
+  bt_origin(g, gid, f, r0, c0);
+  const uint32_t row = r0 + (p >> 3);
+  return static_cast<uint32_t>(usw::i4_code(W[elem(g, row, c0 + (p & 7))], usw::f16_to_f64(scales[row]))) & 0xFu;
 }
 
 template <bool I4>
@@ -211,6 +217,8 @@ __global__ __launch_bounds__(kEThreads) void enc_values_kernel(const uint16_t* _
                                                                const uint16_t* __restrict__ scales,
                                                                void* __restrict__ values, EncGeom g, uint64_t nnz,
                                                                uint64_t logical) {
+  // Four waves, each stages its GroupTile's run (fp16 bits, or INT4 codes)
+  // in storage order.
   __shared__ uint16_t stage[kEWaves][kMaxBt * 64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int gid = blockIdx.x * kEWaves + wv;
@@ -227,15 +235,15 @@ __global__ __launch_bounds__(kEThreads) void enc_values_kernel(const uint16_t* _
   }
   const uint32_t total = __shfl(inc, 63);
   if (bm) {
-    const uint64_t at = bt_origin(g, gid, lane);
+    uint32_t r0, c0;
+    bt_origin(g, gid, lane, r0, c0);
     uint32_t pos = inc - cnt;
     for (int p = 0; p < 8; ++p) {
       const uint32_t byte = static_cast<uint32_t>(bm >> (8 * p)) & 0xFFu;
       if (!byte) continue;
-      const uint64_t e = at + static_cast<uint64_t>(p) * g.K;
-      const uint4 v = *reinterpret_cast<const uint4*>(W + e);
+      const uint4 v = *reinterpret_cast<const uint4*>(W + elem(g, r0 + p, c0));
       double s = 0.0;
-      if (I4) s = usw::f16_to_f64(scales[e / static_cast<uint64_t>(g.K)]);
+      if constexpr (I4) s = usw::f16_to_f64(scales[r0 + p]);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         if (!((byte >> c) & 1u)) continue;
@@ -245,32 +253,48 @@ __global__ __launch_bounds__(kEThreads) void enc_values_kernel(const uint16_t* _
     }
   }
   usw_dev::wave_sync();
-  if (!I4) {
+  if constexpr (!I4) {
+    // Element pairs on 4-byte boundaries go out as one 32-bit store; a
+    // leading element (o0 odd) and a trailing one take 16-bit stores.
     uint16_t* out = static_cast<uint16_t*>(values);
-    for (uint32_t i = lane; i < total; i += 64)
-      if (o0 + i < nnz) out[o0 + i] = st[i];
-    return;
-  }
-  // INT4: bytes ceil(o0 / 2) .. ceil(e / 2) - 1 belong to this GroupTile.
-  const uint64_t e = o0 + total;
-  uint32_t next = 0;
-  if (total && (e & 1) && e < nnz && gid + 1 < g.ngt) {
-    // The GroupTile holding code e: the first one after gid whose run ends past e.
-    int lo = gid + 1, hi = g.ngt - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (offsets[mid + 1] > e)
-        hi = mid;
-      else
-        lo = mid + 1;
+    const uint32_t head = static_cast<uint32_t>(o0 & 1);
+    if (total > head) {
+      if (head && lane == 0 && o0 < nnz) out[o0] = st[0];
+      const uint32_t pairs = (total - head) / 2;
+      for (uint32_t j = lane; j < pairs; j += 64) {
+        const uint32_t i = head + 2 * j;
+        const uint64_t at = o0 + i;
+        if (at + 1 < nnz)
+          *reinterpret_cast<uint32_t*>(out + at) = st[i] | (static_cast<uint32_t>(st[i + 1]) << 16);
+        else if (at < nnz)
+          out[at] = st[i];
+      }
+      if (((total - head) & 1) && lane == 0 && o0 + total - 1 < nnz) out[o0 + total - 1] = st[total - 1];
+    } else if (total == 1 && lane == 0 && o0 < nnz) {
+      out[o0] = st[0];
     }
-    next = first_code(g, W, bitmaps, scales, lo, lane);
-  }
-  uint8_t* out = static_cast<uint8_t*>(values);
-  for (uint64_t b = (o0 + 1) / 2 + lane; b < (e + 1) / 2; b += 64) {
-    const uint32_t lo4 = st[2 * b - o0];
-    const uint32_t hi4 = 2 * b + 1 < e ? st[2 * b + 1 - o0] : next;
-    if (b < logical) out[b] = static_cast<uint8_t>(lo4 | (hi4 << 4));
+  } else {
+    // INT4: bytes ceil(o0 / 2) .. ceil(e / 2) - 1 belong to this GroupTile.
+    const uint64_t e = o0 + total;
+    uint32_t next = 0;
+    if (total && (e & 1) && e < nnz && gid + 1 < g.ngt) {
+      // The GroupTile holding code e: the first one after gid whose run ends past e.
+      int lo = gid + 1, hi = g.ngt - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (offsets[mid + 1] > e)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      next = first_code(g, W, bitmaps, scales, lo, lane);
+    }
+    uint8_t* out = static_cast<uint8_t*>(values);
+    for (uint64_t b = (o0 + 1) / 2 + lane; b < (e + 1) / 2; b += 64) {
+      const uint32_t lo4 = st[2 * b - o0];
+      const uint32_t hi4 = 2 * b + 1 < e ? st[2 * b + 1 - o0] : next;
+      if (b < logical) out[b] = static_cast<uint8_t>(lo4 | (hi4 << 4));
+    }
   }
 }
 
@@ -346,7 +370,7 @@ usw_status usw_encode_device_values(const uint16_t* W, int32_t M, int32_t K, int
   const bool i4 = val_type == USW_VAL_I4;
   const uint64_t logical = i4 ? static_cast<uint64_t>(nnz + 1) / 2 : 2 * static_cast<uint64_t>(nnz);
   if (values_capacity < logical) return USW_ERR_CAPACITY;
-  if (!aligned(W, 16) || !aligned(bitmaps, 8) || !aligned(offsets, 4) || !aligned(values, 2) ||
+  if (!aligned(W, 16) || !aligned(bitmaps, 8) || !aligned(offsets, 4) || !aligned(values, 16) ||
       (i4 && !aligned(scales, 2)))
     return USW_ERR_MISALIGNED;
   hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -16,8 +16,13 @@
 
 namespace usw {
 
-// fp16 bits -> double (exact; NaN stays NaN, infinities stay infinite).
+// fp16 bits -> double (exact; NaN stays NaN, infinities stay infinite).  On
+// the GPU the two hardware conversions fp16 -> fp32 -> fp64, each exact; on
+// the host the bits are placed directly.
 __host__ __device__ inline double f16_to_f64(uint16_t h) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return static_cast<double>(static_cast<float>(__builtin_bit_cast(_Float16, h)));
+#else
   const uint64_t sign = static_cast<uint64_t>(h >> 15) << 63;
   const uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
   if (e == 0) {  // zero or subnormal: m units of 2^-24
@@ -26,6 +31,7 @@ __host__ __device__ inline double f16_to_f64(uint16_t h) {
   }
   const uint64_t be = e == 31 ? 0x7FFull : static_cast<uint64_t>(e) - 15 + 1023;
   return __builtin_bit_cast(double, sign | (be << 52) | (static_cast<uint64_t>(m) << 42));
+#endif
 }
 
 // double -> fp16 bits with a single round-to-nearest-even, from the IEEE
