@@ -325,6 +325,33 @@ usw_status usw_union_encode(const uint16_t* W, const uint8_t* mask, int32_t M, i
 usw_status usw_union_validate(const usw_union_fmt* host_fmt);
 
 /*
+ * Bitmap-aware row reordering of the LTs ("UnionSparse", section on
+ * bitmap-aware row reordering), an offline step before usw_union_encode.
+ * Each LT (row-major order) is solved independently: its rows are split
+ * into groups of r_a minimising the active union-mask entries (a group's
+ * grouped columns j where any of its rows is kept in any of the c_a column
+ * partitions), by the subset DP over the set of ungrouped rows that always
+ * places the smallest one.  Ties go to the first minimum with the other rows
+ * of a group in lexicographic order.  Groups are canonicalised (rows
+ * ascending, groups lexicographic) and laid out partition-wise.
+ *   W, mask:  host, as usw_union_encode_query (the mask decides what is kept).
+ *   perm:     output int32 [NLT][lt_m]: perm[t*lt_m + i] is the LT-local row
+ *             of LT t to place at row i (row p*(lt_m/r_a) + g holds the p-th
+ *             row of group g).
+ *   actives_before, actives_after: optional outputs int32 [NLT]: active
+ *             union-mask entries of each LT as given and after its
+ *             permutation (the DP minimum).
+ * The DP is exponential in lt_m: LTs of at most 20 rows are accepted.  The
+ * union kernel runs 64-row LTs, so a reordered encoding of small LTs is a
+ * storage format here (usw_union_encode of the permuted W), not a kernel input.
+ * Errors: NULL_ARG (perm NULL, or W and mask both NULL), BAD_SHAPE (as
+ * usw_union_encode_query), UNSUPPORTED (lt_m > 20).
+ */
+usw_status usw_union_reorder(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
+                             int32_t lt_k, int32_t r_a, int32_t c_a, int32_t* perm, int32_t* actives_before,
+                             int32_t* actives_after);
+
+/*
  * Workspace bytes and counter bytes of usw_union_spmm for this matrix, N and
  * split factor (splits = 0: automatic; otherwise clamped to
  * [ceil(K / (64 * 4 * 63)), max(1, K / 256)]).  The workspace starts with

@@ -233,6 +233,38 @@ def union_encode_host(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4"
                              b_val, scales)
 
 
+def union_reorder(W, mask=None, lt=(16, 64), areas=(2, 2)):
+    """Bitmap-aware row reordering of every LT (usw_union_reorder).
+
+    Returns (perm int32 [NLT][lt_m] of LT-local rows, active union entries
+    per LT before, after).  ``mask`` None keeps the IEEE nonzeros of W.
+    """
+    W = _as_numpy_f16(W)
+    M, K = W.shape
+    mask = _as_mask(mask, W.shape)
+    nlt = (M // lt[0]) * (K // lt[1]) if lt[0] > 0 and lt[1] > 0 else 0
+    perm = np.zeros((max(nlt, 1), max(lt[0], 1)), dtype=np.int32)
+    before = np.zeros(max(nlt, 1), dtype=np.int32)
+    after = np.zeros(max(nlt, 1), dtype=np.int32)
+    check(lib().usw_union_reorder(W.ctypes.data, mask.ctypes.data if mask is not None else None, M, K, lt[0], lt[1],
+                                  areas[0], areas[1], perm.ctypes.data, before.ctypes.data, after.ctypes.data),
+          "usw_union_reorder")
+    return perm[:nlt], before[:nlt], after[:nlt]
+
+
+def apply_row_permutation(W, perm, lt_m: int, lt_k: int):
+    """W with every LT's rows permuted as usw_union_reorder returned them."""
+    W = np.asarray(W)
+    M, K = W.shape
+    out = np.empty_like(W)
+    lc = K // lt_k
+    for t in range(perm.shape[0]):
+        ti, tj = divmod(t, lc)
+        rows = ti * lt_m + perm[t]
+        out[ti * lt_m:(ti + 1) * lt_m, tj * lt_k:(tj + 1) * lt_k] = W[rows, tj * lt_k:(tj + 1) * lt_k]
+    return out
+
+
 def union_validate(enc: UnionHostEncoding) -> None:
     """usw_union_validate on a host encoding (raises UswError when corrupt)."""
     f = enc.fmt()

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libusw.so")
 
-SOURCES = ["usw_host.cpp", "usw_spmm.hip", "usw_union.hip", "usw_cbc.hip", "usw_encode.hip", "usw_prefill.hip", "usw_probe.hip"]
+SOURCES = ["usw_host.cpp", "usw_reorder.cpp", "usw_spmm.hip", "usw_union.hip", "usw_cbc.hip", "usw_encode.hip", "usw_prefill.hip", "usw_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -9,11 +9,11 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
-#include <thread>
 #include <vector>
 
 #include "usw.h"
 #include "usw_internal.h"
+#include "usw_parallel.h"
 #include "usw_quant.h"
 
 namespace usw {
@@ -75,29 +75,6 @@ namespace {
 inline bool is_kept(const uint16_t* W, const uint8_t* mask, int64_t idx) {
   if (mask) return mask[idx] != 0;
   return (W[idx] & 0x7FFFu) != 0;  // +0 and -0 dropped; NaN and Inf kept
-}
-
-int worker_count(int64_t items) {
-  unsigned hw = std::thread::hardware_concurrency();
-  int n = static_cast<int>(hw ? std::min(hw, 16u) : 4u);
-  if (items < n) n = static_cast<int>(std::max<int64_t>(items, 1));
-  return n;
-}
-
-template <class F>
-void parallel_for(int64_t n, F&& f) {
-  const int nt = worker_count(n);
-  if (nt <= 1) {
-    f(static_cast<int64_t>(0), n);
-    return;
-  }
-  std::vector<std::thread> th;
-  th.reserve(nt);
-  for (int t = 0; t < nt; ++t) {
-    const int64_t lo = n * t / nt, hi = n * (t + 1) / nt;
-    th.emplace_back([&f, lo, hi] { f(lo, hi); });
-  }
-  for (auto& x : th) x.join();
 }
 
 // Visit the elements of GroupTile g in storage order: f(bt_index_in_matrix,
