@@ -325,6 +325,40 @@ usw_status usw_union_encode(const uint16_t* W, const uint8_t* mask, int32_t M, i
 usw_status usw_union_validate(const usw_union_fmt* host_fmt);
 
 /*
+ * On-device IE-BME encoder for a W already in GPU memory: the same bytes as
+ * usw_union_encode, INT4 payload only.  Two calls, as for the TCA-BME device
+ * encoder:
+ *
+ * usw_union_encode_device_index: union words, LT offsets (offsets[NLT] =
+ * payload) and per-row scales.
+ *   W:       device fp16 bits [M][K], 16-byte aligned (required).
+ *   mask:    device uint8 [M][K], 8-byte aligned, or NULL (IEEE nonzeros).
+ *   bitmaps: device output [NLT * NW]; offsets: device output [NLT+1],
+ *            4-byte aligned; scales: device output fp16 [M].
+ *
+ * usw_union_encode_device_values: the Q aligned INT4 streams of every LT,
+ * from W, the mask (a pruned weight of an active group is stored as 0) and
+ * what the first call wrote.
+ *   payload: offsets[NLT] as read back by the caller.
+ *   values:  device output of values_capacity >= ceil(payload / 2) bytes,
+ *            16-byte aligned; bytes past the logical size are zeroed.  Writes
+ *            stay below the logical size even when payload disagrees with
+ *            offsets.
+ * Both: stream as for usw_spmm.  Errors: NULL_ARG, BAD_SHAPE (as
+ * usw_union_encode_query, and M*K >= 2^32), BAD_DTYPE, UNSUPPORTED (fp16
+ * payload, LTs of more than 4096 elements, area rows not a multiple of 8
+ * positions), CAPACITY (values only: payload negative or above M*K,
+ * values_capacity too small), MISALIGNED, HIP.
+ */
+usw_status usw_union_encode_device_index(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
+                                         int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type,
+                                         uint64_t* bitmaps, uint32_t* offsets, uint16_t* scales, void* stream);
+usw_status usw_union_encode_device_values(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K,
+                                          int32_t lt_m, int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type,
+                                          const uint64_t* bitmaps, const uint32_t* offsets, const uint16_t* scales,
+                                          int64_t payload, void* values, size_t values_capacity, void* stream);
+
+/*
  * Bitmap-aware row reordering of the LTs ("UnionSparse", section on
  * bitmap-aware row reordering), an offline step before usw_union_encode.
  * Each LT (row-major order) is solved independently: its rows are split

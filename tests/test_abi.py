@@ -268,6 +268,31 @@ def test_device_encoder_argument_errors_return_before_launch():
     assert val(w, 256, 256, 64, 64, 1, b, o, None, 10, v + 8, 4096, None) == -6
 
 
+def test_device_union_encoder_argument_errors_return_before_launch():
+    L = usw.lib()
+    W = np.zeros((128, 128), np.uint16)
+    m = np.zeros((128, 128), np.uint8)
+    bm = np.zeros(256, np.uint64)
+    off = np.zeros(16, np.uint32)
+    sc = np.zeros(128, np.uint16)
+    vals = np.zeros(4096, np.uint8)
+    w, mp, b, o, s, v = (a.ctypes.data for a in (W, m, bm, off, sc, vals))
+    idx = L.usw_union_encode_device_index
+    assert idx(None, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, None) == -1
+    assert idx(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, None, None) == -1
+    assert idx(w, mp, 128, 120, 64, 64, 2, 2, 2, b, o, s, None) == -2
+    assert idx(w, mp, 128, 128, 64, 64, 2, 2, 7, b, o, s, None) == -3
+    assert idx(w, mp, 128, 128, 64, 64, 2, 2, 1, b, o, s, None) == -5         # fp16 payload
+    assert idx(w, mp, 128, 128, 128, 64, 2, 2, 2, b, o, s, None) == -5        # 8192-element LT
+    assert idx(w, mp, 128, 128, 64, 64, 1, 16, 2, b, o, s, None) == -5       # area rows of 4
+    assert idx(w + 8, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, None) == -6
+    val = L.usw_union_encode_device_values
+    assert val(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, 10, None, 4096, None) == -1
+    assert val(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, -1, v, 4096, None) == -10
+    assert val(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, 8193, v, 4096, None) == -10
+    assert val(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, 10, v + 8, 4096, None) == -6
+
+
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))

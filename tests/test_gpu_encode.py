@@ -221,3 +221,99 @@ def test_full_size_matches_host_encoder(case):
     say(f"[encode] full size {case}")
     enc = dev_encode(W, mask, (64, 64), dtype)
     assert_matches_host(enc, usw.encode_host(W, mask, (64, 64), dtype))
+
+
+# ---------------------------------------------------------------------------
+# IE-BME union-mask encoder on the device (usw_union_encode_device_*)
+# ---------------------------------------------------------------------------
+
+from oracle import ie_bme as ou  # noqa: E402
+
+
+def dev_union_encode(W, mask, lt=(64, 64), areas=(2, 2)):
+    Wt = torch.from_numpy(np.ascontiguousarray(W)).to(DEV)
+    mt = torch.from_numpy(np.ascontiguousarray(mask)).to(DEV) if mask is not None else None
+    enc = usw.union_encode_device(Wt, mt, lt, areas)
+    torch.cuda.synchronize()
+    return enc
+
+
+def assert_union_matches_oracle(enc, o):
+    assert enc.payload == o.payload
+    assert np.array_equal(enc.bitmaps.cpu().numpy().view(np.uint64)[: o.bitmaps.size], o.bitmaps)
+    assert np.array_equal(enc.offsets.cpu().numpy().view(np.uint32), o.offsets)
+    vals = enc.values.cpu().numpy()
+    vb = o.values.view(np.uint8).reshape(-1)
+    assert vals.size % 16 == 0 and vals.size >= max(16, vb.size)
+    assert np.array_equal(vals[: vb.size], vb)
+    assert not vals[vb.size:].any()
+    assert np.array_equal(enc.scales.cpu().numpy().view(np.uint16), o.scales.view(np.uint16))
+
+
+@pytest.mark.parametrize("lt,areas", [((64, 64), (2, 2)), ((32, 64), (2, 2)), ((64, 64), (1, 1)),
+                                      ((16, 64), (2, 2)), ((64, 32), (2, 1)), ((64, 64), (4, 2))])
+@pytest.mark.parametrize("density", [0.0, 0.05, 0.5, 1.0])
+def test_device_union_encoder_matches_oracle(lt, areas, density):
+    rng = np.random.default_rng(int(density * 100) + lt[0] + 3 * lt[1] + 11 * areas[0] + areas[1])
+    M, K = 128, 256
+    W = wl.weight_normal(M, K, rng)
+    W[rng.random((M, K)) < 0.05] = np.float16(0.0)
+    mask = wl.mask_bernoulli(M, K, density, rng)
+    say(f"[union encode] lt={lt} areas={areas} density={density}")
+    enc = dev_union_encode(W, mask, lt, areas)
+    assert_union_matches_oracle(enc, ou.encode_union(W, mask, lt[0], lt[1], areas[0], areas[1], ob.VAL_I4))
+
+
+def test_device_union_null_mask_and_non_finite():
+    rng = np.random.default_rng(21)
+    W = wl.weight_normal(128, 128, rng)
+    W[rng.random(W.shape) < 0.6] = np.float16(0.0)
+    W[0, 1] = np.float16(np.nan)
+    W[5, 9] = np.float16(np.inf)
+    W[70, 3] = np.float16(-0.0)
+    say("[union encode] null mask, NaN/Inf")
+    enc = dev_union_encode(W, None)
+    assert_union_matches_oracle(enc, ou.encode_union(W, None, 64, 64, 2, 2, ob.VAL_I4))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_device_union_odd_runs_across_empty_lts(seed):
+    """LTs whose payload ends on an odd code next to empty LTs, and active
+    groups whose area-0 weight is pruned (a first code of 0)."""
+    rng = np.random.default_rng(300 + seed)
+    M, K = 256, 256
+    W = wl.weight_normal(M, K, rng)
+    mask = np.zeros((M, K), bool)
+    for ti in range(M // 16):
+        for tj in range(K // 64):
+            c = rng.choice([0, 0, 1, 3, 7])
+            pos = rng.choice(16 * 64, size=c, replace=False)
+            mask[ti * 16 + pos // 64, tj * 64 + pos % 64] = True
+    say(f"[union encode] odd runs seed={seed}")
+    enc = dev_union_encode(W, mask, (16, 64), (1, 1))
+    o = ou.encode_union(W, mask, 16, 64, 1, 1, ob.VAL_I4)
+    off = o.offsets.astype(np.int64)
+    ends = off[1:-1]
+    assert ((ends % 2 == 1) & (off[2:] == ends) & (ends < o.payload)).any()
+    assert_union_matches_oracle(enc, o)
+    enc2 = dev_union_encode(W, mask, (16, 64), (2, 2))        # Q = 4: runs of even length
+    assert_union_matches_oracle(enc2, ou.encode_union(W, mask, 16, 64, 2, 2, ob.VAL_I4))
+
+
+def test_device_union_full_size_matches_host_and_runs_spmm():
+    """FFN-up 20480 x 5120 INT4 at 50%: byte-identical to the host union
+    encoder, and the union SpMM of both encodings gives the same bits."""
+    W, mask, X = wl.config_case(5, 20480, 5120, 2, 0.5)
+    say("[union encode] full size FFN-up")
+    enc = dev_union_encode(W, mask)
+    h = usw.union_encode_host(W, mask, (64, 64), (2, 2), "i4")
+    assert enc.payload == h.payload
+    assert np.array_equal(enc.bitmaps.cpu().numpy().view(np.uint64), h.bitmaps)
+    assert np.array_equal(enc.offsets.cpu().numpy().view(np.uint32), h.offsets)
+    assert np.array_equal(enc.values.cpu().numpy(), h.values)
+    assert np.array_equal(enc.scales.cpu().numpy().view(np.uint16), h.scales)
+    x = torch.from_numpy(X).to(DEV)
+    yd = usw.union_spmm(enc, x)
+    yh = usw.union_spmm(usw.union_to_device(h, DEV), x)
+    torch.cuda.synchronize()
+    assert torch.equal(yd, yh)

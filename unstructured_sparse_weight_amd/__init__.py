@@ -233,6 +233,45 @@ def union_encode_host(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4"
                              b_val, scales)
 
 
+def union_encode_device(W, mask=None, lt=(64, 64), areas=(2, 2)) -> UnionEncoding:
+    """IE-BME INT4 encoding of a weight already on the GPU
+    (usw_union_encode_device_index, then usw_union_encode_device_values) on
+    torch's current stream; the same bytes as ``union_encode(W, mask, lt,
+    areas, "i4")``.  Reading the payload size between the calls synchronises
+    the stream."""
+    import torch
+    if not (torch.is_tensor(W) and W.is_cuda and W.dtype == torch.float16 and W.dim() == 2):
+        raise TypeError("W must be a 2-D float16 CUDA tensor")
+    W = W.contiguous()
+    M, K = W.shape
+    if mask is not None:
+        if not torch.is_tensor(mask) or mask.shape != W.shape or mask.device != W.device:
+            raise ValueError("mask must be a tensor of W's shape on W's device")
+        mask = (mask.view(torch.uint8) if mask.dtype == torch.bool else (mask != 0).view(torch.uint8)
+                if mask.dtype != torch.uint8 else mask).contiguous()
+    if lt[0] <= 0 or lt[1] <= 0 or M % lt[0] or K % lt[1] or lt[0] % areas[0] or lt[1] % areas[1]:
+        raise ValueError("M, K must be multiples of the LT shape, and the LT of the area grid")
+    nlt = (M // lt[0]) * (K // lt[1])
+    nw = (lt[0] // areas[0]) * (lt[1] // areas[1]) // 64
+    dev = W.device
+    bitmaps = torch.empty(max(nlt * nw, 1), dtype=torch.int64, device=dev)
+    offsets = torch.empty(nlt + 1, dtype=torch.int32, device=dev)
+    scales = torch.empty(M, dtype=torch.int16, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    L = lib()
+    mp = mask.data_ptr() if mask is not None else None
+    args = (M, K, lt[0], lt[1], areas[0], areas[1], USW_VAL_I4)
+    check(L.usw_union_encode_device_index(W.data_ptr(), mp, *args, bitmaps.data_ptr(), offsets.data_ptr(),
+                                          scales.data_ptr(), st), "usw_union_encode_device_index")
+    payload = int(offsets[nlt].item()) & 0xFFFFFFFF
+    values = torch.empty(_values_alloc_bytes(USW_VAL_I4, payload), dtype=torch.uint8, device=dev)
+    check(L.usw_union_encode_device_values(W.data_ptr(), mp, *args, bitmaps.data_ptr(), offsets.data_ptr(),
+                                           scales.data_ptr(), payload, values.data_ptr(), values.numel(), st),
+          "usw_union_encode_device_values")
+    return UnionEncoding(M, K, lt[0], lt[1], areas[0], areas[1], USW_VAL_I4, payload, bitmaps, offsets, values,
+                         scales)
+
+
 def union_reorder(W, mask=None, lt=(16, 64), areas=(2, 2)):
     """Bitmap-aware row reordering of every LT (usw_union_reorder).
 

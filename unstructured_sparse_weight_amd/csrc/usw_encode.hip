@@ -304,6 +304,160 @@ __global__ __launch_bounds__(kEThreads) void enc_zero_kernel(uint8_t* __restrict
     p[i] = 0;
 }
 
+// ---------------------------------------------------------------------------
+// IE-BME union-mask encoding on the device ("UnionSparse", IE-BME: one union
+// bit per area-aligned group of an LT, Q aligned INT4 streams per LT, stream q
+// of LT t at offsets[t] + q P_t, P_t the LT's active positions).  The same
+// bytes as usw_union_encode; INT4 payload only (what the union kernel runs).
+// ---------------------------------------------------------------------------
+
+struct UnionGeom {
+  int K;
+  int lt_m, lt_k;
+  int am, ak;       // area shape = union-mask shape
+  int c_a, Q;
+  int lc;           // LT columns
+  int nw;           // union words per LT (<= 64)
+  int nlt;
+};
+
+// Linear index in W of position p (row-major in the area) of area q of LT t.
+__device__ inline uint64_t union_elem(const UnionGeom& g, int t, int q, int p) {
+  const int ti = t / g.lc, tj = t - ti * g.lc;
+  const int ar = q / g.c_a, ac = q - ar * g.c_a;
+  const int i = p / g.ak, j = p - i * g.ak;
+  return static_cast<uint64_t>(ti * g.lt_m + ar * g.am + i) * static_cast<uint64_t>(g.K) +
+         static_cast<uint64_t>(tj * g.lt_k + ac * g.ak + j);
+}
+
+// Kept bits of the 8 positions p0 .. p0 + 7 (one row of an area: ak is a
+// multiple of 8) of area q; v receives their fp16 bits.
+template <bool MASK>
+__device__ inline uint32_t union_chunk(const UnionGeom& g, const uint16_t* W, const uint8_t* mask, int t, int q,
+                                       int p0, uint4& v) {
+  const uint64_t e = union_elem(g, t, q, p0);
+  v = *reinterpret_cast<const uint4*>(W + e);
+  return MASK ? kept8(*reinterpret_cast<const uint2*>(mask + e)) : nonzero8(v);
+}
+
+// One wave per LT, lane w builds union word w (positions 64 w .. 64 w + 63,
+// eight rows of 8 per area, ORed over the Q areas); the LT's count is Q times
+// the popcount of its words.
+template <bool MASK>
+__global__ __launch_bounds__(kEThreads) void union_index_kernel(const uint16_t* __restrict__ W,
+                                                                const uint8_t* __restrict__ mask,
+                                                                uint64_t* __restrict__ bitmaps,
+                                                                uint32_t* __restrict__ counts, UnionGeom g) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kEWaves + (threadIdx.x >> 6);
+  if (t >= g.nlt) return;
+  uint64_t word = 0;
+  if (lane < g.nw) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint32_t bits = 0;
+      for (int q = 0; q < g.Q; ++q) {
+        uint4 v;
+        bits |= union_chunk<MASK>(g, W, mask, t, q, 64 * lane + 8 * c, v);
+      }
+      word |= static_cast<uint64_t>(bits) << (8 * c);
+    }
+    bitmaps[static_cast<uint64_t>(t) * g.nw + lane] = word;
+  }
+  uint32_t cnt = __popcll(word);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  if (lane == 0) counts[t] = static_cast<uint32_t>(g.Q) * cnt;
+}
+
+// INT4 code at stream 0, rank 0 of LT t (its first active position, area 0;
+// 0 where that weight is pruned, or when t has no active position).
+template <bool MASK>
+__device__ inline uint32_t union_first_code(const UnionGeom& g, const uint16_t* W, const uint8_t* mask,
+                                            const uint64_t* bitmaps, const uint16_t* scales, int t, int lane) {
+  const uint64_t word = lane < g.nw ? bitmaps[static_cast<uint64_t>(t) * g.nw + lane] : 0ull;
+  const uint64_t any = __ballot(word != 0);
+  if (!any) return 0;
+  const int f = __builtin_ctzll(any);
+  const uint32_t lo = __shfl(static_cast<uint32_t>(word), f), hi = __shfl(static_cast<uint32_t>(word >> 32), f);
+  const int p = 64 * f + __builtin_ctzll((static_cast<uint64_t>(hi) << 32) | lo);
+  const uint64_t e = union_elem(g, t, 0, p);
+  const bool kept = MASK ? mask[e] != 0 : (W[e] & 0x7FFFu) != 0;
+  if (!kept) return 0;
+  const uint32_t row = static_cast<uint32_t>(e / static_cast<uint64_t>(g.K));
+  return static_cast<uint32_t>(usw::i4_code(W[e], usw::f16_to_f64(scales[row]))) & 0xFu;
+}
+
+// One wave per LT: lane w ranks the active positions of word w (wave prefix
+// of the popcounts plus the position in the word) and stages, for each, the
+// Q area codes at q P + rank in LDS (0 for a pruned weight); the run of Q P
+// codes is then packed two per byte, byte b written by the LT holding code
+// 2b (the high nibble past the run: the next non-empty LT's first code).
+template <bool MASK>
+__global__ __launch_bounds__(kEThreads) void union_values_kernel(const uint16_t* __restrict__ W,
+                                                                 const uint8_t* __restrict__ mask,
+                                                                 const uint64_t* __restrict__ bitmaps,
+                                                                 const uint32_t* __restrict__ offsets,
+                                                                 const uint16_t* __restrict__ scales,
+                                                                 uint8_t* __restrict__ values, UnionGeom g,
+                                                                 uint64_t payload, uint64_t logical) {
+  __shared__ uint8_t stage[kEWaves][kMaxBt * 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * kEWaves + wv;
+  if (t >= g.nlt) return;
+  uint8_t* st = stage[wv];
+  const uint64_t o0 = offsets[t];
+  const uint64_t word = lane < g.nw ? bitmaps[static_cast<uint64_t>(t) * g.nw + lane] : 0ull;
+  const uint32_t cnt = __popcll(word);
+  uint32_t inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t x = __shfl_up(inc, o);
+    if (lane >= o) inc += x;
+  }
+  const uint32_t P = __shfl(inc, 63);
+  if (word) {
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t byte = static_cast<uint32_t>(word >> (8 * c)) & 0xFFu;
+      if (!byte) continue;
+      const uint32_t base = inc - cnt + __popcll(word & ((1ull << (8 * c)) - 1));
+      for (int q = 0; q < g.Q; ++q) {
+        uint4 v;
+        const uint32_t keep = union_chunk<MASK>(g, W, mask, t, q, 64 * lane + 8 * c, v);
+        const double s = usw::f16_to_f64(scales[union_elem(g, t, q, 64 * lane + 8 * c) / static_cast<uint64_t>(g.K)]);
+        uint32_t r = base;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (!((byte >> k) & 1u)) continue;
+          const uint32_t code =
+              ((keep >> k) & 1u) ? static_cast<uint32_t>(usw::i4_code(half_of(v, k), s)) & 0xFu : 0u;
+          st[q * P + r] = static_cast<uint8_t>(code);
+          ++r;
+        }
+      }
+    }
+  }
+  usw_dev::wave_sync();
+  const uint64_t e = o0 + static_cast<uint64_t>(g.Q) * P;
+  uint32_t next = 0;
+  if (P && (e & 1) && e < payload && t + 1 < g.nlt) {
+    int lo = t + 1, hi = g.nlt - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (offsets[mid + 1] > e)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    next = union_first_code<MASK>(g, W, mask, bitmaps, scales, lo, lane);
+  }
+  for (uint64_t b = (o0 + 1) / 2 + lane; b < (e + 1) / 2; b += 64) {
+    const uint32_t lo4 = st[2 * b - o0];
+    const uint32_t hi4 = 2 * b + 1 < e ? st[2 * b + 1 - o0] : next;
+    if (b < logical) values[b] = static_cast<uint8_t>(lo4 | (hi4 << 4));
+  }
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 usw_status enc_geometry(int32_t M, int32_t K, int32_t gt_m, int32_t gt_k, int32_t val_type, usw::Geometry* g,
@@ -320,6 +474,28 @@ usw_status enc_geometry(int32_t M, int32_t K, int32_t gt_m, int32_t gt_k, int32_
   eg->Tc = static_cast<int>(g->Tc);
   eg->bpg = static_cast<int>(g->bt_per_gt);
   eg->ngt = static_cast<int>(g->ngt);
+  return USW_OK;
+}
+
+usw_status union_enc_geometry(int32_t M, int32_t K, int32_t lt_m, int32_t lt_k, int32_t r_a, int32_t c_a,
+                              int32_t val_type, usw::UnionGeometry* g, UnionGeom* ug) {
+  usw_status st = usw::make_union_geometry(M, K, lt_m, lt_k, r_a, c_a, g);
+  if (st) return st;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (g->M * g->K >= (int64_t(1) << 32)) return USW_ERR_BAD_SHAPE;   // payload then fits the 32-bit offsets
+  // INT4 payload only; LTs of at most 4096 elements (one wave stages the
+  // whole run in LDS), areas whose rows are multiples of 8 positions.
+  if (val_type != USW_VAL_I4 || g->lt_m * g->lt_k > kMaxBt * 64 || g->ak % 8) return USW_ERR_UNSUPPORTED;
+  ug->K = static_cast<int>(g->K);
+  ug->lt_m = static_cast<int>(g->lt_m);
+  ug->lt_k = static_cast<int>(g->lt_k);
+  ug->am = static_cast<int>(g->am);
+  ug->ak = static_cast<int>(g->ak);
+  ug->c_a = static_cast<int>(g->c_a);
+  ug->Q = static_cast<int>(g->Q);
+  ug->lc = static_cast<int>(g->lc);
+  ug->nw = static_cast<int>(g->nw);
+  ug->nlt = static_cast<int>(g->nlt);
   return USW_OK;
 }
 
@@ -385,6 +561,61 @@ usw_status usw_encode_device_values(const uint16_t* W, int32_t M, int32_t K, int
     const uint64_t blocks = (tail + kEThreads - 1) / kEThreads;
     enc_zero_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), kEThreads, 0, hs>>>(
         static_cast<uint8_t*>(values) + logical, tail);
+  }
+  return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
+}
+
+usw_status usw_union_encode_device_index(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
+                                         int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type,
+                                         uint64_t* bitmaps, uint32_t* offsets, uint16_t* scales, void* stream) {
+  if (!W || !bitmaps || !offsets || !scales) return USW_ERR_NULL_ARG;
+  usw::UnionGeometry g;
+  UnionGeom ug;
+  usw_status st = union_enc_geometry(M, K, lt_m, lt_k, r_a, c_a, val_type, &g, &ug);
+  if (st) return st;
+  if (!aligned(W, 16) || (mask && !aligned(mask, 8)) || !aligned(bitmaps, 8) || !aligned(offsets, 4) ||
+      !aligned(scales, 2))
+    return USW_ERR_MISALIGNED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (mask) {
+    union_index_kernel<true><<<blocks_for(g.nlt), kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, ug);
+    enc_scan_kernel<<<1, 1024, 0, hs>>>(offsets, ug.nlt);
+    enc_scales_kernel<true><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K);
+  } else {
+    union_index_kernel<false><<<blocks_for(g.nlt), kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, ug);
+    enc_scan_kernel<<<1, 1024, 0, hs>>>(offsets, ug.nlt);
+    enc_scales_kernel<false><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K);
+  }
+  return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
+}
+
+usw_status usw_union_encode_device_values(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K,
+                                          int32_t lt_m, int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type,
+                                          const uint64_t* bitmaps, const uint32_t* offsets, const uint16_t* scales,
+                                          int64_t payload, void* values, size_t values_capacity, void* stream) {
+  if (!W || !bitmaps || !offsets || !scales || !values) return USW_ERR_NULL_ARG;
+  usw::UnionGeometry g;
+  UnionGeom ug;
+  usw_status st = union_enc_geometry(M, K, lt_m, lt_k, r_a, c_a, val_type, &g, &ug);
+  if (st) return st;
+  if (payload < 0 || payload > g.M * g.K) return USW_ERR_CAPACITY;
+  const uint64_t logical = static_cast<uint64_t>(payload + 1) / 2;
+  if (values_capacity < logical) return USW_ERR_CAPACITY;
+  if (!aligned(W, 16) || (mask && !aligned(mask, 8)) || !aligned(bitmaps, 8) || !aligned(offsets, 4) ||
+      !aligned(scales, 2) || !aligned(values, 16))
+    return USW_ERR_MISALIGNED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint8_t* vb = static_cast<uint8_t*>(values);
+  if (mask)
+    union_values_kernel<true><<<blocks_for(g.nlt), kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, scales, vb, ug,
+                                                                         static_cast<uint64_t>(payload), logical);
+  else
+    union_values_kernel<false><<<blocks_for(g.nlt), kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, scales, vb, ug,
+                                                                          static_cast<uint64_t>(payload), logical);
+  const uint64_t tail = values_capacity - logical;
+  if (tail) {
+    const uint64_t blocks = (tail + kEThreads - 1) / kEThreads;
+    enc_zero_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), kEThreads, 0, hs>>>(vb + logical, tail);
   }
   return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
 }
