@@ -55,11 +55,12 @@ def parse():
     p.add_argument("--N", type=int, default=16)
     p.add_argument("--sparsity", type=float, default=0.5)
     p.add_argument("--dtype", default="f16", choices=["f16", "i4"])
-    p.add_argument("--format", default="tca", choices=["tca", "union", "cbc", "encode"],
+    p.add_argument("--format", default="tca", choices=["tca", "union", "cbc", "encode", "encode_union"],
                    help="tca: TCA-BME bitmaps (usw_spmm); union: IE-BME union-mask INT4 with 64x64 tiles and 2x2"
                         " areas (usw_union_spmm; implies --dtype i4); cbc: Tiled-CBC spMspV with dynamic pruning"
                         " (usw_cbc_spmspv; implies --N 1 and fp16); encode: the on-device TCA-BME encoder"
-                        " (usw_encode_device_index + usw_encode_device_values) of the weight, not the SpMM")
+                        " (usw_encode_device_index + usw_encode_device_values) of the weight, not the SpMM;"
+                        " encode_union: the on-device IE-BME INT4 encoder (64x64 LTs, 2x2 areas)")
     p.add_argument("--dp", type=float, default=0.5,
                    help="cbc: fraction of activations below the pruning threshold (tau is that quantile of |x|)")
     p.add_argument("--cpu-reps", type=int, default=5)
@@ -159,7 +160,7 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args)
         return
-    if args.format == "encode":
+    if args.format in ("encode", "encode_union"):
         encode_bench(args)
         return
     dev = torch.device("cuda:0")
@@ -418,11 +419,13 @@ def main():
 
 
 def encode_bench(args):
-    """Throughput of the on-device encoder on one layer (default FFN-up
-    20480 x 5120, 50% magnitude pruning, with a mask).  A step is one
-    usw_encode_device_index call (bitmaps, counts, scan, INT4 scales) and one
-    usw_encode_device_values call, given the NNZ that an untimed first run
-    read back (the work per step is the same).  Algorithmic bytes: W and the
+    """Throughput of an on-device encoder on one layer (default FFN-up
+    20480 x 5120, 50% magnitude pruning, with a mask): TCA-BME (--format
+    encode) or IE-BME INT4 with 64x64 LTs and 2x2 areas (--format
+    encode_union).  A step is one *_encode_device_index call (bitmaps or
+    union words, counts, scan, INT4 scales) and one *_encode_device_values
+    call, given the NNZ (payload) that an untimed first run read back (the
+    work per step is the same).  Algorithmic bytes: W and the
     mask read once, bitmaps, offsets, values and scales written once.  W and
     mask rotate over copies of more than 512 MB in total so that reads come
     from HBM."""
@@ -433,17 +436,24 @@ def encode_bench(args):
 
     dev = torch.device("cuda:0")
     M, K, s = args.M, args.K, args.sparsity
+    union = args.format == "encode_union"
+    if union:
+        args.dtype = "i4"
     vt = usw.USW_VAL_F16 if args.dtype == "f16" else usw.USW_VAL_I4
     W, mask, _ = wl.config_case(5 if args.dtype == "i4" else 2, M, K, 1, s, layer_id=2)
     in_bytes = W.nbytes + mask.nbytes
     R = args.rotation if args.rotation > 0 else max(2, math.ceil(600e6 / in_bytes))
     Ws = [torch.from_numpy(W).to(dev) for _ in range(R)]
     ms = [torch.from_numpy(mask.view(np.uint8)).to(dev) for _ in range(R)]
-    first = usw.encode_device(Ws[0], ms[0], (64, 64), args.dtype)
+    if union:
+        enc_fn = lambda w, m: usw.union_encode_device(w, m, (64, 64), (2, 2))  # noqa: E731
+    else:
+        enc_fn = lambda w, m: usw.encode_device(w, m, (64, 64), args.dtype)  # noqa: E731
+    first = enc_fn(Ws[0], ms[0])
     torch.cuda.synchronize()
-    nnz = first.nnz
+    nnz = first.payload if union else first.nnz
     ngt = (M // 64) * (K // 64)
-    outs = [usw.encode_device(Ws[0], ms[0], (64, 64), args.dtype) for _ in range(R)]
+    outs = [enc_fn(Ws[0], ms[0]) for _ in range(R)]
     L = usw.lib()
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -454,13 +464,23 @@ def encode_bench(args):
         sc = o.scales.data_ptr() if o.scales is not None else None
         if ev:
             ev[0].record(stream)
-        st = L.usw_encode_device_index(Ws[j].data_ptr(), ms[j].data_ptr(), M, K, 64, 64, vt, o.bitmaps.data_ptr(),
-                                       o.offsets.data_ptr(), sc, sp)
+        if union:
+            geo = (M, K, 64, 64, 2, 2, vt)
+            st = L.usw_union_encode_device_index(Ws[j].data_ptr(), ms[j].data_ptr(), *geo, o.bitmaps.data_ptr(),
+                                                 o.offsets.data_ptr(), sc, sp)
+        else:
+            st = L.usw_encode_device_index(Ws[j].data_ptr(), ms[j].data_ptr(), M, K, 64, 64, vt,
+                                           o.bitmaps.data_ptr(), o.offsets.data_ptr(), sc, sp)
         if ev:
             ev[1].record(stream)
-        st = st or L.usw_encode_device_values(Ws[j].data_ptr(), M, K, 64, 64, vt, o.bitmaps.data_ptr(),
-                                              o.offsets.data_ptr(), sc, nnz, o.values.data_ptr(), o.values.numel(),
-                                              sp)
+        if union:
+            st = st or L.usw_union_encode_device_values(Ws[j].data_ptr(), ms[j].data_ptr(), *geo, o.bitmaps.data_ptr(),
+                                                        o.offsets.data_ptr(), sc, nnz, o.values.data_ptr(),
+                                                        o.values.numel(), sp)
+        else:
+            st = st or L.usw_encode_device_values(Ws[j].data_ptr(), M, K, 64, 64, vt, o.bitmaps.data_ptr(),
+                                                  o.offsets.data_ptr(), sc, nnz, o.values.data_ptr(),
+                                                  o.values.numel(), sp)
         if ev:
             ev[2].record(stream)
         if st != 0:
@@ -483,7 +503,8 @@ def encode_bench(args):
                 and torch.equal(o.values, first.values)):
             raise RuntimeError("device encode is not deterministic")
     vbytes = 2 * nnz if args.dtype == "f16" else (nnz + 1) // 2
-    out_bytes = 8 * (M * K // 64) + 4 * (ngt + 1) + vbytes + (2 * M if args.dtype == "i4" else 0)
+    words = first.bitmaps.numel() * 8
+    out_bytes = words + 4 * (ngt + 1) + vbytes + (2 * M if args.dtype == "i4" else 0)
     alg = in_bytes + out_bytes
     enc_ms = idx_ms + val_ms
     achieved = alg / (enc_ms * 1e-3) / 1e9
@@ -492,20 +513,28 @@ def encode_bench(args):
 
     # Host encoder (the library's multithreaded C++) and the oracle encoder,
     # each on the whole layer once, for context.
+    import oracle.ie_bme as ou
     t = time.perf_counter()
-    usw.encode_host(W, mask, (64, 64), args.dtype)
+    if union:
+        usw.union_encode_host(W, mask, (64, 64), (2, 2), "i4")
+    else:
+        usw.encode_host(W, mask, (64, 64), args.dtype)
     host_s = time.perf_counter() - t
     cpu = None
     if not args.no_cpu:
         t = time.perf_counter()
-        (ob.encode if args.dtype == "f16" else ob.encode_i4)(W, mask)
+        if union:
+            ou.encode_union(W, mask, 64, 64, 2, 2, ob.VAL_I4)
+        else:
+            (ob.encode if args.dtype == "f16" else ob.encode_i4)(W, mask)
         oracle_s = time.perf_counter() - t
         cpu = {"value": round(alg / oracle_s / 1e9, 3), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
                "kind": "oracle", "sample": f"whole layer {M}x{K}: oracle encoder once ({oracle_s:.1f} s)",
                "seconds_per_step": round(oracle_s, 3)}
-    workload = f"encode_{M}x{K}_s{s}_{args.dtype}"
+    fmt_name = "ie_bme_union_2x2" if union else "tca_bme"
+    workload = f"encode_{fmt_name}_{M}x{K}_s{s}_{args.dtype}"
     out = {
-        "metric": f"device encode GB/s (algorithmic), TCA-BME M={M} K={K} s={int(s * 100)}% {args.dtype}",
+        "metric": f"device encode GB/s (algorithmic), {fmt_name} M={M} K={K} s={int(s * 100)}% {args.dtype}",
         "value": round(achieved, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -517,8 +546,8 @@ def encode_bench(args):
         "vs_baseline": None,
         "dtype": args.dtype,
         "data": "synthetic (seeded N(0,0.02) weights, magnitude pruning)",
-        "config": {"workload": workload, "format": "tca_bme", "M": M, "K": K, "sparsity": s, "values": args.dtype,
-                   "groupTile": "64x64", "rotation_copies": R, "launch": "eager"},
+        "config": {"workload": workload, "format": fmt_name, "M": M, "K": K, "sparsity": s, "values": args.dtype,
+                   "tile": "64x64", "rotation_copies": R, "launch": "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "encode (index + scan + scales, then values)",
