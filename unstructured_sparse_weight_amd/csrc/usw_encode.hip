@@ -340,29 +340,34 @@ __device__ inline uint32_t union_chunk(const UnionGeom& g, const uint16_t* W, co
   return MASK ? kept8(*reinterpret_cast<const uint2*>(mask + e)) : nonzero8(v);
 }
 
-// One wave per LT, lane w builds union word w (positions 64 w .. 64 w + 63,
-// eight rows of 8 per area, ORed over the Q areas); the LT's count is Q times
-// the popcount of its words.
+// One wave per LT, lane w Q + q reads area q of union word w (positions
+// 64 w .. 64 w + 63, eight rows of 8) -- nw Q <= 64 since an LT holds at
+// most 4096 elements; the Q partial words are ORed through LDS by lane w Q.
+// The LT's count is Q times the popcount of its words.
 template <bool MASK>
 __global__ __launch_bounds__(kEThreads) void union_index_kernel(const uint16_t* __restrict__ W,
                                                                 const uint8_t* __restrict__ mask,
                                                                 uint64_t* __restrict__ bitmaps,
                                                                 uint32_t* __restrict__ counts, UnionGeom g) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kEWaves + (threadIdx.x >> 6);
+  __shared__ uint64_t part[kEWaves][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * kEWaves + wv;
   if (t >= g.nlt) return;
-  uint64_t word = 0;
-  if (lane < g.nw) {
+  const int w = lane / g.Q, q = lane - w * g.Q;
+  uint64_t bits = 0;
+  if (w < g.nw) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      uint32_t bits = 0;
-      for (int q = 0; q < g.Q; ++q) {
-        uint4 v;
-        bits |= union_chunk<MASK>(g, W, mask, t, q, 64 * lane + 8 * c, v);
-      }
-      word |= static_cast<uint64_t>(bits) << (8 * c);
+      uint4 v;
+      bits |= static_cast<uint64_t>(union_chunk<MASK>(g, W, mask, t, q, 64 * w + 8 * c, v)) << (8 * c);
     }
-    bitmaps[static_cast<uint64_t>(t) * g.nw + lane] = word;
+  }
+  part[wv][lane] = bits;
+  usw_dev::wave_sync();
+  uint64_t word = 0;
+  if (w < g.nw && q == 0) {
+    for (int k = 0; k < g.Q; ++k) word |= part[wv][lane + k];
+    bitmaps[static_cast<uint64_t>(t) * g.nw + w] = word;
   }
   uint32_t cnt = __popcll(word);
 #pragma unroll
@@ -388,11 +393,12 @@ __device__ inline uint32_t union_first_code(const UnionGeom& g, const uint16_t* 
   return static_cast<uint32_t>(usw::i4_code(W[e], usw::f16_to_f64(scales[row]))) & 0xFu;
 }
 
-// One wave per LT: lane w ranks the active positions of word w (wave prefix
-// of the popcounts plus the position in the word) and stages, for each, the
-// Q area codes at q P + rank in LDS (0 for a pruned weight); the run of Q P
-// codes is then packed two per byte, byte b written by the LT holding code
-// 2b (the high nibble past the run: the next non-empty LT's first code).
+// One wave per LT, lane w Q + q for area q of union word w: it ranks the
+// active positions of word w (wave prefix of the word popcounts plus the
+// position in the word) and stages the area's codes at q P + rank in LDS (0
+// for a pruned weight); the run of Q P codes is then packed two per byte,
+// byte b written by the LT holding code 2b (the high nibble past the run:
+// the next non-empty LT's first code).
 template <bool MASK>
 __global__ __launch_bounds__(kEThreads) void union_values_kernel(const uint16_t* __restrict__ W,
                                                                  const uint8_t* __restrict__ mask,
@@ -407,9 +413,10 @@ __global__ __launch_bounds__(kEThreads) void union_values_kernel(const uint16_t*
   if (t >= g.nlt) return;
   uint8_t* st = stage[wv];
   const uint64_t o0 = offsets[t];
-  const uint64_t word = lane < g.nw ? bitmaps[static_cast<uint64_t>(t) * g.nw + lane] : 0ull;
+  const int w = lane / g.Q, q = lane - w * g.Q;
+  const uint64_t word = w < g.nw ? bitmaps[static_cast<uint64_t>(t) * g.nw + w] : 0ull;
   const uint32_t cnt = __popcll(word);
-  uint32_t inc = cnt;
+  uint32_t inc = q == 0 ? cnt : 0u;   // each word counted once, by its area-0 lane
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t x = __shfl_up(inc, o);
@@ -420,20 +427,17 @@ __global__ __launch_bounds__(kEThreads) void union_values_kernel(const uint16_t*
     for (int c = 0; c < 8; ++c) {
       const uint32_t byte = static_cast<uint32_t>(word >> (8 * c)) & 0xFFu;
       if (!byte) continue;
-      const uint32_t base = inc - cnt + __popcll(word & ((1ull << (8 * c)) - 1));
-      for (int q = 0; q < g.Q; ++q) {
-        uint4 v;
-        const uint32_t keep = union_chunk<MASK>(g, W, mask, t, q, 64 * lane + 8 * c, v);
-        const double s = usw::f16_to_f64(scales[union_elem(g, t, q, 64 * lane + 8 * c) / static_cast<uint64_t>(g.K)]);
-        uint32_t r = base;
+      uint32_t r = inc - cnt + __popcll(word & ((1ull << (8 * c)) - 1));
+      uint4 v;
+      const uint32_t keep = union_chunk<MASK>(g, W, mask, t, q, 64 * w + 8 * c, v);
+      const double s = usw::f16_to_f64(scales[union_elem(g, t, q, 64 * w + 8 * c) / static_cast<uint64_t>(g.K)]);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          if (!((byte >> k) & 1u)) continue;
-          const uint32_t code =
-              ((keep >> k) & 1u) ? static_cast<uint32_t>(usw::i4_code(half_of(v, k), s)) & 0xFu : 0u;
-          st[q * P + r] = static_cast<uint8_t>(code);
-          ++r;
-        }
+      for (int k = 0; k < 8; ++k) {
+        if (!((byte >> k) & 1u)) continue;
+        const uint32_t code =
+            ((keep >> k) & 1u) ? static_cast<uint32_t>(usw::i4_code(half_of(v, k), s)) & 0xFu : 0u;
+        st[q * P + r] = static_cast<uint8_t>(code);
+        ++r;
       }
     }
   }
