@@ -247,8 +247,11 @@ def union_encode_device(W, mask=None, lt=(64, 64), areas=(2, 2)) -> UnionEncodin
     if mask is not None:
         if not torch.is_tensor(mask) or mask.shape != W.shape or mask.device != W.device:
             raise ValueError("mask must be a tensor of W's shape on W's device")
-        mask = (mask.view(torch.uint8) if mask.dtype == torch.bool else (mask != 0).view(torch.uint8)
-                if mask.dtype != torch.uint8 else mask).contiguous()
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        elif mask.dtype != torch.uint8:
+            mask = (mask != 0).view(torch.uint8)
+        mask = mask.contiguous()
     if lt[0] <= 0 or lt[1] <= 0 or M % lt[0] or K % lt[1] or lt[0] % areas[0] or lt[1] % areas[1]:
         raise ValueError("M, K must be multiples of the LT shape, and the LT of the area grid")
     nlt = (M // lt[0]) * (K // lt[1])
