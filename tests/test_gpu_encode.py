@@ -317,3 +317,39 @@ def test_device_union_full_size_matches_host_and_runs_spmm():
     yh = usw.union_spmm(usw.union_to_device(h, DEV), x)
     torch.cuda.synchronize()
     assert torch.equal(yd, yh)
+
+
+def test_device_encoder_replays_from_a_hip_graph():
+    """Both TCA-BME device-encoder calls launch kernels only (no allocation,
+    no memset), so they can be captured: three replays, with eager work and
+    synchronisation in between, each give the eager encoding's bytes."""
+    import ctypes
+    W, mask, _ = wl.config_case(1, 256, 256, 8, 0.5)
+    Wt = torch.from_numpy(W).to(DEV)
+    mt = torch.from_numpy(mask.view(np.uint8)).to(DEV)
+    ref = usw.encode_device(Wt, mt, (64, 64), "i4")
+    torch.cuda.synchronize()
+    bm = torch.zeros_like(ref.bitmaps)
+    off = torch.zeros_like(ref.offsets)
+    sc = torch.zeros_like(ref.scales)
+    vals = torch.zeros_like(ref.values)
+    L = usw.lib()
+    cap = torch.cuda.Stream(DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        sp = ctypes.c_void_p(cap.cuda_stream)
+        assert L.usw_encode_device_index(Wt.data_ptr(), mt.data_ptr(), 256, 256, 64, 64, usw.USW_VAL_I4,
+                                         bm.data_ptr(), off.data_ptr(), sc.data_ptr(), sp) == 0
+        assert L.usw_encode_device_values(Wt.data_ptr(), 256, 256, 64, 64, usw.USW_VAL_I4, bm.data_ptr(),
+                                          off.data_ptr(), sc.data_ptr(), ref.nnz, vals.data_ptr(), vals.numel(),
+                                          sp) == 0
+    for i in range(3):
+        for tns in (bm, off, sc):
+            tns.fill_(-1)
+        vals.fill_(0xAB)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"[encode] graph replay {i}")
+        assert torch.equal(bm, ref.bitmaps) and torch.equal(off, ref.offsets)
+        assert torch.equal(sc, ref.scales) and torch.equal(vals, ref.values)
