@@ -475,6 +475,34 @@ usw_status usw_cbc_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int
 usw_status usw_cbc_validate(const usw_cbc_fmt* host_fmt);
 
 /*
+ * On-device Tiled-CBC encoder for a W already in GPU memory: the same bytes
+ * as usw_cbc_encode ([SPDP] section 4.1 layout above).  Two calls:
+ *
+ * usw_cbc_encode_device_index: bitmaps, ColInfo and TileOffsets
+ * (tile_offsets[NGT] = nnz_padded when the stream reaches it).
+ *   W:    device fp16 bits [M][K], 16-byte aligned (required).
+ *   mask: device uint8 [M][K], 16-byte aligned, or NULL (IEEE nonzeros).
+ *   bitmaps [NGT * 64], tile_offsets [NGT+1], colinfo [NGT * 16]: device
+ *   outputs (8-, 4- and 4-byte aligned).
+ *
+ * usw_cbc_encode_device_values: the padded column runs, from W and what the
+ * first call wrote (the mask is not needed: the bitmaps carry it).
+ *   nnz_padded: tile_offsets[NGT] as read back by the caller.
+ *   values: device output of values_capacity >= 2 * nnz_padded bytes,
+ *           16-byte aligned; whole fp16 elements past the runs are zeroed.
+ *           Writes stay below nnz_padded elements even when it disagrees with
+ *           tile_offsets.
+ * Both: stream as for usw_spmm.  Errors: NULL_ARG, BAD_SHAPE (as
+ * usw_cbc_encode_query, and M*K >= 2^32), CAPACITY (values only), MISALIGNED,
+ * HIP.
+ */
+usw_status usw_cbc_encode_device_index(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K,
+                                       uint64_t* bitmaps, uint32_t* tile_offsets, uint32_t* colinfo, void* stream);
+usw_status usw_cbc_encode_device_values(const uint16_t* W, int32_t M, int32_t K, const uint64_t* bitmaps,
+                                        const uint32_t* tile_offsets, const uint32_t* colinfo, int64_t nnz_padded,
+                                        uint16_t* values, size_t values_capacity, void* stream);
+
+/*
  * Workspace bytes and leading counter bytes of usw_cbc_spmspv for this
  * matrix and split factor (splits = 0: automatic; otherwise clamped to
  * [1, K / 16]).  The counter bytes must be zero when a call starts; each

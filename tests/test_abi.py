@@ -293,6 +293,29 @@ def test_device_union_encoder_argument_errors_return_before_launch():
     assert val(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, 10, v + 8, 4096, None) == -6
 
 
+def test_device_cbc_encoder_argument_errors_return_before_launch():
+    L = usw.lib()
+    W = np.zeros((256, 32), np.uint16)
+    m = np.zeros((256, 32), np.uint8)
+    bm = np.zeros(128, np.uint64)
+    off = np.zeros(4, np.uint32)
+    ci = np.zeros(32, np.uint32)
+    vals = np.zeros(8192, np.uint16)
+    w, mp, b, o, c, v = (a.ctypes.data for a in (W, m, bm, off, ci, vals))
+    idx = L.usw_cbc_encode_device_index
+    assert idx(None, mp, 256, 32, b, o, c, None) == -1
+    assert idx(w, mp, 256, 32, b, o, None, None) == -1
+    assert idx(w, mp, 250, 32, b, o, c, None) == -2
+    assert idx(w, mp, 256, 24, b, o, c, None) == -2
+    assert idx(w, mp + 8, 256, 32, b, o, c, None) == -6
+    assert idx(w + 8, mp, 256, 32, b, o, c, None) == -6
+    val = L.usw_cbc_encode_device_values
+    assert val(w, 256, 32, b, o, c, 10, None, 16384, None) == -1
+    assert val(w, 256, 32, b, o, c, -1, v, 16384, None) == -10
+    assert val(w, 256, 32, b, o, c, 8193, v, 16384, None) == -10
+    assert val(w, 256, 32, b, o, c, 10, v + 8, 16384, None) == -6
+
+
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))

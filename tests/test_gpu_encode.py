@@ -353,3 +353,61 @@ def test_device_encoder_replays_from_a_hip_graph():
         say(f"[encode] graph replay {i}")
         assert torch.equal(bm, ref.bitmaps) and torch.equal(off, ref.offsets)
         assert torch.equal(sc, ref.scales) and torch.equal(vals, ref.values)
+
+
+# ---------------------------------------------------------------------------
+# Tiled-CBC encoder on the device (usw_cbc_encode_device_*)
+# ---------------------------------------------------------------------------
+
+from oracle import tiled_cbc as oc  # noqa: E402
+
+
+def assert_cbc_matches_oracle(enc, o):
+    assert enc.nnz == o.nnz and enc.nnz_padded == o.nnz_padded
+    assert np.array_equal(enc.bitmaps.cpu().numpy().view(np.uint64)[: o.bitmaps.size], o.bitmaps)
+    assert np.array_equal(enc.tile_offsets.cpu().numpy().view(np.uint32), o.tile_offsets)
+    assert np.array_equal(enc.colinfo.cpu().numpy().view(np.uint32)[: o.colinfo.size], o.colinfo)
+    vals = enc.values.cpu().numpy().view(np.uint16)
+    assert np.array_equal(vals[: o.nnz_padded], o.values.view(np.uint16)[: o.nnz_padded])
+    assert not vals[o.nnz_padded:].any()
+
+
+def dev_cbc_encode(W, mask):
+    Wt = torch.from_numpy(np.ascontiguousarray(W)).to(DEV)
+    mt = torch.from_numpy(np.ascontiguousarray(mask)).to(DEV) if mask is not None else None
+    enc = usw.cbc_encode_device(Wt, mt)
+    torch.cuda.synchronize()
+    return enc
+
+
+@pytest.mark.parametrize("shape", [(256, 16), (512, 64), (768, 96)])
+@pytest.mark.parametrize("density", [0.0, 0.03, 0.5, 1.0])
+def test_device_cbc_encoder_matches_oracle(shape, density):
+    rng = np.random.default_rng(int(density * 100) + shape[0] + shape[1])
+    W = wl.weight_normal(*shape, rng)
+    W[rng.random(shape) < 0.05] = np.float16(-0.0)
+    mask = wl.mask_bernoulli(*shape, density, rng)
+    say(f"[cbc encode] shape={shape} density={density}")
+    assert_cbc_matches_oracle(dev_cbc_encode(W, mask), oc.encode_cbc(W, mask))
+
+
+def test_device_cbc_null_mask_and_full_size():
+    rng = np.random.default_rng(31)
+    W = wl.weight_normal(512, 128, rng)
+    W[rng.random(W.shape) < 0.5] = np.float16(0.0)
+    W[3, 4] = np.float16(np.nan)
+    say("[cbc encode] null mask")
+    assert_cbc_matches_oracle(dev_cbc_encode(W, None), oc.encode_cbc(W, None))
+    W, mask, X = wl.config_case(2, 20480, 5120, 1, 0.5, layer_id=2)
+    say("[cbc encode] full size FFN-up")
+    enc = dev_cbc_encode(W, mask)
+    h = usw.cbc_encode_host(W, mask)
+    assert enc.nnz == h.nnz and enc.nnz_padded == h.nnz_padded
+    for a, b in ((enc.bitmaps, h.bitmaps), (enc.tile_offsets, h.tile_offsets), (enc.colinfo, h.colinfo)):
+        assert np.array_equal(a.cpu().numpy().view(b.dtype), b)
+    assert np.array_equal(enc.values.cpu().numpy().view(np.uint16)[: h.values.size], h.values)
+    x = torch.from_numpy(X[0]).to(DEV)
+    yd = usw.cbc_spmspv(enc, x, 0.5)
+    yh = usw.cbc_spmspv(usw.cbc_to_device(h, DEV), x, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(yd, yh)

@@ -400,6 +400,45 @@ def cbc_to_device(enc: CbcHostEncoding, device="cuda") -> CbcEncoding:
                        t(enc.tile_offsets.view(np.int32)), t(enc.colinfo.view(np.int32)), t(enc.values.view(np.int16)))
 
 
+def cbc_encode_device(W, mask=None) -> CbcEncoding:
+    """Tiled-CBC encoding of a weight already on the GPU
+    (usw_cbc_encode_device_index, then usw_cbc_encode_device_values) on
+    torch's current stream; the same bytes as ``cbc_encode(W, mask)``.
+    Reading the padded size between the calls synchronises the stream."""
+    import torch
+    if not (torch.is_tensor(W) and W.is_cuda and W.dtype == torch.float16 and W.dim() == 2):
+        raise TypeError("W must be a 2-D float16 CUDA tensor")
+    W = W.contiguous()
+    M, K = W.shape
+    if mask is not None:
+        if not torch.is_tensor(mask) or mask.shape != W.shape or mask.device != W.device:
+            raise ValueError("mask must be a tensor of W's shape on W's device")
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        elif mask.dtype != torch.uint8:
+            mask = (mask != 0).view(torch.uint8)
+        mask = mask.contiguous()
+    if M % 256 or K % 16:
+        raise ValueError("M and K must be multiples of 256 and 16")
+    ngt = (M // 256) * (K // 16)
+    dev = W.device
+    bitmaps = torch.empty(max(ngt * 64, 1), dtype=torch.int64, device=dev)
+    offs = torch.empty(ngt + 1, dtype=torch.int32, device=dev)
+    colinfo = torch.empty(max(ngt * 16, 1), dtype=torch.int32, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    L = lib()
+    check(L.usw_cbc_encode_device_index(W.data_ptr(), mask.data_ptr() if mask is not None else None, M, K,
+                                        bitmaps.data_ptr(), offs.data_ptr(), colinfo.data_ptr(), st),
+          "usw_cbc_encode_device_index")
+    npad = int(offs[ngt].item()) & 0xFFFFFFFF
+    values = torch.empty(max(npad, 8), dtype=torch.int16, device=dev)
+    check(L.usw_cbc_encode_device_values(W.data_ptr(), M, K, bitmaps.data_ptr(), offs.data_ptr(), colinfo.data_ptr(),
+                                         npad, values.data_ptr(), values.numel() * 2, st),
+          "usw_cbc_encode_device_values")
+    nnz = int((colinfo.cpu().numpy().view(np.uint32) & 0xFFFF).sum()) if ngt else 0
+    return CbcEncoding(M, K, nnz, npad, bitmaps, offs, colinfo, values)
+
+
 def cbc_encode(W, mask=None, device="cuda") -> CbcEncoding:
     """Encode on the host (usw_cbc_encode) and copy the buffers to ``device``."""
     return cbc_to_device(cbc_encode_host(W, mask), device)

@@ -31,7 +31,8 @@ EXPORTED = (
     "usw_union_encode_query", "usw_union_encode", "usw_union_validate", "usw_union_reorder",
     "usw_union_encode_device_index", "usw_union_encode_device_values", "usw_union_spmm_workspace",
     "usw_union_spmm_counter_bytes", "usw_union_spmm",
-    "usw_cbc_encode_query", "usw_cbc_encode", "usw_cbc_validate", "usw_cbc_spmspv_workspace", "usw_cbc_spmspv",
+    "usw_cbc_encode_query", "usw_cbc_encode", "usw_cbc_validate",
+    "usw_cbc_encode_device_index", "usw_cbc_encode_device_values", "usw_cbc_spmspv_workspace", "usw_cbc_spmspv",
 )
 
 
@@ -138,6 +139,10 @@ def _declare(lib):
     lib.usw_union_encode_device_values.restype = c_i32
     lib.usw_union_encode_device_values.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp,
                                                    c_vp, c_vp, c_i64, c_vp, c_sz, c_vp]
+    lib.usw_cbc_encode_device_index.restype = c_i32
+    lib.usw_cbc_encode_device_index.argtypes = [c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
+    lib.usw_cbc_encode_device_values.restype = c_i32
+    lib.usw_cbc_encode_device_values.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_sz, c_vp]
     lib.usw_union_reorder.restype = c_i32
     lib.usw_union_reorder.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
     lib.usw_encode_device_index.restype = c_i32

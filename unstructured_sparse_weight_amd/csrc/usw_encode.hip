@@ -69,6 +69,10 @@ __device__ inline uint64_t elem(const EncGeom& g, uint32_t r, uint32_t c) {
   return static_cast<uint64_t>(r) * static_cast<uint64_t>(g.K) + c;
 }
 
+__device__ inline uint64_t elem_rc(int K, int r, int c) {
+  return static_cast<uint64_t>(r) * static_cast<uint64_t>(K) + static_cast<uint64_t>(c);
+}
+
 // Bit c set where fp16 weight c of the 8 is nonzero in IEEE terms (+0 and
 // -0 dropped, NaN and infinities kept).
 __device__ inline uint32_t nonzero8(const uint4 v) {
@@ -462,6 +466,111 @@ __global__ __launch_bounds__(kEThreads) void union_values_kernel(const uint16_t*
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tiled-CBC encoding on the device ("Unified Static-Dynamic Pruning for
+// Efficient LLM Inference", section 4.1: GTiles of 256 x 16, four 64-bit
+// words per column, each column's kept weights top to bottom padded with +0
+// to a multiple of 8, ColInfo = run offset << 16 | kept count, TileOffset per
+// GTile).  The same bytes as usw_cbc_encode.
+// ---------------------------------------------------------------------------
+
+constexpr int kCbcRows = 256, kCbcCols = 16;
+
+// Kept bits of the 16 columns of one GTile row (mask bytes, or fp16 W).
+template <bool MASK>
+__device__ inline uint32_t cbc_row_bits(const uint16_t* W, const uint8_t* mask, uint64_t e, uint4& w0, uint4& w1) {
+  w0 = *reinterpret_cast<const uint4*>(W + e);
+  w1 = *reinterpret_cast<const uint4*>(W + e + 8);
+  if (MASK) {
+    const uint4 m = *reinterpret_cast<const uint4*>(mask + e);
+    return kept8(make_uint2(m.x, m.y)) | (kept8(make_uint2(m.z, m.w)) << 8);
+  }
+  return nonzero8(w0) | (nonzero8(w1) << 8);
+}
+
+// One wave per GTile; lane l holds rows l, 64 + l, 128 + l, 192 + l.  Word q
+// of column c is the wave's ballot of column c's kept bit over rows 64 q + l;
+// lane 4 c + q stores it.  Column counts, their padded runs and ColInfo are
+// wave-uniform; the GTile's padded total goes to counts[t].
+template <bool MASK>
+__global__ __launch_bounds__(kEThreads) void cbc_index_kernel(const uint16_t* __restrict__ W,
+                                                              const uint8_t* __restrict__ mask,
+                                                              uint64_t* __restrict__ bitmaps,
+                                                              uint32_t* __restrict__ counts,
+                                                              uint32_t* __restrict__ colinfo, int K, int gc, int ngt) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kEWaves + (threadIdx.x >> 6);
+  if (t >= ngt) return;
+  const int ti = t / gc, tj = t - ti * gc;
+  uint32_t bits[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint4 w0, w1;
+    bits[q] = cbc_row_bits<MASK>(W, mask, elem_rc(K, ti * kCbcRows + 64 * q + lane, tj * kCbcCols), w0, w1);
+  }
+  uint64_t mine = 0;
+  uint32_t run = 0, info = 0;
+  for (int c = 0; c < kCbcCols; ++c) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t word = __ballot((bits[q] >> c) & 1u);
+      n += __popcll(word);
+      if (lane == 4 * c + q) mine = word;
+    }
+    if (lane == c) info = (run << 16) | n;
+    run += (n + 7) & ~7u;
+  }
+  bitmaps[static_cast<uint64_t>(t) * 64 + lane] = mine;
+  if (lane < kCbcCols) colinfo[static_cast<uint64_t>(t) * kCbcCols + lane] = info;
+  if (lane == 0) counts[t] = run;
+}
+
+// One wave per GTile, lane l on rows l, 64 + l, 128 + l, 192 + l again: for
+// each column the kept weight of row 64 q + l goes to TileOffset + run +
+// (kept rows above it: earlier words' popcounts plus v_mbcnt of its word),
+// and lanes 0 .. pad - 1 write the column's +0 padding.
+__global__ __launch_bounds__(kEThreads) void cbc_values_kernel(const uint16_t* __restrict__ W,
+                                                               const uint64_t* __restrict__ bitmaps,
+                                                               const uint32_t* __restrict__ toff,
+                                                               const uint32_t* __restrict__ colinfo,
+                                                               uint16_t* __restrict__ values, int K, int gc, int ngt,
+                                                               uint64_t nvals) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kEWaves + (threadIdx.x >> 6);
+  if (t >= ngt) return;
+  const int ti = t / gc, tj = t - ti * gc;
+  const uint64_t base = toff[t];
+  const uint64_t myword = bitmaps[static_cast<uint64_t>(t) * 64 + lane];
+  const uint32_t myinfo = lane < kCbcCols ? colinfo[static_cast<uint64_t>(t) * kCbcCols + lane] : 0u;
+  uint4 w[4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint64_t e = elem_rc(K, ti * kCbcRows + 64 * q + lane, tj * kCbcCols);
+    w[q][0] = *reinterpret_cast<const uint4*>(W + e);
+    w[q][1] = *reinterpret_cast<const uint4*>(W + e + 8);
+  }
+  for (int c = 0; c < kCbcCols; ++c) {
+    const uint32_t info = __shfl(myinfo, c);
+    const uint64_t col = base + (info >> 16);
+    const uint32_t n = info & 0xFFFFu;
+    uint32_t above = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = __shfl(static_cast<uint32_t>(myword), 4 * c + q);
+      const uint32_t hi = __shfl(static_cast<uint32_t>(myword >> 32), 4 * c + q);
+      const uint64_t word = (static_cast<uint64_t>(hi) << 32) | lo;
+      if ((word >> lane) & 1ull) {
+        const uint32_t rank = above + __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+        if (col + rank < nvals) values[col + rank] = half_of(w[q][c >> 3], c & 7);
+      }
+      above += __popcll(word);
+    }
+    const uint32_t pad = ((n + 7) & ~7u) - n;
+    if (static_cast<uint32_t>(lane) < pad && col + n + lane < nvals) values[col + n + lane] = 0;
+  }
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 usw_status enc_geometry(int32_t M, int32_t K, int32_t gt_m, int32_t gt_k, int32_t val_type, usw::Geometry* g,
@@ -620,6 +729,57 @@ usw_status usw_union_encode_device_values(const uint16_t* W, const uint8_t* mask
   if (tail) {
     const uint64_t blocks = (tail + kEThreads - 1) / kEThreads;
     enc_zero_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), kEThreads, 0, hs>>>(vb + logical, tail);
+  }
+  return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
+}
+
+usw_status usw_cbc_encode_device_index(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K,
+                                       uint64_t* bitmaps, uint32_t* tile_offsets, uint32_t* colinfo, void* stream) {
+  if (!W || !bitmaps || !tile_offsets || !colinfo) return USW_ERR_NULL_ARG;
+  usw::CbcGeometry g;
+  usw_status st = usw::make_cbc_geometry(M, K, &g);
+  if (st) return st;
+  if (g.M * g.K >= (int64_t(1) << 32)) return USW_ERR_BAD_SHAPE;
+  if (!aligned(W, 16) || (mask && !aligned(mask, 16)) || !aligned(bitmaps, 8) || !aligned(tile_offsets, 4) ||
+      !aligned(colinfo, 4))
+    return USW_ERR_MISALIGNED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int gc = static_cast<int>(g.gc), ngt = static_cast<int>(g.ngt);
+  if (mask)
+    cbc_index_kernel<true><<<blocks_for(g.ngt), kEThreads, 0, hs>>>(W, mask, bitmaps, tile_offsets, colinfo, K, gc,
+                                                                     ngt);
+  else
+    cbc_index_kernel<false><<<blocks_for(g.ngt), kEThreads, 0, hs>>>(W, mask, bitmaps, tile_offsets, colinfo, K, gc,
+                                                                      ngt);
+  enc_scan_kernel<<<1, 1024, 0, hs>>>(tile_offsets, ngt);
+  return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
+}
+
+usw_status usw_cbc_encode_device_values(const uint16_t* W, int32_t M, int32_t K, const uint64_t* bitmaps,
+                                        const uint32_t* tile_offsets, const uint32_t* colinfo, int64_t nnz_padded,
+                                        uint16_t* values, size_t values_capacity, void* stream) {
+  if (!W || !bitmaps || !tile_offsets || !colinfo || !values) return USW_ERR_NULL_ARG;
+  usw::CbcGeometry g;
+  usw_status st = usw::make_cbc_geometry(M, K, &g);
+  if (st) return st;
+  if (g.M * g.K >= (int64_t(1) << 32)) return USW_ERR_BAD_SHAPE;
+  if (nnz_padded < 0 || nnz_padded > g.M * g.K) return USW_ERR_CAPACITY;
+  if (values_capacity < 2 * static_cast<uint64_t>(nnz_padded)) return USW_ERR_CAPACITY;
+  if (!aligned(W, 16) || !aligned(bitmaps, 8) || !aligned(tile_offsets, 4) || !aligned(colinfo, 4) ||
+      !aligned(values, 16))
+    return USW_ERR_MISALIGNED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  cbc_values_kernel<<<blocks_for(g.ngt), kEThreads, 0, hs>>>(W, bitmaps, tile_offsets, colinfo, values,
+                                                             static_cast<int>(K), static_cast<int>(g.gc),
+                                                             static_cast<int>(g.ngt),
+                                                             static_cast<uint64_t>(nnz_padded));
+  // Whole fp16 elements past the padded runs are zeroed (a trailing odd byte
+  // of the capacity is left alone, as the host encoder does).
+  const uint64_t tail = (values_capacity / 2 - static_cast<uint64_t>(nnz_padded)) * 2;
+  if (tail) {
+    const uint64_t blocks = (tail + kEThreads - 1) / kEThreads;
+    enc_zero_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), kEThreads, 0, hs>>>(
+        reinterpret_cast<uint8_t*>(values + nnz_padded), tail);
   }
   return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
 }
