@@ -55,12 +55,13 @@ def parse():
     p.add_argument("--N", type=int, default=16)
     p.add_argument("--sparsity", type=float, default=0.5)
     p.add_argument("--dtype", default="f16", choices=["f16", "i4"])
-    p.add_argument("--format", default="tca", choices=["tca", "union", "cbc", "encode", "encode_union"],
+    p.add_argument("--format", default="tca", choices=["tca", "union", "cbc", "encode", "encode_union", "encode_cbc"],
                    help="tca: TCA-BME bitmaps (usw_spmm); union: IE-BME union-mask INT4 with 64x64 tiles and 2x2"
                         " areas (usw_union_spmm; implies --dtype i4); cbc: Tiled-CBC spMspV with dynamic pruning"
                         " (usw_cbc_spmspv; implies --N 1 and fp16); encode: the on-device TCA-BME encoder"
                         " (usw_encode_device_index + usw_encode_device_values) of the weight, not the SpMM;"
-                        " encode_union: the on-device IE-BME INT4 encoder (64x64 LTs, 2x2 areas)")
+                        " encode_union: the on-device IE-BME INT4 encoder (64x64 LTs, 2x2 areas); encode_cbc: the"
+                        " on-device Tiled-CBC encoder")
     p.add_argument("--dp", type=float, default=0.5,
                    help="cbc: fraction of activations below the pruning threshold (tau is that quantile of |x|)")
     p.add_argument("--cpu-reps", type=int, default=5)
@@ -160,7 +161,7 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args)
         return
-    if args.format in ("encode", "encode_union"):
+    if args.format in ("encode", "encode_union", "encode_cbc"):
         encode_bench(args)
         return
     dev = torch.device("cuda:0")
@@ -437,8 +438,11 @@ def encode_bench(args):
     dev = torch.device("cuda:0")
     M, K, s = args.M, args.K, args.sparsity
     union = args.format == "encode_union"
+    cbc = args.format == "encode_cbc"
     if union:
         args.dtype = "i4"
+    if cbc:
+        args.dtype = "f16"
     vt = usw.USW_VAL_F16 if args.dtype == "f16" else usw.USW_VAL_I4
     W, mask, _ = wl.config_case(5 if args.dtype == "i4" else 2, M, K, 1, s, layer_id=2)
     in_bytes = W.nbytes + mask.nbytes
@@ -447,12 +451,14 @@ def encode_bench(args):
     ms = [torch.from_numpy(mask.view(np.uint8)).to(dev) for _ in range(R)]
     if union:
         enc_fn = lambda w, m: usw.union_encode_device(w, m, (64, 64), (2, 2))  # noqa: E731
+    elif cbc:
+        enc_fn = lambda w, m: usw.cbc_encode_device(w, m)  # noqa: E731
     else:
         enc_fn = lambda w, m: usw.encode_device(w, m, (64, 64), args.dtype)  # noqa: E731
     first = enc_fn(Ws[0], ms[0])
     torch.cuda.synchronize()
-    nnz = first.payload if union else first.nnz
-    ngt = (M // 64) * (K // 64)
+    nnz = first.payload if union else (first.nnz_padded if cbc else first.nnz)
+    ngt = (M // 256) * (K // 16) if cbc else (M // 64) * (K // 64)
     outs = [enc_fn(Ws[0], ms[0]) for _ in range(R)]
     L = usw.lib()
     stream = torch.cuda.current_stream(dev)
@@ -461,10 +467,13 @@ def encode_bench(args):
     def step(i, ev=None):
         j = i % R
         o = outs[j]
-        sc = o.scales.data_ptr() if o.scales is not None else None
+        sc = o.scales.data_ptr() if getattr(o, "scales", None) is not None else None
         if ev:
             ev[0].record(stream)
-        if union:
+        if cbc:
+            st = L.usw_cbc_encode_device_index(Ws[j].data_ptr(), ms[j].data_ptr(), M, K, o.bitmaps.data_ptr(),
+                                               o.tile_offsets.data_ptr(), o.colinfo.data_ptr(), sp)
+        elif union:
             geo = (M, K, 64, 64, 2, 2, vt)
             st = L.usw_union_encode_device_index(Ws[j].data_ptr(), ms[j].data_ptr(), *geo, o.bitmaps.data_ptr(),
                                                  o.offsets.data_ptr(), sc, sp)
@@ -473,7 +482,11 @@ def encode_bench(args):
                                            o.bitmaps.data_ptr(), o.offsets.data_ptr(), sc, sp)
         if ev:
             ev[1].record(stream)
-        if union:
+        if cbc:
+            st = st or L.usw_cbc_encode_device_values(Ws[j].data_ptr(), M, K, o.bitmaps.data_ptr(),
+                                                      o.tile_offsets.data_ptr(), o.colinfo.data_ptr(), nnz,
+                                                      o.values.data_ptr(), o.values.numel() * 2, sp)
+        elif union:
             st = st or L.usw_union_encode_device_values(Ws[j].data_ptr(), ms[j].data_ptr(), *geo, o.bitmaps.data_ptr(),
                                                         o.offsets.data_ptr(), sc, nnz, o.values.data_ptr(),
                                                         o.values.numel(), sp)
@@ -498,13 +511,14 @@ def encode_bench(args):
     idx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     val_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_step = (t1 - t0) * 1e3 / args.steps
+    offs_of = (lambda e: e.tile_offsets) if cbc else (lambda e: e.offsets)  # noqa: E731
     for o in outs:      # every rotated copy holds the same encoding as the first
-        if not (torch.equal(o.bitmaps, first.bitmaps) and torch.equal(o.offsets, first.offsets)
+        if not (torch.equal(o.bitmaps, first.bitmaps) and torch.equal(offs_of(o), offs_of(first))
                 and torch.equal(o.values, first.values)):
             raise RuntimeError("device encode is not deterministic")
     vbytes = 2 * nnz if args.dtype == "f16" else (nnz + 1) // 2
     words = first.bitmaps.numel() * 8
-    out_bytes = words + 4 * (ngt + 1) + vbytes + (2 * M if args.dtype == "i4" else 0)
+    out_bytes = words + 4 * (ngt + 1) + vbytes + (2 * M if args.dtype == "i4" else 0) + (64 * ngt if cbc else 0)
     alg = in_bytes + out_bytes
     enc_ms = idx_ms + val_ms
     achieved = alg / (enc_ms * 1e-3) / 1e9
@@ -517,6 +531,8 @@ def encode_bench(args):
     t = time.perf_counter()
     if union:
         usw.union_encode_host(W, mask, (64, 64), (2, 2), "i4")
+    elif cbc:
+        usw.cbc_encode_host(W, mask)
     else:
         usw.encode_host(W, mask, (64, 64), args.dtype)
     host_s = time.perf_counter() - t
@@ -525,13 +541,16 @@ def encode_bench(args):
         t = time.perf_counter()
         if union:
             ou.encode_union(W, mask, 64, 64, 2, 2, ob.VAL_I4)
+        elif cbc:
+            import oracle.tiled_cbc as oc
+            oc.encode_cbc(W, mask)
         else:
             (ob.encode if args.dtype == "f16" else ob.encode_i4)(W, mask)
         oracle_s = time.perf_counter() - t
         cpu = {"value": round(alg / oracle_s / 1e9, 3), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
                "kind": "oracle", "sample": f"whole layer {M}x{K}: oracle encoder once ({oracle_s:.1f} s)",
                "seconds_per_step": round(oracle_s, 3)}
-    fmt_name = "ie_bme_union_2x2" if union else "tca_bme"
+    fmt_name = "ie_bme_union_2x2" if union else ("tiled_cbc" if cbc else "tca_bme")
     workload = f"encode_{fmt_name}_{M}x{K}_s{s}_{args.dtype}"
     out = {
         "metric": f"device encode GB/s (algorithmic), {fmt_name} M={M} K={K} s={int(s * 100)}% {args.dtype}",
@@ -547,7 +566,7 @@ def encode_bench(args):
         "dtype": args.dtype,
         "data": "synthetic (seeded N(0,0.02) weights, magnitude pruning)",
         "config": {"workload": workload, "format": fmt_name, "M": M, "K": K, "sparsity": s, "values": args.dtype,
-                   "tile": "64x64", "rotation_copies": R, "launch": "eager"},
+                   "tile": "256x16" if cbc else "64x64", "rotation_copies": R, "launch": "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "encode (index + scan + scales, then values)",

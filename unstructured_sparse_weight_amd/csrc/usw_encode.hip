@@ -536,9 +536,13 @@ __global__ __launch_bounds__(kEThreads) void cbc_values_kernel(const uint16_t* _
                                                                const uint32_t* __restrict__ colinfo,
                                                                uint16_t* __restrict__ values, int K, int gc, int ngt,
                                                                uint64_t nvals) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kEWaves + (threadIdx.x >> 6);
+  // The GTile's padded runs are staged in LDS and written out in 16-byte
+  // pieces: every run is a multiple of 8 values, so each TileOffset is too.
+  __shared__ __align__(16) uint16_t stage[kEWaves][kCbcRows * kCbcCols];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * kEWaves + wv;
   if (t >= ngt) return;
+  uint16_t* st = stage[wv];
   const int ti = t / gc, tj = t - ti * gc;
   const uint64_t base = toff[t];
   const uint64_t myword = bitmaps[static_cast<uint64_t>(t) * 64 + lane];
@@ -550,25 +554,34 @@ __global__ __launch_bounds__(kEThreads) void cbc_values_kernel(const uint16_t* _
     w[q][0] = *reinterpret_cast<const uint4*>(W + e);
     w[q][1] = *reinterpret_cast<const uint4*>(W + e + 8);
   }
+  // Column c's ColInfo and words sit in lanes c and 4 c + q: the lane index
+  // is wave-uniform, so v_readlane brings them into scalar registers.
+  uint32_t total = 0;
   for (int c = 0; c < kCbcCols; ++c) {
-    const uint32_t info = __shfl(myinfo, c);
-    const uint64_t col = base + (info >> 16);
+    const uint32_t info = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(myinfo), c));
+    const uint32_t col = info >> 16;
     const uint32_t n = info & 0xFFFFu;
     uint32_t above = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = __shfl(static_cast<uint32_t>(myword), 4 * c + q);
-      const uint32_t hi = __shfl(static_cast<uint32_t>(myword >> 32), 4 * c + q);
+      const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(myword), 4 * c + q));
+      const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(myword >> 32), 4 * c + q));
       const uint64_t word = (static_cast<uint64_t>(hi) << 32) | lo;
       if ((word >> lane) & 1ull) {
         const uint32_t rank = above + __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-        if (col + rank < nvals) values[col + rank] = half_of(w[q][c >> 3], c & 7);
+        const uint4 v = c < 8 ? w[q][0] : w[q][1];   // a select, not a dynamic register index
+        if (col + rank < kCbcRows * kCbcCols) st[col + rank] = half_of(v, c & 7);
       }
       above += __popcll(word);
     }
-    const uint32_t pad = ((n + 7) & ~7u) - n;
-    if (static_cast<uint32_t>(lane) < pad && col + n + lane < nvals) values[col + n + lane] = 0;
+    const uint32_t np = (n + 7) & ~7u;
+    if (static_cast<uint32_t>(lane) < np - n && col + n + lane < kCbcRows * kCbcCols) st[col + n + lane] = 0;
+    total = col + np;
   }
+  usw_dev::wave_sync();
+  for (uint32_t i = 8 * lane; i < total && i < kCbcRows * kCbcCols; i += 512)
+    if (base + i + 8 <= nvals)
+      *reinterpret_cast<uint4*>(values + base + i) = *reinterpret_cast<const uint4*>(st + i);
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
