@@ -1,6 +1,8 @@
-"""GPU parity of the on-device TCA-BME encoder (usw_encode_device_index and
-usw_encode_device_values, called through the C ABI): every buffer must equal
-the CPU oracle's encoding, and the host encoder's, byte for byte."""
+"""GPU parity of the on-device encoders, called through the C ABI: TCA-BME
+(usw_encode_device_index / _values), IE-BME union-mask INT4
+(usw_union_encode_device_*) and Tiled-CBC (usw_cbc_encode_device_*).  Every
+buffer must equal the CPU oracle's encoding, and the host encoder's, byte
+for byte."""
 import sys
 
 import numpy as np

@@ -1,6 +1,9 @@
-// Device half of the TCA-BME encoder: builds the bitmap encoding of a weight
-// matrix that already sits in GPU memory, the same bytes the host encoder
-// (usw_encode) writes.
+// Device-side encoders for weights already in GPU memory, each writing the
+// same bytes as its host counterpart: TCA-BME (usw_encode; this header's
+// passes below), IE-BME union-mask INT4 (usw_union_encode) and Tiled-CBC
+// (usw_cbc_encode), the last two in their own sections further down.  All
+// three share the in-place scan, the INT4 row-scale kernel and the tail
+// zeroing.
 //
 // Format: blog "SpInfer: How bitmaps make sparse LLMs actually fast", section
 // "How TCA-BME addresses the indexing overhead" (8x8 BitmapTiles in one
