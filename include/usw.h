@@ -207,7 +207,12 @@ usw_status usw_spmm_workspace(const usw_fmt* fmt, int32_t N, size_t* bytes);
  *   Y:  device [N][M] row-major, fp16 (y_type USW_OUT_F16) or fp32
  *       (USW_OUT_F32), 16-byte aligned; fully overwritten.
  *   ws: device workspace of ws_bytes >= usw_spmm_workspace(fmt, N); may be
- *       NULL when that size is 0.  Contents need not be initialised.
+ *       NULL when that size is 0.  Its first usw_spmm_counter_bytes(fmt, N,
+ *       0) bytes are the per-tile counters and must be zero when the call
+ *       starts (the call leaves them zero again); the bytes after them need
+ *       not be initialised.  A workspace whose counters are not zero gives
+ *       wrong Y without an error.  Calls that may run at the same time (on
+ *       different streams) need separate workspaces.
  *   stream: a hipStream_t (NULL = the default stream).  The call only
  *       enqueues work; it returns before the kernels finish.
  * Accumulation is fp32 (each product of two fp16 values is exact in fp32);
@@ -390,7 +395,10 @@ usw_status usw_union_reorder(const uint16_t* W, const uint8_t* mask, int32_t M, 
  * split factor (splits = 0: automatic; otherwise clamped to
  * [ceil(K / (64 * 4 * 63)), max(1, K / 256)]).  The workspace starts with
  * the counter bytes, which must be zero when a call starts (each call leaves
- * them zero), then fp32 partial sums.  Errors: as usw_union_spmm's checks.
+ * them zero), then fp32 partial sums, which need not be initialised.  A
+ * workspace whose counters are not zero gives wrong Y without an error;
+ * calls that may run at the same time need separate workspaces.
+ * Errors: as usw_union_spmm's checks.
  */
 usw_status usw_union_spmm_workspace(const usw_union_fmt* fmt, int32_t N, int32_t splits, size_t* bytes);
 usw_status usw_union_spmm_counter_bytes(const usw_union_fmt* fmt, int32_t N, int32_t splits, size_t* bytes);
@@ -506,7 +514,10 @@ usw_status usw_cbc_encode_device_values(const uint16_t* W, int32_t M, int32_t K,
  * Workspace bytes and leading counter bytes of usw_cbc_spmspv for this
  * matrix and split factor (splits = 0: automatic; otherwise clamped to
  * [1, K / 16]).  The counter bytes must be zero when a call starts; each
- * call leaves them zero.  Errors: as usw_cbc_spmspv's checks.
+ * call leaves them zero.  The partial sums after them need not be
+ * initialised.  A workspace whose counters are not zero gives wrong y
+ * without an error; calls that may run at the same time need separate
+ * workspaces.  Errors: as usw_cbc_spmspv's checks.
  */
 usw_status usw_cbc_spmspv_workspace(const usw_cbc_fmt* fmt, int32_t splits, size_t* bytes, size_t* counter_bytes);
 

@@ -164,6 +164,7 @@ def test_validate_detects_corruption():
         assert L.usw_validate(ctypes.byref(f)) == -8, mutate
 
 
+@pytest.mark.host_pointers
 def test_argument_errors_return_before_launch():
     """Every argument error is reported without touching a GPU (these calls
     pass host pointers and would fail loudly if anything were launched)."""
@@ -229,6 +230,7 @@ def test_argument_errors_return_before_launch():
                         h.offsets.copy().ctypes.data, vals.ctypes.data, 4, None) == -1
 
 
+@pytest.mark.host_pointers
 def test_device_encoder_argument_errors_return_before_launch():
     """usw_encode_device_index / _values report every argument error before
     any launch (host pointers here: a launch would fail)."""
@@ -268,6 +270,7 @@ def test_device_encoder_argument_errors_return_before_launch():
     assert val(w, 256, 256, 64, 64, 1, b, o, None, 10, v + 8, 4096, None) == -6
 
 
+@pytest.mark.host_pointers
 def test_device_union_encoder_argument_errors_return_before_launch():
     L = usw.lib()
     W = np.zeros((128, 128), np.uint16)
@@ -293,6 +296,7 @@ def test_device_union_encoder_argument_errors_return_before_launch():
     assert val(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, 10, v + 8, 4096, None) == -6
 
 
+@pytest.mark.host_pointers
 def test_device_cbc_encoder_argument_errors_return_before_launch():
     L = usw.lib()
     W = np.zeros((256, 32), np.uint16)

@@ -82,6 +82,7 @@ def test_cbc_validate_detects_corruption():
         assert L.usw_cbc_validate(B(f)) == -8, mutate
 
 
+@pytest.mark.host_pointers
 def test_cbc_argument_errors_return_before_launch():
     L = usw.lib()
     rng = np.random.default_rng(7)

@@ -99,6 +99,7 @@ def test_union_validate_detects_corruption():
         assert L.usw_union_validate(B(f)) == -8, mutate
 
 
+@pytest.mark.host_pointers
 def test_union_argument_errors_return_before_launch():
     L = usw.lib()
     rng = np.random.default_rng(7)

@@ -191,12 +191,13 @@ def test_prefill_counters_via_c_abi():
     check(outs[0], Yref, Bnd, "prefill C ABI")
 
 
+@pytest.mark.parametrize("N", [512, 2048])
 @pytest.mark.parametrize("name", ["up", "down"])
-def test_prefill_full_size_integer_exact_bitwise(name):
-    """Llama-7B-shaped layer at N = 512, every output compared bit for bit."""
+def test_prefill_full_size_integer_exact_bitwise(name, N):
+    """Llama-7B-shaped layer at N = 512 and 2048 (the prefill sizes), every
+    output compared bit for bit."""
     M, K = wl.LAYERS_PREFILL[name]
-    N = 512
-    rng = np.random.default_rng(91 if name == "up" else 92)
+    rng = np.random.default_rng((91 if name == "up" else 92) + 1000 * (N != 512))
     W = wl.weight_dyadic(M, K, rng)
     mask = wl.mask_bernoulli(M, K, 0.5, rng)
     X = wl.activations_small_int(N, K, rng)

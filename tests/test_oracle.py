@@ -384,6 +384,64 @@ def test_int4_quantisation_rule():
     assert q.min() >= -8 and q.max() <= 7
 
 
+# Exact .5 quotients, written out by hand.  Row 0 keeps 7.0 as its largest
+# magnitude, so scale = fp16(7 / 7) = 1 and each code is the weight rounded to
+# an integer; row 1 keeps 14.0, scale 2, so each code is half the weight.
+# Round half to even sends every tie to the even neighbour: 0.5 -> 0,
+# 1.5 -> 2, 2.5 -> 2, 3.5 -> 4, 4.5 -> 4, 5.5 -> 6, 6.5 -> 6, and the same
+# with signs; half away from zero (C's round) would give 1, 2, 3, 4, 5, 6, 7.
+INT4_TIE_ROWS = [
+    # (weights of the kept entries, expected codes)
+    ([7.0, 0.5, 1.5, 2.5, -0.5, -2.5, 6.5, 3.5, -3.5, 4.5, -4.5, 5.5, -1.5, -6.5, -5.5, 0.25],
+     [7, 0, 2, 2, 0, -2, 6, 4, -4, 4, -4, 6, -2, -6, -6, 0]),
+    ([14.0, 1.0, 3.0, 5.0, -1.0, -5.0, 13.0, 7.0, -7.0, 9.0, -9.0, 11.0, -3.0, -13.0, -11.0, -14.0],
+     [7, 0, 2, 2, 0, -2, 6, 4, -4, 4, -4, 6, -2, -6, -6, -7]),
+]
+
+
+def int4_tie_case():
+    W = np.zeros((16, 16), dtype=np.float16)
+    mask = np.zeros((16, 16), bool)
+    for r, (w, _) in enumerate(INT4_TIE_ROWS):
+        W[r] = w
+        mask[r] = True
+    return W, mask
+
+
+def int4_ties_hold(quantize):
+    W, mask = int4_tie_case()
+    scales, q = quantize(W, mask)
+    if scales[0] != 1.0 or scales[1] != 2.0:
+        return False
+    return all(q[r].tolist() == codes for r, (_, codes) in enumerate(INT4_TIE_ROWS))
+
+
+def mutant_quantize_half_away(W, mask):
+    """The INT4 rule with C's round (ties away from zero) in place of rint."""
+    Wd = W.astype(np.float64)
+    amax = np.where(mask, np.abs(Wd), 0.0).max(axis=1)
+    scales = ob.fp16_rne(amax / 7.0)
+    s64 = scales.astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = Wd / s64[:, None]
+    q = np.where(s64[:, None] > 0, np.sign(t) * np.floor(np.abs(t) + 0.5), 0.0)
+    return scales, np.where(mask, np.clip(q, -8, 7), 0).astype(np.int8)
+
+
+def test_int4_rounding_ties_half_even():
+    """Exact .5 quotients round to the even code (the RTN rule with ties to
+    even); a quantiser that rounds ties away from zero fails this pin."""
+    assert int4_ties_hold(ob.quantize_rows_i4)
+    assert not int4_ties_hold(mutant_quantize_half_away)
+    # The same codes come out of the encoded INT4 buffers.
+    W, mask = int4_tie_case()
+    enc = ob.encode_i4(W, mask, 16, 16)
+    q, Wd = ob.decode_i4(enc)
+    for r, (w, codes) in enumerate(INT4_TIE_ROWS):
+        assert q[r].tolist() == codes
+        assert Wd[r].tolist() == [c * (1.0 if r == 0 else 2.0) for c in codes]
+
+
 def test_int4_non_finite_weights_reading():
     """The pages state the INT4 rule for finite weights only; the reading
     taken: a kept NaN makes the row's maximum (so its scale) NaN and every
@@ -454,13 +512,21 @@ def test_planted_mistakes_are_caught(golden):
     W, mask, _ = wl.config_case(1, 256, 256, 8, 0.5)
     enc = ob.encode(W, mask)
     assert encoded_bytes(enc) != 8 * enc.geom.nbt + 2 * enc.nnz
-    # transposed operand in the product (non-square W)
+    # a transposed operand in the product (Y = X W instead of X W^T on a
+    # square W) misses the brute-force sums of the definition
     rng = np.random.default_rng(1)
+    Ws = wl.weight_normal(16, 16, rng, sigma=1.0)
+    Xs = wl.activations_normal(2, 16, rng)
+    exact = [[sum(Fraction(float(Ws[m, k])) * Fraction(float(Xs[n, k])) for k in range(16)) for m in range(16)]
+             for n in range(2)]
+    Ygood = ob.spmm(ob.encode(Ws, np.ones(Ws.shape, bool), 16, 16), Xs)
+    Ytrans = Xs.astype(np.float64) @ Ws.astype(np.float64)
+    tol = Fraction(16 * 2.0 ** -52) * 64
+    assert all(abs(Fraction(Ygood[n, m]) - exact[n][m]) <= tol for n in range(2) for m in range(16))
+    assert not all(abs(Fraction(Ytrans[n, m]) - exact[n][m]) <= tol for n in range(2) for m in range(16))
+    # a sign error in one product is outside the tolerance
     Wn = wl.weight_normal(32, 64, rng)
     X = wl.activations_normal(2, 64, rng)
-    with pytest.raises(ValueError):
-        np.asarray(X, dtype=np.float64) @ np.asarray(Wn, dtype=np.float64)
-    # a sign error in one product is outside the tolerance
     Wd = Wn.astype(np.float64)
     Yref = ob.spmm_fp64(Wd, X)
     Ybad = Yref.copy()

@@ -188,6 +188,28 @@ def test_round_trip_i4():
     assert np.array_equal(ou.dense_weight_union(enc), np.where(mask, W, 0).astype(np.float64))
 
 
+def test_i4_rounding_ties_half_even():
+    """Exact .5 quotients in the union format's payload round to the even
+    code.  Row 0 keeps 7.0 as its largest magnitude (scale 1), row 1 keeps
+    14.0 (scale 2); the expected codes are written out by hand."""
+    row0 = [7.0, 0.5, 1.5, 2.5, -0.5, -2.5, 6.5, 3.5, -3.5, 4.5, -4.5, 5.5, -1.5, -6.5, -5.5, 0.25]
+    row1 = [14.0, 1.0, 3.0, 5.0, -1.0, -5.0, 13.0, 7.0, -7.0, 9.0, -9.0, 11.0, -3.0, -13.0, -11.0, -14.0]
+    codes0 = [7, 0, 2, 2, 0, -2, 6, 4, -4, 4, -4, 6, -2, -6, -6, 0]
+    codes1 = [7, 0, 2, 2, 0, -2, 6, 4, -4, 4, -4, 6, -2, -6, -6, -7]
+    W = np.zeros((64, 64), dtype=np.float16)
+    mask = np.zeros((64, 64), bool)
+    W[0, :16], W[1, :16] = row0, row1
+    mask[:2, :16] = True
+    for enc in (ou.encode_union(W, mask, 64, 64, 2, 2, I4), ou.encode_union_loop(W, mask, 64, 64, 2, 2, I4)):
+        assert enc.scales[0] == 1.0 and enc.scales[1] == 2.0
+        q = ou.decode_union(enc)
+        assert q[0, :16].tolist() == codes0 and q[1, :16].tolist() == codes1
+        # Area 0's stream comes first: the 32 union-active positions of rows
+        # 0 and 1 in row-major order, low nibble first.
+        stream = ob.unpack_nibbles(enc.values, 32)
+        assert stream.tolist() == codes0 + codes1
+
+
 def test_single_area_is_plain_row_major_bitmap():
     """Q = 1: the union mask is the mask and each LT's payload is its kept
     values in row-major order (boolean indexing of each LT)."""

@@ -346,8 +346,10 @@ def union_spmm(enc: UnionEncoding, x, y=None, out_dtype=None, splits: int = 0, s
     if not x.is_contiguous():
         x = x.contiguous()
     N = x.shape[0]
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
     if y is None:
-        y = torch.empty((N, enc.M), dtype=out_dtype or torch.float16, device=x.device)
+        with torch.cuda.stream(st):
+            y = torch.empty((N, enc.M), dtype=out_dtype or torch.float16, device=x.device)
     if y.shape != (N, enc.M) or not y.is_contiguous():
         raise ValueError("y must be a contiguous [N][M] tensor")
     yt = {torch.float16: USW_OUT_F16, torch.float32: USW_OUT_F32}.get(y.dtype)
@@ -355,8 +357,7 @@ def union_spmm(enc: UnionEncoding, x, y=None, out_dtype=None, splits: int = 0, s
         raise ValueError("y must be float16 or float32")
     f = enc.fmt()
     nbytes, cbytes = union_workspace_bytes(enc, N, splits)
-    ws = _workspace(x.device, nbytes, cbytes) if nbytes else None
-    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    ws = _workspace(st, nbytes, cbytes) if nbytes else None
     check(lib().usw_union_spmm(ctypes.byref(f), x.data_ptr(), y.data_ptr(), yt, N, int(splits),
                                ws.data_ptr() if ws is not None else None, nbytes, ctypes.c_void_p(st.cuda_stream)),
           "usw_union_spmm")
@@ -459,8 +460,10 @@ def cbc_spmspv(enc: CbcEncoding, x, tau: float = 0.0, y=None, out_dtype=None, sp
     if x.dtype != torch.float16 or x.numel() != enc.K:
         raise ValueError("x must hold K float16 values")
     x = x.reshape(-1).contiguous()
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
     if y is None:
-        y = torch.empty(enc.M, dtype=out_dtype or torch.float16, device=x.device)
+        with torch.cuda.stream(st):
+            y = torch.empty(enc.M, dtype=out_dtype or torch.float16, device=x.device)
     if y.numel() != enc.M or not y.is_contiguous():
         raise ValueError("y must be a contiguous tensor of M values")
     yt = {torch.float16: USW_OUT_F16, torch.float32: USW_OUT_F32}.get(y.dtype)
@@ -468,8 +471,7 @@ def cbc_spmspv(enc: CbcEncoding, x, tau: float = 0.0, y=None, out_dtype=None, sp
         raise ValueError("y must be float16 or float32")
     f = enc.fmt()
     nbytes, cbytes = cbc_workspace_bytes(enc, splits)
-    ws = _workspace(x.device, nbytes, cbytes) if nbytes else None
-    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    ws = _workspace(st, nbytes, cbytes) if nbytes else None
     check(lib().usw_cbc_spmspv(ctypes.byref(f), x.data_ptr(), y.data_ptr(), yt, float(tau), int(splits),
                                ws.data_ptr() if ws is not None else None, nbytes, ctypes.c_void_p(st.cuda_stream)),
           "usw_cbc_spmspv")
@@ -564,22 +566,26 @@ def spmm_counter_bytes(enc: Encoding, N: int, splits: int = 0) -> int:
     return b.value
 
 
-def _workspace(device, nbytes: int, counter_bytes: int):
-    """One zero-filled workspace per device.  Its first ``counter_bytes``
-    bytes must be zero when a call starts; each call leaves them zero, but a
-    call with another counter size may have written partial sums there, so
-    they are cleared (a small fill kernel on the current stream) whenever the
-    counter size changes.  Calls on one device are ordered on the stream they
-    are issued to; do not overlap calls on different streams."""
+def _workspace(stream, nbytes: int, counter_bytes: int):
+    """One zero-filled workspace per (device, stream).
+
+    Its first ``counter_bytes`` bytes must be zero when a call starts; each
+    call leaves them zero, but a call with another counter size may have
+    written partial sums there, so they are cleared (a small fill kernel)
+    whenever the counter size changes.  The allocation and the clear are
+    issued on ``stream``, the stream the call launches on, so they are
+    ordered before it; calls on different streams never share a workspace.
+    """
     import torch
-    key = str(device)
+    key = (str(stream.device), int(stream.cuda_stream))
     ent = _WS.get(key)
-    if ent is None or ent[0].numel() < nbytes:
-        ent = [torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device), counter_bytes]
-        _WS[key] = ent
-    elif ent[1] != counter_bytes:
-        ent[0][:counter_bytes].zero_()
-        ent[1] = counter_bytes
+    with torch.cuda.stream(stream):
+        if ent is None or ent[0].numel() < nbytes:
+            ent = [torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=stream.device), counter_bytes]
+            _WS[key] = ent
+        elif ent[1] != counter_bytes:
+            ent[0][:counter_bytes].zero_()
+            ent[1] = counter_bytes
     return ent[0]
 
 
@@ -595,8 +601,10 @@ def spmm(enc: Encoding, x, y=None, out_dtype=None, splits: int = 0, stream=None)
     if not x.is_contiguous():
         x = x.contiguous()
     N = x.shape[0]
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
     if y is None:
-        y = torch.empty((N, enc.M), dtype=out_dtype or torch.float16, device=x.device)
+        with torch.cuda.stream(st):
+            y = torch.empty((N, enc.M), dtype=out_dtype or torch.float16, device=x.device)
     if y.shape != (N, enc.M) or not y.is_contiguous():
         raise ValueError("y must be a contiguous [N][M] tensor")
     yt = {torch.float16: USW_OUT_F16, torch.float32: USW_OUT_F32}.get(y.dtype)
@@ -604,8 +612,7 @@ def spmm(enc: Encoding, x, y=None, out_dtype=None, splits: int = 0, stream=None)
         raise ValueError("y must be float16 or float32")
     f = enc.fmt()
     nbytes = spmm_workspace_bytes(enc, N, splits)
-    ws = _workspace(x.device, nbytes, spmm_counter_bytes(enc, N, splits)) if nbytes else None
-    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    ws = _workspace(st, nbytes, spmm_counter_bytes(enc, N, splits)) if nbytes else None
     check(lib().usw_spmm_ex(ctypes.byref(f), x.data_ptr(), y.data_ptr(), yt, N, int(splits),
                             ws.data_ptr() if ws is not None else None, nbytes, ctypes.c_void_p(st.cuda_stream)),
           "usw_spmm")
