@@ -260,6 +260,30 @@ usw_status usw_spmm_ex(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * usw_spmm_ex without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory around the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same fmt, X, Y, y_type, N, splits and stream conventions and the same
+ * kernels and results as usw_spmm_ex.  The split-K counters and partial
+ * sums live in a library-owned device array of 16 MiB per GPU (16 KiB of
+ * counters, the rest partial sums), created with the library's code object
+ * on each GPU it runs on and kept until the process ends.  Each call first
+ * clears the counters it uses with a small kernel on the stream, then
+ * launches the product; it never calls hipMalloc or hipFree.  splits = 0 is
+ * usw_spmm's automatic factor, or 1 when that factor's partial sums do not
+ * fit the array (e.g. the prefill kernel's stream-K split).
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (on different streams) race and give wrong Y; order them
+ * on one stream, or use usw_spmm_ex with separate workspaces.
+ * Errors: as usw_spmm_ex, plus WORKSPACE when the call's counters or
+ * partial sums (usw_spmm_counter_bytes, usw_spmm_workspace_ex) exceed the
+ * array, UNSUPPORTED for a device index of 64 or more, HIP when the array's
+ * address cannot be taken on the current device.
+ */
+usw_status usw_spmm_noalloc(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y_type, int32_t N,
+                            int32_t splits, void* stream);
+
+/*
  * ---------------------------------------------------------------------------
  * IE-BME union-mask low-bit format ("UnionSparse: An Index-Efficient Sparsity
  * Framework for Low-Bit Sparse LLM Inference on Edge", section on IE-BME; the

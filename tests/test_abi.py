@@ -231,6 +231,34 @@ def test_argument_errors_return_before_launch():
 
 
 @pytest.mark.host_pointers
+def test_noalloc_argument_errors_return_before_launch():
+    """usw_spmm_noalloc reports argument errors, and partial sums that do not
+    fit its 16 MiB scratch, before it touches the GPU (host pointers here)."""
+    L = usw.lib()
+    W, mask, X = wl.config_case(1, 256, 256, 8, 0.5)
+    h = usw.encode_host(W, mask)
+    f = h.fmt()
+    B = ctypes.byref
+    x = np.zeros((8, 256), np.uint16)
+    y = np.zeros((8, 256), np.uint16)
+    xa, ya = x.ctypes.data, y.ctypes.data
+    assert L.usw_spmm_noalloc(None, xa, ya, 1, 8, 0, None) == -1
+    assert L.usw_spmm_noalloc(B(f), None, ya, 1, 8, 0, None) == -1
+    assert L.usw_spmm_noalloc(B(f), xa, None, 1, 8, 0, None) == -1
+    assert L.usw_spmm_noalloc(B(f), xa, ya, 2, 8, 0, None) == -3
+    assert L.usw_spmm_noalloc(B(f), xa, ya, 1, 0, 0, None) == -4
+    assert L.usw_spmm_noalloc(B(f), xa + 2, ya, 1, 8, 0, None) == -6
+    assert L.usw_spmm_noalloc(B(fmt_of(h, K=200)), xa, ya, 1, 8, 0, None) == -2
+    assert L.usw_spmm_noalloc(B(fmt_of(h, gt_m=32)), xa, ya, 1, 8, 0, None) == -5
+    # 16 splits of 32 tokens x 16384 rows of fp32 partial sums (32 MiB) do
+    # not fit the scratch: WORKSPACE, checked before any HIP call.
+    big = fmt_of(h, M=16384, K=4096, nnz=16384 * 2048)
+    sz = ctypes.c_size_t()
+    assert L.usw_spmm_workspace_ex(B(big), 32, 16, B(sz)) == 0 and sz.value > 16 << 20
+    assert L.usw_spmm_noalloc(B(big), xa, ya, 1, 32, 16, None) == -7
+
+
+@pytest.mark.host_pointers
 def test_device_encoder_argument_errors_return_before_launch():
     """usw_encode_device_index / _values report every argument error before
     any launch (host pointers here: a launch would fail)."""

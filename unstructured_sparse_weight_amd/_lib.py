@@ -27,7 +27,7 @@ EXPORTED = (
     "usw_abi_version", "usw_status_str", "usw_encode_query", "usw_encode", "usw_validate",
     "usw_encode_device_index", "usw_encode_device_values",
     "usw_spmm_workspace", "usw_spmm", "usw_spmm_workspace_ex", "usw_spmm_ex", "usw_spmm_counter_bytes",
-    "usw_probe_read",
+    "usw_spmm_noalloc", "usw_probe_read",
     "usw_union_encode_query", "usw_union_encode", "usw_union_validate", "usw_union_reorder",
     "usw_union_encode_device_index", "usw_union_encode_device_values", "usw_union_spmm_workspace",
     "usw_union_spmm_counter_bytes", "usw_union_spmm",
@@ -104,6 +104,8 @@ def _declare(lib):
     lib.usw_spmm_workspace_ex.argtypes = [P(UswFmt), c_i32, c_i32, P(c_sz)]
     lib.usw_spmm_ex.restype = c_i32
     lib.usw_spmm_ex.argtypes = [P(UswFmt), c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]
+    lib.usw_spmm_noalloc.restype = c_i32
+    lib.usw_spmm_noalloc.argtypes = [P(UswFmt), c_vp, c_vp, c_i32, c_i32, c_i32, c_vp]
     lib.usw_spmm_counter_bytes.restype = c_i32
     lib.usw_spmm_counter_bytes.argtypes = [P(UswFmt), c_i32, c_i32, P(c_sz)]
     lib.usw_probe_read.restype = c_i32

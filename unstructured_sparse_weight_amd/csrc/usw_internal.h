@@ -56,7 +56,10 @@ struct PrefillPlan {
 PrefillPlan prefill_plan(const Geometry& g, int N, int splits_req);
 size_t prefill_counter_bytes(const Geometry& g, const PrefillPlan& p);
 size_t prefill_workspace_bytes(const Geometry& g, int N, const PrefillPlan& p);
-usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X, void* Y, bool f16out, int N, void* ws,
-                          const PrefillPlan& p, void* stream);
+// counters: the plan's per-tile counters (prefill_counter_bytes, zero at the
+// start of the launch); part: its partial sums (prefill_workspace_bytes
+// minus the counter bytes).  Both unused when the counter bytes are 0.
+usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X, void* Y, bool f16out, int N,
+                          uint32_t* counters, float* part, const PrefillPlan& p, void* stream);
 
 }  // namespace usw

@@ -820,17 +820,17 @@ size_t prefill_workspace_bytes(const Geometry& g, int N, const PrefillPlan& p) {
   }
   return cb + static_cast<size_t>(p.splits) * N * g.M * sizeof(float);
 }
-usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X, void* Y, bool f16out, int N, void* ws,
-                          const PrefillPlan& p, void* stream) {
+usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X, void* Y, bool f16out, int N,
+                          uint32_t* counters, float* part, const PrefillPlan& p, void* stream) {
   PArgs a;
   a.bitmaps = f->bitmaps;
   a.offsets = f->offsets;
   a.values = static_cast<const uint8_t*>(f->values);
   a.X = X;
   a.Y = Y;
-  const size_t cbytes = prefill_counter_bytes(g, p);
-  a.counters = cbytes > 0 ? static_cast<uint32_t*>(ws) : nullptr;
-  a.part = cbytes > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + cbytes) : nullptr;
+  const bool shared = prefill_counter_bytes(g, p) > 0;
+  a.counters = shared ? counters : nullptr;
+  a.part = shared ? part : nullptr;
   a.values_alloc = values_alloc_bytes(f->val_type, f->nnz);
   a.M = static_cast<int>(g.M);
   a.K = static_cast<int>(g.K);

@@ -49,11 +49,16 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "usw.h"
 #include "usw_internal.h"
 #include "usw_device.h"
 #include "usw_decode_common.h"
+
+// Scratch of usw_spmm_noalloc (see scratch_address below): split-K counters
+// and partial sums, one copy per GPU, kept until the process ends.
+static __device__ __align__(256) uint8_t scratch[size_t(16) << 20];
 
 namespace {
 
@@ -946,31 +951,49 @@ void launch_decode(const Args& a, bool f16out, dim3 grid, hipStream_t s, int cfg
   }
 }
 
-usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_type, int32_t N, void* ws,
-                     size_t ws_bytes, void* stream, int splits_req) {
-  usw::Geometry g;
-  usw_status st = check_common(f, y_type, N, &g);
+// Argument checks of a product call (nothing is written or launched).
+usw_status check_call(const usw_fmt* f, const uint16_t* X, const void* Y, int32_t y_type, int32_t N,
+                      usw::Geometry* g) {
+  usw_status st = check_common(f, y_type, N, g);
   if (st) return st;
   if (!X || !Y || !f->bitmaps || !f->offsets || !f->values) return USW_ERR_NULL_ARG;
   if (f->val_type == USW_VAL_I4 && !f->scales) return USW_ERR_NULL_ARG;
   if (!aligned16(X) || !aligned16(Y) || !aligned16(f->bitmaps) || !aligned16(f->values) ||
       (reinterpret_cast<uintptr_t>(f->offsets) & 3u))
     return USW_ERR_MISALIGNED;
-  if (use_prefill(f, N)) {
-    const usw::PrefillPlan pp = usw::prefill_plan(g, N, splits_req);
-    const size_t need = usw::prefill_workspace_bytes(g, N, pp);
-    if (need > 0) {
-      if (!ws || ws_bytes < need) return USW_ERR_WORKSPACE;
-      if (!aligned16(ws)) return USW_ERR_MISALIGNED;
-    }
-    return usw::prefill_launch(f, g, X, Y, y_type == USW_OUT_F16, N, ws, pp, stream);
+  return USW_OK;
+}
+
+// Kernel choice, split factor and workspace of one call.
+struct CallPlan {
+  bool prefill;
+  usw::PrefillPlan pp;   // prefill
+  Plan p;                // decode
+  size_t need;           // workspace bytes (0: none)
+  size_t cb;             // leading counter bytes of the workspace
+};
+
+CallPlan make_call_plan(const usw_fmt* f, const usw::Geometry& g, int32_t N, int splits_req) {
+  CallPlan c{};
+  c.prefill = use_prefill(f, N);
+  if (c.prefill) {
+    c.pp = usw::prefill_plan(g, N, splits_req);
+    c.need = usw::prefill_workspace_bytes(g, N, c.pp);
+    c.cb = usw::prefill_counter_bytes(g, c.pp);
+  } else {
+    c.p = make_plan(g, N, splits_req, f->val_type == USW_VAL_I4, lean_values(f, g));
+    c.need = workspace_bytes(g, c.p);
+    c.cb = c.need > 0 ? counters_bytes(g) : 0;
   }
-  const Plan p = make_plan(g, N, splits_req, f->val_type == USW_VAL_I4, lean_values(f, g));
-  const size_t need = workspace_bytes(g, p);
-  if (need > 0) {
-    if (!ws || ws_bytes < need) return USW_ERR_WORKSPACE;
-    if (!aligned16(ws)) return USW_ERR_MISALIGNED;
-  }
+  return c;
+}
+
+// Enqueue a planned call.  counters (c.cb bytes, zero at the start) and part
+// (c.need - c.cb bytes) are used only when c.need > 0.
+usw_status launch_call(const usw_fmt* f, const usw::Geometry& g, const CallPlan& c, const uint16_t* X, void* Y,
+                       int32_t y_type, int32_t N, uint32_t* counters, float* part, void* stream) {
+  if (c.prefill) return usw::prefill_launch(f, g, X, Y, y_type == USW_OUT_F16, N, counters, part, c.pp, stream);
+  const Plan& p = c.p;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t nblk = g.Gr * p.splits;
   const dim3 grid(static_cast<unsigned>(nblk));
@@ -989,8 +1012,8 @@ usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_typ
     a.scales = i4 ? f->scales : nullptr;
     a.X = X + static_cast<size_t>(n0) * K;
     a.Y = static_cast<uint8_t*>(Y) + static_cast<size_t>(n0) * M * ybytes;
-    a.counters = need ? static_cast<uint32_t*>(ws) : nullptr;
-    a.part = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counters_bytes(g)) : nullptr;
+    a.counters = c.need ? counters : nullptr;
+    a.part = c.need ? part : nullptr;
     a.values_alloc = usw::values_alloc_bytes(f->val_type, f->nnz);
     a.M = M;
     a.K = K;
@@ -1016,6 +1039,86 @@ usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_typ
     if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
   }
   return USW_OK;
+}
+
+usw_status spmm_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_type, int32_t N, void* ws,
+                     size_t ws_bytes, void* stream, int splits_req) {
+  usw::Geometry g;
+  usw_status st = check_call(f, X, Y, y_type, N, &g);
+  if (st) return st;
+  const CallPlan c = make_call_plan(f, g, N, splits_req);
+  if (c.need > 0) {
+    if (!ws || ws_bytes < c.need) return USW_ERR_WORKSPACE;
+    if (!aligned16(ws)) return USW_ERR_MISALIGNED;
+  }
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  return launch_call(f, g, c, X, Y, y_type, N, reinterpret_cast<uint32_t*>(w),
+                     c.need ? reinterpret_cast<float*>(w + c.cb) : nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch-backed calls (usw_spmm_noalloc)
+// ---------------------------------------------------------------------------
+//
+// The split-K counters and partial sums of usw_spmm_noalloc live in one
+// statically allocated device array per GPU instead of a caller workspace:
+// counters in its first kScratchCounterBytes, partial sums after them.  In
+// host code the array's name is only a stand-in; its device address on the
+// current GPU comes from hipGetSymbolAddress, taken once per device and kept.
+
+constexpr size_t kScratchBytes = size_t(16) << 20;          // the whole array: 16 MiB
+constexpr size_t kScratchCounterBytes = size_t(16) << 10;   // counters: up to 4096 tiles
+constexpr int kMaxDevices = 64;
+static_assert(sizeof(scratch) == kScratchBytes, "the scratch array has the stated size");
+
+// Clears n 32-bit words (the counters a call needs at zero) with ordinary
+// vector stores; a kernel, so that the call can be captured in a HIP graph.
+__global__ __launch_bounds__(256) void scratch_clear_kernel(uint32_t* __restrict__ p, uint32_t n) {
+  for (uint32_t i = threadIdx.x + blockIdx.x * 256u; i < n; i += 256u * gridDim.x) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the current device.
+usw_status scratch_address(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return USW_ERR_HIP;
+  if (dev >= kMaxDevices) return USW_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return USW_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return USW_OK;
+}
+
+usw_status spmm_noalloc_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_type, int32_t N,
+                             int32_t splits, void* stream) {
+  usw::Geometry g;
+  usw_status st = check_call(f, X, Y, y_type, N, &g);
+  if (st) return st;
+  auto fits = [](const CallPlan& c) {
+    return c.cb <= kScratchCounterBytes && c.need - c.cb <= kScratchBytes - kScratchCounterBytes;
+  };
+  CallPlan c = make_call_plan(f, g, N, splits < 0 ? 0 : splits);
+  // The automatic factor falls back to 1 when its partial sums do not fit.
+  if (splits <= 0 && !fits(c)) c = make_call_plan(f, g, N, 1);
+  if (!fits(c)) return USW_ERR_WORKSPACE;
+  uint8_t* base = nullptr;
+  if (c.need > 0) {
+    st = scratch_address(&base);
+    if (st) return st;
+    // The counters must be zero when the kernels start.  Every call leaves
+    // them zero, but a call that overlapped another on this GPU may not.
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    scratch_clear_kernel<<<1, 256, 0, s>>>(reinterpret_cast<uint32_t*>(base), static_cast<uint32_t>(c.cb / 4));
+    if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
+  }
+  return launch_call(f, g, c, X, Y, y_type, N, reinterpret_cast<uint32_t*>(base),
+                     c.need ? reinterpret_cast<float*>(base + kScratchCounterBytes) : nullptr, stream);
 }
 
 }  // namespace
@@ -1062,6 +1165,11 @@ usw_status usw_spmm_counter_bytes(const usw_fmt* f, int32_t N, int32_t splits, s
 usw_status usw_spmm_ex(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_type, int32_t N, int32_t splits,
                        void* ws, size_t ws_bytes, void* stream) {
   return spmm_impl(f, X, Y, y_type, N, ws, ws_bytes, stream, splits < 0 ? 0 : splits);
+}
+
+usw_status usw_spmm_noalloc(const usw_fmt* f, const uint16_t* X, void* Y, int32_t y_type, int32_t N, int32_t splits,
+                            void* stream) {
+  return spmm_noalloc_impl(f, X, Y, y_type, N, splits, stream);
 }
 
 }  // extern "C"
