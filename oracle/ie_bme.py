@@ -115,7 +115,10 @@ class UnionEncoded:
     bitmaps: np.ndarray        # uint64 [NWORDS]
     offsets: np.ndarray        # uint32 [NLT + 1]
     values: np.ndarray         # F16: uint16 [payload]; I4: uint8 [ceil(payload / 2)]
-    scales: Optional[np.ndarray] = None   # I4: fp16 [M]
+    scales: Optional[np.ndarray] = None   # I4: fp16 [M], per original row
+    # Reordered LTs only: uint8 [NLT][H_L]; rowmap[t][r] is the stored row of
+    # LT t that holds the LT's original row r.  None: rows in natural order.
+    rowmap: Optional[np.ndarray] = None
 
 
 def union_storage_bytes(nlt: int, nwords: int, payload: int, value_bits: int = 4) -> float:
@@ -200,6 +203,11 @@ def encode_union(W: np.ndarray, mask: Optional[np.ndarray], h_l: int = 64, k_l: 
     mask = _check_inputs(W, mask)
     g = UnionGeometry(W.shape[0], W.shape[1], h_l, k_l, r_a, c_a)
     src, scales = _payload_source(W, mask, val_type)
+    return _construct(g, val_type, src, mask, scales)
+
+
+def _construct(g: UnionGeometry, val_type: int, src: np.ndarray, mask: np.ndarray, scales) -> UnionEncoded:
+    """Union words, offsets and area streams of a payload source and mask."""
     areas_m = area_view(mask, g)
     union = areas_m.any(axis=1)                               # [NLT][am*ak]
     areas_v = area_view(src, g)                               # [NLT][Q][am*ak]
@@ -210,6 +218,76 @@ def encode_union(W: np.ndarray, mask: Optional[np.ndarray], h_l: int = 64, k_l: 
     if offsets[-1] >= 1 << 32:
         raise ValueError("payload does not fit 32-bit offsets")
     return _finish(g, val_type, union.reshape(-1), seq, offsets, scales)
+
+
+# --------------------------------------------------------------------------
+# Reordered LTs (the section on bitmap-aware row reordering)
+# --------------------------------------------------------------------------
+#
+# Reordering permutes the rows of each LT before compression; it changes
+# neither the number nor the values of the surviving weights, only where
+# their rows sit inside the LT.  So quantisation (one scale per row of W)
+# happens on the original rows, and the IE-BME construction then runs on
+# every LT with its rows rearranged: stored row s of LT t holds original LT
+# row perms[t][s] (the order usw_union_reorder and row_reorder return).  The
+# encoding keeps, per LT, the inverse map (original row -> stored row) so
+# that a reader can put each row's products back where they belong.
+
+def permute_lt_rows(A: np.ndarray, perms: np.ndarray, h_l: int, k_l: int) -> np.ndarray:
+    """A with the rows of every LT rearranged: stored row s of LT t is the
+    LT's original row perms[t][s]."""
+    M, K = A.shape
+    lc = K // k_l
+    out = np.empty_like(A)
+    for t in range(perms.shape[0]):
+        ti, tj = divmod(t, lc)
+        rows = ti * h_l + np.asarray(perms[t], dtype=np.int64)
+        out[ti * h_l:(ti + 1) * h_l, tj * k_l:(tj + 1) * k_l] = A[rows, tj * k_l:(tj + 1) * k_l]
+    return out
+
+
+def inverse_rowmap(perms: np.ndarray, h_l: int) -> np.ndarray:
+    """rowmap[t][r] = the s with perms[t][s] = r (each row a permutation)."""
+    perms = np.asarray(perms, dtype=np.int64)
+    rowmap = np.empty(perms.shape, dtype=np.uint8)
+    for t in range(perms.shape[0]):
+        if sorted(perms[t].tolist()) != list(range(h_l)):
+            raise ValueError("each LT's row order must be a permutation of its rows")
+        rowmap[t, perms[t]] = np.arange(h_l, dtype=np.uint8)
+    return rowmap
+
+
+def encode_union_reordered(W: np.ndarray, mask: Optional[np.ndarray], perms: np.ndarray, h_l: int = 16,
+                           k_l: int = 64, r_a: int = 2, c_a: int = 2, val_type: int = VAL_I4) -> UnionEncoded:
+    """IE-BME encoding of W after each LT's rows are rearranged by perms
+    ([NLT][H_L]); INT4 scales and codes come from the original rows."""
+    mask = _check_inputs(W, mask)
+    g = UnionGeometry(W.shape[0], W.shape[1], h_l, k_l, r_a, c_a)
+    perms = np.asarray(perms)
+    if perms.shape != (g.nlt, h_l):
+        raise ValueError("one row order per LT")
+    if h_l > 256:
+        raise ValueError("row maps hold one byte per row")
+    rowmap = inverse_rowmap(perms, h_l)
+    src, scales = _payload_source(W, mask, val_type)
+    enc = _construct(g, val_type, permute_lt_rows(src, perms, h_l, k_l), permute_lt_rows(mask, perms, h_l, k_l),
+                     scales)
+    enc.rowmap = rowmap
+    return enc
+
+
+def _unpermute(enc: UnionEncoded, A: np.ndarray) -> np.ndarray:
+    """Per-element array in stored row order -> original row order."""
+    if enc.rowmap is None:
+        return A
+    g = enc.geom
+    out = np.empty_like(A)
+    for t in range(g.nlt):
+        ti, tj = divmod(t, g.lt_cols)
+        r0, c0 = ti * g.h_l, tj * g.k_l
+        for r in range(g.h_l):
+            out[r0 + r, c0:c0 + g.k_l] = A[r0 + int(enc.rowmap[t][r]), c0:c0 + g.k_l]
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -266,7 +344,7 @@ def decode_union_loop(enc: UnionEncoded) -> np.ndarray:
                         ar, ac = divmod(q, g.c_a)
                         out[ti * g.h_l + ar * g.am + i, tj * g.k_l + ac * g.ak + j] = vals[o_t + q * P_t + rank]
             t += 1
-    return out
+    return _unpermute(enc, out)
 
 
 def decode_union(enc: UnionEncoded) -> np.ndarray:
@@ -278,7 +356,7 @@ def decode_union(enc: UnionEncoded) -> np.ndarray:
     vals = _payload_values(enc)
     T = np.zeros((g.nlt, g.Q, g.am * g.ak), dtype=vals.dtype)
     T[np.broadcast_to(union[:, None, :], T.shape)] = vals
-    return area_unview(T, g)
+    return _unpermute(enc, area_unview(T, g))
 
 
 def dense_weight_union(enc: UnionEncoded) -> np.ndarray:
