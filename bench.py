@@ -62,6 +62,11 @@ def parse():
                         " (usw_encode_device_index + usw_encode_device_values) of the weight, not the SpMM;"
                         " encode_union: the on-device IE-BME INT4 encoder (64x64 LTs, 2x2 areas); encode_cbc: the"
                         " on-device Tiled-CBC encoder")
+    p.add_argument("--lt", type=int, default=64, choices=[64, 16],
+                   help="union: LT height (64 x 64 or 16 x 64 LTs, 2 x 2 areas)")
+    p.add_argument("--reorder", action="store_true",
+                   help="union with --lt 16: bitmap-aware row reordering of every LT before encoding"
+                        " (usw_union_reorder, then usw_union_encode_reordered)")
     p.add_argument("--dp", type=float, default=0.5,
                    help="cbc: fraction of activations below the pruning threshold (tau is that quantile of |x|)")
     p.add_argument("--cpu-reps", type=int, default=5)
@@ -198,12 +203,23 @@ def main():
         alg = (h.tile_offsets.nbytes + h.colinfo.nbytes + 2 * K + 2 * M
                + int((32 + 2 * runs[act_cols]).sum()))
     elif union:
-        h = usw.union_encode_host(W, mask, (64, 64), (2, 2), "i4")
+        lt = (args.lt, 64)
+        perms = None
+        if args.reorder:
+            if args.lt != 16:
+                raise SystemExit("--reorder needs --lt 16 (the solver takes LTs of at most 20 rows)")
+            perms, before, after = usw.union_reorder(W, mask, lt, (2, 2))
+            log(f"[bench] row reordering {time.time() - t:.2f} s: active union entries {int(before.sum())}"
+                f" -> {int(after.sum())} ({100.0 * (1 - after.sum() / max(before.sum(), 1)):.2f}% fewer)")
+            t = time.time()
+        h = usw.union_encode_host(W, mask, lt, (2, 2), "i4", perm=perms)
         kept = int(mask.sum())
         log(f"[bench] host union encode {time.time() - t:.2f} s, payload={h.payload} for nnz={kept}"
             f" ({h.payload / max(kept, 1):.3f} stored per kept weight)")
-        # Union words, offsets, INT4 payload, scales, X and Y, each moved once.
-        alg = (h.bitmaps.nbytes + h.offsets.nbytes + h.values_bytes + 2 * M + 2 * N * K + 2 * N * M)
+        # Union words, offsets, INT4 payload, scales, row maps, X and Y, each
+        # moved once.
+        alg = (h.bitmaps.nbytes + h.offsets.nbytes + h.values_bytes + 2 * M + 2 * N * K + 2 * N * M
+               + (h.rowmap.nbytes if h.rowmap is not None else 0))
     else:
         h = usw.encode_host(W, mask, (64, 64), args.dtype)
         log(f"[bench] host encode {time.time() - t:.2f} s, nnz={h.nnz}")
@@ -345,12 +361,13 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(W, mask, X, M, K, N, args.dtype, args.cpu_reps, union, cbc, tau)
+        cpu = cpu_baseline(W, mask, X, M, K, N, args.dtype, args.cpu_reps, union, cbc, tau,
+                           lt=(args.lt, 64), perms=perms if union else None)
 
     if cbc:
         kname = "cbc_spmspv_kernel"
     elif union:
-        kname = "union_decode_kernel"
+        kname = "union16_decode_kernel" if args.lt == 16 else "union_decode_kernel"
     elif prefill:
         kname = "prefill_ws_kernel" if N > 256 else "prefill_kernel"
     else:
@@ -400,7 +417,9 @@ def main():
         "dtype": "f16" if args.dtype == "f16" else "i4",
         "data": "synthetic (seeded N(0,0.02) weights, magnitude pruning, N(0,1) activations)",
         "config": {"workload": workload,
-                   "format": "tiled_cbc_spmspv" if cbc else ("ie_bme_union_2x2" if union else "tca_bme"),
+                   "format": "tiled_cbc_spmspv" if cbc else (
+                       (f"ie_bme_union_2x2_lt{args.lt}" + ("_reordered" if args.reorder else "")) if union
+                       else "tca_bme"),
                    "M": M, "K": K, "N": N, "sparsity": s, "values": args.dtype, "groupTile": "64x64",
                    "rotation_copies": R, "splits": args.splits or "auto",
                    "launch": "eager" if args.eager else "hip_graph"},
@@ -413,6 +432,8 @@ def main():
     }
     if union:
         out["union_payload"] = int(h.payload)
+        out["union_encoded_bytes"] = int(h.bitmaps.nbytes + h.offsets.nbytes + h.values_bytes + 2 * M
+                                         + (h.rowmap.nbytes if h.rowmap is not None else 0))
     if cbc:
         out["config"]["dynamic_sparsity"] = args.dp
         out["config"]["tau"] = tau
@@ -579,7 +600,7 @@ def encode_bench(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(W, mask, X, M, K, N, dtype, reps, union=False, cbc=False, tau=0.0):
+def cpu_baseline(W, mask, X, M, K, N, dtype, reps, union=False, cbc=False, tau=0.0, lt=(64, 64), perms=None):
     """The oracle as it stands (decode + fp64 product) on the host cores."""
     import oracle.tca_bme as ob
     import oracle.ie_bme as ou
@@ -589,7 +610,10 @@ def cpu_baseline(W, mask, X, M, K, N, dtype, reps, union=False, cbc=False, tau=0
         enc = oc.encode_cbc(W, mask)
         product = lambda e, Xm: oc.spmspv(e, Xm[0], tau)  # noqa: E731
     elif union:
-        enc = ou.encode_union(W, mask, 64, 64, 2, 2, ob.VAL_I4)
+        if perms is not None:
+            enc = ou.encode_union_reordered(W, mask, perms, lt[0], lt[1], 2, 2, ob.VAL_I4)
+        else:
+            enc = ou.encode_union(W, mask, lt[0], lt[1], 2, 2, ob.VAL_I4)
         product = ou.spmm_union
     else:
         enc = ob.encode(W, mask) if dtype == "f16" else ob.encode_i4(W, mask)

@@ -320,7 +320,10 @@ typedef struct usw_union_fmt {
   const uint64_t* bitmaps;  /* [NLT * NW] */
   const uint32_t* offsets;  /* [NLT+1] */
   const void* values;       /* I4: uint8 [ceil(payload/2)], padded as usw_union_encode_query says */
-  const uint16_t* scales;   /* I4: fp16 bits [M] */
+  const uint16_t* scales;   /* I4: fp16 bits [M], one per row of W */
+  const uint8_t* rowmap;    /* reordered LTs: [NLT * lt_m], entry t * lt_m + r = the stored row of LT t
+                               that holds the LT's row r of W (usw_union_encode_reordered); NULL: every
+                               LT stores its rows in order */
 } usw_union_fmt;
 
 /*
@@ -348,10 +351,40 @@ usw_status usw_union_encode(const uint16_t* W, const uint8_t* mask, int32_t M, i
 
 /*
  * Check a host copy of an IE-BME encoding: shape fields, offsets[0] = 0,
- * offsets[NLT] = payload, and each LT's span equal to Q times the popcount
- * of its union words.  Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, CORRUPT.
+ * offsets[NLT] = payload, each LT's span equal to Q times the popcount of
+ * its union words, and (when present) each LT's rowmap a permutation of its
+ * rows.  Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, CORRUPT.
  */
 usw_status usw_union_validate(const usw_union_fmt* host_fmt);
+
+/*
+ * IE-BME encoding of W with the rows of every LT rearranged before
+ * compression, as bitmap-aware row reordering prescribes ("UnionSparse",
+ * section on bitmap-aware row reordering: Objective, Practical Effect): the
+ * values of the surviving weights do not change, only which row of its LT
+ * each sits in.
+ *   perm:   host int32 [NLT * lt_m]; stored row s of LT t holds the LT's row
+ *           perm[t * lt_m + s] of W (the order usw_union_reorder returns).
+ *           Each LT's entries must be a permutation of 0 .. lt_m - 1.
+ * The union words, offsets and area streams are those of usw_union_encode
+ * applied to each LT with its rows so arranged.  INT4 scales and codes come
+ * from the rows of W (quantisation precedes reordering), scales[m] for row m.
+ *   rowmap: host output uint8 [NLT * lt_m], the inverse of perm per LT
+ *           (rowmap[t * lt_m + perm[t * lt_m + s]] = s), for usw_union_fmt.
+ * The query returns the payload and the value bytes (logical, padded); the
+ * other buffers have usw_union_encode_query's sizes.  Other arguments as
+ * usw_union_encode.  Errors: NULL_ARG (also perm or rowmap NULL), BAD_SHAPE
+ * (as usw_union_encode_query; lt_m > 256; perm not a permutation per LT),
+ * BAD_DTYPE, CAPACITY.
+ */
+usw_status usw_union_encode_reordered_query(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K,
+                                            int32_t lt_m, int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type,
+                                            const int32_t* perm, int64_t* payload, size_t* bytes_values,
+                                            size_t* bytes_values_alloc);
+usw_status usw_union_encode_reordered(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
+                                      int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type, const int32_t* perm,
+                                      uint64_t* bitmaps, uint32_t* offsets, void* values, size_t values_capacity,
+                                      uint16_t* scales, uint8_t* rowmap);
 
 /*
  * On-device IE-BME encoder for a W already in GPU memory: the same bytes as
@@ -429,13 +462,19 @@ usw_status usw_union_spmm_counter_bytes(const usw_union_fmt* fmt, int32_t N, int
 
 /*
  * Y = W_sp . X on the GPU from an IE-BME encoding (device pointers), with the
- * same X, Y, workspace and stream conventions as usw_spmm.  The kernel takes
- * INT4 values, 64 x 64 LTs and a 2 x 2 area grid, in passes of up to 32
- * tokens; each lane reads one union-mask row's rank once and gathers the
- * rows of all four areas with it (the LSPD gather).  fp32 accumulation,
+ * same X, Y, workspace and stream conventions as usw_spmm.  Kernels take
+ * INT4 values and a 2 x 2 area grid, in passes of up to 32 tokens:
+ *   - 64 x 64 LTs (rowmap NULL);
+ *   - 16 x 64 LTs with M a multiple of 64, with or without a rowmap (the LT
+ *     height the reordering solver handles).  Each lane rebuilds the row of
+ *     W it holds in the product from the stored row the rowmap names, so
+ *     every LT's products land on the rows of W.
+ * Each lane reads one union-mask row's rank once and gathers the rows of
+ * all the areas with it (the LSPD gather).  fp32 accumulation,
  * deterministic.  Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_N,
- * UNSUPPORTED (other LT shapes or area grids, or fp16 values), MISALIGNED,
- * WORKSPACE, HIP.
+ * UNSUPPORTED (other LT shapes or area grids, fp16 values, a rowmap with
+ * 64 x 64 LTs, 16-row LTs with M not a multiple of 64), MISALIGNED,
+ * WORKSPACE, HIP.  The rowmap is not checked here (usw_union_validate does).
  */
 usw_status usw_union_spmm(const usw_union_fmt* fmt, const uint16_t* X, void* Y, int32_t y_type, int32_t N,
                           int32_t splits, void* ws, size_t ws_bytes, void* stream);

@@ -92,11 +92,13 @@ class UnionHostEncoding:
     values: np.ndarray            # uint8, padded allocation
     values_bytes: int             # logical byte count
     scales: Optional[np.ndarray]  # uint16 fp16 bits [M] (INT4) or None
+    rowmap: Optional[np.ndarray] = None   # uint8 [NLT * lt_m] for reordered LTs, else None
 
     def fmt(self) -> UswUnionFmt:
         return UswUnionFmt(self.M, self.K, self.lt_m, self.lt_k, self.r_a, self.c_a, self.val_type, 0, self.payload,
                            self.bitmaps.ctypes.data, self.offsets.ctypes.data, self.values.ctypes.data,
-                           self.scales.ctypes.data if self.scales is not None else None)
+                           self.scales.ctypes.data if self.scales is not None else None,
+                           self.rowmap.ctypes.data if self.rowmap is not None else None)
 
 
 @dataclass
@@ -114,11 +116,13 @@ class UnionEncoding:
     offsets: "object"
     values: "object"
     scales: "object"
+    rowmap: "object" = None
 
     def fmt(self) -> UswUnionFmt:
         return UswUnionFmt(self.M, self.K, self.lt_m, self.lt_k, self.r_a, self.c_a, self.val_type, 0, self.payload,
                            self.bitmaps.data_ptr(), self.offsets.data_ptr(), self.values.data_ptr(),
-                           self.scales.data_ptr() if self.scales is not None else None)
+                           self.scales.data_ptr() if self.scales is not None else None,
+                           self.rowmap.data_ptr() if self.rowmap is not None else None)
 
 
 @dataclass
@@ -206,8 +210,12 @@ def _as_mask(mask, shape):
     return mask
 
 
-def union_encode_host(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4") -> UnionHostEncoding:
-    """Run usw_union_encode on host arrays (IE-BME union-mask format)."""
+def union_encode_host(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4", perm=None) -> UnionHostEncoding:
+    """Run usw_union_encode on host arrays (IE-BME union-mask format).
+
+    ``perm`` (int32 [NLT][lt_m], e.g. from ``union_reorder``) rearranges each
+    LT's rows before compression (usw_union_encode_reordered); the encoding
+    then carries the rowmap the product kernel needs."""
     W = _as_numpy_f16(W)
     if W.ndim != 2:
         raise ValueError("W must be 2-D")
@@ -215,6 +223,8 @@ def union_encode_host(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4"
     mask = _as_mask(mask, W.shape)
     vt = _VAL[dtype]
     L = lib()
+    if perm is not None:
+        return _union_encode_reordered_host(W, mask, lt, areas, vt, perm)
     payload = ctypes.c_int64()
     sz = [ctypes.c_size_t() for _ in range(5)]
     wp = W.ctypes.data
@@ -231,6 +241,36 @@ def union_encode_host(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4"
                              scales.ctypes.data if scales is not None else None), "usw_union_encode")
     return UnionHostEncoding(M, K, lt[0], lt[1], areas[0], areas[1], vt, payload.value, bitmaps, offsets, values,
                              b_val, scales)
+
+
+def _union_encode_reordered_host(W, mask, lt, areas, vt, perm) -> UnionHostEncoding:
+    M, K = W.shape
+    perm = np.ascontiguousarray(np.asarray(perm, dtype=np.int32))
+    if lt[0] <= 0 or lt[1] <= 0 or perm.size != (M // lt[0]) * (K // lt[1]) * lt[0]:
+        raise ValueError("perm must hold one row order of lt_m rows per LT")
+    L = lib()
+    payload = ctypes.c_int64()
+    b_val, b_alloc = ctypes.c_size_t(), ctypes.c_size_t()
+    wp = W.ctypes.data
+    mp = mask.ctypes.data if mask is not None else None
+    args = (M, K, lt[0], lt[1], areas[0], areas[1], vt)
+    check(L.usw_union_encode_reordered_query(wp, mp, *args, perm.ctypes.data, ctypes.byref(payload),
+                                             ctypes.byref(b_val), ctypes.byref(b_alloc)),
+          "usw_union_encode_reordered_query")
+    sz = [ctypes.c_size_t() for _ in range(5)]
+    check(L.usw_union_encode_query(wp, mp, *args, None, *[ctypes.byref(x) for x in sz]), "usw_union_encode_query")
+    b_bm, b_off = sz[0].value, sz[1].value
+    bitmaps = np.empty(b_bm // 8, dtype=np.uint64)
+    offsets = np.empty(b_off // 4, dtype=np.uint32)
+    values = np.empty(b_alloc.value, dtype=np.uint8)
+    scales = np.empty(M, dtype=np.uint16) if vt == USW_VAL_I4 else None
+    rowmap = np.empty(perm.size, dtype=np.uint8)
+    check(L.usw_union_encode_reordered(wp, mp, *args, perm.ctypes.data, bitmaps.ctypes.data, offsets.ctypes.data,
+                                       values.ctypes.data, b_alloc.value,
+                                       scales.ctypes.data if scales is not None else None, rowmap.ctypes.data),
+          "usw_union_encode_reordered")
+    return UnionHostEncoding(M, K, lt[0], lt[1], areas[0], areas[1], vt, payload.value, bitmaps, offsets, values,
+                             b_val.value, scales, rowmap)
 
 
 def union_encode_device(W, mask=None, lt=(64, 64), areas=(2, 2)) -> UnionEncoding:
@@ -318,12 +358,15 @@ def union_to_device(enc: UnionHostEncoding, device="cuda") -> UnionEncoding:
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
     return UnionEncoding(enc.M, enc.K, enc.lt_m, enc.lt_k, enc.r_a, enc.c_a, enc.val_type, enc.payload,
                          t(enc.bitmaps.view(np.int64)), t(enc.offsets.view(np.int32)), t(enc.values),
-                         t(enc.scales.view(np.int16)) if enc.scales is not None else None)
+                         t(enc.scales.view(np.int16)) if enc.scales is not None else None,
+                         t(enc.rowmap) if enc.rowmap is not None else None)
 
 
-def union_encode(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4", device="cuda") -> UnionEncoding:
-    """Encode on the host (usw_union_encode) and copy the buffers to ``device``."""
-    return union_to_device(union_encode_host(W, mask, lt, areas, dtype), device)
+def union_encode(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4", device="cuda",
+                 perm=None) -> UnionEncoding:
+    """Encode on the host (usw_union_encode, or usw_union_encode_reordered
+    with ``perm``) and copy the buffers to ``device``."""
+    return union_to_device(union_encode_host(W, mask, lt, areas, dtype, perm), device)
 
 
 def union_workspace_bytes(enc: UnionEncoding, N: int, splits: int = 0):

@@ -29,6 +29,7 @@ EXPORTED = (
     "usw_spmm_workspace", "usw_spmm", "usw_spmm_workspace_ex", "usw_spmm_ex", "usw_spmm_counter_bytes",
     "usw_spmm_noalloc", "usw_probe_read",
     "usw_union_encode_query", "usw_union_encode", "usw_union_validate", "usw_union_reorder",
+    "usw_union_encode_reordered_query", "usw_union_encode_reordered",
     "usw_union_encode_device_index", "usw_union_encode_device_values", "usw_union_spmm_workspace",
     "usw_union_spmm_counter_bytes", "usw_union_spmm",
     "usw_cbc_encode_query", "usw_cbc_encode", "usw_cbc_validate",
@@ -64,6 +65,7 @@ class UswUnionFmt(ctypes.Structure):
         ("payload", ctypes.c_int64),
         ("bitmaps", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
         ("values", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+        ("rowmap", ctypes.c_void_p),
     ]
 
 
@@ -118,6 +120,12 @@ def _declare(lib):
                                      c_sz, c_vp]
     lib.usw_union_validate.restype = c_i32
     lib.usw_union_validate.argtypes = [P(UswUnionFmt)]
+    lib.usw_union_encode_reordered_query.restype = c_i32
+    lib.usw_union_encode_reordered_query.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                     c_vp, P(c_i64), P(c_sz), P(c_sz)]
+    lib.usw_union_encode_reordered.restype = c_i32
+    lib.usw_union_encode_reordered.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp,
+                                               c_vp, c_vp, c_vp, c_sz, c_vp, c_vp]
     lib.usw_union_spmm_workspace.restype = c_i32
     lib.usw_union_spmm_workspace.argtypes = [P(UswUnionFmt), c_i32, c_i32, P(c_sz)]
     lib.usw_union_spmm_counter_bytes.restype = c_i32

@@ -21,6 +21,7 @@ struct Args {
   void* __restrict__ Y;
   float* __restrict__ part;       // split-K partial sums [splits][N][M] (splits > 1)
   uint32_t* __restrict__ counters;  // per 64-row strip: workgroups done (splits > 1), kept at 0 between calls
+  const uint8_t* __restrict__ rowmap;  // IE-BME with reordered 16-row LTs: [NLT][16] stored row of each row of W
   uint64_t values_alloc;           // padded size of the values buffer in bytes (>= 16)
   int M, K, N, Gc, splits;
   int remap;                       // 1: keep the splits of a strip on one XCD

@@ -145,19 +145,38 @@ void pack_i4(const std::vector<int8_t>& q, int64_t n, uint8_t* vb) {
   });
 }
 
-// Linear index in W of position p = i * ak + j of area q of LT t.
-inline int64_t union_elem(const UnionGeometry& g, int64_t t, int64_t q, int64_t p) {
+// Linear index in W of position p = i * ak + j of area q of LT t.  perm
+// (NULL: rows in order) rearranges each LT's rows: stored row s of LT t is
+// the LT's row perm[t * lt_m + s] of W.
+inline int64_t union_elem(const UnionGeometry& g, const int32_t* perm, int64_t t, int64_t q, int64_t p) {
   const int64_t ti = t / g.lc, tj = t % g.lc;
   const int64_t ar = q / g.c_a, ac = q % g.c_a;
   const int64_t i = p / g.ak, j = p % g.ak;
-  return (ti * g.lt_m + ar * g.am + i) * g.K + tj * g.lt_k + ac * g.ak + j;
+  const int64_t s = ar * g.am + i;
+  const int64_t r = perm ? perm[t * g.lt_m + s] : s;
+  return (ti * g.lt_m + r) * g.K + tj * g.lt_k + ac * g.ak + j;
 }
 
 // Union bit of position p of LT t: any of the Q area weights kept.
-inline bool union_on(const UnionGeometry& g, const uint16_t* W, const uint8_t* mask, int64_t t, int64_t p) {
+inline bool union_on(const UnionGeometry& g, const int32_t* perm, const uint16_t* W, const uint8_t* mask, int64_t t,
+                     int64_t p) {
   for (int64_t q = 0; q < g.Q; ++q)
-    if (is_kept(W, mask, union_elem(g, t, q, p))) return true;
+    if (is_kept(W, mask, union_elem(g, perm, t, q, p))) return true;
   return false;
+}
+
+// Every LT's row order a permutation of its rows.
+bool valid_row_orders(const UnionGeometry& g, const int32_t* perm) {
+  std::vector<uint8_t> seen(static_cast<size_t>(g.lt_m));
+  for (int64_t t = 0; t < g.nlt; ++t) {
+    std::fill(seen.begin(), seen.end(), uint8_t(0));
+    for (int64_t s = 0; s < g.lt_m; ++s) {
+      const int32_t r = perm[t * g.lt_m + s];
+      if (r < 0 || r >= g.lt_m || seen[static_cast<size_t>(r)]) return false;
+      seen[static_cast<size_t>(r)] = 1;
+    }
+  }
+  return true;
 }
 
 // Kept count of every column tile (GTile t, column c at t * 16 + c), their
@@ -185,13 +204,14 @@ void count_cbc(const CbcGeometry& g, const uint16_t* W, const uint8_t* mask, std
 }
 
 // offsets[t] = payload elements before LT t (Q times the active positions).
-usw_status count_union(const UnionGeometry& g, const uint16_t* W, const uint8_t* mask, std::vector<int64_t>* off) {
+usw_status count_union(const UnionGeometry& g, const int32_t* perm, const uint16_t* W, const uint8_t* mask,
+                       std::vector<int64_t>* off) {
   off->assign(g.nlt + 1, 0);
   int64_t* o = off->data();
   parallel_for(g.nlt, [&](int64_t lo, int64_t hi) {
     for (int64_t t = lo; t < hi; ++t) {
       int64_t c = 0;
-      for (int64_t p = 0; p < g.am * g.ak; ++p) c += union_on(g, W, mask, t, p);
+      for (int64_t p = 0; p < g.am * g.ak; ++p) c += union_on(g, perm, W, mask, t, p);
       o[t + 1] = g.Q * c;
     }
   });
@@ -212,6 +232,96 @@ size_t values_alloc_bytes(int32_t val_type, int64_t nnz) {
 }  // namespace usw
 
 using namespace usw;
+
+namespace {
+
+usw_status union_query_impl(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m, int32_t lt_k,
+                            int32_t r_a, int32_t c_a, int32_t val_type, const int32_t* perm, int64_t* payload,
+                            size_t* bytes_bitmaps, size_t* bytes_offsets, size_t* bytes_values,
+                            size_t* bytes_values_alloc, size_t* bytes_scales) {
+  if (!W && !mask) return USW_ERR_NULL_ARG;
+  UnionGeometry g;
+  usw_status st = make_union_geometry(M, K, lt_m, lt_k, r_a, c_a, &g);
+  if (st) return st;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (perm && (g.lt_m > 256 || !valid_row_orders(g, perm))) return USW_ERR_BAD_SHAPE;
+  std::vector<int64_t> off;
+  st = count_union(g, perm, W, mask, &off);
+  if (st) return st;
+  const int64_t n = off[g.nlt];
+  if (payload) *payload = n;
+  if (bytes_bitmaps) *bytes_bitmaps = static_cast<size_t>(8 * g.nlt * g.nw);
+  if (bytes_offsets) *bytes_offsets = static_cast<size_t>(4 * (g.nlt + 1));
+  if (bytes_values) *bytes_values = values_logical_bytes(val_type, n);
+  if (bytes_values_alloc) *bytes_values_alloc = values_alloc_bytes(val_type, n);
+  if (bytes_scales) *bytes_scales = val_type == USW_VAL_I4 ? static_cast<size_t>(2 * M) : 0;
+  return USW_OK;
+}
+
+usw_status union_encode_impl(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
+                             int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type, const int32_t* perm,
+                             uint64_t* bitmaps, uint32_t* offsets, void* values, size_t values_capacity,
+                             uint16_t* scales, uint8_t* rowmap) {
+  if (!W || !bitmaps || !offsets || !values) return USW_ERR_NULL_ARG;
+  UnionGeometry g;
+  usw_status st = make_union_geometry(M, K, lt_m, lt_k, r_a, c_a, &g);
+  if (st) return st;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (val_type == USW_VAL_I4 && !scales) return USW_ERR_NULL_ARG;
+  if (perm && (g.lt_m > 256 || !valid_row_orders(g, perm))) return USW_ERR_BAD_SHAPE;
+  std::vector<int64_t> off;
+  st = count_union(g, perm, W, mask, &off);
+  if (st) return st;
+  const int64_t total = off[g.nlt];
+  const size_t logical = values_logical_bytes(val_type, total);
+  if (values_capacity < logical) return USW_ERR_CAPACITY;
+  for (int64_t i = 0; i <= g.nlt; ++i) offsets[i] = static_cast<uint32_t>(off[i]);
+  if (perm)
+    for (int64_t t = 0; t < g.nlt; ++t)
+      for (int64_t s = 0; s < g.lt_m; ++s) rowmap[t * g.lt_m + perm[t * g.lt_m + s]] = static_cast<uint8_t>(s);
+
+  // INT4: scales and codes of the rows of W, whatever LT row they are
+  // stored in.
+  std::vector<double> rscale;
+  if (val_type == USW_VAL_I4) rscale = row_scales(W, mask, M, K, scales);
+  std::vector<int8_t> q;
+  if (val_type == USW_VAL_I4) q.assign(static_cast<size_t>(total), 0);
+  uint16_t* v16 = static_cast<uint16_t*>(values);
+
+  // Per LT: the union words, then the Q area streams, each holding the area's
+  // weight (0 where pruned) at every active position in row-major order.
+  parallel_for(g.nlt, [&](int64_t lo, int64_t hi) {
+    std::vector<int64_t> active;
+    for (int64_t t = lo; t < hi; ++t) {
+      active.clear();
+      uint64_t* words = bitmaps + t * g.nw;
+      for (int64_t w = 0; w < g.nw; ++w) words[w] = 0;
+      for (int64_t p = 0; p < g.am * g.ak; ++p)
+        if (union_on(g, perm, W, mask, t, p)) {
+          words[p >> 6] |= 1ull << (p & 63);
+          active.push_back(p);
+        }
+      const int64_t P = static_cast<int64_t>(active.size());
+      for (int64_t qa = 0; qa < g.Q; ++qa)
+        for (int64_t r = 0; r < P; ++r) {
+          const int64_t lin = union_elem(g, perm, t, qa, active[static_cast<size_t>(r)]);
+          const int64_t idx = off[t] + qa * P + r;
+          const bool kept = is_kept(W, mask, lin);
+          if (val_type == USW_VAL_F16)
+            v16[idx] = kept ? W[lin] : uint16_t(0);
+          else
+            q[static_cast<size_t>(idx)] = kept ? i4_code(W[lin], rscale[lin / g.K]) : int8_t(0);
+        }
+    }
+  });
+
+  uint8_t* vb = static_cast<uint8_t*>(values);
+  if (val_type == USW_VAL_I4) pack_i4(q, total, vb);
+  if (values_capacity > logical) std::memset(vb + logical, 0, values_capacity - logical);
+  return USW_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -429,78 +539,33 @@ usw_status usw_union_encode_query(const uint16_t* W, const uint8_t* mask, int32_
                                   int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type, int64_t* payload,
                                   size_t* bytes_bitmaps, size_t* bytes_offsets, size_t* bytes_values,
                                   size_t* bytes_values_alloc, size_t* bytes_scales) {
-  if (!W && !mask) return USW_ERR_NULL_ARG;
-  UnionGeometry g;
-  usw_status st = make_union_geometry(M, K, lt_m, lt_k, r_a, c_a, &g);
-  if (st) return st;
-  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
-  std::vector<int64_t> off;
-  st = count_union(g, W, mask, &off);
-  if (st) return st;
-  const int64_t n = off[g.nlt];
-  if (payload) *payload = n;
-  if (bytes_bitmaps) *bytes_bitmaps = static_cast<size_t>(8 * g.nlt * g.nw);
-  if (bytes_offsets) *bytes_offsets = static_cast<size_t>(4 * (g.nlt + 1));
-  if (bytes_values) *bytes_values = values_logical_bytes(val_type, n);
-  if (bytes_values_alloc) *bytes_values_alloc = values_alloc_bytes(val_type, n);
-  if (bytes_scales) *bytes_scales = val_type == USW_VAL_I4 ? static_cast<size_t>(2 * M) : 0;
-  return USW_OK;
+  return union_query_impl(W, mask, M, K, lt_m, lt_k, r_a, c_a, val_type, nullptr, payload, bytes_bitmaps,
+                          bytes_offsets, bytes_values, bytes_values_alloc, bytes_scales);
 }
 
 usw_status usw_union_encode(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
                             int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type, uint64_t* bitmaps,
                             uint32_t* offsets, void* values, size_t values_capacity, uint16_t* scales) {
-  if (!W || !bitmaps || !offsets || !values) return USW_ERR_NULL_ARG;
-  UnionGeometry g;
-  usw_status st = make_union_geometry(M, K, lt_m, lt_k, r_a, c_a, &g);
-  if (st) return st;
-  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
-  if (val_type == USW_VAL_I4 && !scales) return USW_ERR_NULL_ARG;
-  std::vector<int64_t> off;
-  st = count_union(g, W, mask, &off);
-  if (st) return st;
-  const int64_t total = off[g.nlt];
-  const size_t logical = values_logical_bytes(val_type, total);
-  if (values_capacity < logical) return USW_ERR_CAPACITY;
-  for (int64_t i = 0; i <= g.nlt; ++i) offsets[i] = static_cast<uint32_t>(off[i]);
+  return union_encode_impl(W, mask, M, K, lt_m, lt_k, r_a, c_a, val_type, nullptr, bitmaps, offsets, values,
+                           values_capacity, scales, nullptr);
+}
 
-  std::vector<double> rscale;
-  if (val_type == USW_VAL_I4) rscale = row_scales(W, mask, M, K, scales);
-  std::vector<int8_t> q;
-  if (val_type == USW_VAL_I4) q.assign(static_cast<size_t>(total), 0);
-  uint16_t* v16 = static_cast<uint16_t*>(values);
+usw_status usw_union_encode_reordered_query(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K,
+                                            int32_t lt_m, int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type,
+                                            const int32_t* perm, int64_t* payload, size_t* bytes_values,
+                                            size_t* bytes_values_alloc) {
+  if (!perm) return USW_ERR_NULL_ARG;
+  return union_query_impl(W, mask, M, K, lt_m, lt_k, r_a, c_a, val_type, perm, payload, nullptr, nullptr,
+                          bytes_values, bytes_values_alloc, nullptr);
+}
 
-  // Per LT: the union words, then the Q area streams, each holding the area's
-  // weight (0 where pruned) at every active position in row-major order.
-  parallel_for(g.nlt, [&](int64_t lo, int64_t hi) {
-    std::vector<int64_t> active;
-    for (int64_t t = lo; t < hi; ++t) {
-      active.clear();
-      uint64_t* words = bitmaps + t * g.nw;
-      for (int64_t w = 0; w < g.nw; ++w) words[w] = 0;
-      for (int64_t p = 0; p < g.am * g.ak; ++p)
-        if (union_on(g, W, mask, t, p)) {
-          words[p >> 6] |= 1ull << (p & 63);
-          active.push_back(p);
-        }
-      const int64_t P = static_cast<int64_t>(active.size());
-      for (int64_t qa = 0; qa < g.Q; ++qa)
-        for (int64_t r = 0; r < P; ++r) {
-          const int64_t lin = union_elem(g, t, qa, active[static_cast<size_t>(r)]);
-          const int64_t idx = off[t] + qa * P + r;
-          const bool kept = is_kept(W, mask, lin);
-          if (val_type == USW_VAL_F16)
-            v16[idx] = kept ? W[lin] : uint16_t(0);
-          else
-            q[static_cast<size_t>(idx)] = kept ? i4_code(W[lin], rscale[lin / g.K]) : int8_t(0);
-        }
-    }
-  });
-
-  uint8_t* vb = static_cast<uint8_t*>(values);
-  if (val_type == USW_VAL_I4) pack_i4(q, total, vb);
-  if (values_capacity > logical) std::memset(vb + logical, 0, values_capacity - logical);
-  return USW_OK;
+usw_status usw_union_encode_reordered(const uint16_t* W, const uint8_t* mask, int32_t M, int32_t K, int32_t lt_m,
+                                      int32_t lt_k, int32_t r_a, int32_t c_a, int32_t val_type, const int32_t* perm,
+                                      uint64_t* bitmaps, uint32_t* offsets, void* values, size_t values_capacity,
+                                      uint16_t* scales, uint8_t* rowmap) {
+  if (!perm || !rowmap) return USW_ERR_NULL_ARG;
+  return union_encode_impl(W, mask, M, K, lt_m, lt_k, r_a, c_a, val_type, perm, bitmaps, offsets, values,
+                           values_capacity, scales, rowmap);
 }
 
 usw_status usw_union_validate(const usw_union_fmt* f) {
@@ -520,6 +585,18 @@ usw_status usw_union_validate(const usw_union_fmt* f) {
     int64_t c = 0;
     for (int64_t w = 0; w < g.nw; ++w) c += __builtin_popcountll(f->bitmaps[t * g.nw + w]);
     if (g.Q * c != static_cast<int64_t>(f->offsets[t + 1] - f->offsets[t])) return USW_ERR_CORRUPT;
+  }
+  if (f->rowmap) {
+    if (g.lt_m > 256) return USW_ERR_BAD_SHAPE;
+    std::vector<uint8_t> seen(static_cast<size_t>(g.lt_m));
+    for (int64_t t = 0; t < g.nlt; ++t) {
+      std::fill(seen.begin(), seen.end(), uint8_t(0));
+      for (int64_t r = 0; r < g.lt_m; ++r) {
+        const uint8_t s = f->rowmap[t * g.lt_m + r];
+        if (s >= g.lt_m || seen[s]) return USW_ERR_CORRUPT;
+        seen[s] = 1;
+      }
+    }
   }
   return USW_OK;
 }

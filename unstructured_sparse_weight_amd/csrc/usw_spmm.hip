@@ -1005,7 +1005,7 @@ usw_status launch_call(const usw_fmt* f, const usw::Geometry& g, const CallPlan&
 
   for (int n0 = 0; n0 < N; n0 += p.nchunk) {
     const int nc = std::min(p.nchunk, N - n0);
-    Args a;
+    Args a{};
     a.bitmaps = f->bitmaps;
     a.offsets = f->offsets;
     a.values = static_cast<const uint8_t*>(f->values);

@@ -250,6 +250,190 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// 16 x 64 LTs (2 x 2 areas of 8 x 32), optionally with reordered rows
+// ---------------------------------------------------------------------------
+//
+// The LT height the row-reordering solver handles.  Bitmap-aware row
+// reordering ("UnionSparse", section on bitmap-aware row reordering)
+// rearranges each LT's rows before compression, so the stored rows of one LT
+// are a permutation of the rows of W it covers, a different one per LT.
+// Partial products of different LTs can only be summed once they sit on the
+// rows of W; here that happens before the products: the lane that holds row
+// r of W in an MFMA fragment rebuilds it from the stored row the LT's rowmap
+// names, so every accumulator row is a row of W across all LTs.
+//
+//   * One workgroup owns one 64-row strip (four LT rows) and a range of LT
+//     columns; wave w streams LT row 4 gi + w over that range (its LTs are
+//     consecutive in memory), one LT ahead in registers, the current one in
+//     the wave's LDS buffer.  Each wave owns 16 rows of the strip outright.
+//   * Lane l (i = l % 16, g = l / 16) holds row i of the LT and columns
+//     8 g .. 8 g + 7 of each 32-column area column ks.  Its stored row is
+//     s = rowmap[i] (s = i without a rowmap): logical union row s % 8, area
+//     row s / 8.  The union byte g of that logical row, its rank (from a
+//     per-LT table of 8 rows written with a DPP prefix scan) and its v_perm
+//     selectors serve both area columns: the two area rows' payload sits at
+//     rank + q P_t in streams q = 2 (s / 8) + ks (the LSPD gather).
+//   * One LT holds at most 4 x 256 nibbles, so one 16-byte piece per lane
+//     covers its payload and head.
+
+constexpr int kU16Vbuf = 1024 + 64;          // wave's LDS payload buffer (+ what a window reads past it)
+constexpr int kU16RowTab = 8 * 8;            // per logical row: its bits and the rank of its first bit
+constexpr int kU16Waves = 4;
+constexpr int kU16Threads = 64 * kU16Waves;
+
+template <int NB>
+struct U16Slot {
+  u32x4_t v;           // lane's 16-byte piece of the LT's payload
+  uint32_t rowbits;    // lanes 0-7: union row (dword) l of the LT
+  uint32_t srow;       // stored row of the lane's row of W (0-15)
+  u32x4_t x[2][NB];
+  uint32_t delta;      // payload elements before the LT's first one in its first piece
+  uint32_t P;          // active union positions of the LT (wave-uniform)
+};
+
+// Issue the loads of LT (tr, c), whose payload occupies elements [o0, o1).
+template <int NB>
+__device__ __forceinline__ void u16slot_load(U16Slot<NB>& s, const Args& a, int tr, int c, int lane, uint32_t o0,
+                                             uint32_t o1) {
+  const int64_t t = static_cast<int64_t>(tr) * a.Gc + c;
+  // 8 rows of 32 union bits: dword r of the LT's four words is row r.
+  s.rowbits = reinterpret_cast<const uint32_t*>(a.bitmaps + t * 4)[lane & 7];
+  s.srow = a.rowmap ? (static_cast<uint32_t>(a.rowmap[t * 16 + (lane & 15)]) & 15u) : static_cast<uint32_t>(lane & 15);
+  // At most 256 active positions; the clamp keeps windows inside the buffer
+  // even for offsets that disagree with the union words.
+  s.P = min((o1 - o0) >> 2, 256u);
+  const uint64_t top = a.values_alloc - 16;
+  const uint64_t a0 = min(chunk_start<true>(o0), top);
+  s.delta = chunk_delta<true>(o0, a0);
+  const uint32_t nch = min(chunk_count<true>(o1, a0), static_cast<uint32_t>((kU16Vbuf - 16) / 16));
+  const uint32_t last = min(nch > 0 ? nch - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
+  const int span = __builtin_amdgcn_readfirstlane(static_cast<int>(16 * (last + 1)));
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values + a0), 0, span, kBufferRsrcWord3);
+  s.v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * lane, 0, 0));
+  const int row = lane & 15, kb = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = min(nb * 16 + row, a.N - 1);
+      s.x[ks][nb] = *reinterpret_cast<const u32x4_t*>(a.X + static_cast<size_t>(n) * a.K + c * kGT + ks * 32 + kb * 8);
+    }
+}
+
+// Row table of an LT: entry r (r < 8) = {row r's bits, element position of
+// the row's first active value in the LDS buffer (area 0's stream)}.
+__device__ __forceinline__ void u16_tab_write(uint8_t* tab, uint32_t rowbits, uint32_t base, int lane) {
+  const uint32_t pc = lane < 8 ? __builtin_popcount(rowbits) : 0u;
+  const uint32_t excl = wave_inclusive_scan(pc) - pc;
+  if (lane < 8) {
+    u32x2_t e;
+    e.x = rowbits;
+    e.y = base + excl;
+    reinterpret_cast<u32x2_t*>(tab)[lane] = e;
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void u16_tile_mma(const U16Slot<NB>& cur, const uint8_t* smem, const uint8_t* tab,
+                                             const u32x2_t* lut, f32x4_t (&acc)[NB], int lane) {
+  const uint32_t sh = 8u * static_cast<uint32_t>(lane >> 4);
+  const u32x2_t e = reinterpret_cast<const u32x2_t*>(tab)[cur.srow & 7u];
+  const uint32_t byte = __builtin_amdgcn_ubfe(e.x, sh, 8);
+  const uint32_t rb = e.y + __builtin_popcount(e.x & ((1u << sh) - 1u));
+  const u32x2_t sel = lut[byte];
+  const uint32_t q0 = 2u * (cur.srow >> 3);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const half8_t av = expand_row_i4(lds_window_i4(smem, rb + (q0 + ks) * cur.P), sel);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, cur.x[ks][nb]), acc[nb], 0, 0,
+                                                       0);
+  }
+}
+
+template <int NB, bool OUT_F16, int OCC>
+__global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) u32x2_t lut[256];
+  constexpr int kStage = kU16Waves * (kU16Vbuf + kU16RowTab);
+  constexpr int kRed = kU16Waves * NB * 64 * 4 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStage > kRed ? kStage : kRed];
+  __shared__ uint32_t last_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nblk = static_cast<int>(gridDim.x);
+  const int b = static_cast<int>(blockIdx.x);
+  const int L = a.remap ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int gi = L / a.splits;
+  const int sidx = L - gi * a.splits;
+  const int tr = 4 * gi + w;   // the wave's LT row
+
+  lut[tid] = row_byte_selectors(static_cast<uint32_t>(tid));
+  __syncthreads();
+
+  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * sidx / a.splits);
+  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (sidx + 1) / a.splits);
+
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint8_t* vb = smem + w * kU16Vbuf;
+  uint8_t* tab = smem + kU16Waves * kU16Vbuf + w * kU16RowTab;
+  const uint32_t vb_elems = static_cast<uint32_t>(w * kU16Vbuf * 2);
+
+  // The wave's LT offsets, lane i holding offsets[t_begin + i] (the host
+  // keeps the count <= 63).
+  const int cnt = c_end - c_begin;
+  const int64_t t_begin = static_cast<int64_t>(tr) * a.Gc + c_begin;
+  const uint32_t ov = a.offsets[t_begin + min(lane, max(cnt, 0))];
+  auto off_at = [&](int c) -> uint32_t { return __builtin_amdgcn_readlane(ov, min(c - c_begin, 63)); };
+
+  if (cnt > 0) {
+    const int c_last = c_end - 1;
+    auto load = [&](U16Slot<NB>& sl, int c) {
+      const int cc = min(c, c_last);
+      u16slot_load(sl, a, tr, cc, lane, off_at(cc), off_at(cc + 1));
+    };
+    auto write_tab = [&](const U16Slot<NB>& sl) { u16_tab_write(tab, sl.rowbits, sl.delta + vb_elems, lane); };
+    U16Slot<NB> s[2];
+    load(s[0], c_begin);
+    write_tab(s[0]);
+    auto step = [&](U16Slot<NB>& cur, int c, U16Slot<NB>& nxt) {
+      load(nxt, c + 1);
+      reinterpret_cast<u32x4_t*>(vb)[lane] = cur.v;
+      wave_sync();
+      u16_tile_mma<NB>(cur, smem, tab, lut, acc, lane);
+      wave_sync();
+      write_tab(nxt);
+    };
+    int c = c_begin;
+    for (; c + 2 <= c_end; c += 2) {
+      step(s[0], c, s[1]);
+      step(s[1], c + 1, s[0]);
+    }
+    if (c < c_end) step(s[0], c, s[1]);
+  }
+
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);   // [waves][NB][64 lanes][4]
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4_t*>(red + ((w * NB + nb) * 64 + lane) * 4) = acc[nb];
+  __syncthreads();
+
+  finish_strip<NB, true, OUT_F16>(a, gi, sidx, kU16Threads, last_flag, [&](int n, int ml) {
+    // Strip rows ml .. ml+3 belong to wave ml / 16: D rows 4g .. 4g+3
+    // (g = (ml / 4) % 4), registers 0-3 of lane 16 g + n % 16.
+    const int ww = ml >> 4;
+    const int ln = 16 * ((ml >> 2) & 3) + (n & 15);
+    const int nb = n >> 4;
+    return *reinterpret_cast<const f32x4_t*>(red + ((ww * NB + nb) * 64 + ln) * 4);
+  });
+}
+
+// ---------------------------------------------------------------------------
 // Host dispatch
 // ---------------------------------------------------------------------------
 
@@ -261,27 +445,43 @@ constexpr int kOcc2 = 3;
 struct UPlan {
   int splits;
   int nchunk;   // tokens per pass (16 or 32)
+  bool lt16;    // 16 x 64 LTs (union16_decode_kernel)
 };
+
+// Waves per SIMD of the 16-row-LT kernel: 6 up to 16 tokens, 3 for 17..32.
+constexpr int kOcc16a = 6;
+constexpr int kOcc16b = 3;
+
+// 64-row strips of the matrix (one workgroup's rows).
+int64_t union_strips(const usw::UnionGeometry& g) { return g.M / 64; }
 
 UPlan union_plan(const usw::UnionGeometry& g, int N, int splits_req) {
   UPlan p;
   p.nchunk = N <= 16 ? 16 : 32;
-  const int occ = N <= 16 ? kOcc1 : kOcc2;
+  p.lt16 = g.lt_m == 16;
+  const int64_t strips = union_strips(g);
+  // Waves that stream one LT column each per step: four per workgroup for
+  // 64-row LTs (a wave takes a quarter of the columns), one per LT row for
+  // 16-row LTs (every wave takes all the workgroup's columns).
+  const int64_t per_split = p.lt16 ? 1 : kUWaves;
+  const int occ = p.lt16 ? (N <= 16 ? kOcc16a : kOcc16b) : (N <= 16 ? kOcc1 : kOcc2);
   int64_t s = splits_req;
   if (s <= 0) {
     // About one round of resident workgroups, each wave keeping at least 3
     // LTs to stream.
     const int64_t target = 256 * 4 * occ / kUWaves;
-    s = std::max<int64_t>(1, (target + g.lr / 2) / g.lr);
-    s = std::min<int64_t>(s, std::max<int64_t>(1, g.lc / (kUWaves * 3)));
+    s = std::max<int64_t>(1, (target + strips / 2) / strips);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, g.lc / (per_split * 3)));
   }
-  const int64_t smax = std::max<int64_t>(1, g.lc / kUWaves);
-  const int64_t smin = (g.lc + 63 * kUWaves - 1) / (63 * kUWaves);
+  const int64_t smax = std::max<int64_t>(1, g.lc / per_split);
+  const int64_t smin = (g.lc + 63 * per_split - 1) / (63 * per_split);
   p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
   return p;
 }
 
-size_t union_counter_bytes(const usw::UnionGeometry& g) { return (static_cast<size_t>(4 * g.lr) + 255) & ~size_t(255); }
+size_t union_counter_bytes(const usw::UnionGeometry& g) {
+  return (static_cast<size_t>(4 * union_strips(g)) + 255) & ~size_t(255);
+}
 
 size_t union_workspace_bytes(const usw::UnionGeometry& g, const UPlan& p) {
   if (p.splits <= 1) return 0;
@@ -298,20 +498,31 @@ usw_status union_check(const usw_union_fmt* f, int32_t y_type, int32_t N, usw::U
   if (y_type != USW_OUT_F16 && y_type != USW_OUT_F32) return USW_ERR_BAD_DTYPE;
   if (f->reserved != 0) return USW_ERR_BAD_SHAPE;
   if (N < 1) return USW_ERR_BAD_N;
-  if (f->val_type != USW_VAL_I4 || f->lt_m != 64 || f->lt_k != 64 || f->r_a != 2 || f->c_a != 2)
+  if (f->val_type != USW_VAL_I4 || f->lt_k != 64 || f->r_a != 2 || f->c_a != 2) return USW_ERR_UNSUPPORTED;
+  if (f->lt_m == 64) {
+    if (f->rowmap) return USW_ERR_UNSUPPORTED;
+  } else if (f->lt_m != 16 || f->M % 64) {
     return USW_ERR_UNSUPPORTED;
+  }
   if (f->payload < 0 || f->payload >= (int64_t(1) << 32)) return USW_ERR_BAD_SHAPE;
   if (static_cast<int64_t>(N) * g->M > (int64_t(1) << 40)) return USW_ERR_BAD_SHAPE;
   return USW_OK;
 }
 
 template <int NB>
-void union_launch(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
+void union_launch(const Args& a, bool f16out, bool lt16, dim3 grid, hipStream_t s) {
   constexpr int occ = NB == 1 ? kOcc1 : kOcc2;
-  if (f16out)
+  constexpr int occ16 = NB == 1 ? kOcc16a : kOcc16b;
+  if (lt16) {
+    if (f16out)
+      union16_decode_kernel<NB, true, occ16><<<grid, kU16Threads, 0, s>>>(a);
+    else
+      union16_decode_kernel<NB, false, occ16><<<grid, kU16Threads, 0, s>>>(a);
+  } else if (f16out) {
     union_decode_kernel<NB, true, occ><<<grid, kUThreads, 0, s>>>(a);
-  else
+  } else {
     union_decode_kernel<NB, false, occ><<<grid, kUThreads, 0, s>>>(a);
+  }
 }
 
 }  // namespace
@@ -349,17 +560,18 @@ usw_status usw_union_spmm(const usw_union_fmt* f, const uint16_t* X, void* Y, in
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return USW_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t nblk = g.lr * p.splits;
+  const int64_t nblk = union_strips(g) * p.splits;
   const dim3 grid(static_cast<unsigned>(nblk));
   const size_t ybytes = y_type == USW_OUT_F16 ? 2 : 4;
   const bool f16out = y_type == USW_OUT_F16;
   for (int n0 = 0; n0 < N; n0 += p.nchunk) {
     const int nc = std::min(p.nchunk, N - n0);
-    Args a;
+    Args a{};
     a.bitmaps = f->bitmaps;
     a.offsets = f->offsets;
     a.values = static_cast<const uint8_t*>(f->values);
     a.scales = f->scales;
+    a.rowmap = f->rowmap;
     a.X = X + static_cast<size_t>(n0) * g.K;
     a.Y = static_cast<uint8_t*>(Y) + static_cast<size_t>(n0) * g.M * ybytes;
     a.counters = need ? static_cast<uint32_t*>(ws) : nullptr;
@@ -372,9 +584,9 @@ usw_status usw_union_spmm(const usw_union_fmt* f, const uint16_t* X, void* Y, in
     a.splits = p.splits;
     a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
     if (nc > 16)
-      union_launch<2>(a, f16out, grid, s);
+      union_launch<2>(a, f16out, p.lt16, grid, s);
     else
-      union_launch<1>(a, f16out, grid, s);
+      union_launch<1>(a, f16out, p.lt16, grid, s);
     if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
   }
   return USW_OK;
