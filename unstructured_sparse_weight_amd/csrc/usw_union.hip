@@ -259,104 +259,134 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
 // are a permutation of the rows of W it covers, a different one per LT.
 // Partial products of different LTs can only be summed once they sit on the
 // rows of W; here that happens before the products: the lane that holds row
-// r of W in an MFMA fragment rebuilds it from the stored row the LT's rowmap
+// i of W in an MFMA fragment rebuilds it from the stored row the LT's rowmap
 // names, so every accumulator row is a row of W across all LTs.
 //
 //   * One workgroup owns one 64-row strip (four LT rows) and a range of LT
-//     columns; wave w streams LT row 4 gi + w over that range (its LTs are
-//     consecutive in memory), one LT ahead in registers, the current one in
-//     the wave's LDS buffer.  Each wave owns 16 rows of the strip outright.
-//   * Lane l (i = l % 16, g = l / 16) holds row i of the LT and columns
-//     8 g .. 8 g + 7 of each 32-column area column ks.  Its stored row is
-//     s = rowmap[i] (s = i without a rowmap): logical union row s % 8, area
-//     row s / 8.  The union byte g of that logical row, its rank (from a
-//     per-LT table of 8 rows written with a DPP prefix scan) and its v_perm
-//     selectors serve both area columns: the two area rows' payload sits at
-//     rank + q P_t in streams q = 2 (s / 8) + ks (the LSPD gather).
+//     columns; each of its waves streams its own run of columns, one column
+//     ahead in registers.  A column step takes the four stacked LTs
+//     f = 0..3 (LT row 4 gi + f): their union words, row maps and payloads
+//     are four separate ranges, and the column's X^T fragments are loaded
+//     once for all four.
+//   * Fragment (f, ks) is LT f's 16 rows by area column ks.  Lane l
+//     (i = l % 16, g = l / 16) holds row i of W within LT f and columns
+//     8 g .. 8 g + 7 of the area column.  Its stored row is s = rowmap_f[i]
+//     (s = i without a rowmap): logical union row s % 8, area row s / 8.  The
+//     union byte g of that row, its rank (from a table of the four LTs' 8
+//     rows, written with a DPP prefix scan) and its v_perm selectors serve
+//     both area columns: the payload sits at rank + q P_f in streams
+//     q = 2 (s / 8) + ks (the LSPD gather).
 //   * One LT holds at most 4 x 256 nibbles, so one 16-byte piece per lane
 //     covers its payload and head.
 
-constexpr int kU16Vbuf = 1024 + 64;          // wave's LDS payload buffer (+ what a window reads past it)
-constexpr int kU16RowTab = 8 * 8;            // per logical row: its bits and the rank of its first bit
+constexpr int kU16Vbuf = 1024 + 64;          // LDS payload buffer per LT (+ what a window reads past it)
+constexpr int kU16Tab = 32 * 8;              // 4 LTs x 8 logical rows: bits and the rank of the first bit
 constexpr int kU16Waves = 4;
 constexpr int kU16Threads = 64 * kU16Waves;
+constexpr int kU16MaxCols = 15;              // LT columns per wave: 16 offsets per LT row in one register
 
 template <int NB>
 struct U16Slot {
-  u32x4_t v;           // lane's 16-byte piece of the LT's payload
-  uint32_t rowbits;    // lanes 0-7: union row (dword) l of the LT
-  uint32_t srow;       // stored row of the lane's row of W (0-15)
+  u32x4_t v[4];        // lane's 16-byte piece of LT f's payload
+  uint32_t rowbits;    // lane l < 32: union row l % 8 of LT l / 8
+  uint32_t srow[4];    // stored row of the lane's row of W in LT f (with a rowmap)
   u32x4_t x[2][NB];
-  uint32_t delta;      // payload elements before the LT's first one in its first piece
-  uint32_t P;          // active union positions of the LT (wave-uniform)
+  uint32_t delta[4];   // payload elements before LT f's first one in its first piece (wave-uniform)
+  uint32_t P[4];       // active union positions of LT f (wave-uniform)
 };
 
-// Issue the loads of LT (tr, c), whose payload occupies elements [o0, o1).
+// Issue the loads of LT column c of strip gi; o0[f], o1[f] frame LT f's
+// payload elements.
 template <int NB>
-__device__ __forceinline__ void u16slot_load(U16Slot<NB>& s, const Args& a, int tr, int c, int lane, uint32_t o0,
-                                             uint32_t o1) {
-  const int64_t t = static_cast<int64_t>(tr) * a.Gc + c;
-  // 8 rows of 32 union bits: dword r of the LT's four words is row r.
-  s.rowbits = reinterpret_cast<const uint32_t*>(a.bitmaps + t * 4)[lane & 7];
-  s.srow = a.rowmap ? (static_cast<uint32_t>(a.rowmap[t * 16 + (lane & 15)]) & 15u) : static_cast<uint32_t>(lane & 15);
-  // At most 256 active positions; the clamp keeps windows inside the buffer
-  // even for offsets that disagree with the union words.
-  s.P = min((o1 - o0) >> 2, 256u);
+__device__ __forceinline__ void u16slot_load(U16Slot<NB>& s, const Args& a, int gi, int c, int lane,
+                                             const uint32_t (&o0)[4], const uint32_t (&o1)[4]) {
+  const int64_t t0 = static_cast<int64_t>(4 * gi) * a.Gc + c;   // LT f is t0 + f Gc
+  // Union rows first (the rank table is written while the rest may still be
+  // in flight): lane l < 32 loads dword l % 8 of LT l / 8's four words.
+  const int fl = (lane >> 3) & 3;
+  s.rowbits = reinterpret_cast<const uint32_t*>(a.bitmaps + (t0 + static_cast<int64_t>(fl) * a.Gc) * 4)[lane & 7];
+  const int i = lane & 15;
+  // The map byte of the lane's row in each LT, as vector loads: they are
+  // counted in order with the slot's other loads, so the compute waits for
+  // exactly this slot (scalar loads return out of order, and a wait for one
+  // of them waits for all, the next slot's included).
+  if (a.rowmap) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) s.srow[f] = a.rowmap[(t0 + static_cast<int64_t>(f) * a.Gc) * 16 + i];
+  }
   const uint64_t top = a.values_alloc - 16;
-  const uint64_t a0 = min(chunk_start<true>(o0), top);
-  s.delta = chunk_delta<true>(o0, a0);
-  const uint32_t nch = min(chunk_count<true>(o1, a0), static_cast<uint32_t>((kU16Vbuf - 16) / 16));
-  const uint32_t last = min(nch > 0 ? nch - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
-  const int span = __builtin_amdgcn_readfirstlane(static_cast<int>(16 * (last + 1)));
-  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values + a0), 0, span, kBufferRsrcWord3);
-  s.v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * lane, 0, 0));
-  const int row = lane & 15, kb = lane >> 4;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    // At most 256 active positions; the clamp keeps windows inside the
+    // buffer even for offsets that disagree with the union words.
+    s.P[f] = min((o1[f] - o0[f]) >> 2, 256u);
+    const uint64_t a0 = min(chunk_start<true>(o0[f]), top);
+    s.delta[f] = chunk_delta<true>(o0[f], a0);
+    const uint32_t nch = min(chunk_count<true>(o1[f], a0), static_cast<uint32_t>((kU16Vbuf - 16) / 16));
+    const uint32_t last = min(nch > 0 ? nch - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
+    const int span = __builtin_amdgcn_readfirstlane(static_cast<int>(16 * (last + 1)));
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values + a0), 0, span, kBufferRsrcWord3);
+    s.v[f] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * lane, 0, 0));
+  }
+  const int kb = lane >> 4;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int n = min(nb * 16 + row, a.N - 1);
+      const int n = min(nb * 16 + i, a.N - 1);
       s.x[ks][nb] = *reinterpret_cast<const u32x4_t*>(a.X + static_cast<size_t>(n) * a.K + c * kGT + ks * 32 + kb * 8);
     }
 }
 
-// Row table of an LT: entry r (r < 8) = {row r's bits, element position of
-// the row's first active value in the LDS buffer (area 0's stream)}.
-__device__ __forceinline__ void u16_tab_write(uint8_t* tab, uint32_t rowbits, uint32_t base, int lane) {
-  const uint32_t pc = lane < 8 ? __builtin_popcount(rowbits) : 0u;
+// Rank table of a column's four LTs: entry 8 f + r (r < 8) = {row r's bits,
+// element position of the row's first active value in LDS (area 0's
+// stream of LT f)}.  base[f]: where LT f's payload starts in LDS.
+__device__ __forceinline__ void u16_tab_write(uint8_t* tab, uint32_t rowbits, const uint32_t (&base)[4], int lane) {
+  const uint32_t pc = lane < 32 ? __builtin_popcount(rowbits) : 0u;
   const uint32_t excl = wave_inclusive_scan(pc) - pc;
-  if (lane < 8) {
+  const uint32_t first = __shfl(excl, lane & ~7);   // the prefix at the LT's first row
+  if (lane < 32) {
+    const int f = lane >> 3;
+    const uint32_t b = f == 0 ? base[0] : f == 1 ? base[1] : f == 2 ? base[2] : base[3];
     u32x2_t e;
     e.x = rowbits;
-    e.y = base + excl;
+    e.y = b + excl - first;
     reinterpret_cast<u32x2_t*>(tab)[lane] = e;
   }
 }
 
 template <int NB>
-__device__ __forceinline__ void u16_tile_mma(const U16Slot<NB>& cur, const uint8_t* smem, const uint8_t* tab,
-                                             const u32x2_t* lut, f32x4_t (&acc)[NB], int lane) {
+__device__ __forceinline__ void u16_tile_mma(const U16Slot<NB>& cur, bool mapped, const uint8_t* smem,
+                                             const uint8_t* tab, const u32x2_t* lut, f32x4_t (&acc)[4][NB],
+                                             int lane) {
   const uint32_t sh = 8u * static_cast<uint32_t>(lane >> 4);
-  const u32x2_t e = reinterpret_cast<const u32x2_t*>(tab)[cur.srow & 7u];
-  const uint32_t byte = __builtin_amdgcn_ubfe(e.x, sh, 8);
-  const uint32_t rb = e.y + __builtin_popcount(e.x & ((1u << sh) - 1u));
-  const u32x2_t sel = lut[byte];
-  const uint32_t q0 = 2u * (cur.srow >> 3);
+  const uint32_t pmask = (1u << sh) - 1u;
+  const int i = lane & 15;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const half8_t av = expand_row_i4(lds_window_i4(smem, rb + (q0 + ks) * cur.P), sel);
+  for (int f = 0; f < 4; ++f) {
+    // Stored row of the lane's row i of W: byte i of LT f's row map.
+    const uint32_t srow = mapped ? (cur.srow[f] & 15u) : static_cast<uint32_t>(i);
+    const u32x2_t e = reinterpret_cast<const u32x2_t*>(tab)[8 * f + (srow & 7u)];
+    const uint32_t byte = __builtin_amdgcn_ubfe(e.x, sh, 8);
+    const uint32_t rb = e.y + __builtin_popcount(e.x & pmask);
+    const u32x2_t sel = lut[byte];
+    const uint32_t q0 = 2u * (srow >> 3);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, cur.x[ks][nb]), acc[nb], 0, 0,
-                                                       0);
+    for (int ks = 0; ks < 2; ++ks) {
+      const half8_t av = expand_row_i4(lds_window_i4(smem, rb + (q0 + ks) * cur.P[f]), sel);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[f][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, cur.x[ks][nb]),
+                                                            acc[f][nb], 0, 0, 0);
+    }
   }
 }
 
 template <int NB, bool OUT_F16, int OCC>
 __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) u32x2_t lut[256];
-  constexpr int kStage = kU16Waves * (kU16Vbuf + kU16RowTab);
-  constexpr int kRed = kU16Waves * NB * 64 * 4 * 4;
+  constexpr int kStage = kU16Waves * (4 * kU16Vbuf + kU16Tab);
+  constexpr int kRed = kU16Waves * 4 * NB * 64 * 4 * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStage > kRed ? kStage : kRed];
   __shared__ uint32_t last_flag;
 
@@ -368,44 +398,68 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
   const int L = a.remap ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
   const int gi = L / a.splits;
   const int sidx = L - gi * a.splits;
-  const int tr = 4 * gi + w;   // the wave's LT row
 
   lut[tid] = row_byte_selectors(static_cast<uint32_t>(tid));
   __syncthreads();
 
-  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * sidx / a.splits);
-  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (sidx + 1) / a.splits);
+  // Columns of LTs this wave streams (the host keeps the count <= 15).
+  const int parts = a.splits * kU16Waves;
+  const int qw = sidx * kU16Waves + w;
+  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * qw / parts);
+  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (qw + 1) / parts);
 
-  f32x4_t acc[NB];
+  f32x4_t acc[4][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[f][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint8_t* vb = smem + w * kU16Vbuf;
-  uint8_t* tab = smem + kU16Waves * kU16Vbuf + w * kU16RowTab;
-  const uint32_t vb_elems = static_cast<uint32_t>(w * kU16Vbuf * 2);
+  uint8_t* vb = smem + w * 4 * kU16Vbuf;
+  uint8_t* tab = smem + kU16Waves * 4 * kU16Vbuf + w * kU16Tab;
+  // LT f's payload buffer, in elements (nibbles) from the start of smem.
+  const uint32_t vb_elems = static_cast<uint32_t>(w * 4 * kU16Vbuf * 2);
 
-  // The wave's LT offsets, lane i holding offsets[t_begin + i] (the host
-  // keeps the count <= 63).
+  // The LT offsets of the wave's columns: lane 16 f + j holds
+  // offsets[(4 gi + f) Gc + c_begin + j] for j <= count.
   const int cnt = c_end - c_begin;
-  const int64_t t_begin = static_cast<int64_t>(tr) * a.Gc + c_begin;
-  const uint32_t ov = a.offsets[t_begin + min(lane, max(cnt, 0))];
-  auto off_at = [&](int c) -> uint32_t { return __builtin_amdgcn_readlane(ov, min(c - c_begin, 63)); };
+  const int fo = lane >> 4, jo = lane & 15;
+  const uint32_t ov = a.offsets[static_cast<int64_t>(4 * gi + fo) * a.Gc + c_begin + min(jo, max(cnt, 0))];
+  auto offs = [&](int c, uint32_t (&o0)[4], uint32_t (&o1)[4]) {
+    const int j = min(c - c_begin, 15);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      o0[f] = __builtin_amdgcn_readlane(ov, 16 * f + j);
+      o1[f] = __builtin_amdgcn_readlane(ov, 16 * f + min(j + 1, 15));
+    }
+  };
 
+  const bool mapped = a.rowmap != nullptr;
   if (cnt > 0) {
     const int c_last = c_end - 1;
     auto load = [&](U16Slot<NB>& sl, int c) {
       const int cc = min(c, c_last);
-      u16slot_load(sl, a, tr, cc, lane, off_at(cc), off_at(cc + 1));
+      uint32_t o0[4], o1[4];
+      offs(cc, o0, o1);
+      u16slot_load(sl, a, gi, cc, lane, o0, o1);
     };
-    auto write_tab = [&](const U16Slot<NB>& sl) { u16_tab_write(tab, sl.rowbits, sl.delta + vb_elems, lane); };
+    auto commit = [&](const U16Slot<NB>& sl) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) reinterpret_cast<u32x4_t*>(vb + f * kU16Vbuf)[lane] = sl.v[f];
+    };
+    auto write_tab = [&](const U16Slot<NB>& sl) {
+      uint32_t base[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) base[f] = sl.delta[f] + vb_elems + static_cast<uint32_t>(f * kU16Vbuf * 2);
+      u16_tab_write(tab, sl.rowbits, base, lane);
+    };
     U16Slot<NB> s[2];
     load(s[0], c_begin);
     write_tab(s[0]);
     auto step = [&](U16Slot<NB>& cur, int c, U16Slot<NB>& nxt) {
       load(nxt, c + 1);
-      reinterpret_cast<u32x4_t*>(vb)[lane] = cur.v;
+      commit(cur);
       wave_sync();
-      u16_tile_mma<NB>(cur, smem, tab, lut, acc, lane);
+      u16_tile_mma<NB>(cur, mapped, smem, tab, lut, acc, lane);
       wave_sync();
       write_tab(nxt);
     };
@@ -417,19 +471,27 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
     if (c < c_end) step(s[0], c, s[1]);
   }
 
+  // Workgroup reduction over waves (fixed order).
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);   // [waves][NB][64 lanes][4]
+  float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4_t*>(red + ((w * NB + nb) * 64 + lane) * 4) = acc[nb];
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb];
   __syncthreads();
 
   finish_strip<NB, true, OUT_F16>(a, gi, sidx, kU16Threads, last_flag, [&](int n, int ml) {
-    // Strip rows ml .. ml+3 belong to wave ml / 16: D rows 4g .. 4g+3
-    // (g = (ml / 4) % 4), registers 0-3 of lane 16 g + n % 16.
-    const int ww = ml >> 4;
+    // Strip rows ml .. ml+3 are D rows 4g .. 4g+3 (g = (ml / 4) % 4) of
+    // LT ml / 16: registers 0-3 of lane 16 g + n % 16.
+    const int f = ml >> 4;
     const int ln = 16 * ((ml >> 2) & 3) + (n & 15);
     const int nb = n >> 4;
-    return *reinterpret_cast<const f32x4_t*>(red + ((ww * NB + nb) * 64 + ln) * 4);
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < kU16Waves; ++ww)
+      sum += *reinterpret_cast<const f32x4_t*>(red + (((ww * 4 + f) * NB + nb) * 64 + ln) * 4);
+    return sum;
   });
 }
 
@@ -448,9 +510,9 @@ struct UPlan {
   bool lt16;    // 16 x 64 LTs (union16_decode_kernel)
 };
 
-// Waves per SIMD of the 16-row-LT kernel: 6 up to 16 tokens, 3 for 17..32.
-constexpr int kOcc16a = 6;
-constexpr int kOcc16b = 3;
+// Waves per SIMD of the 16-row-LT kernel: 4 up to 16 tokens, 2 for 17..32.
+constexpr int kOcc16a = 4;
+constexpr int kOcc16b = 2;
 
 // 64-row strips of the matrix (one workgroup's rows).
 int64_t union_strips(const usw::UnionGeometry& g) { return g.M / 64; }
@@ -460,10 +522,11 @@ UPlan union_plan(const usw::UnionGeometry& g, int N, int splits_req) {
   p.nchunk = N <= 16 ? 16 : 32;
   p.lt16 = g.lt_m == 16;
   const int64_t strips = union_strips(g);
-  // Waves that stream one LT column each per step: four per workgroup for
-  // 64-row LTs (a wave takes a quarter of the columns), one per LT row for
-  // 16-row LTs (every wave takes all the workgroup's columns).
-  const int64_t per_split = p.lt16 ? 1 : kUWaves;
+  // The four waves of a workgroup share its LT columns; a wave keeps at most
+  // 63 columns' offsets (64-row LTs) or 15 (16-row LTs, four LT rows per
+  // register).
+  const int64_t per_split = kUWaves;
+  const int64_t max_cols = p.lt16 ? kU16MaxCols : 63;
   const int occ = p.lt16 ? (N <= 16 ? kOcc16a : kOcc16b) : (N <= 16 ? kOcc1 : kOcc2);
   int64_t s = splits_req;
   if (s <= 0) {
@@ -474,7 +537,7 @@ UPlan union_plan(const usw::UnionGeometry& g, int N, int splits_req) {
     s = std::min<int64_t>(s, std::max<int64_t>(1, g.lc / (per_split * 3)));
   }
   const int64_t smax = std::max<int64_t>(1, g.lc / per_split);
-  const int64_t smin = (g.lc + 63 * per_split - 1) / (63 * per_split);
+  const int64_t smin = (g.lc + max_cols * per_split - 1) / (max_cols * per_split);
   p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
   return p;
 }
