@@ -36,8 +36,10 @@ W_t[a_r H_L/R_A + i][a_c K_L/C_A + j]; offsets are uint32 payload-element
 counts; the mask is authoritative for the union (a kept exact zero makes its
 group active and stores its bit pattern; a pruned position of an active group
 stores zero).  INT4 payload uses the per-row rule and nibble packing of
-tca_bme (element 2i in the low nibble of byte i); activations stay fp16 (the
-format concerns the weights).  H_L K_L / Q must be a multiple of 64 so that
+tca_bme (element 2i in the low nibble of byte i), 2-bit payload (the W2 of
+the section's W2A4 kernel-level analysis) the same per-row rule with b = 2
+and four codes per byte (tca_bme); activations stay fp16 (the format
+concerns the weights).  H_L K_L / Q must be a multiple of 64 so that
 each LT owns whole words.
 """
 from __future__ import annotations
@@ -47,8 +49,8 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-from .tca_bme import (VAL_F16, VAL_I4, _check_inputs, masked_popcount, pack_nibbles, popcount,
-                      quantize_rows_i4, spmm_fp64, unpack_nibbles)
+from .tca_bme import (VAL_F16, VAL_I2, VAL_I4, _check_inputs, masked_popcount, pack_crumbs, pack_nibbles, popcount,
+                      quantize_rows_i2, quantize_rows_i4, spmm_fp64, unpack_crumbs, unpack_nibbles)
 
 
 # --------------------------------------------------------------------------
@@ -114,8 +116,8 @@ class UnionEncoded:
     payload: int               # stored payload elements, = offsets[NLT]
     bitmaps: np.ndarray        # uint64 [NWORDS]
     offsets: np.ndarray        # uint32 [NLT + 1]
-    values: np.ndarray         # F16: uint16 [payload]; I4: uint8 [ceil(payload / 2)]
-    scales: Optional[np.ndarray] = None   # I4: fp16 [M], per original row
+    values: np.ndarray         # F16: uint16 [payload]; I4: uint8 [ceil(payload / 2)]; I2: uint8 [ceil(payload / 4)]
+    scales: Optional[np.ndarray] = None   # I4, I2: fp16 [M], per original row
     # Reordered LTs only: uint8 [NLT][H_L]; rowmap[t][r] is the stored row of
     # LT t that holds the LT's original row r.  None: rows in natural order.
     rowmap: Optional[np.ndarray] = None
@@ -137,6 +139,9 @@ def _payload_source(W: np.ndarray, mask: np.ndarray, val_type: int):
     if val_type == VAL_I4:
         scales, q = quantize_rows_i4(W, mask)
         return q, scales
+    if val_type == VAL_I2:
+        scales, q = quantize_rows_i2(W, mask)
+        return q, scales
     raise ValueError("unknown value type")
 
 
@@ -144,7 +149,12 @@ def _finish(g: UnionGeometry, val_type: int, bits: np.ndarray, payload_seq: np.n
             offsets: np.ndarray, scales) -> UnionEncoded:
     words = np.packbits(bits.reshape(-1, 64).astype(np.uint8), axis=1, bitorder="little")
     bitmaps = words.view("<u8").reshape(-1).astype(np.uint64)
-    values = payload_seq.astype(np.uint16) if val_type == VAL_F16 else pack_nibbles(payload_seq.astype(np.int8))
+    if val_type == VAL_F16:
+        values = payload_seq.astype(np.uint16)
+    elif val_type == VAL_I4:
+        values = pack_nibbles(payload_seq.astype(np.int8))
+    else:
+        values = pack_crumbs(payload_seq.astype(np.int8))
     return UnionEncoded(g, val_type, int(offsets[-1]), bitmaps, offsets.astype(np.uint32), values, scales)
 
 
@@ -297,7 +307,9 @@ def _unpermute(enc: UnionEncoded, A: np.ndarray) -> np.ndarray:
 def _payload_values(enc: UnionEncoded) -> np.ndarray:
     if enc.val_type == VAL_F16:
         return enc.values.astype(np.uint16)
-    return unpack_nibbles(enc.values, enc.payload)
+    if enc.val_type == VAL_I4:
+        return unpack_nibbles(enc.values, enc.payload)
+    return unpack_crumbs(enc.values, enc.payload)
 
 
 def check_union(enc: UnionEncoded) -> None:

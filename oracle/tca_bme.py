@@ -37,6 +37,13 @@ even (0 when amax is 0), q = clamp(round_half_even(w / scale), -8, 7) in fp64
 (q = 0 when scale is 0).  Element 2i of the packed value stream is the low
 nibble of byte i, element 2i+1 the high nibble (two's complement); a trailing
 high nibble is 0.  Dequantised weight = q * scale, exact in fp64.
+
+2-bit values (the W2 payload of UnionSparse's W2A4 kernel-level analysis,
+read as weight-only like INT4; the pages give no rule): the same per-row rule
+with b = 2, i.e. range [-2, 1] and scale = fp16(amax / (2^(b-1) - 1)) =
+fp16(amax), q = clamp(round_half_even(w / scale), -2, 1).  Four codes per
+byte, element 4i in bits 0-1 of byte i up to element 4i+3 in bits 6-7 (two's
+complement), trailing bits 0.
 """
 from __future__ import annotations
 
@@ -47,6 +54,7 @@ import numpy as np
 
 VAL_F16 = 1
 VAL_I4 = 2
+VAL_I2 = 3
 
 
 # --------------------------------------------------------------------------
@@ -330,24 +338,57 @@ def fp16_rne(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float16)
 
 
-def quantize_rows_i4(W: np.ndarray, mask: np.ndarray):
-    """Per-row symmetric INT4 quantisation over the kept entries.
+def quantize_rows_int(W: np.ndarray, mask: np.ndarray, bits: int):
+    """Per-row symmetric b-bit quantisation over the kept entries: scale =
+    fp16(amax / (2^(b-1) - 1)), q = clamp(rint(w / scale), -2^(b-1),
+    2^(b-1) - 1) in fp64.
 
     Returns (scales fp16 [M], q int8 [M][K]) with q = 0 outside the mask.
     """
+    qmax = (1 << (bits - 1)) - 1
     Wd = W.astype(np.float64)
     absk = np.where(mask, np.abs(Wd), 0.0)
     amax = absk.max(axis=1) if W.shape[1] else np.zeros(W.shape[0])
-    scales = fp16_rne(amax / 7.0)
+    scales = fp16_rne(amax / float(qmax))
     s64 = scales.astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint(Wd / s64[:, None])
     # Zero scale (nothing but zeros kept), NaN scale (a kept NaN makes the
     # row maximum NaN) and a NaN quotient (inf / inf) all give code 0.
     q = np.where((s64[:, None] > 0) & ~np.isnan(q), q, 0.0)
-    q = np.clip(q, -8, 7)
+    q = np.clip(q, -qmax - 1, qmax)
     q = np.where(mask, q, 0.0).astype(np.int8)
     return scales, q
+
+
+def quantize_rows_i4(W: np.ndarray, mask: np.ndarray):
+    """Per-row symmetric INT4 quantisation over the kept entries (b = 4:
+    scale amax / 7, codes in [-8, 7])."""
+    return quantize_rows_int(W, mask, 4)
+
+
+def quantize_rows_i2(W: np.ndarray, mask: np.ndarray):
+    """Per-row symmetric 2-bit quantisation over the kept entries (b = 2:
+    scale amax / 1, codes in [-2, 1])."""
+    return quantize_rows_int(W, mask, 2)
+
+
+def pack_crumbs(q: np.ndarray) -> np.ndarray:
+    """Two's-complement 2-bit codes, element 4i + j in bits 2j, 2j+1 of byte i."""
+    u = (q.astype(np.int16) & 0x3).astype(np.uint8)
+    pad = (-u.size) % 4
+    if pad:
+        u = np.concatenate([u, np.zeros(pad, dtype=np.uint8)])
+    u = u.reshape(-1, 4)
+    return (u[:, 0] | (u[:, 1] << 2) | (u[:, 2] << 4) | (u[:, 3] << 6)).astype(np.uint8)
+
+
+def unpack_crumbs(packed: np.ndarray, n: int) -> np.ndarray:
+    u = np.empty(4 * packed.size, dtype=np.int8)
+    for j in range(4):
+        u[j::4] = ((packed >> (2 * j)) & 0x3).astype(np.int8)
+    u = u[:n]
+    return np.where(u >= 2, u - 4, u).astype(np.int8)
 
 
 def pack_nibbles(q: np.ndarray) -> np.ndarray:

@@ -91,6 +91,22 @@ def weight_int4_exact(M: int, K: int, rng: np.random.Generator, mask: np.ndarray
     return (q * np.exp2(e)[:, None]).astype(np.float16)
 
 
+def weight_int2_exact(M: int, K: int, rng: np.random.Generator, mask: np.ndarray) -> np.ndarray:
+    """fp16 weight whose per-row 2-bit quantisation is exact.
+
+    Row m holds q * 2^e_m with q in {-1, 0, 1} and one kept entry equal to
+    +-2^e_m, so the row's largest kept magnitude is the power of two 2^e_m
+    and every kept entry is an exact multiple of it.
+    """
+    e = rng.integers(-9, -3, size=M)
+    q = rng.integers(-1, 2, size=(M, K)).astype(np.float64)
+    for m in range(M):
+        kept = np.flatnonzero(mask[m])
+        if kept.size:
+            q[m, kept[rng.integers(kept.size)]] = 1.0 if rng.random() < 0.5 else -1.0
+    return (q * np.exp2(e)[:, None]).astype(np.float16)
+
+
 def activations_normal(N: int, K: int, rng: np.random.Generator) -> np.ndarray:
     """Activations X stored [N][K] fp16, entries N(0, 1) sampled in fp64."""
     return rng.normal(0.0, 1.0, size=(N, K)).astype(np.float16)
