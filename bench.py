@@ -54,7 +54,8 @@ def parse():
     p.add_argument("--K", type=int, default=5120)
     p.add_argument("--N", type=int, default=16)
     p.add_argument("--sparsity", type=float, default=0.5)
-    p.add_argument("--dtype", default="f16", choices=["f16", "i4"])
+    p.add_argument("--dtype", default="f16", choices=["f16", "i4", "i2"],
+                   help="value type: fp16, INT4, or 2-bit (union format only)")
     p.add_argument("--format", default="tca", choices=["tca", "union", "cbc", "encode", "encode_union", "encode_cbc"],
                    help="tca: TCA-BME bitmaps (usw_spmm); union: IE-BME union-mask INT4 with 64x64 tiles and 2x2"
                         " areas (usw_union_spmm; implies --dtype i4); cbc: Tiled-CBC spMspV with dynamic pruning"
@@ -172,8 +173,10 @@ def main():
     dev = torch.device("cuda:0")
     union = args.format == "union"
     cbc = args.format == "cbc"
-    if union:
+    if union and args.dtype not in ("i4", "i2"):
         args.dtype = "i4"
+    if not union and args.dtype == "i2":
+        raise SystemExit("2-bit values exist in the union format only (--format union --dtype i2)")
     if cbc:
         args.dtype, args.N = "f16", 1
     M, K, N, s = args.M, args.K, args.N, args.sparsity
@@ -183,7 +186,7 @@ def main():
     # recipe from 33 tokens on.
     prefill = args.dtype == "f16" and N > 96
     layer_id = {(20480, 5120): 2, (11008, 4096): 0, (4096, 11008): 1}.get((M, K), 0)
-    cfg_id = 5 if args.dtype == "i4" else (4 if N > 32 else 2)
+    cfg_id = 5 if args.dtype in ("i4", "i2") else (4 if N > 32 else 2)
 
     log(f"[bench] generating W {M}x{K} (magnitude pruning s={s}) and X [{N}][{K}]")
     W, mask, X = wl.config_case(cfg_id, M, K, N, s, layer_id=layer_id)
@@ -212,7 +215,7 @@ def main():
             log(f"[bench] row reordering {time.time() - t:.2f} s: active union entries {int(before.sum())}"
                 f" -> {int(after.sum())} ({100.0 * (1 - after.sum() / max(before.sum(), 1)):.2f}% fewer)")
             t = time.time()
-        h = usw.union_encode_host(W, mask, lt, (2, 2), "i4", perm=perms)
+        h = usw.union_encode_host(W, mask, lt, (2, 2), args.dtype, perm=perms)
         kept = int(mask.sum())
         log(f"[bench] host union encode {time.time() - t:.2f} s, payload={h.payload} for nnz={kept}"
             f" ({h.payload / max(kept, 1):.3f} stored per kept weight)")
@@ -414,7 +417,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if args.dtype == "f16" else "i4",
+        "dtype": args.dtype,
         "data": "synthetic (seeded N(0,0.02) weights, magnitude pruning, N(0,1) activations)",
         "config": {"workload": workload,
                    "format": "tiled_cbc_spmspv" if cbc else (
@@ -610,10 +613,11 @@ def cpu_baseline(W, mask, X, M, K, N, dtype, reps, union=False, cbc=False, tau=0
         enc = oc.encode_cbc(W, mask)
         product = lambda e, Xm: oc.spmspv(e, Xm[0], tau)  # noqa: E731
     elif union:
+        vt = ob.VAL_I2 if dtype == "i2" else ob.VAL_I4
         if perms is not None:
-            enc = ou.encode_union_reordered(W, mask, perms, lt[0], lt[1], 2, 2, ob.VAL_I4)
+            enc = ou.encode_union_reordered(W, mask, perms, lt[0], lt[1], 2, 2, vt)
         else:
-            enc = ou.encode_union(W, mask, lt[0], lt[1], 2, 2, ob.VAL_I4)
+            enc = ou.encode_union(W, mask, lt[0], lt[1], 2, 2, vt)
         product = ou.spmm_union
     else:
         enc = ob.encode(W, mask) if dtype == "f16" else ob.encode_i4(W, mask)

@@ -36,6 +36,13 @@
  *   payload but not the bitmap metadata ("UnionSparse", motivation section on
  *   the payload-to-metadata ratio).
  *
+ * 2-bit values (USW_VAL_I2, IE-BME union format only; the W2 payload of
+ *   "UnionSparse", kernel-level W2A4 analysis, weight-only like INT4): the
+ *   same rule with 2 bits, scale[m] = fp16_rne(max|w| / 1) and
+ *   q = clamp(round_half_even(w / scale[m]), -2, 1).  Element 4i + j of the
+ *   packed stream is bits 2j, 2j+1 of byte i (two's complement); trailing
+ *   bits are 0.
+ *
  * Layouts of the product: X is [N][K] fp16 row-major (one row per token, the
  * transposed activation tile the pages stage), Y is [N][M] row-major, fp16
  * (rounded to nearest even from the fp32 accumulator) or fp32.
@@ -77,6 +84,7 @@ typedef int32_t usw_status;
 
 #define USW_VAL_F16 1             /* fp16 values */
 #define USW_VAL_I4 2              /* INT4 values + fp16 per-row scales */
+#define USW_VAL_I2 3              /* 2-bit values + fp16 per-row scales (IE-BME union format only) */
 #define USW_OUT_F16 1             /* Y in fp16 */
 #define USW_OUT_F32 3             /* Y in fp32 */
 
@@ -314,13 +322,14 @@ typedef struct usw_union_fmt {
   int32_t M, K;             /* W is M x K */
   int32_t lt_m, lt_k;       /* LT shape */
   int32_t r_a, c_a;         /* area grid of an LT */
-  int32_t val_type;         /* USW_VAL_I4 (USW_VAL_F16 for host-side use only) */
+  int32_t val_type;         /* USW_VAL_I4 or USW_VAL_I2 (USW_VAL_F16 for host-side use only) */
   int32_t reserved;         /* must be 0 */
   int64_t payload;          /* stored payload elements = offsets[NLT] */
   const uint64_t* bitmaps;  /* [NLT * NW] */
   const uint32_t* offsets;  /* [NLT+1] */
-  const void* values;       /* I4: uint8 [ceil(payload/2)], padded as usw_union_encode_query says */
-  const uint16_t* scales;   /* I4: fp16 bits [M], one per row of W */
+  const void* values;       /* I4: uint8 [ceil(payload/2)], I2: [ceil(payload/4)], padded as
+                               usw_union_encode_query says */
+  const uint16_t* scales;   /* I4, I2: fp16 bits [M], one per row of W */
   const uint8_t* rowmap;    /* reordered LTs: [NLT * lt_m], entry t * lt_m + r = the stored row of LT t
                                that holds the LT's row r of W (usw_union_encode_reordered); NULL: every
                                LT stores its rows in order */

@@ -19,7 +19,7 @@ from typing import Optional
 
 import numpy as np
 
-from ._lib import (USW_OUT_F16, USW_OUT_F32, USW_VAL_F16, USW_VAL_I4, EXPORTED, UswCbcFmt, UswError,  # noqa: F401
+from ._lib import (USW_OUT_F16, USW_OUT_F32, USW_VAL_F16, USW_VAL_I2, USW_VAL_I4, EXPORTED, UswCbcFmt, UswError,  # noqa: F401
                    UswFmt, UswUnionFmt, check, lib)
 
 __all__ = ["HostEncoding", "Encoding", "encode_host", "encode", "to_device", "validate", "spmm",
@@ -28,7 +28,7 @@ __all__ = ["HostEncoding", "Encoding", "encode_host", "encode", "to_device", "va
            "union_workspace_bytes", "CbcHostEncoding", "CbcEncoding", "cbc_encode_host", "cbc_encode",
            "cbc_to_device", "cbc_validate", "cbc_spmspv", "cbc_workspace_bytes", "UswError", "lib"]
 
-_VAL = {"f16": USW_VAL_F16, "i4": USW_VAL_I4}
+_VAL = {"f16": USW_VAL_F16, "i4": USW_VAL_I4, "i2": USW_VAL_I2}
 
 
 @dataclass
@@ -235,7 +235,7 @@ def union_encode_host(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4"
     bitmaps = np.empty(b_bm // 8, dtype=np.uint64)
     offsets = np.empty(b_off // 4, dtype=np.uint32)
     values = np.empty(b_alloc, dtype=np.uint8)
-    scales = np.empty(M, dtype=np.uint16) if vt == USW_VAL_I4 else None
+    scales = np.empty(M, dtype=np.uint16) if vt != USW_VAL_F16 else None
     check(L.usw_union_encode(wp, mp, M, K, lt[0], lt[1], areas[0], areas[1], vt, bitmaps.ctypes.data,
                              offsets.ctypes.data, values.ctypes.data, b_alloc,
                              scales.ctypes.data if scales is not None else None), "usw_union_encode")
@@ -263,7 +263,7 @@ def _union_encode_reordered_host(W, mask, lt, areas, vt, perm) -> UnionHostEncod
     bitmaps = np.empty(b_bm // 8, dtype=np.uint64)
     offsets = np.empty(b_off // 4, dtype=np.uint32)
     values = np.empty(b_alloc.value, dtype=np.uint8)
-    scales = np.empty(M, dtype=np.uint16) if vt == USW_VAL_I4 else None
+    scales = np.empty(M, dtype=np.uint16) if vt != USW_VAL_F16 else None
     rowmap = np.empty(perm.size, dtype=np.uint8)
     check(L.usw_union_encode_reordered(wp, mp, *args, perm.ctypes.data, bitmaps.ctypes.data, offsets.ctypes.data,
                                        values.ctypes.data, b_alloc.value,

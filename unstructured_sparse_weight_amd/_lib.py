@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libusw.so")
 USW_OK = 0
 USW_VAL_F16 = 1
 USW_VAL_I4 = 2
+USW_VAL_I2 = 3
 USW_OUT_F16 = 1
 USW_OUT_F32 = 3
 

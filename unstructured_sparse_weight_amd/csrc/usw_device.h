@@ -201,6 +201,26 @@ __device__ __forceinline__ u32x2_t lds_window_i4(const uint8_t* buf, uint32_t e)
   return r;
 }
 
+// 8 packed 2-bit codes starting at code e of an LDS buffer, widened to
+// two's-complement nibbles (code k in nibble k, its sign bit copied into the
+// nibble's upper two bits) and split into the even (lo4) and odd (hi4)
+// nibbles, one per byte, as lds_window_i4 returns them.  v_alignbit uses
+// only the low five bits of its shift operand, here 2 * (e mod 16).
+__device__ __forceinline__ u32x2_t lds_window_i2(const uint8_t* buf, uint32_t e) {
+  const uint32_t ba = e >> 2;
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(buf + (ba & ~3u));
+  uint32_t t = __builtin_amdgcn_alignbit(p[1], p[0], e << 1) & 0xFFFFu;
+  t = (t | (t << 8)) & 0x00FF00FFu;   // codes 0-3 in byte 0, 4-7 in byte 2
+  t = (t | (t << 4)) & 0x0F0F0F0Fu;   // two codes per byte
+  t = (t | (t << 2)) & 0x33333333u;   // one code per nibble
+  const uint32_t sgn = t & 0x22222222u;
+  t |= (sgn << 1) | (sgn << 2);
+  u32x2_t r;
+  r.x = t & 0x0F0F0F0Fu;
+  r.y = (t >> 4) & 0x0F0F0F0Fu;
+  return r;
+}
+
 // The 8 fp16 slots of an INT4 row from its 8-nibble window (split into
 // lo4 / hi4 by lds_window_i4) and its selectors.
 __device__ __forceinline__ half8_t expand_row_i4(u32x2_t w8, u32x2_t sel) {
@@ -247,6 +267,33 @@ __device__ __forceinline__ half8_t rebuild_row(const uint8_t* vb, const uint32_t
     return expand_row_i4(lds_window_i4(vb, rb), reinterpret_cast<const u32x2_t*>(lut)[byte]);
   }
 }
+
+// Packed-code payloads of BITS = 4 or 2 bits per element: the 16-byte chunk
+// arithmetic of chunk_start / chunk_delta / chunk_count below, and the
+// 8-element window of a row.
+template <int BITS>
+struct Packed {
+  static_assert(BITS == 4 || BITS == 2, "4- or 2-bit codes");
+  static constexpr uint32_t kPerByte = 8 / BITS;
+  static constexpr int kShift = BITS == 4 ? 1 : 2;   // log2(kPerByte)
+  // Byte offset of the 16-byte chunk holding element e.
+  __device__ static uint64_t chunk_start(uint32_t e) { return (static_cast<uint64_t>(e) >> kShift) & ~15ull; }
+  // Elements of the first chunk that precede element e.
+  __device__ static uint32_t chunk_delta(uint32_t e, uint64_t a0) {
+    return static_cast<uint32_t>(e - kPerByte * a0);
+  }
+  // 16-byte chunks spanned by elements [e0, e1) counted from a0.
+  __device__ static uint32_t chunk_count(uint32_t e1, uint64_t a0) {
+    const uint64_t end = (static_cast<uint64_t>(e1) + kPerByte - 1) >> kShift;
+    return static_cast<uint32_t>((end - a0 + 15ull) >> 4);
+  }
+  __device__ static u32x2_t window(const uint8_t* buf, uint32_t e) {
+    if constexpr (BITS == 4)
+      return lds_window_i4(buf, e);
+    else
+      return lds_window_i2(buf, e);
+  }
+};
 
 // Byte offset of the 16-byte chunk holding value element e (fp16: 2 B per
 // element; INT4: 4 bits per element).

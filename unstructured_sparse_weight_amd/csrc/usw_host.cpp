@@ -111,13 +111,19 @@ usw_status count_groups(const Geometry& g, const uint16_t* W, const uint8_t* mas
 }
 
 size_t values_logical_bytes(int32_t val_type, int64_t nnz) {
-  return val_type == USW_VAL_F16 ? static_cast<size_t>(2 * nnz) : static_cast<size_t>((nnz + 1) / 2);
+  if (val_type == USW_VAL_F16) return static_cast<size_t>(2 * nnz);
+  if (val_type == USW_VAL_I2) return static_cast<size_t>((nnz + 3) / 4);
+  return static_cast<size_t>((nnz + 1) / 2);
 }
 
-// INT4 row scales over the kept entries (largest kept magnitude as
-// sign-cleared fp16 bits, then i4_scale_bits): writes the fp16 bits and
+// Largest positive code of a quantised value type (INT4 7, 2-bit 1).
+int code_max(int32_t val_type) { return val_type == USW_VAL_I2 ? 1 : 7; }
+
+// b-bit row scales over the kept entries (largest kept magnitude as
+// sign-cleared fp16 bits, then int_scale_bits): writes the fp16 bits and
 // returns their values.
-std::vector<double> row_scales(const uint16_t* W, const uint8_t* mask, int64_t M, int64_t K, uint16_t* scales) {
+std::vector<double> row_scales(const uint16_t* W, const uint8_t* mask, int64_t M, int64_t K, uint16_t* scales,
+                               int qmax = 7) {
   std::vector<double> rscale(static_cast<size_t>(M), 0.0);
   parallel_for(M, [&](int64_t lo, int64_t hi) {
     for (int64_t m = lo; m < hi; ++m) {
@@ -126,7 +132,7 @@ std::vector<double> row_scales(const uint16_t* W, const uint8_t* mask, int64_t M
         const uint16_t a = W[m * K + k] & 0x7FFFu;
         if (a > amax && is_kept(W, mask, m * K + k)) amax = a;
       }
-      const uint16_t s = i4_scale_bits(amax);
+      const uint16_t s = int_scale_bits(amax, qmax);
       scales[m] = s;
       rscale[m] = f16_to_f64(s);
     }
@@ -141,6 +147,18 @@ void pack_i4(const std::vector<int8_t>& q, int64_t n, uint8_t* vb) {
       const uint8_t a = static_cast<uint8_t>(q[2 * i]) & 0xF;
       const uint8_t b = (2 * i + 1 < n) ? (static_cast<uint8_t>(q[2 * i + 1]) & 0xF) : 0;
       vb[i] = static_cast<uint8_t>(a | (b << 4));
+    }
+  });
+}
+
+// Packs 2-bit codes four per byte, element 4i + j in bits 2j, 2j+1 of byte i.
+void pack_i2(const std::vector<int8_t>& q, int64_t n, uint8_t* vb) {
+  parallel_for((n + 3) / 4, [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i) {
+      uint8_t b = 0;
+      for (int j = 0; j < 4; ++j)
+        if (4 * i + j < n) b |= static_cast<uint8_t>((static_cast<uint8_t>(q[4 * i + j]) & 0x3) << (2 * j));
+      vb[i] = b;
     }
   });
 }
@@ -243,7 +261,7 @@ usw_status union_query_impl(const uint16_t* W, const uint8_t* mask, int32_t M, i
   UnionGeometry g;
   usw_status st = make_union_geometry(M, K, lt_m, lt_k, r_a, c_a, &g);
   if (st) return st;
-  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4 && val_type != USW_VAL_I2) return USW_ERR_BAD_DTYPE;
   if (perm && (g.lt_m > 256 || !valid_row_orders(g, perm))) return USW_ERR_BAD_SHAPE;
   std::vector<int64_t> off;
   st = count_union(g, perm, W, mask, &off);
@@ -254,7 +272,7 @@ usw_status union_query_impl(const uint16_t* W, const uint8_t* mask, int32_t M, i
   if (bytes_offsets) *bytes_offsets = static_cast<size_t>(4 * (g.nlt + 1));
   if (bytes_values) *bytes_values = values_logical_bytes(val_type, n);
   if (bytes_values_alloc) *bytes_values_alloc = values_alloc_bytes(val_type, n);
-  if (bytes_scales) *bytes_scales = val_type == USW_VAL_I4 ? static_cast<size_t>(2 * M) : 0;
+  if (bytes_scales) *bytes_scales = val_type != USW_VAL_F16 ? static_cast<size_t>(2 * M) : 0;
   return USW_OK;
 }
 
@@ -266,8 +284,9 @@ usw_status union_encode_impl(const uint16_t* W, const uint8_t* mask, int32_t M, 
   UnionGeometry g;
   usw_status st = make_union_geometry(M, K, lt_m, lt_k, r_a, c_a, &g);
   if (st) return st;
-  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
-  if (val_type == USW_VAL_I4 && !scales) return USW_ERR_NULL_ARG;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4 && val_type != USW_VAL_I2) return USW_ERR_BAD_DTYPE;
+  const bool quant = val_type != USW_VAL_F16;
+  if (quant && !scales) return USW_ERR_NULL_ARG;
   if (perm && (g.lt_m > 256 || !valid_row_orders(g, perm))) return USW_ERR_BAD_SHAPE;
   std::vector<int64_t> off;
   st = count_union(g, perm, W, mask, &off);
@@ -280,12 +299,13 @@ usw_status union_encode_impl(const uint16_t* W, const uint8_t* mask, int32_t M, 
     for (int64_t t = 0; t < g.nlt; ++t)
       for (int64_t s = 0; s < g.lt_m; ++s) rowmap[t * g.lt_m + perm[t * g.lt_m + s]] = static_cast<uint8_t>(s);
 
-  // INT4: scales and codes of the rows of W, whatever LT row they are
-  // stored in.
+  // INT4 / 2-bit: scales and codes of the rows of W, whatever LT row they
+  // are stored in.
+  const int qmax = code_max(val_type);
   std::vector<double> rscale;
-  if (val_type == USW_VAL_I4) rscale = row_scales(W, mask, M, K, scales);
+  if (quant) rscale = row_scales(W, mask, M, K, scales, qmax);
   std::vector<int8_t> q;
-  if (val_type == USW_VAL_I4) q.assign(static_cast<size_t>(total), 0);
+  if (quant) q.assign(static_cast<size_t>(total), 0);
   uint16_t* v16 = static_cast<uint16_t*>(values);
 
   // Per LT: the union words, then the Q area streams, each holding the area's
@@ -310,13 +330,14 @@ usw_status union_encode_impl(const uint16_t* W, const uint8_t* mask, int32_t M, 
           if (val_type == USW_VAL_F16)
             v16[idx] = kept ? W[lin] : uint16_t(0);
           else
-            q[static_cast<size_t>(idx)] = kept ? i4_code(W[lin], rscale[lin / g.K]) : int8_t(0);
+            q[static_cast<size_t>(idx)] = kept ? int_code(W[lin], rscale[lin / g.K], qmax) : int8_t(0);
         }
     }
   });
 
   uint8_t* vb = static_cast<uint8_t*>(values);
   if (val_type == USW_VAL_I4) pack_i4(q, total, vb);
+  if (val_type == USW_VAL_I2) pack_i2(q, total, vb);
   if (values_capacity > logical) std::memset(vb + logical, 0, values_capacity - logical);
   return USW_OK;
 }
@@ -573,10 +594,10 @@ usw_status usw_union_validate(const usw_union_fmt* f) {
   UnionGeometry g;
   usw_status st = make_union_geometry(f->M, f->K, f->lt_m, f->lt_k, f->r_a, f->c_a, &g);
   if (st) return st;
-  if (f->val_type != USW_VAL_F16 && f->val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (f->val_type != USW_VAL_F16 && f->val_type != USW_VAL_I4 && f->val_type != USW_VAL_I2) return USW_ERR_BAD_DTYPE;
   if (!f->bitmaps || !f->offsets) return USW_ERR_NULL_ARG;
   if (f->payload > 0 && !f->values) return USW_ERR_NULL_ARG;
-  if (f->val_type == USW_VAL_I4 && !f->scales) return USW_ERR_NULL_ARG;
+  if (f->val_type != USW_VAL_F16 && !f->scales) return USW_ERR_NULL_ARG;
   if (f->reserved != 0) return USW_ERR_BAD_SHAPE;
   if (f->payload < 0 || f->payload >= (int64_t(1) << 32)) return USW_ERR_CORRUPT;
   if (f->offsets[0] != 0 || static_cast<int64_t>(f->offsets[g.nlt]) != f->payload) return USW_ERR_CORRUPT;

@@ -1,11 +1,14 @@
-// fp16 <-> fp64 conversions and the INT4 round-to-nearest quantiser, used by
+// fp16 <-> fp64 conversions and the b-bit (INT4, 2-bit) round-to-nearest
+// quantiser, used by
 // both the host encoder and the device encoder so that the two write the
 // same bytes.
 //
-// INT4 rule (per output row m of W, over the kept weights only): scale_m is
-// max |w| / 7 computed in fp64 and rounded once to fp16; a kept weight w gets
-// the code clamp(round_half_even(w / scale_m), -8, 7) in fp64, or 0 when the
-// scale is 0 (a row with nothing kept, or only zeros kept).  Non-finite
+// b-bit rule (per output row m of W, over the kept weights only; INT4 is
+// b = 4, the 2-bit payload b = 2, qmax = 2^(b-1) - 1): scale_m is
+// max |w| / qmax computed in fp64 and rounded once to fp16; a kept weight w
+// gets the code clamp(round_half_even(w / scale_m), -qmax - 1, qmax) in
+// fp64, or 0 when the scale is 0 (a row with nothing kept, or only zeros
+// kept).  Non-finite
 // weights: a kept NaN makes the row maximum, and so the scale, NaN (fp16
 // 0x7E00), and every code of that row 0; a NaN quotient (an infinite weight
 // under an infinite scale) gives code 0.
@@ -70,20 +73,27 @@ __host__ __device__ inline uint16_t f64_to_f16_rne(double x) {
   return sign | static_cast<uint16_t>(r);
 }
 
-// Row scale bits from the largest kept magnitude, as fp16 bits with the sign
-// cleared (integer order is magnitude order, with NaN above infinity).
-__host__ __device__ inline uint16_t i4_scale_bits(uint16_t amax_bits) {
-  return f64_to_f16_rne(f16_to_f64(amax_bits) / 7.0);
+// Row scale bits of a b-bit code (qmax = 2^(b-1) - 1) from the largest kept
+// magnitude, as fp16 bits with the sign cleared (integer order is magnitude
+// order, with NaN above infinity).
+__host__ __device__ inline uint16_t int_scale_bits(uint16_t amax_bits, int qmax) {
+  return f64_to_f16_rne(f16_to_f64(amax_bits) / static_cast<double>(qmax));
 }
 
-// INT4 code of fp16 weight w under scale s (fp64).
-__host__ __device__ inline int8_t i4_code(uint16_t w, double s) {
+// b-bit code of fp16 weight w under scale s (fp64): clamp to
+// [-qmax - 1, qmax] of the quotient rounded half to even.
+__host__ __device__ inline int8_t int_code(uint16_t w, double s, int qmax) {
   if (!(s > 0.0)) return 0;  // zero or NaN scale
   double v = __builtin_rint(f16_to_f64(w) / s);
   if (v != v) return 0;      // inf / inf
-  v = (-8.0 < v) ? v : -8.0;
-  v = (v < 7.0) ? v : 7.0;
+  const double lo = -static_cast<double>(qmax) - 1.0, hi = static_cast<double>(qmax);
+  v = (lo < v) ? v : lo;
+  v = (v < hi) ? v : hi;
   return static_cast<int8_t>(v);
 }
+
+// INT4 (b = 4): scale max / 7, codes in [-8, 7].
+__host__ __device__ inline uint16_t i4_scale_bits(uint16_t amax_bits) { return int_scale_bits(amax_bits, 7); }
+__host__ __device__ inline int8_t i4_code(uint16_t w, double s) { return int_code(w, s, 7); }
 
 }  // namespace usw

@@ -67,7 +67,7 @@ struct USlot {
 
 // Issue the loads of LT column c of strip gi, whose payload occupies
 // elements [o0, o1) of the stream.
-template <int NB>
+template <int NB, int BITS>
 __device__ __forceinline__ void uslot_load(USlot<NB>& s, const Args& a, int gi, int c, int lane, uint32_t o0,
                                            uint32_t o1) {
   const int64_t t = static_cast<int64_t>(gi) * a.Gc + c;
@@ -80,9 +80,9 @@ __device__ __forceinline__ void uslot_load(USlot<NB>& s, const Args& a, int gi, 
   // union words.
   s.P = min((o1 - o0) >> 2, 1024u);
   const uint64_t top = a.values_alloc - 16;
-  const uint64_t a0 = min(chunk_start<true>(o0), top);
-  s.delta = chunk_delta<true>(o0, a0);
-  const uint32_t nch = min(chunk_count<true>(o1, a0), static_cast<uint32_t>((kUVbuf - 16) / 16));
+  const uint64_t a0 = min(Packed<BITS>::chunk_start(o0), top);
+  s.delta = Packed<BITS>::chunk_delta(o0, a0);
+  const uint32_t nch = min(Packed<BITS>::chunk_count(o1, a0), static_cast<uint32_t>((kUVbuf - 16) / 16));
   // Buffer resources that end after the LT's last piece: pieces past it read
   // as zero, one vector offset (the lane's) for all chunks.  The size is
   // wave-uniform; saying so keeps the compiler from wrapping each load in a
@@ -122,7 +122,7 @@ __device__ __forceinline__ void urow_tab_write(uint8_t* tab, uint32_t rowbits, u
 
 // Rebuild the 8 fragments of an LT whose row table is at tab and whose
 // payload is in LDS, and multiply them with the X^T fragments.
-template <int NB>
+template <int NB, int BITS>
 __device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const uint8_t* smem, const uint8_t* tab,
                                                const u32x2_t* lut, uint32_t P, f32x4_t (&acc)[4][NB], int lane) {
   const int i = lane & 15;
@@ -138,7 +138,7 @@ __device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const 
     const u32x2_t sel = lut[byte];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const half8_t av = expand_row_i4(lds_window_i4(smem, rb + static_cast<uint32_t>(q) * P), sel);
+      const half8_t av = expand_row_i4(Packed<BITS>::window(smem, rb + static_cast<uint32_t>(q) * P), sel);
       const int f = 2 * (q >> 1) + h;   // area row q / 2, logical row half h
       const int ks = q & 1;             // area column
 #pragma unroll
@@ -149,7 +149,7 @@ __device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const 
   }
 }
 
-template <int NB, bool OUT_F16, int OCC>
+template <int NB, int BITS, bool OUT_F16, int OCC>
 __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) u32x2_t lut[256];
   constexpr int kStage = kUWaves * (kUVbuf + kURowTab);
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
   uint8_t* tab = smem + kUWaves * kUVbuf + w * kURowTab;
   // Windows address smem directly: the wave buffer's offset in payload
   // elements (nibbles) is folded into the row bases.
-  const uint32_t vb_elems = static_cast<uint32_t>(w * kUVbuf * 2);
+  const uint32_t vb_elems = static_cast<uint32_t>(w * kUVbuf) * Packed<BITS>::kPerByte;
 
   // The wave's LT offsets, lane i holding offsets[t_begin + i] (the host
   // keeps the count <= 63).
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
     const int c_last = c_end - 1;
     auto load = [&](USlot<NB>& sl, int c) {
       const int cc = min(c, c_last);
-      uslot_load(sl, a, gi, cc, lane, off_at(cc), off_at(cc + 1));
+      uslot_load<NB, BITS>(sl, a, gi, cc, lane, off_at(cc), off_at(cc + 1));
     };
     auto commit = [&](const USlot<NB>& sl) {
 #pragma unroll
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
       load(nxt, c + 1);
       commit(cur);
       wave_sync();
-      union_tile_mma<NB>(cur.x, smem, tab, lut, cur.P, acc, lane);
+      union_tile_mma<NB, BITS>(cur.x, smem, tab, lut, cur.P, acc, lane);
       wave_sync();
       write_tab(nxt);
     };
@@ -297,7 +297,7 @@ struct U16Slot {
 
 // Issue the loads of LT column c of strip gi; o0[f], o1[f] frame LT f's
 // payload elements.
-template <int NB>
+template <int NB, int BITS>
 __device__ __forceinline__ void u16slot_load(U16Slot<NB>& s, const Args& a, int gi, int c, int lane,
                                              const uint32_t (&o0)[4], const uint32_t (&o1)[4]) {
   const int64_t t0 = static_cast<int64_t>(4 * gi) * a.Gc + c;   // LT f is t0 + f Gc
@@ -320,9 +320,9 @@ __device__ __forceinline__ void u16slot_load(U16Slot<NB>& s, const Args& a, int 
     // At most 256 active positions; the clamp keeps windows inside the
     // buffer even for offsets that disagree with the union words.
     s.P[f] = min((o1[f] - o0[f]) >> 2, 256u);
-    const uint64_t a0 = min(chunk_start<true>(o0[f]), top);
-    s.delta[f] = chunk_delta<true>(o0[f], a0);
-    const uint32_t nch = min(chunk_count<true>(o1[f], a0), static_cast<uint32_t>((kU16Vbuf - 16) / 16));
+    const uint64_t a0 = min(Packed<BITS>::chunk_start(o0[f]), top);
+    s.delta[f] = Packed<BITS>::chunk_delta(o0[f], a0);
+    const uint32_t nch = min(Packed<BITS>::chunk_count(o1[f], a0), static_cast<uint32_t>((kU16Vbuf - 16) / 16));
     const uint32_t last = min(nch > 0 ? nch - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
     const int span = __builtin_amdgcn_readfirstlane(static_cast<int>(16 * (last + 1)));
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values + a0), 0, span, kBufferRsrcWord3);
@@ -355,7 +355,7 @@ __device__ __forceinline__ void u16_tab_write(uint8_t* tab, uint32_t rowbits, co
   }
 }
 
-template <int NB>
+template <int NB, int BITS>
 __device__ __forceinline__ void u16_tile_mma(const U16Slot<NB>& cur, bool mapped, const uint8_t* smem,
                                              const uint8_t* tab, const u32x2_t* lut, f32x4_t (&acc)[4][NB],
                                              int lane) {
@@ -373,7 +373,7 @@ __device__ __forceinline__ void u16_tile_mma(const U16Slot<NB>& cur, bool mapped
     const uint32_t q0 = 2u * (srow >> 3);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const half8_t av = expand_row_i4(lds_window_i4(smem, rb + (q0 + ks) * cur.P[f]), sel);
+      const half8_t av = expand_row_i4(Packed<BITS>::window(smem, rb + (q0 + ks) * cur.P[f]), sel);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         acc[f][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, cur.x[ks][nb]),
@@ -382,7 +382,7 @@ __device__ __forceinline__ void u16_tile_mma(const U16Slot<NB>& cur, bool mapped
   }
 }
 
-template <int NB, bool OUT_F16, int OCC>
+template <int NB, int BITS, bool OUT_F16, int OCC>
 __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) u32x2_t lut[256];
   constexpr int kStage = kU16Waves * (4 * kU16Vbuf + kU16Tab);
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
   uint8_t* vb = smem + w * 4 * kU16Vbuf;
   uint8_t* tab = smem + kU16Waves * 4 * kU16Vbuf + w * kU16Tab;
   // LT f's payload buffer, in elements (nibbles) from the start of smem.
-  const uint32_t vb_elems = static_cast<uint32_t>(w * 4 * kU16Vbuf * 2);
+  const uint32_t vb_elems = static_cast<uint32_t>(w * 4 * kU16Vbuf) * Packed<BITS>::kPerByte;
 
   // The LT offsets of the wave's columns: lane 16 f + j holds
   // offsets[(4 gi + f) Gc + c_begin + j] for j <= count.
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
       const int cc = min(c, c_last);
       uint32_t o0[4], o1[4];
       offs(cc, o0, o1);
-      u16slot_load(sl, a, gi, cc, lane, o0, o1);
+      u16slot_load<NB, BITS>(sl, a, gi, cc, lane, o0, o1);
     };
     auto commit = [&](const U16Slot<NB>& sl) {
 #pragma unroll
@@ -449,7 +449,8 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
     auto write_tab = [&](const U16Slot<NB>& sl) {
       uint32_t base[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) base[f] = sl.delta[f] + vb_elems + static_cast<uint32_t>(f * kU16Vbuf * 2);
+      for (int f = 0; f < 4; ++f)
+        base[f] = sl.delta[f] + vb_elems + static_cast<uint32_t>(f * kU16Vbuf) * Packed<BITS>::kPerByte;
       u16_tab_write(tab, sl.rowbits, base, lane);
     };
     U16Slot<NB> s[2];
@@ -459,7 +460,7 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
       load(nxt, c + 1);
       commit(cur);
       wave_sync();
-      u16_tile_mma<NB>(cur, mapped, smem, tab, lut, acc, lane);
+      u16_tile_mma<NB, BITS>(cur, mapped, smem, tab, lut, acc, lane);
       wave_sync();
       write_tab(nxt);
     };
@@ -557,11 +558,12 @@ usw_status union_check(const usw_union_fmt* f, int32_t y_type, int32_t N, usw::U
   if (!f) return USW_ERR_NULL_ARG;
   usw_status st = usw::make_union_geometry(f->M, f->K, f->lt_m, f->lt_k, f->r_a, f->c_a, g);
   if (st) return st;
-  if (f->val_type != USW_VAL_F16 && f->val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (f->val_type != USW_VAL_F16 && f->val_type != USW_VAL_I4 && f->val_type != USW_VAL_I2) return USW_ERR_BAD_DTYPE;
   if (y_type != USW_OUT_F16 && y_type != USW_OUT_F32) return USW_ERR_BAD_DTYPE;
   if (f->reserved != 0) return USW_ERR_BAD_SHAPE;
   if (N < 1) return USW_ERR_BAD_N;
-  if (f->val_type != USW_VAL_I4 || f->lt_k != 64 || f->r_a != 2 || f->c_a != 2) return USW_ERR_UNSUPPORTED;
+  if ((f->val_type != USW_VAL_I4 && f->val_type != USW_VAL_I2) || f->lt_k != 64 || f->r_a != 2 || f->c_a != 2)
+    return USW_ERR_UNSUPPORTED;
   if (f->lt_m == 64) {
     if (f->rowmap) return USW_ERR_UNSUPPORTED;
   } else if (f->lt_m != 16 || f->M % 64) {
@@ -572,19 +574,19 @@ usw_status union_check(const usw_union_fmt* f, int32_t y_type, int32_t N, usw::U
   return USW_OK;
 }
 
-template <int NB>
+template <int NB, int BITS>
 void union_launch(const Args& a, bool f16out, bool lt16, dim3 grid, hipStream_t s) {
   constexpr int occ = NB == 1 ? kOcc1 : kOcc2;
   constexpr int occ16 = NB == 1 ? kOcc16a : kOcc16b;
   if (lt16) {
     if (f16out)
-      union16_decode_kernel<NB, true, occ16><<<grid, kU16Threads, 0, s>>>(a);
+      union16_decode_kernel<NB, BITS, true, occ16><<<grid, kU16Threads, 0, s>>>(a);
     else
-      union16_decode_kernel<NB, false, occ16><<<grid, kU16Threads, 0, s>>>(a);
+      union16_decode_kernel<NB, BITS, false, occ16><<<grid, kU16Threads, 0, s>>>(a);
   } else if (f16out) {
-    union_decode_kernel<NB, true, occ><<<grid, kUThreads, 0, s>>>(a);
+    union_decode_kernel<NB, BITS, true, occ><<<grid, kUThreads, 0, s>>>(a);
   } else {
-    union_decode_kernel<NB, false, occ><<<grid, kUThreads, 0, s>>>(a);
+    union_decode_kernel<NB, BITS, false, occ><<<grid, kUThreads, 0, s>>>(a);
   }
 }
 
@@ -639,17 +641,21 @@ usw_status usw_union_spmm(const usw_union_fmt* f, const uint16_t* X, void* Y, in
     a.Y = static_cast<uint8_t*>(Y) + static_cast<size_t>(n0) * g.M * ybytes;
     a.counters = need ? static_cast<uint32_t*>(ws) : nullptr;
     a.part = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + union_counter_bytes(g)) : nullptr;
-    a.values_alloc = usw::values_alloc_bytes(USW_VAL_I4, f->payload);
+    a.values_alloc = usw::values_alloc_bytes(f->val_type, f->payload);
     a.M = static_cast<int>(g.M);
     a.K = static_cast<int>(g.K);
     a.N = nc;
     a.Gc = static_cast<int>(g.lc);
     a.splits = p.splits;
     a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
-    if (nc > 16)
-      union_launch<2>(a, f16out, p.lt16, grid, s);
-    else
-      union_launch<1>(a, f16out, p.lt16, grid, s);
+    const bool i2 = f->val_type == USW_VAL_I2;
+    if (nc > 16) {
+      if (i2) union_launch<2, 2>(a, f16out, p.lt16, grid, s);
+      else union_launch<2, 4>(a, f16out, p.lt16, grid, s);
+    } else {
+      if (i2) union_launch<1, 2>(a, f16out, p.lt16, grid, s);
+      else union_launch<1, 4>(a, f16out, p.lt16, grid, s);
+    }
     if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
   }
   return USW_OK;
