@@ -224,10 +224,11 @@ def test_argument_errors_return_before_launch():
     assert L.usw_encode_query(W.ctypes.data, None, 256, 256, 64, 48, 1, B(nnz), None, None, None, None, None) == -2
     assert L.usw_encode_query(W.ctypes.data, None, 256, 256, 64, 64, 9, B(nnz), None, None, None, None, None) == -3
     vals = np.zeros(4, np.uint8)
-    assert L.usw_encode(W.ctypes.data, None, 256, 256, 64, 64, 1, h.bitmaps.copy().ctypes.data,
-                        h.offsets.copy().ctypes.data, vals.ctypes.data, 4, None) == -10
-    assert L.usw_encode(W.ctypes.data, None, 256, 256, 64, 64, 2, h.bitmaps.copy().ctypes.data,
-                        h.offsets.copy().ctypes.data, vals.ctypes.data, 4, None) == -1
+    bm_out, off_out = h.bitmaps.copy(), h.offsets.copy()     # kept alive across the calls
+    assert L.usw_encode(W.ctypes.data, None, 256, 256, 64, 64, 1, bm_out.ctypes.data,
+                        off_out.ctypes.data, vals.ctypes.data, 4, None) == -10
+    assert L.usw_encode(W.ctypes.data, None, 256, 256, 64, 64, 2, bm_out.ctypes.data,
+                        off_out.ctypes.data, vals.ctypes.data, 4, None) == -1
 
 
 @pytest.mark.host_pointers

@@ -122,6 +122,7 @@ def test_cbc_argument_errors_return_before_launch():
     assert L.usw_cbc_encode_query(W.ctypes.data, None, 500, 256, B(nnz), B(npad), None, None, None, None) == -2
     assert L.usw_cbc_encode_query(W.ctypes.data, None, 512, 250, B(nnz), B(npad), None, None, None, None) == -2
     vals = np.zeros(4, np.uint16)
-    assert L.usw_cbc_encode(W.ctypes.data, None, 512, 256, h.bitmaps.copy().ctypes.data,
-                            h.tile_offsets.copy().ctypes.data, h.colinfo.copy().ctypes.data,
+    bm_out, to_out, ci_out = h.bitmaps.copy(), h.tile_offsets.copy(), h.colinfo.copy()   # kept alive
+    assert L.usw_cbc_encode(W.ctypes.data, None, 512, 256, bm_out.ctypes.data,
+                            to_out.ctypes.data, ci_out.ctypes.data,
                             vals.ctypes.data, 8) == -10

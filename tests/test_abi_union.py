@@ -156,7 +156,8 @@ def test_union_argument_errors_return_before_launch():
     assert L.usw_union_encode_query(W.ctypes.data, None, 256, 512, 64, 64, 2, 2, 9, B(pl),
                                     None, None, None, None, None) == -3
     vals = np.zeros(4, np.uint8)
-    assert L.usw_union_encode(W.ctypes.data, None, 256, 512, 64, 64, 2, 2, 1, h.bitmaps.copy().ctypes.data,
-                              h.offsets.copy().ctypes.data, vals.ctypes.data, 4, None) == -10
-    assert L.usw_union_encode(W.ctypes.data, None, 256, 512, 64, 64, 2, 2, 2, h.bitmaps.copy().ctypes.data,
-                              h.offsets.copy().ctypes.data, vals.ctypes.data, 4, None) == -1
+    bm_out, off_out = h.bitmaps.copy(), h.offsets.copy()     # kept alive across the calls
+    assert L.usw_union_encode(W.ctypes.data, None, 256, 512, 64, 64, 2, 2, 1, bm_out.ctypes.data,
+                              off_out.ctypes.data, vals.ctypes.data, 4, None) == -10
+    assert L.usw_union_encode(W.ctypes.data, None, 256, 512, 64, 64, 2, 2, 2, bm_out.ctypes.data,
+                              off_out.ctypes.data, vals.ctypes.data, 4, None) == -1

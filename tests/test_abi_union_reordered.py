@@ -106,7 +106,8 @@ def test_reordered_argument_errors():
     mask = wl.mask_bernoulli(M, K, 0.5, rng)
     perms = random_perms(16, 16, 7)
     pl, bv, ba = ctypes.c_int64(), ctypes.c_size_t(), ctypes.c_size_t()
-    wp, mp = W.ctypes.data, mask.astype(np.uint8).ctypes.data
+    mask8 = mask.astype(np.uint8)                               # kept alive across the calls
+    wp, mp = W.ctypes.data, mask8.ctypes.data
     args = (M, K, 16, 64, 2, 2, 2)
     assert L.usw_union_encode_reordered_query(wp, mp, *args, perms.ctypes.data, B(pl), B(bv), B(ba)) == 0
     assert L.usw_union_encode_reordered_query(wp, mp, *args, None, B(pl), B(bv), B(ba)) == -1

@@ -9,7 +9,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libusw.so")
+# USW_LIB_PATH names another build of the same library (the sanitizer
+# build of the host code that the test suite runs the C-ABI tests against).
+LIB_PATH = os.environ.get("USW_LIB_PATH") or os.path.join(_PKG, "libusw.so")
 
 USW_OK = 0
 USW_VAL_F16 = 1

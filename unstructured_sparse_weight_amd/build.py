@@ -39,15 +39,29 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP toolchain is required to build libusw")
 
 
-def build(verbose: bool = False, tuning: bool = False) -> str:
-    """Compile every source into libusw.so next to this file; returns its path.
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer: every flag
+# applies to the host compilation only (the GPU code is built as usual).
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-shared-libsan", "-O1"]
+
+
+def build(verbose: bool = False, tuning: bool = False, sanitize: bool = False, out: str = "") -> str:
+    """Compile every source into libusw.so next to this file (or into
+    ``out``); returns its path.
 
     ``tuning`` also compiles the alternative decode launch configurations,
     selected at run time by the USW_DECODE_CFG environment variable.
+    ``sanitize`` instruments the host code with ASan and UBSan; such a build
+    needs the sanitizer runtime preloaded and is meant for the CPU tests of
+    the C ABI.
     """
     srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    tmp = LIB + ".tmp"
+    lib_path = out or LIB
+    tmp = lib_path + ".tmp"
     extra = ["-DUSW_TUNING"] if tuning else []
+    if sanitize:
+        extra += SANITIZE_FLAGS
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -55,8 +69,8 @@ def build(verbose: bool = False, tuning: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
