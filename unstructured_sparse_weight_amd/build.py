@@ -46,22 +46,19 @@ SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitiz
                   "-shared-libsan", "-O1"]
 
 
-def build(verbose: bool = False, tuning: bool = False, sanitize: bool = False, out: str = "") -> str:
+def build(verbose: bool = False, sanitize: bool = False, out: str = "") -> str:
     """Compile every source into libusw.so next to this file (or into
     ``out``); returns its path.
 
-    ``tuning`` also compiles the alternative decode launch configurations,
-    selected at run time by the USW_DECODE_CFG environment variable.
     ``sanitize`` instruments the host code with ASan and UBSan; such a build
     needs the sanitizer runtime preloaded and is meant for the CPU tests of
     the C ABI.
     """
     srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    lib_path = out or LIB
+    # A sanitized build never replaces the product library.
+    lib_path = out or (os.path.join(PKG, "libusw_sanitized.so") if sanitize else LIB)
     tmp = lib_path + ".tmp"
-    extra = ["-DUSW_TUNING"] if tuning else []
-    if sanitize:
-        extra += SANITIZE_FLAGS
+    extra = list(SANITIZE_FLAGS) if sanitize else []
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -74,4 +71,4 @@ def build(verbose: bool = False, tuning: bool = False, sanitize: bool = False, o
 
 
 if __name__ == "__main__":
-    print(build(verbose=True, tuning="--tuning" in sys.argv[1:]))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))

@@ -48,7 +48,6 @@
 
 #include <algorithm>
 #include <cstdint>
-#include <cstdlib>
 #include <mutex>
 
 #include "usw.h"
@@ -712,9 +711,7 @@ __global__ __launch_bounds__(kRingThreads, 5) void decode_ring_kernel(Args a) {
 // ---------------------------------------------------------------------------
 
 // Decode launch configurations (waves per workgroup, pipeline depth,
-// minimum waves per SIMD).  The default is the measured best on MI355X; a
-// tuning build (-DUSW_TUNING) also compiles the others and picks one from
-// the USW_DECODE_CFG environment variable.
+// minimum waves per SIMD), each the measured best on MI355X for its case.
 using DefaultCfg = Cfg<4, 1, 4>;
 // fp16 with five-chunk value slots: 96 VGPRs, so a fifth wave per SIMD fits
 // (measured 2% faster than four on the 20480x5120 layer at N = 16).
@@ -726,62 +723,17 @@ using DefaultCfg2 = Cfg<4, 1, 3>;
 // (85 VGPRs), so a fifth wave per SIMD fits and hides more of the rebuild
 // latency (measured 6% faster on the 20480x5120 layer at N = 2).
 using DefaultCfgI4 = Cfg<4, 1, 5>;
-#ifdef USW_TUNING
-using TuneCfg1 = Cfg<4, 1, 3>;
-using TuneCfg2 = Cfg<4, 2, 3>;
-using TuneCfg3 = Cfg<8, 1, 4>;
-using TuneCfg4 = Cfg<8, 1, 3>;
-using TuneCfg5 = Cfg<4, 2, 2>;
-using TuneCfg6 = Cfg<4, 3, 2>;
-using TuneCfg7 = Cfg<4, 3, 3>;
-using TuneCfg8 = Cfg<8, 3, 2>;
-using TuneCfg9 = Cfg<2, 3, 2>;
-using TuneCfg10 = Cfg<4, 0, 5>;
-using TuneCfg11 = Cfg<4, 0, 6>;
-using TuneCfg12 = Cfg<4, 0, 4>;
-using TuneCfg13 = Cfg<4, 1, 5>;
-using TuneCfg14 = Cfg<4, 2, 4>;
-using TuneCfg15 = Cfg<4, 1, 6>;
-#endif
-
-int choose_cfg() {
-#ifdef USW_TUNING
-  const char* e = std::getenv("USW_DECODE_CFG");
-  if (e) return std::atoi(e);
-#endif
-  return 0;
-}
 
 struct CfgInfo {
   int waves;   // waves per workgroup
   int occ;     // waves per SIMD the configuration allows
 };
 
-CfgInfo cfg_info(int cfg, bool two, bool i4, bool lean) {
-  switch (cfg) {
-#ifdef USW_TUNING
-    case 1: return {TuneCfg1::kWavesPerGroup, TuneCfg1::kOcc};
-    case 2: return {TuneCfg2::kWavesPerGroup, TuneCfg2::kOcc};
-    case 3: return {TuneCfg3::kWavesPerGroup, TuneCfg3::kOcc};
-    case 4: return {TuneCfg4::kWavesPerGroup, TuneCfg4::kOcc};
-    case 5: return {TuneCfg5::kWavesPerGroup, TuneCfg5::kOcc};
-    case 6: return {TuneCfg6::kWavesPerGroup, TuneCfg6::kOcc};
-    case 7: return {TuneCfg7::kWavesPerGroup, TuneCfg7::kOcc};
-    case 8: return {TuneCfg8::kWavesPerGroup, TuneCfg8::kOcc};
-    case 9: return {TuneCfg9::kWavesPerGroup, TuneCfg9::kOcc};
-    case 10: return {TuneCfg10::kWavesPerGroup, TuneCfg10::kOcc};
-    case 11: return {TuneCfg11::kWavesPerGroup, TuneCfg11::kOcc};
-    case 12: return {TuneCfg12::kWavesPerGroup, TuneCfg12::kOcc};
-    case 13: return {TuneCfg13::kWavesPerGroup, TuneCfg13::kOcc};
-    case 14: return {TuneCfg14::kWavesPerGroup, TuneCfg14::kOcc};
-    case 15: return {TuneCfg15::kWavesPerGroup, TuneCfg15::kOcc};
-#endif
-    default:
-      if (two) return CfgInfo{DefaultCfg2::kWavesPerGroup, DefaultCfg2::kOcc};
-      if (i4) return CfgInfo{DefaultCfgI4::kWavesPerGroup, DefaultCfgI4::kOcc};
-      return lean ? CfgInfo{DefaultCfgLean::kWavesPerGroup, DefaultCfgLean::kOcc}
-                  : CfgInfo{DefaultCfg::kWavesPerGroup, DefaultCfg::kOcc};
-  }
+CfgInfo cfg_info(bool two, bool i4, bool lean) {
+  if (two) return CfgInfo{DefaultCfg2::kWavesPerGroup, DefaultCfg2::kOcc};
+  if (i4) return CfgInfo{DefaultCfgI4::kWavesPerGroup, DefaultCfgI4::kOcc};
+  return lean ? CfgInfo{DefaultCfgLean::kWavesPerGroup, DefaultCfgLean::kOcc}
+              : CfgInfo{DefaultCfg::kWavesPerGroup, DefaultCfg::kOcc};
 }
 
 // Compute units of MI355X; the automatic split aims at one full round of
@@ -791,38 +743,28 @@ constexpr int64_t kComputeUnits = 256;
 struct Plan {
   int splits;     // workgroups per 64-row strip
   int nchunk;     // columns of N per kernel pass (16 or 32)
-  int cfg;        // launch configuration
   int waves;      // waves per workgroup
-  int ring;       // > 0: the workgroup-cooperative kernel with this many LDS slots
+  bool ring;      // the workgroup-cooperative kernel
 };
 
-// Ring depth of the workgroup-cooperative decode (0: not used).  The default
-// is the measured best on MI355X; a tuning build reads USW_DECODE_RING.
-int choose_ring() {
-#ifdef USW_TUNING
-  const char* e = std::getenv("USW_DECODE_RING");
-  if (e) return std::atoi(e);
-#endif
-  return 3;
-}
+// LDS slots of the workgroup-cooperative decode: two GroupTiles load while
+// one is computed (measured on MI355X: 2 slots 2% slower, 4 slots, which
+// leave room for four workgroups per compute unit instead of five, 24%
+// slower).
+constexpr int kRingDepth = 3;
 
-template <int R>
 void ring_launch(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
   if (f16out)
-    decode_ring_kernel<R, true><<<grid, kRingThreads, 0, s>>>(a);
+    decode_ring_kernel<kRingDepth, true><<<grid, kRingThreads, 0, s>>>(a);
   else
-    decode_ring_kernel<R, false><<<grid, kRingThreads, 0, s>>>(a);
+    decode_ring_kernel<kRingDepth, false><<<grid, kRingThreads, 0, s>>>(a);
 }
 
 // Workgroups of the ring kernel resident per compute unit (registers, LDS).
-int ring_resident(int R) {
+int ring_resident() {
   int n = 0;
-  hipError_t e = hipErrorInvalidValue;
-  switch (R) {
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ring_kernel<2, true>, kRingThreads, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ring_kernel<4, true>, kRingThreads, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ring_kernel<3, true>, kRingThreads, 0); break;
-  }
+  const hipError_t e =
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ring_kernel<kRingDepth, true>, kRingThreads, 0);
   return (e == hipSuccess && n > 0) ? n : 4;
 }
 
@@ -832,16 +774,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // fewer take the decode kernels in passes of up to 32 tokens, which re-read
 // the weight per pass but beat the 256-token prefill tiles up to 96 tokens
 // on MI355X (11008x4096 and 4096x11008: 1.3-2.0x at 48-96, even at 128).
-// A tuning build reads USW_DECODE_MAX_N.
-int decode_max_n() {
-#ifdef USW_TUNING
-  const char* e = std::getenv("USW_DECODE_MAX_N");
-  if (e) return std::atoi(e);
-#endif
-  return 96;
-}
+constexpr int kDecodeMaxN = 96;
 
-bool use_prefill(const usw_fmt* f, int32_t N) { return f->val_type == USW_VAL_F16 && N > decode_max_n(); }
+bool use_prefill(const usw_fmt* f, int32_t N) { return f->val_type == USW_VAL_F16 && N > kDecodeMaxN; }
 
 // Five 1 KB value chunks per slot when an fp16 matrix is at most 55% dense on
 // average (a GroupTile then needs more than five only far in the tail; such
@@ -854,22 +789,19 @@ bool lean_values(const usw_fmt* f, const usw::Geometry& g) {
 Plan make_plan(const usw::Geometry& g, int N, int splits_req, bool i4, bool lean) {
   Plan p;
   p.nchunk = N <= 16 ? 16 : 32;
-  p.cfg = choose_cfg();
-  p.ring = (!i4 && lean && N <= 16) ? choose_ring() : 0;
-  if (p.ring == 1 || p.ring > 4) p.ring = 3;
-  if (p.ring > 0) {
+  p.ring = !i4 && lean && N <= 16;
+  if (p.ring) {
     // One round of resident workgroups, each keeping at most 63 GroupTiles;
     // the factor is clamped to K/256 like the other decode kernel's.
     p.waves = 5;
-    static int resident[5] = {0, 0, 0, 0, 0};
-    if (resident[p.ring] == 0) resident[p.ring] = ring_resident(p.ring);
-    int64_t s = splits_req > 0 ? splits_req : (kComputeUnits * resident[p.ring]) / g.Gr;
+    static const int resident = ring_resident();
+    int64_t s = splits_req > 0 ? splits_req : (kComputeUnits * resident) / g.Gr;
     const int64_t smax = std::max<int64_t>(1, g.Gc / 4);
     const int64_t smin = (g.Gc + 62) / 63;
     p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
     return p;
   }
-  const CfgInfo ci = cfg_info(p.cfg, N > 16, i4, lean);
+  const CfgInfo ci = cfg_info(N > 16, i4, lean);
   p.waves = ci.waves;
   int64_t s = splits_req;
   if (s <= 0) {
@@ -919,36 +851,15 @@ void launch_cfg(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
 }
 
 template <int NB, bool I4, int CH>
-void launch_decode(const Args& a, bool f16out, dim3 grid, hipStream_t s, int cfg) {
-  switch (cfg) {
-#ifdef USW_TUNING
-    case 1: launch_cfg<NB, I4, CH, TuneCfg1>(a, f16out, grid, s); return;
-    case 2: launch_cfg<NB, I4, CH, TuneCfg2>(a, f16out, grid, s); return;
-    case 3: launch_cfg<NB, I4, CH, TuneCfg3>(a, f16out, grid, s); return;
-    case 4: launch_cfg<NB, I4, CH, TuneCfg4>(a, f16out, grid, s); return;
-    case 5: launch_cfg<NB, I4, CH, TuneCfg5>(a, f16out, grid, s); return;
-    case 6: launch_cfg<NB, I4, CH, TuneCfg6>(a, f16out, grid, s); return;
-    case 7: launch_cfg<NB, I4, CH, TuneCfg7>(a, f16out, grid, s); return;
-    case 8: launch_cfg<NB, I4, CH, TuneCfg8>(a, f16out, grid, s); return;
-    case 9: launch_cfg<NB, I4, CH, TuneCfg9>(a, f16out, grid, s); return;
-    case 10: launch_cfg<NB, I4, CH, TuneCfg10>(a, f16out, grid, s); return;
-    case 11: launch_cfg<NB, I4, CH, TuneCfg11>(a, f16out, grid, s); return;
-    case 12: launch_cfg<NB, I4, CH, TuneCfg12>(a, f16out, grid, s); return;
-    case 13: launch_cfg<NB, I4, CH, TuneCfg13>(a, f16out, grid, s); return;
-    case 14: launch_cfg<NB, I4, CH, TuneCfg14>(a, f16out, grid, s); return;
-    case 15: launch_cfg<NB, I4, CH, TuneCfg15>(a, f16out, grid, s); return;
-#endif
-    default:
-      if constexpr (NB == 2)
-        launch_cfg<NB, I4, CH, DefaultCfg2>(a, f16out, grid, s);
-      else if constexpr (I4)
-        launch_cfg<NB, I4, CH, DefaultCfgI4>(a, f16out, grid, s);
-      else if constexpr (CH == 5)
-        launch_cfg<NB, I4, CH, DefaultCfgLean>(a, f16out, grid, s);
-      else
-        launch_cfg<NB, I4, CH, DefaultCfg>(a, f16out, grid, s);
-      return;
-  }
+void launch_decode(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
+  if constexpr (NB == 2)
+    launch_cfg<NB, I4, CH, DefaultCfg2>(a, f16out, grid, s);
+  else if constexpr (I4)
+    launch_cfg<NB, I4, CH, DefaultCfgI4>(a, f16out, grid, s);
+  else if constexpr (CH == 5)
+    launch_cfg<NB, I4, CH, DefaultCfgLean>(a, f16out, grid, s);
+  else
+    launch_cfg<NB, I4, CH, DefaultCfg>(a, f16out, grid, s);
 }
 
 // Argument checks of a product call (nothing is written or launched).
@@ -1022,19 +933,17 @@ usw_status launch_call(const usw_fmt* f, const usw::Geometry& g, const CallPlan&
     a.splits = p.splits;
     a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
     const bool two = nc > 16;
-    if (p.ring > 0) {
-      if (p.ring == 2) ring_launch<2>(a, f16out, grid, s);
-      else if (p.ring == 4) ring_launch<4>(a, f16out, grid, s);
-      else ring_launch<3>(a, f16out, grid, s);
+    if (p.ring) {
+      ring_launch(a, f16out, grid, s);
     } else if (i4) {
-      if (two) launch_decode<2, true, 3>(a, f16out, grid, s, p.cfg);
-      else launch_decode<1, true, 3>(a, f16out, grid, s, p.cfg);
+      if (two) launch_decode<2, true, 3>(a, f16out, grid, s);
+      else launch_decode<1, true, 3>(a, f16out, grid, s);
     } else if (lean) {
-      if (two) launch_decode<2, false, 5>(a, f16out, grid, s, p.cfg);
-      else launch_decode<1, false, 5>(a, f16out, grid, s, p.cfg);
+      if (two) launch_decode<2, false, 5>(a, f16out, grid, s);
+      else launch_decode<1, false, 5>(a, f16out, grid, s);
     } else {
-      if (two) launch_decode<2, false, 6>(a, f16out, grid, s, p.cfg);
-      else launch_decode<1, false, 6>(a, f16out, grid, s, p.cfg);
+      if (two) launch_decode<2, false, 6>(a, f16out, grid, s);
+      else launch_decode<1, false, 6>(a, f16out, grid, s);
     }
     if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
   }
