@@ -46,19 +46,27 @@ SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitiz
                   "-shared-libsan", "-O1"]
 
 
-def build(verbose: bool = False, sanitize: bool = False, out: str = "") -> str:
+DEBUG_LIB = os.path.join(PKG, "libusw_debug.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False, debug: bool = False, out: str = "") -> str:
     """Compile every source into libusw.so next to this file (or into
     ``out``); returns its path.
 
     ``sanitize`` instruments the host code with ASan and UBSan; such a build
     needs the sanitizer runtime preloaded and is meant for the CPU tests of
-    the C ABI.
+    the C ABI.  ``debug`` (-DUSW_DEBUG) poisons the kernels' LDS staging
+    buffers with NaNs before use (libusw_debug.so, for the GPU test that
+    checks no kernel reads LDS that no stage wrote).
     """
     srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    # A sanitized build never replaces the product library.
-    lib_path = out or (os.path.join(PKG, "libusw_sanitized.so") if sanitize else LIB)
+    # Sanitized and debug builds never replace the product library.
+    default = os.path.join(PKG, "libusw_sanitized.so") if sanitize else (DEBUG_LIB if debug else LIB)
+    lib_path = out or default
     tmp = lib_path + ".tmp"
     extra = list(SANITIZE_FLAGS) if sanitize else []
+    if debug:
+        extra.append("-DUSW_DEBUG")
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -71,4 +79,4 @@ def build(verbose: bool = False, sanitize: bool = False, out: str = "") -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:], debug="--debug" in sys.argv[1:]))

@@ -170,6 +170,7 @@ template <bool OUT_F16>
 __global__ __launch_bounds__(kCThreads, 4) void cbc_spmspv_kernel(CArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kCWaves * kWaveBuf];   // staging; then the wave reduction
   __shared__ uint32_t last_flag;
+  USW_LDS_POISON(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -108,6 +108,28 @@ __device__ __forceinline__ void wait_vm(int n) {
 // memory loads stay in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
 
+// Debug builds (-DUSW_DEBUG) fill LDS staging buffers with fp16 NaNs
+// (0x7E00) at kernel entry, and the ring decode kernel refills each ring slot
+// before its next loads are issued: a read of LDS that no stage wrote, or
+// one that runs ahead of the load that fills it, then turns the product into
+// NaN instead of a plausible stale value.  Release builds compile none of it.
+constexpr uint32_t kLdsPoison = 0x7E007E00u;
+#ifdef USW_DEBUG
+__device__ __forceinline__ void lds_poison_all(void* p, uint32_t bytes) {
+  uint32_t* q = static_cast<uint32_t*>(p);
+  for (uint32_t i = threadIdx.x; i < bytes / 4; i += blockDim.x) q[i] = kLdsPoison;
+}
+#define USW_LDS_POISON(buf)                                        \
+  do {                                                             \
+    ::usw_dev::lds_poison_all((void*)(buf), sizeof(buf));          \
+    __syncthreads();                                               \
+  } while (0)
+#else
+#define USW_LDS_POISON(buf) \
+  do {                      \
+  } while (0)
+#endif
+
 // Inclusive prefix sum over the 64 lanes with DPP (no LDS round trips):
 // Hillis-Steele inside each 16-lane row, then the row totals are carried by
 // the row_bcast:15 and row_bcast:31 broadcasts.

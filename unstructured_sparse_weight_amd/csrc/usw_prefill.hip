@@ -94,6 +94,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a)
   __shared__ __attribute__((aligned(16))) uint32_t lut[32];
   __shared__ uint32_t offtab[kMaxCols + 1];
   __shared__ uint32_t last_flag;
+  USW_LDS_POISON(stage);
+  USW_LDS_POISON(abuf);
+  USW_LDS_POISON(xs);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -394,6 +397,10 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
   __shared__ __attribute__((aligned(16))) u32x2_t bmw[3][64];   // their bitmap words
   __shared__ uint32_t offtab[kMaxCols + 1];
   __shared__ uint32_t last_flag;
+  USW_LDS_POISON(stage);
+  USW_LDS_POISON(abuf);
+  USW_LDS_POISON(xs);
+  USW_LDS_POISON(bmw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

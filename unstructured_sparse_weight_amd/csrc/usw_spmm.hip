@@ -242,6 +242,7 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   constexpr int kRed = kW * 4 * NB * 64 * 4 * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStage > kRed ? kStage : kRed];
   __shared__ uint32_t last_flag;
+  USW_LDS_POISON(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -464,6 +465,7 @@ __global__ __launch_bounds__(kRingThreads, 5) void decode_ring_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[32];
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing > kRed ? kRing : kRed];
   __shared__ uint32_t last_flag;
+  USW_LDS_POISON(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -591,6 +593,20 @@ __global__ __launch_bounds__(kRingThreads, 5) void decode_ring_kernel(Args a) {
       auto step_loads = [&](int c) -> int {
         const int sv = (c + R - 1 - c_begin) % R;
         int n = 0;
+#ifdef USW_DEBUG
+        // The areas this step loads into hold NaNs until the loads land:
+        // slot sv's values and X^T, the next slot's bitmap words.
+        auto poison = [&](uint8_t* p, int bytes) {
+          const u32x4_t v = {kLdsPoison, kLdsPoison, kLdsPoison, kLdsPoison};
+          for (int off = 16 * lane; off < bytes; off += 1024) lds_store_b128(lds_addr(p) + off, v);
+        };
+        if (c + R - 1 < c_end) {
+          poison(slot_vals(sv), kRingVals);
+          poison(slot_x(sv), kRingX);
+        }
+        if (c + R < c_end) poison(slot_bm(sv == R - 1 ? 0 : sv + 1), 512);
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+#endif
         if (c + R - 1 < c_end) {
           issue_x(c + R - 1, sv);
           n += 2 + issue_vals(off_at(c + R - 1), off_at(c + R), sv);

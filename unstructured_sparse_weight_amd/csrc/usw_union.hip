@@ -156,6 +156,7 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
   constexpr int kRed = kUWaves * 4 * NB * 64 * 4 * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStage > kRed ? kStage : kRed];
   __shared__ uint32_t last_flag;
+  USW_LDS_POISON(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -389,6 +390,7 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
   constexpr int kRed = kU16Waves * 4 * NB * 64 * 4 * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStage > kRed ? kStage : kRed];
   __shared__ uint32_t last_flag;
+  USW_LDS_POISON(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
