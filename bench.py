@@ -396,6 +396,10 @@ def main():
                     "frac_of_streaming_ceiling": round(achieved / stream_gbps, 4)}
     if (M, K) == (20480, 5120):
         workload = f"opt13b_ffn_up_{M}x{K}_s{s}_N{N}"
+        if union:
+            # the union layouts and payloads are separate measurements
+            workload += (f"_{args.dtype}" if args.dtype != "i4" else "") + (f"_lt{args.lt}" if args.lt != 64 else "") + \
+                ("_reordered" if args.reorder else "")
     elif prefill and (M, K) in ((11008, 4096), (4096, 11008)):
         workload = f"llama7b_prefill_{M}x{K}_s{s}_N{N}"
     else:
