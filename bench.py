@@ -57,14 +57,16 @@ def parse():
     p.add_argument("--dtype", default="f16", choices=["f16", "i4", "i2"],
                    help="value type: fp16, INT4, or 2-bit (union format only)")
     p.add_argument("--format", default="tca", choices=["tca", "union", "cbc", "encode", "encode_union", "encode_cbc"],
-                   help="tca: TCA-BME bitmaps (usw_spmm); union: IE-BME union-mask INT4 with 64x64 tiles and 2x2"
-                        " areas (usw_union_spmm; implies --dtype i4); cbc: Tiled-CBC spMspV with dynamic pruning"
+                   help="tca: TCA-BME bitmaps (usw_spmm); union: IE-BME union-mask INT4 or 2-bit, LT shape and"
+                        " area grid from --lt and --areas (usw_union_spmm; fp16 becomes INT4); cbc: Tiled-CBC spMspV with dynamic pruning"
                         " (usw_cbc_spmspv; implies --N 1 and fp16); encode: the on-device TCA-BME encoder"
                         " (usw_encode_device_index + usw_encode_device_values) of the weight, not the SpMM;"
                         " encode_union: the on-device IE-BME INT4 encoder (64x64 LTs, 2x2 areas); encode_cbc: the"
                         " on-device Tiled-CBC encoder")
-    p.add_argument("--lt", type=int, default=64, choices=[64, 16],
-                   help="union: LT height (64 x 64 or 16 x 64 LTs, 2 x 2 areas)")
+    p.add_argument("--lt", type=int, default=64, choices=[64, 32, 16],
+                   help="union: LT height (LTs of 64, 32 or 16 rows by 64 columns)")
+    p.add_argument("--areas", default="2x2",
+                   help="union: the R_A x C_A area grid of an LT, e.g. 2x2, 4x1, 1x8")
     p.add_argument("--reorder", action="store_true",
                    help="union with --lt 16: bitmap-aware row reordering of every LT before encoding"
                         " (usw_union_reorder, then usw_union_encode_reordered)")
@@ -177,6 +179,11 @@ def main():
         args.dtype = "i4"
     if not union and args.dtype == "i2":
         raise SystemExit("2-bit values exist in the union format only (--format union --dtype i2)")
+    try:
+        areas = tuple(int(v) for v in args.areas.lower().split("x"))
+        assert len(areas) == 2
+    except (ValueError, AssertionError):
+        raise SystemExit("--areas takes R_AxC_A, e.g. 2x2 or 4x1")
     if cbc:
         args.dtype, args.N = "f16", 1
     M, K, N, s = args.M, args.K, args.N, args.sparsity
@@ -211,11 +218,11 @@ def main():
         if args.reorder:
             if args.lt != 16:
                 raise SystemExit("--reorder needs --lt 16 (the solver takes LTs of at most 20 rows)")
-            perms, before, after = usw.union_reorder(W, mask, lt, (2, 2))
+            perms, before, after = usw.union_reorder(W, mask, lt, areas)
             log(f"[bench] row reordering {time.time() - t:.2f} s: active union entries {int(before.sum())}"
                 f" -> {int(after.sum())} ({100.0 * (1 - after.sum() / max(before.sum(), 1)):.2f}% fewer)")
             t = time.time()
-        h = usw.union_encode_host(W, mask, lt, (2, 2), args.dtype, perm=perms)
+        h = usw.union_encode_host(W, mask, lt, areas, args.dtype, perm=perms)
         kept = int(mask.sum())
         log(f"[bench] host union encode {time.time() - t:.2f} s, payload={h.payload} for nnz={kept}"
             f" ({h.payload / max(kept, 1):.3f} stored per kept weight)")
@@ -365,12 +372,15 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(W, mask, X, M, K, N, args.dtype, args.cpu_reps, union, cbc, tau,
-                           lt=(args.lt, 64), perms=perms if union else None)
+                           lt=(args.lt, 64), perms=perms if union else None, areas=areas)
 
     if cbc:
         kname = "cbc_spmspv_kernel"
     elif union:
-        kname = "union16_decode_kernel" if args.lt == 16 else "union_decode_kernel"
+        if areas != (2, 2) or args.lt == 32 or (args.lt == 64 and args.reorder):
+            kname = "union_grid_decode_kernel"
+        else:
+            kname = "union16_decode_kernel" if args.lt == 16 else "union_decode_kernel"
     elif prefill:
         kname = "prefill_ws_kernel" if N > 256 else "prefill_kernel"
     else:
@@ -399,7 +409,7 @@ def main():
         if union:
             # the union layouts and payloads are separate measurements
             workload += (f"_{args.dtype}" if args.dtype != "i4" else "") + (f"_lt{args.lt}" if args.lt != 64 else "") + \
-                ("_reordered" if args.reorder else "")
+                (f"_a{areas[0]}x{areas[1]}" if areas != (2, 2) else "") + ("_reordered" if args.reorder else "")
     elif prefill and (M, K) in ((11008, 4096), (4096, 11008)):
         workload = f"llama7b_prefill_{M}x{K}_s{s}_N{N}"
     else:
@@ -425,7 +435,7 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, magnitude pruning, N(0,1) activations)",
         "config": {"workload": workload,
                    "format": "tiled_cbc_spmspv" if cbc else (
-                       (f"ie_bme_union_2x2_lt{args.lt}" + ("_reordered" if args.reorder else "")) if union
+                       (f"ie_bme_union_{areas[0]}x{areas[1]}_lt{args.lt}" + ("_reordered" if args.reorder else "")) if union
                        else "tca_bme"),
                    "M": M, "K": K, "N": N, "sparsity": s, "values": args.dtype, "groupTile": "64x64",
                    "rotation_copies": R, "splits": args.splits or "auto",
@@ -607,7 +617,8 @@ def encode_bench(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(W, mask, X, M, K, N, dtype, reps, union=False, cbc=False, tau=0.0, lt=(64, 64), perms=None):
+def cpu_baseline(W, mask, X, M, K, N, dtype, reps, union=False, cbc=False, tau=0.0, lt=(64, 64), perms=None,
+                 areas=(2, 2)):
     """The oracle as it stands (decode + fp64 product) on the host cores."""
     import oracle.tca_bme as ob
     import oracle.ie_bme as ou
@@ -619,9 +630,9 @@ def cpu_baseline(W, mask, X, M, K, N, dtype, reps, union=False, cbc=False, tau=0
     elif union:
         vt = ob.VAL_I2 if dtype == "i2" else ob.VAL_I4
         if perms is not None:
-            enc = ou.encode_union_reordered(W, mask, perms, lt[0], lt[1], 2, 2, vt)
+            enc = ou.encode_union_reordered(W, mask, perms, lt[0], lt[1], areas[0], areas[1], vt)
         else:
-            enc = ou.encode_union(W, mask, lt[0], lt[1], 2, 2, vt)
+            enc = ou.encode_union(W, mask, lt[0], lt[1], areas[0], areas[1], vt)
         product = ou.spmm_union
     else:
         enc = ob.encode(W, mask) if dtype == "f16" else ob.encode_i4(W, mask)

@@ -124,8 +124,14 @@ def test_union_argument_errors_return_before_launch():
     assert L.usw_union_spmm_workspace(B(fmt_of(h, val_type=7)), 8, 0, B(sz)) == -3
     # valid formats the kernel does not take
     assert L.usw_union_spmm_workspace(B(fmt_of(h, val_type=1)), 8, 0, B(sz)) == -5
-    assert L.usw_union_spmm_workspace(B(fmt_of(h, r_a=4, c_a=1)), 8, 0, B(sz)) == -5
-    assert L.usw_union_spmm_workspace(B(fmt_of(h, lt_m=32)), 8, 0, B(sz)) == -5
+    assert L.usw_union_spmm_workspace(B(fmt_of(h, lt_k=32)), 8, 0, B(sz)) == -5          # LTs 64 columns wide
+    assert L.usw_union_spmm_workspace(B(fmt_of(h, c_a=16)), 8, 0, B(sz)) == -5           # areas 4 columns wide
+    assert L.usw_union_spmm_workspace(B(fmt_of(h, lt_m=128)), 8, 0, B(sz)) == -5         # LTs taller than a strip
+    assert L.usw_union_spmm_workspace(B(fmt_of(h, lt_m=8, r_a=1, c_a=4)), 8, 0, B(sz)) == -5
+    # other area grids and LT heights of 16, 32 and 64 rows run
+    assert L.usw_union_spmm_workspace(B(fmt_of(h, r_a=4, c_a=1)), 8, 0, B(sz)) == 0
+    assert L.usw_union_spmm_workspace(B(fmt_of(h, lt_m=32)), 8, 0, B(sz)) == 0
+    assert L.usw_union_spmm_workspace(B(fmt_of(h, r_a=1, c_a=8)), 8, 0, B(sz)) == 0
     # spmm argument checks (host pointers: any launch would fail)
     x = np.zeros((8, 512), np.uint16)
     y = np.zeros((8, 256), np.uint16)

@@ -128,8 +128,8 @@ def test_reordered_argument_errors():
                                         vals.ctypes.data, 4, sc.ctypes.data, rm.ctypes.data) == -10
     assert L.usw_union_encode_reordered(wp, mp, *args, perms.ctypes.data, bm.ctypes.data, off.ctypes.data,
                                         vals.ctypes.data, vals.size, sc.ctypes.data, rm.ctypes.data) == 0
-    # product entry points: 16-row LTs need M a multiple of 64; a rowmap
-    # needs 16-row LTs
+    # product entry points: LTs shorter than 64 rows need M a multiple of
+    # 64; row maps run on LTs of 16, 32 and 64 rows
     h = usw.union_encode_host(W, mask, (16, 64), (2, 2), "i4", perm=perms)
     sz = ctypes.c_size_t()
     assert L.usw_union_spmm_workspace(B(h.fmt()), 8, 0, B(sz)) == 0
@@ -139,6 +139,9 @@ def test_reordered_argument_errors():
     h64 = usw.union_encode_host(W, mask, (64, 64), (2, 2), "i4")
     f = h64.fmt()
     f.rowmap = rm.ctypes.data
+    assert L.usw_union_spmm_workspace(B(f), 8, 0, B(sz)) == 0
+    h8 = usw.union_encode_host(W, mask, (8, 64), (2, 2), "i4", perm=random_perms(128 // 8 * 2, 8, 8))
+    f = h8.fmt()
     assert L.usw_union_spmm_workspace(B(f), 8, 0, B(sz)) == -5
     x = np.zeros((8, K), np.uint16)
     y = np.zeros((8, M), np.uint16)

@@ -110,16 +110,18 @@ def test_int4_kernel_under_lds_poison(dbg, N):
     check(y, ob.spmm_fp64(np.where(mask, W, np.float16(0)), X), f"INT4 N={N}")
 
 
-@pytest.mark.parametrize("lt,dtype,reorder", [((64, 64), "i4", False), ((16, 64), "i4", True),
-                                             ((64, 64), "i2", False), ((16, 64), "i2", True)])
-def test_union_kernels_under_lds_poison(dbg, lt, dtype, reorder):
+@pytest.mark.parametrize("lt,areas,dtype,reorder", [((64, 64), (2, 2), "i4", False), ((16, 64), (2, 2), "i4", True),
+                                                   ((64, 64), (2, 2), "i2", False), ((16, 64), (2, 2), "i2", True),
+                                                   ((16, 64), (4, 1), "i4", True), ((32, 64), (1, 4), "i4", False),
+                                                   ((64, 64), (4, 4), "i2", False)])
+def test_union_kernels_under_lds_poison(dbg, lt, areas, dtype, reorder):
     M, K, N = 512, 2048, 16
     rng = np.random.default_rng(70 + lt[0])
     mask = wl.mask_bernoulli(M, K, 0.5, rng)
     W = (wl.weight_int4_exact if dtype == "i4" else wl.weight_int2_exact)(M, K, rng, mask)
     X = wl.activations_small_int(N, K, rng)
-    perms = usw.union_reorder(W, mask, lt, (2, 2))[0] if reorder else None
-    enc = usw.union_to_device(usw.union_encode_host(W, mask, lt, (2, 2), dtype, perm=perms), DEV)
+    perms = usw.union_reorder(W, mask, lt, areas)[0] if reorder else None
+    enc = usw.union_to_device(usw.union_encode_host(W, mask, lt, areas, dtype, perm=perms), DEV)
     f = enc.fmt()
     x = torch.from_numpy(X).to(DEV)
     y = torch.empty((N, M), dtype=torch.float32, device=DEV)
@@ -127,7 +129,7 @@ def test_union_kernels_under_lds_poison(dbg, lt, dtype, reorder):
     ws = workspace(need)
     assert dbg.usw_union_spmm(B(f), x.data_ptr(), y.data_ptr(), 3, N, 0, ws.data_ptr(), need, stream()) == 0
     torch.cuda.synchronize()
-    check(y, ob.spmm_fp64(np.where(mask, W, np.float16(0)), X), f"union {lt} {dtype} reorder={reorder}")
+    check(y, ob.spmm_fp64(np.where(mask, W, np.float16(0)), X), f"union {lt} {areas} {dtype} reorder={reorder}")
 
 
 def test_cbc_kernel_under_lds_poison(dbg):

@@ -21,10 +21,13 @@ struct Args {
   void* __restrict__ Y;
   float* __restrict__ part;       // split-K partial sums [splits][N][M] (splits > 1)
   uint32_t* __restrict__ counters;  // per 64-row strip: workgroups done (splits > 1), kept at 0 between calls
-  const uint8_t* __restrict__ rowmap;  // IE-BME with reordered 16-row LTs: [NLT][16] stored row of each row of W
+  const uint8_t* __restrict__ rowmap;  // IE-BME with reordered LTs: [NLT][lt_m] stored row of each row of W
   uint64_t values_alloc;           // padded size of the values buffer in bytes (>= 16)
   int M, K, N, Gc, splits;
   int remap;                       // 1: keep the splits of a strip on one XCD
+  // IE-BME area grid (union_grid_decode_kernel): log2 of the area (= union
+  // mask) rows and columns, of the area columns C_A and of Q = R_A C_A.
+  int lg_am, lg_ak, lg_ca, lg_q;
 };
 
 // Writes a strip's sums to Y or, with split K, to split sidx's partial sums.

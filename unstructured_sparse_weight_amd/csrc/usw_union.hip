@@ -284,7 +284,6 @@ constexpr int kU16Vbuf = 1024 + 64;          // LDS payload buffer per LT (+ wha
 constexpr int kU16Tab = 32 * 8;              // 4 LTs x 8 logical rows: bits and the rank of the first bit
 constexpr int kU16Waves = 4;
 constexpr int kU16Threads = 64 * kU16Waves;
-constexpr int kU16MaxCols = 15;              // LT columns per wave: 16 offsets per LT row in one register
 
 template <int NB>
 struct U16Slot {
@@ -499,6 +498,301 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
 }
 
 // ---------------------------------------------------------------------------
+// General area grids: LTs of 16, 32 or 64 rows by 64 columns, any R_A x C_A
+// ---------------------------------------------------------------------------
+//
+// The section states IE-BME and the LSPD gather for a general R_A x C_A grid
+// (Q = R_A C_A areas of (H_L / R_A) x (K_L / C_A)); the two kernels above are
+// the 2 x 2 cases.  This one takes the grid at run time (powers of two, area
+// width 8..64 columns, whole 64-bit words per LT) and the LT height as a
+// template parameter, with or without row maps.
+//
+//   * One workgroup owns one 64-row strip, i.e. F = 64 / H_L stacked LTs, and
+//     a range of LT columns; each wave streams its own run of columns one
+//     column ahead in registers, as in the kernels above.
+//   * Table row t < 64 / R_A of a column step is logical union row t % am of
+//     the strip's LT t / am (am = H_L / R_A rows of ak = 64 / C_A bits): its
+//     bits and the LDS element position of its first active value in area
+//     stream 0 (a DPP prefix scan, segmented per LT).
+//   * Fragment (fr, ks) holds strip rows 16 fr .. +15, i.e. rows of LT
+//     fr / (H_L / 16); lane (i, g) holds row r of that LT and columns
+//     kc = 32 ks + 8 g .. +7.  Its stored row s (rowmap, else r) lies in area
+//     row s / am at logical row s % am; its columns lie in area column
+//     kc / ak at logical columns kc % ak .. +7 (an area is at least 8 wide,
+//     so one byte of the union row).  That byte's selectors and its rank
+//     (row base + masked popcount) address stream q = (s / am) C_A + kc / ak
+//     at rank + q P: one traversal and one rank for the row's values in
+//     every area stream.
+
+constexpr int kUGWaves = 4;
+constexpr int kUGThreads = 64 * kUGWaves;
+constexpr int kUGTab = 64 * 16;                // up to 64 table rows of {bits lo, bits hi, base, -}
+
+// Per column step: F LTs of C 1 KB payload chunks each (payload <= H_L 64
+// codes plus a 16-byte head).
+template <int LTM, int BITS>
+struct UGShape {
+  static constexpr int F = 64 / LTM;
+  static constexpr int C = (LTM * 64 * BITS / 8 + 16 + 1023) / 1024;
+  static constexpr int NCH = F * C;
+  static constexpr int kVbuf = NCH * 1024 + 64;   // + what a window reads past the last chunk
+  static constexpr int kMaxCols = 64 / F - 1;     // LT columns per wave: offsets of F LT rows in one register
+  static_assert(LTM == 16 || LTM == 32 || LTM == 64, "LT heights of 16, 32 or 64 rows");
+  static_assert(NCH <= 4, "four payload chunks per step");
+};
+
+template <int NB, int NCH, int F>
+struct UGSlot {
+  u32x4_t v[NCH];      // lane's 16-byte piece of each payload chunk
+  uint32_t lo, hi;     // lane t < 64 / R_A: table row t's union bits
+  uint32_t srow[4];    // stored row of the lane's row of W, per fragment (with a rowmap)
+  u32x4_t x[2][NB];
+  uint32_t delta[F];   // payload elements before LT f's first one in its first piece (wave-uniform)
+  uint32_t P[F];       // active union positions of LT f (wave-uniform)
+};
+
+// Issue the loads of LT column c of strip gi; o0[f], o1[f] frame LT f's
+// payload elements.
+template <int LTM, int NB, int BITS>
+__device__ __forceinline__ void ugslot_load(UGSlot<NB, UGShape<LTM, BITS>::NCH, UGShape<LTM, BITS>::F>& s,
+                                            const Args& a, int gi, int c, int lane,
+                                            const uint32_t (&o0)[UGShape<LTM, BITS>::F],
+                                            const uint32_t (&o1)[UGShape<LTM, BITS>::F]) {
+  using S = UGShape<LTM, BITS>;
+  const int64_t t0 = static_cast<int64_t>(S::F * gi) * a.Gc + c;   // LT f of the strip is t0 + f Gc
+  // Union rows first (the table is written while the rest may still be in
+  // flight).  Row lr of an LT is bits lr ak .. lr ak + ak - 1 of its words.
+  {
+    const int rows = S::F << a.lg_am;
+    const int t = min(lane, rows - 1);
+    const int f = t >> a.lg_am;
+    const int lr = t & ((1 << a.lg_am) - 1);
+    const int bit = lr << a.lg_ak;
+    const int lg_wpl = a.lg_am + a.lg_ak - 6;
+    uint64_t wd = a.bitmaps[((t0 + static_cast<int64_t>(f) * a.Gc) << lg_wpl) + (bit >> 6)];
+    wd >>= (bit & 63);
+    if (a.lg_ak < 6) wd &= (1ull << (1 << a.lg_ak)) - 1ull;
+    if (lane >= rows) wd = 0;
+    s.lo = static_cast<uint32_t>(wd);
+    s.hi = static_cast<uint32_t>(wd >> 32);
+  }
+  const int i = lane & 15;
+  // The map byte of the lane's row in each fragment, as vector loads (counted
+  // in order with the slot's other loads).
+  if (a.rowmap) {
+#pragma unroll
+    for (int fr = 0; fr < 4; ++fr) {
+      const int f = fr / (LTM / 16);
+      const int r = (fr % (LTM / 16)) * 16 + i;
+      s.srow[fr] = a.rowmap[(t0 + static_cast<int64_t>(f) * a.Gc) * LTM + r];
+    }
+  }
+  const uint64_t top = a.values_alloc - 16;
+  const uint32_t pmax = static_cast<uint32_t>(LTM * 64) >> a.lg_q;
+#pragma unroll
+  for (int f = 0; f < S::F; ++f) {
+    // The clamps keep windows inside the buffer even for offsets that
+    // disagree with the union words.
+    s.P[f] = min((o1[f] - o0[f]) >> a.lg_q, pmax);
+    const uint64_t a0 = min(Packed<BITS>::chunk_start(o0[f]), top);
+    s.delta[f] = Packed<BITS>::chunk_delta(o0[f], a0);
+    const uint32_t nch = min(Packed<BITS>::chunk_count(o1[f], a0), static_cast<uint32_t>(S::C * 64));
+    const uint32_t last = min(nch > 0 ? nch - 1 : 0u, static_cast<uint32_t>((top - a0) >> 4));
+    const int span = __builtin_amdgcn_readfirstlane(static_cast<int>(16 * (last + 1)));
+#pragma unroll
+    for (int k = 0; k < S::C; ++k) {
+      const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values + a0 + 1024 * k), 0,
+                                                          max(span - 1024 * k, 0), kBufferRsrcWord3);
+      s.v[f * S::C + k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * lane, 0, 0));
+    }
+  }
+  const int kb = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = min(nb * 16 + i, a.N - 1);
+      s.x[ks][nb] = *reinterpret_cast<const u32x4_t*>(a.X + static_cast<size_t>(n) * a.K + c * kGT + ks * 32 + kb * 8);
+    }
+}
+
+// Rank table of a column step: entry t = {row bits lo, hi, element position
+// of the row's first active value in LDS (area stream 0 of its LT)}.
+// base[f]: where LT f's payload starts in LDS.
+template <int F>
+__device__ __forceinline__ void ug_tab_write(uint8_t* tab, uint32_t lo, uint32_t hi, const uint32_t (&base)[F],
+                                             int lg_am, int lane) {
+  const uint32_t pc = __builtin_popcount(lo) + __builtin_popcount(hi);   // zero past the last row
+  const uint32_t excl = wave_inclusive_scan(pc) - pc;
+  const uint32_t first = __shfl(excl, lane & ~((1 << lg_am) - 1));      // the prefix at the LT's first row
+  const int f = lane >> lg_am;
+  uint32_t b = base[0];
+#pragma unroll
+  for (int k = 1; k < F; ++k) b = f == k ? base[k] : b;
+  if (lane < (F << lg_am)) {
+    u32x4_t e;
+    e.x = lo;
+    e.y = hi;
+    e.z = b + excl - first;
+    e.w = 0;
+    reinterpret_cast<u32x4_t*>(tab)[lane] = e;
+  }
+}
+
+template <int LTM, int NB, int BITS>
+__device__ __forceinline__ void ug_tile_mma(const UGSlot<NB, UGShape<LTM, BITS>::NCH, UGShape<LTM, BITS>::F>& cur,
+                                            const Args& a, bool mapped, const uint8_t* smem, const uint8_t* tab,
+                                            const u32x2_t* lut, f32x4_t (&acc)[4][NB], int lane) {
+  const int i = lane & 15;
+  const int g = lane >> 4;
+  const uint32_t am_mask = (1u << a.lg_am) - 1u;
+  const uint32_t ak_mask = (1u << a.lg_ak) - 1u;
+#pragma unroll
+  for (int fr = 0; fr < 4; ++fr) {
+    constexpr int kFr = LTM / 16;             // fragments per LT
+    const int f = fr / kFr;
+    const uint32_t r = static_cast<uint32_t>((fr % kFr) * 16 + i);
+    const uint32_t s = mapped ? (cur.srow[fr] & static_cast<uint32_t>(LTM - 1)) : r;
+    const uint32_t ar = s >> a.lg_am;
+    const u32x4_t e = reinterpret_cast<const u32x4_t*>(tab)[(f << a.lg_am) + (s & am_mask)];
+    const uint64_t bits = static_cast<uint64_t>(e.x) | (static_cast<uint64_t>(e.y) << 32);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t kc = static_cast<uint32_t>(32 * ks + 8 * g);
+      const uint32_t lc = kc & ak_mask;
+      const uint32_t q = (ar << a.lg_ca) + (kc >> a.lg_ak);
+      const uint32_t byte = static_cast<uint32_t>(bits >> lc) & 0xFFu;
+      const uint64_t below = bits & ((1ull << lc) - 1ull);
+      const uint32_t rb = e.z + __builtin_popcount(static_cast<uint32_t>(below)) +
+                          __builtin_popcount(static_cast<uint32_t>(below >> 32));
+      const half8_t av = expand_row_i4(Packed<BITS>::window(smem, rb + q * cur.P[f]), lut[byte]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[fr][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, cur.x[ks][nb]),
+                                                             acc[fr][nb], 0, 0, 0);
+    }
+  }
+}
+
+template <int LTM, int NB, int BITS, bool OUT_F16, int OCC>
+__global__ __launch_bounds__(kUGThreads, OCC) void union_grid_decode_kernel(Args a) {
+  using S = UGShape<LTM, BITS>;
+  using Slot = UGSlot<NB, S::NCH, S::F>;
+  __shared__ __attribute__((aligned(16))) u32x2_t lut[256];
+  constexpr int kStage = kUGWaves * (S::kVbuf + kUGTab);
+  constexpr int kRed = kUGWaves * 4 * NB * 64 * 4 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStage > kRed ? kStage : kRed];
+  __shared__ uint32_t last_flag;
+  USW_LDS_POISON(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nblk = static_cast<int>(gridDim.x);
+  const int b = static_cast<int>(blockIdx.x);
+  const int L = a.remap ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int gi = L / a.splits;
+  const int sidx = L - gi * a.splits;
+
+  lut[tid] = row_byte_selectors(static_cast<uint32_t>(tid));
+  __syncthreads();
+
+  // Columns of LTs this wave streams (the host keeps the count <= kMaxCols).
+  const int parts = a.splits * kUGWaves;
+  const int qw = sidx * kUGWaves + w;
+  const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * qw / parts);
+  const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (qw + 1) / parts);
+
+  f32x4_t acc[4][NB];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[f][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint8_t* vb = smem + w * S::kVbuf;
+  uint8_t* tab = smem + kUGWaves * S::kVbuf + w * kUGTab;
+  // LT f's payload buffer, in elements from the start of smem.
+  const uint32_t vb_elems = static_cast<uint32_t>(w * S::kVbuf) * Packed<BITS>::kPerByte;
+
+  // The LT offsets of the wave's columns: lane (64 / F) f + j holds
+  // offsets[(F gi + f) Gc + c_begin + j] for j <= count.
+  constexpr int kLanesPerRow = 64 / S::F;
+  const int cnt = c_end - c_begin;
+  const int fo = lane / kLanesPerRow, jo = lane % kLanesPerRow;
+  const uint32_t ov = a.offsets[static_cast<int64_t>(S::F * gi + fo) * a.Gc + c_begin + min(jo, max(cnt, 0))];
+  auto offs = [&](int c, uint32_t (&o0)[S::F], uint32_t (&o1)[S::F]) {
+    const int j = min(c - c_begin, kLanesPerRow - 1);
+#pragma unroll
+    for (int f = 0; f < S::F; ++f) {
+      o0[f] = __builtin_amdgcn_readlane(ov, kLanesPerRow * f + j);
+      o1[f] = __builtin_amdgcn_readlane(ov, kLanesPerRow * f + min(j + 1, kLanesPerRow - 1));
+    }
+  };
+
+  const bool mapped = a.rowmap != nullptr;
+  if (cnt > 0) {
+    const int c_last = c_end - 1;
+    auto load = [&](Slot& sl, int c) {
+      const int cc = min(c, c_last);
+      uint32_t o0[S::F], o1[S::F];
+      offs(cc, o0, o1);
+      ugslot_load<LTM, NB, BITS>(sl, a, gi, cc, lane, o0, o1);
+    };
+    auto commit = [&](const Slot& sl) {
+#pragma unroll
+      for (int k = 0; k < S::NCH; ++k) reinterpret_cast<u32x4_t*>(vb + k * 1024)[lane] = sl.v[k];
+    };
+    auto write_tab = [&](const Slot& sl) {
+      uint32_t base[S::F];
+#pragma unroll
+      for (int f = 0; f < S::F; ++f)
+        base[f] = sl.delta[f] + vb_elems + static_cast<uint32_t>(f * S::C * 1024) * Packed<BITS>::kPerByte;
+      ug_tab_write<S::F>(tab, sl.lo, sl.hi, base, a.lg_am, lane);
+    };
+    Slot s[2];
+    load(s[0], c_begin);
+    write_tab(s[0]);
+    auto step = [&](Slot& cur, int c, Slot& nxt) {
+      load(nxt, c + 1);
+      commit(cur);
+      wave_sync();
+      ug_tile_mma<LTM, NB, BITS>(cur, a, mapped, smem, tab, lut, acc, lane);
+      wave_sync();
+      write_tab(nxt);
+    };
+    int c = c_begin;
+    for (; c + 2 <= c_end; c += 2) {
+      step(s[0], c, s[1]);
+      step(s[1], c + 1, s[0]);
+    }
+    if (c < c_end) step(s[0], c, s[1]);
+  }
+
+  // Workgroup reduction over waves (fixed order).
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb];
+  __syncthreads();
+
+  finish_strip<NB, true, OUT_F16>(a, gi, sidx, kUGThreads, last_flag, [&](int n, int ml) {
+    // Strip rows ml .. ml+3 are D rows 4g .. 4g+3 (g = (ml / 4) % 4) of
+    // fragment ml / 16: registers 0-3 of lane 16 g + n % 16.
+    const int f = ml >> 4;
+    const int ln = 16 * ((ml >> 2) & 3) + (n & 15);
+    const int nb = n >> 4;
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < kUGWaves; ++ww)
+      sum += *reinterpret_cast<const f32x4_t*>(red + (((ww * 4 + f) * NB + nb) * 64 + ln) * 4);
+    return sum;
+  });
+}
+
+// ---------------------------------------------------------------------------
 // Host dispatch
 // ---------------------------------------------------------------------------
 
@@ -507,10 +801,15 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
 constexpr int kOcc1 = 5;
 constexpr int kOcc2 = 3;
 
+// Which kernel runs a format: the 2 x 2 kernels for their LT shapes, the
+// area-grid kernel for the rest.
+enum class UKind { kLt64, kLt16, kGrid };
+
 struct UPlan {
   int splits;
   int nchunk;   // tokens per pass (16 or 32)
-  bool lt16;    // 16 x 64 LTs (union16_decode_kernel)
+  UKind kind;
+  int ltm;      // LT rows
 };
 
 // Waves per SIMD of the 16-row-LT kernel: 4 up to 16 tokens, 2 for 17..32.
@@ -520,17 +819,21 @@ constexpr int kOcc16b = 2;
 // 64-row strips of the matrix (one workgroup's rows).
 int64_t union_strips(const usw::UnionGeometry& g) { return g.M / 64; }
 
-UPlan union_plan(const usw::UnionGeometry& g, int N, int splits_req) {
+UPlan union_plan(const usw::UnionGeometry& g, bool mapped, int N, int splits_req) {
   UPlan p;
   p.nchunk = N <= 16 ? 16 : 32;
-  p.lt16 = g.lt_m == 16;
+  p.ltm = static_cast<int>(g.lt_m);
+  const bool two_by_two = g.r_a == 2 && g.c_a == 2;
+  p.kind = (two_by_two && g.lt_m == 64 && !mapped) ? UKind::kLt64
+           : (two_by_two && g.lt_m == 16)           ? UKind::kLt16
+                                                    : UKind::kGrid;
   const int64_t strips = union_strips(g);
-  // The four waves of a workgroup share its LT columns; a wave keeps at most
-  // 63 columns' offsets (64-row LTs) or 15 (16-row LTs, four LT rows per
-  // register).
+  // The four waves of a workgroup share its LT columns; a wave keeps the
+  // offsets of at most 63 columns (64-row LTs), 31 (32-row LTs: two LT rows
+  // per register) or 15 (16-row LTs: four LT rows per register).
   const int64_t per_split = kUWaves;
-  const int64_t max_cols = p.lt16 ? kU16MaxCols : 63;
-  const int occ = p.lt16 ? (N <= 16 ? kOcc16a : kOcc16b) : (N <= 16 ? kOcc1 : kOcc2);
+  const int64_t max_cols = g.lt_m - 1;
+  const int occ = p.kind == UKind::kLt64 ? (N <= 16 ? kOcc1 : kOcc2) : (N <= 16 ? kOcc16a : kOcc16b);
   int64_t s = splits_req;
   if (s <= 0) {
     // About one round of resident workgroups, each wave keeping at least 3
@@ -564,23 +867,35 @@ usw_status union_check(const usw_union_fmt* f, int32_t y_type, int32_t N, usw::U
   if (y_type != USW_OUT_F16 && y_type != USW_OUT_F32) return USW_ERR_BAD_DTYPE;
   if (f->reserved != 0) return USW_ERR_BAD_SHAPE;
   if (N < 1) return USW_ERR_BAD_N;
-  if ((f->val_type != USW_VAL_I4 && f->val_type != USW_VAL_I2) || f->lt_k != 64 || f->r_a != 2 || f->c_a != 2)
-    return USW_ERR_UNSUPPORTED;
-  if (f->lt_m == 64) {
-    if (f->rowmap) return USW_ERR_UNSUPPORTED;
-  } else if (f->lt_m != 16 || f->M % 64) {
-    return USW_ERR_UNSUPPORTED;
-  }
+  // Low-bit payloads; LTs of 16, 32 or 64 rows by 64 columns stacked into
+  // 64-row strips; areas at least 8 columns wide (one byte of a union row
+  // per lane).  The geometry already holds R_A | H_L, C_A | 64 and whole
+  // words per LT, so R_A and C_A are powers of two.
+  if ((f->val_type != USW_VAL_I4 && f->val_type != USW_VAL_I2) || f->lt_k != 64) return USW_ERR_UNSUPPORTED;
+  if ((f->lt_m != 16 && f->lt_m != 32 && f->lt_m != 64) || f->M % 64 || g->ak < 8) return USW_ERR_UNSUPPORTED;
   if (f->payload < 0 || f->payload >= (int64_t(1) << 32)) return USW_ERR_BAD_SHAPE;
   if (static_cast<int64_t>(N) * g->M > (int64_t(1) << 40)) return USW_ERR_BAD_SHAPE;
   return USW_OK;
 }
 
+template <int LTM, int NB, int BITS>
+void union_grid_launch(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
+  constexpr int occ = NB == 1 ? kOcc16a : kOcc16b;
+  if (f16out)
+    union_grid_decode_kernel<LTM, NB, BITS, true, occ><<<grid, kUGThreads, 0, s>>>(a);
+  else
+    union_grid_decode_kernel<LTM, NB, BITS, false, occ><<<grid, kUGThreads, 0, s>>>(a);
+}
+
 template <int NB, int BITS>
-void union_launch(const Args& a, bool f16out, bool lt16, dim3 grid, hipStream_t s) {
+void union_launch(const Args& a, bool f16out, const UPlan& p, dim3 grid, hipStream_t s) {
   constexpr int occ = NB == 1 ? kOcc1 : kOcc2;
   constexpr int occ16 = NB == 1 ? kOcc16a : kOcc16b;
-  if (lt16) {
+  if (p.kind == UKind::kGrid) {
+    if (p.ltm == 16) union_grid_launch<16, NB, BITS>(a, f16out, grid, s);
+    else if (p.ltm == 32) union_grid_launch<32, NB, BITS>(a, f16out, grid, s);
+    else union_grid_launch<64, NB, BITS>(a, f16out, grid, s);
+  } else if (p.kind == UKind::kLt16) {
     if (f16out)
       union16_decode_kernel<NB, BITS, true, occ16><<<grid, kU16Threads, 0, s>>>(a);
     else
@@ -592,6 +907,12 @@ void union_launch(const Args& a, bool f16out, bool lt16, dim3 grid, hipStream_t 
   }
 }
 
+int log2i(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << l) < v) ++l;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -601,7 +922,7 @@ usw_status usw_union_spmm_workspace(const usw_union_fmt* f, int32_t N, int32_t s
   usw::UnionGeometry g;
   usw_status st = union_check(f, USW_OUT_F16, N, &g);
   if (st) return st;
-  *bytes = union_workspace_bytes(g, union_plan(g, N, splits < 0 ? 0 : splits));
+  *bytes = union_workspace_bytes(g, union_plan(g, f->rowmap != nullptr, N, splits < 0 ? 0 : splits));
   return USW_OK;
 }
 
@@ -610,7 +931,7 @@ usw_status usw_union_spmm_counter_bytes(const usw_union_fmt* f, int32_t N, int32
   usw::UnionGeometry g;
   usw_status st = union_check(f, USW_OUT_F16, N, &g);
   if (st) return st;
-  *bytes = union_plan(g, N, splits < 0 ? 0 : splits).splits > 1 ? union_counter_bytes(g) : 0;
+  *bytes = union_plan(g, f->rowmap != nullptr, N, splits < 0 ? 0 : splits).splits > 1 ? union_counter_bytes(g) : 0;
   return USW_OK;
 }
 
@@ -622,7 +943,7 @@ usw_status usw_union_spmm(const usw_union_fmt* f, const uint16_t* X, void* Y, in
   // The kernel reads whole 16-byte chunks of values even for an empty payload.
   if (!X || !Y || !f->bitmaps || !f->offsets || !f->scales || !f->values) return USW_ERR_NULL_ARG;
   if (!aligned16(X) || !aligned16(Y) || !aligned16(f->bitmaps) || !aligned16(f->values)) return USW_ERR_MISALIGNED;
-  const UPlan p = union_plan(g, N, splits < 0 ? 0 : splits);
+  const UPlan p = union_plan(g, f->rowmap != nullptr, N, splits < 0 ? 0 : splits);
   const size_t need = union_workspace_bytes(g, p);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return USW_ERR_WORKSPACE;
 
@@ -650,13 +971,17 @@ usw_status usw_union_spmm(const usw_union_fmt* f, const uint16_t* X, void* Y, in
     a.Gc = static_cast<int>(g.lc);
     a.splits = p.splits;
     a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
+    a.lg_am = log2i(g.am);
+    a.lg_ak = log2i(g.ak);
+    a.lg_ca = log2i(g.c_a);
+    a.lg_q = log2i(g.Q);
     const bool i2 = f->val_type == USW_VAL_I2;
     if (nc > 16) {
-      if (i2) union_launch<2, 2>(a, f16out, p.lt16, grid, s);
-      else union_launch<2, 4>(a, f16out, p.lt16, grid, s);
+      if (i2) union_launch<2, 2>(a, f16out, p, grid, s);
+      else union_launch<2, 4>(a, f16out, p, grid, s);
     } else {
-      if (i2) union_launch<1, 2>(a, f16out, p.lt16, grid, s);
-      else union_launch<1, 4>(a, f16out, p.lt16, grid, s);
+      if (i2) union_launch<1, 2>(a, f16out, p, grid, s);
+      else union_launch<1, 4>(a, f16out, p, grid, s);
     }
     if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
   }
