@@ -131,6 +131,38 @@ def measured_traffic(name, kind):
         return None
 
 
+def probe_same_bytes(L, nbytes, dev, stream, steps):
+    """Per-launch time of the library's streaming-read probe over nbytes,
+    timed as the SpMM is: a HIP graph of `steps` launches, each on the next
+    of enough buffers (> 768 MB together) that reads come from HBM, one
+    untimed replay, then HIP events around one replay."""
+    import torch
+    nb = (int(nbytes) + 15) // 16 * 16
+    R = max(2, -(-(768 << 20) // nb))
+    bufs = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(R)]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    cap = torch.cuda.Stream(dev)
+    cap_sp = ctypes.c_void_p(cap.cuda_stream)
+    for b in bufs:
+        if L.usw_probe_read(b.data_ptr(), nb, sink.data_ptr(), cap_sp) != 0:
+            raise RuntimeError("usw_probe_read failed")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(steps):
+            L.usw_probe_read(bufs[i % R].data_ptr(), nb, sink.data_ptr(), cap_sp)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del graph, bufs, sink
+    return us
+
+
 def calibrate_copy(args):
     """A plain copy of 1 GiB (read 1 GiB, write 1 GiB), rotating over two
     buffer pairs so that it streams from HBM."""
@@ -333,6 +365,7 @@ def main():
     torch.cuda.synchronize()
     stream_gbps = probe.numel() / (float(np.median([a_.elapsed_time(b_) for a_, b_ in pe])) * 1e-3) / 1e9
     del probe, sink
+    same_us = probe_same_bytes(L, alg, dev, stream, args.steps) if not args.eager else None
 
     flops = 2.0 * M * K * N
     value = flops / (ms_step * 1e-3) / 1e12
@@ -340,7 +373,8 @@ def main():
     achieved = alg / (kern_avg_ms * 1e-3) / 1e9
     log(f"[bench] step {ms_step * 1e3:.2f} us, kernel avg {kern_avg_ms * 1e3:.2f} us (median {kern_med_ms * 1e3:.2f}),"
         f" {achieved:.0f} GB/s algorithmic, {flops / (kern_avg_ms * 1e-3) / 1e12:.1f} eff TFLOP/s;"
-        f" streaming-read ceiling {stream_gbps:.0f} GB/s")
+        f" streaming-read ceiling {stream_gbps:.0f} GB/s"
+        + (f"; a plain read of the same {alg / 1e6:.1f} MB: {same_us:.2f} us" if same_us else ""))
 
     # Dense fp16 baseline of the same shape and rotation (hipBLASLt through
     # torch.matmul); its output also serves as a sanity check of the timed
@@ -403,7 +437,8 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": kname,
                     "kernel_avg_us": round(kern_avg_ms * 1e3, 3), "alg_bytes_per_launch": int(alg),
                     "streaming_read_ceiling": round(stream_gbps, 1),
-                    "frac_of_streaming_ceiling": round(achieved / stream_gbps, 4)}
+                    "frac_of_streaming_ceiling": round(achieved / stream_gbps, 4),
+                    "plain_read_same_bytes_us": round(same_us, 3) if same_us else None}
     if (M, K) == (20480, 5120):
         workload = f"opt13b_ffn_up_{M}x{K}_s{s}_N{N}"
         if union:

@@ -75,7 +75,7 @@ typedef int32_t usw_status;
 #define USW_ERR_BAD_SHAPE (-2)    /* M, K not positive multiples of gt_m, gt_k; gt_* not multiples of 16 */
 #define USW_ERR_BAD_DTYPE (-3)    /* unknown val_type or y_type */
 #define USW_ERR_BAD_N (-4)        /* N < 1 */
-#define USW_ERR_UNSUPPORTED (-5)  /* valid request with no kernel (a GroupTile shape other than 64x64) */
+#define USW_ERR_UNSUPPORTED (-5)  /* valid request with no kernel for it (e.g. a GroupTile other than 64x64) */
 #define USW_ERR_MISALIGNED (-6)   /* a device pointer is not 16-byte aligned */
 #define USW_ERR_WORKSPACE (-7)    /* workspace NULL or smaller than usw_spmm_workspace() reports */
 #define USW_ERR_CORRUPT (-8)      /* usw_validate: offsets disagree with the bitmaps */
@@ -447,8 +447,8 @@ usw_status usw_union_encode_device_values(const uint16_t* W, const uint8_t* mask
  *             union-mask entries of each LT as given and after its
  *             permutation (the DP minimum).
  * The DP is exponential in lt_m: LTs of at most 20 rows are accepted.  The
- * union kernel runs 64-row LTs, so a reordered encoding of small LTs is a
- * storage format here (usw_union_encode of the permuted W), not a kernel input.
+ * orders feed usw_union_encode_reordered, whose encoding (16-row LTs)
+ * usw_union_spmm multiplies back onto the rows of W.
  * Errors: NULL_ARG (perm NULL, or W and mask both NULL), BAD_SHAPE (as
  * usw_union_encode_query), UNSUPPORTED (lt_m > 20).
  */
@@ -459,7 +459,7 @@ usw_status usw_union_reorder(const uint16_t* W, const uint8_t* mask, int32_t M, 
 /*
  * Workspace bytes and counter bytes of usw_union_spmm for this matrix, N and
  * split factor (splits = 0: automatic; otherwise clamped to
- * [ceil(K / (64 * 4 * 63)), max(1, K / 256)]).  The workspace starts with
+ * [ceil(K / (64 * 4 * (lt_m - 1))), max(1, K / 256)]).  The workspace starts with
  * the counter bytes, which must be zero when a call starts (each call leaves
  * them zero), then fp32 partial sums, which need not be initialised.  A
  * workspace whose counters are not zero gives wrong Y without an error;
@@ -471,19 +471,22 @@ usw_status usw_union_spmm_counter_bytes(const usw_union_fmt* fmt, int32_t N, int
 
 /*
  * Y = W_sp . X on the GPU from an IE-BME encoding (device pointers), with the
- * same X, Y, workspace and stream conventions as usw_spmm.  Kernels take
- * INT4 values and a 2 x 2 area grid, in passes of up to 32 tokens:
- *   - 64 x 64 LTs (rowmap NULL);
- *   - 16 x 64 LTs with M a multiple of 64, with or without a rowmap (the LT
- *     height the reordering solver handles).  Each lane rebuilds the row of
- *     W it holds in the product from the stored row the rowmap names, so
- *     every LT's products land on the rows of W.
- * Each lane reads one union-mask row's rank once and gathers the rows of
- * all the areas with it (the LSPD gather).  fp32 accumulation,
- * deterministic.  Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_N,
- * UNSUPPORTED (other LT shapes or area grids, fp16 values, a rowmap with
- * 64 x 64 LTs, 16-row LTs with M not a multiple of 64), MISALIGNED,
- * WORKSPACE, HIP.  The rowmap is not checked here (usw_union_validate does).
+ * same X, Y, workspace and stream conventions as usw_spmm, in passes of up
+ * to 32 tokens.  The kernels take INT4 or 2-bit values on LTs of 16, 32 or
+ * 64 rows by 64 columns (M a multiple of 64), any area grid the format
+ * allows with areas at least 8 columns wide (c_a <= 8), and a rowmap or none.
+ * The section illustrates R_A = C_A = 2 and states the LSPD gather for a
+ * general grid; 2 x 2 grids on 64 x 64 LTs (no rowmap) and on 16 x 64 LTs
+ * run on kernels specialised for them, every other grid on one that takes
+ * the grid at run time.  Each lane reads the rank of the union-mask byte it
+ * needs once and gathers its row of every area stream with it (the LSPD
+ * gather); with a rowmap it rebuilds the row of W it holds in the product
+ * from the stored row the rowmap names, so every LT's products land on the
+ * rows of W.  fp32 accumulation, deterministic.  Errors: NULL_ARG,
+ * BAD_SHAPE, BAD_DTYPE, BAD_N, UNSUPPORTED (fp16 values, lt_k other than 64,
+ * lt_m other than 16, 32 or 64, M not a multiple of 64, c_a > 8),
+ * MISALIGNED, WORKSPACE, HIP.  The rowmap is not checked here
+ * (usw_union_validate does).
  */
 usw_status usw_union_spmm(const usw_union_fmt* fmt, const uint16_t* X, void* Y, int32_t y_type, int32_t N,
                           int32_t splits, void* ws, size_t ws_bytes, void* stream);
@@ -613,10 +616,10 @@ usw_status usw_cbc_spmspv(const usw_cbc_fmt* fmt, const uint16_t* x, void* y, in
  * non-temporal) on the stream, so that a caller can time the GPU's
  * streaming-read rate, the practical ceiling of the memory-bound SpMM.
  *   buf:  device pointer, 16-byte aligned.
- *   sink: device buffer of at least ceil(bytes / 262144) uint32 words; the
- *         kernel may write some of them (their values carry no meaning).
+ *   sink: device buffer of at least one uint32 word; the kernel may write it
+ *         (its value carries no meaning).
  * Errors: NULL_ARG, MISALIGNED, BAD_SHAPE (more than 2^31 - 1 blocks of
- * 256 KB), HIP.
+ * 8 KB), HIP.
  */
 usw_status usw_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 

@@ -1,10 +1,12 @@
 // Streaming-read probe: the HBM read rate a plain kernel reaches on this
 // GPU, the ceiling the bitmap SpMM's bandwidth is also reported against.
 //
-// Each workgroup reads a contiguous 256 KB run of the buffer in 1 KB wave
-// steps (16-byte loads, lane-contiguous, non-temporal so the reads do not
-// stay in the caches) and folds what it read into one word, written to the
-// sink so that no load is dead.
+// Each workgroup of 512 threads reads a contiguous 8 KB run of the buffer,
+// one 16-byte load per thread (lane-contiguous, non-temporal so the reads do
+// not stay in the caches), and folds what it read into one word, written to
+// the sink so that no load is dead.  Of the run lengths from 8 to 256 KB and
+// 256 to 1024 threads per workgroup measured on MI355X, this shape read
+// fastest at every size from 119 MB to 1 GiB.
 
 #include <hip/hip_runtime.h>
 
@@ -17,8 +19,8 @@ namespace {
 
 using usw_dev::u32x4_t;
 
-constexpr int kProbeThreads = 256;
-constexpr size_t kProbeRun = 256 * 1024;   // bytes per workgroup
+constexpr int kProbeThreads = 512;
+constexpr size_t kProbeRun = 8 * 1024;     // bytes per workgroup
 
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t* __restrict__ buf, size_t n16,
                                                                    uint32_t* __restrict__ sink) {
@@ -33,7 +35,7 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t
       acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
   }
-  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;   // practically never taken; keeps the loads live
+  if (acc == 0x9E3779B9u) sink[0] = acc;   // practically never taken; keeps the loads live
 }
 
 }  // namespace
