@@ -169,3 +169,17 @@ def test_grid_full_size_ffn_up_reordered():
     Xe = wl.activations_small_int(2, 5120, rng)
     he, oe = encode_both(We, mask, 16, (4, 1), "i4", perms)
     assert np.array_equal(gpu(he, Xe), ob.spmm_fp64(ou.dense_weight_union(oe), Xe))
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 64, 1), (64, 64, 33), (128, 192, 5), (64, 4096, 16)])
+@pytest.mark.parametrize("ltm,areas", [(16, (4, 1)), (32, (2, 4)), (64, (1, 1)), (64, (8, 8))])
+def test_grid_small_and_ragged_shapes(M, K, N, ltm, areas):
+    """One strip, one LT column, token counts across pass boundaries, and a
+    single long strip: bit for bit on integer-exact inputs."""
+    if (ltm // areas[0]) * (64 // areas[1]) % 64:
+        pytest.skip("not a valid IE-BME grid")
+    W, mask, X = exact_case(M, K, N, 0.5, 1600 + M + K + N + ltm, "i4")
+    h, o = encode_both(W, mask, ltm, areas, "i4", random_perms(M, K, ltm, 11))
+    Yref = ob.spmm_fp64(ou.dense_weight_union(o), X)
+    assert np.array_equal(gpu(h, X), Yref)
+    assert np.array_equal(gpu(h, X, torch.float16), Yref.astype(np.float16).astype(np.float64))
