@@ -616,24 +616,19 @@ __device__ __forceinline__ void ugslot_load(UGSlot<NB, UGShape<LTM, BITS>::NCH, 
     }
 }
 
-// Rank table of a column step: entry t = {row bits lo, hi, element position
-// of the row's first active value in LDS (area stream 0 of its LT)}.
-// base[f]: where LT f's payload starts in LDS.
-template <int F>
-__device__ __forceinline__ void ug_tab_write(uint8_t* tab, uint32_t lo, uint32_t hi, const uint32_t (&base)[F],
-                                             int lg_am, int lane) {
+// Rank table of a column step: entry t = {row bits lo, hi, active union
+// positions of its LT before the row}.  The reader adds where its LT's
+// payload starts in LDS (wave-uniform), so no lane has to pick one of the
+// F bases by a run-time index.
+__device__ __forceinline__ void ug_tab_write(uint8_t* tab, uint32_t lo, uint32_t hi, int rows, int lg_am, int lane) {
   const uint32_t pc = __builtin_popcount(lo) + __builtin_popcount(hi);   // zero past the last row
   const uint32_t excl = wave_inclusive_scan(pc) - pc;
   const uint32_t first = __shfl(excl, lane & ~((1 << lg_am) - 1));      // the prefix at the LT's first row
-  const int f = lane >> lg_am;
-  uint32_t b = base[0];
-#pragma unroll
-  for (int k = 1; k < F; ++k) b = f == k ? base[k] : b;
-  if (lane < (F << lg_am)) {
+  if (lane < rows) {
     u32x4_t e;
     e.x = lo;
     e.y = hi;
-    e.z = b + excl - first;
+    e.z = excl - first;
     e.w = 0;
     reinterpret_cast<u32x4_t*>(tab)[lane] = e;
   }
@@ -642,7 +637,8 @@ __device__ __forceinline__ void ug_tab_write(uint8_t* tab, uint32_t lo, uint32_t
 template <int LTM, int NB, int BITS>
 __device__ __forceinline__ void ug_tile_mma(const UGSlot<NB, UGShape<LTM, BITS>::NCH, UGShape<LTM, BITS>::F>& cur,
                                             const Args& a, bool mapped, const uint8_t* smem, const uint8_t* tab,
-                                            const u32x2_t* lut, f32x4_t (&acc)[4][NB], int lane) {
+                                            const u32x2_t* lut, uint32_t vb_elems, f32x4_t (&acc)[4][NB], int lane) {
+  using S = UGShape<LTM, BITS>;
   const int i = lane & 15;
   const int g = lane >> 4;
   const uint32_t am_mask = (1u << a.lg_am) - 1u;
@@ -656,6 +652,8 @@ __device__ __forceinline__ void ug_tile_mma(const UGSlot<NB, UGShape<LTM, BITS>:
     const uint32_t ar = s >> a.lg_am;
     const u32x4_t e = reinterpret_cast<const u32x4_t*>(tab)[(f << a.lg_am) + (s & am_mask)];
     const uint64_t bits = static_cast<uint64_t>(e.x) | (static_cast<uint64_t>(e.y) << 32);
+    // Where LT f's payload starts in LDS, in elements.
+    const uint32_t lt_base = cur.delta[f] + vb_elems + static_cast<uint32_t>(f * S::C * 1024) * Packed<BITS>::kPerByte;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const uint32_t kc = static_cast<uint32_t>(32 * ks + 8 * g);
@@ -663,7 +661,7 @@ __device__ __forceinline__ void ug_tile_mma(const UGSlot<NB, UGShape<LTM, BITS>:
       const uint32_t q = (ar << a.lg_ca) + (kc >> a.lg_ak);
       const uint32_t byte = static_cast<uint32_t>(bits >> lc) & 0xFFu;
       const uint64_t below = bits & ((1ull << lc) - 1ull);
-      const uint32_t rb = e.z + __builtin_popcount(static_cast<uint32_t>(below)) +
+      const uint32_t rb = lt_base + e.z + __builtin_popcount(static_cast<uint32_t>(below)) +
                           __builtin_popcount(static_cast<uint32_t>(below >> 32));
       const half8_t av = expand_row_i4(Packed<BITS>::window(smem, rb + q * cur.P[f]), lut[byte]);
 #pragma unroll
@@ -742,13 +740,7 @@ __global__ __launch_bounds__(kUGThreads, OCC) void union_grid_decode_kernel(Args
 #pragma unroll
       for (int k = 0; k < S::NCH; ++k) reinterpret_cast<u32x4_t*>(vb + k * 1024)[lane] = sl.v[k];
     };
-    auto write_tab = [&](const Slot& sl) {
-      uint32_t base[S::F];
-#pragma unroll
-      for (int f = 0; f < S::F; ++f)
-        base[f] = sl.delta[f] + vb_elems + static_cast<uint32_t>(f * S::C * 1024) * Packed<BITS>::kPerByte;
-      ug_tab_write<S::F>(tab, sl.lo, sl.hi, base, a.lg_am, lane);
-    };
+    auto write_tab = [&](const Slot& sl) { ug_tab_write(tab, sl.lo, sl.hi, S::F << a.lg_am, a.lg_am, lane); };
     Slot s[2];
     load(s[0], c_begin);
     write_tab(s[0]);
@@ -756,7 +748,7 @@ __global__ __launch_bounds__(kUGThreads, OCC) void union_grid_decode_kernel(Args
       load(nxt, c + 1);
       commit(cur);
       wave_sync();
-      ug_tile_mma<LTM, NB, BITS>(cur, a, mapped, smem, tab, lut, acc, lane);
+      ug_tile_mma<LTM, NB, BITS>(cur, a, mapped, smem, tab, lut, vb_elems, acc, lane);
       wave_sync();
       write_tab(nxt);
     };
