@@ -472,7 +472,9 @@ def main():
                    "format": "tiled_cbc_spmspv" if cbc else (
                        (f"ie_bme_union_{areas[0]}x{areas[1]}_lt{args.lt}" + ("_reordered" if args.reorder else "")) if union
                        else "tca_bme"),
-                   "M": M, "K": K, "N": N, "sparsity": s, "values": args.dtype, "groupTile": "64x64",
+                   "M": M, "K": K, "N": N, "sparsity": s, "values": args.dtype,
+                   **({"localTile": f"{args.lt}x64", "areas": f"{areas[0]}x{areas[1]}"} if union
+                      else {"gTile": "256x16"} if cbc else {"groupTile": "64x64"}),
                    "rotation_copies": R, "splits": args.splits or "auto",
                    "launch": "eager" if args.eager else "hip_graph"},
         "gbps": round(gbps_step, 1),
