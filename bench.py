@@ -131,6 +131,20 @@ def measured_traffic(name, kind):
         return None
 
 
+def format_stats(h, M, K, kept, union, cbc):
+    """Storage figures of the encoding: compression ratio (dense fp16 bytes
+    over stored bytes), payload-to-metadata ratio (value bytes over index
+    bytes) and the realized sparsity of the mask."""
+    if cbc:
+        index = h.bitmaps.nbytes + h.tile_offsets.nbytes + h.colinfo.nbytes
+        payload = 2 * h.nnz_padded
+    else:
+        index = h.bitmaps.nbytes + h.offsets.nbytes + (h.rowmap.nbytes if union and h.rowmap is not None else 0)
+        payload = h.values_bytes + (h.scales.nbytes if h.scales is not None else 0)
+    return {"cr": round(2.0 * M * K / (index + payload), 4), "pmr": round(payload / index, 4),
+            "realized_sparsity": round(1.0 - kept / (M * K), 6), "stored_bytes": int(index + payload)}
+
+
 def probe_same_bytes(L, nbytes, dev, stream, steps):
     """Per-launch time of the library's streaming-read probe over nbytes,
     timed as the SpMM is: a HIP graph of `steps` launches, each on the next
@@ -491,6 +505,7 @@ def main():
     if cbc:
         out["config"]["dynamic_sparsity"] = args.dp
         out["config"]["tau"] = tau
+    out["format_stats"] = format_stats(h, M, K, int(mask.sum()), union, cbc)
     print(json.dumps(out), flush=True)
 
 

@@ -17,7 +17,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ABI_TESTS = ["tests/test_abi.py", "tests/test_abi_union.py", "tests/test_abi_cbc.py", "tests/test_abi_reorder.py",
-             "tests/test_abi_union_reordered.py", "tests/test_abi_w2.py", "tests/test_properties.py"]
+             "tests/test_abi_union_reordered.py", "tests/test_abi_w2.py", "tests/test_properties.py",
+             "tests/test_store.py"]
 
 
 def asan_runtime():

@@ -26,7 +26,7 @@ __all__ = ["HostEncoding", "Encoding", "encode_host", "encode", "to_device", "va
            "spmm_workspace_bytes", "spmm_counter_bytes", "UnionHostEncoding", "UnionEncoding",
            "union_encode_host", "union_encode", "union_to_device", "union_validate", "union_spmm",
            "union_workspace_bytes", "CbcHostEncoding", "CbcEncoding", "cbc_encode_host", "cbc_encode",
-           "cbc_to_device", "cbc_validate", "cbc_spmspv", "cbc_workspace_bytes", "UswError", "lib"]
+           "cbc_to_device", "cbc_validate", "cbc_spmspv", "cbc_workspace_bytes", "save", "load", "UswError", "lib"]
 
 _VAL = {"f16": USW_VAL_F16, "i4": USW_VAL_I4, "i2": USW_VAL_I2}
 
@@ -543,7 +543,7 @@ def encode(W, mask=None, gt=(64, 64), dtype: str = "f16", device="cuda") -> Enco
 def _values_alloc_bytes(val_type: int, nnz: int) -> int:
     """Values allocation usw_spmm expects: the logical size rounded down to a
     multiple of 16, plus 16 (as usw_encode_query reports it)."""
-    logical = 2 * nnz if val_type == USW_VAL_F16 else (nnz + 1) // 2
+    logical = 2 * nnz if val_type == USW_VAL_F16 else (nnz + 1) // 2 if val_type == USW_VAL_I4 else (nnz + 3) // 4
     return (logical & ~15) + 16
 
 
@@ -660,3 +660,112 @@ def spmm(enc: Encoding, x, y=None, out_dtype=None, splits: int = 0, stream=None)
                             ws.data_ptr() if ws is not None else None, nbytes, ctypes.c_void_p(st.cuda_stream)),
           "usw_spmm")
     return y
+
+
+# ---------------------------------------------------------------------------
+# Offline cache of encoded weights
+# ---------------------------------------------------------------------------
+#
+# Encoding (and for IE-BME the row-reordering search) is offline work; the
+# pages keep the converted weights and load them at inference time.  save()
+# writes a host encoding's buffers and shape fields to an .npz archive (no
+# pickled objects); load() reads it back with pickling disabled and runs the
+# library's validator on it before returning, so a truncated or edited file
+# is rejected instead of reaching a kernel.
+
+_SCALARS = {
+    "tca_bme": ("M", "K", "gt_m", "gt_k", "val_type", "nnz", "values_bytes"),
+    "ie_bme": ("M", "K", "lt_m", "lt_k", "r_a", "c_a", "val_type", "payload", "values_bytes"),
+    "tiled_cbc": ("M", "K", "nnz", "nnz_padded"),
+}
+_ARRAYS = {
+    "tca_bme": (("bitmaps", np.uint64), ("offsets", np.uint32), ("values", np.uint8), ("scales", np.uint16)),
+    "ie_bme": (("bitmaps", np.uint64), ("offsets", np.uint32), ("values", np.uint8), ("scales", np.uint16),
+               ("rowmap", np.uint8)),
+    "tiled_cbc": (("bitmaps", np.uint64), ("tile_offsets", np.uint32), ("colinfo", np.uint32), ("values", np.uint16)),
+}
+_CLASSES = {"tca_bme": HostEncoding, "ie_bme": UnionHostEncoding, "tiled_cbc": CbcHostEncoding}
+_VALIDATE = {"tca_bme": validate, "ie_bme": union_validate, "tiled_cbc": cbc_validate}
+
+
+def save(path, enc) -> None:
+    """Write a host encoding (HostEncoding, UnionHostEncoding or
+    CbcHostEncoding) to an .npz archive."""
+    kind = next((k for k, c in _CLASSES.items() if isinstance(enc, c)), None)
+    if kind is None:
+        raise TypeError("save takes a host encoding; copy device encodings back first")
+    out = {"kind": np.array(kind)}
+    for name in _SCALARS[kind]:
+        out[name] = np.array(int(getattr(enc, name)), dtype=np.int64)
+    for name, dt in _ARRAYS[kind]:
+        a = getattr(enc, name)
+        if a is not None:
+            out[name] = np.ascontiguousarray(a, dtype=dt)
+    np.savez(path, **out)
+
+
+def load(path):
+    """Read an archive written by save(); the result has passed the
+    library's validator (UswError otherwise)."""
+    with np.load(path, allow_pickle=False) as z:
+        if "kind" not in z.files:
+            raise ValueError("not an encoding archive")
+        kind = str(z["kind"])
+        if kind not in _CLASSES:
+            raise ValueError(f"unknown encoding kind {kind!r}")
+        fields = {}
+        for name in _SCALARS[kind]:
+            if name not in z.files or z[name].shape != ():
+                raise ValueError(f"archive lacks the field {name}")
+            fields[name] = int(z[name])
+        for name, dt in _ARRAYS[kind]:
+            if name in z.files:
+                a = z[name]
+                if a.dtype != dt or a.ndim != 1:
+                    raise ValueError(f"field {name} must be a 1-D {np.dtype(dt).name} array")
+                fields[name] = np.ascontiguousarray(a)
+            elif name in ("scales", "rowmap"):
+                fields[name] = None
+            else:
+                raise ValueError(f"archive lacks the field {name}")
+    enc = _CLASSES[kind](**fields)
+    _check_sizes(kind, enc)
+    _VALIDATE[kind](enc)
+    return enc
+
+
+def _check_sizes(kind, enc) -> None:
+    """Array lengths against the shape fields, before any pointer reaches
+    the library (the validator trusts them)."""
+    def need(a, n, name):
+        if a is None or a.size < n:
+            raise ValueError(f"field {name} is shorter than its shape requires")
+    if kind == "tca_bme":
+        if enc.gt_m <= 0 or enc.gt_k <= 0 or enc.M % enc.gt_m or enc.K % enc.gt_k or enc.gt_m % 8 or enc.gt_k % 8:
+            raise ValueError("bad GroupTile shape")
+        ngt = (enc.M // enc.gt_m) * (enc.K // enc.gt_k)
+        need(enc.bitmaps, ngt * (enc.gt_m // 8) * (enc.gt_k // 8), "bitmaps")
+        need(enc.offsets, ngt + 1, "offsets")
+        need(enc.values, _values_alloc_bytes(enc.val_type, enc.nnz), "values")
+        if enc.val_type != USW_VAL_F16:
+            need(enc.scales, enc.M, "scales")
+    elif kind == "ie_bme":
+        if min(enc.lt_m, enc.lt_k, enc.r_a, enc.c_a) <= 0 or enc.M % enc.lt_m or enc.K % enc.lt_k \
+                or enc.lt_m % enc.r_a or enc.lt_k % enc.c_a:
+            raise ValueError("bad LT shape or area grid")
+        nlt = (enc.M // enc.lt_m) * (enc.K // enc.lt_k)
+        need(enc.bitmaps, nlt * (enc.lt_m // enc.r_a) * (enc.lt_k // enc.c_a) // 64, "bitmaps")
+        need(enc.offsets, nlt + 1, "offsets")
+        need(enc.values, _values_alloc_bytes(enc.val_type, enc.payload), "values")
+        if enc.val_type != USW_VAL_F16:
+            need(enc.scales, enc.M, "scales")
+        if enc.rowmap is not None:
+            need(enc.rowmap, nlt * enc.lt_m, "rowmap")
+    else:
+        if enc.M % 256 or enc.K % 16 or enc.M <= 0 or enc.K <= 0:
+            raise ValueError("bad Tiled-CBC shape")
+        ngt = (enc.M // 256) * (enc.K // 16)
+        need(enc.bitmaps, ngt * 64, "bitmaps")
+        need(enc.tile_offsets, ngt + 1, "tile_offsets")
+        need(enc.colinfo, ngt * 16, "colinfo")
+        need(enc.values, enc.nnz_padded, "values")
