@@ -61,7 +61,7 @@ def parse():
                         " area grid from --lt and --areas (usw_union_spmm; fp16 becomes INT4); cbc: Tiled-CBC spMspV with dynamic pruning"
                         " (usw_cbc_spmspv; implies --N 1 and fp16); encode: the on-device TCA-BME encoder"
                         " (usw_encode_device_index + usw_encode_device_values) of the weight, not the SpMM;"
-                        " encode_union: the on-device IE-BME INT4 encoder (64x64 LTs, 2x2 areas); encode_cbc: the"
+                        " encode_union: the on-device IE-BME encoder, INT4 or 2-bit (64x64 LTs, 2x2 areas); encode_cbc: the"
                         " on-device Tiled-CBC encoder")
     p.add_argument("--lt", type=int, default=64, choices=[64, 32, 16],
                    help="union: LT height (LTs of 64, 32 or 16 rows by 64 columns)")
@@ -529,18 +529,20 @@ def encode_bench(args):
     M, K, s = args.M, args.K, args.sparsity
     union = args.format == "encode_union"
     cbc = args.format == "encode_cbc"
-    if union:
+    if union and args.dtype not in ("i4", "i2"):
         args.dtype = "i4"
+    if not union and args.dtype == "i2":
+        raise SystemExit("2-bit values exist in the union format only (--format encode_union --dtype i2)")
     if cbc:
         args.dtype = "f16"
-    vt = usw.USW_VAL_F16 if args.dtype == "f16" else usw.USW_VAL_I4
-    W, mask, _ = wl.config_case(5 if args.dtype == "i4" else 2, M, K, 1, s, layer_id=2)
+    vt = {"f16": usw.USW_VAL_F16, "i4": usw.USW_VAL_I4, "i2": usw.USW_VAL_I2}[args.dtype]
+    W, mask, _ = wl.config_case(2 if args.dtype == "f16" else 5, M, K, 1, s, layer_id=2)
     in_bytes = W.nbytes + mask.nbytes
     R = args.rotation if args.rotation > 0 else max(2, math.ceil(600e6 / in_bytes))
     Ws = [torch.from_numpy(W).to(dev) for _ in range(R)]
     ms = [torch.from_numpy(mask.view(np.uint8)).to(dev) for _ in range(R)]
     if union:
-        enc_fn = lambda w, m: usw.union_encode_device(w, m, (64, 64), (2, 2))  # noqa: E731
+        enc_fn = lambda w, m: usw.union_encode_device(w, m, (64, 64), (2, 2), args.dtype)  # noqa: E731
     elif cbc:
         enc_fn = lambda w, m: usw.cbc_encode_device(w, m)  # noqa: E731
     else:
@@ -606,9 +608,9 @@ def encode_bench(args):
         if not (torch.equal(o.bitmaps, first.bitmaps) and torch.equal(offs_of(o), offs_of(first))
                 and torch.equal(o.values, first.values)):
             raise RuntimeError("device encode is not deterministic")
-    vbytes = 2 * nnz if args.dtype == "f16" else (nnz + 1) // 2
+    vbytes = 2 * nnz if args.dtype == "f16" else (nnz + 1) // 2 if args.dtype == "i4" else (nnz + 3) // 4
     words = first.bitmaps.numel() * 8
-    out_bytes = words + 4 * (ngt + 1) + vbytes + (2 * M if args.dtype == "i4" else 0) + (64 * ngt if cbc else 0)
+    out_bytes = words + 4 * (ngt + 1) + vbytes + (2 * M if args.dtype != "f16" else 0) + (64 * ngt if cbc else 0)
     alg = in_bytes + out_bytes
     enc_ms = idx_ms + val_ms
     achieved = alg / (enc_ms * 1e-3) / 1e9
@@ -620,7 +622,7 @@ def encode_bench(args):
     import oracle.ie_bme as ou
     t = time.perf_counter()
     if union:
-        usw.union_encode_host(W, mask, (64, 64), (2, 2), "i4")
+        usw.union_encode_host(W, mask, (64, 64), (2, 2), args.dtype)
     elif cbc:
         usw.cbc_encode_host(W, mask)
     else:
@@ -630,7 +632,7 @@ def encode_bench(args):
     if not args.no_cpu:
         t = time.perf_counter()
         if union:
-            ou.encode_union(W, mask, 64, 64, 2, 2, ob.VAL_I4)
+            ou.encode_union(W, mask, 64, 64, 2, 2, ob.VAL_I4 if args.dtype == "i4" else ob.VAL_I2)
         elif cbc:
             import oracle.tiled_cbc as oc
             oc.encode_cbc(W, mask)

@@ -397,7 +397,8 @@ usw_status usw_union_encode_reordered(const uint16_t* W, const uint8_t* mask, in
 
 /*
  * On-device IE-BME encoder for a W already in GPU memory: the same bytes as
- * usw_union_encode, INT4 payload only.  Two calls, as for the TCA-BME device
+ * usw_union_encode for INT4 and 2-bit payloads (val_type USW_VAL_I4 or
+ * USW_VAL_I2; rows in natural order).  Two calls, as for the TCA-BME device
  * encoder:
  *
  * usw_union_encode_device_index: union words, LT offsets (offsets[NLT] =
@@ -405,13 +406,15 @@ usw_status usw_union_encode_reordered(const uint16_t* W, const uint8_t* mask, in
  *   W:       device fp16 bits [M][K], 16-byte aligned (required).
  *   mask:    device uint8 [M][K], 8-byte aligned, or NULL (IEEE nonzeros).
  *   bitmaps: device output [NLT * NW]; offsets: device output [NLT+1],
- *            4-byte aligned; scales: device output fp16 [M].
+ *            4-byte aligned; scales: device output fp16 [M] (the b-bit rule
+ *            of the val_type).
  *
- * usw_union_encode_device_values: the Q aligned INT4 streams of every LT,
+ * usw_union_encode_device_values: the Q aligned code streams of every LT,
  * from W, the mask (a pruned weight of an active group is stored as 0) and
  * what the first call wrote.
  *   payload: offsets[NLT] as read back by the caller.
- *   values:  device output of values_capacity >= ceil(payload / 2) bytes,
+ *   values:  device output of values_capacity >= ceil(payload / 2) bytes
+ *            (INT4) or ceil(payload / 4) bytes (2-bit),
  *            16-byte aligned; bytes past the logical size are zeroed.  Writes
  *            stay below the logical size even when payload disagrees with
  *            offsets.

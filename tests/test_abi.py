@@ -323,6 +323,10 @@ def test_device_union_encoder_argument_errors_return_before_launch():
     assert val(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, -1, v, 4096, None) == -10
     assert val(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, 8193, v, 4096, None) == -10
     assert val(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, 10, v + 8, 4096, None) == -6
+    # 2-bit payload: four codes per byte
+    assert val(w, mp, 128, 128, 64, 64, 2, 2, 3, b, o, s, 4096, v, 1023, None) == -10
+    assert val(w, mp, 128, 128, 64, 64, 2, 2, 2, b, o, s, 4096, v, 2047, None) == -10
+    assert val(w, mp, 128, 128, 64, 64, 2, 2, 3, b, o, s, 10, v + 8, 4096, None) == -6
 
 
 @pytest.mark.host_pointers

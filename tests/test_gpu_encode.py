@@ -232,10 +232,10 @@ def test_full_size_matches_host_encoder(case):
 from oracle import ie_bme as ou  # noqa: E402
 
 
-def dev_union_encode(W, mask, lt=(64, 64), areas=(2, 2)):
+def dev_union_encode(W, mask, lt=(64, 64), areas=(2, 2), dtype="i4"):
     Wt = torch.from_numpy(np.ascontiguousarray(W)).to(DEV)
     mt = torch.from_numpy(np.ascontiguousarray(mask)).to(DEV) if mask is not None else None
-    enc = usw.union_encode_device(Wt, mt, lt, areas)
+    enc = usw.union_encode_device(Wt, mt, lt, areas, dtype)
     torch.cuda.synchronize()
     return enc
 
@@ -255,15 +255,17 @@ def assert_union_matches_oracle(enc, o):
 @pytest.mark.parametrize("lt,areas", [((64, 64), (2, 2)), ((32, 64), (2, 2)), ((64, 64), (1, 1)),
                                       ((16, 64), (2, 2)), ((64, 32), (2, 1)), ((64, 64), (4, 2))])
 @pytest.mark.parametrize("density", [0.0, 0.05, 0.5, 1.0])
-def test_device_union_encoder_matches_oracle(lt, areas, density):
+@pytest.mark.parametrize("dtype", ["i4", "i2"])
+def test_device_union_encoder_matches_oracle(lt, areas, density, dtype):
     rng = np.random.default_rng(int(density * 100) + lt[0] + 3 * lt[1] + 11 * areas[0] + areas[1])
     M, K = 128, 256
     W = wl.weight_normal(M, K, rng)
     W[rng.random((M, K)) < 0.05] = np.float16(0.0)
     mask = wl.mask_bernoulli(M, K, density, rng)
-    say(f"[union encode] lt={lt} areas={areas} density={density}")
-    enc = dev_union_encode(W, mask, lt, areas)
-    assert_union_matches_oracle(enc, ou.encode_union(W, mask, lt[0], lt[1], areas[0], areas[1], ob.VAL_I4))
+    say(f"[union encode] lt={lt} areas={areas} density={density} {dtype}")
+    enc = dev_union_encode(W, mask, lt, areas, dtype)
+    vt = ob.VAL_I4 if dtype == "i4" else ob.VAL_I2
+    assert_union_matches_oracle(enc, ou.encode_union(W, mask, lt[0], lt[1], areas[0], areas[1], vt))
 
 
 def test_device_union_null_mask_and_non_finite():
@@ -300,6 +302,52 @@ def test_device_union_odd_runs_across_empty_lts(seed):
     assert_union_matches_oracle(enc, o)
     enc2 = dev_union_encode(W, mask, (16, 64), (2, 2))        # Q = 4: runs of even length
     assert_union_matches_oracle(enc2, ou.encode_union(W, mask, 16, 64, 2, 2, ob.VAL_I4))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_device_union_2bit_runs_across_empty_lts(seed):
+    """2-bit payload: four codes per byte, so a byte can hold the end of one
+    LT's run and the first codes of up to three following LTs (runs of one
+    to three codes next to empty LTs, Q = 1), and active groups whose
+    weight is pruned."""
+    rng = np.random.default_rng(400 + seed)
+    M, K = 256, 512
+    W = wl.weight_normal(M, K, rng)
+    mask = np.zeros((M, K), bool)
+    for ti in range(M // 16):
+        for tj in range(K // 64):
+            c = rng.choice([0, 0, 1, 1, 2, 3, 5])
+            pos = rng.choice(16 * 64, size=c, replace=False)
+            mask[ti * 16 + pos // 64, tj * 64 + pos % 64] = True
+    say(f"[union encode] 2-bit short runs seed={seed}")
+    o = ou.encode_union(W, mask, 16, 64, 1, 1, ob.VAL_I2)
+    off = o.offsets.astype(np.int64)
+    runs = np.diff(off)
+    assert ((runs > 0) & (runs < 4) & (off[1:] % 4 != 0)).any()       # bytes shared across LTs
+    assert_union_matches_oracle(dev_union_encode(W, mask, (16, 64), (1, 1), "i2"), o)
+    # Q = 2 and Q = 8 grids: runs of even lengths and multiples of 8
+    for areas in [(2, 1), (4, 2)]:
+        assert_union_matches_oracle(dev_union_encode(W, mask, (16, 64), areas, "i2"),
+                                    ou.encode_union(W, mask, 16, 64, areas[0], areas[1], ob.VAL_I2))
+
+
+def test_device_union_full_size_2bit_matches_host_and_runs_spmm():
+    """FFN-up 20480 x 5120 with a 2-bit payload at 50%: byte-identical to
+    the host union encoder, and both encodings give the same product bits."""
+    W, mask, X = wl.config_case(5, 20480, 5120, 2, 0.5)
+    say("[union encode] full size FFN-up, 2-bit")
+    enc = dev_union_encode(W, mask, (64, 64), (2, 2), "i2")
+    h = usw.union_encode_host(W, mask, (64, 64), (2, 2), "i2")
+    assert enc.payload == h.payload
+    assert np.array_equal(enc.bitmaps.cpu().numpy().view(np.uint64), h.bitmaps)
+    assert np.array_equal(enc.offsets.cpu().numpy().view(np.uint32), h.offsets)
+    assert np.array_equal(enc.values.cpu().numpy(), h.values)
+    assert np.array_equal(enc.scales.cpu().numpy().view(np.uint16), h.scales)
+    x = torch.from_numpy(X).to(DEV)
+    yd = usw.union_spmm(enc, x)
+    yh = usw.union_spmm(usw.union_to_device(h, DEV), x)
+    torch.cuda.synchronize()
+    assert torch.equal(yd, yh)
 
 
 def test_device_union_full_size_matches_host_and_runs_spmm():

@@ -273,12 +273,15 @@ def _union_encode_reordered_host(W, mask, lt, areas, vt, perm) -> UnionHostEncod
                              b_val.value, scales, rowmap)
 
 
-def union_encode_device(W, mask=None, lt=(64, 64), areas=(2, 2)) -> UnionEncoding:
-    """IE-BME INT4 encoding of a weight already on the GPU
-    (usw_union_encode_device_index, then usw_union_encode_device_values) on
-    torch's current stream; the same bytes as ``union_encode(W, mask, lt,
-    areas, "i4")``.  Reading the payload size between the calls synchronises
-    the stream."""
+def union_encode_device(W, mask=None, lt=(64, 64), areas=(2, 2), dtype: str = "i4") -> UnionEncoding:
+    """IE-BME encoding (INT4, or 2-bit with dtype="i2") of a weight already
+    on the GPU (usw_union_encode_device_index, then
+    usw_union_encode_device_values) on torch's current stream; the same
+    bytes as ``union_encode(W, mask, lt, areas, dtype)``.  Reading the
+    payload size between the calls synchronises the stream."""
+    if dtype not in ("i4", "i2"):
+        raise ValueError("the device IE-BME encoder writes INT4 or 2-bit payloads")
+    vt = _VAL[dtype]
     import torch
     if not (torch.is_tensor(W) and W.is_cuda and W.dtype == torch.float16 and W.dim() == 2):
         raise TypeError("W must be a 2-D float16 CUDA tensor")
@@ -303,16 +306,15 @@ def union_encode_device(W, mask=None, lt=(64, 64), areas=(2, 2)) -> UnionEncodin
     st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     L = lib()
     mp = mask.data_ptr() if mask is not None else None
-    args = (M, K, lt[0], lt[1], areas[0], areas[1], USW_VAL_I4)
+    args = (M, K, lt[0], lt[1], areas[0], areas[1], vt)
     check(L.usw_union_encode_device_index(W.data_ptr(), mp, *args, bitmaps.data_ptr(), offsets.data_ptr(),
                                           scales.data_ptr(), st), "usw_union_encode_device_index")
     payload = int(offsets[nlt].item()) & 0xFFFFFFFF
-    values = torch.empty(_values_alloc_bytes(USW_VAL_I4, payload), dtype=torch.uint8, device=dev)
+    values = torch.empty(_values_alloc_bytes(vt, payload), dtype=torch.uint8, device=dev)
     check(L.usw_union_encode_device_values(W.data_ptr(), mp, *args, bitmaps.data_ptr(), offsets.data_ptr(),
                                            scales.data_ptr(), payload, values.data_ptr(), values.numel(), st),
           "usw_union_encode_device_values")
-    return UnionEncoding(M, K, lt[0], lt[1], areas[0], areas[1], USW_VAL_I4, payload, bitmaps, offsets, values,
-                         scales)
+    return UnionEncoding(M, K, lt[0], lt[1], areas[0], areas[1], vt, payload, bitmaps, offsets, values, scales)
 
 
 def union_reorder(W, mask=None, lt=(16, 64), areas=(2, 2)):

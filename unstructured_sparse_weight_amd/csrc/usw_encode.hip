@@ -1,9 +1,9 @@
 // Device-side encoders for weights already in GPU memory, each writing the
 // same bytes as its host counterpart: TCA-BME (usw_encode; this header's
-// passes below), IE-BME union-mask INT4 (usw_union_encode) and Tiled-CBC
-// (usw_cbc_encode), the last two in their own sections further down.  All
-// three share the in-place scan, the INT4 row-scale kernel and the tail
-// zeroing.
+// passes below), IE-BME union-mask INT4 or 2-bit (usw_union_encode) and
+// Tiled-CBC (usw_cbc_encode), the last two in their own sections further
+// down.  All three share the in-place scan, the b-bit row-scale kernel and
+// the tail zeroing.
 //
 // Format: blog "SpInfer: How bitmaps make sparse LLMs actually fast", section
 // "How TCA-BME addresses the indexing overhead" (8x8 BitmapTiles in one
@@ -18,8 +18,8 @@
 //      offsets[g] as a count.
 //   2. scan:   one workgroup turns the counts in offsets[0..NGT) into the
 //      exclusive prefix offsets[0..NGT] in place.
-//   3. scales (INT4): one wave per row: the largest kept magnitude as
-//      sign-cleared fp16 bits, then i4_scale_bits.
+//   3. scales (INT4, 2-bit): one wave per row: the largest kept magnitude
+//      as sign-cleared fp16 bits, then int_scale_bits for the code width.
 //   4. values: one wave per GroupTile: lane j ranks the kept weights of its
 //      BitmapTile from the bitmap (the wave's exclusive popcount prefix plus
 //      the position inside the tile) and stages the fp16 bits, or the INT4
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(1024) void enc_scan_kernel(uint32_t* __restrict__ o
 template <bool MASK>
 __global__ __launch_bounds__(kEThreads) void enc_scales_kernel(const uint16_t* __restrict__ W,
                                                                const uint8_t* __restrict__ mask,
-                                                               uint16_t* __restrict__ scales, int M, int K) {
+                                                               uint16_t* __restrict__ scales, int M, int K, int qmax) {
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * kEWaves + (threadIdx.x >> 6);
   if (m >= M) return;
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kEThreads) void enc_scales_kernel(const uint16_t* _
     const uint32_t t = __shfl_xor(amax, o);
     amax = t > amax ? t : amax;
   }
-  if (lane == 0) scales[m] = usw::i4_scale_bits(static_cast<uint16_t>(amax));
+  if (lane == 0) scales[m] = usw::int_scale_bits(static_cast<uint16_t>(amax), qmax);
 }
 
 // INT4 code of the first kept weight of GroupTile gid (0 when it has none).
@@ -313,9 +313,10 @@ __global__ __launch_bounds__(kEThreads) void enc_zero_kernel(uint8_t* __restrict
 
 // ---------------------------------------------------------------------------
 // IE-BME union-mask encoding on the device ("UnionSparse", IE-BME: one union
-// bit per area-aligned group of an LT, Q aligned INT4 streams per LT, stream q
-// of LT t at offsets[t] + q P_t, P_t the LT's active positions).  The same
-// bytes as usw_union_encode; INT4 payload only (what the union kernel runs).
+// bit per area-aligned group of an LT, Q aligned streams of INT4 or 2-bit
+// codes per LT, stream q of LT t at offsets[t] + q P_t, P_t the LT's active
+// positions).  The same bytes as usw_union_encode for those payloads (what
+// the union kernels run); reordered rows are a host-side step.
 // ---------------------------------------------------------------------------
 
 struct UnionGeom {
@@ -382,31 +383,62 @@ __global__ __launch_bounds__(kEThreads) void union_index_kernel(const uint16_t* 
   if (lane == 0) counts[t] = static_cast<uint32_t>(g.Q) * cnt;
 }
 
-// INT4 code at stream 0, rank 0 of LT t (its first active position, area 0;
-// 0 where that weight is pruned, or when t has no active position).
-template <bool MASK>
-__device__ inline uint32_t union_first_code(const UnionGeom& g, const uint16_t* W, const uint8_t* mask,
-                                            const uint64_t* bitmaps, const uint16_t* scales, int t, int lane) {
-  const uint64_t word = lane < g.nw ? bitmaps[static_cast<uint64_t>(t) * g.nw + lane] : 0ull;
-  const uint64_t any = __ballot(word != 0);
-  if (!any) return 0;
-  const int f = __builtin_ctzll(any);
-  const uint32_t lo = __shfl(static_cast<uint32_t>(word), f), hi = __shfl(static_cast<uint32_t>(word >> 32), f);
-  const int p = 64 * f + __builtin_ctzll((static_cast<uint64_t>(hi) << 32) | lo);
-  const uint64_t e = union_elem(g, t, 0, p);
+// b-bit code of payload element x (x >= offsets[t + 1], x < payload): the
+// LT t' holding it (offsets[t'] <= x < offsets[t' + 1], found by binary
+// search among the LTs after t), its stream q and rank r there, the r-th
+// active position of t' (wave prefix of its word popcounts, then the r'-th
+// set bit of the word that holds it), and that position's weight in area q
+// (0 where pruned).  Wave-uniform: every lane returns the same value.
+template <bool MASK, int BITS>
+__device__ inline uint32_t union_code_at(const UnionGeom& g, const uint16_t* W, const uint8_t* mask,
+                                         const uint64_t* bitmaps, const uint32_t* offsets, const uint16_t* scales,
+                                         int t, uint64_t x, int lane) {
+  constexpr int kQmax = (1 << (BITS - 1)) - 1;
+  int lo = t + 1, hi = g.nlt - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid + 1] > x)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  const uint64_t ox = offsets[lo];
+  const uint32_t P = static_cast<uint32_t>((offsets[lo + 1] - ox) / static_cast<uint64_t>(g.Q));
+  if (P == 0) return 0;   // offsets that disagree with the words: stay inside the LT
+  const uint32_t i = static_cast<uint32_t>(x - ox);
+  const int q = static_cast<int>(min(i / P, static_cast<uint32_t>(g.Q - 1)));
+  const uint32_t r = i - static_cast<uint32_t>(q) * P;
+  const uint64_t word = lane < g.nw ? bitmaps[static_cast<uint64_t>(lo) * g.nw + lane] : 0ull;
+  const uint32_t pc = __popcll(word);
+  uint32_t incl = pc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  const uint64_t past = __ballot(incl > r);
+  if (!past) return 0;
+  const int owner = __builtin_ctzll(past);
+  const uint32_t before = __shfl(incl - pc, owner);
+  uint64_t w = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl(static_cast<int>(word >> 32), owner))) << 32) |
+               static_cast<uint32_t>(__shfl(static_cast<int>(word), owner));
+  for (uint32_t k = before; k < r; ++k) w &= w - 1;   // drop the active positions ranked before r
+  if (w == 0) return 0;
+  const int p = 64 * owner + __builtin_ctzll(w);
+  const uint64_t e = union_elem(g, lo, q, p);
   const bool kept = MASK ? mask[e] != 0 : (W[e] & 0x7FFFu) != 0;
   if (!kept) return 0;
   const uint32_t row = static_cast<uint32_t>(e / static_cast<uint64_t>(g.K));
-  return static_cast<uint32_t>(usw::i4_code(W[e], usw::f16_to_f64(scales[row]))) & 0xFu;
+  return static_cast<uint32_t>(usw::int_code(W[e], usw::f16_to_f64(scales[row]), kQmax)) & ((1u << BITS) - 1u);
 }
 
 // One wave per LT, lane w Q + q for area q of union word w: it ranks the
 // active positions of word w (wave prefix of the word popcounts plus the
 // position in the word) and stages the area's codes at q P + rank in LDS (0
-// for a pruned weight); the run of Q P codes is then packed two per byte,
-// byte b written by the LT holding code 2b (the high nibble past the run:
-// the next non-empty LT's first code).
-template <bool MASK>
+// for a pruned weight); the run of Q P codes is then packed 8 / BITS per
+// byte, byte b written by the LT holding its first code (codes of the byte
+// past the run come from the following LTs).
+template <bool MASK, int BITS>
 __global__ __launch_bounds__(kEThreads) void union_values_kernel(const uint16_t* __restrict__ W,
                                                                  const uint8_t* __restrict__ mask,
                                                                  const uint64_t* __restrict__ bitmaps,
@@ -414,6 +446,9 @@ __global__ __launch_bounds__(kEThreads) void union_values_kernel(const uint16_t*
                                                                  const uint16_t* __restrict__ scales,
                                                                  uint8_t* __restrict__ values, UnionGeom g,
                                                                  uint64_t payload, uint64_t logical) {
+  constexpr int kQmax = (1 << (BITS - 1)) - 1;
+  constexpr uint32_t kPer = 8 / BITS;
+  constexpr uint32_t kCodeMask = (1u << BITS) - 1u;
   __shared__ uint8_t stage[kEWaves][kMaxBt * 64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * kEWaves + wv;
@@ -442,7 +477,7 @@ __global__ __launch_bounds__(kEThreads) void union_values_kernel(const uint16_t*
       for (int k = 0; k < 8; ++k) {
         if (!((byte >> k) & 1u)) continue;
         const uint32_t code =
-            ((keep >> k) & 1u) ? static_cast<uint32_t>(usw::i4_code(half_of(v, k), s)) & 0xFu : 0u;
+            ((keep >> k) & 1u) ? static_cast<uint32_t>(usw::int_code(half_of(v, k), s, kQmax)) & kCodeMask : 0u;
         st[q * P + r] = static_cast<uint8_t>(code);
         ++r;
       }
@@ -450,22 +485,32 @@ __global__ __launch_bounds__(kEThreads) void union_values_kernel(const uint16_t*
   }
   usw_dev::wave_sync();
   const uint64_t e = o0 + static_cast<uint64_t>(g.Q) * P;
-  uint32_t next = 0;
-  if (P && (e & 1) && e < payload && t + 1 < g.nlt) {
-    int lo = t + 1, hi = g.nlt - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (offsets[mid + 1] > e)
-        hi = mid;
-      else
-        lo = mid + 1;
-    }
-    next = union_first_code<MASK>(g, W, mask, bitmaps, scales, lo, lane);
+  // Codes after the run that share its last byte (the following LTs' first
+  // ones; 0 past the payload).
+  uint32_t tail[kPer - 1];
+#pragma unroll
+  for (uint32_t j = 0; j + 1 < kPer; ++j) {
+    const uint64_t x = e + j;
+    tail[j] = (P && x % kPer != 0 && x < payload && t + 1 < g.nlt && (x / kPer) == ((e - 1) / kPer))
+                  ? union_code_at<MASK, BITS>(g, W, mask, bitmaps, offsets, scales, t, x, lane)
+                  : 0u;
   }
-  for (uint64_t b = (o0 + 1) / 2 + lane; b < (e + 1) / 2; b += 64) {
-    const uint32_t lo4 = st[2 * b - o0];
-    const uint32_t hi4 = 2 * b + 1 < e ? st[2 * b + 1 - o0] : next;
-    if (b < logical) values[b] = static_cast<uint8_t>(lo4 | (hi4 << 4));
+  for (uint64_t b = (o0 + kPer - 1) / kPer + lane; b * kPer < e; b += 64) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kPer; ++j) {
+      const uint64_t x = b * kPer + j;
+      uint32_t c = 0;
+      if (x < e) {
+        c = st[x - o0];
+      } else {
+#pragma unroll
+        for (uint32_t k = 0; k + 1 < kPer; ++k)
+          if (x == e + k) c = tail[k];
+      }
+      packed |= c << (BITS * j);
+    }
+    if (b < logical) values[b] = static_cast<uint8_t>(packed);
   }
 }
 
@@ -610,11 +655,11 @@ usw_status union_enc_geometry(int32_t M, int32_t K, int32_t lt_m, int32_t lt_k, 
                               int32_t val_type, usw::UnionGeometry* g, UnionGeom* ug) {
   usw_status st = usw::make_union_geometry(M, K, lt_m, lt_k, r_a, c_a, g);
   if (st) return st;
-  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4) return USW_ERR_BAD_DTYPE;
+  if (val_type != USW_VAL_F16 && val_type != USW_VAL_I4 && val_type != USW_VAL_I2) return USW_ERR_BAD_DTYPE;
   if (g->M * g->K >= (int64_t(1) << 32)) return USW_ERR_BAD_SHAPE;   // payload then fits the 32-bit offsets
-  // INT4 payload only; LTs of at most 4096 elements (one wave stages the
-  // whole run in LDS), areas whose rows are multiples of 8 positions.
-  if (val_type != USW_VAL_I4 || g->lt_m * g->lt_k > kMaxBt * 64 || g->ak % 8) return USW_ERR_UNSUPPORTED;
+  // INT4 or 2-bit payload; LTs of at most 4096 elements (one wave stages
+  // the whole run in LDS), areas whose rows are multiples of 8 positions.
+  if (val_type == USW_VAL_F16 || g->lt_m * g->lt_k > kMaxBt * 64 || g->ak % 8) return USW_ERR_UNSUPPORTED;
   ug->K = static_cast<int>(g->K);
   ug->lt_m = static_cast<int>(g->lt_m);
   ug->lt_k = static_cast<int>(g->lt_k);
@@ -654,9 +699,9 @@ usw_status usw_encode_device_index(const uint16_t* W, const uint8_t* mask, int32
   enc_scan_kernel<<<1, 1024, 0, hs>>>(offsets, eg.ngt);
   if (val_type == USW_VAL_I4) {
     if (mask)
-      enc_scales_kernel<true><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K);
+      enc_scales_kernel<true><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K, 7);
     else
-      enc_scales_kernel<false><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K);
+      enc_scales_kernel<false><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K, 7);
   }
   return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
 }
@@ -705,15 +750,16 @@ usw_status usw_union_encode_device_index(const uint16_t* W, const uint8_t* mask,
   if (!aligned(W, 16) || (mask && !aligned(mask, 8)) || !aligned(bitmaps, 8) || !aligned(offsets, 4) ||
       !aligned(scales, 2))
     return USW_ERR_MISALIGNED;
+  const int qmax = val_type == USW_VAL_I2 ? 1 : 7;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (mask) {
     union_index_kernel<true><<<blocks_for(g.nlt), kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, ug);
     enc_scan_kernel<<<1, 1024, 0, hs>>>(offsets, ug.nlt);
-    enc_scales_kernel<true><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K);
+    enc_scales_kernel<true><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K, qmax);
   } else {
     union_index_kernel<false><<<blocks_for(g.nlt), kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, ug);
     enc_scan_kernel<<<1, 1024, 0, hs>>>(offsets, ug.nlt);
-    enc_scales_kernel<false><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K);
+    enc_scales_kernel<false><<<blocks_for(g.M), kEThreads, 0, hs>>>(W, mask, scales, M, K, qmax);
   }
   return hipGetLastError() == hipSuccess ? USW_OK : USW_ERR_HIP;
 }
@@ -728,19 +774,26 @@ usw_status usw_union_encode_device_values(const uint16_t* W, const uint8_t* mask
   usw_status st = union_enc_geometry(M, K, lt_m, lt_k, r_a, c_a, val_type, &g, &ug);
   if (st) return st;
   if (payload < 0 || payload > g.M * g.K) return USW_ERR_CAPACITY;
-  const uint64_t logical = static_cast<uint64_t>(payload + 1) / 2;
+  const bool i2 = val_type == USW_VAL_I2;
+  const uint64_t logical = i2 ? static_cast<uint64_t>(payload + 3) / 4 : static_cast<uint64_t>(payload + 1) / 2;
   if (values_capacity < logical) return USW_ERR_CAPACITY;
   if (!aligned(W, 16) || (mask && !aligned(mask, 8)) || !aligned(bitmaps, 8) || !aligned(offsets, 4) ||
       !aligned(scales, 2) || !aligned(values, 16))
     return USW_ERR_MISALIGNED;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   uint8_t* vb = static_cast<uint8_t*>(values);
-  if (mask)
-    union_values_kernel<true><<<blocks_for(g.nlt), kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, scales, vb, ug,
-                                                                         static_cast<uint64_t>(payload), logical);
-  else
-    union_values_kernel<false><<<blocks_for(g.nlt), kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, scales, vb, ug,
-                                                                          static_cast<uint64_t>(payload), logical);
+  const uint64_t pl = static_cast<uint64_t>(payload);
+  const dim3 grid = blocks_for(g.nlt);
+  if (mask) {
+    if (i2)
+      union_values_kernel<true, 2><<<grid, kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, scales, vb, ug, pl, logical);
+    else
+      union_values_kernel<true, 4><<<grid, kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, scales, vb, ug, pl, logical);
+  } else if (i2) {
+    union_values_kernel<false, 2><<<grid, kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, scales, vb, ug, pl, logical);
+  } else {
+    union_values_kernel<false, 4><<<grid, kEThreads, 0, hs>>>(W, mask, bitmaps, offsets, scales, vb, ug, pl, logical);
+  }
   const uint64_t tail = values_capacity - logical;
   if (tail) {
     const uint64_t blocks = (tail + kEThreads - 1) / kEThreads;
