@@ -1,0 +1,130 @@
+"""Seeded random sweep of shapes, token counts, densities and launch options
+for every product entry point (usw_spmm, usw_union_spmm, usw_cbc_spmspv),
+bit for bit against the CPU oracle on integer-exact inputs (dyadic or
+exactly quantisable weights, small-integer activations), so that any
+summation order gives the same bits.  The cases are drawn once from fixed
+seeds, so each run tests the same ones; they cover combinations the other
+GPU tests fix one at a time: shapes that are not multiples of the launch
+tiles, token counts on both sides of every pass and kernel boundary, forced
+split factors, LT heights, area grids and row maps together."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import ie_bme as ou
+from oracle import tca_bme as ob
+from oracle import tiled_cbc as oc
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import unstructured_sparse_weight_amd as usw  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def keep_of(rng):
+    return float(rng.choice([0.0, 0.02, 1.0, rng.uniform(0.05, 0.95), rng.uniform(0.3, 0.7)]))
+
+
+def tca_cases(n=28, seed=7100):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = "i4" if i % 3 == 2 else "f16"
+        M = 64 * int(rng.integers(1, 13))
+        K = 64 * int(rng.integers(1, 41))
+        N = int(rng.choice([1, 2, 5, 16, 17, 31, 32, 33, 64, 96, 97, 130, 257, 300]))
+        if dtype == "f16" and N > 96:                  # MFMA prefill kernels: keep the oracle fast
+            M, K = min(M, 320), min(K, 1024)
+        splits = int(rng.choice([0, 0, 1, 2, 3]))
+        out.append((i, dtype, M, K, N, keep_of(rng), splits))
+    return out
+
+
+@pytest.mark.parametrize("case", tca_cases(), ids=lambda c: f"tca{c[0]}_{c[1]}_{c[2]}x{c[3]}_N{c[4]}")
+def test_random_tca_bme(case):
+    i, dtype, M, K, N, keep, splits = case
+    rng = np.random.default_rng(9000 + i)
+    mask = wl.mask_bernoulli(M, K, keep, rng)
+    W = wl.weight_dyadic(M, K, rng) if dtype == "f16" else wl.weight_int4_exact(M, K, rng, mask)
+    X = wl.activations_small_int(N, K, rng)
+    say(f"[random tca] {case}")
+    enc = usw.to_device(usw.encode_host(W, mask, (64, 64), dtype), DEV)
+    x = torch.from_numpy(X).to(DEV)
+    y = usw.spmm(enc, x, out_dtype=torch.float32, splits=splits)
+    torch.cuda.synchronize()
+    Wd = ob.dense_weight((ob.encode if dtype == "f16" else ob.encode_i4)(W, mask))
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ob.spmm_fp64(Wd, X))
+
+
+def union_cases(n=28, seed=7200):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        ltm = int(rng.choice([16, 32, 64]))
+        while True:
+            ra = int(rng.choice([r for r in (1, 2, 4, 8, 16, 32, 64) if r <= ltm]))
+            ca = int(rng.choice([1, 2, 4, 8]))
+            if (ltm // ra) * (64 // ca) % 64 == 0:
+                break
+        M = 64 * int(rng.integers(1, 9))
+        K = 64 * int(rng.integers(1, 33))
+        N = int(rng.choice([1, 2, 7, 16, 17, 32, 33, 50]))
+        out.append((i, ltm, ra, ca, bool(rng.integers(0, 2)), "i2" if i % 4 == 3 else "i4", M, K, N,
+                    keep_of(rng), int(rng.choice([0, 0, 1, 2, 5]))))
+    return out
+
+
+@pytest.mark.parametrize("case", union_cases(), ids=lambda c: f"union{c[0]}_{c[1]}x64_{c[2]}x{c[3]}_N{c[8]}")
+def test_random_union(case):
+    i, ltm, ra, ca, mapped, dtype, M, K, N, keep, splits = case
+    rng = np.random.default_rng(9100 + i)
+    mask = wl.mask_bernoulli(M, K, keep, rng)
+    W = (wl.weight_int4_exact if dtype == "i4" else wl.weight_int2_exact)(M, K, rng, mask)
+    X = wl.activations_small_int(N, K, rng)
+    vt = ob.VAL_I4 if dtype == "i4" else ob.VAL_I2
+    say(f"[random union] {case}")
+    if mapped:
+        perms = np.array([rng.permutation(ltm) for _ in range((M // ltm) * (K // 64))], dtype=np.int32)
+        h = usw.union_encode_host(W, mask, (ltm, 64), (ra, ca), dtype, perm=perms)
+        o = ou.encode_union_reordered(W, mask, perms, ltm, 64, ra, ca, vt)
+    else:
+        h = usw.union_encode_host(W, mask, (ltm, 64), (ra, ca), dtype)
+        o = ou.encode_union(W, mask, ltm, 64, ra, ca, vt)
+    enc = usw.union_to_device(h, DEV)
+    x = torch.from_numpy(X).to(DEV)
+    y = usw.union_spmm(enc, x, out_dtype=torch.float32, splits=splits)
+    torch.cuda.synchronize()
+    Yref = ob.spmm_fp64(ou.dense_weight_union(o), X)
+    assert np.array_equal(Yref, ob.spmm_fp64(np.where(mask, W, np.float16(0)), X))
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), Yref)
+
+
+def cbc_cases(n=16, seed=7300):
+    rng = np.random.default_rng(seed)
+    return [(i, 256 * int(rng.integers(1, 5)), 16 * int(rng.integers(1, 129)), keep_of(rng),
+             float(rng.choice([0.0, 1.0, 2.0, 3.0])), int(rng.choice([0, 0, 1, 3]))) for i in range(n)]
+
+
+@pytest.mark.parametrize("case", cbc_cases(), ids=lambda c: f"cbc{c[0]}_{c[1]}x{c[2]}_tau{c[4]}")
+def test_random_cbc(case):
+    i, M, K, keep, tau, splits = case
+    rng = np.random.default_rng(9200 + i)
+    W = wl.weight_dyadic(M, K, rng)
+    mask = wl.mask_bernoulli(M, K, keep, rng)
+    x = wl.activations_small_int(1, K, rng)[0]
+    say(f"[random cbc] {case}")
+    enc = usw.cbc_to_device(usw.cbc_encode_host(W, mask), DEV)
+    y = usw.cbc_spmspv(enc, torch.from_numpy(x).to(DEV), tau, out_dtype=torch.float32, splits=splits)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), oc.spmspv(oc.encode_cbc(W, mask), x, tau))
