@@ -768,6 +768,8 @@ struct Plan {
 // leave room for four workgroups per compute unit instead of five, 24%
 // slower).
 constexpr int kRingDepth = 3;
+// Fewest GroupTile columns the automatic split gives a ring workgroup.
+constexpr int64_t kRingMinCols = 10;
 
 void ring_launch(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
   if (f16out)
@@ -807,11 +809,18 @@ Plan make_plan(const usw::Geometry& g, int N, int splits_req, bool i4, bool lean
   p.nchunk = N <= 16 ? 16 : 32;
   p.ring = !i4 && lean && N <= 16;
   if (p.ring) {
-    // One round of resident workgroups, each keeping at most 63 GroupTiles;
-    // the factor is clamped to K/256 like the other decode kernel's.
+    // One round of resident workgroups, each keeping at most 63 GroupTiles
+    // and, when the matrix has few strips, at least kRingMinCols: a
+    // workgroup fills and drains its ring over the first and last steps, so
+    // shorter runs lose more to that than a full round gains (measured on
+    // MI355X: 5120x5120 at N = 16 13.5 us with 8 splits against 15.5 us with
+    // the 16 of a full round).  The factor is clamped to K/256 like the
+    // other decode kernel's.
     p.waves = 5;
     static const int resident = ring_resident();
-    int64_t s = splits_req > 0 ? splits_req : (kComputeUnits * resident) / g.Gr;
+    int64_t s = splits_req > 0 ? splits_req
+                               : std::min<int64_t>((kComputeUnits * resident) / g.Gr,
+                                                   std::max<int64_t>(1, g.Gc / kRingMinCols));
     const int64_t smax = std::max<int64_t>(1, g.Gc / 4);
     const int64_t smin = (g.Gc + 62) / 63;
     p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
