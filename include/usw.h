@@ -200,7 +200,10 @@ usw_status usw_encode_device_values(const uint16_t* W, int32_t M, int32_t K, int
  * Workspace bytes usw_spmm needs for this matrix and N (0 when none).  The
  * workspace starts with 32-bit counters (usw_spmm_counter_bytes of them,
  * one per output tile) followed by the fp32 partial sums of the workgroups
- * that share an output tile.  The counter bytes must be zero when a call starts: allocate
+ * that share an output tile; for the 512-token prefill kernel (N > 256) a
+ * copy of X in the order of its matrix-core fragments follows (N rounded up
+ * to 512, times K, fp16), written by the call itself before the product.
+ * The counter bytes must be zero when a call starts: allocate
  * the workspace zero-filled; every call leaves its counter bytes zero again.
  * A workspace last used by a call with a different counter size (another M,
  * or N on the other side of 32, or another prefill token tiling) may hold
@@ -227,8 +230,10 @@ usw_status usw_spmm_workspace(const usw_fmt* fmt, int32_t N, size_t* bytes);
  * the result is deterministic: the same inputs give the same bits.
  * Kernels: fp16 values with N <= 96 take the decode kernels, in passes of
  * up to 32 tokens (one pass for N <= 32), N > 96 the prefill (MFMA)
- * kernels; INT4 values take the INT4 decode kernel, in passes of up to 32
- * tokens, for any N.
+ * kernels (tiles of 256 tokens up to N = 256, of 512 above); INT4 values
+ * take the INT4 decode kernel, in passes of up to 32 tokens, for any N.
+ * The 512-token prefill kernel returns UNSUPPORTED when N rounded up to 512,
+ * times K, reaches 2^36.
  * The values buffer must hold the padded size usw_encode_query reports.
  * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_N, UNSUPPORTED, MISALIGNED,
  * WORKSPACE, HIP.
@@ -279,7 +284,9 @@ usw_status usw_spmm_ex(const usw_fmt* fmt, const uint16_t* X, void* Y, int32_t y
  * clears the counters it uses with a small kernel on the stream, then
  * launches the product; it never calls hipMalloc or hipFree.  splits = 0 is
  * usw_spmm's automatic factor, or 1 when that factor's partial sums do not
- * fit the array (e.g. the prefill kernel's stream-K split).
+ * fit the array (e.g. the prefill kernel's stream-K split).  With splits 0
+ * or 1, N > 256 takes the 256-token prefill kernel (no workspace at one
+ * split) when the 512-token kernel's copy of X does not fit the array.
  * Every call on one GPU shares that GPU's array: calls that may overlap in
  * time on one GPU (on different streams) race and give wrong Y; order them
  * on one stream, or use usw_spmm_ex with separate workspaces.

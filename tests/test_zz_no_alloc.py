@@ -133,3 +133,28 @@ def test_noalloc_rejects_what_does_not_fit():
     rc = L.usw_spmm_noalloc(ctypes.byref(f), x.data_ptr(), y.data_ptr(), 1, N, 16, st)
     assert rc == -7                                  # USW_ERR_WORKSPACE
     torch.cuda.synchronize()
+
+
+def test_noalloc_prefill_falls_back_to_256_token_tiles():
+    """N > 256 whose 512-token kernel needs a copy of X larger than the
+    scratch (1536 x 8192 fp16 = 24 MiB) runs on the 256-token prefill
+    kernel, which needs no workspace at one split: bit for bit on
+    integer-exact inputs, twice in a row, and within the tolerance on
+    general inputs."""
+    M, K, N = 512, 8192, 1100
+    rng = np.random.default_rng(910)
+    W = wl.weight_dyadic(M, K, rng)
+    mask = wl.mask_bernoulli(M, K, 0.5, rng)
+    X = wl.activations_small_int(N, K, rng)
+    enc = usw.to_device(usw.encode_host(W, mask), DEV)
+    assert not fits(enc, N, 1)
+    say(f"[no-alloc] prefill fallback M={M} K={K} N={N}")
+    x = torch.from_numpy(X).to(DEV)
+    Yref = ob.spmm_fp64(np.where(mask, W, np.float16(0)), X)
+    for _ in range(2):
+        y = no_alloc(enc, x, 0, 3)
+        assert np.array_equal(y.cpu().numpy().astype(np.float64), Yref)
+    enc2, x2, Yref2, Bnd2 = make(M, K, N, "f16", 911)
+    ok, rel, worst = ob.compare(no_alloc(enc2, x2, 0, 1).float().cpu().numpy().astype(np.float64), Yref2, Bnd2)
+    say(f"[no-alloc]   general inputs rel_l2={rel:.3e} worst/bound={worst:.3f}")
+    assert ok

@@ -48,17 +48,20 @@ size_t values_alloc_bytes(int32_t val_type, int64_t nnz);
 // Prefill (MFMA) kernel for fp16 values and N > 32: launch shape and split-K
 // factor, workspace size, launch.
 struct PrefillPlan {
-  int waves;    // waves per workgroup (64 tokens each)
+  int waves;    // 8: the 512-token kernel, 4: the 256-token kernel
   int ntiles;   // token tiles of 64 * waves
   int splits;   // workgroups per (strip, token tile)
   int wgs;      // > 0: stream-K over this many workgroups (512-token tiles only)
 };
-PrefillPlan prefill_plan(const Geometry& g, int N, int splits_req);
+// tiles512 = false keeps N > 256 on the 256-token kernel, which needs no
+// workspace at splits = 1 (the 512-token kernel reads a copy of X there).
+PrefillPlan prefill_plan(const Geometry& g, int N, int splits_req, bool tiles512 = true);
 size_t prefill_counter_bytes(const Geometry& g, const PrefillPlan& p);
 size_t prefill_workspace_bytes(const Geometry& g, int N, const PrefillPlan& p);
 // counters: the plan's per-tile counters (prefill_counter_bytes, zero at the
-// start of the launch); part: its partial sums (prefill_workspace_bytes
-// minus the counter bytes).  Both unused when the counter bytes are 0.
+// start of the launch); part: the rest of the workspace (prefill_workspace_bytes
+// minus the counter bytes): partial sums, then for the 512-token kernel the
+// fragment-ordered copy of X.  Unused when the workspace size is 0.
 usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X, void* Y, bool f16out, int N,
                           uint32_t* counters, float* part, const PrefillPlan& p, void* stream);
 

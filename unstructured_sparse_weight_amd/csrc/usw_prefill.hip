@@ -47,6 +47,7 @@ struct PArgs {
   const uint32_t* __restrict__ offsets;
   const uint8_t* __restrict__ values;
   const uint16_t* __restrict__ X;
+  const u32x4_t* __restrict__ xf;   // prefill_ws_kernel: X in fragment order (xfrag_kernel)
   void* __restrict__ Y;
   float* __restrict__ part;         // partial sums: [splits][N][M], or slots of 512 x 64 (prefill_ws_kernel)
   uint32_t* __restrict__ counters;  // per (strip, token tile): workgroups done; kept at 0 between calls
@@ -55,6 +56,7 @@ struct PArgs {
   int tiles;                        // strips x token tiles
   int wgs;                          // prefill_ws_kernel: > 0 stream-K over this many workgroups
   int remap;                        // 1: keep consecutive tiles (and a tile's splits) on one XCD
+  int kb32;                         // K / 32
 };
 
 template <int WAVES>
@@ -333,35 +335,63 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_kernel(PArgs a)
   if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The same for a wave-uniform count n in [8, 12]; any other count waits as
-// for 8 (never for fewer loads than asked).
-__device__ __forceinline__ void producer_barrier(int n) {
+// Builder-side barrier: wait until at most n (wave-uniform, 0..4) of this
+// wave's LDS-DMA loads are in flight, then a workgroup barrier; a larger n
+// waits as for 4 (never for fewer loads than asked).
+__device__ __forceinline__ void builder_barrier(int n) {
   switch (__builtin_amdgcn_readfirstlane(n)) {
-    case 9: USW_PRODUCER_BARRIER(9); break;
-    case 10: USW_PRODUCER_BARRIER(10); break;
-    case 11: USW_PRODUCER_BARRIER(11); break;
-    case 12: USW_PRODUCER_BARRIER(12); break;
-    default: USW_PRODUCER_BARRIER(8); break;
+    case 0: USW_PRODUCER_BARRIER(0); break;
+    case 1: USW_PRODUCER_BARRIER(1); break;
+    case 2: USW_PRODUCER_BARRIER(2); break;
+    case 3: USW_PRODUCER_BARRIER(3); break;
+    default: USW_PRODUCER_BARRIER(4); break;
   }
 }
 
+// X in the order of the MFMA B fragments of prefill_ws_kernel, written once
+// per call before it: the 16-byte unit u = ((nt * K/32 + j) * 32 + tb) * 64 + l
+// holds X[n][k0 .. k0 + 7] with n = 512 nt + 16 tb + (l % 16) and
+// k0 = 32 j + 8 (l / 16) -- lane l's register of fragment tb of k-block j --
+// or zeros for n >= N.  A wave's eight fragments of one half GroupTile column
+// are then 8 KB in a row, and a 512-token tile's X for that half column 32 KB.
+// A thread writes the units of k-blocks 2jj and 2jj + 1 of one lane slot (its
+// two reads lie in one 128-byte line of X); 32-bit index arithmetic (the host
+// keeps the unit count below 2^31).
+__global__ __launch_bounds__(256) void xfrag_kernel(const uint16_t* __restrict__ X, u32x4_t* __restrict__ xf, int N,
+                                                    int K, uint32_t pairs) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  if (t >= pairs) return;
+  const uint32_t l = t & 63u, tb = (t >> 6) & 31u;
+  const uint32_t blk = t >> 11;             // nt * K/64 + jj
+  const uint32_t kp = static_cast<uint32_t>(K) / 64u;
+  const uint32_t nt = blk / kp, jj = blk - nt * kp;
+  const uint32_t n = 512u * nt + 16u * tb + (l & 15u);
+  u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+  if (n < static_cast<uint32_t>(N)) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(X + static_cast<size_t>(n) * K + 64u * jj + 8u * (l >> 4));
+    v0 = src[0];
+    v1 = src[4];
+  }
+  const size_t u0 = ((static_cast<size_t>(nt) * (2u * kp) + 2u * jj) * 32u + tb) * 64u + l;
+  xf[u0] = v0;
+  xf[u0 + 32 * 64] = v1;
+}
+
 // Warp-specialised variant for N > 256: a tile is 64 rows (one GroupTile
-// strip) by 512 tokens, and twelve waves in three roles pass the same
-// barriers, one per half GroupTile column (32 k).
-//  - Waves 0-3 (consumers) only multiply: each owns 128 tokens (64 rows x
-//    128 tokens of fp32 accumulators) and per half column reads 4 A and 8
-//    X^T fragments from LDS for 32 MFMAs.
-//  - Waves 4-7 (loaders) bring the operands into LDS with
-//    global_load_lds_dwordx4 (no register round trip): the X tile in
-//    32-column halves, three buffers deep, one half a phase ahead of its
-//    use, and the values and bitmap words of a GroupTile two columns ahead.
-//    Before each barrier a loader waits until the loads the next phase
-//    reads have landed (s_waitcnt vmcnt).
-//  - Waves 8-11 (builders) rebuild the A tile of the next column, two
-//    fragments each, from the staged values.
-// A loader spends most of its time waiting for the address unit to accept
-// its loads, a builder for LDS round trips; in separate waves the two
-// overlap.
+// strip) by 512 tokens, and eight waves in two roles pass the same barriers,
+// one per GroupTile column.
+//  - Waves 0-3 (consumers) multiply: each owns 128 tokens (64 rows x 128
+//    tokens of fp32 accumulators) and per half column reads 4 A fragments
+//    from LDS and 8 X^T fragments straight from the fragment-ordered copy of
+//    X (xfrag_kernel) into registers, a half column ahead, for 32 MFMAs.
+//    X never passes through LDS: every 64-row strip re-reads the whole X
+//    tile, and staging it in LDS made LDS the bound.
+//  - Waves 4-7 (builders) rebuild the A tile of the next column (two
+//    fragments each) from the staged values, and bring the values and
+//    bitmap words of a GroupTile three columns ahead into LDS with
+//    global_load_lds_dwordx4 (no register round trip).  Before each barrier
+//    a builder waits until the loads that the next column's rebuild reads
+//    have landed (s_waitcnt vmcnt).
 //
 // Work split.  The (tile, GroupTile column) units are numbered tile-major.
 // With a.wgs > 0 (stream-K) every compute unit gets the same number of
@@ -372,34 +402,29 @@ __device__ __forceinline__ void producer_barrier(int n) {
 // L % splits of tile L / splits.  A workgroup first runs the pieces of its
 // range (one per tile it touches) from the last to the first -- the
 // workgroups that share a tile then start its columns at both ends at once,
-// so that at any moment they all stream nearly the same few X columns, and
-// the partial sums are added while whole tiles still run -- then its whole
-// tiles.  A piece that covers its whole tile stores Y; otherwise it stores
-// fp32 partial sums in a slot of its own, and the workgroup that completes
-// the tile's count adds the tile's slots in a fixed order (that of the
-// ranges), so results do not depend on timing.
+// and the partial sums are added while whole tiles still run -- then its
+// whole tiles.  A piece that covers its whole tile stores Y; otherwise it
+// stores fp32 partial sums in a slot of its own, and the workgroup that
+// completes the tile's count adds the tile's slots in a fixed order (that of
+// the ranges), so results do not depend on timing.
 template <bool OUT_F16>
-__global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
+__global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PArgs a) {
   constexpr int kBN = 512;
-  constexpr int kThreads = 768;
-  constexpr int kPThreads = 256;                                      // loader threads
-  constexpr int kCpt = (kStageChunks + kPThreads - 1) / kPThreads;   // value chunks per loader thread
+  constexpr int kThreads = 512;
+  constexpr int kPThreads = 256;                                      // builder threads
+  constexpr int kCpt = (kStageChunks + kPThreads - 1) / kPThreads;   // value chunks per builder thread
   constexpr int kStageBytes = kPThreads * kCpt * 16 + 16;
   constexpr int kSlot = kBN * kGT;                                    // floats per partial-sum slot
+  static_assert(kCpt + 1 <= 4, "builder_barrier counts at most 4 loads per column");
 
   __shared__ __attribute__((aligned(16))) uint8_t stage[3][kStageBytes];   // values of columns c .. c+2 (by c % 3)
   __shared__ __attribute__((aligned(16))) u32x4_t abuf[2][8 * 64];
-  // X tile halves: xs[b][4n + (q ^ ((n >> 2) & 3))] holds the 16-byte chunk q
-  // (k = 32h + 8q .. +7) of token n of the tile; a fragment read (16 tokens,
-  // one chunk) covers 16 distinct bank groups.
-  __shared__ __attribute__((aligned(16))) u32x4_t xs[3][kBN * 4];
   __shared__ __attribute__((aligned(16))) uint32_t lut[32];
   __shared__ __attribute__((aligned(16))) u32x2_t bmw[3][64];   // their bitmap words
   __shared__ uint32_t offtab[kMaxCols + 1];
   __shared__ uint32_t last_flag;
   USW_LDS_POISON(stage);
   USW_LDS_POISON(abuf);
-  USW_LDS_POISON(xs);
   USW_LDS_POISON(bmw);
 
   const int tid = threadIdx.x;
@@ -437,7 +462,6 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
     reinterpret_cast<u32x2_t*>(lut)[tid] = e;
   }
 
-  auto xslot = [](int n, int q) { return 4 * n + (q ^ ((n >> 2) & 3)); };
 
   auto store_y4 = [&](int n, int m, f32x4_t v) {
     const size_t yi = static_cast<size_t>(n) * a.M + m;
@@ -456,7 +480,7 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
 
   // One piece: columns [c_begin, c_end) of one tile.
   struct Piece {
-    int tile, c_begin, c_end, c_last, cnt, m0, n_base, slot;
+    int tile, c_begin, c_end, cnt, m0, n_base, slot;
     int64_t t0, g_row;
     bool full;
   };
@@ -541,7 +565,6 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
     pc.m0 = gi * kGT;
     pc.n_base = (tile - gi * a.ntiles) * kBN;
     pc.cnt = c_end - c_begin;           // >= 1
-    pc.c_last = c_end - 1;
     pc.g_row = static_cast<int64_t>(gi) * a.Gc;
 
     const uint32_t* otab = a.offsets + pc.g_row + c_begin;
@@ -583,36 +606,42 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      __syncthreads();   // loaders: X halves 0, 1 and three columns' values landed
-      __syncthreads();   // builders: first column's A tile rebuilt
-      for (int c = pc.c_begin; c < pc.c_end; ++c) {
+      // This wave's 8 X^T fragments of half column h of column c: lane l of
+      // fragment nb holds token nl + 16 nb + l % 16, k 64 c + 32 h + 8 (l / 16) .. +7.
+      const u32x4_t* xw = a.xf + (static_cast<size_t>(pc.n_base / kBN) * a.kb32 * 32 + 8 * w) * 64 + lane;
+      auto xload = [&](int c, int h, u32x4_t* d) {
+        const u32x4_t* src = xw + static_cast<size_t>(2 * c + h) * (32 * 64);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4_t* xb = xs[(2 * (c - pc.c_begin) + h) % 3];
-          u32x4_t af[4];
+        for (int nb = 0; nb < 8; ++nb) d[nb] = src[64 * nb];
+      };
+      auto mma = [&](int c, int h, const u32x4_t* bf) {
+        u32x4_t af[4];
 #pragma unroll
-          for (int rs = 0; rs < 4; ++rs) af[rs] = abuf[c & 1][(rs * 2 + h) * 64 + lane];
-          u32x4_t bf[8];
+        for (int rs = 0; rs < 4; ++rs) af[rs] = abuf[c & 1][(rs * 2 + h) * 64 + lane];
 #pragma unroll
-          for (int nb = 0; nb < 8; ++nb) bf[nb] = xb[xslot(nl + 16 * nb + row, kb)];
+        for (int rs = 0; rs < 4; ++rs)
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-            for (int rs = 0; rs < 4; ++rs)
-              acc[rs][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, af[rs]),
-                                                                   __builtin_bit_cast(half8_t, bf[nb]), acc[rs][nb], 0,
-                                                                   0, 0);
-          // Schedule: the 4 A reads and the first 2 X^T reads, then for each
-          // X^T fragment its 4 MFMAs followed by the read 2 fragments ahead,
-          // so that two LDS reads are always in flight behind the MFMAs.
-          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-          for (int nb = 0; nb < 8; ++nb) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            if (nb + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __syncthreads();
-        }
+            acc[rs][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, af[rs]),
+                                                                 __builtin_bit_cast(half8_t, bf[nb]), acc[rs][nb], 0,
+                                                                 0, 0);
+      };
+      // Two register sets, each loaded a half column before its use; the
+      // scheduling barriers keep the compiler from sinking the loads to
+      // their use.
+      u32x4_t xa[8], xb[8];
+      xload(pc.c_begin, 0, xa);
+      __syncthreads();   // builders: first three columns' values and bitmap words landed
+      __syncthreads();   // builders: first column's A tile rebuilt
+      for (int c = pc.c_begin; c < pc.c_end; ++c) {
+        xload(c, 1, xb);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(c, 0, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 1 < pc.c_end) xload(c + 1, 0, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(c, 1, xb);
+        __syncthreads();   // builders: column c+1's A tile rebuilt; abuf[c & 1] free
       }
       // lane l of block (rs, nb): rows 16rs + 4(l/16) + i, token 16nb + l%16.
       if (pc.full) {
@@ -637,12 +666,15 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
                                                    ((rs * 8 + nb) * 64 + lane) * 16, 0, kCacheSc1);
       }
     });
-  } else if (w < 8) {
-    // ---------------- loader ----------------
+  } else {
+    // ---------------- builder ----------------
     for_pieces([&](const Piece& pc) {
-      const int dw = w - 4;               // X of tokens 128dw .. +127; value chunk slots 64dw + 256i + lane
+      const int bw = w - 4;               // A fragments 2bw, 2bw+1: rows 16bw .. +15; value chunk slots 64bw + 256i + lane
       const uint64_t top = a.values_alloc - 16;
-      // Values of column c into stage[c % 3]: slot 64dw + lane + 256i of
+      const int r8 = row & 7;
+      const int bt_lane = 4 * (kb >> 1) + 2 * (row >> 3) + (kb & 1);
+      const uint64_t rowmask = (1ull << (8 * r8)) - 1ull;
+      // Values of column c into stage[c % 3]: slot 64bw + lane + 256i of
       // the buffer takes chunk slot of the GroupTile's range; an instruction
       // whose 64 slots all lie past the range is not issued.  Returns how
       // many were.
@@ -652,11 +684,11 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
         const uint32_t nch = __builtin_amdgcn_readfirstlane(
             min(chunk_count<false>(o1, a0), static_cast<uint32_t>((top - a0) >> 4) + 1u));
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.values + a0);
-        const uint32_t dst = lds_addr(stage[c % 3]) + 16 * 64 * dw;
+        const uint32_t dst = lds_addr(stage[c % 3]) + 16 * 64 * bw;
         int issued = 0;
 #pragma unroll
         for (int i = 0; i < kCpt; ++i) {
-          const uint32_t slot0 = static_cast<uint32_t>(64 * dw + kPThreads * i);
+          const uint32_t slot0 = static_cast<uint32_t>(64 * bw + kPThreads * i);
           if (slot0 < nch) {
             lds_dma16(src + min(slot0 + lane, nch - 1), dst + 16 * kPThreads * i);
             ++issued;
@@ -664,68 +696,13 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
         }
         return issued;
       };
-      // The 64 bitmap words of column c into bmw[c % 3] (loader 0, lanes
+      // The 64 bitmap words of column c into bmw[c % 3] (builder 0, lanes
       // 0-31, two words each).  Returns how many loads this wave issued.
       auto dma_bm = [&](int c) {
-        if (dw != 0) return 0;
+        if (bw != 0) return 0;
         if (lane < 32) lds_dma16(a.bitmaps + (pc.g_row + c) * kBtPerGt + 2 * lane, lds_addr(bmw[c % 3]));
         return 1;
       };
-      // X half j (counted from the first column: column pc.c_begin + j/2, k
-      // half j%2) for this wave's 128 tokens into xs[j % 3]: instruction i
-      // fills the 1 KB of slots of tokens 128dw + 16i .. +15, lane l the
-      // slot 4(128dw + 16i) + l, i.e. token n = 128dw + 16i + l/4, chunk
-      // q = (l & 3) ^ ((n >> 2) & 3).
-      auto dma_x = [&](int j) {
-        const int cc = min(pc.c_begin + (j >> 1), pc.c_last);
-        const uint32_t dst = lds_addr(xs[j % 3]) + 16 * 4 * 128 * dw;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int nloc = 128 * dw + 16 * i + (lane >> 2);
-          const int q = (lane & 3) ^ ((nloc >> 2) & 3);
-          const int n = min(pc.n_base + nloc, a.N - 1);
-          lds_dma16(a.X + static_cast<size_t>(n) * a.K + cc * kGT + (j & 1) * 32 + q * 8, dst + 1024 * i);
-        }
-      };
-
-      dma_x(0);
-      dma_x(1);
-      for (int c = pc.c_begin; c < min(pc.c_begin + 3, pc.c_end); ++c) {
-        dma_bm(c);
-        dma_v(c);
-      }
-      USW_PRODUCER_BARRIER(0);
-      USW_PRODUCER_BARRIER(0);   // builders: first column's A tile rebuilt
-
-      // Phase t = 2 (c - pc.c_begin) + h: consumers read X half t from
-      // xs[t % 3].  First phase of column c: X half t+2 into xs[(t+2) % 3]
-      // (read in phase t-1); at the barrier everything older has landed: X
-      // half t+1 and column c+2's values and bitmap words.  Second phase: X
-      // half t+3, then the bitmap words and values of column c+3 into
-      // bmw[c % 3] and stage[c % 3] (read for column c in the column
-      // before); at the barrier X half t+2 has landed.
-      for (int c = pc.c_begin; c < pc.c_end; ++c) {
-        const int t = 2 * (c - pc.c_begin);
-        dma_x(t + 2);
-        USW_PRODUCER_BARRIER(8);
-        dma_x(t + 3);
-        int n = 8;
-        if (c + 3 < pc.c_end) {
-          n += dma_bm(c + 3);
-          n += dma_v(c + 3);
-        }
-        producer_barrier(n);
-      }
-      __builtin_amdgcn_s_waitcnt(0);   // no LDS write of this wave outlives the piece
-    });
-  } else {
-    // ---------------- builder ----------------
-    for_pieces([&](const Piece& pc) {
-      const int bw = w - 8;               // A fragments 2bw, 2bw+1: rows 16bw .. +15, k halves 0 and 1
-      const uint64_t top = a.values_alloc - 16;
-      const int r8 = row & 7;
-      const int bt_lane = 4 * (kb >> 1) + 2 * (row >> 3) + (kb & 1);
-      const uint64_t rowmask = (1ull << (8 * r8)) - 1ull;
       // Rebuild inputs of column c for this wave's two fragments: for the
       // BitmapTile row a lane rebuilds, the bitmap and the element index of
       // the tile's first value inside the staged chunk range.
@@ -746,30 +723,38 @@ __global__ __launch_bounds__(768, 1) void prefill_ws_kernel(PArgs a) {
         }
         return in;
       };
-      auto rebuild = [&](int c, int j, const RbIn<2>& in) {
-        const int f = 2 * bw + j;
-        const uint64_t bm = (static_cast<uint64_t>(in.hi[j]) << 32) | in.lo[j];
-        const uint32_t rb = in.base[j] + __popcll(bm & rowmask);
-        const uint32_t byte = static_cast<uint32_t>(bm >> (8 * r8)) & 0xFFu;
-        abuf[c & 1][f * 64 + lane] = __builtin_bit_cast(u32x4_t, rebuild_row<false>(stage[c % 3], lut, rb, byte));
+      auto rebuild = [&](int c, const RbIn<2>& in) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int f = 2 * bw + j;
+          const uint64_t bm = (static_cast<uint64_t>(in.hi[j]) << 32) | in.lo[j];
+          const uint32_t rb = in.base[j] + __popcll(bm & rowmask);
+          const uint32_t byte = static_cast<uint32_t>(bm >> (8 * r8)) & 0xFFu;
+          abuf[c & 1][f * 64 + lane] = __builtin_bit_cast(u32x4_t, rebuild_row<false>(stage[c % 3], lut, rb, byte));
+        }
       };
 
-      __syncthreads();   // loaders: first three columns' values and bitmap words landed
-      RbIn<2> rin = prep(pc.c_begin);
-      rebuild(pc.c_begin, 0, rin);
-      rebuild(pc.c_begin, 1, rin);
-      __syncthreads();
-      // Column c: rebuild column c+1 (staged two columns before), one
-      // fragment per phase.
-      for (int c = pc.c_begin; c < pc.c_end; ++c) {
-        if (c + 1 < pc.c_end) {
-          rin = prep(c + 1);
-          rebuild(c + 1, 0, rin);
-        }
-        __syncthreads();
-        if (c + 1 < pc.c_end) rebuild(c + 1, 1, rin);
-        __syncthreads();
+      for (int c = pc.c_begin; c < min(pc.c_begin + 3, pc.c_end); ++c) {
+        dma_bm(c);
+        dma_v(c);
       }
+      USW_PRODUCER_BARRIER(0);   // first three columns' values and bitmap words landed
+      rebuild(pc.c_begin, prep(pc.c_begin));
+      __syncthreads();
+      // Column c: rebuild column c+1 (staged at least a column before), then
+      // stage column c+3 into the buffers column c used.  At the barrier
+      // everything but those loads has landed: column c+2's values and
+      // bitmap words, which the next column's rebuild reads.
+      for (int c = pc.c_begin; c < pc.c_end; ++c) {
+        if (c + 1 < pc.c_end) rebuild(c + 1, prep(c + 1));
+        int n = 0;
+        if (c + 3 < pc.c_end) {
+          n += dma_bm(c + 3);
+          n += dma_v(c + 3);
+        }
+        builder_barrier(n);
+      }
+      __builtin_amdgcn_s_waitcnt(0);   // no LDS write of this wave outlives the piece
     });
   }
 }
@@ -783,9 +768,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 namespace usw {
 
-PrefillPlan prefill_plan(const Geometry& g, int N, int splits_req) {
+PrefillPlan prefill_plan(const Geometry& g, int N, int splits_req, bool tiles512) {
   PrefillPlan p;
-  p.waves = N > 256 ? 8 : 4;
+  p.waves = (N > 256 && tiles512) ? 8 : 4;
   const int bn = 64 * p.waves;
   p.ntiles = (N + bn - 1) / bn;
   p.wgs = 0;
@@ -816,15 +801,23 @@ static bool uses_slots(const PrefillPlan& p) { return p.waves == 8 && (p.wgs > 0
 size_t prefill_counter_bytes(const Geometry& g, const PrefillPlan& p) {
   return (p.splits > 1 || p.wgs > 0) ? align256(static_cast<size_t>(4) * g.Gr * p.ntiles) : 0;
 }
+// Slot bytes of the 512-token kernel's split tiles (0 without them): slots
+// of 512 tokens x 64 rows, two per stream-K workgroup (the pieces that open
+// and close its range), one per split-K workgroup.
+static size_t slot_bytes(const Geometry& g, const PrefillPlan& p) {
+  if (!uses_slots(p)) return 0;
+  const size_t slots = p.wgs > 0 ? static_cast<size_t>(2) * p.wgs : static_cast<size_t>(g.Gr) * p.ntiles * p.splits;
+  return align256(slots * 512 * kGT * sizeof(float));
+}
+// Bytes of the fragment-ordered copy of X the 512-token kernel reads (0 for
+// the 256-token kernel).
+static size_t xfrag_bytes(const Geometry& g, const PrefillPlan& p) {
+  return p.waves == 8 ? align256(static_cast<size_t>(p.ntiles) * 512 * g.K * sizeof(uint16_t)) : 0;
+}
 size_t prefill_workspace_bytes(const Geometry& g, int N, const PrefillPlan& p) {
   const size_t cb = prefill_counter_bytes(g, p);
+  if (p.waves == 8) return cb + slot_bytes(g, p) + xfrag_bytes(g, p);
   if (cb == 0) return 0;
-  if (uses_slots(p)) {
-    // Partial-sum slots of 512 tokens x 64 rows: two per stream-K workgroup
-    // (the pieces that open and close its range), one per split-K workgroup.
-    const size_t slots = p.wgs > 0 ? static_cast<size_t>(2) * p.wgs : static_cast<size_t>(g.Gr) * p.ntiles * p.splits;
-    return cb + slots * 512 * kGT * sizeof(float);
-  }
   return cb + static_cast<size_t>(p.splits) * N * g.M * sizeof(float);
 }
 usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X, void* Y, bool f16out, int N,
@@ -838,6 +831,9 @@ usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X
   const bool shared = prefill_counter_bytes(g, p) > 0;
   a.counters = shared ? counters : nullptr;
   a.part = shared ? part : nullptr;
+  // Workspace after the counters: the slots, then the copy of X.
+  a.xf = p.waves == 8 ? reinterpret_cast<const u32x4_t*>(reinterpret_cast<uint8_t*>(part) + slot_bytes(g, p)) : nullptr;
+  a.kb32 = static_cast<int>(g.K / 32);
   a.values_alloc = values_alloc_bytes(f->val_type, f->nnz);
   a.M = static_cast<int>(g.M);
   a.K = static_cast<int>(g.K);
@@ -852,8 +848,12 @@ usw_status prefill_launch(const usw_fmt* f, const Geometry& g, const uint16_t* X
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(nblk));
   if (p.waves == 8) {
-    if (f16out) prefill_ws_kernel<true><<<grid, 768, 0, s>>>(a);
-    else prefill_ws_kernel<false><<<grid, 768, 0, s>>>(a);
+    const int64_t pairs = static_cast<int64_t>(p.ntiles) * (a.kb32 / 2) * 32 * 64;
+    if (pairs >= (int64_t(1) << 31)) return USW_ERR_UNSUPPORTED;
+    xfrag_kernel<<<dim3(static_cast<unsigned>((pairs + 255) / 256)), 256, 0, s>>>(
+        X, const_cast<u32x4_t*>(a.xf), N, a.K, static_cast<uint32_t>(pairs));
+    if (f16out) prefill_ws_kernel<true><<<grid, 512, 0, s>>>(a);
+    else prefill_ws_kernel<false><<<grid, 512, 0, s>>>(a);
   } else {
     if (f16out) prefill_kernel<4, true><<<grid, 256, 0, s>>>(a);
     else prefill_kernel<4, false><<<grid, 256, 0, s>>>(a);

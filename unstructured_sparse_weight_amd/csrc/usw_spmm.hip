@@ -909,11 +909,11 @@ struct CallPlan {
   size_t cb;             // leading counter bytes of the workspace
 };
 
-CallPlan make_call_plan(const usw_fmt* f, const usw::Geometry& g, int32_t N, int splits_req) {
+CallPlan make_call_plan(const usw_fmt* f, const usw::Geometry& g, int32_t N, int splits_req, bool tiles512 = true) {
   CallPlan c{};
   c.prefill = use_prefill(f, N);
   if (c.prefill) {
-    c.pp = usw::prefill_plan(g, N, splits_req);
+    c.pp = usw::prefill_plan(g, N, splits_req, tiles512);
     c.need = usw::prefill_workspace_bytes(g, N, c.pp);
     c.cb = usw::prefill_counter_bytes(g, c.pp);
   } else {
@@ -1038,8 +1038,11 @@ usw_status spmm_noalloc_impl(const usw_fmt* f, const uint16_t* X, void* Y, int32
     return c.cb <= kScratchCounterBytes && c.need - c.cb <= kScratchBytes - kScratchCounterBytes;
   };
   CallPlan c = make_call_plan(f, g, N, splits < 0 ? 0 : splits);
-  // The automatic factor falls back to 1 when its partial sums do not fit.
+  // The automatic factor falls back to 1 when its partial sums do not fit,
+  // and N > 256 to the 256-token prefill kernel when the 512-token kernel's
+  // copy of X does not.
   if (splits <= 0 && !fits(c)) c = make_call_plan(f, g, N, 1);
+  if (splits <= 1 && c.prefill && !fits(c)) c = make_call_plan(f, g, N, 1, false);
   if (!fits(c)) return USW_ERR_WORKSPACE;
   uint8_t* base = nullptr;
   if (c.need > 0) {
