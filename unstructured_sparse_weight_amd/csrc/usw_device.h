@@ -177,10 +177,10 @@ __device__ __forceinline__ uint32_t nibble_selector(uint32_t q, int j) {
 // v_perm selectors that expand the packed nibbles of an 8-nibble window into
 // the 8 slots of a BitmapTile row with mask byte b: slot p takes nibble
 // k = (set bits of b below p) when bit p is set, else zero.  Nibble k sits in
-// byte k/2 of lo4 (k even) or of hi4 (k odd), lo4 = w & 0x0F0F0F0F and
-// hi4 = (w >> 4) & 0x0F0F0F0F, and v_perm(hi4, lo4, sel) numbers lo4's bytes
-// 0-3 and hi4's bytes 4-7.  .x serves slots 0-3, .y slots 4-7; a table of
-// all 256 mask bytes lives in LDS.
+// byte k/2 of lo4 (k even) or of hi4 (k odd), as lds_window_i4 splits a
+// window, and v_perm(hi4, lo4, sel) numbers lo4's bytes 0-3 and hi4's bytes
+// 4-7.  .x serves slots 0-3, .y slots 4-7; a table of all 256 mask bytes
+// lives in LDS.
 __device__ __forceinline__ u32x2_t row_byte_selectors(uint32_t b) {
   u32x2_t sel = {0u, 0u};
   for (int p = 0; p < 8; ++p) {
@@ -211,15 +211,16 @@ __device__ __forceinline__ u32x2_t lds_window_f16(const uint8_t* buf, uint32_t e
 }
 
 // 8 packed nibbles starting at nibble e of an LDS buffer, split into the
-// even (lo4) and odd (hi4) nibbles, one per byte.  v_alignbit uses only the
-// low five bits of its shift operand, here 4 * (e mod 8).
+// even (lo4) and odd (hi4) nibbles, one per byte, each in the upper half of
+// its byte.  v_alignbit uses only the low five bits of its shift operand,
+// here 4 * (e mod 8).
 __device__ __forceinline__ u32x2_t lds_window_i4(const uint8_t* buf, uint32_t e) {
   const uint32_t ba = e >> 1;
   const uint32_t* p = reinterpret_cast<const uint32_t*>(buf + (ba & ~3u));
   const uint32_t win = __builtin_amdgcn_alignbit(p[1], p[0], e << 2);
   u32x2_t r;
-  r.x = win & 0x0F0F0F0Fu;
-  r.y = (win >> 4) & 0x0F0F0F0Fu;
+  r.x = (win << 4) & 0xF0F0F0F0u;
+  r.y = win & 0xF0F0F0F0u;
   return r;
 }
 
@@ -238,28 +239,85 @@ __device__ __forceinline__ u32x2_t lds_window_i2(const uint8_t* buf, uint32_t e)
   const uint32_t sgn = t & 0x22222222u;
   t |= (sgn << 1) | (sgn << 2);
   u32x2_t r;
-  r.x = t & 0x0F0F0F0Fu;
-  r.y = (t >> 4) & 0x0F0F0F0Fu;
+  r.x = (t << 4) & 0xF0F0F0F0u;
+  r.y = t & 0xF0F0F0F0u;
   return r;
 }
 
-// The 8 fp16 slots of an INT4 row from its 8-nibble window (split into
-// lo4 / hi4 by lds_window_i4) and its selectors.
+// Offset of the code rows expand_row_i4 returns: a slot holds code + 72.
+constexpr float kCodeBias = 72.0f;
+
+// The 8 fp16 slots of a code row, each holding its code plus kCodeBias
+// (empty slots kCodeBias), from its 8-nibble window (split into lo4 / hi4,
+// nibbles in the upper half of each byte, by lds_window_i4 / _i2) and its
+// selectors.  The offset keeps the expansion to byte permutes: the kernels
+// take it out with code_bias_mma, once per X^T fragment.
 __device__ __forceinline__ half8_t expand_row_i4(u32x2_t w8, u32x2_t sel) {
-  // Slots as bytes; xor 8 maps the two's-complement nibble q to q + 8 in
-  // [0, 15] (an empty slot's 0 becomes 8, i.e. q = 0).
-  const uint32_t e0 = __builtin_amdgcn_perm(w8.y, w8.x, sel.x) ^ 0x08080808u;
-  const uint32_t e1 = __builtin_amdgcn_perm(w8.y, w8.x, sel.y) ^ 0x08080808u;
-  // fp16 bit pattern 0x6400 | u is 1024 + u exactly; subtracting 1032
-  // leaves q exactly.
+  // Slots as bytes, the nibble in the upper half; xor 0x80 maps the
+  // two's-complement nibble q to u = q + 8 in [0, 15] (an empty slot's 0
+  // becomes 8, i.e. q = 0).
+  const uint32_t e0 = __builtin_amdgcn_perm(w8.y, w8.x, sel.x) ^ 0x80808080u;
+  const uint32_t e1 = __builtin_amdgcn_perm(w8.y, w8.x, sel.y) ^ 0x80808080u;
+  // fp16 bit pattern 0x5400 | (u << 4) is 64 (1 + u / 64) = 64 + u exactly,
+  // i.e. q + 72.
   u32x4_t a;
-  a.x = __builtin_amdgcn_perm(0x64646464u, e0, 0x04010400u);
-  a.y = __builtin_amdgcn_perm(0x64646464u, e0, 0x04030402u);
-  a.z = __builtin_amdgcn_perm(0x64646464u, e1, 0x04010400u);
-  a.w = __builtin_amdgcn_perm(0x64646464u, e1, 0x04030402u);
-  half8_t h = __builtin_bit_cast(half8_t, a);
-  h += static_cast<_Float16>(-1032.0f);
-  return h;
+  a.x = __builtin_amdgcn_perm(0x54545454u, e0, 0x04010400u);
+  a.y = __builtin_amdgcn_perm(0x54545454u, e0, 0x04030402u);
+  a.z = __builtin_amdgcn_perm(0x54545454u, e1, 0x04010400u);
+  a.w = __builtin_amdgcn_perm(0x54545454u, e1, 0x04030402u);
+  return __builtin_bit_cast(half8_t, a);
+}
+
+// Takes the expansion's offset out of a tile: every slot of a rebuilt
+// fragment carries kCodeBias, so fragment A times X^T fragment x exceeds the
+// true product by kCodeBias times x's column sums, the same for every row.
+// corr[nb] collects -kCodeBias times those sums; code_bias_finish puts them
+// in the accumulator layout, and the kernel adds them to every row block's
+// accumulators before the reduction.  With one token block the sums come
+// from one MFMA with a constant A per X^T fragment (the matrix cores are
+// mostly idle in decode); with two, from v_dot2 on the vector ALUs (the
+// MFMA form measured slower there), each lane summing its 8 k of its token
+// in corr[nb].x.  With integer-valued inputs every product and partial sum
+// is an integer, exact while its magnitude stays below 2^24.
+template <int NB>
+__device__ __forceinline__ void code_bias_mma(f32x4_t (&corr)[NB], const u32x4_t (&x)[2][NB]) {
+  const _Float16 m = static_cast<_Float16>(-kCodeBias);
+  if constexpr (NB == 1) {
+    const half8_t neg = {m, m, m, m, m, m, m, m};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      corr[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg, __builtin_bit_cast(half8_t, x[ks][0]), corr[0], 0, 0, 0);
+  } else {
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    const half2_t neg2 = {m, m};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          // Through a scalar: bit-casting the vector element itself made
+          // the compiler take element 0 for every d.
+          const uint32_t pair = x[ks][nb][d];
+          corr[nb].x = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pair), neg2, corr[nb].x, false);
+        }
+  }
+}
+
+// The collected corrections in the MFMA D layout (lane l: token l % 16 of
+// its block, four rows): with v_dot2 the four lanes of a token (l % 16
+// equal) add their partial sums.
+template <int NB>
+__device__ __forceinline__ void code_bias_finish(f32x4_t (&corr)[NB]) {
+  if constexpr (NB > 1) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float t = corr[nb].x;
+      t += __shfl_xor(t, 16);
+      t += __shfl_xor(t, 32);
+      corr[nb] = f32x4_t{t, t, t, t};
+    }
+  }
 }
 
 // The 8 dense fp16 slots (one BitmapTile row) of a lane's A fragment: the

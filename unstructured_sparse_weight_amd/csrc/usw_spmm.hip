@@ -192,10 +192,14 @@ __device__ __forceinline__ uint32_t bitmap_prefix_reg(u32x2_t bm) {
 
 // Rebuild and multiply fragments f = F0 .. F1-1 (both ks) of a GroupTile
 // whose bitmap table is at tab and whose values are in the LDS staging area
-// starting at vals.
+// starting at vals.  INT4 rows carry the expansion's offset: corr collects
+// its correction (code_bias_mma, all four fragments of a GroupTile at once).
 template <int NB, bool I4, int F0 = 0, int F1 = 4>
 __device__ __forceinline__ void tile_mma(const u32x4_t (&x)[2][NB], const uint8_t* vals, const uint8_t* tab,
-                                         const uint32_t* lut, f32x4_t (&acc)[4][NB], const LaneMap& lm) {
+                                         const uint32_t* lut, f32x4_t (&acc)[4][NB], f32x4_t (&corr)[NB],
+                                         const LaneMap& lm) {
+  static_assert(!I4 || (F0 == 0 && F1 == 4), "the INT4 correction covers whole GroupTiles");
+  if constexpr (I4) code_bias_mma<NB>(corr, x);
   u32x2_t e[F1 - F0][2];
 #pragma unroll
   for (int f = F0; f < F1; ++f)
@@ -283,6 +287,9 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t corr[NB];   // INT4: the expansion offset's correction, same for every row
+#pragma unroll
+  for (int j = 0; j < NB; ++j) corr[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   uint8_t* vb = smem + w * VT::kVbuf;
   uint8_t* tab = smem + kW * VT::kVbuf + w * kTabBytes;
@@ -337,9 +344,9 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
           tab_write(tab, s0.bm, excl - (h ? mid : 0u) + delta + vb_elems, lane);
           wave_sync();
           if (h == 0)
-            tile_mma<NB, I4, 0, 2>(s0.x, smem, tab, lut, acc, lm);
+            tile_mma<NB, I4, 0, 2>(s0.x, smem, tab, lut, acc, corr, lm);
           else
-            tile_mma<NB, I4, 2, 4>(s0.x, smem, tab, lut, acc, lm);
+            tile_mma<NB, I4, 2, 4>(s0.x, smem, tab, lut, acc, corr, lm);
           wave_sync();
         }
       }
@@ -362,7 +369,7 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
       const int cn = min(c + 1, c_last);
       slot_load(s0, a, gi, cn, lane, off_at(cn), off_at(cn + 1));
       wave_sync();
-      tile_mma<NB, I4>(xc, smem, tab, lut, acc, lm);
+      tile_mma<NB, I4>(xc, smem, tab, lut, acc, corr, lm);
       wave_sync();
       write_tab(s0);
     }
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
       load(nxt, c + kD);
       slot_commit(cur, vb, lane);
       wave_sync();
-      tile_mma<NB, I4>(cur.x, smem, tab, lut, acc, lm);
+      tile_mma<NB, I4>(cur.x, smem, tab, lut, acc, corr, lm);
       wave_sync();
       write_tab(after);
     };
@@ -402,13 +409,14 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   }
 
   // Workgroup reduction over waves (fixed order).
+  if constexpr (I4) code_bias_finish<NB>(corr);
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb];
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = I4 ? acc[f][nb] + corr[nb] : acc[f][nb];
   __syncthreads();
 
   finish_strip<NB, I4, OUT_F16>(a, gi, sidx, kThreads, last_flag, [&](int n, int ml) {

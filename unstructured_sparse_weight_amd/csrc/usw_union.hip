@@ -124,7 +124,9 @@ __device__ __forceinline__ void urow_tab_write(uint8_t* tab, uint32_t rowbits, u
 // payload is in LDS, and multiply them with the X^T fragments.
 template <int NB, int BITS>
 __device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const uint8_t* smem, const uint8_t* tab,
-                                               const u32x2_t* lut, uint32_t P, f32x4_t (&acc)[4][NB], int lane) {
+                                               const u32x2_t* lut, uint32_t P, f32x4_t (&acc)[4][NB],
+                                               f32x4_t (&corr)[NB], int lane) {
+  code_bias_mma<NB>(corr, x);
   const int i = lane & 15;
   const uint32_t sh = 8u * static_cast<uint32_t>(lane >> 4);
   const uint32_t pmask = (1u << sh) - 1u;
@@ -180,6 +182,9 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[f][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t corr[NB];   // the code expansion offset's correction, same for every row
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) corr[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   uint8_t* vb = smem + w * kUVbuf;
   uint8_t* tab = smem + kUWaves * kUVbuf + w * kURowTab;
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
       load(nxt, c + 1);
       commit(cur);
       wave_sync();
-      union_tile_mma<NB, BITS>(cur.x, smem, tab, lut, cur.P, acc, lane);
+      union_tile_mma<NB, BITS>(cur.x, smem, tab, lut, cur.P, acc, corr, lane);
       wave_sync();
       write_tab(nxt);
     };
@@ -227,13 +232,14 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
   }
 
   // Workgroup reduction over waves (fixed order).
+  code_bias_finish<NB>(corr);
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb];
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb] + corr[nb];
   __syncthreads();
 
   finish_strip<NB, true, OUT_F16>(a, gi, sidx, kUThreads, last_flag, [&](int n, int ml) {
@@ -358,7 +364,8 @@ __device__ __forceinline__ void u16_tab_write(uint8_t* tab, uint32_t rowbits, co
 template <int NB, int BITS>
 __device__ __forceinline__ void u16_tile_mma(const U16Slot<NB>& cur, bool mapped, const uint8_t* smem,
                                              const uint8_t* tab, const u32x2_t* lut, f32x4_t (&acc)[4][NB],
-                                             int lane) {
+                                             f32x4_t (&corr)[NB], int lane) {
+  code_bias_mma<NB>(corr, cur.x);
   const uint32_t sh = 8u * static_cast<uint32_t>(lane >> 4);
   const uint32_t pmask = (1u << sh) - 1u;
   const int i = lane & 15;
@@ -414,6 +421,9 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[f][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t corr[NB];   // the code expansion offset's correction, same for every row
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) corr[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   uint8_t* vb = smem + w * 4 * kU16Vbuf;
   uint8_t* tab = smem + kU16Waves * 4 * kU16Vbuf + w * kU16Tab;
@@ -461,7 +471,7 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
       load(nxt, c + 1);
       commit(cur);
       wave_sync();
-      u16_tile_mma<NB, BITS>(cur, mapped, smem, tab, lut, acc, lane);
+      u16_tile_mma<NB, BITS>(cur, mapped, smem, tab, lut, acc, corr, lane);
       wave_sync();
       write_tab(nxt);
     };
@@ -474,13 +484,14 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
   }
 
   // Workgroup reduction over waves (fixed order).
+  code_bias_finish<NB>(corr);
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb];
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb] + corr[nb];
   __syncthreads();
 
   finish_strip<NB, true, OUT_F16>(a, gi, sidx, kU16Threads, last_flag, [&](int n, int ml) {
@@ -637,7 +648,9 @@ __device__ __forceinline__ void ug_tab_write(uint8_t* tab, uint32_t lo, uint32_t
 template <int LTM, int NB, int BITS>
 __device__ __forceinline__ void ug_tile_mma(const UGSlot<NB, UGShape<LTM, BITS>::NCH, UGShape<LTM, BITS>::F>& cur,
                                             const Args& a, bool mapped, const uint8_t* smem, const uint8_t* tab,
-                                            const u32x2_t* lut, uint32_t vb_elems, f32x4_t (&acc)[4][NB], int lane) {
+                                            const u32x2_t* lut, uint32_t vb_elems, f32x4_t (&acc)[4][NB],
+                                            f32x4_t (&corr)[NB], int lane) {
+  code_bias_mma<NB>(corr, cur.x);
   using S = UGShape<LTM, BITS>;
   const int i = lane & 15;
   const int g = lane >> 4;
@@ -706,6 +719,9 @@ __global__ __launch_bounds__(kUGThreads, OCC) void union_grid_decode_kernel(Args
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[f][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t corr[NB];   // the code expansion offset's correction, same for every row
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) corr[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   uint8_t* vb = smem + w * S::kVbuf;
   uint8_t* tab = smem + kUGWaves * S::kVbuf + w * kUGTab;
@@ -748,7 +764,7 @@ __global__ __launch_bounds__(kUGThreads, OCC) void union_grid_decode_kernel(Args
       load(nxt, c + 1);
       commit(cur);
       wave_sync();
-      ug_tile_mma<LTM, NB, BITS>(cur, a, mapped, smem, tab, lut, vb_elems, acc, lane);
+      ug_tile_mma<LTM, NB, BITS>(cur, a, mapped, smem, tab, lut, vb_elems, acc, corr, lane);
       wave_sync();
       write_tab(nxt);
     };
@@ -761,13 +777,14 @@ __global__ __launch_bounds__(kUGThreads, OCC) void union_grid_decode_kernel(Args
   }
 
   // Workgroup reduction over waves (fixed order).
+  code_bias_finish<NB>(corr);
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb];
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb] + corr[nb];
   __syncthreads();
 
   finish_strip<NB, true, OUT_F16>(a, gi, sidx, kUGThreads, last_flag, [&](int n, int ml) {
