@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
+from oracle import ie_bme as ou
 from oracle import tca_bme as ob
 
 torch = pytest.importorskip("torch")
@@ -344,3 +345,28 @@ def test_probe_read_runs():
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     assert L.usw_probe_read(buf.data_ptr(), buf.numel(), sink.data_ptr(), stream) == 0
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("N", [2, 24])
+@pytest.mark.parametrize("fmt", ["tca", "union"])
+def test_low_bit_offset_cancels_on_large_activations(fmt, N):
+    """The low-bit kernels multiply code + 72 and take 72 times X's column
+    sums back out; activations with a large common offset (N(40, 1)) make
+    those sums large.  The result must still pass the oracle's acceptance
+    test (one token block: the matrix-core correction; two: v_dot2)."""
+    M, K = 1024, 5120
+    rng = np.random.default_rng(470 + N)
+    W = wl.weight_normal(M, K, rng)
+    mask = wl.mask_magnitude(W, 0.5)
+    X = (40.0 + rng.normal(0.0, 1.0, size=(N, K))).astype(np.float16)
+    x = torch.from_numpy(X).to(DEV)
+    if fmt == "tca":
+        Y = run_gpu(W, mask, X, "i4", out=torch.float32)
+        Yref, Bnd = oracle_ref(W, mask, X, "i4")
+    else:
+        enc = usw.union_to_device(usw.union_encode_host(W, mask, (64, 64), (2, 2), "i4"), DEV)
+        Y = usw.union_spmm(enc, x, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+        torch.cuda.synchronize()
+        Wd = ou.dense_weight_union(ou.encode_union(W, mask, 64, 64, 2, 2, ob.VAL_I4))
+        Yref, Bnd = ob.spmm_fp64(Wd, X), ob.abs_bound(Wd, X)
+    assert_parity(Y, Yref, Bnd, f"{fmt} INT4 N={N}, activations N(40, 1)")
