@@ -4,9 +4,11 @@ row of packed two's-complement codes into fp16 A-fragment slots: the row's
 of a byte), v_perm places nibble k in the slot of the k-th set bit of the
 row's mask byte (selector 0x0C gives a zero byte for a clear bit), a xor
 with 0x80 turns the nibble q into q + 8, and 0x54 in the high byte makes the
-fp16 value 64 + (q + 8) = q + 72.  The expected values come from the mask
-and the codes alone: slot p holds its code + 72 when bit p is set, else 72.
-No kernel is launched."""
+fp16 value 64 + (q + 8) = q + 72.  2-bit codes are placed in the top two
+bits of their byte instead, so a code c becomes 4c + 72 (the kernels scale
+the corrected sums by 1/4).  The expected values come from the mask and the
+codes alone: slot p holds its code (times 4 for 2-bit) + 72 when bit p is
+set, else 72.  No kernel is launched."""
 import numpy as np
 
 
@@ -37,13 +39,30 @@ def row_selectors(b):
     return sel
 
 
-def expand(codes, b):
-    """fp16 slots of a row: codes are the row's kept values in order."""
+def split4(codes):
+    """The 4-bit window of a row's codes, split as the kernels do."""
     win = 0
     for k, q in enumerate(codes):
         win |= (q & 0xF) << (4 * k)
-    lo4 = (win << 4) & 0xF0F0F0F0
-    hi4 = win & 0xF0F0F0F0
+    return (win << 4) & 0xF0F0F0F0, win & 0xF0F0F0F0
+
+
+def split2(codes):
+    """The 2-bit window (16 bits) spread to one code per nibble, then each
+    code moved to the top two bits of its byte, even codes in lo4 and odd
+    codes in hi4."""
+    t = 0
+    for k, c in enumerate(codes):
+        t |= (c & 0x3) << (2 * k)
+    t = (t | (t << 8)) & 0x00FF00FF
+    t = (t | (t << 4)) & 0x0F0F0F0F
+    t = (t | (t << 2)) & 0x33333333
+    return (t << 6) & 0xC0C0C0C0, (t << 2) & 0xC0C0C0C0
+
+
+def expand(codes, b, bits=4):
+    """fp16 slots of a row: codes are the row's kept values in order."""
+    lo4, hi4 = (split4 if bits == 4 else split2)(codes)
     sx, sy = row_selectors(b)
     e0 = v_perm(hi4, lo4, sx) ^ 0x80808080
     e1 = v_perm(hi4, lo4, sy) ^ 0x80808080
@@ -75,3 +94,19 @@ def test_extreme_codes_are_exact():
     for u in range(16):
         h = np.array([0x5400 | (u << 4)], dtype=np.uint16).view(np.float16)[0]
         assert float(h) == 64.0 + u
+
+
+def test_two_bit_codes_every_mask_byte():
+    rng = np.random.default_rng(6)
+    for b in range(256):
+        n = bin(b).count("1")
+        for _ in range(4):
+            codes = [int(c) for c in rng.integers(-2, 2, size=n)]
+            slots = expand(codes, b, bits=2)
+            want = np.full(8, 72.0)
+            k = 0
+            for p in range(8):
+                if (b >> p) & 1:
+                    want[p] += 4 * codes[k]
+                    k += 1
+            assert np.array_equal(slots, want), (b, codes, slots, want)

@@ -224,23 +224,22 @@ __device__ __forceinline__ u32x2_t lds_window_i4(const uint8_t* buf, uint32_t e)
   return r;
 }
 
-// 8 packed 2-bit codes starting at code e of an LDS buffer, widened to
-// two's-complement nibbles (code k in nibble k, its sign bit copied into the
-// nibble's upper two bits) and split into the even (lo4) and odd (hi4)
-// nibbles, one per byte, as lds_window_i4 returns them.  v_alignbit uses
-// only the low five bits of its shift operand, here 2 * (e mod 16).
+// 8 packed 2-bit codes starting at code e of an LDS buffer, split into the
+// even (lo4) and odd (hi4) codes, one per byte in the byte's top two bits,
+// where expand_row_i4 reads them as the top of a nibble: a code c becomes
+// the slot 4c + 72 (the row is 4 times the codes, plus the offset; the
+// kernels scale the sum by 1/4).  v_alignbit uses only the low five bits of
+// its shift operand, here 2 * (e mod 16).
 __device__ __forceinline__ u32x2_t lds_window_i2(const uint8_t* buf, uint32_t e) {
   const uint32_t ba = e >> 2;
   const uint32_t* p = reinterpret_cast<const uint32_t*>(buf + (ba & ~3u));
   uint32_t t = __builtin_amdgcn_alignbit(p[1], p[0], e << 1) & 0xFFFFu;
   t = (t | (t << 8)) & 0x00FF00FFu;   // codes 0-3 in byte 0, 4-7 in byte 2
   t = (t | (t << 4)) & 0x0F0F0F0Fu;   // two codes per byte
-  t = (t | (t << 2)) & 0x33333333u;   // one code per nibble
-  const uint32_t sgn = t & 0x22222222u;
-  t |= (sgn << 1) | (sgn << 2);
+  t = (t | (t << 2)) & 0x33333333u;   // code k in bits 0-1 of nibble k
   u32x2_t r;
-  r.x = (t << 4) & 0xF0F0F0F0u;
-  r.y = t & 0xF0F0F0F0u;
+  r.x = (t << 6) & 0xC0C0C0C0u;
+  r.y = (t << 2) & 0xC0C0C0C0u;
   return r;
 }
 
@@ -248,9 +247,9 @@ __device__ __forceinline__ u32x2_t lds_window_i2(const uint8_t* buf, uint32_t e)
 constexpr float kCodeBias = 72.0f;
 
 // The 8 fp16 slots of a code row, each holding its code plus kCodeBias
-// (empty slots kCodeBias), from its 8-nibble window (split into lo4 / hi4,
-// nibbles in the upper half of each byte, by lds_window_i4 / _i2) and its
-// selectors.  The offset keeps the expansion to byte permutes: the kernels
+// (empty slots kCodeBias; 2-bit rows four times the code plus kCodeBias),
+// from its 8-nibble window (split into lo4 / hi4, nibbles in the upper half
+// of each byte, by lds_window_i4 / _i2) and its selectors.  The offset keeps the expansion to byte permutes: the kernels
 // take it out with code_bias_mma, once per X^T fragment.
 __device__ __forceinline__ half8_t expand_row_i4(u32x2_t w8, u32x2_t sel) {
   // Slots as bytes, the nibble in the upper half; xor 0x80 maps the
@@ -373,6 +372,9 @@ struct Packed {
     else
       return lds_window_i2(buf, e);
   }
+  // What a row's expanded slots count each code as (window above): the
+  // corrected sums are multiplied by this, exactly.
+  static constexpr float kSumScale = BITS == 4 ? 1.0f : 0.25f;
 };
 
 // Byte offset of the 16-byte chunk holding value element e (fp16: 2 B per

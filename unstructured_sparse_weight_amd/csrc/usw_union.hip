@@ -239,7 +239,8 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb] + corr[nb];
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) =
+          (acc[f][nb] + corr[nb]) * Packed<BITS>::kSumScale;
   __syncthreads();
 
   finish_strip<NB, true, OUT_F16>(a, gi, sidx, kUThreads, last_flag, [&](int n, int ml) {
@@ -491,7 +492,8 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb] + corr[nb];
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) =
+          (acc[f][nb] + corr[nb]) * Packed<BITS>::kSumScale;
   __syncthreads();
 
   finish_strip<NB, true, OUT_F16>(a, gi, sidx, kU16Threads, last_flag, [&](int n, int ml) {
@@ -784,7 +786,8 @@ __global__ __launch_bounds__(kUGThreads, OCC) void union_grid_decode_kernel(Args
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = acc[f][nb] + corr[nb];
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) =
+          (acc[f][nb] + corr[nb]) * Packed<BITS>::kSumScale;
   __syncthreads();
 
   finish_strip<NB, true, OUT_F16>(a, gi, sidx, kUGThreads, last_flag, [&](int n, int ml) {
