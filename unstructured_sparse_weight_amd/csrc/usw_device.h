@@ -244,13 +244,14 @@ __device__ __forceinline__ u32x2_t lds_window_i2(const uint8_t* buf, uint32_t e)
 }
 
 // Offset of the code rows expand_row_i4 returns: a slot holds code + 72.
-constexpr float kCodeBias = 72.0f;
+constexpr float kCodeOffset = 72.0f;
 
-// The 8 fp16 slots of a code row, each holding its code plus kCodeBias
-// (empty slots kCodeBias; 2-bit rows four times the code plus kCodeBias),
-// from its 8-nibble window (split into lo4 / hi4, nibbles in the upper half
-// of each byte, by lds_window_i4 / _i2) and its selectors.  The offset keeps the expansion to byte permutes: the kernels
-// take it out with code_bias_mma, once per X^T fragment.
+// The 8 fp16 slots of a code row, each holding its code plus kCodeOffset
+// (empty slots kCodeOffset; 2-bit rows four times the code plus
+// kCodeOffset), from its 8-nibble window (split into lo4 / hi4, nibbles in
+// the upper half of each byte, by lds_window_i4 / _i2) and its selectors.
+// The offset keeps the expansion to byte permutes: the kernels take it out
+// with code_offset_collect, once per X^T fragment.
 __device__ __forceinline__ half8_t expand_row_i4(u32x2_t w8, u32x2_t sel) {
   // Slots as bytes, the nibble in the upper half; xor 0x80 maps the
   // two's-complement nibble q to u = q + 8 in [0, 15] (an empty slot's 0
@@ -268,10 +269,10 @@ __device__ __forceinline__ half8_t expand_row_i4(u32x2_t w8, u32x2_t sel) {
 }
 
 // Takes the expansion's offset out of a tile: every slot of a rebuilt
-// fragment carries kCodeBias, so fragment A times X^T fragment x exceeds the
-// true product by kCodeBias times x's column sums, the same for every row.
-// corr[nb] collects -kCodeBias times those sums; code_bias_finish puts them
-// in the accumulator layout, and the kernel adds them to every row block's
+// fragment carries kCodeOffset, so fragment A times X^T fragment x exceeds
+// the true product by kCodeOffset times x's column sums, the same for every
+// row.  corr[nb] collects -kCodeOffset times those sums; code_offset_finish
+// puts them in the accumulator layout, and the kernel adds them to every row block's
 // accumulators before the reduction.  With one token block the sums come
 // from one MFMA with a constant A per X^T fragment (the matrix cores are
 // mostly idle in decode); with two, from v_dot2 on the vector ALUs (the
@@ -279,8 +280,8 @@ __device__ __forceinline__ half8_t expand_row_i4(u32x2_t w8, u32x2_t sel) {
 // in corr[nb].x.  With integer-valued inputs every product and partial sum
 // is an integer, exact while its magnitude stays below 2^24.
 template <int NB>
-__device__ __forceinline__ void code_bias_mma(f32x4_t (&corr)[NB], const u32x4_t (&x)[2][NB]) {
-  const _Float16 m = static_cast<_Float16>(-kCodeBias);
+__device__ __forceinline__ void code_offset_collect(f32x4_t (&corr)[NB], const u32x4_t (&x)[2][NB]) {
+  const _Float16 m = static_cast<_Float16>(-kCodeOffset);
   if constexpr (NB == 1) {
     const half8_t neg = {m, m, m, m, m, m, m, m};
 #pragma unroll
@@ -307,7 +308,7 @@ __device__ __forceinline__ void code_bias_mma(f32x4_t (&corr)[NB], const u32x4_t
 // its block, four rows): with v_dot2 the four lanes of a token (l % 16
 // equal) add their partial sums.
 template <int NB>
-__device__ __forceinline__ void code_bias_finish(f32x4_t (&corr)[NB]) {
+__device__ __forceinline__ void code_offset_finish(f32x4_t (&corr)[NB]) {
   if constexpr (NB > 1) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {

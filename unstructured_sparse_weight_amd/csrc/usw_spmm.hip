@@ -193,13 +193,13 @@ __device__ __forceinline__ uint32_t bitmap_prefix_reg(u32x2_t bm) {
 // Rebuild and multiply fragments f = F0 .. F1-1 (both ks) of a GroupTile
 // whose bitmap table is at tab and whose values are in the LDS staging area
 // starting at vals.  INT4 rows carry the expansion's offset: corr collects
-// its correction (code_bias_mma, all four fragments of a GroupTile at once).
+// its correction (code_offset_collect, all four fragments of a GroupTile at once).
 template <int NB, bool I4, int F0 = 0, int F1 = 4>
 __device__ __forceinline__ void tile_mma(const u32x4_t (&x)[2][NB], const uint8_t* vals, const uint8_t* tab,
                                          const uint32_t* lut, f32x4_t (&acc)[4][NB], f32x4_t (&corr)[NB],
                                          const LaneMap& lm) {
   static_assert(!I4 || (F0 == 0 && F1 == 4), "the INT4 correction covers whole GroupTiles");
-  if constexpr (I4) code_bias_mma<NB>(corr, x);
+  if constexpr (I4) code_offset_collect<NB>(corr, x);
   u32x2_t e[F1 - F0][2];
 #pragma unroll
   for (int f = F0; f < F1; ++f)
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   }
 
   // Workgroup reduction over waves (fixed order).
-  if constexpr (I4) code_bias_finish<NB>(corr);
+  if constexpr (I4) code_offset_finish<NB>(corr);
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll

@@ -126,7 +126,7 @@ template <int NB, int BITS>
 __device__ __forceinline__ void union_tile_mma(const u32x4_t (&x)[2][NB], const uint8_t* smem, const uint8_t* tab,
                                                const u32x2_t* lut, uint32_t P, f32x4_t (&acc)[4][NB],
                                                f32x4_t (&corr)[NB], int lane) {
-  code_bias_mma<NB>(corr, x);
+  code_offset_collect<NB>(corr, x);
   const int i = lane & 15;
   const uint32_t sh = 8u * static_cast<uint32_t>(lane >> 4);
   const uint32_t pmask = (1u << sh) - 1u;
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
   }
 
   // Workgroup reduction over waves (fixed order).
-  code_bias_finish<NB>(corr);
+  code_offset_finish<NB>(corr);
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll
@@ -366,7 +366,7 @@ template <int NB, int BITS>
 __device__ __forceinline__ void u16_tile_mma(const U16Slot<NB>& cur, bool mapped, const uint8_t* smem,
                                              const uint8_t* tab, const u32x2_t* lut, f32x4_t (&acc)[4][NB],
                                              f32x4_t (&corr)[NB], int lane) {
-  code_bias_mma<NB>(corr, cur.x);
+  code_offset_collect<NB>(corr, cur.x);
   const uint32_t sh = 8u * static_cast<uint32_t>(lane >> 4);
   const uint32_t pmask = (1u << sh) - 1u;
   const int i = lane & 15;
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
   }
 
   // Workgroup reduction over waves (fixed order).
-  code_bias_finish<NB>(corr);
+  code_offset_finish<NB>(corr);
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll
@@ -652,7 +652,7 @@ __device__ __forceinline__ void ug_tile_mma(const UGSlot<NB, UGShape<LTM, BITS>:
                                             const Args& a, bool mapped, const uint8_t* smem, const uint8_t* tab,
                                             const u32x2_t* lut, uint32_t vb_elems, f32x4_t (&acc)[4][NB],
                                             f32x4_t (&corr)[NB], int lane) {
-  code_bias_mma<NB>(corr, cur.x);
+  code_offset_collect<NB>(corr, cur.x);
   using S = UGShape<LTM, BITS>;
   const int i = lane & 15;
   const int g = lane >> 4;
@@ -779,7 +779,7 @@ __global__ __launch_bounds__(kUGThreads, OCC) void union_grid_decode_kernel(Args
   }
 
   // Workgroup reduction over waves (fixed order).
-  code_bias_finish<NB>(corr);
+  code_offset_finish<NB>(corr);
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [waves][4][NB][64 lanes][4]
 #pragma unroll
