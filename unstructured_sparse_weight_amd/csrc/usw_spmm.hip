@@ -416,7 +416,8 @@ __global__ __launch_bounds__(C::kThreadsPerGroup, C::kOcc) void decode_kernel(Ar
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) = I4 ? acc[f][nb] + corr[nb] : acc[f][nb];
+      *reinterpret_cast<f32x4_t*>(red + (((w * 4 + f) * NB + nb) * 64 + lane) * 4) =
+          I4 ? acc[f][nb] + corr[nb] : acc[f][nb];
   __syncthreads();
 
   finish_strip<NB, I4, OUT_F16>(a, gi, sidx, kThreads, last_flag, [&](int n, int ml) {
