@@ -10,9 +10,9 @@
 // Design (wave64):
 //   * One workgroup of four waves owns one 256-row strip of GTiles and a
 //     range of GTile columns; each wave streams its own run of GTiles over
-//     all 256 rows (lane l holds rows l, 64 + l, 128 + l, 192 + l), with its
-//     own LDS staging area, so the main loop has no workgroup barrier.  The
-//     four waves' row sums are added in LDS at the end, in a fixed order.
+//     all 256 rows (lane l holds rows 4l .. 4l+3), with its own LDS staging
+//     area, so the main loop has no workgroup barrier.  The four waves' row
+//     sums are added in LDS at the end, in a fixed order.
 //   * Per GTile: lane j (mod 16) reads column j's ColInfo and x_j, and the
 //     wave ballots |x_j| >= tau into a 16-bit mask of active columns.  The
 //     padded runs of the active columns are loaded (16 bytes per load; lane
@@ -22,12 +22,13 @@
 //     bytes.  ColInfo, x and TileOffset run two GTiles ahead, since the
 //     value loads depend on them.
 //   * The active columns' bitmap words load with the values (lane 4c + q:
-//     word q of column c).  For each active column (a scalar loop over the
-//     mask) v_readlane brings its four words into SGPRs and SALU popcounts
-//     give each word's base.  Per word, every lane takes base + v_mbcnt of the word
-//     (the masked popcount of the bits below it) as its rank, reads that
-//     value from LDS, and accumulates it times x_k, with x_k replaced by 0
-//     where its bit is clear.
+//     word q of column c).  At the copy, lane 4c + q also writes a table
+//     entry: the word and the set bits of the column's earlier words.
+//   * Per active column (a scalar loop over the mask) every lane reads the
+//     entry of its word, takes its rank (the set bits below its first row)
+//     by masked popcount, and expands the values of its four rows from one
+//     LDS window with v_perm byte selectors indexed by its 4-bit nibble of
+//     the bitmap (a clear bit selects 0), then four fp32 FMAs with x_k.
 //   * Split K: each workgroup writes its row sums to an fp32 workspace with
 //     device-coherent stores; the last workgroup of the strip (a per-strip
 //     counter) adds them in split order and writes y.
@@ -87,7 +88,6 @@ struct CData {
   u32x2_t bw;          // lane 4c + q: bitmap word q of column c (0 when inactive)
   float xf;            // lane j: x_j
   uint32_t amask;      // active columns (wave-uniform)
-  uint32_t pieces;     // lane 4c + q: 16-byte pieces of column c's run (0 when inactive)
 };
 
 __device__ __forceinline__ CMeta cbc_meta(const CArgs& a, int gi, int c, int lane) {
@@ -105,10 +105,16 @@ __device__ __forceinline__ void cbc_load(CData& d, const CArgs& a, int gi, int c
   d.amask = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(fabsf(m.xf) >= a.tau)) & 0xFFFFu;
   const uint32_t tbase = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(m.tbase));
   const int bc = lane >> 2, bq = lane & 3;
+  const bool active = (d.amask >> bc) & 1u;
   const uint32_t cib = __shfl(m.ci, bc);
-  d.pieces = ((d.amask >> bc) & 1u) ? ((cib & 0xFFFFu) + 7u) >> 3 : 0u;
-  d.bw = u32x2_t{0u, 0u};
-  if ((d.amask >> bc) & 1u) d.bw = reinterpret_cast<const u32x2_t*>(a.bitmaps)[(t * kTK + bc) * kWpc + bq];
+  const uint32_t pieces = active ? ((cib & 0xFFFFu) + 7u) >> 3 : 0u;
+  // The GTile's bitmap words through a buffer descriptor of their 512
+  // bytes: an inactive column's lanes take an offset past it and read zeros
+  // without a fetch, and without a branch.
+  const auto brs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(a.bitmaps + t * kTK * kWpc), 0,
+                                                     kTK * kWpc * 8, kBufferRsrcWord3);
+  const uint32_t boff = active ? 8u * static_cast<uint32_t>(bc * kWpc + bq) : 2u * kTK * kWpc * 8;
+  d.bw = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(brs, static_cast<int>(boff), 0, 0));
   // Buffer loads over the whole values array: a lane past its column's run
   // (or on an inactive column) gets an offset beyond the array, which the
   // hardware answers with zeros without a fetch, so no branch is needed;
@@ -119,56 +125,104 @@ __device__ __forceinline__ void cbc_load(CData& d, const CArgs& a, int gi, int c
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const uint32_t q = static_cast<uint32_t>(bq + 4 * i);
-    const uint32_t off = q < d.pieces ? src0 + 16u * q : kPastValues;
+    const uint32_t off = q < pieces ? src0 + 16u * q : kPastValues;
     d.v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(off), 0, 0));
   }
 }
 
-// Every lane stores its pieces, zeros past the run included (such slots are
-// only read by lanes whose bit is clear, which weight them by 0).
-__device__ __forceinline__ void cbc_commit(const CData& d, uint8_t* buf, int lane) {
+// Every lane stores its pieces, zeros past the run included.  Lane 4c + q
+// also writes table entry 4c + q: word q of column c (0 when inactive) and
+// the set bits of words 0 .. q-1, a prefix over the lane's quad by DPP.
+__device__ __forceinline__ void cbc_commit(const CData& d, uint8_t* buf, u32x4_t* tab, int lane) {
   const int bc = lane >> 2, bq = lane & 3;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) *reinterpret_cast<u32x4_t*>(buf + bc * kColBytes + 16 * (bq + 4 * i)) = d.v[i];
+  const uint32_t pc = __builtin_popcount(d.bw.x) + __builtin_popcount(d.bw.y);
+  uint32_t inc = pc;
+  const uint32_t t1 = __builtin_amdgcn_update_dpp(0u, inc, 0x111, 0xf, 0xf, false);   // row_shr:1
+  if (bq >= 1) inc += t1;
+  const uint32_t t2 = __builtin_amdgcn_update_dpp(0u, inc, 0x112, 0xf, 0xf, false);   // row_shr:2
+  if (bq >= 2) inc += t2;
+  tab[lane] = u32x4_t{d.bw.x, d.bw.y, inc - pc, 0u};
 }
 
-// x_k where the lane's bit of word is set, else 0 (the word is wave-uniform,
-// so it serves directly as the lane mask of v_cndmask).
-__device__ __forceinline__ float select_by_word(float xk, uint64_t word) {
-  float r;
-  asm volatile("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(r) : "v"(xk), "s"(word));
-  return r;
+// What a lane needs to find its four rows 4l .. 4l+3 in a column: they are
+// bits sh .. sh+3 of word l / 16 (sh = 4 (l mod 16)); the masks keep the
+// word's bits below sh.
+struct CLane {
+  uint32_t mlo, mhi;   // bits of the word's low / high half below sh
+  uint32_t sh;         // sh mod 32
+  bool hi;             // the nibble is in the high half
+};
+
+__device__ __forceinline__ CLane cbc_lane(int lane) {
+  const uint32_t sh = 4u * static_cast<uint32_t>(lane & 15);
+  CLane c;
+  c.hi = sh >= 32u;
+  c.sh = sh & 31u;
+  c.mlo = c.hi ? 0xFFFFFFFFu : (1u << sh) - 1u;
+  c.mhi = c.hi ? (1u << c.sh) - 1u : 0u;
+  return c;
 }
 
-// Accumulate a staged GTile over its active columns.  bw is the GTile's
-// bitmap words (lane 4c + q: word q of column c); each word is read into
-// SGPRs with v_readlane, its base is the SALU popcount of the column's
-// earlier words.
-__device__ __forceinline__ void cbc_compute(float xf, uint32_t amask, u32x2_t bw, const _Float16* vals,
-                                            float (&acc)[4]) {
-  for (uint32_t m = amask; m != 0; m &= m - 1) {
-    const int cc = __builtin_ctz(m);
-    const float xc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xf), cc));
-    // The word's base (set bits of the column's earlier words) goes into
-    // the scalar part of the address; a rank counts bits among the
-    // column's 256 rows, so it stays below 256.
-    const _Float16* col = vals + cc * kTM;
-#pragma unroll
-    for (int q = 0; q < kWpc; ++q) {
-      const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(bw.x, 4 * cc + q));
-      const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(bw.y, 4 * cc + q));
-      const uint64_t word = (static_cast<uint64_t>(hi) << 32) | lo;
-      const uint32_t below = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-      const float v = static_cast<float>(col[below]);
-      acc[q] = fmaf(v, select_by_word(xc, word), acc[q]);
-      col += __builtin_popcountll(word);
+// Accumulate a staged GTile over its active columns.  Per column: the
+// lane's table entry gives its rank (bits below its first row); its four
+// rows' values are the kept ones among window values rank .. rank+3, placed
+// by the 16-entry nibble selector table (clear bits select 0).
+__device__ __forceinline__ void cbc_compute(float xf, uint32_t amask, const uint8_t* buf, const u32x4_t* tab,
+                                            const uint32_t* lut, const CLane& cl, float (&acc)[4], int lane) {
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+  const u32x4_t* mytab = tab + (lane >> 4);
+  // A column's window and selectors, then its four FMAs.
+  struct Col {
+    u32x2_t w, sel;
+    float xc;
+  };
+  auto fetch = [&](int cc) {
+    Col c;
+    c.xc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xf), cc));
+    const u32x3_t e = *reinterpret_cast<const u32x3_t*>(mytab + kWpc * cc);
+    const uint32_t rank = __builtin_popcount(e.y & cl.mhi) + __builtin_popcount(e.x & cl.mlo) + e.z;
+    const uint32_t nib = __builtin_amdgcn_ubfe(cl.hi ? e.y : e.x, cl.sh, 4);
+    c.w = lds_window_f16(buf + cc * kColBytes, rank);
+    c.sel = reinterpret_cast<const u32x2_t*>(lut)[nib];
+    return c;
+  };
+  auto accumulate = [&](const Col& c) {
+    const half2_t v01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(c.w.y, c.w.x, c.sel.x));
+    const half2_t v23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(c.w.y, c.w.x, c.sel.y));
+    acc[0] = fmaf(static_cast<float>(v01.x), c.xc, acc[0]);
+    acc[1] = fmaf(static_cast<float>(v01.y), c.xc, acc[1]);
+    acc[2] = fmaf(static_cast<float>(v23.x), c.xc, acc[2]);
+    acc[3] = fmaf(static_cast<float>(v23.y), c.xc, acc[3]);
+  };
+  // Two columns per pass, so that their chains of LDS round trips overlap;
+  // the sums are still added in column order.
+  uint32_t m = amask;
+  while (m != 0) {
+    const int c0 = __builtin_ctz(m);
+    m &= m - 1;
+    if (m == 0) {
+      accumulate(fetch(c0));
+      break;
     }
+    const int c1 = __builtin_ctz(m);
+    m &= m - 1;
+    const Col a0 = fetch(c0);
+    const Col a1 = fetch(c1);
+    accumulate(a0);
+    accumulate(a1);
   }
 }
 
 template <bool OUT_F16>
 __global__ __launch_bounds__(kCThreads, 4) void cbc_spmspv_kernel(CArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kCWaves * kWaveBuf];   // staging; then the wave reduction
+  // Staging areas (then the wave reduction), 16 bytes that a window at the
+  // end of the last column may read, and the word tables.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kCWaves * kWaveBuf + 16];
+  __shared__ __attribute__((aligned(16))) u32x4_t tabs[kCWaves][kTK * kWpc];
+  __shared__ __attribute__((aligned(16))) uint32_t lut[32];
   __shared__ uint32_t last_flag;
   USW_LDS_POISON(smem);
 
@@ -185,15 +239,17 @@ __global__ __launch_bounds__(kCThreads, 4) void cbc_spmspv_kernel(CArgs a) {
   const int c_begin = static_cast<int>(static_cast<int64_t>(a.Gc) * qw / parts);
   const int c_end = static_cast<int>(static_cast<int64_t>(a.Gc) * (qw + 1) / parts);
 
+  if (tid < 16) {
+    u32x2_t e;
+    e.x = nibble_selector(tid, 0);
+    e.y = nibble_selector(tid, 1);
+    reinterpret_cast<u32x2_t*>(lut)[tid] = e;
+  }
+  __syncthreads();
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   uint8_t* buf = smem + w * kWaveBuf;
-  const _Float16* vals = reinterpret_cast<const _Float16*>(buf);
-  // A lane whose bit is clear still reads a value (then weighted by 0);
-  // zeroing the staging area first means such a read only ever sees a
-  // finite weight of this call or 0.
-#pragma unroll
-  for (int i = 0; i < kWaveBuf / 1024; ++i) reinterpret_cast<u32x4_t*>(buf)[lane + 64 * i] = u32x4_t{0u, 0u, 0u, 0u};
-  wave_sync();
+  u32x4_t* tab = tabs[w];
+  const CLane cl = cbc_lane(lane);
   if (c_begin < c_end) {
     // One register slot: a step copies GTile c's values into LDS, then
     // issues c+1's value loads into the same registers (and c+2's metadata)
@@ -205,23 +261,21 @@ __global__ __launch_bounds__(kCThreads, 4) void cbc_spmspv_kernel(CArgs a) {
     cbc_load(d, a, gi, c_begin, cbc_meta(a, gi, c_begin, lane), lane);
     for (int c = c_begin; c < c_end; ++c) {
       const CMeta m2 = cbc_meta(a, gi, min(c + 2, c_last), lane);
-      cbc_commit(d, buf, lane);
+      cbc_commit(d, buf, tab, lane);
       const float xf = d.xf;
       const uint32_t amask = d.amask;
-      const u32x2_t bw = d.bw;
       cbc_load(d, a, gi, min(c + 1, c_last), m1, lane);
       wave_sync();
-      cbc_compute(xf, amask, bw, vals, acc);
+      cbc_compute(xf, amask, buf, tab, lut, cl, acc, lane);
       wave_sync();
       m1 = m2;
     }
   }
 
-  // The waves' sums of strip row 64 q + lane, added in wave order.
+  // The waves' sums of strip row tid, added in wave order.
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [waves][256]
-#pragma unroll
-  for (int q = 0; q < 4; ++q) red[w * kTM + 64 * q + lane] = acc[q];
+  *reinterpret_cast<f32x4_t*>(red + w * kTM + 4 * lane) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
   __syncthreads();
   float rsum = 0.f;
 #pragma unroll
