@@ -527,19 +527,29 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PArgs a) {
     // it would stay live in every role's registers.
     int me = tid;
     asm volatile("" : "+v"(me));
-    f32x4_t sum[kJ];
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) sum[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < np; ++k) {
-      const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(slot_of(pc, q0 + k)) * kSlot, 0,
-                                                          kSlot * 4, kBufferRsrcWord3);
-      f32x4_t v[kJ];
+    // The first two slots' loads go out together; the sum keeps range
+    // order, starting from +0 as a plain running sum would (x + 0 is x,
+    // except that -0 becomes +0).
+    auto slot_rsrc = [&](int k) {
+      return __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(slot_of(pc, q0 + k)) * kSlot, 0,
+                                               kSlot * 4, kBufferRsrcWord3);
+    };
+    auto load_slot = [&](int k, f32x4_t* d) {
+      const auto r = slot_rsrc(k);
 #pragma unroll
       for (int j = 0; j < kJ; ++j)
-        v[j] = __builtin_bit_cast(f32x4_t,
-                                  __builtin_amdgcn_raw_buffer_load_b128(rsrc, (me + kThreads * j) * 16, 0, kCacheSc1));
+        d[j] = __builtin_bit_cast(f32x4_t,
+                                  __builtin_amdgcn_raw_buffer_load_b128(r, (me + kThreads * j) * 16, 0, kCacheSc1));
+    };
+    f32x4_t sum[kJ], u[kJ];
+    load_slot(0, sum);
+    if (np > 1) load_slot(1, u);
 #pragma unroll
-      for (int j = 0; j < kJ; ++j) sum[j] += v[j];
+    for (int j = 0; j < kJ; ++j) sum[j] += f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 1; k < np; ++k) {
+      if (k > 1) load_slot(k, u);
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) sum[j] += u[j];
     }
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
