@@ -233,11 +233,11 @@ def main():
     if cbc:
         args.dtype, args.N = "f16", 1
     M, K, N, s = args.M, args.K, args.N, args.sparsity
-    # Kernel family as usw_spmm picks it: fp16 with more than 96 tokens runs
+    # Kernel family as usw_spmm picks it: fp16 with more than 128 tokens runs
     # the prefill kernels, everything else the decode kernels (in passes of
-    # up to 32 tokens).  The synthetic inputs follow the prefill workload's
+    # up to 64 tokens).  The synthetic inputs follow the prefill workload's
     # recipe from 33 tokens on.
-    prefill = args.dtype == "f16" and N > 96
+    prefill = args.dtype == "f16" and N > 128
     layer_id = {(20480, 5120): 2, (11008, 4096): 0, (4096, 11008): 1}.get((M, K), 0)
     cfg_id = 5 if args.dtype in ("i4", "i2") else (4 if N > 32 else 2)
 

@@ -228,10 +228,10 @@ usw_status usw_spmm_workspace(const usw_fmt* fmt, int32_t N, size_t* bytes);
  *       enqueues work; it returns before the kernels finish.
  * Accumulation is fp32 (each product of two fp16 values is exact in fp32);
  * the result is deterministic: the same inputs give the same bits.
- * Kernels: fp16 values with N <= 96 take the decode kernels, in passes of
- * up to 32 tokens (one pass for N <= 32), N > 96 the prefill (MFMA)
+ * Kernels: fp16 values with N <= 128 take the decode kernels, in passes of
+ * up to 64 tokens (one pass for N <= 64), N > 128 the prefill (MFMA)
  * kernels (tiles of 256 tokens up to N = 256, of 512 above); INT4 values
- * take the INT4 decode kernel, in passes of up to 32 tokens, for any N.
+ * take the INT4 decode kernel, in passes of up to 64 tokens, for any N.
  * The 512-token prefill kernel returns UNSUPPORTED when N rounded up to 512,
  * times K, reaches 2^36.
  * The values buffer must hold the padded size usw_encode_query reports.

@@ -77,7 +77,25 @@ def test_tiny_integer_exact_bitwise(dtype):
     assert np.array_equal(Y16, Yref.astype(np.float16).astype(np.float64))
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 7, 15, 16, 17, 24, 31, 32, 33, 40, 64])
+@pytest.mark.parametrize("N,splits", [(33, 0), (64, 0), (64, 3), (100, 0), (128, 2)])
+@pytest.mark.parametrize("dtype", ["f16", "i4"])
+def test_four_block_passes_integer_exact_bitwise(dtype, N, splits):
+    """Decode passes of up to 64 tokens (four 16-token blocks per wave), alone
+    and followed by a shorter pass, with and without split K: on
+    integer-exact inputs every partial sum is exact, so Y equals the fp64
+    oracle bit for bit."""
+    M, K = 320, 1024
+    W, mask, X = wl.config_case(1, M, K, N, 0.5, exact=True)
+    if dtype == "i4":
+        W = wl.weight_int4_exact(M, K, np.random.default_rng(30 + N), mask)
+    Yref, _ = oracle_ref(W, mask, X, dtype)
+    assert np.array_equal(run_gpu(W, mask, X, dtype, out=torch.float32, splits=splits), Yref)
+    assert np.array_equal(run_gpu(W, mask, X, dtype, out=torch.float16, splits=splits),
+                          Yref.astype(np.float16).astype(np.float64))
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 7, 15, 16, 17, 24, 31, 32, 33, 40, 48, 63, 64, 65, 80, 96, 97, 112, 128,
+                               129])
 def test_ragged_n(N):
     rng = np.random.default_rng(100 + N)
     M, K = 320, 448          # 5 x 7 GroupTiles: uneven column ranges per wave

@@ -44,7 +44,7 @@ def tca_cases(n=28, seed=7100):
         M = 64 * int(rng.integers(1, 13))
         K = 64 * int(rng.integers(1, 41))
         N = int(rng.choice([1, 2, 5, 16, 17, 31, 32, 33, 64, 96, 97, 130, 257, 300]))
-        if dtype == "f16" and N > 96:                  # MFMA prefill kernels: keep the oracle fast
+        if dtype == "f16" and N > 96:                  # many tokens: keep the oracle fast
             M, K = min(M, 320), min(K, 1024)
         splits = int(rng.choice([0, 0, 1, 2, 3]))
         out.append((i, dtype, M, K, N, keep_of(rng), splits))

@@ -744,6 +744,8 @@ using DefaultCfgLean = Cfg<4, 1, 5>;
 // 17..32 columns of N: twice the accumulators and X fragments, which do not
 // fit 128 registers; three waves per SIMD leave room for them.
 using DefaultCfg2 = Cfg<4, 1, 3>;
+// 33..64 columns of N in one pass (four token blocks): two waves per SIMD.
+using DefaultCfg4 = Cfg<4, 1, 2>;
 // INT4 values, up to 16 columns of N: a third of the fp16 slot registers
 // (85 VGPRs), so a fifth wave per SIMD fits and hides more of the rebuild
 // latency (measured 6% faster on the 20480x5120 layer at N = 2).
@@ -754,8 +756,9 @@ struct CfgInfo {
   int occ;     // waves per SIMD the configuration allows
 };
 
-CfgInfo cfg_info(bool two, bool i4, bool lean) {
-  if (two) return CfgInfo{DefaultCfg2::kWavesPerGroup, DefaultCfg2::kOcc};
+CfgInfo cfg_info(int nchunk, bool i4, bool lean) {
+  if (nchunk > 32) return CfgInfo{DefaultCfg4::kWavesPerGroup, DefaultCfg4::kOcc};
+  if (nchunk > 16) return CfgInfo{DefaultCfg2::kWavesPerGroup, DefaultCfg2::kOcc};
   if (i4) return CfgInfo{DefaultCfgI4::kWavesPerGroup, DefaultCfgI4::kOcc};
   return lean ? CfgInfo{DefaultCfgLean::kWavesPerGroup, DefaultCfgLean::kOcc}
               : CfgInfo{DefaultCfg::kWavesPerGroup, DefaultCfg::kOcc};
@@ -767,7 +770,7 @@ constexpr int64_t kComputeUnits = 256;
 
 struct Plan {
   int splits;     // workgroups per 64-row strip
-  int nchunk;     // columns of N per kernel pass (16 or 32)
+  int nchunk;     // columns of N per kernel pass (16, 32 or 64)
   int waves;      // waves per workgroup
   bool ring;      // the workgroup-cooperative kernel
 };
@@ -798,10 +801,12 @@ int ring_resident() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // fp16 values with more than this many tokens take the prefill kernels;
-// fewer take the decode kernels in passes of up to 32 tokens, which re-read
-// the weight per pass but beat the 256-token prefill tiles up to 96 tokens
-// on MI355X (11008x4096 and 4096x11008: 1.3-2.0x at 48-96, even at 128).
-constexpr int kDecodeMaxN = 96;
+// fewer take the decode kernels in passes of up to 64 tokens, which re-read
+// the weight per pass but beat the 256-token prefill tiles up to 128 tokens
+// on MI355X (at 128: 71.7 against 84.5 us on 11008x4096, 59.4 against 77.8
+// on 4096x11008, 115.8 against 154.6 on 20480x5120; at 192 the prefill
+// kernel is as fast or faster).
+constexpr int kDecodeMaxN = 128;
 
 bool use_prefill(const usw_fmt* f, int32_t N) { return f->val_type == USW_VAL_F16 && N > kDecodeMaxN; }
 
@@ -815,7 +820,7 @@ bool lean_values(const usw_fmt* f, const usw::Geometry& g) {
 
 Plan make_plan(const usw::Geometry& g, int N, int splits_req, bool i4, bool lean) {
   Plan p;
-  p.nchunk = N <= 16 ? 16 : 32;
+  p.nchunk = N <= 16 ? 16 : N <= 32 ? 32 : 64;
   p.ring = !i4 && lean && N <= 16;
   if (p.ring) {
     // One round of resident workgroups, each keeping at most 63 GroupTiles
@@ -835,7 +840,7 @@ Plan make_plan(const usw::Geometry& g, int N, int splits_req, bool i4, bool lean
     p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
     return p;
   }
-  const CfgInfo ci = cfg_info(N > 16, i4, lean);
+  const CfgInfo ci = cfg_info(p.nchunk, i4, lean);
   p.waves = ci.waves;
   int64_t s = splits_req;
   if (s <= 0) {
@@ -886,7 +891,9 @@ void launch_cfg(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
 
 template <int NB, bool I4, int CH>
 void launch_decode(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
-  if constexpr (NB == 2)
+  if constexpr (NB == 4)
+    launch_cfg<NB, I4, CH, DefaultCfg4>(a, f16out, grid, s);
+  else if constexpr (NB == 2)
     launch_cfg<NB, I4, CH, DefaultCfg2>(a, f16out, grid, s);
   else if constexpr (I4)
     launch_cfg<NB, I4, CH, DefaultCfgI4>(a, f16out, grid, s);
@@ -966,17 +973,20 @@ usw_status launch_call(const usw_fmt* f, const usw::Geometry& g, const CallPlan&
     a.Gc = Gc;
     a.splits = p.splits;
     a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
-    const bool two = nc > 16;
+    const int nb = nc > 32 ? 4 : nc > 16 ? 2 : 1;   // 16-token blocks of this pass
     if (p.ring) {
       ring_launch(a, f16out, grid, s);
     } else if (i4) {
-      if (two) launch_decode<2, true, 3>(a, f16out, grid, s);
+      if (nb == 4) launch_decode<4, true, 3>(a, f16out, grid, s);
+      else if (nb == 2) launch_decode<2, true, 3>(a, f16out, grid, s);
       else launch_decode<1, true, 3>(a, f16out, grid, s);
     } else if (lean) {
-      if (two) launch_decode<2, false, 5>(a, f16out, grid, s);
+      if (nb == 4) launch_decode<4, false, 5>(a, f16out, grid, s);
+      else if (nb == 2) launch_decode<2, false, 5>(a, f16out, grid, s);
       else launch_decode<1, false, 5>(a, f16out, grid, s);
     } else {
-      if (two) launch_decode<2, false, 6>(a, f16out, grid, s);
+      if (nb == 4) launch_decode<4, false, 6>(a, f16out, grid, s);
+      else if (nb == 2) launch_decode<2, false, 6>(a, f16out, grid, s);
       else launch_decode<1, false, 6>(a, f16out, grid, s);
     }
     if (hipGetLastError() != hipSuccess) return USW_ERR_HIP;
