@@ -482,7 +482,8 @@ usw_status usw_union_spmm_counter_bytes(const usw_union_fmt* fmt, int32_t N, int
 /*
  * Y = W_sp . X on the GPU from an IE-BME encoding (device pointers), with the
  * same X, Y, workspace and stream conventions as usw_spmm, in passes of up
- * to 32 tokens.  The kernels take INT4 or 2-bit values on LTs of 16, 32 or
+ * to 32 tokens (64 for 2 x 2 grids on 64 x 64 LTs without a rowmap).  The
+ * kernels take INT4 or 2-bit values on LTs of 16, 32 or
  * 64 rows by 64 columns (M a multiple of 64), any area grid the format
  * allows with areas at least 8 columns wide (c_a <= 8), and a rowmap or none.
  * The section illustrates R_A = C_A = 2 and states the LSPD gather for a

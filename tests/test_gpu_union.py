@@ -80,10 +80,17 @@ def test_union_tiny_integer_exact_bitwise():
     assert_exact(W, mask, X, "tiny exact")
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 15, 16, 17, 31, 32, 33, 48, 70])
+@pytest.mark.parametrize("N", [1, 2, 3, 15, 16, 17, 31, 32, 33, 48, 64, 65, 70, 100, 128])
 def test_union_ragged_n(N):
     W, mask, X = exact_case(192, 640, N, 0.5, 100 + N)
     assert_exact(W, mask, X, f"N={N}")
+
+
+@pytest.mark.parametrize("N,splits", [(64, 3), (100, 2)])
+def test_union_64_token_passes_with_split_k(N, splits):
+    """Passes of 64 tokens (four token blocks per wave) with split K."""
+    W, mask, X = exact_case(256, 2048, N, 0.5, 300 + N)
+    assert_exact(W, mask, X, f"N={N} splits={splits}", splits=splits)
 
 
 @pytest.mark.parametrize("shape", [(64, 64), (64, 1024), (1024, 64), (192, 320), (128, 4096), (64, 32768)])

@@ -61,7 +61,7 @@ def encode(W, mask, layout):
     return usw.union_encode_host(W, mask, (16, 64), (2, 2), "i2", perm=perms)
 
 
-@pytest.mark.parametrize("N", [1, 2, 8, 16, 17, 32, 40])
+@pytest.mark.parametrize("N", [1, 2, 8, 16, 17, 32, 40, 64, 80])
 @pytest.mark.parametrize("layout", ["lt64", "lt16", "lt16_reordered"])
 def test_w2_integer_exact_bitwise(N, layout):
     M, K = 320, 1024

@@ -809,9 +809,11 @@ __global__ __launch_bounds__(kUGThreads, OCC) void union_grid_decode_kernel(Args
 // ---------------------------------------------------------------------------
 
 // Waves per SIMD the register allocation allows: 5 up to 16 tokens, 3 for
-// 17..32 (twice the accumulators and X fragments).
+// 17..32 (twice the accumulators and X fragments), 2 for passes of 64
+// tokens (64-row LTs with 2 x 2 areas only).
 constexpr int kOcc1 = 5;
 constexpr int kOcc2 = 3;
+constexpr int kOcc4 = 2;
 
 // Which kernel runs a format: the 2 x 2 kernels for their LT shapes, the
 // area-grid kernel for the rest.
@@ -819,7 +821,7 @@ enum class UKind { kLt64, kLt16, kGrid };
 
 struct UPlan {
   int splits;
-  int nchunk;   // tokens per pass (16 or 32)
+  int nchunk;   // tokens per pass (16, 32, or 64 for the 64-row-LT 2 x 2 kernel)
   UKind kind;
   int ltm;      // LT rows
 };
@@ -833,19 +835,22 @@ int64_t union_strips(const usw::UnionGeometry& g) { return g.M / 64; }
 
 UPlan union_plan(const usw::UnionGeometry& g, bool mapped, int N, int splits_req) {
   UPlan p;
-  p.nchunk = N <= 16 ? 16 : 32;
   p.ltm = static_cast<int>(g.lt_m);
   const bool two_by_two = g.r_a == 2 && g.c_a == 2;
   p.kind = (two_by_two && g.lt_m == 64 && !mapped) ? UKind::kLt64
            : (two_by_two && g.lt_m == 16)           ? UKind::kLt16
                                                     : UKind::kGrid;
+  // One LT rebuild serves every token of a pass; the 64-row-LT kernel takes
+  // passes of 64 tokens (one instead of two up to N = 64).
+  p.nchunk = N <= 16 ? 16 : (N <= 32 || p.kind != UKind::kLt64) ? 32 : 64;
   const int64_t strips = union_strips(g);
   // The four waves of a workgroup share its LT columns; a wave keeps the
   // offsets of at most 63 columns (64-row LTs), 31 (32-row LTs: two LT rows
   // per register) or 15 (16-row LTs: four LT rows per register).
   const int64_t per_split = kUWaves;
   const int64_t max_cols = g.lt_m - 1;
-  const int occ = p.kind == UKind::kLt64 ? (N <= 16 ? kOcc1 : kOcc2) : (N <= 16 ? kOcc16a : kOcc16b);
+  const int occ = p.kind == UKind::kLt64 ? (p.nchunk == 16 ? kOcc1 : p.nchunk == 32 ? kOcc2 : kOcc4)
+                                         : (N <= 16 ? kOcc16a : kOcc16b);
   int64_t s = splits_req;
   if (s <= 0) {
     // About one round of resident workgroups, each wave keeping at least 3
@@ -901,9 +906,15 @@ void union_grid_launch(const Args& a, bool f16out, dim3 grid, hipStream_t s) {
 
 template <int NB, int BITS>
 void union_launch(const Args& a, bool f16out, const UPlan& p, dim3 grid, hipStream_t s) {
-  constexpr int occ = NB == 1 ? kOcc1 : kOcc2;
+  constexpr int occ = NB == 1 ? kOcc1 : NB == 2 ? kOcc2 : kOcc4;
   constexpr int occ16 = NB == 1 ? kOcc16a : kOcc16b;
-  if (p.kind == UKind::kGrid) {
+  if constexpr (NB == 4) {
+    // Passes of 64 tokens exist for the 64-row-LT 2 x 2 kernel only.
+    if (f16out)
+      union_decode_kernel<NB, BITS, true, occ><<<grid, kUThreads, 0, s>>>(a);
+    else
+      union_decode_kernel<NB, BITS, false, occ><<<grid, kUThreads, 0, s>>>(a);
+  } else if (p.kind == UKind::kGrid) {
     if (p.ltm == 16) union_grid_launch<16, NB, BITS>(a, f16out, grid, s);
     else if (p.ltm == 32) union_grid_launch<32, NB, BITS>(a, f16out, grid, s);
     else union_grid_launch<64, NB, BITS>(a, f16out, grid, s);
@@ -988,7 +999,10 @@ usw_status usw_union_spmm(const usw_union_fmt* f, const uint16_t* X, void* Y, in
     a.lg_ca = log2i(g.c_a);
     a.lg_q = log2i(g.Q);
     const bool i2 = f->val_type == USW_VAL_I2;
-    if (nc > 16) {
+    if (nc > 32) {
+      if (i2) union_launch<4, 2>(a, f16out, p, grid, s);
+      else union_launch<4, 4>(a, f16out, p, grid, s);
+    } else if (nc > 16) {
       if (i2) union_launch<2, 2>(a, f16out, p, grid, s);
       else union_launch<2, 4>(a, f16out, p, grid, s);
     } else {
