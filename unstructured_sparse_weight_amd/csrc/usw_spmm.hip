@@ -846,8 +846,18 @@ Plan make_plan(const usw::Geometry& g, int N, int splits_req, bool i4, bool lean
   if (s <= 0) {
     // About one round of resident workgroups (occ waves per SIMD, 4 SIMDs
     // per compute unit), each wave keeping at least 3 GroupTiles to stream.
+    // Passes of 64 tokens on a matrix with at most one strip per compute
+    // unit take as many workgroups as there are compute units, no more: the
+    // split partial sums (64 x M fp32 per split, written and read back) then
+    // cost more than the second workgroup per compute unit gains (measured
+    // on MI355X at N = 64: 11008x4096 31.0 us with 1 split against 37.3 with
+    // 3; 4096x11008 27.3 with 4 against 31.0 with 8; 15360x5120 38.1 with 1
+    // against 44.5 with 2).
     const int64_t target = kComputeUnits * 4 * ci.occ / ci.waves;
-    s = std::max<int64_t>(1, (target + g.Gr / 2) / g.Gr);
+    if (p.nchunk == 64 && g.Gr <= kComputeUnits)
+      s = kComputeUnits / g.Gr;
+    else
+      s = std::max<int64_t>(1, (target + g.Gr / 2) / g.Gr);
     s = std::min<int64_t>(s, std::max<int64_t>(1, g.Gc / (p.waves * 3)));
   }
   const int64_t smax = std::max<int64_t>(1, g.Gc / p.waves);

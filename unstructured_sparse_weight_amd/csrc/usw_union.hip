@@ -855,8 +855,14 @@ UPlan union_plan(const usw::UnionGeometry& g, bool mapped, int N, int splits_req
   if (s <= 0) {
     // About one round of resident workgroups, each wave keeping at least 3
     // LTs to stream.
+    // Passes of 64 tokens with at most one strip per compute unit: one
+    // workgroup per compute unit, as in the TCA-BME decode (the split
+    // partial sums cost more than a second workgroup gains).
     const int64_t target = 256 * 4 * occ / kUWaves;
-    s = std::max<int64_t>(1, (target + strips / 2) / strips);
+    if (p.nchunk == 64 && strips <= 256)
+      s = 256 / strips;
+    else
+      s = std::max<int64_t>(1, (target + strips / 2) / strips);
     s = std::min<int64_t>(s, std::max<int64_t>(1, g.lc / (per_split * 3)));
   }
   const int64_t smax = std::max<int64_t>(1, g.lc / per_split);
