@@ -94,6 +94,21 @@ def test_four_block_passes_integer_exact_bitwise(dtype, N, splits):
                           Yref.astype(np.float16).astype(np.float64))
 
 
+@pytest.mark.parametrize("N", [80, 90])
+@pytest.mark.parametrize("dtype", ["f16", "i4"])
+def test_short_last_pass_with_its_own_split_factor_bitwise(dtype, N):
+    """200 strips of 24 GroupTile columns: a 64-token pass takes one split
+    (one workgroup per compute unit), the shorter last pass (16 or 26
+    tokens) two, so only the last pass uses the split-K workspace."""
+    M, K = 64 * 200, 64 * 24
+    W, mask, X = wl.config_case(1, M, K, N, 0.5, exact=True)
+    if dtype == "i4":
+        W = wl.weight_int4_exact(M, K, np.random.default_rng(40 + N), mask)
+    Yref, _ = oracle_ref(W, mask, X, dtype)
+    assert np.array_equal(run_gpu(W, mask, X, dtype, out=torch.float32), Yref)
+    assert np.array_equal(run_gpu(W, mask, X, dtype, out=torch.float16), Yref.astype(np.float16).astype(np.float64))
+
+
 @pytest.mark.parametrize("N", [1, 2, 3, 7, 15, 16, 17, 24, 31, 32, 33, 40, 48, 63, 64, 65, 80, 96, 97, 112, 128,
                                129])
 def test_ragged_n(N):

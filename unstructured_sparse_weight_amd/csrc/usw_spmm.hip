@@ -769,8 +769,10 @@ CfgInfo cfg_info(int nchunk, bool i4, bool lean) {
 constexpr int64_t kComputeUnits = 256;
 
 struct Plan {
-  int splits;     // workgroups per 64-row strip
+  int splits;     // workgroups per 64-row strip, passes of nchunk tokens
   int nchunk;     // columns of N per kernel pass (16, 32 or 64)
+  int rsplits;    // the same for the last pass when it is shorter (N > 64,
+  int rchunk;     // N mod 64 tokens in a pass of rchunk), else splits, 0
   int waves;      // waves per workgroup
   bool ring;      // the workgroup-cooperative kernel
 };
@@ -818,9 +820,41 @@ bool lean_values(const usw_fmt* f, const usw::Geometry& g) {
          static_cast<double>(f->nnz) <= 0.55 * static_cast<double>(g.M) * static_cast<double>(g.K);
 }
 
+// Pass size (16, 32 or 64 tokens) that n tokens take.
+int pass_chunk(int n) { return n <= 16 ? 16 : n <= 32 ? 32 : 64; }
+
+// Split factor of the per-wave decode kernel for passes of `chunk` tokens.
+int wave_splits(const usw::Geometry& g, int chunk, int splits_req, bool i4, bool lean) {
+  const CfgInfo ci = cfg_info(chunk, i4, lean);
+  int64_t s = splits_req;
+  if (s <= 0) {
+    // About one round of resident workgroups (occ waves per SIMD, 4 SIMDs
+    // per compute unit), each wave keeping at least 3 GroupTiles to stream.
+    // Passes of 64 tokens on a matrix with at most one strip per compute
+    // unit take as many workgroups as there are compute units, no more: the
+    // split partial sums (64 x M fp32 per split, written and read back) then
+    // cost more than the second workgroup per compute unit gains (measured
+    // on MI355X at N = 64: 11008x4096 31.0 us with 1 split against 37.3 with
+    // 3; 4096x11008 27.3 with 4 against 31.0 with 8; 15360x5120 38.1 with 1
+    // against 44.5 with 2).
+    const int64_t target = kComputeUnits * 4 * ci.occ / ci.waves;
+    if (chunk == 64 && g.Gr <= kComputeUnits)
+      s = kComputeUnits / g.Gr;
+    else
+      s = std::max<int64_t>(1, (target + g.Gr / 2) / g.Gr);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, g.Gc / (ci.waves * 3)));
+  }
+  const int64_t smax = std::max<int64_t>(1, g.Gc / ci.waves);
+  // Each wave caches its GroupTile offsets in one register: at most 63
+  // GroupTiles per wave.
+  const int64_t smin = (g.Gc + 63 * ci.waves - 1) / (63 * ci.waves);
+  return static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
+}
+
 Plan make_plan(const usw::Geometry& g, int N, int splits_req, bool i4, bool lean) {
   Plan p;
-  p.nchunk = N <= 16 ? 16 : N <= 32 ? 32 : 64;
+  p.nchunk = pass_chunk(N);
+  p.rchunk = 0;
   p.ring = !i4 && lean && N <= 16;
   if (p.ring) {
     // One round of resident workgroups, each keeping at most 63 GroupTiles
@@ -838,33 +872,15 @@ Plan make_plan(const usw::Geometry& g, int N, int splits_req, bool i4, bool lean
     const int64_t smax = std::max<int64_t>(1, g.Gc / 4);
     const int64_t smin = (g.Gc + 62) / 63;
     p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
+    p.rsplits = p.splits;
     return p;
   }
-  const CfgInfo ci = cfg_info(p.nchunk, i4, lean);
-  p.waves = ci.waves;
-  int64_t s = splits_req;
-  if (s <= 0) {
-    // About one round of resident workgroups (occ waves per SIMD, 4 SIMDs
-    // per compute unit), each wave keeping at least 3 GroupTiles to stream.
-    // Passes of 64 tokens on a matrix with at most one strip per compute
-    // unit take as many workgroups as there are compute units, no more: the
-    // split partial sums (64 x M fp32 per split, written and read back) then
-    // cost more than the second workgroup per compute unit gains (measured
-    // on MI355X at N = 64: 11008x4096 31.0 us with 1 split against 37.3 with
-    // 3; 4096x11008 27.3 with 4 against 31.0 with 8; 15360x5120 38.1 with 1
-    // against 44.5 with 2).
-    const int64_t target = kComputeUnits * 4 * ci.occ / ci.waves;
-    if (p.nchunk == 64 && g.Gr <= kComputeUnits)
-      s = kComputeUnits / g.Gr;
-    else
-      s = std::max<int64_t>(1, (target + g.Gr / 2) / g.Gr);
-    s = std::min<int64_t>(s, std::max<int64_t>(1, g.Gc / (p.waves * 3)));
-  }
-  const int64_t smax = std::max<int64_t>(1, g.Gc / p.waves);
-  // Each wave caches its GroupTile offsets in one register: at most 63
-  // GroupTiles per wave.
-  const int64_t smin = (g.Gc + 63 * p.waves - 1) / (63 * p.waves);
-  p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
+  p.waves = cfg_info(p.nchunk, i4, lean).waves;
+  p.splits = wave_splits(g, p.nchunk, splits_req, i4, lean);
+  // A shorter last pass gets the split factor of its own size.
+  const int rem = N > p.nchunk ? N % p.nchunk : 0;
+  p.rchunk = rem > 0 ? pass_chunk(rem) : 0;
+  p.rsplits = rem > 0 ? wave_splits(g, p.rchunk, splits_req, i4, lean) : p.splits;
   return p;
 }
 
@@ -886,9 +902,13 @@ usw_status check_common(const usw_fmt* f, int32_t y_type, int32_t N, usw::Geomet
 // partial sums of every split.
 size_t counters_bytes(const usw::Geometry& g) { return (static_cast<size_t>(4 * g.Gr) + 255) & ~size_t(255); }
 
+// Partial sums of the largest pass: splits x tokens of the pass x M fp32.
 size_t workspace_bytes(const usw::Geometry& g, const Plan& p) {
-  if (p.splits <= 1) return 0;
-  return counters_bytes(g) + static_cast<size_t>(p.splits) * p.nchunk * g.M * sizeof(float);
+  const size_t full = p.splits > 1 ? static_cast<size_t>(p.splits) * p.nchunk : 0;
+  const size_t last = p.rchunk > 0 && p.rsplits > 1 ? static_cast<size_t>(p.rsplits) * p.rchunk : 0;
+  const size_t cols = std::max(full, last);
+  if (cols == 0) return 0;
+  return counters_bytes(g) + cols * g.M * sizeof(float);
 }
 
 template <int NB, bool I4, int CH, class C>
@@ -957,8 +977,6 @@ usw_status launch_call(const usw_fmt* f, const usw::Geometry& g, const CallPlan&
   if (c.prefill) return usw::prefill_launch(f, g, X, Y, y_type == USW_OUT_F16, N, counters, part, c.pp, stream);
   const Plan& p = c.p;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t nblk = g.Gr * p.splits;
-  const dim3 grid(static_cast<unsigned>(nblk));
   const int M = static_cast<int>(g.M), K = static_cast<int>(g.K), Gc = static_cast<int>(g.Gc);
   const size_t ybytes = y_type == USW_OUT_F16 ? 2 : 4;
   const bool f16out = y_type == USW_OUT_F16;
@@ -967,6 +985,10 @@ usw_status launch_call(const usw_fmt* f, const usw::Geometry& g, const CallPlan&
 
   for (int n0 = 0; n0 < N; n0 += p.nchunk) {
     const int nc = std::min(p.nchunk, N - n0);
+    // The shorter last pass of a multi-pass call has its own split factor.
+    const int splits = (p.rchunk > 0 && n0 + p.nchunk > N) ? p.rsplits : p.splits;
+    const int64_t nblk = g.Gr * splits;
+    const dim3 grid(static_cast<unsigned>(nblk));
     Args a{};
     a.bitmaps = f->bitmaps;
     a.offsets = f->offsets;
@@ -981,8 +1003,8 @@ usw_status launch_call(const usw_fmt* f, const usw::Geometry& g, const CallPlan&
     a.K = K;
     a.N = nc;
     a.Gc = Gc;
-    a.splits = p.splits;
-    a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
+    a.splits = splits;
+    a.remap = (splits > 1 && nblk % 8 == 0) ? 1 : 0;
     const int nb = nc > 32 ? 4 : nc > 16 ? 2 : 1;   // 16-token blocks of this pass
     if (p.ring) {
       ring_launch(a, f16out, grid, s);
@@ -1123,7 +1145,7 @@ usw_status usw_spmm_counter_bytes(const usw_fmt* f, int32_t N, int32_t splits, s
     *bytes = usw::prefill_counter_bytes(g, usw::prefill_plan(g, N, sr));
   } else {
     const Plan p = make_plan(g, N, sr, f->val_type == USW_VAL_I4, lean_values(f, g));
-    *bytes = p.splits > 1 ? counters_bytes(g) : 0;
+    *bytes = workspace_bytes(g, p) > 0 ? counters_bytes(g) : 0;
   }
   return USW_OK;
 }
