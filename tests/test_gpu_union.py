@@ -86,6 +86,14 @@ def test_union_ragged_n(N):
     assert_exact(W, mask, X, f"N={N}")
 
 
+@pytest.mark.parametrize("N", [80, 90])
+def test_union_short_last_pass_with_its_own_split_factor(N):
+    """200 strips of 24 LT columns: the 64-token pass takes one split, the
+    shorter last pass two, so only the last pass uses the workspace."""
+    W, mask, X = exact_case(64 * 200, 64 * 24, N, 0.5, 400 + N)
+    assert_exact(W, mask, X, f"N={N}")
+
+
 @pytest.mark.parametrize("N,splits", [(64, 3), (100, 2)])
 def test_union_64_token_passes_with_split_k(N, splits):
     """Passes of 64 tokens (four token blocks per wave) with split K."""

@@ -822,6 +822,8 @@ enum class UKind { kLt64, kLt16, kGrid };
 struct UPlan {
   int splits;
   int nchunk;   // tokens per pass (16, 32, or 64 for the 64-row-LT 2 x 2 kernel)
+  int rsplits;  // the same for the last pass when it is shorter (N > nchunk,
+  int rchunk;   // N mod nchunk tokens in a pass of rchunk), else splits, 0
   UKind kind;
   int ltm;      // LT rows
 };
@@ -833,6 +835,38 @@ constexpr int kOcc16b = 2;
 // 64-row strips of the matrix (one workgroup's rows).
 int64_t union_strips(const usw::UnionGeometry& g) { return g.M / 64; }
 
+// Tokens per pass for n tokens on a kernel kind.
+int union_chunk(UKind kind, int n) { return n <= 16 ? 16 : (n <= 32 || kind != UKind::kLt64) ? 32 : 64; }
+
+// Split factor for passes of `chunk` tokens.
+int union_splits(const usw::UnionGeometry& g, UKind kind, int chunk, int splits_req) {
+  const int64_t strips = union_strips(g);
+  // The four waves of a workgroup share its LT columns; a wave keeps the
+  // offsets of at most 63 columns (64-row LTs), 31 (32-row LTs: two LT rows
+  // per register) or 15 (16-row LTs: four LT rows per register).
+  const int64_t per_split = kUWaves;
+  const int64_t max_cols = g.lt_m - 1;
+  const int occ = kind == UKind::kLt64 ? (chunk == 16 ? kOcc1 : chunk == 32 ? kOcc2 : kOcc4)
+                                       : (chunk == 16 ? kOcc16a : kOcc16b);
+  int64_t s = splits_req;
+  if (s <= 0) {
+    // About one round of resident workgroups, each wave keeping at least 3
+    // LTs to stream.  Passes of 64 tokens with at most one strip per
+    // compute unit: one workgroup per compute unit, as in the TCA-BME
+    // decode (the split partial sums cost more than a second workgroup
+    // gains).
+    const int64_t target = 256 * 4 * occ / kUWaves;
+    if (chunk == 64 && strips <= 256)
+      s = 256 / strips;
+    else
+      s = std::max<int64_t>(1, (target + strips / 2) / strips);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, g.lc / (per_split * 3)));
+  }
+  const int64_t smax = std::max<int64_t>(1, g.lc / per_split);
+  const int64_t smin = (g.lc + max_cols * per_split - 1) / (max_cols * per_split);
+  return static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
+}
+
 UPlan union_plan(const usw::UnionGeometry& g, bool mapped, int N, int splits_req) {
   UPlan p;
   p.ltm = static_cast<int>(g.lt_m);
@@ -842,32 +876,12 @@ UPlan union_plan(const usw::UnionGeometry& g, bool mapped, int N, int splits_req
                                                     : UKind::kGrid;
   // One LT rebuild serves every token of a pass; the 64-row-LT kernel takes
   // passes of 64 tokens (one instead of two up to N = 64).
-  p.nchunk = N <= 16 ? 16 : (N <= 32 || p.kind != UKind::kLt64) ? 32 : 64;
-  const int64_t strips = union_strips(g);
-  // The four waves of a workgroup share its LT columns; a wave keeps the
-  // offsets of at most 63 columns (64-row LTs), 31 (32-row LTs: two LT rows
-  // per register) or 15 (16-row LTs: four LT rows per register).
-  const int64_t per_split = kUWaves;
-  const int64_t max_cols = g.lt_m - 1;
-  const int occ = p.kind == UKind::kLt64 ? (p.nchunk == 16 ? kOcc1 : p.nchunk == 32 ? kOcc2 : kOcc4)
-                                         : (N <= 16 ? kOcc16a : kOcc16b);
-  int64_t s = splits_req;
-  if (s <= 0) {
-    // About one round of resident workgroups, each wave keeping at least 3
-    // LTs to stream.
-    // Passes of 64 tokens with at most one strip per compute unit: one
-    // workgroup per compute unit, as in the TCA-BME decode (the split
-    // partial sums cost more than a second workgroup gains).
-    const int64_t target = 256 * 4 * occ / kUWaves;
-    if (p.nchunk == 64 && strips <= 256)
-      s = 256 / strips;
-    else
-      s = std::max<int64_t>(1, (target + strips / 2) / strips);
-    s = std::min<int64_t>(s, std::max<int64_t>(1, g.lc / (per_split * 3)));
-  }
-  const int64_t smax = std::max<int64_t>(1, g.lc / per_split);
-  const int64_t smin = (g.lc + max_cols * per_split - 1) / (max_cols * per_split);
-  p.splits = static_cast<int>(std::max(smin, std::max<int64_t>(1, std::min(s, smax))));
+  p.nchunk = union_chunk(p.kind, N);
+  p.splits = union_splits(g, p.kind, p.nchunk, splits_req);
+  // A shorter last pass gets the split factor of its own size.
+  const int rem = N > p.nchunk ? N % p.nchunk : 0;
+  p.rchunk = rem > 0 ? union_chunk(p.kind, rem) : 0;
+  p.rsplits = rem > 0 ? union_splits(g, p.kind, p.rchunk, splits_req) : p.splits;
   return p;
 }
 
@@ -875,9 +889,13 @@ size_t union_counter_bytes(const usw::UnionGeometry& g) {
   return (static_cast<size_t>(4 * union_strips(g)) + 255) & ~size_t(255);
 }
 
+// Partial sums of the largest pass: splits x tokens of the pass x M fp32.
 size_t union_workspace_bytes(const usw::UnionGeometry& g, const UPlan& p) {
-  if (p.splits <= 1) return 0;
-  return union_counter_bytes(g) + static_cast<size_t>(p.splits) * p.nchunk * g.M * sizeof(float);
+  const size_t full = p.splits > 1 ? static_cast<size_t>(p.splits) * p.nchunk : 0;
+  const size_t last = p.rchunk > 0 && p.rsplits > 1 ? static_cast<size_t>(p.rsplits) * p.rchunk : 0;
+  const size_t cols = std::max(full, last);
+  if (cols == 0) return 0;
+  return union_counter_bytes(g) + cols * g.M * sizeof(float);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -960,7 +978,9 @@ usw_status usw_union_spmm_counter_bytes(const usw_union_fmt* f, int32_t N, int32
   usw::UnionGeometry g;
   usw_status st = union_check(f, USW_OUT_F16, N, &g);
   if (st) return st;
-  *bytes = union_plan(g, f->rowmap != nullptr, N, splits < 0 ? 0 : splits).splits > 1 ? union_counter_bytes(g) : 0;
+  *bytes = union_workspace_bytes(g, union_plan(g, f->rowmap != nullptr, N, splits < 0 ? 0 : splits)) > 0
+               ? union_counter_bytes(g)
+               : 0;
   return USW_OK;
 }
 
@@ -977,12 +997,14 @@ usw_status usw_union_spmm(const usw_union_fmt* f, const uint16_t* X, void* Y, in
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return USW_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t nblk = union_strips(g) * p.splits;
-  const dim3 grid(static_cast<unsigned>(nblk));
   const size_t ybytes = y_type == USW_OUT_F16 ? 2 : 4;
   const bool f16out = y_type == USW_OUT_F16;
   for (int n0 = 0; n0 < N; n0 += p.nchunk) {
     const int nc = std::min(p.nchunk, N - n0);
+    // The shorter last pass of a multi-pass call has its own split factor.
+    const int splits = (p.rchunk > 0 && n0 + p.nchunk > N) ? p.rsplits : p.splits;
+    const int64_t nblk = union_strips(g) * splits;
+    const dim3 grid(static_cast<unsigned>(nblk));
     Args a{};
     a.bitmaps = f->bitmaps;
     a.offsets = f->offsets;
@@ -998,8 +1020,8 @@ usw_status usw_union_spmm(const usw_union_fmt* f, const uint16_t* X, void* Y, in
     a.K = static_cast<int>(g.K);
     a.N = nc;
     a.Gc = static_cast<int>(g.lc);
-    a.splits = p.splits;
-    a.remap = (p.splits > 1 && nblk % 8 == 0) ? 1 : 0;
+    a.splits = splits;
+    a.remap = (splits > 1 && nblk % 8 == 0) ? 1 : 0;
     a.lg_am = log2i(g.am);
     a.lg_ak = log2i(g.ak);
     a.lg_ca = log2i(g.c_a);
