@@ -260,11 +260,16 @@ __global__ __launch_bounds__(kCThreads, 4) void cbc_spmspv_kernel(CArgs a) {
     CData d;
     cbc_load(d, a, gi, c_begin, cbc_meta(a, gi, c_begin, lane), lane);
     for (int c = c_begin; c < c_end; ++c) {
+      // Loads go out at a raised wave priority (as in the TCA-BME decode).
+      __builtin_amdgcn_s_setprio(2);
       const CMeta m2 = cbc_meta(a, gi, min(c + 2, c_last), lane);
+      __builtin_amdgcn_s_setprio(0);
       cbc_commit(d, buf, tab, lane);
       const float xf = d.xf;
       const uint32_t amask = d.amask;
+      __builtin_amdgcn_s_setprio(2);
       cbc_load(d, a, gi, min(c + 1, c_last), m1, lane);
+      __builtin_amdgcn_s_setprio(0);
       wave_sync();
       cbc_compute(xf, amask, buf, tab, lut, cl, acc, lane);
       wave_sync();

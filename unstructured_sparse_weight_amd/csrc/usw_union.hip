@@ -216,7 +216,9 @@ __global__ __launch_bounds__(kUThreads, OCC) void union_decode_kernel(Args a) {
     load(s[0], c_begin);
     write_tab(s[0]);
     auto step = [&](USlot<NB>& cur, int c, USlot<NB>& nxt) {
+      __builtin_amdgcn_s_setprio(2);   // loads first (see the TCA-BME decode step)
       load(nxt, c + 1);
+      __builtin_amdgcn_s_setprio(0);
       commit(cur);
       wave_sync();
       union_tile_mma<NB, BITS>(cur.x, smem, tab, lut, cur.P, acc, corr, lane);
@@ -469,7 +471,9 @@ __global__ __launch_bounds__(kU16Threads, OCC) void union16_decode_kernel(Args a
     load(s[0], c_begin);
     write_tab(s[0]);
     auto step = [&](U16Slot<NB>& cur, int c, U16Slot<NB>& nxt) {
+      __builtin_amdgcn_s_setprio(2);   // loads first (see the TCA-BME decode step)
       load(nxt, c + 1);
+      __builtin_amdgcn_s_setprio(0);
       commit(cur);
       wave_sync();
       u16_tile_mma<NB, BITS>(cur, mapped, smem, tab, lut, acc, corr, lane);
@@ -763,7 +767,9 @@ __global__ __launch_bounds__(kUGThreads, OCC) void union_grid_decode_kernel(Args
     load(s[0], c_begin);
     write_tab(s[0]);
     auto step = [&](Slot& cur, int c, Slot& nxt) {
+      __builtin_amdgcn_s_setprio(2);   // loads first (see the TCA-BME decode step)
       load(nxt, c + 1);
+      __builtin_amdgcn_s_setprio(0);
       commit(cur);
       wave_sync();
       ug_tile_mma<LTM, NB, BITS>(cur, a, mapped, smem, tab, lut, vb_elems, acc, corr, lane);
