@@ -818,7 +818,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // fp16 values with more than this many tokens take the prefill kernels;
 // fewer take the decode kernels in passes of up to 64 tokens, which re-read
 // the weight per pass but beat the 256-token prefill tiles up to 128 tokens
-// on MI355X (at 128: 71.7 against 84.5 us on 11008x4096, 59.4 against 77.8
+// on MI355X (at 128: 59.5 against 84.5 us on 11008x4096, 53.0 against 77.8
 // on 4096x11008, 115.8 against 154.6 on 20480x5120; at 192 the prefill
 // kernel is as fast or faster).
 constexpr int kDecodeMaxN = 128;
